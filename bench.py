@@ -1,0 +1,219 @@
+"""Benchmark: single-token MLA decode on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one decode call (stage-1 split kernel + merge kernel) over one batch
+of seeded synthetic inputs already resident in HBM; the split plan is made
+once beforehand (reported as plan_us).  Every timed step is cold: a 1 GiB
+buffer is written before it, which evicts the 256 MB last-level (MALL) cache,
+so the KV stream comes from HBM.  ms_per_step is the mean of the per-step
+event times; value = algorithmic KV bytes / that time.
+
+Algorithmic bytes = tokens x stored bytes per row (bf16 1152, fp8 576, MXFP4
+288 + 18 scale bytes); query, output, partials and page ids are overhead.
+
+Prints one JSON line.  Also reports the roofline of the dominant kernel
+(stage 1, timed with HIP events recorded by the library around its own
+launch on the same stream) and the fp64 oracle timed on the host cores on a
+bounded sample of the same workload.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+DEFAULT_WORKLOAD = "bs64_kv1024_fp8"
+METRIC = "µs/call and effective KV HBM GB/s (% of peak), MLA decode bs×kv_len"
+KERNEL_SRC = os.path.join(ROOT, "latent_attention_decode_amd", "csrc", "mla_kernels.hip")
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_record(workload: str):
+    """HBM bytes per stage-1 launch from a committed rocprofv3 --pmc summary,
+    if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"stage1_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_sha256_16") != kernel_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(case, budget_s: float = 12.0):
+    """The oracle as it stands, on a bounded sample of whole sequences."""
+    import oracle
+    threads = max(1, len(os.sched_getaffinity(0)))
+    per_seq = case.kv_algorithmic_bytes() / max(case.batch, 1)
+    t0 = time.perf_counter()
+    oracle.decode_case(case, batches=[0], nthreads=1)
+    one = max(time.perf_counter() - t0, 1e-4)
+    # sequences that fit the budget with every thread busy
+    n = int(min(case.batch, max(threads, (budget_s / one) * threads * 0.8)))
+    n = max(1, min(n, case.batch))
+    batches = list(range(n))
+    t0 = time.perf_counter()
+    oracle.decode_case(case, batches=batches, nthreads=threads)
+    dt = time.perf_counter() - t0
+    sample_bytes = per_seq * n if case.page_size == 1 and len(set(case.lens.tolist())) == 1 else \
+        float(sum(int(case.lens[b]) for b in batches)) * (case.kv_algorithmic_bytes() / case.total_tokens)
+    gbs = sample_bytes / dt / 1e9
+    full_us = case.kv_algorithmic_bytes() / (gbs * 1e9) * 1e6
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {case.batch} sequences ({int(sum(case.lens[:n]))} tokens), "
+                      f"{dt:.2f} s wall, fp64 C oracle",
+            "us_per_call_extrapolated": round(full_us, 1)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--warm-iters", type=int, default=100)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--split", type=int, default=0, help="split override (0 = planner)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this decode path "
+              "shards by sequence with no exchange, so run one process per GPU.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from latent_attention_decode_amd import binding, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+
+    name = args.workload
+    kv_dtype, batch, kv_len, ps, shuffled, seed = synth.CONFIGS[name]
+    print(f"[bench] generating {name}", file=sys.stderr, flush=True)
+    case = synth.config_case(name)
+    t = binding.case_to_device(case, dev)
+    out = torch.empty((case.batch, 16, 512), dtype=torch.bfloat16, device=dev)
+    alg_bytes = case.kv_algorithmic_bytes()
+
+    dec = binding.MlaDecode(kv_dtype, ps, device=0)
+    t0 = time.perf_counter()
+    ws_bytes = dec.plan(case.kv_indptr, case.kv_last_page_len, args.split)
+    plan_us = (time.perf_counter() - t0) * 1e6
+    n_items, max_splits, merge = binding.mla_decode_plan_info(dec.h)
+    res1 = binding.mla_decode_kernel_resources(dec.h, 0)
+    binding.mla_decode_set_profiling(dec.h, True)
+
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def run():
+        dec.run(t["q"], t["kv"], t["kv_scales"], t["kv_indptr"], out, t["kv_page_indices"],
+                t["kv_last_page_len"])
+
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+
+    for _ in range(args.warmup):
+        flush.zero_()
+        run()
+    torch.cuda.synchronize()
+
+    call_ms, s1_ms, mg_ms = [], [], []
+    print(f"[bench] timing {args.steps} cold steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for _ in range(args.steps):
+        flush.zero_()
+        ev0.record(stream)
+        run()
+        ev1.record(stream)
+        ev1.synchronize()
+        call_ms.append(ev0.elapsed_time(ev1))
+        s1_ms.append(binding.mla_decode_kernel_time_ms(dec.h, 0))
+        mg_ms.append(binding.mla_decode_kernel_time_ms(dec.h, 1))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    # warm: back-to-back calls, no flush (the KV may sit in the MALL)
+    binding.mla_decode_set_profiling(dec.h, False)
+    run()
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.warm_iters):
+        run()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    warm_us = ev0.elapsed_time(ev1) / args.warm_iters * 1e3
+
+    call = np.array(call_ms)
+    s1 = np.array(s1_ms)
+    mean_ms = float(call.mean())
+    trimmed = float(np.sort(call)[1:-1].mean()) if call.size > 2 else mean_ms
+    value = alg_bytes / (mean_ms * 1e-3) / 1e9
+    s1_mean = float(s1.mean())
+    achieved = alg_bytes / (s1_mean * 1e-3) / 1e9
+    traffic = traffic_record(name)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(mean_ms, 5),
+        "us_per_call": round(mean_ms * 1e3, 2),
+        "us_per_call_median": round(float(np.median(call)) * 1e3, 2),
+        "us_per_call_trimmed_mean": round(trimmed * 1e3, 2),
+        "us_per_call_warm": round(warm_us, 2),
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"bf16": "bf16", "fp8": "fp8-e4m3 (bf16 MFMA, fp32 acc)",
+                  "mxfp4": "mxfp4 (bf16 MFMA, fp32 acc)"}[kv_dtype],
+        "data": "synthetic",
+        "config": {"workload": name, "kv_dtype": kv_dtype, "batch": int(case.batch),
+                   "kv_len": kv_len if isinstance(kv_len, int) else list(kv_len),
+                   "total_tokens": int(case.total_tokens), "page_size": ps,
+                   "algorithmic_kv_bytes": int(alg_bytes)},
+        "plan": {"items": n_items, "max_splits": max_splits, "merge_launched": merge,
+                 "workspace_bytes": int(ws_bytes), "plan_us": round(plan_us, 1)},
+        "kernels": {"stage1_us": round(s1_mean * 1e3, 2),
+                    "merge_us": round(float(np.mean(mg_ms)) * 1e3, 2),
+                    "stage1_vgprs": res1["vgprs"], "stage1_lds_bytes": res1["lds_bytes"],
+                    "stage1_scratch_bytes": res1["scratch_bytes"]},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+        "timed_wall_s": round(wall, 3),
+    }
+    dec.close()
+    del flush
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(case)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

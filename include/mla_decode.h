@@ -1,0 +1,183 @@
+/*
+ * mla_decode.h -- C ABI of the MI355X (gfx950) single-token multi-head latent
+ * attention (MLA) decode library, libmla_decode.so.
+ *
+ * The operation.  For every sequence b of a batch and every query head h
+ * (16 heads share one latent KV head):
+ *
+ *   s_t       = sm_scale * < q[b,h,0:576], c_t[0:576] >
+ *   out[b,h,:] = sum_t softmax(s)_t * c_t[0:512]
+ *
+ * where c_t is the dequantised 576-wide cache row of token t (512 latent +
+ * 64 rope columns) and V is the first 512 columns of the same row.  This is
+ * the decode step of the amd-mixed-mla submissions: submission 599694
+ * ("overhead elimination"), function `_bmm` and kernel `_flash_fp8_single`;
+ * submission 727205 ("v25: LEAN"), kernels `mla_s1` (split-K stage 1) and
+ * `mla_rd` (stage 2 merge); submission 700955 ("locked baseline dispatch"),
+ * kernels `mla_attn_v71` / `reduce_lse_v71`.
+ *
+ * Cache formats (one per handle):
+ *   MLA_KV_BF16      rows of 576 bf16 (1152 bytes).
+ *   MLA_KV_FP8_E4M3  rows of 576 OCP e4m3fn codes (576 bytes); value = code x
+ *                    kv_scale, kv_scale one fp32 for the whole tensor, read
+ *                    from device memory (599694, `_flash_fp8_single`).
+ *   MLA_KV_MXFP4     rows of 288 bytes of e2m1 nibbles (element 2i in the low
+ *                    nibble of byte i) plus, in a separate array, one e8m0
+ *                    scale byte per 32 elements (18 per row, row stride >= 18);
+ *                    value = e2m1 x 2^(e-127) (700955, `mla_attn_v71`).
+ *
+ * Addressing.  With page_size == 1 the rows of sequence b are
+ * kv[kv_indptr[b] .. kv_indptr[b+1]).  With page_size > 1 (a power of two),
+ * kv is viewed as pages of page_size rows; kv_indptr counts pages, the pages
+ * of sequence b are kv_page_indices[kv_indptr[b] .. kv_indptr[b+1]) and its
+ * last page holds kv_last_page_len[b] (1..page_size) valid tokens; logical
+ * token j lives in row page*page_size + j%page_size.  A sequence of length 0
+ * produces a zero output.
+ *
+ * Ownership.  The caller owns every tensor, the workspace and the stream.  A
+ * handle owns only its plan (a small device work list, allocated by
+ * mla_decode_plan and freed by mla_decode_destroy).  All pointers passed to
+ * mla_decode_run are device pointers unless the name ends in _host.
+ *
+ * Errors.  Every call validates its arguments on the host before touching the
+ * GPU and returns a status; nothing is launched when a call fails, no
+ * exception crosses the ABI and the process is never terminated.  Launch
+ * failures map to MLA_ERR_HIP; faults inside a kernel surface at the caller's
+ * next synchronisation.  mla_decode_last_error() gives a per-handle message.
+ *
+ * Threading.  A handle may be used from one host thread at a time.
+ */
+#ifndef MLA_DECODE_H
+#define MLA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_KV_BF16 = 0,
+  MLA_KV_FP8_E4M3 = 1,
+  MLA_KV_MXFP4 = 2
+} mla_kv_dtype;
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1,          /* null pointer, bad size, inconsistent indptr ... */
+  MLA_ERR_UNSUPPORTED = 2,          /* shape or option this library does not implement */
+  MLA_ERR_NOT_PLANNED = 3,          /* run before a successful plan */
+  MLA_ERR_WORKSPACE_TOO_SMALL = 4,  /* workspace_bytes below the planned size */
+  MLA_ERR_HIP = 5                   /* a HIP runtime call failed */
+} mla_status;
+
+typedef struct mla_decode_s* mla_decode_t;
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int mla_decode_version(void);
+
+/* Human-readable name of a status code (static storage). */
+const char* mla_status_string(mla_status s);
+
+/*
+ * Create a handle.  Supported: num_heads 16, qk_dim 576, v_dim 512 (the
+ * shape of the amd-mixed-mla task, 727205 module constants), any finite
+ * sm_scale > 0 (the task uses 1/sqrt(576)), page_size a power of two in
+ * [1, 1024].  `device` is the HIP device ordinal the handle will run on; it
+ * is not touched until mla_decode_plan.  *out is set to NULL on failure.
+ */
+mla_status mla_decode_create(mla_decode_t* out, int device, int num_heads, int qk_dim, int v_dim,
+                             float sm_scale, mla_kv_dtype kv_dtype, int page_size);
+
+/*
+ * Plan a batch: splits every sequence into work items (token ranges, whole
+ * 64-token tiles except at a sequence's end) sized against the device's
+ * compute-unit count and the stage-1 kernel's residency, uploads the
+ * work list to the device (synchronously) and reports the workspace size the
+ * run needs (bytes; may be 0).  kv_indptr_host has batch+1 entries (tokens if
+ * page_size == 1, pages otherwise; non-decreasing, starting anywhere >= 0);
+ * kv_last_page_len_host has batch entries when page_size > 1 and is ignored
+ * (may be NULL) otherwise.  split_override > 0 forces that many items per
+ * non-empty sequence (at most one per 32 tokens); 0 lets the planner choose.
+ * The plan stays valid until the next plan or destroy; the device copies of
+ * kv_indptr / kv_last_page_len passed to run must hold the same values.
+ */
+mla_status mla_decode_plan(mla_decode_t h, int batch, const int32_t* kv_indptr_host,
+                           const int32_t* kv_last_page_len_host, int split_override,
+                           size_t* workspace_bytes);
+
+/*
+ * The planner alone, on the host, for inspection and testing (no handle, no
+ * GPU).  Same inputs as mla_decode_plan plus the device figures it would read
+ * (compute units, resident stage-1 workgroups per unit).  Writes up to
+ * max_items work items as int32 quadruples (sequence, first token, end token,
+ * partial slot or -1 when the item is the whole sequence) in launch order,
+ * and the number of items, partial slots and the workspace bytes.  Returns
+ * MLA_ERR_INVALID_ARG when max_items is too small (num_items still set).
+ */
+mla_status mla_decode_plan_preview(int batch, const int32_t* kv_indptr_host,
+                                   const int32_t* kv_last_page_len_host, int page_size,
+                                   int split_override, int num_cus, int blocks_per_cu,
+                                   int32_t* items_out, int max_items, int* num_items,
+                                   int* num_slots, size_t* workspace_bytes);
+
+/*
+ * Describe the current plan: number of work items (stage-1 workgroups), the
+ * largest number of items given to one sequence, and whether the merge kernel
+ * runs.  Any output pointer may be NULL.
+ */
+mla_status mla_decode_plan_info(mla_decode_t h, int* num_items, int* max_splits,
+                                int* merge_launched);
+
+/*
+ * Run the planned decode on `stream` (a hipStream_t; NULL = the default
+ * stream).  Asynchronous: no allocation, no host synchronisation.
+ *   q                 bf16 [batch, 16, 576], row-major, 16-byte aligned.
+ *   kv                cache rows (layout above), 16-byte aligned; may be NULL
+ *                     only when every planned sequence is empty.
+ *   kv_scales         FP8: float32[1] per-tensor scale.  MXFP4: uint8
+ *                     [rows, kv_scale_stride] e8m0 scales.  BF16: ignored.
+ *   kv_scale_stride   MXFP4 scale row stride in bytes (>= 18); else ignored.
+ *   kv_indptr         int32 [batch+1] (as planned).
+ *   kv_page_indices   int32 page ids (page_size > 1), else ignored.
+ *   kv_last_page_len  int32 [batch] (page_size > 1), else ignored.
+ *   out               bf16 [batch, 16, 512], row-major; every element written.
+ *   workspace         device scratch of >= the planned size (16-byte aligned;
+ *                     may be NULL when the planned size is 0).  Its contents
+ *                     need no initialisation and are garbage afterwards.
+ */
+mla_status mla_decode_run(mla_decode_t h, const void* q, const void* kv, const void* kv_scales,
+                          int64_t kv_scale_stride, const int32_t* kv_indptr,
+                          const int32_t* kv_page_indices, const int32_t* kv_last_page_len,
+                          void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Per-kernel timing for measurement.  While enabled, mla_decode_run records a
+ * HIP event before and after each of its kernels on the run's stream;
+ * mla_decode_kernel_time_ms then waits for the last run's events and returns
+ * the elapsed milliseconds of kernel `which` (0 = stage 1, 1 = merge; a
+ * kernel that was not launched reports 0).
+ */
+mla_status mla_decode_set_profiling(mla_decode_t h, int enable);
+mla_status mla_decode_kernel_time_ms(mla_decode_t h, int which, float* ms);
+
+/*
+ * Static resource usage of the stage-1 kernel for this handle's format and of
+ * the merge kernel (which = 0 / 1): registers per lane (arch VGPRs +
+ * accumulation VGPRs), LDS bytes, scratch (spill) bytes per lane.
+ */
+mla_status mla_decode_kernel_resources(mla_decode_t h, int which, int* vgprs, int* lds_bytes,
+                                       int* scratch_bytes);
+
+/* Destroy a handle (NULL is accepted and ignored). */
+mla_status mla_decode_destroy(mla_decode_t h);
+
+/* Detail of the last failure on this handle (empty string if none). */
+const char* mla_decode_last_error(mla_decode_t h);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H */

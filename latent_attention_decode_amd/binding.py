@@ -1,0 +1,253 @@
+"""Thin ctypes binding of libmla_decode.so (see include/mla_decode.h).
+
+Functions carry the C names and only marshal arguments: torch tensors become
+device pointers, the current torch stream becomes the hipStream_t.  Every step
+of the decode runs in the library's HIP kernels; there is no fallback, and
+importing this module raises if the library has not been built.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_decode.so")
+
+MLA_KV_BF16, MLA_KV_FP8_E4M3, MLA_KV_MXFP4 = 0, 1, 2
+KV_DTYPES = {"bf16": MLA_KV_BF16, "fp8": MLA_KV_FP8_E4M3, "mxfp4": MLA_KV_MXFP4}
+STATUS = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED",
+          3: "MLA_ERR_NOT_PLANNED", 4: "MLA_ERR_WORKSPACE_TOO_SMALL", 5: "MLA_ERR_HIP"}
+
+NUM_HEADS, QK_DIM, V_DIM = 16, 576, 512
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m latent_attention_decode_amd.build`"
+                      " (there is no fallback implementation)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_P = ctypes.c_void_p
+_I32P = ctypes.POINTER(ctypes.c_int32)
+_H = ctypes.c_void_p
+
+_lib.mla_decode_version.restype = ctypes.c_int
+_lib.mla_status_string.argtypes = [ctypes.c_int]
+_lib.mla_status_string.restype = ctypes.c_char_p
+_lib.mla_decode_create.argtypes = [ctypes.POINTER(_H), ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_int]
+_lib.mla_decode_plan.argtypes = [_H, ctypes.c_int, _P, _P, ctypes.c_int,
+                                 ctypes.POINTER(ctypes.c_size_t)]
+_lib.mla_decode_plan_preview.argtypes = [ctypes.c_int, _P, _P, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_int, _P, ctypes.c_int,
+                                         ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
+                                         ctypes.POINTER(ctypes.c_size_t)]
+_lib.mla_decode_plan_info.argtypes = [_H, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
+                                      ctypes.POINTER(ctypes.c_int)]
+_lib.mla_decode_run.argtypes = [_H, _P, _P, _P, ctypes.c_int64, _P, _P, _P, _P, _P,
+                                ctypes.c_size_t, _P]
+_lib.mla_decode_set_profiling.argtypes = [_H, ctypes.c_int]
+_lib.mla_decode_kernel_time_ms.argtypes = [_H, ctypes.c_int, ctypes.POINTER(ctypes.c_float)]
+_lib.mla_decode_kernel_resources.argtypes = [_H, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
+                                             ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
+_lib.mla_decode_destroy.argtypes = [_H]
+_lib.mla_decode_last_error.argtypes = [_H]
+_lib.mla_decode_last_error.restype = ctypes.c_char_p
+for _name in ("mla_decode_create", "mla_decode_plan", "mla_decode_plan_preview",
+              "mla_decode_plan_info", "mla_decode_run", "mla_decode_set_profiling",
+              "mla_decode_kernel_time_ms", "mla_decode_kernel_resources", "mla_decode_destroy"):
+    getattr(_lib, _name).restype = ctypes.c_int
+
+EXPORTED = ("mla_decode_version", "mla_status_string", "mla_decode_create", "mla_decode_plan",
+            "mla_decode_plan_preview", "mla_decode_plan_info", "mla_decode_run",
+            "mla_decode_set_profiling", "mla_decode_kernel_time_ms", "mla_decode_kernel_resources",
+            "mla_decode_destroy", "mla_decode_last_error")
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str = ""):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)}" + (f" ({detail})" if detail else ""))
+
+
+def _check(st: int, where: str, h=None):
+    if st != 0:
+        detail = _lib.mla_decode_last_error(h).decode() if h else ""
+        raise MlaError(st, where, detail)
+
+
+def _host_i32(a) -> np.ndarray:
+    if isinstance(a, torch.Tensor):
+        a = a.detach().cpu().numpy()
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _dptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("mla_decode_run takes device tensors")
+    if not t.is_contiguous():
+        raise ValueError("mla_decode_run takes contiguous tensors")
+    return t.data_ptr()
+
+
+def mla_decode_version() -> int:
+    return _lib.mla_decode_version()
+
+
+def mla_status_string(status: int) -> str:
+    return _lib.mla_status_string(int(status)).decode()
+
+
+def mla_decode_create(device: int, kv_dtype: str, page_size: int = 1, num_heads: int = NUM_HEADS,
+                      qk_dim: int = QK_DIM, v_dim: int = V_DIM, sm_scale: Optional[float] = None):
+    """Returns an opaque handle (int)."""
+    if sm_scale is None:
+        sm_scale = 1.0 / float(np.sqrt(qk_dim))
+    h = _H()
+    st = _lib.mla_decode_create(ctypes.byref(h), int(device), int(num_heads), int(qk_dim), int(v_dim),
+                                float(sm_scale), KV_DTYPES[kv_dtype] if isinstance(kv_dtype, str)
+                                else int(kv_dtype), int(page_size))
+    _check(st, "mla_decode_create")
+    return h.value
+
+
+def mla_decode_plan(h, kv_indptr_host, kv_last_page_len_host=None, split_override: int = 0) -> int:
+    """Plans the batch; returns the workspace size in bytes."""
+    ip = _host_i32(kv_indptr_host)
+    lp = None if kv_last_page_len_host is None else _host_i32(kv_last_page_len_host)
+    ws = ctypes.c_size_t()
+    st = _lib.mla_decode_plan(h, ip.size - 1, ip.ctypes.data, None if lp is None else lp.ctypes.data,
+                              int(split_override), ctypes.byref(ws))
+    _check(st, "mla_decode_plan", h)
+    return ws.value
+
+
+def mla_decode_plan_preview(kv_indptr_host, kv_last_page_len_host=None, page_size: int = 1,
+                            split_override: int = 0, num_cus: int = 256, blocks_per_cu: int = 2):
+    """Host-only planner.  Returns (items int32 [n, 4], num_slots, workspace_bytes)."""
+    ip = _host_i32(kv_indptr_host)
+    lp = None if kv_last_page_len_host is None else _host_i32(kv_last_page_len_host)
+    n = ctypes.c_int()
+    slots = ctypes.c_int()
+    ws = ctypes.c_size_t()
+    args = (ip.size - 1, ip.ctypes.data, None if lp is None else lp.ctypes.data, int(page_size),
+            int(split_override), int(num_cus), int(blocks_per_cu))
+    st = _lib.mla_decode_plan_preview(*args, None, 0, ctypes.byref(n), ctypes.byref(slots),
+                                      ctypes.byref(ws))
+    if st != 0 and n.value == 0:
+        _check(st, "mla_decode_plan_preview")
+    items = np.zeros((max(n.value, 1), 4), dtype=np.int32)
+    st = _lib.mla_decode_plan_preview(*args, items.ctypes.data, n.value, ctypes.byref(n),
+                                      ctypes.byref(slots), ctypes.byref(ws))
+    _check(st, "mla_decode_plan_preview")
+    return items[:n.value], slots.value, ws.value
+
+
+def mla_decode_plan_info(h):
+    n, ms, mg = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(_lib.mla_decode_plan_info(h, ctypes.byref(n), ctypes.byref(ms), ctypes.byref(mg)),
+           "mla_decode_plan_info", h)
+    return n.value, ms.value, bool(mg.value)
+
+
+def mla_decode_run(h, q: torch.Tensor, kv: torch.Tensor, kv_scales: Optional[torch.Tensor],
+                   kv_indptr: torch.Tensor, out: torch.Tensor,
+                   workspace: Optional[torch.Tensor] = None,
+                   kv_page_indices: Optional[torch.Tensor] = None,
+                   kv_last_page_len: Optional[torch.Tensor] = None,
+                   stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Launches the planned decode on `stream` (default: torch's current stream)."""
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    stride = int(kv_scales.shape[-1]) if (kv_scales is not None and kv_scales.dtype == torch.uint8) else 0
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _lib.mla_decode_run(h, _dptr(q), _dptr(kv), _dptr(kv_scales), stride, _dptr(kv_indptr),
+                             _dptr(kv_page_indices), _dptr(kv_last_page_len), _dptr(out),
+                             _dptr(workspace), ws_bytes, stream.cuda_stream)
+    _check(st, "mla_decode_run", h)
+
+
+def mla_decode_set_profiling(h, enable: bool) -> None:
+    _check(_lib.mla_decode_set_profiling(h, int(bool(enable))), "mla_decode_set_profiling", h)
+
+
+def mla_decode_kernel_time_ms(h, which: int) -> float:
+    ms = ctypes.c_float()
+    _check(_lib.mla_decode_kernel_time_ms(h, int(which), ctypes.byref(ms)), "mla_decode_kernel_time_ms", h)
+    return ms.value
+
+
+def mla_decode_kernel_resources(h, which: int):
+    v, l, s = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(_lib.mla_decode_kernel_resources(h, int(which), ctypes.byref(v), ctypes.byref(l),
+                                            ctypes.byref(s)), "mla_decode_kernel_resources", h)
+    return {"vgprs": v.value, "lds_bytes": l.value, "scratch_bytes": s.value}
+
+
+def mla_decode_destroy(h) -> None:
+    _check(_lib.mla_decode_destroy(h), "mla_decode_destroy")
+
+
+def mla_decode_last_error(h) -> str:
+    return _lib.mla_decode_last_error(h).decode()
+
+
+class MlaDecode:
+    """Convenience owner of one handle plus its workspace (torch-allocated)."""
+
+    def __init__(self, kv_dtype: str, page_size: int = 1, device: Optional[int] = None,
+                 sm_scale: Optional[float] = None):
+        self.device = torch.cuda.current_device() if device is None else int(device)
+        self.kv_dtype = kv_dtype
+        self.page_size = page_size
+        self.h = mla_decode_create(self.device, kv_dtype, page_size, sm_scale=sm_scale)
+        self.workspace: Optional[torch.Tensor] = None
+
+    def plan(self, kv_indptr_host, kv_last_page_len_host=None, split_override: int = 0) -> int:
+        nbytes = mla_decode_plan(self.h, kv_indptr_host, kv_last_page_len_host, split_override)
+        if nbytes and (self.workspace is None or self.workspace.numel() * 4 < nbytes):
+            self.workspace = torch.empty((nbytes + 3) // 4, dtype=torch.float32,
+                                         device=f"cuda:{self.device}")
+        return nbytes
+
+    def run(self, q, kv, kv_scales, kv_indptr, out, kv_page_indices=None, kv_last_page_len=None,
+            stream=None) -> torch.Tensor:
+        mla_decode_run(self.h, q, kv, kv_scales, kv_indptr, out, self.workspace, kv_page_indices,
+                       kv_last_page_len, stream)
+        return out
+
+    def close(self) -> None:
+        if self.h:
+            mla_decode_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def case_to_device(case, device="cuda") -> dict:
+    """Device tensors for a synthetic case (see synth.DecodeCase)."""
+    t = {
+        "q": torch.from_numpy(case.q_bits.view(np.int16)).view(torch.bfloat16).to(device),
+        "kv": torch.from_numpy(case.kv).to(device),
+        "kv_indptr": torch.from_numpy(case.kv_indptr.astype(np.int32)).to(device),
+        "kv_page_indices": None,
+        "kv_last_page_len": None,
+    }
+    if case.kv_dtype == "fp8":
+        t["kv_scales"] = torch.tensor([case.kv_scale], dtype=torch.float32, device=device)
+    elif case.kv_dtype == "mxfp4":
+        t["kv_scales"] = torch.from_numpy(case.kv_scales).to(device)
+    else:
+        t["kv_scales"] = None
+    if case.page_size > 1:
+        t["kv_page_indices"] = torch.from_numpy(case.kv_page_indices.astype(np.int32)).to(device)
+        t["kv_last_page_len"] = torch.from_numpy(case.kv_last_page_len.astype(np.int32)).to(device)
+    return t

@@ -1,0 +1,473 @@
+// Host side of libmla_decode.so: argument validation, the split planner and
+// the two kernel launches behind the C ABI of include/mla_decode.h.
+
+#include "mla_decode.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "mla_internal.h"
+
+struct mla_decode_s {
+  int device = 0;
+  int kv_dtype = 0;
+  int page_size = 1;
+  int page_shift = 0;
+  float sm_scale = 0.f;
+  std::string last_error;
+
+  // plan
+  bool planned = false;
+  int batch = 0;
+  int num_items = 0;
+  int num_slots = 0;
+  int max_splits = 0;
+  bool merge_needed = false;
+  size_t workspace_bytes = 0;
+  void* dev_plan = nullptr;  // [num_items] WorkItem then [batch] SeqInfo
+  size_t dev_plan_bytes = 0;
+  int num_cus = 0;
+  int blocks_per_cu = 0;
+
+  // measurement
+  bool profiling = false;
+  bool events_ready = false;
+  hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
+  bool merge_timed = false;
+};
+
+namespace {
+
+constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+
+mla_status fail(mla_decode_t h, mla_status st, const char* fmt, ...) {
+  if (h) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    h->last_error = buf;
+  }
+  return st;
+}
+
+// Restores the calling thread's current device on scope exit.
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = false;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) return;
+    if (prev != dev && hipSetDevice(dev) != hipSuccess) return;
+    ok = true;
+  }
+  ~DeviceGuard() {
+    if (ok && prev >= 0) (void)hipSetDevice(prev);
+  }
+};
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+size_t slot_bytes() {
+  return static_cast<size_t>(mla::kNumHeads) * (mla::kVDim + 1) * sizeof(float);
+}
+
+}  // namespace
+
+namespace mla {
+
+// Sequence lengths from the host page table (or token offsets).
+static bool seq_lengths(const int32_t* indptr, const int32_t* last, int batch, int page_size,
+                        std::vector<int64_t>* lens, std::string* err) {
+  lens->resize(batch);
+  if (indptr[0] < 0) {
+    *err = "kv_indptr[0] is negative";
+    return false;
+  }
+  for (int b = 0; b < batch; ++b) {
+    const int64_t n = static_cast<int64_t>(indptr[b + 1]) - indptr[b];
+    if (n < 0) {
+      *err = "kv_indptr is not non-decreasing at sequence " + std::to_string(b);
+      return false;
+    }
+    if (page_size == 1) {
+      (*lens)[b] = n;
+    } else if (n == 0) {
+      (*lens)[b] = 0;
+    } else {
+      const int lp = last[b];
+      if (lp < 1 || lp > page_size) {
+        *err = "kv_last_page_len[" + std::to_string(b) + "] outside [1, page_size]";
+        return false;
+      }
+      (*lens)[b] = (n - 1) * page_size + lp;
+    }
+    if ((*lens)[b] > INT32_MAX) {
+      *err = "sequence too long";
+      return false;
+    }
+  }
+  return true;
+}
+
+// The split planner.  Items are whole 64-token tiles (the last item of a
+// sequence may end mid-tile).  With C compute units holding W stage-1
+// workgroups each, the auto plan aims at C*W items of equal size for uniform
+// batches (one wave of workgroups, nothing idle) and four times as many for
+// ragged ones (the dispatcher then balances them as slots free up).  Longer
+// items are listed first so the last workgroups to start are short ones.
+struct PlanOut {
+  std::vector<WorkItem> items;
+  std::vector<SeqInfo> seqs;
+  int num_slots = 0;
+  int max_splits = 0;
+  bool merge_needed = false;
+};
+
+static int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+static void plan_items(const std::vector<int64_t>& lens, int split_override, int num_cus,
+                       int blocks_per_cu, PlanOut* out) {
+  const int batch = static_cast<int>(lens.size());
+  const int64_t tile = 2 * kTile;  // tokens per stage-1 iteration
+  int64_t total = 0, max_len = 0, nonempty = 0;
+  for (int64_t n : lens) {
+    total += n;
+    max_len = std::max(max_len, n);
+    nonempty += n > 0;
+  }
+  std::vector<int64_t> chunk(batch, 0);
+  if (split_override > 0) {
+    for (int b = 0; b < batch; ++b) {
+      if (!lens[b]) continue;
+      const int64_t ns = std::min<int64_t>(split_override, (lens[b] + kTile - 1) / kTile);
+      chunk[b] = round_up((lens[b] + ns - 1) / ns, kTile);
+    }
+  } else if (total > 0) {
+    const double mean = static_cast<double>(total) / static_cast<double>(nonempty);
+    const bool ragged = static_cast<double>(max_len) > 1.25 * mean;
+    const int64_t slots = static_cast<int64_t>(num_cus) * std::max(blocks_per_cu, 1);
+    const int64_t target = slots * (ragged ? 4 : 1);
+    const int64_t c = std::max<int64_t>(tile, round_up((total + target - 1) / target, tile));
+    for (int b = 0; b < batch; ++b) {
+      if (!lens[b]) continue;
+      // even out the pieces of this sequence
+      const int64_t ns = (lens[b] + c - 1) / c;
+      chunk[b] = round_up((lens[b] + ns - 1) / ns, tile);
+    }
+  }
+  out->items.clear();
+  out->seqs.assign(batch, SeqInfo{0, 0});
+  out->num_slots = 0;
+  out->max_splits = 0;
+  out->merge_needed = false;
+  for (int b = 0; b < batch; ++b) {
+    if (!lens[b]) {
+      out->seqs[b] = SeqInfo{0, 0};
+      out->merge_needed = true;  // the merge kernel writes the zeros
+      continue;
+    }
+    const int64_t ns = (lens[b] + chunk[b] - 1) / chunk[b];
+    out->max_splits = std::max<int>(out->max_splits, static_cast<int>(ns));
+    if (ns == 1) {
+      out->items.push_back(WorkItem{b, 0, static_cast<int32_t>(lens[b]), -1});
+      out->seqs[b] = SeqInfo{0, -1};
+      continue;
+    }
+    out->merge_needed = true;
+    out->seqs[b] = SeqInfo{out->num_slots, static_cast<int32_t>(ns)};
+    for (int64_t s = 0; s < ns; ++s) {
+      const int64_t t0 = s * chunk[b];
+      const int64_t t1 = std::min(lens[b], t0 + chunk[b]);
+      out->items.push_back(WorkItem{b, static_cast<int32_t>(t0), static_cast<int32_t>(t1),
+                                    out->num_slots + static_cast<int32_t>(s)});
+    }
+    out->num_slots += static_cast<int>(ns);
+  }
+  std::stable_sort(out->items.begin(), out->items.end(), [](const WorkItem& x, const WorkItem& y) {
+    return (x.tok_end - x.tok_begin) > (y.tok_end - y.tok_begin);
+  });
+}
+
+}  // namespace mla
+
+extern "C" {
+
+int mla_decode_version(void) { return kVersion; }
+
+const char* mla_status_string(mla_status s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
+    case MLA_ERR_NOT_PLANNED: return "MLA_ERR_NOT_PLANNED";
+    case MLA_ERR_WORKSPACE_TOO_SMALL: return "MLA_ERR_WORKSPACE_TOO_SMALL";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP";
+  }
+  return "MLA_ERR_UNKNOWN";
+}
+
+mla_status mla_decode_create(mla_decode_t* out, int device, int num_heads, int qk_dim, int v_dim,
+                             float sm_scale, mla_kv_dtype kv_dtype, int page_size) {
+  if (!out) return MLA_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (device < 0 || !(sm_scale > 0.f) || !std::isfinite(sm_scale) || page_size < 1)
+    return MLA_ERR_INVALID_ARG;
+  if (num_heads != mla::kNumHeads || qk_dim != mla::kQkDim || v_dim != mla::kVDim)
+    return MLA_ERR_UNSUPPORTED;
+  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3 && kv_dtype != MLA_KV_MXFP4)
+    return MLA_ERR_UNSUPPORTED;
+  if (!is_pow2(page_size) || page_size > 1024) return MLA_ERR_UNSUPPORTED;
+  mla_decode_t h = new (std::nothrow) mla_decode_s();
+  if (!h) return MLA_ERR_INVALID_ARG;
+  h->device = device;
+  h->kv_dtype = kv_dtype;
+  h->page_size = page_size;
+  while ((1 << h->page_shift) < page_size) ++h->page_shift;
+  h->sm_scale = sm_scale;
+  *out = h;
+  return MLA_OK;
+}
+
+mla_status mla_decode_plan(mla_decode_t h, int batch, const int32_t* kv_indptr_host,
+                           const int32_t* kv_last_page_len_host, int split_override,
+                           size_t* workspace_bytes) {
+  if (!h) return MLA_ERR_INVALID_ARG;
+  h->last_error.clear();
+  if (batch < 1) return fail(h, MLA_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", batch);
+  if (!kv_indptr_host) return fail(h, MLA_ERR_INVALID_ARG, "kv_indptr_host is NULL");
+  if (h->page_size > 1 && !kv_last_page_len_host)
+    return fail(h, MLA_ERR_INVALID_ARG, "kv_last_page_len_host is NULL with page_size > 1");
+  if (split_override < 0) return fail(h, MLA_ERR_INVALID_ARG, "split_override is negative");
+  if (!workspace_bytes) return fail(h, MLA_ERR_INVALID_ARG, "workspace_bytes is NULL");
+  std::vector<int64_t> lens;
+  std::string err;
+  if (!mla::seq_lengths(kv_indptr_host, kv_last_page_len_host, batch, h->page_size, &lens, &err))
+    return fail(h, MLA_ERR_INVALID_ARG, "%s", err.c_str());
+
+  h->planned = false;
+  DeviceGuard guard(h->device);
+  if (!guard.ok) return fail(h, MLA_ERR_HIP, "cannot select HIP device %d", h->device);
+  if (!h->num_cus) {
+    int cus = 0, bpc = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device) != hipSuccess ||
+        cus <= 0)
+      return fail(h, MLA_ERR_HIP, "cannot read the compute-unit count of device %d", h->device);
+    if (mla::stage1_occupancy(h->kv_dtype, h->page_size > 1, &bpc) != hipSuccess || bpc <= 0)
+      return fail(h, MLA_ERR_HIP, "cannot read the stage-1 occupancy");
+    h->num_cus = cus;
+    h->blocks_per_cu = bpc;
+  }
+
+  mla::PlanOut plan;
+  mla::plan_items(lens, split_override, h->num_cus, h->blocks_per_cu, &plan);
+
+  const size_t items_bytes = plan.items.size() * sizeof(mla::WorkItem);
+  const size_t need = items_bytes + plan.seqs.size() * sizeof(mla::SeqInfo);
+  if (need > h->dev_plan_bytes) {
+    if (h->dev_plan) (void)hipFree(h->dev_plan);
+    h->dev_plan = nullptr;
+    h->dev_plan_bytes = 0;
+    if (hipMalloc(&h->dev_plan, need) != hipSuccess)
+      return fail(h, MLA_ERR_HIP, "hipMalloc of %zu plan bytes failed", need);
+    h->dev_plan_bytes = need;
+  }
+  std::vector<unsigned char> blob(need);
+  if (items_bytes) std::memcpy(blob.data(), plan.items.data(), items_bytes);
+  std::memcpy(blob.data() + items_bytes, plan.seqs.data(), plan.seqs.size() * sizeof(mla::SeqInfo));
+  if (hipMemcpy(h->dev_plan, blob.data(), need, hipMemcpyHostToDevice) != hipSuccess)
+    return fail(h, MLA_ERR_HIP, "uploading the work list failed");
+
+  h->batch = batch;
+  h->num_items = static_cast<int>(plan.items.size());
+  h->num_slots = plan.num_slots;
+  h->max_splits = plan.max_splits;
+  h->merge_needed = plan.merge_needed;
+  h->workspace_bytes = static_cast<size_t>(plan.num_slots) * slot_bytes();
+  h->planned = true;
+  *workspace_bytes = h->workspace_bytes;
+  return MLA_OK;
+}
+
+mla_status mla_decode_plan_preview(int batch, const int32_t* kv_indptr_host,
+                                   const int32_t* kv_last_page_len_host, int page_size,
+                                   int split_override, int num_cus, int blocks_per_cu,
+                                   int32_t* items_out, int max_items, int* num_items,
+                                   int* num_slots, size_t* workspace_bytes) {
+  if (batch < 1 || !kv_indptr_host || page_size < 1 || !is_pow2(page_size) || split_override < 0 ||
+      num_cus < 1 || blocks_per_cu < 1 || max_items < 0 || (max_items > 0 && !items_out))
+    return MLA_ERR_INVALID_ARG;
+  if (page_size > 1 && !kv_last_page_len_host) return MLA_ERR_INVALID_ARG;
+  std::vector<int64_t> lens;
+  std::string err;
+  if (!mla::seq_lengths(kv_indptr_host, kv_last_page_len_host, batch, page_size, &lens, &err))
+    return MLA_ERR_INVALID_ARG;
+  mla::PlanOut plan;
+  mla::plan_items(lens, split_override, num_cus, blocks_per_cu, &plan);
+  const int n = static_cast<int>(plan.items.size());
+  if (num_items) *num_items = n;
+  if (num_slots) *num_slots = plan.num_slots;
+  if (workspace_bytes) *workspace_bytes = static_cast<size_t>(plan.num_slots) * slot_bytes();
+  if (n > max_items) return MLA_ERR_INVALID_ARG;
+  for (int i = 0; i < n; ++i) {
+    items_out[4 * i + 0] = plan.items[i].batch;
+    items_out[4 * i + 1] = plan.items[i].tok_begin;
+    items_out[4 * i + 2] = plan.items[i].tok_end;
+    items_out[4 * i + 3] = plan.items[i].slot;
+  }
+  return MLA_OK;
+}
+
+mla_status mla_decode_plan_info(mla_decode_t h, int* num_items, int* max_splits,
+                                int* merge_launched) {
+  if (!h) return MLA_ERR_INVALID_ARG;
+  if (!h->planned) return fail(h, MLA_ERR_NOT_PLANNED, "no plan");
+  if (num_items) *num_items = h->num_items;
+  if (max_splits) *max_splits = h->max_splits;
+  if (merge_launched) *merge_launched = h->merge_needed ? 1 : 0;
+  return MLA_OK;
+}
+
+mla_status mla_decode_run(mla_decode_t h, const void* q, const void* kv, const void* kv_scales,
+                          int64_t kv_scale_stride, const int32_t* kv_indptr,
+                          const int32_t* kv_page_indices, const int32_t* kv_last_page_len,
+                          void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!h) return MLA_ERR_INVALID_ARG;
+  h->last_error.clear();
+  if (!h->planned) return fail(h, MLA_ERR_NOT_PLANNED, "mla_decode_run before a successful plan");
+  // With every sequence empty nothing reads the cache, which may then be empty.
+  const bool reads_cache = h->num_items > 0;
+  if (!q || !kv_indptr || !out || (reads_cache && !kv))
+    return fail(h, MLA_ERR_INVALID_ARG, "null q/kv/kv_indptr/out");
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(kv)) & 15)
+    return fail(h, MLA_ERR_INVALID_ARG, "q and kv must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(out) & 7)
+    return fail(h, MLA_ERR_INVALID_ARG, "out must be 8-byte aligned");
+  if (reads_cache && h->kv_dtype != MLA_KV_BF16 && !kv_scales)
+    return fail(h, MLA_ERR_INVALID_ARG, "kv_scales is NULL for a scaled cache format");
+  if (h->kv_dtype == MLA_KV_MXFP4 && kv_scale_stride < 18)
+    return fail(h, MLA_ERR_INVALID_ARG, "MXFP4 kv_scale_stride must be >= 18 (got %lld)",
+                static_cast<long long>(kv_scale_stride));
+  if (h->page_size > 1 && (!kv_page_indices || !kv_last_page_len))
+    return fail(h, MLA_ERR_INVALID_ARG, "page table arrays are NULL with page_size > 1");
+  if (workspace_bytes < h->workspace_bytes)
+    return fail(h, MLA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, plan needs %zu",
+                workspace_bytes, h->workspace_bytes);
+  if (h->workspace_bytes && (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 15)))
+    return fail(h, MLA_ERR_INVALID_ARG, "workspace is NULL or not 16-byte aligned");
+
+  DeviceGuard guard(h->device);
+  if (!guard.ok) return fail(h, MLA_ERR_HIP, "cannot select HIP device %d", h->device);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  mla::Stage1Args a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.kv = static_cast<const uint8_t*>(kv);
+  a.kv_mx_scales = h->kv_dtype == MLA_KV_MXFP4 ? static_cast<const uint8_t*>(kv_scales) : nullptr;
+  a.kv_scale = h->kv_dtype == MLA_KV_FP8_E4M3 ? static_cast<const float*>(kv_scales) : nullptr;
+  a.scale_stride = kv_scale_stride;
+  a.kv_indptr = kv_indptr;
+  a.page_indices = kv_page_indices;
+  a.page_shift = h->page_shift;
+  a.items = static_cast<const mla::WorkItem*>(h->dev_plan);
+  a.part_o = static_cast<float*>(workspace);
+  a.part_lse = h->num_slots
+                   ? reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) +
+                                              static_cast<size_t>(h->num_slots) * mla::kNumHeads *
+                                                  mla::kVDim * sizeof(float))
+                   : nullptr;
+  a.out = static_cast<uint16_t*>(out);
+  a.score_scale = h->sm_scale * 1.4426950408889634f;
+
+  const bool timed = h->profiling && h->events_ready;
+  if (timed && hipEventRecord(h->ev[0], s) != hipSuccess)
+    return fail(h, MLA_ERR_HIP, "hipEventRecord failed");
+  if (h->num_items > 0) {
+    const hipError_t e = mla::launch_stage1(h->kv_dtype, h->page_size > 1, a, h->num_items, s);
+    if (e != hipSuccess) return fail(h, MLA_ERR_HIP, "stage-1 launch: %s", hipGetErrorString(e));
+  }
+  if (timed && hipEventRecord(h->ev[1], s) != hipSuccess)
+    return fail(h, MLA_ERR_HIP, "hipEventRecord failed");
+  h->merge_timed = false;
+  if (h->merge_needed) {
+    mla::MergeArgs m{};
+    m.seqs = reinterpret_cast<const mla::SeqInfo*>(static_cast<const unsigned char*>(h->dev_plan) +
+                                                   h->num_items * sizeof(mla::WorkItem));
+    m.part_o = a.part_o;
+    m.part_lse = a.part_lse;
+    m.out = a.out;
+    if (timed && hipEventRecord(h->ev[2], s) != hipSuccess)
+      return fail(h, MLA_ERR_HIP, "hipEventRecord failed");
+    const hipError_t e = mla::launch_merge(m, h->batch, s);
+    if (e != hipSuccess) return fail(h, MLA_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
+    if (timed && hipEventRecord(h->ev[3], s) != hipSuccess)
+      return fail(h, MLA_ERR_HIP, "hipEventRecord failed");
+    h->merge_timed = timed;
+  }
+  return MLA_OK;
+}
+
+mla_status mla_decode_set_profiling(mla_decode_t h, int enable) {
+  if (!h) return MLA_ERR_INVALID_ARG;
+  if (enable && !h->events_ready) {
+    DeviceGuard guard(h->device);
+    if (!guard.ok) return fail(h, MLA_ERR_HIP, "cannot select HIP device %d", h->device);
+    for (auto& e : h->ev)
+      if (hipEventCreate(&e) != hipSuccess) return fail(h, MLA_ERR_HIP, "hipEventCreate failed");
+    h->events_ready = true;
+  }
+  h->profiling = enable != 0;
+  return MLA_OK;
+}
+
+mla_status mla_decode_kernel_time_ms(mla_decode_t h, int which, float* ms) {
+  if (!h || !ms || (which != 0 && which != 1)) return MLA_ERR_INVALID_ARG;
+  if (!h->events_ready) return fail(h, MLA_ERR_NOT_PLANNED, "profiling was never enabled");
+  *ms = 0.f;
+  if (which == 1 && !h->merge_timed) return MLA_OK;
+  hipEvent_t e0 = h->ev[which == 0 ? 0 : 2], e1 = h->ev[which == 0 ? 1 : 3];
+  if (hipEventSynchronize(e1) != hipSuccess || hipEventElapsedTime(ms, e0, e1) != hipSuccess)
+    return fail(h, MLA_ERR_HIP, "reading the kernel events failed");
+  return MLA_OK;
+}
+
+mla_status mla_decode_kernel_resources(mla_decode_t h, int which, int* vgprs, int* lds_bytes,
+                                       int* scratch_bytes) {
+  if (!h || (which != 0 && which != 1)) return MLA_ERR_INVALID_ARG;
+  DeviceGuard guard(h->device);
+  if (!guard.ok) return fail(h, MLA_ERR_HIP, "cannot select HIP device %d", h->device);
+  hipFuncAttributes attr{};
+  if (mla::kernel_attributes(h->kv_dtype, h->page_size > 1, which, &attr) != hipSuccess)
+    return fail(h, MLA_ERR_HIP, "hipFuncGetAttributes failed");
+  if (vgprs) *vgprs = attr.numRegs;
+  if (lds_bytes) *lds_bytes = static_cast<int>(attr.sharedSizeBytes);
+  if (scratch_bytes) *scratch_bytes = static_cast<int>(attr.localSizeBytes);
+  return MLA_OK;
+}
+
+mla_status mla_decode_destroy(mla_decode_t h) {
+  if (!h) return MLA_OK;
+  {
+    DeviceGuard guard(h->device);
+    if (h->dev_plan) (void)hipFree(h->dev_plan);
+    for (auto& e : h->ev)
+      if (e) (void)hipEventDestroy(e);
+  }
+  delete h;
+  return MLA_OK;
+}
+
+const char* mla_decode_last_error(mla_decode_t h) {
+  if (!h) return "null handle";
+  return h->last_error.c_str();
+}
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// Internal interface between the host library (mla_decode.cpp) and the HIP
+// kernels (mla_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace mla {
+
+constexpr int kNumHeads = 16;
+constexpr int kQkDim = 576;
+constexpr int kVDim = 512;
+constexpr int kTile = 32;        // tokens one wave consumes per main-loop iteration
+constexpr int kWaves = 4;        // waves per stage-1 workgroup
+constexpr int kStage1Threads = 64 * kWaves;
+constexpr int kMergeThreads = kVDim / 4;  // one float4 of one head per thread
+
+enum KvFormat : int { kBf16 = 0, kFp8 = 1, kMxfp4 = 2 };
+
+// One stage-1 workgroup's job: tokens [tok_begin, tok_end) of sequence
+// `batch` (logical token indices within the sequence).  slot >= 0: write the
+// normalised partial (O, lse) to partial slot `slot`; slot < 0: the item is
+// the whole sequence, write the bf16 output directly.
+struct WorkItem {
+  int32_t batch;
+  int32_t tok_begin;
+  int32_t tok_end;
+  int32_t slot;
+};
+
+// Per sequence, for the merge kernel: partial slots [slot_begin, slot_begin +
+// nslots).  nslots == 0: empty sequence (write zeros); nslots < 0: stage 1
+// wrote the output; nslots >= 2: merge.
+struct SeqInfo {
+  int32_t slot_begin;
+  int32_t nslots;
+};
+
+struct Stage1Args {
+  const uint16_t* q;            // bf16 [batch, 16, 576]
+  const uint8_t* kv;            // cache rows
+  const uint8_t* kv_mx_scales;  // MXFP4 e8m0 [rows, stride]
+  const float* kv_scale;        // FP8 per-tensor scale (device scalar)
+  int64_t scale_stride;
+  const int32_t* kv_indptr;
+  const int32_t* page_indices;
+  int page_shift;               // log2(page_size); 0 = contiguous
+  const WorkItem* items;
+  float* part_o;                // [slots, 16, 512]
+  float* part_lse;              // [slots, 16], log2 domain
+  uint16_t* out;                // bf16 [batch, 16, 512]
+  float score_scale;            // sm_scale * log2(e)
+};
+
+struct MergeArgs {
+  const SeqInfo* seqs;
+  const float* part_o;
+  const float* part_lse;
+  uint16_t* out;
+};
+
+// Launchers (mla_kernels.hip).  Return the launch status.
+hipError_t launch_stage1(int fmt, bool paged, const Stage1Args& a, int num_items, hipStream_t s);
+hipError_t launch_merge(const MergeArgs& a, int batch, hipStream_t s);
+// Static resources of a kernel (which: 0 stage 1 for `fmt`/`paged`, 1 merge).
+hipError_t kernel_attributes(int fmt, bool paged, int which, hipFuncAttributes* attr);
+// Resident stage-1 workgroups per compute unit.
+hipError_t stage1_occupancy(int fmt, bool paged, int* blocks_per_cu);
+
+}  // namespace mla

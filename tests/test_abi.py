@@ -1,0 +1,159 @@
+"""C-ABI library: exported symbols, host-side validation and the planner (CPU only)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_decode.h")
+
+
+@pytest.fixture(scope="module")
+def B():
+    from latent_attention_decode_amd import binding
+    return binding
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_symbols_are_exported(B):
+    names = _declared_functions()
+    assert "mla_decode_run" in names and "mla_decode_plan" in names
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(B.EXPORTED) == names
+
+
+def test_version_and_status_strings(B):
+    assert B.mla_decode_version() >= 10000
+    for code, name in B.STATUS.items():
+        assert B.mla_status_string(code) == name
+
+
+def test_create_validates_arguments(B):
+    with pytest.raises(B.MlaError) as e:
+        B.mla_decode_create(0, "fp8", num_heads=8)
+    assert e.value.status == 2
+    with pytest.raises(B.MlaError) as e:
+        B.mla_decode_create(0, "fp8", page_size=3)
+    assert e.value.status == 2
+    with pytest.raises(B.MlaError) as e:
+        B.mla_decode_create(0, "fp8", sm_scale=-1.0)
+    assert e.value.status == 1
+    with pytest.raises(B.MlaError) as e:
+        B.mla_decode_create(-1, "fp8")
+    assert e.value.status == 1
+    with pytest.raises(B.MlaError):
+        B.mla_decode_create(0, 7)
+    h = B.mla_decode_create(0, "fp8")  # touches no GPU
+    B.mla_decode_destroy(h)
+    B.mla_decode_destroy(None)
+
+
+def test_plan_and_run_validate_before_any_gpu_call(B):
+    h = B.mla_decode_create(0, "fp8", page_size=2)
+    try:
+        with pytest.raises(B.MlaError) as e:  # decreasing indptr
+            B.mla_decode_plan(h, [0, 5, 3], [1, 1])
+        assert e.value.status == 1 and "non-decreasing" in str(e.value)
+        with pytest.raises(B.MlaError) as e:  # last page length outside [1, page_size]
+            B.mla_decode_plan(h, [0, 2, 3], [3, 1])
+        assert e.value.status == 1
+        with pytest.raises(B.MlaError) as e:  # missing last_page_len for a paged cache
+            B.mla_decode_plan(h, [0, 2, 3], None)
+        assert e.value.status == 1
+        with pytest.raises(B.MlaError) as e:
+            B.mla_decode_plan(h, [0], [])  # batch 0
+        assert e.value.status == 1
+        # run before a successful plan: raw call with dummy pointers
+        st = B._lib.mla_decode_run(h, 16, 16, 16, 0, 16, 16, 16, 16, None, 0, None)
+        assert st == 3
+        with pytest.raises(B.MlaError) as e:
+            B.mla_decode_plan_info(h)
+        assert e.value.status == 3
+    finally:
+        B.mla_decode_destroy(h)
+
+
+def _check_cover(items, lens, slots):
+    """Every token of every sequence is in exactly one item; slots are a partition."""
+    seen = {b: np.zeros(n, dtype=np.int32) for b, n in enumerate(lens)}
+    used_slots = []
+    for b, t0, t1, s in items:
+        assert 0 <= t0 < t1 <= lens[b]
+        seen[b][t0:t1] += 1
+        if s >= 0:
+            used_slots.append(s)
+    for b, n in enumerate(lens):
+        assert np.all(seen[b] == 1), b
+    assert sorted(used_slots) == list(range(slots))
+    # a sequence with a single item writes its output directly
+    per_seq = {}
+    for b, t0, t1, s in items:
+        per_seq.setdefault(b, []).append(s)
+    for b, ss in per_seq.items():
+        assert (ss == [-1]) if len(ss) == 1 else all(x >= 0 for x in ss)
+        if len(ss) > 1:  # a sequence's slots are consecutive
+            assert sorted(ss) == list(range(min(ss), min(ss) + len(ss)))
+
+
+@pytest.mark.parametrize("lens", [
+    [1024] * 4, [1024] * 64, [8192] * 4, [8192] * 32, [8192] * 64, [1] * 3, [0, 5, 0, 700],
+    [63, 64, 65, 127, 128, 129], list(range(1, 300, 7)),
+])
+def test_planner_covers_every_token_once(B, lens):
+    indptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    items, slots, ws = B.mla_decode_plan_preview(indptr, num_cus=256, blocks_per_cu=2)
+    _check_cover(items.tolist(), lens, slots)
+    assert ws == slots * 16 * 513 * 4
+    # items are listed longest first
+    sizes = items[:, 2] - items[:, 1]
+    assert np.all(np.diff(sizes) <= 0)
+
+
+def test_planner_paged_lengths(B):
+    ps = 4
+    lens = [9, 4, 1, 0, 16]
+    pages = [(n + ps - 1) // ps for n in lens]
+    indptr = np.concatenate([[0], np.cumsum(pages)]).astype(np.int32)
+    last = [n - ps * (p - 1) if p else 0 for n, p in zip(lens, pages)]
+    items, slots, _ = B.mla_decode_plan_preview(indptr, last, page_size=ps)
+    _check_cover(items.tolist(), lens, slots)
+
+
+def test_planner_fills_the_gpu_for_uniform_batches(B):
+    # 256 CUs x 2 resident workgroups: uniform batches become one wave of equal items
+    for bs, n in [(32, 8192), (64, 8192), (64, 1024), (4, 8192)]:
+        indptr = np.arange(bs + 1, dtype=np.int32) * n
+        items, slots, _ = B.mla_decode_plan_preview(indptr, num_cus=256, blocks_per_cu=2)
+        sizes = items[:, 2] - items[:, 1]
+        assert len(items) <= 512 and len(set(sizes.tolist())) == 1, (bs, n)
+        assert len(items) >= min(512, bs * n // 64) // 2
+
+
+def test_planner_split_override(B):
+    indptr = np.array([0, 1000, 1033, 1034], dtype=np.int32)
+    items, slots, _ = B.mla_decode_plan_preview(indptr, split_override=4)
+    counts = np.bincount(items[:, 0], minlength=3)
+    assert counts.tolist() == [4, 2, 1]  # at most one split per 32 tokens
+    _check_cover(items.tolist(), [1000, 33, 1], slots)
+
+
+def test_planner_ragged_gets_more_items(B):
+    from latent_attention_decode_amd import synth
+    lens = synth.config_lens("bs256_ragged1024-8192_fp8_paged2")
+    pages = (lens + 1) // 2
+    indptr = np.concatenate([[0], np.cumsum(pages)]).astype(np.int32)
+    last = (lens - 2 * (pages - 1)).astype(np.int32)
+    items, slots, _ = B.mla_decode_plan_preview(indptr, last, page_size=2, num_cus=256,
+                                                blocks_per_cu=2)
+    assert len(items) > 2 * 512
+    _check_cover(items.tolist(), lens.tolist(), slots)

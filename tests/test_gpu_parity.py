@@ -1,0 +1,185 @@
+"""GPU parity: the HIP path against the fp64 oracle, through the C ABI.
+
+Tolerances (fixed here, from the task): bf16 cache -> max |gpu - oracle| <= 1e-2;
+fp8 / MXFP4 cache -> |gpu - oracle| <= 0.1 + 0.1 |oracle| for every element.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from latent_attention_decode_amd import synth
+from conftest import gpu_available
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+TOL = {"bf16": (1e-2, 0.0), "fp8": (0.1, 0.1), "mxfp4": (0.1, 0.1)}
+
+
+@pytest.fixture(scope="module")
+def B():
+    from latent_attention_decode_amd import binding
+    return binding
+
+
+def note(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def run_gpu(B, case, split_override=0, repeats=1):
+    t = B.case_to_device(case)
+    dec = B.MlaDecode(case.kv_dtype, case.page_size)
+    try:
+        dec.plan(case.kv_indptr, case.kv_last_page_len, split_override)
+        outs = []
+        for _ in range(repeats):
+            out = torch.full((case.batch, 16, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
+            dec.run(t["q"], t["kv"], t["kv_scales"], t["kv_indptr"], out, t["kv_page_indices"],
+                    t["kv_last_page_len"])
+            torch.cuda.synchronize()
+            outs.append(out.float().cpu().numpy().astype(np.float64))
+        return outs if repeats > 1 else outs[0]
+    finally:
+        dec.close()
+
+
+def check_close(got, ref, fmt, what=""):
+    atol, rtol = TOL[fmt]
+    err = np.abs(got - ref)
+    bound = atol + rtol * np.abs(ref)
+    bad = ~(err <= bound)  # NaN counts as bad
+    stats = (f"{what} max|err|={np.nanmax(err):.3e} p99={np.nanpercentile(err, 99):.3e} "
+             f"mean={np.nanmean(err):.3e}")
+    note(stats)
+    assert not bad.any(), f"{bad.sum()} elements outside tolerance; {stats}"
+
+
+def oracle_out(oracle_mod, case, batches=None):
+    out, _ = oracle_mod.decode_case(case, batches=batches)
+    return out
+
+
+SMALL = [
+    # fmt, lens, page_size, shuffled
+    ("fp8", [1, 63, 64, 65, 200, 1000], 1, False),
+    ("bf16", [1, 63, 64, 65, 200, 1000], 1, False),
+    ("mxfp4", [1, 63, 64, 65, 200, 1000], 1, False),
+    ("fp8", [5, 130, 777, 2], 2, True),
+    ("bf16", [33, 300, 64], 4, True),
+    ("mxfp4", [31, 129, 500], 2, True),
+    ("fp8", [3000, 17], 8, True),
+]
+
+
+@pytest.mark.parametrize("split", [0, 1, 3])
+@pytest.mark.parametrize("fmt,lens,ps,shuffled", SMALL)
+def test_small_parity(B, oracle_mod, fmt, lens, ps, shuffled, split):
+    note(f"case fmt={fmt} lens={lens} ps={ps} split={split}")
+    case = synth.make_case(fmt, lens, seed=100 + sum(lens) + ps, page_size=ps,
+                           shuffle_pages=shuffled, guard_rows=2)
+    got = run_gpu(B, case, split)
+    ref = oracle_out(oracle_mod, case)
+    check_close(got, ref, fmt, f"{fmt} {lens} ps{ps} split{split}")
+
+
+@pytest.mark.parametrize("fmt", synth.FORMATS)
+def test_single_token_cache_returns_value_row(B, oracle_mod, fmt):
+    case = synth.make_case(fmt, [1, 1, 1, 1], seed=21)
+    got = run_gpu(B, case)
+    rows = oracle_mod.dequant_rows(fmt, case.kv, np.arange(4), kv_scale=case.kv_scale,
+                                   kv_scales=case.kv_scales)
+    ref = np.broadcast_to(rows[:, None, :512], (4, 16, 512))
+    if fmt == "bf16":
+        assert np.array_equal(got, ref)  # weight exactly 1: bit-exact
+    else:
+        check_close(got, ref, fmt, "one token")
+
+
+@pytest.mark.parametrize("fmt", synth.FORMATS)
+def test_zero_query_gives_mean(B, oracle_mod, fmt):
+    lens = [300, 65]
+    case = synth.make_case(fmt, lens, seed=22, q_values=np.zeros((2, 16, 576), np.float32))
+    got = run_gpu(B, case)
+    check_close(got, oracle_out(oracle_mod, case), fmt, "q=0")
+
+
+@pytest.mark.parametrize("fmt", synth.FORMATS)
+def test_constant_values(B, oracle_mod, fmt):
+    lens = [500, 70]
+    rng = np.random.default_rng(23)
+    kv = rng.standard_normal((sum(lens), 576)).astype(np.float32)
+    kv[:, :512] = 1.0
+    case = synth.make_case(fmt, lens, seed=23, kv_values=kv)
+    got = run_gpu(B, case)
+    ref = oracle_out(oracle_mod, case)
+    check_close(got, ref, fmt, "V=1")
+    assert np.abs(got - ref).max() <= 1e-2
+
+
+def test_empty_sequences_give_zero(B, oracle_mod):
+    case = synth.make_case("fp8", [0, 100, 0, 1], seed=24)
+    got = run_gpu(B, case)
+    assert np.all(got[0] == 0) and np.all(got[2] == 0)
+    check_close(got, oracle_out(oracle_mod, case), "fp8", "empty")
+    case = synth.make_case("bf16", [0, 0], seed=25)
+    assert np.all(run_gpu(B, case) == 0)
+
+
+@pytest.mark.parametrize("fmt", synth.FORMATS)
+def test_deterministic(B, fmt):
+    case = synth.make_case(fmt, [2000, 64, 5], seed=26)
+    a, b = run_gpu(B, case, repeats=2)
+    assert np.array_equal(a, b)
+
+
+def test_page_table_permutation_and_size_invariance(B):
+    lens = [700, 129, 64, 3]
+    base = run_gpu(B, synth.make_case("fp8", lens, seed=27))
+    for ps in (2, 8):
+        got = run_gpu(B, synth.make_case("fp8", lens, seed=27, page_size=ps, shuffle_pages=True,
+                                         guard_rows=5))
+        assert np.array_equal(got, base), ps
+
+
+def test_split_count_changes_only_rounding(B, oracle_mod):
+    case = synth.make_case("fp8", [4096, 1500], seed=28)
+    ref = oracle_out(oracle_mod, case)
+    outs = [run_gpu(B, case, s) for s in (1, 2, 7, 40)]
+    for o in outs:
+        check_close(o, ref, "fp8", "splits")
+        assert np.abs(o - outs[0]).max() < 2e-2
+
+
+def test_workspace_too_small_is_rejected(B):
+    case = synth.make_case("fp8", [4096], seed=29)
+    t = B.case_to_device(case)
+    dec = B.MlaDecode("fp8")
+    try:
+        ws = dec.plan(case.kv_indptr, None, 4)
+        assert ws > 0
+        small = torch.empty(ws // 4 - 1, dtype=torch.float32, device="cuda")
+        out = torch.empty((1, 16, 512), dtype=torch.bfloat16, device="cuda")
+        with pytest.raises(B.MlaError) as e:
+            B.mla_decode_run(dec.h, t["q"], t["kv"], t["kv_scales"], t["kv_indptr"], out, small)
+        assert e.value.status == 4
+    finally:
+        dec.close()
+
+
+# Full-size workloads: every output of a few sampled sequences against the oracle.
+FULL = list(synth.CONFIGS)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_configs(B, oracle_mod, name):
+    note(f"config {name}")
+    case = synth.config_case(name)
+    got = run_gpu(B, case)
+    assert np.all(np.isfinite(got))
+    rng = np.random.default_rng(30)
+    sample = sorted(rng.choice(case.batch, size=min(case.batch, 4), replace=False).tolist())
+    ref = oracle_out(oracle_mod, case, batches=sample)
+    check_close(got[sample], ref[sample], case.kv_dtype, name)
