@@ -34,10 +34,18 @@
  * token j lives in row page*page_size + j%page_size.  A sequence of length 0
  * produces a zero output.
  *
+ * Execution.  Two kernel launches per call: each workgroup of the first
+ * streams one token range ("work item") of one sequence with an online
+ * softmax and writes either the output (the item is the whole sequence) or a
+ * normalised partial and its log-sum-exp; the second merges the partials of
+ * every split sequence by their log-sum-exp weights (727205 `mla_rd`, 700955
+ * `reduce_lse_v71`, 599694 `_flash_fp8_split_s2`).  It is not launched when
+ * no sequence is split.
+ *
  * Ownership.  The caller owns every tensor, the workspace and the stream.  A
  * handle owns only its plan (a small device work list, allocated by
- * mla_decode_plan and freed by mla_decode_destroy).  All pointers passed to
- * mla_decode_run are device pointers unless the name ends in _host.
+ * mla_decode_plan and freed by mla_decode_destroy).  All pointers passed to mla_decode_run are device
+ * pointers unless the name ends in _host.
  *
  * Errors.  Every call validates its arguments on the host before touching the
  * GPU and returns a status; nothing is launched when a call fails, no
@@ -112,7 +120,8 @@ mla_status mla_decode_plan(mla_decode_t h, int batch, const int32_t* kv_indptr_h
  * GPU).  Same inputs as mla_decode_plan plus the device figures it would read
  * (compute units, resident stage-1 workgroups per unit).  Writes up to
  * max_items work items as int32 quadruples (sequence, first token, end token,
- * partial slot or -1 when the item is the whole sequence) in launch order,
+ * partial slot, or -1 when the item is the whole sequence, or -2 for the item
+ * that writes an empty sequence's zero output) in launch order,
  * and the number of items, partial slots and the workspace bytes.  Returns
  * MLA_ERR_INVALID_ARG when max_items is too small (num_items still set).
  */
@@ -123,12 +132,12 @@ mla_status mla_decode_plan_preview(int batch, const int32_t* kv_indptr_host,
                                    int* num_slots, size_t* workspace_bytes);
 
 /*
- * Describe the current plan: number of work items (stage-1 workgroups), the
- * largest number of items given to one sequence, and whether the merge kernel
- * runs.  Any output pointer may be NULL.
+ * Describe the current plan: number of work items (workgroups launched), the
+ * largest number of items given to one sequence, and the number of partials
+ * written to the workspace.  Any output pointer may be NULL.
  */
 mla_status mla_decode_plan_info(mla_decode_t h, int* num_items, int* max_splits,
-                                int* merge_launched);
+                                int* num_partials);
 
 /*
  * Run the planned decode on `stream` (a hipStream_t; NULL = the default
@@ -153,19 +162,20 @@ mla_status mla_decode_run(mla_decode_t h, const void* q, const void* kv, const v
                           void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Per-kernel timing for measurement.  While enabled, mla_decode_run records a
- * HIP event before and after each of its kernels on the run's stream;
+ * Kernel timing for measurement.  While enabled, mla_decode_run records a HIP
+ * event before and after each of its kernel launches on the run's stream;
  * mla_decode_kernel_time_ms then waits for the last run's events and returns
- * the elapsed milliseconds of kernel `which` (0 = stage 1, 1 = merge; a
- * kernel that was not launched reports 0).
+ * the elapsed milliseconds of kernel `which` (0 = split stage, 1 = merge; a
+ * merge that was not launched reports 0).  MLA_ERR_NOT_PLANNED if the last
+ * run was not timed.
  */
 mla_status mla_decode_set_profiling(mla_decode_t h, int enable);
 mla_status mla_decode_kernel_time_ms(mla_decode_t h, int which, float* ms);
 
 /*
- * Static resource usage of the stage-1 kernel for this handle's format and of
- * the merge kernel (which = 0 / 1): registers per lane (arch VGPRs +
- * accumulation VGPRs), LDS bytes, scratch (spill) bytes per lane.
+ * Static resource usage of kernel `which` (0 = split stage for this handle's
+ * format and layout, 1 = merge): registers per lane, LDS bytes per
+ * workgroup, scratch (spill) bytes per lane.  Any output pointer may be NULL.
  */
 mla_status mla_decode_kernel_resources(mla_decode_t h, int which, int* vgprs, int* lds_bytes,
                                        int* scratch_bytes);

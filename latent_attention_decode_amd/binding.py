@@ -148,10 +148,11 @@ def mla_decode_plan_preview(kv_indptr_host, kv_last_page_len_host=None, page_siz
 
 
 def mla_decode_plan_info(h):
-    n, ms, mg = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
-    _check(_lib.mla_decode_plan_info(h, ctypes.byref(n), ctypes.byref(ms), ctypes.byref(mg)),
+    """Returns (num_items, max_splits, num_partials)."""
+    n, ms, npart = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(_lib.mla_decode_plan_info(h, ctypes.byref(n), ctypes.byref(ms), ctypes.byref(npart)),
            "mla_decode_plan_info", h)
-    return n.value, ms.value, bool(mg.value)
+    return n.value, ms.value, npart.value
 
 
 def mla_decode_run(h, q: torch.Tensor, kv: torch.Tensor, kv_scales: Optional[torch.Tensor],
@@ -175,13 +176,15 @@ def mla_decode_set_profiling(h, enable: bool) -> None:
     _check(_lib.mla_decode_set_profiling(h, int(bool(enable))), "mla_decode_set_profiling", h)
 
 
-def mla_decode_kernel_time_ms(h, which: int) -> float:
+def mla_decode_kernel_time_ms(h, which: int = 0) -> float:
+    """Elapsed ms of kernel `which` (0 split stage, 1 merge) in the last timed run."""
     ms = ctypes.c_float()
-    _check(_lib.mla_decode_kernel_time_ms(h, int(which), ctypes.byref(ms)), "mla_decode_kernel_time_ms", h)
+    _check(_lib.mla_decode_kernel_time_ms(h, int(which), ctypes.byref(ms)),
+           "mla_decode_kernel_time_ms", h)
     return ms.value
 
 
-def mla_decode_kernel_resources(h, which: int):
+def mla_decode_kernel_resources(h, which: int = 0):
     v, l, s = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
     _check(_lib.mla_decode_kernel_resources(h, int(which), ctypes.byref(v), ctypes.byref(l),
                                             ctypes.byref(s)), "mla_decode_kernel_resources", h)

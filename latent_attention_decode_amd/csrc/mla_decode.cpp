@@ -30,9 +30,11 @@ struct mla_decode_s {
   int num_items = 0;
   int num_slots = 0;
   int max_splits = 0;
-  bool merge_needed = false;
+  int64_t total_tokens = 0;
   size_t workspace_bytes = 0;
-  void* dev_plan = nullptr;  // [num_items] WorkItem then [batch] SeqInfo
+  int num_merge = 0;  // sequences with >= 2 partials
+  // device: [num_items] WorkItem, [batch] SeqInfo, [num_merge] int32 sequence ids
+  void* dev_plan = nullptr;
   size_t dev_plan_bytes = 0;
   int num_cus = 0;
   int blocks_per_cu = 0;
@@ -40,8 +42,9 @@ struct mla_decode_s {
   // measurement
   bool profiling = false;
   bool events_ready = false;
-  hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
+  bool timed_run = false;
   bool merge_timed = false;
+  hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
 };
 
 namespace {
@@ -119,23 +122,30 @@ static bool seq_lengths(const int32_t* indptr, const int32_t* last, int batch, i
 }
 
 // The split planner.  Items are whole 64-token tiles (the last item of a
-// sequence may end mid-tile).  With C compute units holding W stage-1
-// workgroups each, the auto plan aims at C*W items of equal size for uniform
-// batches (one wave of workgroups, nothing idle) and four times as many for
-// ragged ones (the dispatcher then balances them as slots free up).  Longer
-// items are listed first so the last workgroups to start are short ones.
+// sequence may end mid-tile).  With C compute units holding W workgroups
+// each, the auto plan aims at C*W items of equal size for uniform batches (one
+// wave of workgroups, nothing idle) and four times as many for ragged ones
+// (the dispatcher then balances them as slots free up).  Longer items are
+// listed first so the last workgroups to start are short ones; empty
+// sequences get an item of their own that writes the zero output.
 struct PlanOut {
   std::vector<WorkItem> items;
   std::vector<SeqInfo> seqs;
+  std::vector<int32_t> merge_seqs;
   int num_slots = 0;
   int max_splits = 0;
-  bool merge_needed = false;
 };
 
 static int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
+// An item of fewer than two tiles has no load/compute overlap; each (sequence,
+// head) is merged by one workgroup, so the number of partials stays small.
+constexpr int64_t kMinItemTokens = 4 * kTile;
+constexpr int64_t kMaxAutoSplits = 32;
+constexpr int64_t kMaxItemPages = 512;  // LDS staging of one item's page ids (mla_kernels.hip)
+
 static void plan_items(const std::vector<int64_t>& lens, int split_override, int num_cus,
-                       int blocks_per_cu, PlanOut* out) {
+                       int blocks_per_cu, int page_size, PlanOut* out) {
   const int batch = static_cast<int>(lens.size());
   const int64_t tile = 2 * kTile;  // tokens per stage-1 iteration
   int64_t total = 0, max_len = 0, nonempty = 0;
@@ -144,6 +154,9 @@ static void plan_items(const std::vector<int64_t>& lens, int split_override, int
     max_len = std::max(max_len, n);
     nonempty += n > 0;
   }
+  // A paged item's page ids are staged in LDS: at most kMaxItemPages of them.
+  const int64_t max_item =
+      page_size > 1 ? (kMaxItemPages - 2) * static_cast<int64_t>(page_size) / tile * tile : INT64_MAX;
   std::vector<int64_t> chunk(batch, 0);
   if (split_override > 0) {
     for (int b = 0; b < batch; ++b) {
@@ -156,34 +169,35 @@ static void plan_items(const std::vector<int64_t>& lens, int split_override, int
     const bool ragged = static_cast<double>(max_len) > 1.25 * mean;
     const int64_t slots = static_cast<int64_t>(num_cus) * std::max(blocks_per_cu, 1);
     const int64_t target = slots * (ragged ? 4 : 1);
-    const int64_t c = std::max<int64_t>(tile, round_up((total + target - 1) / target, tile));
+    const int64_t c = std::max<int64_t>(kMinItemTokens,
+                                        round_up((total + target - 1) / target, tile));
     for (int b = 0; b < batch; ++b) {
       if (!lens[b]) continue;
+      // bound the partials one merge workgroup reads
+      const int64_t ns = std::min<int64_t>((lens[b] + c - 1) / c, kMaxAutoSplits);
       // even out the pieces of this sequence
-      const int64_t ns = (lens[b] + c - 1) / c;
       chunk[b] = round_up((lens[b] + ns - 1) / ns, tile);
     }
   }
   out->items.clear();
+  out->merge_seqs.clear();
   out->seqs.assign(batch, SeqInfo{0, 0});
   out->num_slots = 0;
   out->max_splits = 0;
-  out->merge_needed = false;
   for (int b = 0; b < batch; ++b) {
     if (!lens[b]) {
-      out->seqs[b] = SeqInfo{0, 0};
-      out->merge_needed = true;  // the merge kernel writes the zeros
+      out->items.push_back(WorkItem{b, 0, 0, WorkItem::kEmpty});
       continue;
     }
+    if (chunk[b] > max_item) chunk[b] = max_item;
     const int64_t ns = (lens[b] + chunk[b] - 1) / chunk[b];
     out->max_splits = std::max<int>(out->max_splits, static_cast<int>(ns));
     if (ns == 1) {
-      out->items.push_back(WorkItem{b, 0, static_cast<int32_t>(lens[b]), -1});
-      out->seqs[b] = SeqInfo{0, -1};
+      out->items.push_back(WorkItem{b, 0, static_cast<int32_t>(lens[b]), WorkItem::kWhole});
       continue;
     }
-    out->merge_needed = true;
     out->seqs[b] = SeqInfo{out->num_slots, static_cast<int32_t>(ns)};
+    out->merge_seqs.push_back(b);
     for (int64_t s = 0; s < ns; ++s) {
       const int64_t t0 = s * chunk[b];
       const int64_t t1 = std::min(lens[b], t0 + chunk[b]);
@@ -268,10 +282,12 @@ mla_status mla_decode_plan(mla_decode_t h, int batch, const int32_t* kv_indptr_h
   }
 
   mla::PlanOut plan;
-  mla::plan_items(lens, split_override, h->num_cus, h->blocks_per_cu, &plan);
+  mla::plan_items(lens, split_override, h->num_cus, h->blocks_per_cu, h->page_size, &plan);
 
   const size_t items_bytes = plan.items.size() * sizeof(mla::WorkItem);
-  const size_t need = items_bytes + plan.seqs.size() * sizeof(mla::SeqInfo);
+  const size_t seqs_bytes = plan.seqs.size() * sizeof(mla::SeqInfo);
+  const size_t merge_bytes = plan.merge_seqs.size() * sizeof(int32_t);
+  const size_t need = items_bytes + seqs_bytes + merge_bytes;
   if (need > h->dev_plan_bytes) {
     if (h->dev_plan) (void)hipFree(h->dev_plan);
     h->dev_plan = nullptr;
@@ -280,9 +296,11 @@ mla_status mla_decode_plan(mla_decode_t h, int batch, const int32_t* kv_indptr_h
       return fail(h, MLA_ERR_HIP, "hipMalloc of %zu plan bytes failed", need);
     h->dev_plan_bytes = need;
   }
-  std::vector<unsigned char> blob(need);
+  std::vector<unsigned char> blob(need, 0);
   if (items_bytes) std::memcpy(blob.data(), plan.items.data(), items_bytes);
-  std::memcpy(blob.data() + items_bytes, plan.seqs.data(), plan.seqs.size() * sizeof(mla::SeqInfo));
+  std::memcpy(blob.data() + items_bytes, plan.seqs.data(), seqs_bytes);
+  if (merge_bytes)
+    std::memcpy(blob.data() + items_bytes + seqs_bytes, plan.merge_seqs.data(), merge_bytes);
   if (hipMemcpy(h->dev_plan, blob.data(), need, hipMemcpyHostToDevice) != hipSuccess)
     return fail(h, MLA_ERR_HIP, "uploading the work list failed");
 
@@ -290,7 +308,9 @@ mla_status mla_decode_plan(mla_decode_t h, int batch, const int32_t* kv_indptr_h
   h->num_items = static_cast<int>(plan.items.size());
   h->num_slots = plan.num_slots;
   h->max_splits = plan.max_splits;
-  h->merge_needed = plan.merge_needed;
+  h->num_merge = static_cast<int>(plan.merge_seqs.size());
+  h->total_tokens = 0;
+  for (int64_t n : lens) h->total_tokens += n;
   h->workspace_bytes = static_cast<size_t>(plan.num_slots) * slot_bytes();
   h->planned = true;
   *workspace_bytes = h->workspace_bytes;
@@ -311,7 +331,7 @@ mla_status mla_decode_plan_preview(int batch, const int32_t* kv_indptr_host,
   if (!mla::seq_lengths(kv_indptr_host, kv_last_page_len_host, batch, page_size, &lens, &err))
     return MLA_ERR_INVALID_ARG;
   mla::PlanOut plan;
-  mla::plan_items(lens, split_override, num_cus, blocks_per_cu, &plan);
+  mla::plan_items(lens, split_override, num_cus, blocks_per_cu, page_size, &plan);
   const int n = static_cast<int>(plan.items.size());
   if (num_items) *num_items = n;
   if (num_slots) *num_slots = plan.num_slots;
@@ -327,12 +347,12 @@ mla_status mla_decode_plan_preview(int batch, const int32_t* kv_indptr_host,
 }
 
 mla_status mla_decode_plan_info(mla_decode_t h, int* num_items, int* max_splits,
-                                int* merge_launched) {
+                                int* num_partials) {
   if (!h) return MLA_ERR_INVALID_ARG;
   if (!h->planned) return fail(h, MLA_ERR_NOT_PLANNED, "no plan");
   if (num_items) *num_items = h->num_items;
   if (max_splits) *max_splits = h->max_splits;
-  if (merge_launched) *merge_launched = h->merge_needed ? 1 : 0;
+  if (num_partials) *num_partials = h->num_slots;
   return MLA_OK;
 }
 
@@ -344,7 +364,7 @@ mla_status mla_decode_run(mla_decode_t h, const void* q, const void* kv, const v
   h->last_error.clear();
   if (!h->planned) return fail(h, MLA_ERR_NOT_PLANNED, "mla_decode_run before a successful plan");
   // With every sequence empty nothing reads the cache, which may then be empty.
-  const bool reads_cache = h->num_items > 0;
+  const bool reads_cache = h->total_tokens > 0;
   if (!q || !kv_indptr || !out || (reads_cache && !kv))
     return fail(h, MLA_ERR_INVALID_ARG, "null q/kv/kv_indptr/out");
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(kv)) & 15)
@@ -377,7 +397,10 @@ mla_status mla_decode_run(mla_decode_t h, const void* q, const void* kv, const v
   a.kv_indptr = kv_indptr;
   a.page_indices = kv_page_indices;
   a.page_shift = h->page_shift;
-  a.items = static_cast<const mla::WorkItem*>(h->dev_plan);
+  unsigned char* plan_base = static_cast<unsigned char*>(h->dev_plan);
+  const size_t items_bytes = static_cast<size_t>(h->num_items) * sizeof(mla::WorkItem);
+  const size_t seqs_bytes = static_cast<size_t>(h->batch) * sizeof(mla::SeqInfo);
+  a.items = reinterpret_cast<const mla::WorkItem*>(plan_base);
   a.part_o = static_cast<float*>(workspace);
   a.part_lse = h->num_slots
                    ? reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) +
@@ -388,30 +411,30 @@ mla_status mla_decode_run(mla_decode_t h, const void* q, const void* kv, const v
   a.score_scale = h->sm_scale * 1.4426950408889634f;
 
   const bool timed = h->profiling && h->events_ready;
+  h->timed_run = false;
+  h->merge_timed = false;
   if (timed && hipEventRecord(h->ev[0], s) != hipSuccess)
     return fail(h, MLA_ERR_HIP, "hipEventRecord failed");
-  if (h->num_items > 0) {
-    const hipError_t e = mla::launch_stage1(h->kv_dtype, h->page_size > 1, a, h->num_items, s);
-    if (e != hipSuccess) return fail(h, MLA_ERR_HIP, "stage-1 launch: %s", hipGetErrorString(e));
-  }
+  hipError_t e = mla::launch_stage1(h->kv_dtype, h->page_size > 1, a, h->num_items, s);
+  if (e != hipSuccess) return fail(h, MLA_ERR_HIP, "stage-1 launch: %s", hipGetErrorString(e));
   if (timed && hipEventRecord(h->ev[1], s) != hipSuccess)
     return fail(h, MLA_ERR_HIP, "hipEventRecord failed");
-  h->merge_timed = false;
-  if (h->merge_needed) {
+  if (h->num_merge > 0) {
     mla::MergeArgs m{};
-    m.seqs = reinterpret_cast<const mla::SeqInfo*>(static_cast<const unsigned char*>(h->dev_plan) +
-                                                   h->num_items * sizeof(mla::WorkItem));
+    m.seqs = reinterpret_cast<const mla::SeqInfo*>(plan_base + items_bytes);
+    m.merge_seqs = reinterpret_cast<const int32_t*>(plan_base + items_bytes + seqs_bytes);
     m.part_o = a.part_o;
     m.part_lse = a.part_lse;
     m.out = a.out;
     if (timed && hipEventRecord(h->ev[2], s) != hipSuccess)
       return fail(h, MLA_ERR_HIP, "hipEventRecord failed");
-    const hipError_t e = mla::launch_merge(m, h->batch, s);
+    e = mla::launch_merge(m, h->num_merge, s);
     if (e != hipSuccess) return fail(h, MLA_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
     if (timed && hipEventRecord(h->ev[3], s) != hipSuccess)
       return fail(h, MLA_ERR_HIP, "hipEventRecord failed");
     h->merge_timed = timed;
   }
+  h->timed_run = timed;
   return MLA_OK;
 }
 
@@ -430,7 +453,7 @@ mla_status mla_decode_set_profiling(mla_decode_t h, int enable) {
 
 mla_status mla_decode_kernel_time_ms(mla_decode_t h, int which, float* ms) {
   if (!h || !ms || (which != 0 && which != 1)) return MLA_ERR_INVALID_ARG;
-  if (!h->events_ready) return fail(h, MLA_ERR_NOT_PLANNED, "profiling was never enabled");
+  if (!h->timed_run) return fail(h, MLA_ERR_NOT_PLANNED, "the last run was not timed");
   *ms = 0.f;
   if (which == 1 && !h->merge_timed) return MLA_OK;
   hipEvent_t e0 = h->ev[which == 0 ? 0 : 2], e1 = h->ev[which == 0 ? 1 : 3];

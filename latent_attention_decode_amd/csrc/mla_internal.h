@@ -21,18 +21,19 @@ enum KvFormat : int { kBf16 = 0, kFp8 = 1, kMxfp4 = 2 };
 
 // One stage-1 workgroup's job: tokens [tok_begin, tok_end) of sequence
 // `batch` (logical token indices within the sequence).  slot >= 0: write the
-// normalised partial (O, lse) to partial slot `slot`; slot < 0: the item is
-// the whole sequence, write the bf16 output directly.
+// normalised partial (O, lse) to partial slot `slot`; kWhole: the item is the
+// whole sequence, write the bf16 output directly; kEmpty (with tok_begin ==
+// tok_end): the sequence is empty, write zeros.
 struct WorkItem {
   int32_t batch;
   int32_t tok_begin;
   int32_t tok_end;
   int32_t slot;
+  static constexpr int32_t kWhole = -1;
+  static constexpr int32_t kEmpty = -2;
 };
 
-// Per sequence, for the merge kernel: partial slots [slot_begin, slot_begin +
-// nslots).  nslots == 0: empty sequence (write zeros); nslots < 0: stage 1
-// wrote the output; nslots >= 2: merge.
+// Per sequence: its partial slots are [slot_begin, slot_begin + nslots).
 struct SeqInfo {
   int32_t slot_begin;
   int32_t nslots;
@@ -55,7 +56,8 @@ struct Stage1Args {
 };
 
 struct MergeArgs {
-  const SeqInfo* seqs;
+  const int32_t* merge_seqs;    // the sequences with >= 2 partials
+  const SeqInfo* seqs;          // [batch]
   const float* part_o;
   const float* part_lse;
   uint16_t* out;
@@ -63,7 +65,7 @@ struct MergeArgs {
 
 // Launchers (mla_kernels.hip).  Return the launch status.
 hipError_t launch_stage1(int fmt, bool paged, const Stage1Args& a, int num_items, hipStream_t s);
-hipError_t launch_merge(const MergeArgs& a, int batch, hipStream_t s);
+hipError_t launch_merge(const MergeArgs& a, int num_merge_seqs, hipStream_t s);
 // Static resources of a kernel (which: 0 stage 1 for `fmt`/`paged`, 1 merge).
 hipError_t kernel_attributes(int fmt, bool paged, int which, hipFuncAttributes* attr);
 // Resident stage-1 workgroups per compute unit.

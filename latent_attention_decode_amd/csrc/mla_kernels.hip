@@ -1,14 +1,15 @@
 // HIP kernels (gfx950) for single-token multi-head latent attention decode.
 //
-// Stage 1 (mla_stage1): one 256-thread workgroup per planned work item, i.e. a
-// token range of one sequence, streamed in 64-token tiles with an online
-// softmax (flash-decoding, as in the split-K kernels of amd-mixed-mla
-// submissions 727205 "v25: LEAN" `mla_s1` and 599694 "overhead elimination"
-// `_flash_fp8_split_s1`).  The workgroup writes the normalised partial plus its
-// log-sum-exp or, when the item is the whole sequence, the bf16 output.
-// Stage 2 (mla_merge): per (sequence, head), the log-sum-exp weighted merge of
-// the partials (727205 `mla_rd`; 700955 "locked baseline dispatch"
-// `reduce_lse_v71`; 599694 `_flash_fp8_split_s2`).
+// mla_stage1: one 256-thread workgroup per planned work item, i.e. a token
+// range of one sequence, streamed in 64-token tiles with an online softmax
+// (flash-decoding, as in the split-K kernels of amd-mixed-mla submissions
+// 727205 "v25: LEAN" `mla_s1` and 599694 "overhead elimination"
+// `_flash_fp8_split_s1`).  A workgroup whose item is the whole sequence
+// writes the bf16 output; otherwise it writes a normalised partial plus its
+// log-sum-exp.  An empty sequence's item writes zeros.
+// mla_merge: per (sequence, head) of the split sequences, the log-sum-exp
+// weighted merge of the partials (727205 `mla_rd`; 700955 "locked baseline
+// dispatch" `reduce_lse_v71`; 599694 `_flash_fp8_split_s2`).
 //
 // Per 64-token tile:
 //   1. every thread loads 16-byte chunks of the tile's cache rows into
@@ -46,6 +47,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -63,8 +65,8 @@ template <> struct Traits<kFp8> {
   static constexpr int kRowBytes = 576;  // stored row
   static constexpr int kLdsPitch = 592;  // LDS row pitch (fp8 codes + 16 B)
   static constexpr bool kLdsFp8 = true;
-  static constexpr int kBuffers = 2;     // LDS tile buffers (double-buffered)
-  static constexpr bool kPrefetch = true;  // next tile's loads in flight during compute
+  static constexpr int kBuffers = 1;     // unused: fp8 runs mla_stage1_fp8
+  static constexpr bool kPrefetch = false;
 };
 template <> struct Traits<kBf16> {
   static constexpr int kRowBytes = 1152;
@@ -249,26 +251,252 @@ struct TileRegs {
 };
 
 // ---------------------------------------------------------------------------
+// workgroup barrier that orders LDS only
+// ---------------------------------------------------------------------------
+// s_waitcnt immediates (gfx9 encoding): vmcnt in bits 3:0 and 15:14, expcnt in
+// 6:4, lgkmcnt in 11:8.  Waiting on lgkmcnt(0) alone leaves the cache-to-LDS
+// loads of later tiles in flight across the barrier.
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 0xF) | (0x7 << 4) | ((lgkm & 0xF) << 8) | (((vm >> 4) & 0x3) << 14);
+}
+constexpr int kWaitLgkm0 = waitcnt_imm(63, 0);
+
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // this wave's LDS reads/writes are done
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Wait until at most n of this wave's vector-memory loads are outstanding.
+// (Vector loads complete in issue order.)
+__device__ __forceinline__ void wait_vm(int n) {
+  if (n == 19)
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(19, 15));
+  else
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+  asm volatile("" ::: "memory");
+}
+
+// ---------------------------------------------------------------------------
+// fp8: per-wave 32-token tiles straight from HBM into LDS
+// ---------------------------------------------------------------------------
+// Each wave owns two LDS tile buffers and streams its own tiles (wave w takes
+// tiles w, w+4, ... of the item) with no workgroup barrier in the main loop.
+// A wave tile holds 32 rows with the padded layout of Tile::row_offset (row r
+// at 592r + 64(r/16)): a run of 16-byte slots, row r starting at slot
+// 37r + 4(r/16), 36 data slots per row, the rest padding.  One cache-to-LDS
+// load (global_load_lds_dwordx4) writes 64 consecutive slots, lane l to slot
+// base + l, so each lane fetches whichever 16-byte chunk belongs in its slot
+// and lanes on padding slots sit the load out.
+constexpr int kWTile = 32;                             // tokens per wave tile
+constexpr int kWTileBytes = kWTile * 592 + 64;         // rows 16..31 shifted by 64 B
+constexpr int kWTileSlots = kWTileBytes / 16;          // 1188
+constexpr int kWTileLoads = (kWTileSlots + 63) / 64;   // 19 loads per wave tile
+constexpr int kMaxItemPages = 512;                     // page ids of one item staged in LDS
+static_assert(kWTileLoads == 19, "fp8 wave-tile load count");
+
+__host__ __device__ constexpr int wrow_offset(int r) { return r * 592 + (r >> 4) * 64; }
+
+// One cache-to-LDS load: lane l's 16 bytes at `src` go to LDS lds_base + 16l.
+// Written as inline assembly so that the compiler does not guard later LDS
+// reads with a wait for every such load in flight; each wave waits for its
+// own tile explicitly (wait_vm) before reading it.
+__device__ __forceinline__ void dma16(const void* src, const uint8_t* lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)lds_base);
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(src), "s"(m0)
+      : "memory", "m0");
+}
+
+template <bool PAGED>
+struct WaveDma {
+  int rc[kWTileLoads];  // (tile row << 8) | 16-byte chunk of this lane's slot; -1 on padding
+
+  __device__ __forceinline__ void init(int lane) {
+#pragma unroll
+    for (int k = 0; k < kWTileLoads; ++k) {
+      const int slot = 64 * k + lane;
+      const int grp = slot / (16 * 37 + 4);  // group of 16 rows
+      const int rem = slot - grp * (16 * 37 + 4);
+      const int rr = rem / 37;
+      const int cc = rem - 37 * rr;
+      const bool data = slot < kWTileSlots && rr < 16 && cc < 36;
+      rc[k] = data ? ((16 * grp + rr) << 8) | cc : -1;
+    }
+  }
+
+  // Issue the loads of the wave tile whose first token is tok0.  Rows past
+  // tok_last fetch row tok_last (finite data, masked later by index).
+  __device__ __forceinline__ void issue(const Stage1Args& a, const uint8_t* buf, int64_t seq_base,
+                                        const int32_t* pages, int page0, int tok0, int tok_last,
+                                        int lane) const {
+    uint32_t my_row = 0;  // physical row of tile row (lane & 31)
+    if (PAGED) {
+      const int tok = min(tok0 + (lane & 31), tok_last);
+      const uint32_t page = (uint32_t)pages[(tok >> a.page_shift) - page0];
+      my_row = (page << a.page_shift) + (uint32_t)(tok & ((1 << a.page_shift) - 1));
+    }
+    const bool full = tok0 + kWTile - 1 <= tok_last;
+    const uint8_t* tile_base = a.kv + (seq_base + tok0) * 576;
+#pragma unroll
+    for (int k = 0; k < kWTileLoads; ++k) {
+      const int r = rc[k] >> 8;
+      const int c16 = (rc[k] & 0xFF) * 16;
+      const uint8_t* src;
+      if (PAGED) {
+        const uint32_t pr = (uint32_t)__shfl((int)my_row, r & 31, 64);
+        src = a.kv + (int64_t)pr * 576 + c16;
+      } else if (full) {
+        src = tile_base + (r * 576 + c16);
+      } else {
+        src = a.kv + (seq_base + min(tok0 + r, tok_last)) * 576 + c16;
+      }
+      if (rc[k] >= 0) dma16(src, buf + 1024 * k);
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
 // stage 1
 // ---------------------------------------------------------------------------
-// LDS: tile buffer(s), the bf16 P^T fragments of the four waves, and the
-// per-wave tile maxima.
+// LDS: the tile buffers, and apart from them (a separate object, so that the
+// compiler sees these accesses cannot alias the cache-to-LDS loads in flight)
+// the bf16 P^T fragments of the four waves, the per-wave tile maxima and sums,
+// and (paged fp8) the page ids of the item.
 template <int F>
-struct Stage1Lds {
+struct Stage1Tiles {
   uint8_t tile[Traits<F>::kBuffers][Tile<F>::kBytes];
-  uint2 p[kWaves][64];           // 4 bf16 probabilities per lane
-  float tmax[kWaves][kNumHeads];
+};
+template <int F, bool PAGED>
+struct Stage1Lds {
+  uint2 p[kWaves][64];               // 4 bf16 probabilities per lane
+  f32x4 tmax[kWaves][kNumHeads];     // [wave][head][lane group] tile maxima
   float lsum[kWaves][kNumHeads];
 };
 
+// One 64-token tile held in `cur`: scores, shared lazy max, P.V.  Ends after
+// the P.V reads were issued; the caller orders what follows.
+template <int F, bool PAGED>
+__device__ __forceinline__ void attend_tile(Stage1Lds<F, PAGED>& sh, const uint8_t* cur, const bf16x8 (&qf)[18],
+                                            f32x4 (&o)[8], float& m_ref, float& l_part,
+                                            int tok0, int tok_last, float xscale, int wave,
+                                            int lane, int k_off, int v_off_lo, int v_off_hi) {
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  // ---- scores S^T for tokens 16*wave .. +15 of the tile ----
+  // four independent accumulation chains over the 18 k-steps
+  f32x4 sacc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) sacc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  {
+    const uint8_t* kr = cur + k_off;
+#pragma unroll
+    for (int j = 0; j < 9; ++j) {
+      bf16x8 kl, kh;
+      if constexpr (Traits<F>::kLdsFp8) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(kr + 64 * j);
+        kl = fp8x8_to_bf16(w[0], w[1]);
+        kh = fp8x8_to_bf16(w[2], w[3]);
+      } else {
+        const bf16x8* p = reinterpret_cast<const bf16x8*>(kr + 128 * j);
+        kl = p[0];
+        kh = p[1];
+      }
+      const int c = 2 * (j & 1);
+      sacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl, qf[2 * j], sacc[c], 0, 0, 0);
+      sacc[c + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qf[2 * j + 1], sacc[c + 1], 0, 0, 0);
+    }
+  }
+  float x[4];
+  float tmax = kNegInf;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = ((sacc[0][i] + sacc[1][i]) + (sacc[2][i] + sacc[3][i])) * xscale;
+    if (tok0 + 16 * wave + 4 * g + i > tok_last) x[i] = kNegInf;
+    tmax = fmaxf(tmax, x[i]);
+  }
+  reinterpret_cast<float*>(&sh.tmax[wave][r16])[g] = tmax;
+  float p[4];
+  {
+    const float mr = (m_ref == kNegInf) ? 0.0f : m_ref;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - mr);
+    sh.p[wave][lane] = uint2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+  }
+  lds_barrier();  // scores, maxima and P of all waves are in LDS
+
+  // ---- lazy rescale: only when a tile max passes m_ref + 8 ----
+  float tile_max = kNegInf;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const f32x4 t = sh.tmax[w][r16];
+    tile_max = fmaxf(tile_max, fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])));
+  }
+  if (__ballot(tile_max > m_ref + kLazyRescale) != 0) {  // same outcome in every wave
+    const float m_new = fmaxf(m_ref, tile_max);
+    const float alpha = (m_new == kNegInf) ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
+#pragma unroll
+    for (int v = 0; v < 8; ++v) o[v] *= alpha;
+    l_part *= alpha;
+    m_ref = m_new;
+    const float mr = (m_ref == kNegInf) ? 0.0f : m_ref;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - mr);
+    lds_barrier();  // everyone has read the old P
+    sh.p[wave][lane] = uint2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+    lds_barrier();
+  }
+  l_part += (p[0] + p[1]) + (p[2] + p[3]);
+
+  // ---- O^T[dims of this wave] += V^T P^T over the 64 tokens ----
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const uint2 p_lo = sh.p[2 * kk][lane];
+    const uint2 p_hi = sh.p[2 * kk + 1][lane];
+    const bf16x8 pt = __builtin_bit_cast(bf16x8, u32x4{p_lo.x, p_lo.y, p_hi.x, p_hi.y});
+    const uint8_t* vb = cur + kk * Tile<F>::row_offset(32);
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      bf16x8 va;
+      if constexpr (Traits<F>::kLdsFp8) {
+        const i32x2 raw =
+            __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vb + v_off_lo + 16 * v));
+        va = fp8x8_to_bf16((uint32_t)raw[0], (uint32_t)raw[1]);
+      } else {
+        const i16x4 lo =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + v_off_lo + 32 * v));
+        const i16x4 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + v_off_hi + 32 * v));
+        const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo);
+        const bf16x4 h4 = __builtin_bit_cast(bf16x4, hi);
+        va = bf16x8{l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
+      }
+      o[v] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pt, o[v], 0, 0, 0);
+    }
+  }
+}
+
 template <int F, bool PAGED>
 __global__ __launch_bounds__(kStage1Threads, 2) void mla_stage1(Stage1Args a) {
-  __shared__ __attribute__((aligned(16))) Stage1Lds<F> sh;
-  constexpr int NB = Traits<F>::kBuffers;
+  __shared__ __attribute__((aligned(16))) Stage1Tiles<F> tiles;
+  __shared__ __attribute__((aligned(16))) Stage1Lds<F, PAGED> sh;
 
   const WorkItem item = a.items[blockIdx.x];
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  if (item.slot == WorkItem::kEmpty) {  // empty sequence: its output is zero
+    uint4* dst = reinterpret_cast<uint4*>(a.out + (int64_t)item.batch * kNumHeads * kVDim);
+#pragma unroll
+    for (int k = 0; k < (kNumHeads * kVDim * 2 / 16) / kStage1Threads; ++k)
+      dst[tid + kStage1Threads * k] = uint4{0u, 0u, 0u, 0u};
+    return;
+  }
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int lane = tid & 63;
   const int r16 = lane & 15;  // MFMA row/column index of this lane
   const int g = lane >> 4;    // MFMA k-group of this lane
@@ -320,116 +548,22 @@ __global__ __launch_bounds__(kStage1Threads, 2) void mla_stage1(Stage1Args a) {
     v_off_hi = Tile<F>::row_offset(pv_token(g, 4 + (r16 >> 2))) + (r16 & 3) * 8 + 2 * dv0;
   }
 
-  TileRegs<F, PAGED> regs;
-  regs.issue(a, seq_base, item.tok_begin, tok_last, tid);
-  regs.store(sh.tile[0], tid);
-  if (Traits<F>::kPrefetch && ntiles > 1)
-    regs.issue(a, seq_base, item.tok_begin + kTileTokens, tok_last, tid);
-  __syncthreads();
-
-  for (int n = 0; n < ntiles; ++n) {
-    const int tok0 = item.tok_begin + n * kTileTokens;
-    const uint8_t* cur = sh.tile[NB == 2 ? (n & 1) : 0];
-
-    // ---- scores S^T for tokens 16*wave .. +15 of the tile ----
-    f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = sa;
-    {
-      const uint8_t* kr = cur + k_off;
-#pragma unroll
-      for (int j = 0; j < 9; ++j) {
-        bf16x8 kl, kh;
-        if constexpr (Traits<F>::kLdsFp8) {
-          const u32x4 w = *reinterpret_cast<const u32x4*>(kr + 64 * j);
-          kl = fp8x8_to_bf16(w[0], w[1]);
-          kh = fp8x8_to_bf16(w[2], w[3]);
-        } else {
-          const bf16x8* p = reinterpret_cast<const bf16x8*>(kr + 128 * j);
-          kl = p[0];
-          kh = p[1];
-        }
-        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl, qf[2 * j], sa, 0, 0, 0);
-        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qf[2 * j + 1], sb, 0, 0, 0);
-      }
-    }
-    float x[4];
-    float tmax = kNegInf;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[i] = (sa[i] + sb[i]) * xscale;
-      if (tok0 + 16 * wave + 4 * g + i > tok_last) x[i] = kNegInf;
-      tmax = fmaxf(tmax, x[i]);
-    }
-    tmax = xor_max_groups(tmax);
-    if (g == 0) sh.tmax[wave][r16] = tmax;
-    float p[4];
-    {
-      const float mr = (m_ref == kNegInf) ? 0.0f : m_ref;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - mr);
-      sh.p[wave][lane] = uint2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
-    }
-    __syncthreads();  // scores, maxima and P of all waves are in LDS
-
-    if constexpr (NB == 2) {
-      // the other buffer's last readers finished before this barrier
-      if (n + 1 < ntiles) {
-        regs.store(sh.tile[(n + 1) & 1], tid);
-        if (n + 2 < ntiles) regs.issue(a, seq_base, tok0 + 2 * kTileTokens, tok_last, tid);
-      }
-    }
-
-    // ---- lazy rescale: only when a tile max passes m_ref + 8 ----
-    float tile_max = sh.tmax[0][r16];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) tile_max = fmaxf(tile_max, sh.tmax[w][r16]);
-    if (__ballot(tile_max > m_ref + kLazyRescale) != 0) {  // same outcome in every wave
-      const float m_new = fmaxf(m_ref, tile_max);
-      const float alpha = (m_new == kNegInf) ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
-#pragma unroll
-      for (int v = 0; v < 8; ++v) o[v] *= alpha;
-      l_part *= alpha;
-      m_ref = m_new;
-      const float mr = (m_ref == kNegInf) ? 0.0f : m_ref;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - mr);
-      __syncthreads();  // everyone has read the old maxima
-      sh.p[wave][lane] = uint2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
-      __syncthreads();
-    }
-    l_part += (p[0] + p[1]) + (p[2] + p[3]);
-
-    // ---- O^T[dims of this wave] += V^T P^T over the 64 tokens ----
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const uint2 p_lo = sh.p[2 * kk][lane];
-      const uint2 p_hi = sh.p[2 * kk + 1][lane];
-      const bf16x8 pt = __builtin_bit_cast(bf16x8, u32x4{p_lo.x, p_lo.y, p_hi.x, p_hi.y});
-      const uint8_t* vb = cur + kk * Tile<F>::row_offset(32);
-#pragma unroll
-      for (int v = 0; v < 8; ++v) {
-        bf16x8 va;
-        if constexpr (Traits<F>::kLdsFp8) {
-          const i32x2 raw =
-              __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vb + v_off_lo + 16 * v));
-          va = fp8x8_to_bf16((uint32_t)raw[0], (uint32_t)raw[1]);
-        } else {
-          const i16x4 lo =
-              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + v_off_lo + 32 * v));
-          const i16x4 hi =
-              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + v_off_hi + 32 * v));
-          const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo);
-          const bf16x4 h4 = __builtin_bit_cast(bf16x4, hi);
-          va = bf16x8{l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
-        }
-        o[v] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pt, o[v], 0, 0, 0);
-      }
-    }
-    __syncthreads();  // P, maxima (and a single tile buffer) are free again
-
-    if constexpr (NB == 1) {
+  {
+    // ---- register-staged tiles through one LDS buffer ----
+    TileRegs<F, PAGED> regs;
+    regs.issue(a, seq_base, item.tok_begin, tok_last, tid);
+    regs.store(tiles.tile[0], tid);
+    if (Traits<F>::kPrefetch && ntiles > 1)
+      regs.issue(a, seq_base, item.tok_begin + kTileTokens, tok_last, tid);
+    __syncthreads();
+    for (int n = 0; n < ntiles; ++n) {
+      const int tok0 = item.tok_begin + n * kTileTokens;
+      attend_tile<F, PAGED>(sh, tiles.tile[0], qf, o, m_ref, l_part, tok0, tok_last, xscale, wave, lane,
+                     k_off, v_off_lo, v_off_hi);
+      __syncthreads();  // P, maxima and the tile buffer are free again
       if (n + 1 < ntiles) {
         if (!Traits<F>::kPrefetch) regs.issue(a, seq_base, tok0 + kTileTokens, tok_last, tid);
-        regs.store(sh.tile[0], tid);
+        regs.store(tiles.tile[0], tid);
         if (Traits<F>::kPrefetch && n + 2 < ntiles)
           regs.issue(a, seq_base, tok0 + 2 * kTileTokens, tok_last, tid);
         __syncthreads();
@@ -451,50 +585,337 @@ __global__ __launch_bounds__(kStage1Threads, 2) void mla_stage1(Stage1Args a) {
       *reinterpret_cast<uint2*>(dst + 16 * v) =
           uint2{pack_bf16x2(val[0], val[1]), pack_bf16x2(val[2], val[3])};
     }
-  } else {
-    float* dst = a.part_o + ((int64_t)item.slot * kNumHeads + r16) * kVDim + dv0 + 4 * g;
-#pragma unroll
-    for (int v = 0; v < 8; ++v) *reinterpret_cast<f32x4*>(dst + 16 * v) = o[v] * f;
-    if (tid < kNumHeads) a.part_lse[(int64_t)item.slot * kNumHeads + tid] = m_ref + __log2f(L);
+    return;
   }
+  float* dst = a.part_o + ((int64_t)item.slot * kNumHeads + r16) * kVDim + dv0 + 4 * g;
+#pragma unroll
+  for (int v = 0; v < 8; ++v) *reinterpret_cast<f32x4*>(dst + 16 * v) = o[v] * f;
+  if (tid < kNumHeads) a.part_lse[(int64_t)item.slot * kNumHeads + tid] = m_ref + __log2f(L);
 }
 
 // ---------------------------------------------------------------------------
-// stage 2: log-sum-exp merge of the partials, one workgroup per (seq, head)
+// stage 1, fp8 cache: four independent waves per workgroup
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kMergeThreads) void mla_merge(MergeArgs a) {
-  const int b = blockIdx.x / kNumHeads;
-  const int h = blockIdx.x % kNumHeads;
-  const int d = threadIdx.x * 4;
-  const SeqInfo info = a.seqs[b];
-  if (info.nslots < 0) return;  // written by stage 1
-  uint16_t* dst = a.out + ((int64_t)b * kNumHeads + h) * kVDim + d;
-  if (info.nslots == 0) {
-    *reinterpret_cast<uint2*>(dst) = uint2{0u, 0u};
+// Both contractions run on v_mfma_f32_16x16x32_fp8_fp8 (OCP e4m3) straight on
+// the cached codes; nothing is decoded.  The other operand is written as a sum
+// of two e4m3 numbers, hi + lo, and each product is taken twice:
+//   * the query row of head h is first scaled by 2^s_h (max |q| in [128, 256))
+//     and split q = hi + lo with hi = e4m3(q) and lo = e4m3(q - hi).  A bf16
+//     value has 8 significant bits and hi keeps the leading 4, so the rest fits
+//     lo exactly whenever it is a normal e4m3 number (|scaled q| >= 1/4, i.e.
+//     every element above 1/1024 of the row maximum; smaller ones are off by at
+//     most 2^-10 in scaled units).  2^-s_h is folded into the score scale.
+//   * the softmax weights p <= 2^8 (lazy maximum) are split the same way,
+//     which keeps about 8 significant bits, as many as a bf16 weight has.
+// Per 32-token wave tile:
+//   S^T[token, head] = K (Qhi + Qlo)^T in two 16-token subtiles (four
+//   accumulation chains each); the wave's own online softmax in the log2
+//   domain with the lazy maximum; O^T[dim, head] += V^T (Phi + Plo)^T for all
+//   512 dims (32 MFMA column tiles): the score registers are the B operand as
+//   they are (token order chosen to match), V^T comes from the transposing
+//   LDS read ds_read_b64_tr_b8.
+// The four waves' (O, max, sum) are merged through LDS once, at the end.
+struct Fp8Lds {
+  uint8_t tile[kWaves][2][kWTileBytes];  // reused by the end-of-item merge
+  float red_m[kWaves][kNumHeads];
+  float red_l[kWaves][kNumHeads];
+  int32_t pages[kMaxItemPages];
+};
+constexpr int kMergePitch = kVDim + 8;  // floats per head row in the merge buffer
+static_assert(2 * kNumHeads * kMergePitch * 4 <= (int)sizeof(Fp8Lds::tile), "merge buffer");
+
+typedef long fp8x8;  // eight e4m3 codes, the operand of one fp8 MFMA step
+
+__device__ __forceinline__ fp8x8 pack_fp8x8(uint32_t lo, uint32_t hi) {
+  return (fp8x8)(((uint64_t)hi << 32) | lo);
+}
+
+// Split eight floats (|x| <= 448) into e4m3 hi + lo (see above).
+__device__ __forceinline__ void split_fp8x8(const float (&x)[8], fp8x8& hi, fp8x8& lo) {
+  int h0 = 0, h1 = 0, l0 = 0, l1 = 0;
+  h0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], h0, false);
+  h0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], h0, true);
+  h1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[4], x[5], h1, false);
+  h1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[6], x[7], h1, true);
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(h0, false);
+  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(h0, true);
+  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8(h1, false);
+  const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8(h1, true);
+  l0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] - a[0], x[1] - a[1], l0, false);
+  l0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] - b[0], x[3] - b[1], l0, true);
+  l1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[4] - c[0], x[5] - c[1], l1, false);
+  l1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[6] - d[0], x[7] - d[1], l1, true);
+  hi = pack_fp8x8((uint32_t)h0, (uint32_t)h1);
+  lo = pack_fp8x8((uint32_t)l0, (uint32_t)l1);
+}
+
+__device__ __forceinline__ f32x4 mfma_fp8(fp8x8 a, fp8x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, 0, 0, 0);
+}
+
+template <bool PAGED>
+__global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a) {
+  __shared__ __attribute__((aligned(16))) Fp8Lds sh;
+
+  const WorkItem item = a.items[blockIdx.x];
+  const int tid = threadIdx.x;
+  if (item.slot == WorkItem::kEmpty) {  // empty sequence: its output is zero
+    uint4* dst = reinterpret_cast<uint4*>(a.out + (int64_t)item.batch * kNumHeads * kVDim);
+#pragma unroll
+    for (int k = 0; k < (kNumHeads * kVDim * 2 / 16) / kStage1Threads; ++k)
+      dst[tid + kStage1Threads * k] = uint4{0u, 0u, 0u, 0u};
     return;
   }
-  const float* lse = a.part_lse + (int64_t)info.slot_begin * kNumHeads + h;
-  float M = kNegInf;
-  for (int s = 0; s < info.nslots; ++s) M = fmaxf(M, lse[s * kNumHeads]);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+  const int lane = tid & 63;
+  const int r16 = lane & 15;  // MFMA row/column index of this lane
+  const int g = lane >> 4;    // MFMA k-group of this lane
+  const int b = item.batch;
+  const int tok_last = item.tok_end - 1;
+  const int ntiles = (item.tok_end - item.tok_begin + kWTile - 1) / kWTile;
+  const int64_t seq_base = a.kv_indptr[b];  // first row, or first page slot
+  const float kv_scale = *a.kv_scale;
+
+  int page0 = 0;
+  if constexpr (PAGED) {
+    page0 = item.tok_begin >> a.page_shift;
+    const int npages = min(((item.tok_end - 1) >> a.page_shift) - page0 + 1, kMaxItemPages);
+    for (int i = tid; i < npages; i += kStage1Threads)
+      sh.pages[i] = a.page_indices[seq_base + page0 + i];
+    __syncthreads();
+  }
+
+  WaveDma<PAGED> dma;
+  dma.init(lane);
+  const uint8_t* buf0 = sh.tile[wave][0];
+  const uint8_t* buf1 = sh.tile[wave][1];
+  if (wave < ntiles)
+    dma.issue(a, buf0, seq_base, sh.pages, page0, item.tok_begin + wave * kWTile, tok_last, lane);
+
+  // Query, loaded while the first tile flies, as the B operand of
+  // S^T = K Q^T: lane (head r16, group g) holds, for k-step 2j+h,
+  // q[head][64j + 16g + 8h .. +8], split into e4m3 hi + lo after scaling.
+  fp8x8 qh[18], ql[18];
+  float xscale;
+  {
+    const bf16x8* qrow = reinterpret_cast<const bf16x8*>(
+        a.q + ((int64_t)b * kNumHeads + r16) * kQkDim + 16 * g);
+    bf16x8 qv[18];
+#pragma unroll
+    for (int j = 0; j < 9; ++j) {
+      qv[2 * j] = qrow[8 * j];
+      qv[2 * j + 1] = qrow[8 * j + 1];
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int k = 0; k < 18; ++k)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)qv[k][e]));
+    amax = xor_max_groups(amax);
+    // 2^s with amax * 2^s in [128, 256)
+    const int s = (amax > 0.f) ? 8 - __builtin_amdgcn_frexp_expf(amax) : 0;
+    xscale = a.score_scale * kv_scale * __builtin_ldexpf(1.0f, -s);
+#pragma unroll
+    for (int k = 0; k < 18; ++k) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = __builtin_ldexpf((float)qv[k][e], s);
+      split_fp8x8(x, qh[k], ql[k]);
+    }
+  }
+
+  f32x4 o[32];  // dims 16v + 4g + i of head r16
+#pragma unroll
+  for (int v = 0; v < 32; ++v) o[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref = kNegInf;  // this wave's running max (log2 units) of head r16
+  float l_part = 0.f;     // this lane's share of the running sum
+
+  const int k_off0 = wrow_offset(r16) + 16 * g;
+  const int k_off1 = wrow_offset(16 + r16) + 16 * g;
+  // ds_read_b64_tr_b8: lane pair (2e, 2e+1) names row e of an 8 x 16-byte block
+  // (8 bytes each); lane i receives byte i of each of the 8 rows.
+  const int v_off = wrow_offset(pv_token(g, r16 >> 1)) + (r16 & 1) * 8;
+
+  int it = 0;
+  for (int t = wave; t < ntiles; t += kWaves, ++it) {
+    const int tok0 = item.tok_begin + t * kWTile;
+    const uint8_t* cur = (it & 1) ? buf1 : buf0;
+    const bool more = t + kWaves < ntiles;
+    if (more)
+      dma.issue(a, (it & 1) ? buf0 : buf1, seq_base, sh.pages, page0, tok0 + kWaves * kWTile,
+                tok_last, lane);
+    wait_vm(more ? kWTileLoads : 0);  // this tile (and the query) have arrived
+
+    // ---- scores for the tile's two 16-token subtiles ----
+    f32x4 sacc[2][4];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) sacc[q][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 9; ++j) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(cur + (q ? k_off1 : k_off0) + 64 * j);
+        const fp8x8 ka = pack_fp8x8(w[0], w[1]);  // k-step 2j
+        const fp8x8 kb = pack_fp8x8(w[2], w[3]);  // k-step 2j+1
+        sacc[q][0] = mfma_fp8(ka, qh[2 * j], sacc[q][0]);
+        sacc[q][1] = mfma_fp8(ka, ql[2 * j], sacc[q][1]);
+        sacc[q][2] = mfma_fp8(kb, qh[2 * j + 1], sacc[q][2]);
+        sacc[q][3] = mfma_fp8(kb, ql[2 * j + 1], sacc[q][3]);
+      }
+    }
+
+    // ---- online softmax of this wave (log2 domain, lazy maximum) ----
+    float x[8];
+    float tmax = kNegInf;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const f32x4* sq = sacc[e >> 2];
+      const int i = e & 3;
+      x[e] = ((sq[0][i] + sq[1][i]) + (sq[2][i] + sq[3][i])) * xscale;
+      if (tok0 + pv_token(g, e) > tok_last) x[e] = kNegInf;
+      tmax = fmaxf(tmax, x[e]);
+    }
+    tmax = xor_max_groups(tmax);
+    if (__ballot(tmax > m_ref + kLazyRescale) != 0) {
+      const float m_new = fmaxf(m_ref, tmax);
+      const float alpha = (m_new == kNegInf) ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
+#pragma unroll
+      for (int v = 0; v < 32; ++v) o[v] *= alpha;
+      l_part *= alpha;
+      m_ref = m_new;
+    }
+    const float mr = (m_ref == kNegInf) ? 0.0f : m_ref;
+    float p[8];  // element e: token pv_token(g, e) of this lane's head
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      p[e] = __builtin_amdgcn_exp2f(x[e] - mr);
+      l_part += p[e];
+    }
+    fp8x8 ph, pl;
+    split_fp8x8(p, ph, pl);
+
+    // ---- O^T += V^T P^T over the tile ----
+#pragma unroll
+    for (int v = 0; v < 32; ++v) {
+      const i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(cur + v_off + 16 * v));
+      const fp8x8 va = pack_fp8x8((uint32_t)raw[0], (uint32_t)raw[1]);
+      o[v] = mfma_fp8(va, ph, o[v]);
+      o[v] = mfma_fp8(va, pl, o[v]);
+    }
+  }
+
+  // ---- merge the four waves: shared maximum, summed sums, summed outputs ----
+  const float l_w = xor_sum_groups(l_part);
+  __syncthreads();  // every wave is done with its tile buffers
+  if (g == 0) {
+    sh.red_m[wave][r16] = m_ref;
+    sh.red_l[wave][r16] = l_w;
+  }
+  __syncthreads();
+  float M = sh.red_m[0][r16];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sh.red_m[w][r16]);
+  float L = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const float mw = sh.red_m[w][r16];
+    L += (mw == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(mw - M) * sh.red_l[w][r16];
+  }
+  const float mine = (m_ref == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_ref - M);
+  const float f = mine / L * kv_scale;
+
+  float* red = reinterpret_cast<float*>(&sh.tile[0][0][0]);  // [2][16][kMergePitch]
+  float* my_slot = red + ((wave & 1) * kNumHeads + r16) * kMergePitch + 4 * g;
+  if (wave >= 2) {
+#pragma unroll
+    for (int v = 0; v < 32; ++v) *reinterpret_cast<f32x4*>(my_slot + 16 * v) = o[v] * f;
+  }
+  __syncthreads();
+  if (wave < 2) {
+#pragma unroll
+    for (int v = 0; v < 32; ++v) {
+      f32x4* pp = reinterpret_cast<f32x4*>(my_slot + 16 * v);
+      *pp = o[v] * f + *pp;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < (kNumHeads * kVDim / 4) / kStage1Threads; ++k) {
+    const int q4 = tid + kStage1Threads * k;
+    const int h = q4 >> 7;
+    const int d = (q4 & 127) * 4;
+    const f32x4 val = *reinterpret_cast<const f32x4*>(red + h * kMergePitch + d) +
+                      *reinterpret_cast<const f32x4*>(red + (kNumHeads + h) * kMergePitch + d);
+    if (item.slot < 0) {
+      *reinterpret_cast<uint2*>(a.out + ((int64_t)b * kNumHeads + h) * kVDim + d) =
+          uint2{pack_bf16x2(val[0], val[1]), pack_bf16x2(val[2], val[3])};
+    } else {
+      *reinterpret_cast<f32x4*>(a.part_o + ((int64_t)item.slot * kNumHeads + h) * kVDim + d) = val;
+    }
+  }
+  // threads 0..15 are lanes (r16 = tid, g = 0) of wave 0: M and L are theirs
+  if (item.slot >= 0 && tid < kNumHeads)
+    a.part_lse[(int64_t)item.slot * kNumHeads + tid] = M + __log2f(L);
+}
+
+// ---------------------------------------------------------------------------
+// mla_merge: LSE merge of the partials of one (sequence, head) per workgroup,
+//   M = max_s lse_s,  out = sum_s 2^(lse_s - M) O_s / sum_s 2^(lse_s - M)
+// (727205 `mla_rd`; 700955 `reduce_lse_v71`; 599694 `_flash_fp8_split_s2`).
+// Thread t owns dims 4t..4t+3; the partials are read kMergeBatch at a time so
+// their loads are in flight together.
+// ---------------------------------------------------------------------------
+constexpr int kMergeBatch = 8;
+
+__global__ __launch_bounds__(kMergeThreads) void mla_merge(MergeArgs a) {
+  const int b = a.merge_seqs[blockIdx.x / kNumHeads];
+  const int h = blockIdx.x % kNumHeads;
+  const int d = threadIdx.x * 4;
+  const SeqInfo seq = a.seqs[b];
+  const float* lse = a.part_lse + (int64_t)seq.slot_begin * kNumHeads + h;
+  const f32x4* po = reinterpret_cast<const f32x4*>(
+                        a.part_o + ((int64_t)seq.slot_begin * kNumHeads + h) * kVDim + d);
+  constexpr int kSlotStride = kNumHeads * kVDim / 4;  // f32x4 per partial
+  float M = kNegInf;  // running maximum of the lse seen so far
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float W = 0.f;
-  for (int s = 0; s < info.nslots; ++s) {
-    const float w = __builtin_amdgcn_exp2f(lse[s * kNumHeads] - M);
-    const f32x4 po = *reinterpret_cast<const f32x4*>(
-        a.part_o + ((int64_t)(info.slot_begin + s) * kNumHeads + h) * kVDim + d);
-    acc += w * po;
-    W += w;
+  for (int s0 = 0; s0 < seq.nslots; s0 += kMergeBatch) {
+    float l[kMergeBatch];
+    f32x4 x[kMergeBatch];
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {  // all loads of the batch in flight together
+      const int s = min(s0 + k, seq.nslots - 1);
+      l[k] = lse[s * kNumHeads];
+      x[k] = po[(int64_t)s * kSlotStride];
+    }
+    float mb = M;
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k)
+      if (s0 + k < seq.nslots) mb = fmaxf(mb, l[k]);
+    const float r = __builtin_amdgcn_exp2f(M - mb);  // 0 on the first batch
+    acc *= r;
+    W *= r;
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      const float wk = (s0 + k < seq.nslots) ? __builtin_amdgcn_exp2f(l[k] - mb) : 0.f;
+      W += wk;
+      acc += wk * x[k];
+    }
+    M = mb;
   }
-  const float inv = 1.0f / W;
-  uint2 packed;
-  packed.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-  packed.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-  *reinterpret_cast<uint2*>(dst) = packed;
+  const f32x4 r = acc * (1.0f / W);
+  *reinterpret_cast<uint2*>(a.out + ((int64_t)b * kNumHeads + h) * kVDim + d) =
+      uint2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
 }
 
 template <int F, bool P>
 const void* stage1_fn() {
-  return reinterpret_cast<const void*>(&mla_stage1<F, P>);
+  if constexpr (F == kFp8)
+    return reinterpret_cast<const void*>(&mla_stage1_fp8<P>);
+  else
+    return reinterpret_cast<const void*>(&mla_stage1<F, P>);
 }
 
 const void* pick_stage1(int fmt, bool paged) {
@@ -516,11 +937,11 @@ hipError_t launch_stage1(int fmt, bool paged, const Stage1Args& a, int num_items
   return hipLaunchKernel(fn, dim3(num_items), dim3(kStage1Threads), params, 0, s);
 }
 
-hipError_t launch_merge(const MergeArgs& a, int batch, hipStream_t s) {
+hipError_t launch_merge(const MergeArgs& a, int num_merge_seqs, hipStream_t s) {
   MergeArgs args = a;
   void* params[] = {&args};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&mla_merge), dim3(batch * kNumHeads),
-                         dim3(kMergeThreads), params, 0, s);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&mla_merge),
+                         dim3(num_merge_seqs * kNumHeads), dim3(kMergeThreads), params, 0, s);
 }
 
 hipError_t kernel_attributes(int fmt, bool paged, int which, hipFuncAttributes* attr) {
