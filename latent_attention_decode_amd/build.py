@@ -4,7 +4,9 @@
 
 Every HIP translation unit is compiled with packed fp32 arithmetic disabled
 (-packed-fp32-ops); the host compiler pass warns that it does not know the
-feature, which is harmless.
+feature, which is harmless.  MFMA accumulators are kept in ordinary VGPRs
+(-amdgpu-mfma-vgpr-form): the stage-1 kernels fit in 256 of them, and the
+accumulation registers would otherwise cost a copy in and out of every tile.
 """
 
 import os
@@ -23,13 +25,15 @@ ARCH = "gfx950"
 def build(verbose: bool = False) -> str:
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-mllvm", "-amdgpu-mfma-vgpr-form",
            "-Wall", "-Wno-unused-command-line-argument",
            "-I", INCLUDE, "-I", CSRC, "-o", LIB + ".tmp"] + SOURCES
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     msgs = [l for l in (res.stdout + res.stderr).splitlines()
-            if "packed-fp32-ops" not in l and "unknown target feature" not in l.lower()]
+            if "packed-fp32-ops" not in l and "unknown target feature" not in l.lower()
+            and "reserved registers: m0" not in l]
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:

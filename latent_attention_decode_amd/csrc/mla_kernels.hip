@@ -268,99 +268,6 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Wait until at most n of this wave's vector-memory loads are outstanding.
-// (Vector loads complete in issue order.)
-__device__ __forceinline__ void wait_vm(int n) {
-  if (n == 19)
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(19, 15));
-  else
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
-  asm volatile("" ::: "memory");
-}
-
-// ---------------------------------------------------------------------------
-// fp8: per-wave 32-token tiles straight from HBM into LDS
-// ---------------------------------------------------------------------------
-// Each wave owns two LDS tile buffers and streams its own tiles (wave w takes
-// tiles w, w+4, ... of the item) with no workgroup barrier in the main loop.
-// A wave tile holds 32 rows with the padded layout of Tile::row_offset (row r
-// at 592r + 64(r/16)): a run of 16-byte slots, row r starting at slot
-// 37r + 4(r/16), 36 data slots per row, the rest padding.  One cache-to-LDS
-// load (global_load_lds_dwordx4) writes 64 consecutive slots, lane l to slot
-// base + l, so each lane fetches whichever 16-byte chunk belongs in its slot
-// and lanes on padding slots sit the load out.
-constexpr int kWTile = 32;                             // tokens per wave tile
-constexpr int kWTileBytes = kWTile * 592 + 64;         // rows 16..31 shifted by 64 B
-constexpr int kWTileSlots = kWTileBytes / 16;          // 1188
-constexpr int kWTileLoads = (kWTileSlots + 63) / 64;   // 19 loads per wave tile
-constexpr int kMaxItemPages = 512;                     // page ids of one item staged in LDS
-static_assert(kWTileLoads == 19, "fp8 wave-tile load count");
-
-__host__ __device__ constexpr int wrow_offset(int r) { return r * 592 + (r >> 4) * 64; }
-
-// One cache-to-LDS load: lane l's 16 bytes at `src` go to LDS lds_base + 16l.
-// Written as inline assembly so that the compiler does not guard later LDS
-// reads with a wait for every such load in flight; each wave waits for its
-// own tile explicitly (wait_vm) before reading it.
-__device__ __forceinline__ void dma16(const void* src, const uint8_t* lds_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)lds_base);
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, off"
-      :
-      : "v"(src), "s"(m0)
-      : "memory", "m0");
-}
-
-template <bool PAGED>
-struct WaveDma {
-  int rc[kWTileLoads];  // (tile row << 8) | 16-byte chunk of this lane's slot; -1 on padding
-
-  __device__ __forceinline__ void init(int lane) {
-#pragma unroll
-    for (int k = 0; k < kWTileLoads; ++k) {
-      const int slot = 64 * k + lane;
-      const int grp = slot / (16 * 37 + 4);  // group of 16 rows
-      const int rem = slot - grp * (16 * 37 + 4);
-      const int rr = rem / 37;
-      const int cc = rem - 37 * rr;
-      const bool data = slot < kWTileSlots && rr < 16 && cc < 36;
-      rc[k] = data ? ((16 * grp + rr) << 8) | cc : -1;
-    }
-  }
-
-  // Issue the loads of the wave tile whose first token is tok0.  Rows past
-  // tok_last fetch row tok_last (finite data, masked later by index).
-  __device__ __forceinline__ void issue(const Stage1Args& a, const uint8_t* buf, int64_t seq_base,
-                                        const int32_t* pages, int page0, int tok0, int tok_last,
-                                        int lane) const {
-    uint32_t my_row = 0;  // physical row of tile row (lane & 31)
-    if (PAGED) {
-      const int tok = min(tok0 + (lane & 31), tok_last);
-      const uint32_t page = (uint32_t)pages[(tok >> a.page_shift) - page0];
-      my_row = (page << a.page_shift) + (uint32_t)(tok & ((1 << a.page_shift) - 1));
-    }
-    const bool full = tok0 + kWTile - 1 <= tok_last;
-    const uint8_t* tile_base = a.kv + (seq_base + tok0) * 576;
-#pragma unroll
-    for (int k = 0; k < kWTileLoads; ++k) {
-      const int r = rc[k] >> 8;
-      const int c16 = (rc[k] & 0xFF) * 16;
-      const uint8_t* src;
-      if (PAGED) {
-        const uint32_t pr = (uint32_t)__shfl((int)my_row, r & 31, 64);
-        src = a.kv + (int64_t)pr * 576 + c16;
-      } else if (full) {
-        src = tile_base + (r * 576 + c16);
-      } else {
-        src = a.kv + (seq_base + min(tok0 + r, tok_last)) * 576 + c16;
-      }
-      if (rc[k] >= 0) dma16(src, buf + 1024 * k);
-    }
-  }
-};
 
 // ---------------------------------------------------------------------------
 // stage 1
@@ -594,7 +501,7 @@ __global__ __launch_bounds__(kStage1Threads, 2) void mla_stage1(Stage1Args a) {
 }
 
 // ---------------------------------------------------------------------------
-// stage 1, fp8 cache: four independent waves per workgroup
+// stage 1, fp8 cache: cooperative 64-token tiles streamed into LDS
 // ---------------------------------------------------------------------------
 // Both contractions run on v_mfma_f32_16x16x32_fp8_fp8 (OCP e4m3) straight on
 // the cached codes; nothing is decoded.  The other operand is written as a sum
@@ -607,22 +514,132 @@ __global__ __launch_bounds__(kStage1Threads, 2) void mla_stage1(Stage1Args a) {
 //     most 2^-10 in scaled units).  2^-s_h is folded into the score scale.
 //   * the softmax weights p <= 2^8 (lazy maximum) are split the same way,
 //     which keeps about 8 significant bits, as many as a bf16 weight has.
-// Per 32-token wave tile:
-//   S^T[token, head] = K (Qhi + Qlo)^T in two 16-token subtiles (four
-//   accumulation chains each); the wave's own online softmax in the log2
-//   domain with the lazy maximum; O^T[dim, head] += V^T (Phi + Plo)^T for all
-//   512 dims (32 MFMA column tiles): the score registers are the B operand as
-//   they are (token order chosen to match), V^T comes from the transposing
-//   LDS read ds_read_b64_tr_b8.
-// The four waves' (O, max, sum) are merged through LDS once, at the end.
+//
+// Data movement: every byte of the item's cache rows goes HBM -> LDS by
+// cache-to-LDS loads (global_load_lds_dwordx4), four 64-token tiles in a
+// ring, so three tiles are in flight while one is computed; the query comes
+// the same way.  A tile is its 64 rows at pitch 576 with no padding, 36 loads
+// of 1 KB each (wave w issues loads 9w..9w+8).  One load writes 64
+// consecutive 16-byte LDS slots, lane l to slot l, and each lane fetches the
+// chunk that belongs there; inside each aligned group of four chunks of a row
+// the chunks are stored XOR-permuted by chunk_swz(row), which makes every LDS
+// read below free of bank conflicts while each load still reads whole 64-byte
+// runs of the rows.
+//
+// Per tile, with wave w:
+//   1. S^T[token, head] = K (Qhi + Qlo)^T for tokens 16w..16w+15, all 576
+//      columns (four accumulation chains); the query stays in registers;
+//   2. softmax in the log2 domain with a lazy maximum shared by the four
+//      waves: it moves (and O and the sums are rescaled) only when a tile
+//      maximum passes it by more than 8, so p <= 2^8; each wave writes its
+//      e4m3 hi/lo weights P^T to LDS;
+//   3. O^T[dim, head] += V^T (Phi + Plo)^T for dims 128w..128w+127 over all 64
+//      tokens; V^T comes from the tile through the transposing LDS read
+//      ds_read_b64_tr_b8.
+// Because the maximum is shared, the waves' outputs need no merge: each wave
+// writes its own 128 columns.
+constexpr int kCTile = 64;                          // tokens per tile
+constexpr int kCTileBytes = kCTile * kQkDim;        // 36864
+constexpr int kCRing = 4;                           // tiles in the LDS ring
+constexpr int kCLoads = kCTileBytes / 1024;         // 36 loads per tile
+constexpr int kCLoadsPerWave = kCLoads / kWaves;    // 9
+constexpr int kQBytes = kNumHeads * kQkDim * 2;     // bf16 query of one sequence
+constexpr int kQLoads = kQBytes / 1024;             // 18
+constexpr int kPRow = 72;                           // bytes per head row of P^T
+constexpr int kMaxItemPages = 512;                  // page ids of one item staged in LDS
+static_assert(kCLoads == kWaves * kCLoadsPerWave && kQLoads * 1024 == kQBytes, "load split");
+static_assert(kQBytes <= kCTileBytes, "the query is staged in the last ring slot");
+
+// Position of 16-byte chunk c of tile row r inside the row.
+__host__ __device__ constexpr int chunk_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+__host__ __device__ constexpr int tile_slot(int r, int c) { return r * 36 + (c ^ chunk_swz(r)); }
+// Position of 16-byte chunk c (0..71) of query head h.
+__host__ __device__ constexpr int q_slot(int h, int c) { return h * 72 + (c ^ (h & 7)); }
+
+// Every slot of a tile holds exactly one chunk of one row, and vice versa.
+constexpr bool tile_slots_are_a_permutation() {
+  bool seen[kCLoads * 64] = {};
+  for (int r = 0; r < kCTile; ++r)
+    for (int c = 0; c < 36; ++c) {
+      const int s = tile_slot(r, c);
+      if (s / 36 != r || seen[s]) return false;
+      seen[s] = true;
+    }
+  return true;
+}
+constexpr bool q_slots_are_a_permutation() {
+  bool seen[kQLoads * 64] = {};
+  for (int h = 0; h < kNumHeads; ++h)
+    for (int c = 0; c < 72; ++c) {
+      const int s = q_slot(h, c);
+      if (s / 72 != h || seen[s]) return false;
+      seen[s] = true;
+    }
+  return true;
+}
+static_assert(tile_slots_are_a_permutation() && q_slots_are_a_permutation(), "slot maps");
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+
+// The loads below name m0 as clobbered, which they do write; nothing else in
+// these kernels keeps a value in m0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+
+// One cache-to-LDS load, lane l's 16 bytes at base + off (a 32-bit per-lane
+// offset from a uniform base) to LDS address m0 + 16 l.  Written as inline
+// assembly so that the compiler does not guard later LDS reads with a wait for
+// every such load in flight; the kernel waits for them explicitly.
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t off, uint32_t m0) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(off), "s"(base), "s"(m0)
+      : "memory", "m0");
+}
+// The same from a per-lane 64-bit address.
+__device__ __forceinline__ void dma16(const uint8_t* src, uint32_t m0) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(src), "s"(m0)
+      : "memory", "m0");
+}
+
+#pragma clang diagnostic pop
+
+// Wait until at most 9n of this wave's loads are outstanding (n = 0..3).
+// Loads complete in issue order.
+__device__ __forceinline__ void wait_tiles(int n) {
+  switch (n) {
+    case 3: __builtin_amdgcn_s_waitcnt(waitcnt_imm(27, 15)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(waitcnt_imm(18, 15)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(waitcnt_imm(9, 15)); break;
+    default: __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15)); break;
+  }
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const uint8_t*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 struct Fp8Lds {
-  uint8_t tile[kWaves][2][kWTileBytes];  // reused by the end-of-item merge
-  float red_m[kWaves][kNumHeads];
-  float red_l[kWaves][kNumHeads];
-  int32_t pages[kMaxItemPages];
+  uint8_t tile[kCRing][kCTileBytes];       // the ring; slot 3 first holds the query
+  uint8_t p[2][kNumHeads][kPRow];          // P^T hi / lo as [head][token]
+  float red_m[kWaves][kNumHeads];          // per-wave tile maxima
+  float red_l[kWaves][kNumHeads];          // per-wave sums, at the end
+  int32_t pages[kMaxItemPages];            // paged: page ids of the item
 };
-constexpr int kMergePitch = kVDim + 8;  // floats per head row in the merge buffer
-static_assert(2 * kNumHeads * kMergePitch * 4 <= (int)sizeof(Fp8Lds::tile), "merge buffer");
 
 typedef long fp8x8;  // eight e4m3 codes, the operand of one fp8 MFMA step
 
@@ -649,6 +666,19 @@ __device__ __forceinline__ void split_fp8x8(const float (&x)[8], fp8x8& hi, fp8x
   lo = pack_fp8x8((uint32_t)l0, (uint32_t)l1);
 }
 
+// Four floats (|x| <= 448) -> e4m3 hi + lo codes, one 32-bit word each.
+__device__ __forceinline__ void split_fp8x4(const float (&x)[4], uint32_t& hi, uint32_t& lo) {
+  int h = 0, l = 0;
+  h = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], h, false);
+  h = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], h, true);
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(h, false);
+  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(h, true);
+  l = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] - a[0], x[1] - a[1], l, false);
+  l = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] - b[0], x[3] - b[1], l, true);
+  hi = (uint32_t)h;
+  lo = (uint32_t)l;
+}
+
 __device__ __forceinline__ f32x4 mfma_fp8(fp8x8 a, fp8x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, 0, 0, 0);
 }
@@ -672,7 +702,7 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a
   const int g = lane >> 4;    // MFMA k-group of this lane
   const int b = item.batch;
   const int tok_last = item.tok_end - 1;
-  const int ntiles = (item.tok_end - item.tok_begin + kWTile - 1) / kWTile;
+  const int ntiles = (item.tok_end - item.tok_begin + kCTile - 1) / kCTile;
   const int64_t seq_base = a.kv_indptr[b];  // first row, or first page slot
   const float kv_scale = *a.kv_scale;
 
@@ -685,26 +715,78 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a
     __syncthreads();
   }
 
-  WaveDma<PAGED> dma;
-  dma.init(lane);
-  const uint8_t* buf0 = sh.tile[wave][0];
-  const uint8_t* buf1 = sh.tile[wave][1];
-  if (wave < ntiles)
-    dma.issue(a, buf0, seq_base, sh.pages, page0, item.tok_begin + wave * kWTile, tok_last, lane);
+  // This lane's slot in each of its wave's nine loads of a tile: tile row and
+  // chunk, and (contiguous cache) the byte offset of that chunk in the tile.
+  uint32_t rc[kCLoadsPerWave], off[kCLoadsPerWave];
+#pragma unroll
+  for (int j = 0; j < kCLoadsPerWave; ++j) {
+    const int s = 64 * (kCLoadsPerWave * wave + j) + lane;
+    const int r = s / 36;
+    const int c = (s - 36 * r) ^ chunk_swz(r);
+    rc[j] = (uint32_t)(r << 8 | c);
+    off[j] = (uint32_t)(r * kQkDim + 16 * c);
+  }
+  const uint32_t ring0 = lds_u32(&sh.tile[0][0]) + 1024 * kCLoadsPerWave * wave;
 
-  // Query, loaded while the first tile flies, as the B operand of
-  // S^T = K Q^T: lane (head r16, group g) holds, for k-step 2j+h,
-  // q[head][64j + 16g + 8h .. +8], split into e4m3 hi + lo after scaling.
+  // Issue this wave's loads of tile t into ring slot t % 4.  Rows past the
+  // item's last token fetch that token's row (finite data, masked later).
+  auto issue = [&](int t) {
+    const int tok0 = item.tok_begin + t * kCTile;
+    const int lim = tok_last - tok0;  // last valid tile row
+    const uint32_t m0 = ring0 + (uint32_t)((t & (kCRing - 1)) * kCTileBytes);
+    if constexpr (!PAGED) {
+      const uint8_t* base = uniform_ptr(a.kv + (seq_base + tok0) * kQkDim);
+      if (lim >= kCTile - 1) {
+#pragma unroll
+        for (int j = 0; j < kCLoadsPerWave; ++j) dma16(base, off[j], m0 + 1024 * j);
+      } else {
+#pragma unroll
+        for (int j = 0; j < kCLoadsPerWave; ++j) {
+          const uint32_t r = min((int)(rc[j] >> 8), lim);
+          dma16(base, r * kQkDim + 16 * (rc[j] & 0xFF), m0 + 1024 * j);
+        }
+      }
+    } else {
+      const int pmask = (1 << a.page_shift) - 1;
+#pragma unroll
+      for (int j = 0; j < kCLoadsPerWave; ++j) {
+        const int tok = tok0 + min((int)(rc[j] >> 8), lim);
+        const uint32_t page = (uint32_t)sh.pages[(tok >> a.page_shift) - page0];
+        const int64_t row = (int64_t)((page << a.page_shift) + (uint32_t)(tok & pmask));
+        dma16(a.kv + row * kQkDim + 16 * (rc[j] & 0xFF), m0 + 1024 * j);
+      }
+    }
+  };
+
+  // The query: 18 loads into ring slot 3 (load k by wave k % 4), then the
+  // first three tiles.
+  {
+    const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(a.q + (int64_t)b * kNumHeads * kQkDim);
+    const uint32_t qm0 = lds_u32(&sh.tile[kCRing - 1][0]);
+    for (int k = wave; k < kQLoads; k += kWaves) {
+      const int s = 64 * k + lane;
+      const int h = s / 72;
+      const int c = (s - 72 * h) ^ (h & 7);
+      dma16(qsrc + (h * 72 + c) * 16, qm0 + 1024 * k);
+    }
+  }
+  const int npre = min(ntiles, kCRing - 1);
+  for (int t = 0; t < npre; ++t) issue(t);
+  wait_tiles(npre);  // this wave's query loads have landed
+  lds_barrier();     // ... and everyone's
+
+  // Query as the B operand of S^T = K Q^T: lane (head r16, group g) holds,
+  // for k-step 2j+h, q[head][64j + 16g + 8h .. +8], scaled by 2^s and split
+  // into e4m3 hi + lo.
   fp8x8 qh[18], ql[18];
   float xscale;
   {
-    const bf16x8* qrow = reinterpret_cast<const bf16x8*>(
-        a.q + ((int64_t)b * kNumHeads + r16) * kQkDim + 16 * g);
+    const uint8_t* qlds = &sh.tile[kCRing - 1][0];
     bf16x8 qv[18];
 #pragma unroll
     for (int j = 0; j < 9; ++j) {
-      qv[2 * j] = qrow[8 * j];
-      qv[2 * j + 1] = qrow[8 * j + 1];
+      qv[2 * j] = *reinterpret_cast<const bf16x8*>(qlds + 16 * q_slot(r16, 8 * j + 2 * g));
+      qv[2 * j + 1] = *reinterpret_cast<const bf16x8*>(qlds + 16 * q_slot(r16, 8 * j + 2 * g + 1));
     }
     float amax = 0.f;
 #pragma unroll
@@ -724,140 +806,130 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a
     }
   }
 
-  f32x4 o[32];  // dims 16v + 4g + i of head r16
+  f32x4 o[8];  // O^T[dim 128w + 16v + 4g + i][head r16]
 #pragma unroll
-  for (int v = 0; v < 32; ++v) o[v] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref = kNegInf;  // this wave's running max (log2 units) of head r16
+  for (int v = 0; v < 8; ++v) o[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref = kNegInf;  // shared running maximum (log2 units) of head r16
   float l_part = 0.f;     // this lane's share of the running sum
 
-  const int k_off0 = wrow_offset(r16) + 16 * g;
-  const int k_off1 = wrow_offset(16 + r16) + 16 * g;
-  // ds_read_b64_tr_b8: lane pair (2e, 2e+1) names row e of an 8 x 16-byte block
-  // (8 bytes each); lane i receives byte i of each of the 8 rows.
-  const int v_off = wrow_offset(pv_token(g, r16 >> 1)) + (r16 & 1) * 8;
-
-  int it = 0;
-  for (int t = wave; t < ntiles; t += kWaves, ++it) {
-    const int tok0 = item.tok_begin + t * kWTile;
-    const uint8_t* cur = (it & 1) ? buf1 : buf0;
-    const bool more = t + kWaves < ntiles;
-    if (more)
-      dma.issue(a, (it & 1) ? buf0 : buf1, seq_base, sh.pages, page0, tok0 + kWaves * kWTile,
-                tok_last, lane);
-    wait_vm(more ? kWTileLoads : 0);  // this tile (and the query) have arrived
-
-    // ---- scores for the tile's two 16-token subtiles ----
-    f32x4 sacc[2][4];
+  // LDS byte offsets of this lane's reads within a tile.
+  const int k_row = 16 * wave + r16;
+  const int k_off = k_row * kQkDim + 16 * (g ^ chunk_swz(k_row));
+  int v_off[2][4];  // [k-step][v % 4]; + 64 (v / 4)
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
+  for (int kt = 0; kt < 2; ++kt) {
+    const int row = 32 * kt + 8 * g + (r16 >> 1);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) sacc[q][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c4 = 0; c4 < 4; ++c4)
+      v_off[kt][c4] = row * kQkDim + 16 * (8 * wave + (c4 ^ chunk_swz(row))) + 8 * (r16 & 1);
+  }
+  uint8_t* const p_hi = &sh.p[0][r16][0];
+  uint8_t* const p_lo = &sh.p[1][r16][0];
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int tok0 = item.tok_begin + t * kCTile;
+    wait_tiles(min(ntiles - 1 - t, kCRing - 2));  // this wave's part of tile t
+    lds_barrier();  // all of tile t; everyone is past tile t-1 (and the query)
+    if (t + kCRing - 1 < ntiles) issue(t + kCRing - 1);
+    const uint8_t* cur = &sh.tile[t & (kCRing - 1)][0];
+
+    // ---- scores of tokens 16w..16w+15 ----
+    f32x4 sacc[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sacc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 9; ++j) {
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(cur + (q ? k_off1 : k_off0) + 64 * j);
-        const fp8x8 ka = pack_fp8x8(w[0], w[1]);  // k-step 2j
-        const fp8x8 kb = pack_fp8x8(w[2], w[3]);  // k-step 2j+1
-        sacc[q][0] = mfma_fp8(ka, qh[2 * j], sacc[q][0]);
-        sacc[q][1] = mfma_fp8(ka, ql[2 * j], sacc[q][1]);
-        sacc[q][2] = mfma_fp8(kb, qh[2 * j + 1], sacc[q][2]);
-        sacc[q][3] = mfma_fp8(kb, ql[2 * j + 1], sacc[q][3]);
-      }
+      const u32x4 w = *reinterpret_cast<const u32x4*>(cur + k_off + 64 * j);
+      const fp8x8 ka = pack_fp8x8(w[0], w[1]);  // k-step 2j
+      const fp8x8 kb = pack_fp8x8(w[2], w[3]);  // k-step 2j+1
+      sacc[0] = mfma_fp8(ka, qh[2 * j], sacc[0]);
+      sacc[1] = mfma_fp8(ka, ql[2 * j], sacc[1]);
+      sacc[2] = mfma_fp8(kb, qh[2 * j + 1], sacc[2]);
+      sacc[3] = mfma_fp8(kb, ql[2 * j + 1], sacc[3]);
     }
 
-    // ---- online softmax of this wave (log2 domain, lazy maximum) ----
-    float x[8];
+    // ---- softmax: element i is token 16w + 4g + i of head r16 ----
+    float x[4];
     float tmax = kNegInf;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const f32x4* sq = sacc[e >> 2];
-      const int i = e & 3;
-      x[e] = ((sq[0][i] + sq[1][i]) + (sq[2][i] + sq[3][i])) * xscale;
-      if (tok0 + pv_token(g, e) > tok_last) x[e] = kNegInf;
-      tmax = fmaxf(tmax, x[e]);
+    for (int i = 0; i < 4; ++i) {
+      x[i] = ((sacc[0][i] + sacc[1][i]) + (sacc[2][i] + sacc[3][i])) * xscale;
+      if (tok0 + 16 * wave + 4 * g + i > tok_last) x[i] = kNegInf;
+      tmax = fmaxf(tmax, x[i]);
     }
     tmax = xor_max_groups(tmax);
-    if (__ballot(tmax > m_ref + kLazyRescale) != 0) {
-      const float m_new = fmaxf(m_ref, tmax);
-      const float alpha = (m_new == kNegInf) ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
+    if (g == 0) sh.red_m[wave][r16] = tmax;
+    float p[4];
+    uint32_t ph, pl;
+    const float mr = (m_ref == kNegInf) ? 0.0f : m_ref;
 #pragma unroll
-      for (int v = 0; v < 32; ++v) o[v] *= alpha;
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - mr);
+    split_fp8x4(p, ph, pl);
+    *reinterpret_cast<uint32_t*>(p_hi + 16 * wave + 4 * g) = ph;
+    *reinterpret_cast<uint32_t*>(p_lo + 16 * wave + 4 * g) = pl;
+    lds_barrier();  // P^T and the tile maxima of all waves
+
+    float tile_max = sh.red_m[0][r16];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) tile_max = fmaxf(tile_max, sh.red_m[w][r16]);
+    // Every wave reads the same maxima, so this branch is uniform.
+    if (__ballot(tile_max > m_ref + kLazyRescale) != 0) {
+      const float m_new = fmaxf(m_ref, tile_max);
+      const float alpha = (m_ref == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
+#pragma unroll
+      for (int v = 0; v < 8; ++v) o[v] *= alpha;
       l_part *= alpha;
       m_ref = m_new;
-    }
-    const float mr = (m_ref == kNegInf) ? 0.0f : m_ref;
-    float p[8];  // element e: token pv_token(g, e) of this lane's head
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      p[e] = __builtin_amdgcn_exp2f(x[e] - mr);
-      l_part += p[e];
+      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - m_ref);
+      split_fp8x4(p, ph, pl);
+      lds_barrier();  // everyone has read the maxima before they are rewritten
+      *reinterpret_cast<uint32_t*>(p_hi + 16 * wave + 4 * g) = ph;
+      *reinterpret_cast<uint32_t*>(p_lo + 16 * wave + 4 * g) = pl;
+      lds_barrier();
     }
-    fp8x8 ph, pl;
-    split_fp8x8(p, ph, pl);
+    l_part += (p[0] + p[1]) + (p[2] + p[3]);
 
-    // ---- O^T += V^T P^T over the tile ----
+    // ---- O^T += V^T P^T over the 64 tokens ----
 #pragma unroll
-    for (int v = 0; v < 32; ++v) {
-      const i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(cur + v_off + 16 * v));
-      const fp8x8 va = pack_fp8x8((uint32_t)raw[0], (uint32_t)raw[1]);
-      o[v] = mfma_fp8(va, ph, o[v]);
-      o[v] = mfma_fp8(va, pl, o[v]);
+    for (int kt = 0; kt < 2; ++kt) {
+      const fp8x8 bh = *reinterpret_cast<const fp8x8*>(p_hi + 32 * kt + 8 * g);
+      const fp8x8 bl = *reinterpret_cast<const fp8x8*>(p_lo + 32 * kt + 8 * g);
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (lds_i32x2*)(cur + v_off[kt][v & 3] + 64 * (v >> 2)));
+        const fp8x8 va = pack_fp8x8((uint32_t)raw[0], (uint32_t)raw[1]);
+        o[v] = mfma_fp8(va, bh, o[v]);
+        o[v] = mfma_fp8(va, bl, o[v]);
+      }
     }
   }
 
-  // ---- merge the four waves: shared maximum, summed sums, summed outputs ----
+  // ---- sums over the item; each wave writes its 128 columns ----
   const float l_w = xor_sum_groups(l_part);
-  __syncthreads();  // every wave is done with its tile buffers
-  if (g == 0) {
-    sh.red_m[wave][r16] = m_ref;
-    sh.red_l[wave][r16] = l_w;
-  }
-  __syncthreads();
-  float M = sh.red_m[0][r16];
-#pragma unroll
-  for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sh.red_m[w][r16]);
+  if (g == 0) sh.red_l[wave][r16] = l_w;
+  lds_barrier();
   float L = 0.f;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const float mw = sh.red_m[w][r16];
-    L += (mw == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(mw - M) * sh.red_l[w][r16];
-  }
-  const float mine = (m_ref == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_ref - M);
-  const float f = mine / L * kv_scale;
-
-  float* red = reinterpret_cast<float*>(&sh.tile[0][0][0]);  // [2][16][kMergePitch]
-  float* my_slot = red + ((wave & 1) * kNumHeads + r16) * kMergePitch + 4 * g;
-  if (wave >= 2) {
+  for (int w = 0; w < kWaves; ++w) L += sh.red_l[w][r16];
+  const float f = kv_scale / L;
+  const int dim0 = 128 * wave + 4 * g;
+  if (item.slot < 0) {
+    uint16_t* dst = a.out + ((int64_t)b * kNumHeads + r16) * kVDim + dim0;
 #pragma unroll
-    for (int v = 0; v < 32; ++v) *reinterpret_cast<f32x4*>(my_slot + 16 * v) = o[v] * f;
-  }
-  __syncthreads();
-  if (wave < 2) {
-#pragma unroll
-    for (int v = 0; v < 32; ++v) {
-      f32x4* pp = reinterpret_cast<f32x4*>(my_slot + 16 * v);
-      *pp = o[v] * f + *pp;
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < (kNumHeads * kVDim / 4) / kStage1Threads; ++k) {
-    const int q4 = tid + kStage1Threads * k;
-    const int h = q4 >> 7;
-    const int d = (q4 & 127) * 4;
-    const f32x4 val = *reinterpret_cast<const f32x4*>(red + h * kMergePitch + d) +
-                      *reinterpret_cast<const f32x4*>(red + (kNumHeads + h) * kMergePitch + d);
-    if (item.slot < 0) {
-      *reinterpret_cast<uint2*>(a.out + ((int64_t)b * kNumHeads + h) * kVDim + d) =
+    for (int v = 0; v < 8; ++v) {
+      const f32x4 val = o[v] * f;
+      *reinterpret_cast<uint2*>(dst + 16 * v) =
           uint2{pack_bf16x2(val[0], val[1]), pack_bf16x2(val[2], val[3])};
-    } else {
-      *reinterpret_cast<f32x4*>(a.part_o + ((int64_t)item.slot * kNumHeads + h) * kVDim + d) = val;
     }
+  } else {
+    float* dst = a.part_o + ((int64_t)item.slot * kNumHeads + r16) * kVDim + dim0;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) *reinterpret_cast<f32x4*>(dst + 16 * v) = o[v] * f;
+    if (wave == 0 && g == 0)
+      a.part_lse[(int64_t)item.slot * kNumHeads + r16] = m_ref + __log2f(L);
   }
-  // threads 0..15 are lanes (r16 = tid, g = 0) of wave 0: M and L are theirs
-  if (item.slot >= 0 && tid < kNumHeads)
-    a.part_lse[(int64_t)item.slot * kNumHeads + tid] = M + __log2f(L);
 }
 
 // ---------------------------------------------------------------------------
