@@ -149,16 +149,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Max / sum over the four lanes l, l^16, l^32, l^48 (the four MFMA k-groups
+// of one row), with the gfx950 lane-swap instructions: permlane32_swap(x, x)
+// gives every lane the value of its own half in one result and of the other
+// half in the other, and permlane16_swap does the same for 16-lane rows.
 __device__ __forceinline__ float xor_max_groups(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  v = fmaxf(v, __shfl_xor(v, 32, 64));
-  return v;
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 __device__ __forceinline__ float xor_sum_groups(float v) {
-  v += __shfl_xor(v, 16, 64);
-  v += __shfl_xor(v, 32, 64);
-  return v;
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Token (within a 32-token P.V step) of element e (0..7) of lane group g.
@@ -501,11 +507,14 @@ __global__ __launch_bounds__(kStage1Threads, 2) void mla_stage1(Stage1Args a) {
 }
 
 // ---------------------------------------------------------------------------
-// stage 1, fp8 cache: cooperative 64-token tiles streamed into LDS
+// stage 1, fp8 cache: cooperative 128-token tiles streamed into LDS
 // ---------------------------------------------------------------------------
-// Both contractions run on v_mfma_f32_16x16x32_fp8_fp8 (OCP e4m3) straight on
-// the cached codes; nothing is decoded.  The other operand is written as a sum
-// of two e4m3 numbers, hi + lo, and each product is taken twice:
+// Both contractions run straight on the cached e4m3 codes (nothing is
+// decoded), on the gfx950 MX matrix instruction v_mfma_scale_f32_16x16x128_
+// f8f6f4 (fp8 x fp8, unit block scales), which takes 128 k-values per step,
+// and on v_mfma_f32_16x16x32_fp8_fp8 for the 64 rope columns.  The other
+// operand is written as a sum of two e4m3 numbers, hi + lo, and each product
+// is taken twice:
 //   * the query row of head h is first scaled by 2^s_h (max |q| in [128, 256))
 //     and split q = hi + lo with hi = e4m3(q) and lo = e4m3(q - hi).  A bf16
 //     value has 8 significant bits and hi keeps the leading 4, so the rest fits
@@ -516,42 +525,42 @@ __global__ __launch_bounds__(kStage1Threads, 2) void mla_stage1(Stage1Args a) {
 //     which keeps about 8 significant bits, as many as a bf16 weight has.
 //
 // Data movement: every byte of the item's cache rows goes HBM -> LDS by
-// cache-to-LDS loads (global_load_lds_dwordx4), four 64-token tiles in a
-// ring, so three tiles are in flight while one is computed; the query comes
-// the same way.  A tile is its 64 rows at pitch 576 with no padding, 36 loads
-// of 1 KB each (wave w issues loads 9w..9w+8).  One load writes 64
-// consecutive 16-byte LDS slots, lane l to slot l, and each lane fetches the
-// chunk that belongs there; inside each aligned group of four chunks of a row
-// the chunks are stored XOR-permuted by chunk_swz(row), which makes every LDS
-// read below free of bank conflicts while each load still reads whole 64-byte
-// runs of the rows.
+// cache-to-LDS loads (global_load_lds_dwordx4), in a ring of two 128-token
+// tiles, so one tile is in flight while the other is computed; the query
+// comes the same way.  A tile is its 128 rows at pitch 576 with no padding,
+// 72 loads of 1 KB each (wave w issues loads 18w..18w+17).  One load writes
+// 64 consecutive 16-byte LDS slots, lane l to slot l, and each lane fetches
+// the chunk that belongs there; inside each aligned group of four chunks of a
+// row the chunks are stored XOR-permuted by chunk_swz(row), which makes every
+// LDS read below free of bank conflicts while each load still covers whole
+// 64-byte runs of the rows.
 //
 // Per tile, with wave w:
-//   1. S^T[token, head] = K (Qhi + Qlo)^T for tokens 16w..16w+15, all 576
-//      columns (four accumulation chains); the query stays in registers;
+//   1. S^T[token, head] = K (Qhi + Qlo)^T for tokens 32w..32w+31 (two 16-token
+//      row blocks), all 576 columns; the query stays in registers;
 //   2. softmax in the log2 domain with a lazy maximum shared by the four
 //      waves: it moves (and O and the sums are rescaled) only when a tile
 //      maximum passes it by more than 8, so p <= 2^8; each wave writes its
 //      e4m3 hi/lo weights P^T to LDS;
-//   3. O^T[dim, head] += V^T (Phi + Plo)^T for dims 128w..128w+127 over all 64
-//      tokens; V^T comes from the tile through the transposing LDS read
-//      ds_read_b64_tr_b8.
+//   3. O^T[dim, head] += V^T (Phi + Plo)^T for dims 128w..128w+127 over all
+//      128 tokens, one MX step per 16 columns; V^T comes from the tile through
+//      the transposing LDS read ds_read_b64_tr_b8.
 // Because the maximum is shared, the waves' outputs need no merge: each wave
 // writes its own 128 columns.
-constexpr int kCTile = 64;                          // tokens per tile
-constexpr int kCTileBytes = kCTile * kQkDim;        // 36864
-constexpr int kCRing = 4;                           // tiles in the LDS ring
-constexpr int kCLoads = kCTileBytes / 1024;         // 36 loads per tile
-constexpr int kCLoadsPerWave = kCLoads / kWaves;    // 9
+constexpr int kCTile = 128;                         // tokens per tile
+constexpr int kCTileBytes = kCTile * kQkDim;        // 73728
+constexpr int kCRing = 2;                           // tiles in the LDS ring
+constexpr int kCLoads = kCTileBytes / 1024;         // 72 loads per tile
+constexpr int kCLoadsPerWave = kCLoads / kWaves;    // 18
 constexpr int kQBytes = kNumHeads * kQkDim * 2;     // bf16 query of one sequence
 constexpr int kQLoads = kQBytes / 1024;             // 18
-constexpr int kPRow = 72;                           // bytes per head row of P^T
+constexpr int kPRow = kCTile + 16;                  // bytes per head row of P^T
 constexpr int kMaxItemPages = 512;                  // page ids of one item staged in LDS
 static_assert(kCLoads == kWaves * kCLoadsPerWave && kQLoads * 1024 == kQBytes, "load split");
 static_assert(kQBytes <= kCTileBytes, "the query is staged in the last ring slot");
 
 // Position of 16-byte chunk c of tile row r inside the row.
-__host__ __device__ constexpr int chunk_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+__host__ __device__ constexpr int chunk_swz(int r) { return (r >> 1) & 3; }
 __host__ __device__ constexpr int tile_slot(int r, int c) { return r * 36 + (c ^ chunk_swz(r)); }
 // Position of 16-byte chunk c (0..71) of query head h.
 __host__ __device__ constexpr int q_slot(int h, int c) { return h * 72 + (c ^ (h & 7)); }
@@ -583,46 +592,78 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
 }
 
-// The loads below name m0 as clobbered, which they do write; nothing else in
+// Cache-to-LDS loads: load b of a group writes lane l's 16 bytes to LDS
+// m0 + 1024 b + 16 l; the instruction offset 1024 b is added to the global
+// address as well, so the per-lane address passed in excludes it.  Written as
+// inline assembly so that the compiler does not guard later LDS reads with a
+// wait for every such load in flight; the kernel waits for them explicitly.
+// The loads carry the non-temporal hint: each byte is read once, and
+// streaming reads that do not try to stay in the caches reach a higher HBM
+// rate.  They name m0 as clobbered, which they do write; nothing else in
 // these kernels keeps a value in m0.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-
-// One cache-to-LDS load, lane l's 16 bytes at base + off (a 32-bit per-lane
-// offset from a uniform base) to LDS address m0 + 16 l.  Written as inline
-// assembly so that the compiler does not guard later LDS reads with a wait for
-// every such load in flight; the kernel waits for them explicitly.
-__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t off, uint32_t m0) {
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, %1"
-      :
-      : "v"(off), "s"(base), "s"(m0)
-      : "memory", "m0");
+template <int N>
+__device__ __forceinline__ void dma_group(const uint8_t* base, const uint32_t* off, uint32_t m0) {
+  static_assert(N >= 1 && N <= 4, "group size");
+  if constexpr (N == 4)
+    asm volatile(
+        "s_mov_b32 m0, %5\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %4 nt\n\t"
+        "global_load_lds_dwordx4 %1, %4 offset:1024 nt\n\t"
+        "global_load_lds_dwordx4 %2, %4 offset:2048 nt\n\t"
+        "global_load_lds_dwordx4 %3, %4 offset:3072 nt"
+        :
+        : "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "s"(base), "s"(m0)
+        : "memory", "m0");
+  else if constexpr (N == 2)
+    asm volatile(
+        "s_mov_b32 m0, %3\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %2 nt\n\t"
+        "global_load_lds_dwordx4 %1, %2 offset:1024 nt"
+        :
+        : "v"(off[0]), "v"(off[1]), "s"(base), "s"(m0)
+        : "memory", "m0");
+  else
+    static_assert(N == 4 || N == 2, "group size");
 }
-// The same from a per-lane 64-bit address.
-__device__ __forceinline__ void dma16(const uint8_t* src, uint32_t m0) {
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, off"
-      :
-      : "v"(src), "s"(m0)
-      : "memory", "m0");
+template <int N>
+__device__ __forceinline__ void dma_group(const uint8_t* const* src, uint32_t m0) {
+  if constexpr (N == 4)
+    asm volatile(
+        "s_mov_b32 m0, %4\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, off nt\n\t"
+        "global_load_lds_dwordx4 %1, off offset:1024 nt\n\t"
+        "global_load_lds_dwordx4 %2, off offset:2048 nt\n\t"
+        "global_load_lds_dwordx4 %3, off offset:3072 nt"
+        :
+        : "v"(src[0]), "v"(src[1]), "v"(src[2]), "v"(src[3]), "s"(m0)
+        : "memory", "m0");
+  else if constexpr (N == 2)
+    asm volatile(
+        "s_mov_b32 m0, %2\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, off nt\n\t"
+        "global_load_lds_dwordx4 %1, off offset:1024 nt"
+        :
+        : "v"(src[0]), "v"(src[1]), "s"(m0)
+        : "memory", "m0");
+  else
+    static_assert(N == 4 || N == 2, "group size");
 }
-
+// One load, lane l's 16 bytes at src to LDS m0 + 16 l.
+__device__ __forceinline__ void dma_one(const void* src, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+               :
+               : "v"(src), "s"(m0)
+               : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
-// Wait until at most 9n of this wave's loads are outstanding (n = 0..3).
-// Loads complete in issue order.
-__device__ __forceinline__ void wait_tiles(int n) {
-  switch (n) {
-    case 3: __builtin_amdgcn_s_waitcnt(waitcnt_imm(27, 15)); break;
-    case 2: __builtin_amdgcn_s_waitcnt(waitcnt_imm(18, 15)); break;
-    case 1: __builtin_amdgcn_s_waitcnt(waitcnt_imm(9, 15)); break;
-    default: __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15)); break;
-  }
+// Wait until at most N of this wave's loads are outstanding (loads complete
+// in issue order).
+template <int N>
+__device__ __forceinline__ void wait_loads() {
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(N, 15));
   asm volatile("" ::: "memory");
 }
 
@@ -634,53 +675,44 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
 }
 
 struct Fp8Lds {
-  uint8_t tile[kCRing][kCTileBytes];       // the ring; slot 3 first holds the query
+  uint8_t tile[kCRing][kCTileBytes];       // the ring; slot 1 first holds the query
   uint8_t p[2][kNumHeads][kPRow];          // P^T hi / lo as [head][token]
-  float red_m[kWaves][kNumHeads];          // per-wave tile maxima
-  float red_l[kWaves][kNumHeads];          // per-wave sums, at the end
+  float red_m[kNumHeads][kWaves];          // per-wave tile maxima
+  float red_l[kNumHeads][kWaves];          // per-wave sums, at the end
   int32_t pages[kMaxItemPages];            // paged: page ids of the item
 };
 
-typedef long fp8x8;  // eight e4m3 codes, the operand of one fp8 MFMA step
+typedef long fp8x8;                                             // 8 e4m3 codes
+typedef int fp8x32 __attribute__((ext_vector_type(8)));         // 32 e4m3 codes
 
 __device__ __forceinline__ fp8x8 pack_fp8x8(uint32_t lo, uint32_t hi) {
   return (fp8x8)(((uint64_t)hi << 32) | lo);
 }
 
-// Split eight floats (|x| <= 448) into e4m3 hi + lo (see above).
-__device__ __forceinline__ void split_fp8x8(const float (&x)[8], fp8x8& hi, fp8x8& lo) {
-  int h0 = 0, h1 = 0, l0 = 0, l1 = 0;
-  h0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], h0, false);
-  h0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], h0, true);
-  h1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[4], x[5], h1, false);
-  h1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[6], x[7], h1, true);
-  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(h0, false);
-  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(h0, true);
-  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8(h1, false);
-  const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8(h1, true);
-  l0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] - a[0], x[1] - a[1], l0, false);
-  l0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] - b[0], x[3] - b[1], l0, true);
-  l1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[4] - c[0], x[5] - c[1], l1, false);
-  l1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[6] - d[0], x[7] - d[1], l1, true);
-  hi = pack_fp8x8((uint32_t)h0, (uint32_t)h1);
-  lo = pack_fp8x8((uint32_t)l0, (uint32_t)l1);
-}
-
-// Four floats (|x| <= 448) -> e4m3 hi + lo codes, one 32-bit word each.
-__device__ __forceinline__ void split_fp8x4(const float (&x)[4], uint32_t& hi, uint32_t& lo) {
+// Four floats (|x| <= 448) -> e4m3 hi + lo codes (see above), one word each.
+__device__ __forceinline__ void split_fp8x4(float x0, float x1, float x2, float x3,
+                                            uint32_t& hi, uint32_t& lo) {
   int h = 0, l = 0;
-  h = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], h, false);
-  h = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], h, true);
+  h = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, h, false);
+  h = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, h, true);
   const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(h, false);
   const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(h, true);
-  l = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] - a[0], x[1] - a[1], l, false);
-  l = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] - b[0], x[3] - b[1], l, true);
+  l = __builtin_amdgcn_cvt_pk_fp8_f32(x0 - a[0], x1 - a[1], l, false);
+  l = __builtin_amdgcn_cvt_pk_fp8_f32(x2 - b[0], x3 - b[1], l, true);
   hi = (uint32_t)h;
   lo = (uint32_t)l;
 }
 
 __device__ __forceinline__ f32x4 mfma_fp8(fp8x8 a, fp8x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, 0, 0, 0);
+}
+// fp8 x fp8, 128 k-values, block scales 2^0 (e8m0 code 127).
+__device__ __forceinline__ f32x4 mfma_fp8_k128(fp8x32 a, fp8x32 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+__device__ __forceinline__ fp8x32 join16(u32x4 a, u32x4 b) {
+  return fp8x32{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
 }
 
 template <bool PAGED>
@@ -704,7 +736,6 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a
   const int tok_last = item.tok_end - 1;
   const int ntiles = (item.tok_end - item.tok_begin + kCTile - 1) / kCTile;
   const int64_t seq_base = a.kv_indptr[b];  // first row, or first page slot
-  const float kv_scale = *a.kv_scale;
 
   int page0 = 0;
   if constexpr (PAGED) {
@@ -715,51 +746,54 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a
     __syncthreads();
   }
 
-  // This lane's slot in each of its wave's nine loads of a tile: tile row and
-  // chunk, and (contiguous cache) the byte offset of that chunk in the tile.
-  uint32_t rc[kCLoadsPerWave], off[kCLoadsPerWave];
+  // This lane's slot in each of its wave's 18 loads of a tile: (tile row << 8)
+  // | chunk.  Load j = 4q + e of a group goes to LDS m0_q + 1024 e.
+  uint32_t rc[kCLoadsPerWave];
 #pragma unroll
   for (int j = 0; j < kCLoadsPerWave; ++j) {
     const int s = 64 * (kCLoadsPerWave * wave + j) + lane;
     const int r = s / 36;
     const int c = (s - 36 * r) ^ chunk_swz(r);
     rc[j] = (uint32_t)(r << 8 | c);
-    off[j] = (uint32_t)(r * kQkDim + 16 * c);
   }
   const uint32_t ring0 = lds_u32(&sh.tile[0][0]) + 1024 * kCLoadsPerWave * wave;
 
-  // Issue this wave's loads of tile t into ring slot t % 4.  Rows past the
+  // Issue this wave's 18 loads of tile t into ring slot t % 2.  Rows past the
   // item's last token fetch that token's row (finite data, masked later).
   auto issue = [&](int t) {
     const int tok0 = item.tok_begin + t * kCTile;
     const int lim = tok_last - tok0;  // last valid tile row
     const uint32_t m0 = ring0 + (uint32_t)((t & (kCRing - 1)) * kCTileBytes);
     if constexpr (!PAGED) {
-      const uint8_t* base = uniform_ptr(a.kv + (seq_base + tok0) * kQkDim);
-      if (lim >= kCTile - 1) {
+      // base 3072 bytes before the tile, so that no per-lane offset (which
+      // excludes the instruction offset of up to 3072) is negative
+      const uint8_t* base = uniform_ptr(a.kv + (seq_base + tok0) * kQkDim - 3072);
+      uint32_t off[kCLoadsPerWave];
 #pragma unroll
-        for (int j = 0; j < kCLoadsPerWave; ++j) dma16(base, off[j], m0 + 1024 * j);
-      } else {
-#pragma unroll
-        for (int j = 0; j < kCLoadsPerWave; ++j) {
-          const uint32_t r = min((int)(rc[j] >> 8), lim);
-          dma16(base, r * kQkDim + 16 * (rc[j] & 0xFF), m0 + 1024 * j);
-        }
+      for (int j = 0; j < kCLoadsPerWave; ++j) {
+        const uint32_t r = min((int)(rc[j] >> 8), lim);
+        off[j] = r * kQkDim + 16 * (rc[j] & 0xFF) + 3072 - 1024 * (j & 3);
       }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dma_group<4>(base, off + 4 * q, m0 + 4096 * q);
+      dma_group<2>(base, off + 16, m0 + 4096 * 4);
     } else {
       const int pmask = (1 << a.page_shift) - 1;
+      const uint8_t* src[kCLoadsPerWave];
 #pragma unroll
       for (int j = 0; j < kCLoadsPerWave; ++j) {
         const int tok = tok0 + min((int)(rc[j] >> 8), lim);
         const uint32_t page = (uint32_t)sh.pages[(tok >> a.page_shift) - page0];
         const int64_t row = (int64_t)((page << a.page_shift) + (uint32_t)(tok & pmask));
-        dma16(a.kv + row * kQkDim + 16 * (rc[j] & 0xFF), m0 + 1024 * j);
+        src[j] = a.kv + row * kQkDim + 16 * (rc[j] & 0xFF) - 1024 * (j & 3);
       }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dma_group<4>(src + 4 * q, m0 + 4096 * q);
+      dma_group<2>(src + 16, m0 + 4096 * 4);
     }
   };
 
-  // The query: 18 loads into ring slot 3 (load k by wave k % 4), then the
-  // first three tiles.
+  // The query: 18 loads into ring slot 1 (load k by wave k % 4), then tile 0.
   {
     const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(a.q + (int64_t)b * kNumHeads * kQkDim);
     const uint32_t qm0 = lds_u32(&sh.tile[kCRing - 1][0]);
@@ -767,27 +801,32 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a
       const int s = 64 * k + lane;
       const int h = s / 72;
       const int c = (s - 72 * h) ^ (h & 7);
-      dma16(qsrc + (h * 72 + c) * 16, qm0 + 1024 * k);
+      dma_one(qsrc + (h * 72 + c) * 16, qm0 + 1024 * k);
     }
   }
-  const int npre = min(ntiles, kCRing - 1);
-  for (int t = 0; t < npre; ++t) issue(t);
-  wait_tiles(npre);  // this wave's query loads have landed
-  lds_barrier();     // ... and everyone's
+  issue(0);
+  wait_loads<kCLoadsPerWave>();  // this wave's query loads have landed
+  lds_barrier();                 // ... and everyone's
+  const float kv_scale = *a.kv_scale;
 
-  // Query as the B operand of S^T = K Q^T: lane (head r16, group g) holds,
-  // for k-step 2j+h, q[head][64j + 16g + 8h .. +8], scaled by 2^s and split
-  // into e4m3 hi + lo.
-  fp8x8 qh[18], ql[18];
+  // Query, B operand of S^T = K Q^T, scaled by 2^s and split into e4m3
+  // hi + lo: for 128-column block K (0..3) lane (head r16, group g) holds
+  // q[head][128K + 32g .. +32]; for the rope columns, k-step h (0, 1),
+  // q[head][512 + 16g + 8h .. +8].
+  fp8x32 qh[4], ql[4];
+  fp8x8 rh[2], rl[2];
   float xscale;
   {
     const uint8_t* qlds = &sh.tile[kCRing - 1][0];
-    bf16x8 qv[18];
+    bf16x8 qv[18];  // [4K + i]: chunk 16K + 4g + i; [16 + h]: chunk 64 + 2g + h
 #pragma unroll
-    for (int j = 0; j < 9; ++j) {
-      qv[2 * j] = *reinterpret_cast<const bf16x8*>(qlds + 16 * q_slot(r16, 8 * j + 2 * g));
-      qv[2 * j + 1] = *reinterpret_cast<const bf16x8*>(qlds + 16 * q_slot(r16, 8 * j + 2 * g + 1));
-    }
+    for (int K = 0; K < 4; ++K)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        qv[4 * K + i] = *reinterpret_cast<const bf16x8*>(qlds + 16 * q_slot(r16, 16 * K + 4 * g + i));
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      qv[16 + h] = *reinterpret_cast<const bf16x8*>(qlds + 16 * q_slot(r16, 64 + 2 * g + h));
     float amax = 0.f;
 #pragma unroll
     for (int k = 0; k < 18; ++k)
@@ -797,12 +836,25 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a
     // 2^s with amax * 2^s in [128, 256)
     const int s = (amax > 0.f) ? 8 - __builtin_amdgcn_frexp_expf(amax) : 0;
     xscale = a.score_scale * kv_scale * __builtin_ldexpf(1.0f, -s);
+    uint32_t hw[36], lw[36];  // word 2k + m: elements 4m..4m+3 of qv[k]
 #pragma unroll
-    for (int k = 0; k < 18; ++k) {
-      float x[8];
+    for (int k = 0; k < 18; ++k)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = __builtin_ldexpf((float)qv[k][e], s);
-      split_fp8x8(x, qh[k], ql[k]);
+      for (int m = 0; m < 2; ++m)
+        split_fp8x4(__builtin_ldexpf((float)qv[k][4 * m], s), __builtin_ldexpf((float)qv[k][4 * m + 1], s),
+                    __builtin_ldexpf((float)qv[k][4 * m + 2], s), __builtin_ldexpf((float)qv[k][4 * m + 3], s),
+                    hw[2 * k + m], lw[2 * k + m]);
+#pragma unroll
+    for (int K = 0; K < 4; ++K)
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        qh[K][d] = (int)hw[8 * K + d];
+        ql[K][d] = (int)lw[8 * K + d];
+      }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      rh[h] = pack_fp8x8(hw[32 + 2 * h], hw[33 + 2 * h]);
+      rl[h] = pack_fp8x8(lw[32 + 2 * h], lw[33 + 2 * h]);
     }
   }
 
@@ -812,66 +864,91 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a
   float m_ref = kNegInf;  // shared running maximum (log2 units) of head r16
   float l_part = 0.f;     // this lane's share of the running sum
 
-  // LDS byte offsets of this lane's reads within a tile.
-  const int k_row = 16 * wave + r16;
-  const int k_off = k_row * kQkDim + 16 * (g ^ chunk_swz(k_row));
-  int v_off[2][4];  // [k-step][v % 4]; + 64 (v / 4)
+  // LDS byte offsets of this lane's reads within a tile.  Score rows
+  // 32w + 16s + r16 have chunk_swz(r16) and value rows 32g + 8q + (r16 >> 1)
+  // have chunk_swz(r16 >> 1), whatever s, q and g.
+  const int ksw = chunk_swz(r16);
+  const int k_row = (32 * wave + r16) * kQkDim;
+  const int k_off0 = k_row + 16 * ((2 * g) ^ ksw);      // chunk 8K + 2g
+  const int k_off1 = k_row + 16 * ((2 * g + 1) ^ ksw);  // chunk 8K + 2g + 1
+  const int k_offr = k_row + 16 * (32 + (g ^ ksw));     // chunk 32 + g
+  const int vsw = chunk_swz(r16 >> 1);
+  int v_off[4];  // + 64 (v / 4) + 4608 q; column chunk 8w + v
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
-    const int row = 32 * kt + 8 * g + (r16 >> 1);
-#pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4)
-      v_off[kt][c4] = row * kQkDim + 16 * (8 * wave + (c4 ^ chunk_swz(row))) + 8 * (r16 & 1);
-  }
+  for (int c4 = 0; c4 < 4; ++c4)
+    v_off[c4] = (32 * g + (r16 >> 1)) * kQkDim + 16 * (8 * wave + (c4 ^ vsw)) + 8 * (r16 & 1);
   uint8_t* const p_hi = &sh.p[0][r16][0];
   uint8_t* const p_lo = &sh.p[1][r16][0];
 
   for (int t = 0; t < ntiles; ++t) {
     const int tok0 = item.tok_begin + t * kCTile;
-    wait_tiles(min(ntiles - 1 - t, kCRing - 2));  // this wave's part of tile t
-    lds_barrier();  // all of tile t; everyone is past tile t-1 (and the query)
-    if (t + kCRing - 1 < ntiles) issue(t + kCRing - 1);
+    wait_loads<0>();  // this wave's part of tile t
+    lds_barrier();    // all of tile t; everyone is past tile t-1 (and the query)
+    if (t + 1 < ntiles) issue(t + 1);
     const uint8_t* cur = &sh.tile[t & (kCRing - 1)][0];
 
-    // ---- scores of tokens 16w..16w+15 ----
-    f32x4 sacc[4];
+    // ---- scores of tokens 32w + 16s + (0..15), s = 0, 1 ----
+    f32x4 sacc[2][2];  // [s][hi/lo]
 #pragma unroll
-    for (int c = 0; c < 4; ++c) sacc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < 2; ++s)
 #pragma unroll
-    for (int j = 0; j < 9; ++j) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(cur + k_off + 64 * j);
-      const fp8x8 ka = pack_fp8x8(w[0], w[1]);  // k-step 2j
-      const fp8x8 kb = pack_fp8x8(w[2], w[3]);  // k-step 2j+1
-      sacc[0] = mfma_fp8(ka, qh[2 * j], sacc[0]);
-      sacc[1] = mfma_fp8(ka, ql[2 * j], sacc[1]);
-      sacc[2] = mfma_fp8(kb, qh[2 * j + 1], sacc[2]);
-      sacc[3] = mfma_fp8(kb, ql[2 * j + 1], sacc[3]);
+      for (int c = 0; c < 2; ++c) sacc[s][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int K = 0; K < 4; ++K) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int ro = s * 16 * kQkDim + 128 * K;
+        const fp8x32 ka = join16(*reinterpret_cast<const u32x4*>(cur + k_off0 + ro),
+                                 *reinterpret_cast<const u32x4*>(cur + k_off1 + ro));
+        sacc[s][0] = mfma_fp8_k128(ka, qh[K], sacc[s][0]);
+        sacc[s][1] = mfma_fp8_k128(ka, ql[K], sacc[s][1]);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(cur + k_offr + s * 16 * kQkDim);
+      const fp8x8 ka = pack_fp8x8(w[0], w[1]);
+      const fp8x8 kb = pack_fp8x8(w[2], w[3]);
+      sacc[s][0] = mfma_fp8(ka, rh[0], sacc[s][0]);
+      sacc[s][1] = mfma_fp8(ka, rl[0], sacc[s][1]);
+      sacc[s][0] = mfma_fp8(kb, rh[1], sacc[s][0]);
+      sacc[s][1] = mfma_fp8(kb, rl[1], sacc[s][1]);
     }
 
-    // ---- softmax: element i is token 16w + 4g + i of head r16 ----
-    float x[4];
+    // ---- softmax: x[s][i] is token 32w + 16s + 4g + i of head r16 ----
+    float x[2][4];
     float tmax = kNegInf;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[i] = ((sacc[0][i] + sacc[1][i]) + (sacc[2][i] + sacc[3][i])) * xscale;
-      if (tok0 + 16 * wave + 4 * g + i > tok_last) x[i] = kNegInf;
-      tmax = fmaxf(tmax, x[i]);
-    }
-    tmax = xor_max_groups(tmax);
-    if (g == 0) sh.red_m[wave][r16] = tmax;
-    float p[4];
-    uint32_t ph, pl;
-    const float mr = (m_ref == kNegInf) ? 0.0f : m_ref;
+    for (int s = 0; s < 2; ++s)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - mr);
-    split_fp8x4(p, ph, pl);
-    *reinterpret_cast<uint32_t*>(p_hi + 16 * wave + 4 * g) = ph;
-    *reinterpret_cast<uint32_t*>(p_lo + 16 * wave + 4 * g) = pl;
+      for (int i = 0; i < 4; ++i) {
+        x[s][i] = (sacc[s][0][i] + sacc[s][1][i]) * xscale;
+        if (tok0 + 32 * wave + 16 * s + 4 * g + i > tok_last) x[s][i] = kNegInf;
+        tmax = fmaxf(tmax, x[s][i]);
+      }
+    tmax = xor_max_groups(tmax);
+    if (g == 0) sh.red_m[r16][wave] = tmax;
+    float p[2][4];
+    uint32_t ph[2], pl[2];
+    {
+      const float mr = (m_ref == kNegInf) ? 0.0f : m_ref;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[s][i] = __builtin_amdgcn_exp2f(x[s][i] - mr);
+        split_fp8x4(p[s][0], p[s][1], p[s][2], p[s][3], ph[s], pl[s]);
+        *reinterpret_cast<uint32_t*>(p_hi + 32 * wave + 16 * s + 4 * g) = ph[s];
+        *reinterpret_cast<uint32_t*>(p_lo + 32 * wave + 16 * s + 4 * g) = pl[s];
+      }
+    }
     lds_barrier();  // P^T and the tile maxima of all waves
 
-    float tile_max = sh.red_m[0][r16];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) tile_max = fmaxf(tile_max, sh.red_m[w][r16]);
+    const f32x4 maxima = *reinterpret_cast<const f32x4*>(&sh.red_m[r16][0]);
+    fp8x32 bh = join16(*reinterpret_cast<const u32x4*>(p_hi + 32 * g),
+                       *reinterpret_cast<const u32x4*>(p_hi + 32 * g + 16));
+    fp8x32 bl = join16(*reinterpret_cast<const u32x4*>(p_lo + 32 * g),
+                       *reinterpret_cast<const u32x4*>(p_lo + 32 * g + 16));
+    const float tile_max = fmaxf(fmaxf(maxima[0], maxima[1]), fmaxf(maxima[2], maxima[3]));
     // Every wave reads the same maxima, so this branch is uniform.
     if (__ballot(tile_max > m_ref + kLazyRescale) != 0) {
       const float m_new = fmaxf(m_ref, tile_max);
@@ -880,39 +957,50 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a
       for (int v = 0; v < 8; ++v) o[v] *= alpha;
       l_part *= alpha;
       m_ref = m_new;
+      lds_barrier();  // everyone has read the old P^T
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - m_ref);
-      split_fp8x4(p, ph, pl);
-      lds_barrier();  // everyone has read the maxima before they are rewritten
-      *reinterpret_cast<uint32_t*>(p_hi + 16 * wave + 4 * g) = ph;
-      *reinterpret_cast<uint32_t*>(p_lo + 16 * wave + 4 * g) = pl;
-      lds_barrier();
-    }
-    l_part += (p[0] + p[1]) + (p[2] + p[3]);
-
-    // ---- O^T += V^T P^T over the 64 tokens ----
+      for (int s = 0; s < 2; ++s) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const fp8x8 bh = *reinterpret_cast<const fp8x8*>(p_hi + 32 * kt + 8 * g);
-      const fp8x8 bl = *reinterpret_cast<const fp8x8*>(p_lo + 32 * kt + 8 * g);
-#pragma unroll
-      for (int v = 0; v < 8; ++v) {
-        const i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (lds_i32x2*)(cur + v_off[kt][v & 3] + 64 * (v >> 2)));
-        const fp8x8 va = pack_fp8x8((uint32_t)raw[0], (uint32_t)raw[1]);
-        o[v] = mfma_fp8(va, bh, o[v]);
-        o[v] = mfma_fp8(va, bl, o[v]);
+        for (int i = 0; i < 4; ++i) p[s][i] = __builtin_amdgcn_exp2f(x[s][i] - m_ref);
+        split_fp8x4(p[s][0], p[s][1], p[s][2], p[s][3], ph[s], pl[s]);
+        *reinterpret_cast<uint32_t*>(p_hi + 32 * wave + 16 * s + 4 * g) = ph[s];
+        *reinterpret_cast<uint32_t*>(p_lo + 32 * wave + 16 * s + 4 * g) = pl[s];
       }
+      lds_barrier();
+      bh = join16(*reinterpret_cast<const u32x4*>(p_hi + 32 * g),
+                  *reinterpret_cast<const u32x4*>(p_hi + 32 * g + 16));
+      bl = join16(*reinterpret_cast<const u32x4*>(p_lo + 32 * g),
+                  *reinterpret_cast<const u32x4*>(p_lo + 32 * g + 16));
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) l_part += (p[s][0] + p[s][1]) + (p[s][2] + p[s][3]);
+
+    // ---- O^T += V^T P^T over the 128 tokens, two column tiles at a time ----
+#pragma unroll
+    for (int v = 0; v < 8; v += 2) {
+      fp8x32 va[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (lds_i32x2*)(cur + v_off[(v + u) & 3] + 64 * ((v + u) >> 2) + 8 * kQkDim * q));
+          va[u][2 * q] = raw[0];
+          va[u][2 * q + 1] = raw[1];
+        }
+      o[v] = mfma_fp8_k128(va[0], bh, o[v]);
+      o[v + 1] = mfma_fp8_k128(va[1], bh, o[v + 1]);
+      o[v] = mfma_fp8_k128(va[0], bl, o[v]);
+      o[v + 1] = mfma_fp8_k128(va[1], bl, o[v + 1]);
     }
   }
 
   // ---- sums over the item; each wave writes its 128 columns ----
   const float l_w = xor_sum_groups(l_part);
-  if (g == 0) sh.red_l[wave][r16] = l_w;
+  if (g == 0) sh.red_l[r16][wave] = l_w;
   lds_barrier();
-  float L = 0.f;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) L += sh.red_l[w][r16];
+  const f32x4 ls = *reinterpret_cast<const f32x4*>(&sh.red_l[r16][0]);
+  const float L = (ls[0] + ls[1]) + (ls[2] + ls[3]);
   const float f = kv_scale / L;
   const int dim0 = 128 * wave + 4 * g;
   if (item.slot < 0) {
