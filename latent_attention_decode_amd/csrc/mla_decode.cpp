@@ -33,7 +33,7 @@ struct mla_decode_s {
   int64_t total_tokens = 0;
   size_t workspace_bytes = 0;
   int num_merge = 0;  // sequences with >= 2 partials
-  // device: [num_items] WorkItem, [batch] SeqInfo, [num_merge] int32 sequence ids
+  // device: [num_items] WorkItem, [num_merge] MergeSeq
   void* dev_plan = nullptr;
   size_t dev_plan_bytes = 0;
   int num_cus = 0;
@@ -121,7 +121,7 @@ static bool seq_lengths(const int32_t* indptr, const int32_t* last, int batch, i
   return true;
 }
 
-// The split planner.  Items are whole 64-token tiles (the last item of a
+// The split planner.  Items are whole 128-token tiles (the last item of a
 // sequence may end mid-tile).  With C compute units holding W workgroups
 // each, the auto plan aims at C*W items of equal size for uniform batches (one
 // wave of workgroups, nothing idle) and four times as many for ragged ones
@@ -130,8 +130,7 @@ static bool seq_lengths(const int32_t* indptr, const int32_t* last, int batch, i
 // sequences get an item of their own that writes the zero output.
 struct PlanOut {
   std::vector<WorkItem> items;
-  std::vector<SeqInfo> seqs;
-  std::vector<int32_t> merge_seqs;
+  std::vector<MergeSeq> merge;
   int num_slots = 0;
   int max_splits = 0;
 };
@@ -140,14 +139,14 @@ static int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 // An item of fewer than two tiles has no load/compute overlap; each (sequence,
 // head) is merged by one workgroup, so the number of partials stays small.
-constexpr int64_t kMinItemTokens = 4 * kTile;
+constexpr int64_t kMinItemTokens = 2 * kPlanTile;
 constexpr int64_t kMaxAutoSplits = 32;
 constexpr int64_t kMaxItemPages = 512;  // LDS staging of one item's page ids (mla_kernels.hip)
 
 static void plan_items(const std::vector<int64_t>& lens, int split_override, int num_cus,
                        int blocks_per_cu, int page_size, PlanOut* out) {
   const int batch = static_cast<int>(lens.size());
-  const int64_t tile = 2 * kTile;  // tokens per stage-1 iteration
+  const int64_t tile = kPlanTile;
   int64_t total = 0, max_len = 0, nonempty = 0;
   for (int64_t n : lens) {
     total += n;
@@ -180,8 +179,7 @@ static void plan_items(const std::vector<int64_t>& lens, int split_override, int
     }
   }
   out->items.clear();
-  out->merge_seqs.clear();
-  out->seqs.assign(batch, SeqInfo{0, 0});
+  out->merge.clear();
   out->num_slots = 0;
   out->max_splits = 0;
   for (int b = 0; b < batch; ++b) {
@@ -196,8 +194,7 @@ static void plan_items(const std::vector<int64_t>& lens, int split_override, int
       out->items.push_back(WorkItem{b, 0, static_cast<int32_t>(lens[b]), WorkItem::kWhole});
       continue;
     }
-    out->seqs[b] = SeqInfo{out->num_slots, static_cast<int32_t>(ns)};
-    out->merge_seqs.push_back(b);
+    out->merge.push_back(MergeSeq{b, out->num_slots, static_cast<int32_t>(ns), 0});
     for (int64_t s = 0; s < ns; ++s) {
       const int64_t t0 = s * chunk[b];
       const int64_t t1 = std::min(lens[b], t0 + chunk[b]);
@@ -285,9 +282,8 @@ mla_status mla_decode_plan(mla_decode_t h, int batch, const int32_t* kv_indptr_h
   mla::plan_items(lens, split_override, h->num_cus, h->blocks_per_cu, h->page_size, &plan);
 
   const size_t items_bytes = plan.items.size() * sizeof(mla::WorkItem);
-  const size_t seqs_bytes = plan.seqs.size() * sizeof(mla::SeqInfo);
-  const size_t merge_bytes = plan.merge_seqs.size() * sizeof(int32_t);
-  const size_t need = items_bytes + seqs_bytes + merge_bytes;
+  const size_t merge_bytes = plan.merge.size() * sizeof(mla::MergeSeq);
+  const size_t need = items_bytes + merge_bytes;
   if (need > h->dev_plan_bytes) {
     if (h->dev_plan) (void)hipFree(h->dev_plan);
     h->dev_plan = nullptr;
@@ -298,9 +294,7 @@ mla_status mla_decode_plan(mla_decode_t h, int batch, const int32_t* kv_indptr_h
   }
   std::vector<unsigned char> blob(need, 0);
   if (items_bytes) std::memcpy(blob.data(), plan.items.data(), items_bytes);
-  std::memcpy(blob.data() + items_bytes, plan.seqs.data(), seqs_bytes);
-  if (merge_bytes)
-    std::memcpy(blob.data() + items_bytes + seqs_bytes, plan.merge_seqs.data(), merge_bytes);
+  if (merge_bytes) std::memcpy(blob.data() + items_bytes, plan.merge.data(), merge_bytes);
   if (hipMemcpy(h->dev_plan, blob.data(), need, hipMemcpyHostToDevice) != hipSuccess)
     return fail(h, MLA_ERR_HIP, "uploading the work list failed");
 
@@ -308,7 +302,7 @@ mla_status mla_decode_plan(mla_decode_t h, int batch, const int32_t* kv_indptr_h
   h->num_items = static_cast<int>(plan.items.size());
   h->num_slots = plan.num_slots;
   h->max_splits = plan.max_splits;
-  h->num_merge = static_cast<int>(plan.merge_seqs.size());
+  h->num_merge = static_cast<int>(plan.merge.size());
   h->total_tokens = 0;
   for (int64_t n : lens) h->total_tokens += n;
   h->workspace_bytes = static_cast<size_t>(plan.num_slots) * slot_bytes();
@@ -399,7 +393,6 @@ mla_status mla_decode_run(mla_decode_t h, const void* q, const void* kv, const v
   a.page_shift = h->page_shift;
   unsigned char* plan_base = static_cast<unsigned char*>(h->dev_plan);
   const size_t items_bytes = static_cast<size_t>(h->num_items) * sizeof(mla::WorkItem);
-  const size_t seqs_bytes = static_cast<size_t>(h->batch) * sizeof(mla::SeqInfo);
   a.items = reinterpret_cast<const mla::WorkItem*>(plan_base);
   a.part_o = static_cast<float*>(workspace);
   a.part_lse = h->num_slots
@@ -421,8 +414,7 @@ mla_status mla_decode_run(mla_decode_t h, const void* q, const void* kv, const v
     return fail(h, MLA_ERR_HIP, "hipEventRecord failed");
   if (h->num_merge > 0) {
     mla::MergeArgs m{};
-    m.seqs = reinterpret_cast<const mla::SeqInfo*>(plan_base + items_bytes);
-    m.merge_seqs = reinterpret_cast<const int32_t*>(plan_base + items_bytes + seqs_bytes);
+    m.work = reinterpret_cast<const mla::MergeSeq*>(plan_base + items_bytes);
     m.part_o = a.part_o;
     m.part_lse = a.part_lse;
     m.out = a.out;

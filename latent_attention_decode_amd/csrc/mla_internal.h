@@ -12,7 +12,8 @@ namespace mla {
 constexpr int kNumHeads = 16;
 constexpr int kQkDim = 576;
 constexpr int kVDim = 512;
-constexpr int kTile = 32;        // tokens one wave consumes per main-loop iteration
+constexpr int kTile = 32;        // token granularity of the planner's splits
+constexpr int kPlanTile = 128;   // tokens per stage-1 tile (fp8); items are whole tiles
 constexpr int kWaves = 4;        // waves per stage-1 workgroup
 constexpr int kStage1Threads = 64 * kWaves;
 constexpr int kMergeThreads = kVDim / 4;  // one float4 of one head per thread
@@ -33,10 +34,13 @@ struct WorkItem {
   static constexpr int32_t kEmpty = -2;
 };
 
-// Per sequence: its partial slots are [slot_begin, slot_begin + nslots).
-struct SeqInfo {
+// One merge job: the partials of sequence `batch` are slots
+// [slot_begin, slot_begin + nslots), nslots >= 2.
+struct MergeSeq {
+  int32_t batch;
   int32_t slot_begin;
   int32_t nslots;
+  int32_t pad;
 };
 
 struct Stage1Args {
@@ -56,8 +60,7 @@ struct Stage1Args {
 };
 
 struct MergeArgs {
-  const int32_t* merge_seqs;    // the sequences with >= 2 partials
-  const SeqInfo* seqs;          // [batch]
+  const MergeSeq* work;         // the sequences with >= 2 partials
   const float* part_o;
   const float* part_lse;
   uint16_t* out;

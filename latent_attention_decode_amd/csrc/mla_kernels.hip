@@ -735,6 +735,20 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a
   const int b = item.batch;
   const int tok_last = item.tok_end - 1;
   const int ntiles = (item.tok_end - item.tok_begin + kCTile - 1) / kCTile;
+  const float kv_scale = *a.kv_scale;
+
+  // The query first (it needs only the sequence id): 18 loads into ring slot
+  // 1, load k by wave k % 4.
+  {
+    const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(a.q + (int64_t)b * kNumHeads * kQkDim);
+    const uint32_t qm0 = lds_u32(&sh.tile[kCRing - 1][0]);
+    for (int k = wave; k < kQLoads; k += kWaves) {
+      const int s = 64 * k + lane;
+      const int h = s / 72;
+      const int c = (s - 72 * h) ^ (h & 7);
+      dma_one(qsrc + (h * 72 + c) * 16, qm0 + 1024 * k);
+    }
+  }
   const int64_t seq_base = a.kv_indptr[b];  // first row, or first page slot
 
   int page0 = 0;
@@ -758,9 +772,11 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a
   }
   const uint32_t ring0 = lds_u32(&sh.tile[0][0]) + 1024 * kCLoadsPerWave * wave;
 
-  // Issue this wave's 18 loads of tile t into ring slot t % 2.  Rows past the
-  // item's last token fetch that token's row (finite data, masked later).
-  auto issue = [&](int t) {
+  // Issue part `part` of this wave's 18 loads of tile t into ring slot t % 2:
+  // loads 4 part .. 4 part + 3 (part 0..3), loads 16 and 17 (part 4), or all
+  // of them (part -1).  Rows past the item's last token fetch that token's row
+  // (finite data, masked later).
+  auto issue = [&](int t, int part) {
     const int tok0 = item.tok_begin + t * kCTile;
     const int lim = tok_last - tok0;  // last valid tile row
     const uint32_t m0 = ring0 + (uint32_t)((t & (kCRing - 1)) * kCTileBytes);
@@ -775,8 +791,9 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a
         off[j] = r * kQkDim + 16 * (rc[j] & 0xFF) + 3072 - 1024 * (j & 3);
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) dma_group<4>(base, off + 4 * q, m0 + 4096 * q);
-      dma_group<2>(base, off + 16, m0 + 4096 * 4);
+      for (int q = 0; q < 4; ++q)
+        if (part < 0 || part == q) dma_group<4>(base, off + 4 * q, m0 + 4096 * q);
+      if (part < 0 || part == 4) dma_group<2>(base, off + 16, m0 + 4096 * 4);
     } else {
       const int pmask = (1 << a.page_shift) - 1;
       const uint8_t* src[kCLoadsPerWave];
@@ -788,26 +805,15 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a
         src[j] = a.kv + row * kQkDim + 16 * (rc[j] & 0xFF) - 1024 * (j & 3);
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) dma_group<4>(src + 4 * q, m0 + 4096 * q);
-      dma_group<2>(src + 16, m0 + 4096 * 4);
+      for (int q = 0; q < 4; ++q)
+        if (part < 0 || part == q) dma_group<4>(src + 4 * q, m0 + 4096 * q);
+      if (part < 0 || part == 4) dma_group<2>(src + 16, m0 + 4096 * 4);
     }
   };
 
-  // The query: 18 loads into ring slot 1 (load k by wave k % 4), then tile 0.
-  {
-    const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(a.q + (int64_t)b * kNumHeads * kQkDim);
-    const uint32_t qm0 = lds_u32(&sh.tile[kCRing - 1][0]);
-    for (int k = wave; k < kQLoads; k += kWaves) {
-      const int s = 64 * k + lane;
-      const int h = s / 72;
-      const int c = (s - 72 * h) ^ (h & 7);
-      dma_one(qsrc + (h * 72 + c) * 16, qm0 + 1024 * k);
-    }
-  }
-  issue(0);
+  issue(0, -1);
   wait_loads<kCLoadsPerWave>();  // this wave's query loads have landed
   lds_barrier();                 // ... and everyone's
-  const float kv_scale = *a.kv_scale;
 
   // Query, B operand of S^T = K Q^T, scaled by 2^s and split into e4m3
   // hi + lo: for 128-column block K (0..3) lane (head r16, group g) holds
@@ -884,7 +890,10 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a
     const int tok0 = item.tok_begin + t * kCTile;
     wait_loads<0>();  // this wave's part of tile t
     lds_barrier();    // all of tile t; everyone is past tile t-1 (and the query)
-    if (t + 1 < ntiles) issue(t + 1);
+    // Tile t+1 goes into the other slot in five parts spread over this tile's
+    // work, so that the loads queue while the matrix cores run.
+    const bool more = t + 1 < ntiles;
+    if (more) issue(t + 1, 0);
     const uint8_t* cur = &sh.tile[t & (kCRing - 1)][0];
 
     // ---- scores of tokens 32w + 16s + (0..15), s = 0, 1 ----
@@ -903,6 +912,7 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a
         sacc[s][0] = mfma_fp8_k128(ka, qh[K], sacc[s][0]);
         sacc[s][1] = mfma_fp8_k128(ka, ql[K], sacc[s][1]);
       }
+      if (more && (K == 1 || K == 3)) issue(t + 1, K == 1 ? 1 : 2);
     }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -941,6 +951,7 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a
         *reinterpret_cast<uint32_t*>(p_lo + 32 * wave + 16 * s + 4 * g) = pl[s];
       }
     }
+    if (more) issue(t + 1, 3);
     lds_barrier();  // P^T and the tile maxima of all waves
 
     const f32x4 maxima = *reinterpret_cast<const f32x4*>(&sh.red_m[r16][0]);
@@ -992,6 +1003,7 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a
       o[v + 1] = mfma_fp8_k128(va[1], bh, o[v + 1]);
       o[v] = mfma_fp8_k128(va[0], bl, o[v]);
       o[v + 1] = mfma_fp8_k128(va[1], bl, o[v + 1]);
+      if (more && v == 2) issue(t + 1, 4);
     }
   }
 
@@ -1030,10 +1042,10 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a
 constexpr int kMergeBatch = 8;
 
 __global__ __launch_bounds__(kMergeThreads) void mla_merge(MergeArgs a) {
-  const int b = a.merge_seqs[blockIdx.x / kNumHeads];
+  const MergeSeq seq = a.work[blockIdx.x / kNumHeads];
+  const int b = seq.batch;
   const int h = blockIdx.x % kNumHeads;
   const int d = threadIdx.x * 4;
-  const SeqInfo seq = a.seqs[b];
   const float* lse = a.part_lse + (int64_t)seq.slot_begin * kNumHeads + h;
   const f32x4* po = reinterpret_cast<const f32x4*>(
                         a.part_o + ((int64_t)seq.slot_begin * kNumHeads + h) * kVDim + d);
