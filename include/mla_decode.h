@@ -100,7 +100,7 @@ mla_status mla_decode_create(mla_decode_t* out, int device, int num_heads, int q
 
 /*
  * Plan a batch: splits every sequence into work items (token ranges, whole
- * 64-token tiles except at a sequence's end) sized against the device's
+ * 128-token tiles except at a sequence's end) sized against the device's
  * compute-unit count and the stage-1 kernel's residency, uploads the
  * work list to the device (synchronously) and reports the workspace size the
  * run needs (bytes; may be 0).  kv_indptr_host has batch+1 entries (tokens if
@@ -109,7 +109,9 @@ mla_status mla_decode_create(mla_decode_t* out, int device, int num_heads, int q
  * (may be NULL) otherwise.  split_override > 0 forces that many items per
  * non-empty sequence (at most one per 32 tokens); 0 lets the planner choose.
  * The plan stays valid until the next plan or destroy; the device copies of
- * kv_indptr / kv_last_page_len passed to run must hold the same values.
+ * kv_indptr / kv_last_page_len passed to run must hold the same values (the
+ * work list carries each sequence's kv_indptr entry as planned, and the
+ * kernels address the cache through it).
  */
 mla_status mla_decode_plan(mla_decode_t h, int batch, const int32_t* kv_indptr_host,
                            const int32_t* kv_last_page_len_host, int split_override,
@@ -162,8 +164,9 @@ mla_status mla_decode_run(mla_decode_t h, const void* q, const void* kv, const v
                           void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Kernel timing for measurement.  While enabled, mla_decode_run records a HIP
- * event before and after each of its kernel launches on the run's stream;
+ * Kernel timing for measurement.  While enabled, mla_decode_run launches its
+ * kernels with a pair of HIP events each, which the launch itself records
+ * when the kernel starts and when it ends (hipExtLaunchKernel);
  * mla_decode_kernel_time_ms then waits for the last run's events and returns
  * the elapsed milliseconds of kernel `which` (0 = split stage, 1 = merge; a
  * merge that was not launched reports 0).  MLA_ERR_NOT_PLANNED if the last

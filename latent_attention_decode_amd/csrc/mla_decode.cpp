@@ -143,7 +143,8 @@ constexpr int64_t kMinItemTokens = 2 * kPlanTile;
 constexpr int64_t kMaxAutoSplits = 32;
 constexpr int64_t kMaxItemPages = 512;  // LDS staging of one item's page ids (mla_kernels.hip)
 
-static void plan_items(const std::vector<int64_t>& lens, int split_override, int num_cus,
+static void plan_items(const std::vector<int64_t>& lens, const int32_t* indptr, int split_override,
+                       int num_cus,
                        int blocks_per_cu, int page_size, PlanOut* out) {
   const int batch = static_cast<int>(lens.size());
   const int64_t tile = kPlanTile;
@@ -184,14 +185,15 @@ static void plan_items(const std::vector<int64_t>& lens, int split_override, int
   out->max_splits = 0;
   for (int b = 0; b < batch; ++b) {
     if (!lens[b]) {
-      out->items.push_back(WorkItem{b, 0, 0, WorkItem::kEmpty});
+      out->items.push_back(WorkItem{b, 0, 0, WorkItem::kEmpty, indptr[b], {0, 0, 0}});
       continue;
     }
     if (chunk[b] > max_item) chunk[b] = max_item;
     const int64_t ns = (lens[b] + chunk[b] - 1) / chunk[b];
     out->max_splits = std::max<int>(out->max_splits, static_cast<int>(ns));
     if (ns == 1) {
-      out->items.push_back(WorkItem{b, 0, static_cast<int32_t>(lens[b]), WorkItem::kWhole});
+      out->items.push_back(
+          WorkItem{b, 0, static_cast<int32_t>(lens[b]), WorkItem::kWhole, indptr[b], {0, 0, 0}});
       continue;
     }
     out->merge.push_back(MergeSeq{b, out->num_slots, static_cast<int32_t>(ns), 0});
@@ -199,7 +201,7 @@ static void plan_items(const std::vector<int64_t>& lens, int split_override, int
       const int64_t t0 = s * chunk[b];
       const int64_t t1 = std::min(lens[b], t0 + chunk[b]);
       out->items.push_back(WorkItem{b, static_cast<int32_t>(t0), static_cast<int32_t>(t1),
-                                    out->num_slots + static_cast<int32_t>(s)});
+                                    out->num_slots + static_cast<int32_t>(s), indptr[b], {0, 0, 0}});
     }
     out->num_slots += static_cast<int>(ns);
   }
@@ -279,7 +281,8 @@ mla_status mla_decode_plan(mla_decode_t h, int batch, const int32_t* kv_indptr_h
   }
 
   mla::PlanOut plan;
-  mla::plan_items(lens, split_override, h->num_cus, h->blocks_per_cu, h->page_size, &plan);
+  mla::plan_items(lens, kv_indptr_host, split_override, h->num_cus, h->blocks_per_cu, h->page_size,
+                  &plan);
 
   const size_t items_bytes = plan.items.size() * sizeof(mla::WorkItem);
   const size_t merge_bytes = plan.merge.size() * sizeof(mla::MergeSeq);
@@ -325,7 +328,7 @@ mla_status mla_decode_plan_preview(int batch, const int32_t* kv_indptr_host,
   if (!mla::seq_lengths(kv_indptr_host, kv_last_page_len_host, batch, page_size, &lens, &err))
     return MLA_ERR_INVALID_ARG;
   mla::PlanOut plan;
-  mla::plan_items(lens, split_override, num_cus, blocks_per_cu, page_size, &plan);
+  mla::plan_items(lens, kv_indptr_host, split_override, num_cus, blocks_per_cu, page_size, &plan);
   const int n = static_cast<int>(plan.items.size());
   if (num_items) *num_items = n;
   if (num_slots) *num_slots = plan.num_slots;
@@ -406,24 +409,18 @@ mla_status mla_decode_run(mla_decode_t h, const void* q, const void* kv, const v
   const bool timed = h->profiling && h->events_ready;
   h->timed_run = false;
   h->merge_timed = false;
-  if (timed && hipEventRecord(h->ev[0], s) != hipSuccess)
-    return fail(h, MLA_ERR_HIP, "hipEventRecord failed");
-  hipError_t e = mla::launch_stage1(h->kv_dtype, h->page_size > 1, a, h->num_items, s);
+  hipError_t e = mla::launch_stage1(h->kv_dtype, h->page_size > 1, a, h->num_items, s,
+                                     timed ? h->ev[0] : nullptr, timed ? h->ev[1] : nullptr);
   if (e != hipSuccess) return fail(h, MLA_ERR_HIP, "stage-1 launch: %s", hipGetErrorString(e));
-  if (timed && hipEventRecord(h->ev[1], s) != hipSuccess)
-    return fail(h, MLA_ERR_HIP, "hipEventRecord failed");
   if (h->num_merge > 0) {
     mla::MergeArgs m{};
     m.work = reinterpret_cast<const mla::MergeSeq*>(plan_base + items_bytes);
     m.part_o = a.part_o;
     m.part_lse = a.part_lse;
     m.out = a.out;
-    if (timed && hipEventRecord(h->ev[2], s) != hipSuccess)
-      return fail(h, MLA_ERR_HIP, "hipEventRecord failed");
-    e = mla::launch_merge(m, h->num_merge, s);
+    e = mla::launch_merge(m, h->num_merge, s, timed ? h->ev[2] : nullptr,
+                          timed ? h->ev[3] : nullptr);
     if (e != hipSuccess) return fail(h, MLA_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
-    if (timed && hipEventRecord(h->ev[3], s) != hipSuccess)
-      return fail(h, MLA_ERR_HIP, "hipEventRecord failed");
     h->merge_timed = timed;
   }
   h->timed_run = timed;

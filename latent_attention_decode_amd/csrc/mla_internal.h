@@ -16,7 +16,7 @@ constexpr int kTile = 32;        // token granularity of the planner's splits
 constexpr int kPlanTile = 128;   // tokens per stage-1 tile (fp8); items are whole tiles
 constexpr int kWaves = 4;        // waves per stage-1 workgroup
 constexpr int kStage1Threads = 64 * kWaves;
-constexpr int kMergeThreads = kVDim / 4;  // one float4 of one head per thread
+constexpr int kMergeThreads = 256;  // two float4 of one head per thread
 
 enum KvFormat : int { kBf16 = 0, kFp8 = 1, kMxfp4 = 2 };
 
@@ -30,9 +30,12 @@ struct WorkItem {
   int32_t tok_begin;
   int32_t tok_end;
   int32_t slot;
+  int32_t kv_base;  // kv_indptr[batch] as planned
+  int32_t pad[3];
   static constexpr int32_t kWhole = -1;
   static constexpr int32_t kEmpty = -2;
 };
+static_assert(sizeof(WorkItem) == 32, "work item layout");
 
 // One merge job: the partials of sequence `batch` are slots
 // [slot_begin, slot_begin + nslots), nslots >= 2.
@@ -67,8 +70,10 @@ struct MergeArgs {
 };
 
 // Launchers (mla_kernels.hip).  Return the launch status.
-hipError_t launch_stage1(int fmt, bool paged, const Stage1Args& a, int num_items, hipStream_t s);
-hipError_t launch_merge(const MergeArgs& a, int num_merge_seqs, hipStream_t s);
+hipError_t launch_stage1(int fmt, bool paged, const Stage1Args& a, int num_items, hipStream_t s,
+                         hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
+hipError_t launch_merge(const MergeArgs& a, int num_merge_seqs, hipStream_t s,
+                        hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 // Static resources of a kernel (which: 0 stage 1 for `fmt`/`paged`, 1 merge).
 hipError_t kernel_attributes(int fmt, bool paged, int which, hipFuncAttributes* attr);
 // Resident stage-1 workgroups per compute unit.

@@ -35,6 +35,7 @@
 // Everything accumulates in fp32; the fp8 per-tensor scale is folded into the
 // score scale and the final normalisation.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -173,6 +174,18 @@ __device__ __forceinline__ float xor_sum_groups(float v) {
 // of the wave that scored the next 16 (16+4g..16+4g+3).
 __device__ __forceinline__ int pv_token(int g, int e) {
   return (e < 4) ? 4 * g + e : 16 + 4 * g + (e - 4);
+}
+
+// Layout of one partial O (a workspace slot, 16 x 512 fp32): the float4 that
+// lane l of wave w holds for column tile v (heads l % 16, dims
+// 128w + 16v + 4(l / 16) .. +3) is float4 number (8w + v) * 64 + l of the
+// slot, so that each store instruction of a wave writes 1 KB contiguously.
+constexpr int kSlotFloat4 = kNumHeads * kVDim / 4;
+__device__ __forceinline__ void store_partial(float* part_o, int slot, int wave, int lane,
+                                              const f32x4 (&o)[8], float f) {
+  f32x4* dst = reinterpret_cast<f32x4*>(part_o) + (int64_t)slot * kSlotFloat4 + 8 * 64 * wave + lane;
+#pragma unroll
+  for (int v = 0; v < 8; ++v) dst[64 * v] = o[v] * f;
 }
 
 // ---------------------------------------------------------------------------
@@ -416,7 +429,7 @@ __global__ __launch_bounds__(kStage1Threads, 2) void mla_stage1(Stage1Args a) {
   const int b = item.batch;
   const int tok_last = item.tok_end - 1;
   const int ntiles = (item.tok_end - item.tok_begin + kTileTokens - 1) / kTileTokens;
-  const int64_t seq_base = a.kv_indptr[b];  // first row, or first page slot
+  const int64_t seq_base = item.kv_base;  // kv_indptr[b]: first row, or first page slot
 
   float vscale = 1.0f;
   float xscale = a.score_scale;
@@ -500,9 +513,7 @@ __global__ __launch_bounds__(kStage1Threads, 2) void mla_stage1(Stage1Args a) {
     }
     return;
   }
-  float* dst = a.part_o + ((int64_t)item.slot * kNumHeads + r16) * kVDim + dv0 + 4 * g;
-#pragma unroll
-  for (int v = 0; v < 8; ++v) *reinterpret_cast<f32x4*>(dst + 16 * v) = o[v] * f;
+  store_partial(a.part_o, item.slot, wave, lane, o, f);
   if (tid < kNumHeads) a.part_lse[(int64_t)item.slot * kNumHeads + tid] = m_ref + __log2f(L);
 }
 
@@ -749,7 +760,7 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a
       dma_one(qsrc + (h * 72 + c) * 16, qm0 + 1024 * k);
     }
   }
-  const int64_t seq_base = a.kv_indptr[b];  // first row, or first page slot
+  const int64_t seq_base = item.kv_base;  // kv_indptr[b]: first row, or first page slot
 
   int page0 = 0;
   if constexpr (PAGED) {
@@ -1024,62 +1035,72 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a
           uint2{pack_bf16x2(val[0], val[1]), pack_bf16x2(val[2], val[3])};
     }
   } else {
-    float* dst = a.part_o + ((int64_t)item.slot * kNumHeads + r16) * kVDim + dim0;
-#pragma unroll
-    for (int v = 0; v < 8; ++v) *reinterpret_cast<f32x4*>(dst + 16 * v) = o[v] * f;
+    store_partial(a.part_o, item.slot, wave, lane, o, f);
     if (wave == 0 && g == 0)
       a.part_lse[(int64_t)item.slot * kNumHeads + r16] = m_ref + __log2f(L);
   }
 }
 
 // ---------------------------------------------------------------------------
-// mla_merge: LSE merge of the partials of one (sequence, head) per workgroup,
+// mla_merge: LSE merge of the partials of one sequence,
 //   M = max_s lse_s,  out = sum_s 2^(lse_s - M) O_s / sum_s 2^(lse_s - M)
 // (727205 `mla_rd`; 700955 `reduce_lse_v71`; 599694 `_flash_fp8_split_s2`).
-// Thread t owns dims 4t..4t+3; the partials are read kMergeBatch at a time so
+// One workgroup per (sequence, quarter of the columns): thread t merges
+// float4 numbers t and t + 256 of that quarter of every partial (both of head
+// t % 16, see store_partial), reading kMergeBatch partials at a time so that
 // their loads are in flight together.
 // ---------------------------------------------------------------------------
-constexpr int kMergeBatch = 8;
+constexpr int kMergeBatch = 4;
 
 __global__ __launch_bounds__(kMergeThreads) void mla_merge(MergeArgs a) {
-  const MergeSeq seq = a.work[blockIdx.x / kNumHeads];
-  const int b = seq.batch;
-  const int h = blockIdx.x % kNumHeads;
-  const int d = threadIdx.x * 4;
+  const MergeSeq seq = a.work[blockIdx.x >> 2];
+  const int quarter = blockIdx.x & 3;
+  const int t = threadIdx.x;
+  const int h = t & 15;
   const float* lse = a.part_lse + (int64_t)seq.slot_begin * kNumHeads + h;
-  const f32x4* po = reinterpret_cast<const f32x4*>(
-                        a.part_o + ((int64_t)seq.slot_begin * kNumHeads + h) * kVDim + d);
-  constexpr int kSlotStride = kNumHeads * kVDim / 4;  // f32x4 per partial
+  const f32x4* po = reinterpret_cast<const f32x4*>(a.part_o) + (int64_t)seq.slot_begin * kSlotFloat4 +
+                    512 * quarter + t;
   float M = kNegInf;  // running maximum of the lse seen so far
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   float W = 0.f;
   for (int s0 = 0; s0 < seq.nslots; s0 += kMergeBatch) {
     float l[kMergeBatch];
-    f32x4 x[kMergeBatch];
+    f32x4 x0[kMergeBatch], x1[kMergeBatch];
 #pragma unroll
     for (int k = 0; k < kMergeBatch; ++k) {  // all loads of the batch in flight together
       const int s = min(s0 + k, seq.nslots - 1);
       l[k] = lse[s * kNumHeads];
-      x[k] = po[(int64_t)s * kSlotStride];
+      x0[k] = po[(int64_t)s * kSlotFloat4];
+      x1[k] = po[(int64_t)s * kSlotFloat4 + 256];
     }
     float mb = M;
 #pragma unroll
     for (int k = 0; k < kMergeBatch; ++k)
       if (s0 + k < seq.nslots) mb = fmaxf(mb, l[k]);
     const float r = __builtin_amdgcn_exp2f(M - mb);  // 0 on the first batch
-    acc *= r;
+    acc0 *= r;
+    acc1 *= r;
     W *= r;
 #pragma unroll
     for (int k = 0; k < kMergeBatch; ++k) {
       const float wk = (s0 + k < seq.nslots) ? __builtin_amdgcn_exp2f(l[k] - mb) : 0.f;
       W += wk;
-      acc += wk * x[k];
+      acc0 += wk * x0[k];
+      acc1 += wk * x1[k];
     }
     M = mb;
   }
-  const f32x4 r = acc * (1.0f / W);
-  *reinterpret_cast<uint2*>(a.out + ((int64_t)b * kNumHeads + h) * kVDim + d) =
-      uint2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
+  const float inv = 1.0f / W;
+  // float4 e (= t or t + 256) of this quarter: column tile v = e / 64,
+  // lane e % 64, i.e. dims 128 quarter + 16 v + 4 ((e % 64) / 16)
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int e = t + 256 * half;
+    const int d = 128 * quarter + 16 * (e >> 6) + 4 * ((e & 63) >> 4);
+    const f32x4 r = (half ? acc1 : acc0) * inv;
+    *reinterpret_cast<uint2*>(a.out + ((int64_t)seq.batch * kNumHeads + h) * kVDim + d) =
+        uint2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
+  }
 }
 
 template <int F, bool P>
@@ -1101,19 +1122,29 @@ const void* pick_stage1(int fmt, bool paged) {
 
 }  // namespace
 
-hipError_t launch_stage1(int fmt, bool paged, const Stage1Args& a, int num_items, hipStream_t s) {
+// With events, the launch records them at the start and the end of the
+// kernel itself (hipExtLaunchKernel), so their difference is its duration.
+static hipError_t launch(const void* fn, dim3 grid, dim3 block, void** params, hipStream_t s,
+                         hipEvent_t start, hipEvent_t stop) {
+  if (start && stop) return hipExtLaunchKernel(fn, grid, block, params, 0, s, start, stop, 0);
+  return hipLaunchKernel(fn, grid, block, params, 0, s);
+}
+
+hipError_t launch_stage1(int fmt, bool paged, const Stage1Args& a, int num_items, hipStream_t s,
+                         hipEvent_t start, hipEvent_t stop) {
   const void* fn = pick_stage1(fmt, paged);
   if (!fn) return hipErrorInvalidValue;
   Stage1Args args = a;
   void* params[] = {&args};
-  return hipLaunchKernel(fn, dim3(num_items), dim3(kStage1Threads), params, 0, s);
+  return launch(fn, dim3(num_items), dim3(kStage1Threads), params, s, start, stop);
 }
 
-hipError_t launch_merge(const MergeArgs& a, int num_merge_seqs, hipStream_t s) {
+hipError_t launch_merge(const MergeArgs& a, int num_merge_seqs, hipStream_t s, hipEvent_t start,
+                        hipEvent_t stop) {
   MergeArgs args = a;
   void* params[] = {&args};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&mla_merge),
-                         dim3(num_merge_seqs * kNumHeads), dim3(kMergeThreads), params, 0, s);
+  return launch(reinterpret_cast<const void*>(&mla_merge), dim3(num_merge_seqs * 4),
+                dim3(kMergeThreads), params, s, start, stop);
 }
 
 hipError_t kernel_attributes(int fmt, bool paged, int which, hipFuncAttributes* attr) {
