@@ -1,39 +1,35 @@
 // HIP kernels (gfx950) for single-token multi-head latent attention decode.
 //
-// mla_stage1: one 256-thread workgroup per planned work item, i.e. a token
-// range of one sequence, streamed in 64-token tiles with an online softmax
-// (flash-decoding, as in the split-K kernels of amd-mixed-mla submissions
-// 727205 "v25: LEAN" `mla_s1` and 599694 "overhead elimination"
-// `_flash_fp8_split_s1`).  A workgroup whose item is the whole sequence
-// writes the bf16 output; otherwise it writes a normalised partial plus its
-// log-sum-exp.  An empty sequence's item writes zeros.
-// mla_merge: per (sequence, head) of the split sequences, the log-sum-exp
-// weighted merge of the partials (727205 `mla_rd`; 700955 "locked baseline
-// dispatch" `reduce_lse_v71`; 599694 `_flash_fp8_split_s2`).
+// Split-K flash-decoding, as in the split kernels of amd-mixed-mla
+// submissions 727205 "v25: LEAN" (`mla_s1`) and 599694 "overhead
+// elimination" (`_flash_fp8_split_s1`): one 256-thread workgroup per planned
+// work item, i.e. a token range of one sequence, streamed in tiles with an
+// online softmax.  A workgroup whose item is the whole sequence writes the
+// bf16 output; otherwise it writes a normalised partial plus its log-sum-exp.
+// An empty sequence's item writes zeros.
 //
-// Per 64-token tile:
-//   1. every thread loads 16-byte chunks of the tile's cache rows into
-//      registers one tile ahead and writes them to LDS -- fp8 codes as stored,
-//      bf16 as stored, MXFP4 decoded to bf16 with its block scale (exact);
-//   2. wave w scores tokens 16w..16w+15 against the 16 heads:
-//      S^T[token, head] = K Q^T on v_mfma_f32_16x16x32_bf16, A = cache rows
-//      (fp8 decoded to bf16 in registers, exact), B = the query, held in
-//      registers for the whole item.  The 576-long contraction runs in a
-//      permuted column order (any order common to both operands is valid) so
-//      that one 16-byte LDS read feeds two MFMA steps;
-//   3. the waves exchange their tile maxima and bf16 probabilities through
-//      LDS.  The softmax runs in the log2 domain with a lazy shared maximum:
-//      it only moves (and O and the sums are rescaled) when a tile maximum
-//      passes it by more than 8, which bounds every weight by 2^8 and keeps the
-//      result exact;
-//   4. wave w accumulates output columns 128w..128w+127 over the 64 tokens:
-//      O^T[dim, head] += V^T P^T on the same MFMA.  The score registers of the
-//      two waves that scored a 32-token step are the B operand as they are
-//      (the token order inside the step is chosen to match), and V^T comes
-//      from the LDS rows through the gfx950 transposing reads
-//      ds_read_b64_tr_b8 (fp8) / ds_read_b64_tr_b16 (bf16).
-// Everything accumulates in fp32; the fp8 per-tensor scale is folded into the
-// score scale and the final normalisation.
+//   mla_stage1_fp8  fp8 cache: 128-token tiles moved HBM -> LDS by
+//                   cache-to-LDS loads; both contractions on fp8 / MX matrix
+//                   instructions straight on the cached codes (section below).
+//   mla_stage1      bf16 and MXFP4 caches: 64-token tiles staged through
+//                   registers, MXFP4 decoded to bf16 exactly on the way into
+//                   LDS, both contractions on v_mfma_f32_16x16x32_bf16.
+//   mla_merge       per (sequence, quarter of the columns) of the split
+//                   sequences, the log-sum-exp weighted merge of the partials
+//                   (727205 `mla_rd`; 700955 "locked baseline dispatch"
+//                   `reduce_lse_v71`; 599694 `_flash_fp8_split_s2`).
+//
+// In both stage-1 kernels wave w scores a quarter of the tile's tokens
+// against the 16 heads (S^T[token, head] = K Q^T) and accumulates output
+// columns 128w..128w+127 over all of the tile's tokens (O^T[dim, head] +=
+// V^T P^T, V^T through the gfx950 transposing LDS reads); the softmax runs in
+// the log2 domain with a lazy maximum shared by the four waves, which only
+// moves (and O and the sums are rescaled) when a tile maximum passes it by
+// more than 8, bounding every weight by 2^8 and keeping the result exact.
+// Contractions over the 576 columns run in a permuted column order (any order
+// common to both operands is valid).  Everything accumulates in fp32; the fp8
+// per-tensor scale is folded into the score scale and the final
+// normalisation.
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
