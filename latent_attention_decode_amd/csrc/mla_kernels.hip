@@ -566,8 +566,15 @@ constexpr int kMaxItemPages = 512;                  // page ids of one item stag
 static_assert(kCLoads == kWaves * kCLoadsPerWave && kQLoads * 1024 == kQBytes, "load split");
 static_assert(kQBytes <= kCTileBytes, "the query is staged in the last ring slot");
 
-// Position of 16-byte chunk c of tile row r inside the row.
-__host__ __device__ constexpr int chunk_swz(int r) { return (r >> 1) & 3; }
+// Position of 16-byte chunk c of tile row r inside the row: c ^ chunk_swz(r),
+// a permutation inside each aligned group of four chunks.  The LDS has 64
+// banks of 4 bytes; with rows at pitch 576, the reads below touch, per phase,
+// 16 rows r0..r0+15 of one chunk (score reads, 16 B per lane) or rows
+// {32g + 8q + e : e < 8} of two neighbouring g (transposing V reads, 8 B per
+// lane), and this permutation puts every phase on distinct banks.
+__host__ __device__ constexpr int chunk_swz(int r) {
+  return ((r >> 2) & 1) | ((((r >> 3) ^ (r >> 5)) & 1) << 1);
+}
 __host__ __device__ constexpr int tile_slot(int r, int c) { return r * 36 + (c ^ chunk_swz(r)); }
 // Position of 16-byte chunk c (0..71) of query head h.
 __host__ __device__ constexpr int q_slot(int h, int c) { return h * 72 + (c ^ (h & 7)); }
@@ -878,18 +885,21 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a
   float l_part = 0.f;     // this lane's share of the running sum
 
   // LDS byte offsets of this lane's reads within a tile.  Score rows
-  // 32w + 16s + r16 have chunk_swz(r16) and value rows 32g + 8q + (r16 >> 1)
-  // have chunk_swz(r16 >> 1), whatever s, q and g.
-  const int ksw = chunk_swz(r16);
+  // 32w + 16s + r16 have chunk_swz(32w + r16) whatever s; value rows
+  // 32g + 8q + (r16 >> 1) have chunk_swz(32g + 8(q & 1) + (r16 >> 1)).
+  const int ksw = chunk_swz(32 * wave + r16);
   const int k_row = (32 * wave + r16) * kQkDim;
   const int k_off0 = k_row + 16 * ((2 * g) ^ ksw);      // chunk 8K + 2g
   const int k_off1 = k_row + 16 * ((2 * g + 1) ^ ksw);  // chunk 8K + 2g + 1
   const int k_offr = k_row + 16 * (32 + (g ^ ksw));     // chunk 32 + g
-  const int vsw = chunk_swz(r16 >> 1);
-  int v_off[4];  // + 64 (v / 4) + 4608 q; column chunk 8w + v
+  int v_off[2][4];  // [q % 2][v % 4]; + 64 (v / 4) + 4608 (q & ~1); column chunk 8w + v
 #pragma unroll
-  for (int c4 = 0; c4 < 4; ++c4)
-    v_off[c4] = (32 * g + (r16 >> 1)) * kQkDim + 16 * (8 * wave + (c4 ^ vsw)) + 8 * (r16 & 1);
+  for (int qp = 0; qp < 2; ++qp) {
+    const int vrow = 32 * g + 8 * qp + (r16 >> 1);
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4)
+      v_off[qp][c4] = vrow * kQkDim + 16 * (8 * wave + (c4 ^ chunk_swz(vrow))) + 8 * (r16 & 1);
+  }
   uint8_t* const p_hi = &sh.p[0][r16][0];
   uint8_t* const p_lo = &sh.p[1][r16][0];
 
@@ -1002,7 +1012,8 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              (lds_i32x2*)(cur + v_off[(v + u) & 3] + 64 * ((v + u) >> 2) + 8 * kQkDim * q));
+              (lds_i32x2*)(cur + v_off[q & 1][(v + u) & 3] + 64 * ((v + u) >> 2) +
+                           8 * kQkDim * (q & ~1)));
           va[u][2 * q] = raw[0];
           va[u][2 * q + 1] = raw[1];
         }
