@@ -33,6 +33,7 @@ struct mla_decode_s {
   int64_t total_tokens = 0;
   size_t workspace_bytes = 0;
   int num_merge = 0;  // sequences with >= 2 partials
+  int uniform_splits = 0, uniform_chunk = 0, uniform_len = 0, uniform_base = 0;
   // device: [num_items] WorkItem, [num_merge] MergeSeq
   void* dev_plan = nullptr;
   size_t dev_plan_bytes = 0;
@@ -131,6 +132,8 @@ static bool seq_lengths(const int32_t* indptr, const int32_t* last, int batch, i
 struct PlanOut {
   std::vector<WorkItem> items;
   std::vector<MergeSeq> merge;
+  // uniform plan (see Stage1Args): splits per sequence, chunk, length; 0 if not
+  int uniform_splits = 0, uniform_chunk = 0, uniform_len = 0;
   int num_slots = 0;
   int max_splits = 0;
 };
@@ -208,6 +211,35 @@ static void plan_items(const std::vector<int64_t>& lens, const int32_t* indptr, 
   std::stable_sort(out->items.begin(), out->items.end(), [](const WorkItem& x, const WorkItem& y) {
     return (x.tok_end - x.tok_begin) > (y.tok_end - y.tok_begin);
   });
+
+  // A uniform plan (equal lengths, contiguous cache, every item exactly what
+  // uniform_item computes, merge jobs in sequence order) lets the kernels
+  // compute their item instead of loading it.
+  out->uniform_splits = out->uniform_chunk = out->uniform_len = 0;
+  const size_t n_items = out->items.size();
+  if (page_size != 1 || batch < 1 || lens[0] <= 0 || n_items % static_cast<size_t>(batch) != 0) return;
+  for (int b = 0; b < batch; ++b)
+    if (lens[b] != lens[0]) return;
+  const int splits = static_cast<int>(n_items / static_cast<size_t>(batch));
+  const int len = static_cast<int>(lens[0]);
+  const int uchunk = splits == 1 ? len : out->items[0].tok_end - out->items[0].tok_begin;
+  for (size_t i = 0; i < n_items; ++i) {
+    const WorkItem u = uniform_item(static_cast<int>(i), splits, uchunk, len, indptr[0]);
+    const WorkItem& w = out->items[i];
+    if (w.batch != u.batch || w.tok_begin != u.tok_begin || w.tok_end != u.tok_end || w.slot != u.slot ||
+        w.kv_base != u.kv_base)
+      return;
+  }
+  if (splits > 1) {
+    if (out->merge.size() != static_cast<size_t>(batch)) return;
+    for (int m = 0; m < batch; ++m) {
+      const MergeSeq& j = out->merge[m];
+      if (j.batch != m || j.slot_begin != m * splits || j.nslots != splits) return;
+    }
+  }
+  out->uniform_splits = splits;
+  out->uniform_chunk = uchunk;
+  out->uniform_len = len;
 }
 
 }  // namespace mla
@@ -306,6 +338,10 @@ mla_status mla_decode_plan(mla_decode_t h, int batch, const int32_t* kv_indptr_h
   h->num_slots = plan.num_slots;
   h->max_splits = plan.max_splits;
   h->num_merge = static_cast<int>(plan.merge.size());
+  h->uniform_splits = plan.uniform_splits;
+  h->uniform_chunk = plan.uniform_chunk;
+  h->uniform_len = plan.uniform_len;
+  h->uniform_base = kv_indptr_host[0];
   h->total_tokens = 0;
   for (int64_t n : lens) h->total_tokens += n;
   h->workspace_bytes = static_cast<size_t>(plan.num_slots) * slot_bytes();
@@ -405,6 +441,10 @@ mla_status mla_decode_run(mla_decode_t h, const void* q, const void* kv, const v
                    : nullptr;
   a.out = static_cast<uint16_t*>(out);
   a.score_scale = h->sm_scale * 1.4426950408889634f;
+  a.uniform_splits = h->uniform_splits;
+  a.uniform_chunk = h->uniform_chunk;
+  a.uniform_len = h->uniform_len;
+  a.uniform_base = h->uniform_base;
 
   const bool timed = h->profiling && h->events_ready;
   h->timed_run = false;
@@ -415,6 +455,7 @@ mla_status mla_decode_run(mla_decode_t h, const void* q, const void* kv, const v
   if (h->num_merge > 0) {
     mla::MergeArgs m{};
     m.work = reinterpret_cast<const mla::MergeSeq*>(plan_base + items_bytes);
+    m.uniform_nslots = h->uniform_splits > 1 ? h->uniform_splits : 0;
     m.part_o = a.part_o;
     m.part_lse = a.part_lse;
     m.out = a.out;

@@ -25,6 +25,9 @@ enum KvFormat : int { kBf16 = 0, kFp8 = 1, kMxfp4 = 2 };
 // normalised partial (O, lse) to partial slot `slot`; kWhole: the item is the
 // whole sequence, write the bf16 output directly; kEmpty (with tok_begin ==
 // tok_end): the sequence is empty, write zeros.
+struct WorkItem;
+__host__ __device__ inline WorkItem uniform_item(int i, int splits, int chunk, int len, int base);
+
 struct WorkItem {
   int32_t batch;
   int32_t tok_begin;
@@ -36,6 +39,19 @@ struct WorkItem {
   static constexpr int32_t kEmpty = -2;
 };
 static_assert(sizeof(WorkItem) == 32, "work item layout");
+
+// Item i of a uniform plan (see Stage1Args).
+__host__ __device__ inline WorkItem uniform_item(int i, int splits, int chunk, int len, int base) {
+  const int b = i / splits;
+  const int s = i - b * splits;
+  WorkItem w{};
+  w.batch = b;
+  w.tok_begin = s * chunk;
+  w.tok_end = (s + 1) * chunk < len ? (s + 1) * chunk : len;
+  w.slot = splits == 1 ? WorkItem::kWhole : i;
+  w.kv_base = base + b * len;
+  return w;
+}
 
 // One merge job: the partials of sequence `batch` are slots
 // [slot_begin, slot_begin + nslots), nslots >= 2.
@@ -60,10 +76,18 @@ struct Stage1Args {
   float* part_lse;              // [slots, 16], log2 domain
   uint16_t* out;                // bf16 [batch, 16, 512]
   float score_scale;            // sm_scale * log2(e)
+  // Uniform plan (every sequence of length uniform_len, contiguous cache,
+  // cut into uniform_splits items of uniform_chunk tokens, in order):
+  // item i is computed, not loaded.  uniform_splits == 0: use `items`.
+  int uniform_splits;
+  int uniform_chunk;
+  int uniform_len;
+  int uniform_base;             // kv_indptr[0]
 };
 
 struct MergeArgs {
   const MergeSeq* work;         // the sequences with >= 2 partials
+  int uniform_nslots;           // > 0: merge job m is sequence m, slots [m n, m n + n)
   const float* part_o;
   const float* part_lse;
   uint16_t* out;

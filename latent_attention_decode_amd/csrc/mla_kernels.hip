@@ -409,7 +409,10 @@ __global__ __launch_bounds__(kStage1Threads, 2) void mla_stage1(Stage1Args a) {
   __shared__ __attribute__((aligned(16))) Stage1Tiles<F> tiles;
   __shared__ __attribute__((aligned(16))) Stage1Lds<F, PAGED> sh;
 
-  const WorkItem item = a.items[blockIdx.x];
+  const WorkItem item = a.uniform_splits
+                            ? uniform_item(blockIdx.x, a.uniform_splits, a.uniform_chunk,
+                                           a.uniform_len, a.uniform_base)
+                            : a.items[blockIdx.x];
   const int tid = threadIdx.x;
   if (item.slot == WorkItem::kEmpty) {  // empty sequence: its output is zero
     uint4* dst = reinterpret_cast<uint4*>(a.out + (int64_t)item.batch * kNumHeads * kVDim);
@@ -733,7 +736,10 @@ template <bool PAGED>
 __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a) {
   __shared__ __attribute__((aligned(16))) Fp8Lds sh;
 
-  const WorkItem item = a.items[blockIdx.x];
+  const WorkItem item = a.uniform_splits
+                            ? uniform_item(blockIdx.x, a.uniform_splits, a.uniform_chunk,
+                                           a.uniform_len, a.uniform_base)
+                            : a.items[blockIdx.x];
   const int tid = threadIdx.x;
   if (item.slot == WorkItem::kEmpty) {  // empty sequence: its output is zero
     uint4* dst = reinterpret_cast<uint4*>(a.out + (int64_t)item.batch * kNumHeads * kVDim);
@@ -1060,7 +1066,10 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a
 constexpr int kMergeBatch = 4;
 
 __global__ __launch_bounds__(kMergeThreads) void mla_merge(MergeArgs a) {
-  const MergeSeq seq = a.work[blockIdx.x >> 2];
+  const MergeSeq seq =
+      a.uniform_nslots > 0
+          ? MergeSeq{(int)(blockIdx.x >> 2), (int)(blockIdx.x >> 2) * a.uniform_nslots, a.uniform_nslots, 0}
+          : a.work[blockIdx.x >> 2];
   const int quarter = blockIdx.x & 3;
   const int t = threadIdx.x;
   const int h = t & 15;
