@@ -53,6 +53,29 @@ __host__ __device__ inline WorkItem uniform_item(int i, int splits, int chunk, i
   return w;
 }
 
+// Workgroups are handed to the eight XCDs in turn (workgroup x runs on XCD
+// x % 8, each XCD with its own L2).  xcd_block(x, n) renumbers a grid of n
+// so that each XCD takes one contiguous run of jobs: the splits of a sequence
+// then share one L2 (the query is fetched once per XCD), and so do the merge
+// jobs of the sequences whose partials that XCD wrote.  A bijection of [0, n).
+__host__ __device__ constexpr int xcd_block(int x, int n) {
+  return (x & 7) * (n >> 3) + ((x & 7) < (n & 7) ? (x & 7) : (n & 7)) + (x >> 3);
+}
+constexpr bool xcd_block_is_bijection(int n) {
+  int seen = 0;
+  for (int x = 0; x < n; ++x) {
+    const int y = xcd_block(x, n);
+    if (y < 0 || y >= n) return false;
+    for (int z = 0; z < x; ++z)
+      if (xcd_block(z, n) == y) return false;
+    ++seen;
+  }
+  return seen == n;
+}
+static_assert(xcd_block_is_bijection(1) && xcd_block_is_bijection(7) && xcd_block_is_bijection(64) &&
+                  xcd_block_is_bijection(131) && xcd_block_is_bijection(256),
+              "xcd_block");
+
 // One merge job: the partials of sequence `batch` are slots
 // [slot_begin, slot_begin + nslots), nslots >= 2.
 struct MergeSeq {

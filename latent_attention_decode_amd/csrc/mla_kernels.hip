@@ -410,7 +410,7 @@ __global__ __launch_bounds__(kStage1Threads, 2) void mla_stage1(Stage1Args a) {
   __shared__ __attribute__((aligned(16))) Stage1Lds<F, PAGED> sh;
 
   const WorkItem item = a.uniform_splits
-                            ? uniform_item(blockIdx.x, a.uniform_splits, a.uniform_chunk,
+                            ? uniform_item(xcd_block(blockIdx.x, gridDim.x), a.uniform_splits, a.uniform_chunk,
                                            a.uniform_len, a.uniform_base)
                             : a.items[blockIdx.x];
   const int tid = threadIdx.x;
@@ -737,7 +737,7 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a
   __shared__ __attribute__((aligned(16))) Fp8Lds sh;
 
   const WorkItem item = a.uniform_splits
-                            ? uniform_item(blockIdx.x, a.uniform_splits, a.uniform_chunk,
+                            ? uniform_item(xcd_block(blockIdx.x, gridDim.x), a.uniform_splits, a.uniform_chunk,
                                            a.uniform_len, a.uniform_base)
                             : a.items[blockIdx.x];
   const int tid = threadIdx.x;
@@ -909,13 +909,23 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a
   uint8_t* const p_hi = &sh.p[0][r16][0];
   uint8_t* const p_lo = &sh.p[1][r16][0];
 
+  // Tile 1 goes into the query's slot as soon as every wave has its query in
+  // registers, so that the first two tiles stream in together.
+  if (ntiles > 1) {
+    lds_barrier();
+    issue(1, -1);
+  }
+
   for (int t = 0; t < ntiles; ++t) {
     const int tok0 = item.tok_begin + t * kCTile;
-    wait_loads<0>();  // this wave's part of tile t
-    lds_barrier();    // all of tile t; everyone is past tile t-1 (and the query)
-    // Tile t+1 goes into the other slot in five parts spread over this tile's
-    // work, so that the loads queue while the matrix cores run.
-    const bool more = t + 1 < ntiles;
+    if (t == 0 && ntiles > 1)
+      wait_loads<kCLoadsPerWave>();  // tile 0, not tile 1 behind it
+    else
+      wait_loads<0>();  // this wave's part of tile t
+    lds_barrier();      // all of tile t; everyone is past tile t-1 (and the query)
+    // From tile 1 on, tile t+1 goes into the other slot in five parts spread
+    // over this tile's work, so that the loads queue while the matrix cores run.
+    const bool more = t > 0 && t + 1 < ntiles;
     if (more) issue(t + 1, 0);
     const uint8_t* cur = &sh.tile[t & (kCRing - 1)][0];
 
@@ -1066,11 +1076,11 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a
 constexpr int kMergeBatch = 4;
 
 __global__ __launch_bounds__(kMergeThreads) void mla_merge(MergeArgs a) {
-  const MergeSeq seq =
-      a.uniform_nslots > 0
-          ? MergeSeq{(int)(blockIdx.x >> 2), (int)(blockIdx.x >> 2) * a.uniform_nslots, a.uniform_nslots, 0}
-          : a.work[blockIdx.x >> 2];
-  const int quarter = blockIdx.x & 3;
+  const int job = a.uniform_nslots > 0 ? xcd_block(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+  const MergeSeq seq = a.uniform_nslots > 0
+                           ? MergeSeq{job >> 2, (job >> 2) * a.uniform_nslots, a.uniform_nslots, 0}
+                           : a.work[job >> 2];
+  const int quarter = job & 3;
   const int t = threadIdx.x;
   const int h = t & 15;
   const float* lse = a.part_lse + (int64_t)seq.slot_begin * kNumHeads + h;
