@@ -33,8 +33,9 @@ struct mla_decode_s {
   int64_t total_tokens = 0;
   size_t workspace_bytes = 0;
   int num_merge = 0;  // sequences with >= 2 partials
+  bool fused_merge = false;  // the fp8 kernel merges them itself (no merge launch)
   int uniform_splits = 0, uniform_chunk = 0, uniform_len = 0, uniform_base = 0;
-  // device: [num_items] WorkItem, [num_merge] MergeSeq
+  // device: [num_items] WorkItem, [num_merge] MergeSeq, [num_merge] int32 counters
   void* dev_plan = nullptr;
   size_t dev_plan_bytes = 0;
   int num_cus = 0;
@@ -188,7 +189,7 @@ static void plan_items(const std::vector<int64_t>& lens, const int32_t* indptr, 
   out->max_splits = 0;
   for (int b = 0; b < batch; ++b) {
     if (!lens[b]) {
-      out->items.push_back(WorkItem{b, 0, 0, WorkItem::kEmpty, indptr[b], {0, 0, 0}});
+      out->items.push_back(WorkItem{b, 0, 0, WorkItem::kEmpty, indptr[b], -1, 0, 0});
       continue;
     }
     if (chunk[b] > max_item) chunk[b] = max_item;
@@ -196,15 +197,17 @@ static void plan_items(const std::vector<int64_t>& lens, const int32_t* indptr, 
     out->max_splits = std::max<int>(out->max_splits, static_cast<int>(ns));
     if (ns == 1) {
       out->items.push_back(
-          WorkItem{b, 0, static_cast<int32_t>(lens[b]), WorkItem::kWhole, indptr[b], {0, 0, 0}});
+          WorkItem{b, 0, static_cast<int32_t>(lens[b]), WorkItem::kWhole, indptr[b], -1, 0, 0});
       continue;
     }
+    const int32_t job = static_cast<int32_t>(out->merge.size());
     out->merge.push_back(MergeSeq{b, out->num_slots, static_cast<int32_t>(ns), 0});
     for (int64_t s = 0; s < ns; ++s) {
       const int64_t t0 = s * chunk[b];
       const int64_t t1 = std::min(lens[b], t0 + chunk[b]);
       out->items.push_back(WorkItem{b, static_cast<int32_t>(t0), static_cast<int32_t>(t1),
-                                    out->num_slots + static_cast<int32_t>(s), indptr[b], {0, 0, 0}});
+                                    out->num_slots + static_cast<int32_t>(s), indptr[b], job,
+                                    out->num_slots, static_cast<int32_t>(ns)});
     }
     out->num_slots += static_cast<int>(ns);
   }
@@ -227,7 +230,8 @@ static void plan_items(const std::vector<int64_t>& lens, const int32_t* indptr, 
     const WorkItem u = uniform_item(static_cast<int>(i), splits, uchunk, len, indptr[0]);
     const WorkItem& w = out->items[i];
     if (w.batch != u.batch || w.tok_begin != u.tok_begin || w.tok_end != u.tok_end || w.slot != u.slot ||
-        w.kv_base != u.kv_base)
+        w.kv_base != u.kv_base || (splits > 1 && (w.merge_job != u.merge_job || w.slot_begin != u.slot_begin ||
+                                                  w.nslots != u.nslots)))
       return;
   }
   if (splits > 1) {
@@ -318,7 +322,9 @@ mla_status mla_decode_plan(mla_decode_t h, int batch, const int32_t* kv_indptr_h
 
   const size_t items_bytes = plan.items.size() * sizeof(mla::WorkItem);
   const size_t merge_bytes = plan.merge.size() * sizeof(mla::MergeSeq);
-  const size_t need = items_bytes + merge_bytes;
+  // completion counters of the fused merge, zero as uploaded
+  const size_t counter_bytes = plan.merge.size() * sizeof(int32_t);
+  const size_t need = items_bytes + merge_bytes + counter_bytes;
   if (need > h->dev_plan_bytes) {
     if (h->dev_plan) (void)hipFree(h->dev_plan);
     h->dev_plan = nullptr;
@@ -338,6 +344,12 @@ mla_status mla_decode_plan(mla_decode_t h, int batch, const int32_t* kv_indptr_h
   h->num_slots = plan.num_slots;
   h->max_splits = plan.max_splits;
   h->num_merge = static_cast<int>(plan.merge.size());
+  // The fused merge adds the last item's read-back of the other partials to
+  // that item; it pays where items finish at different times (ragged plans),
+  // while a uniform plan, whose items all finish together, merges faster in
+  // the merge kernel.
+  h->fused_merge = h->kv_dtype == MLA_KV_FP8_E4M3 && plan.max_splits <= mla::kFusedMergeMaxSlots &&
+                   plan.uniform_splits == 0;
   h->uniform_splits = plan.uniform_splits;
   h->uniform_chunk = plan.uniform_chunk;
   h->uniform_len = plan.uniform_len;
@@ -445,6 +457,10 @@ mla_status mla_decode_run(mla_decode_t h, const void* q, const void* kv, const v
   a.uniform_chunk = h->uniform_chunk;
   a.uniform_len = h->uniform_len;
   a.uniform_base = h->uniform_base;
+  const size_t merge_bytes = static_cast<size_t>(h->num_merge) * sizeof(mla::MergeSeq);
+  a.counters = h->fused_merge && h->num_merge > 0
+                   ? reinterpret_cast<int*>(plan_base + items_bytes + merge_bytes)
+                   : nullptr;
 
   const bool timed = h->profiling && h->events_ready;
   h->timed_run = false;
@@ -452,7 +468,7 @@ mla_status mla_decode_run(mla_decode_t h, const void* q, const void* kv, const v
   hipError_t e = mla::launch_stage1(h->kv_dtype, h->page_size > 1, a, h->num_items, s,
                                      timed ? h->ev[0] : nullptr, timed ? h->ev[1] : nullptr);
   if (e != hipSuccess) return fail(h, MLA_ERR_HIP, "stage-1 launch: %s", hipGetErrorString(e));
-  if (h->num_merge > 0) {
+  if (h->num_merge > 0 && !a.counters) {
     mla::MergeArgs m{};
     m.work = reinterpret_cast<const mla::MergeSeq*>(plan_base + items_bytes);
     m.uniform_nslots = h->uniform_splits > 1 ? h->uniform_splits : 0;

@@ -24,7 +24,9 @@ enum KvFormat : int { kBf16 = 0, kFp8 = 1, kMxfp4 = 2 };
 // `batch` (logical token indices within the sequence).  slot >= 0: write the
 // normalised partial (O, lse) to partial slot `slot`; kWhole: the item is the
 // whole sequence, write the bf16 output directly; kEmpty (with tok_begin ==
-// tok_end): the sequence is empty, write zeros.
+// tok_end): the sequence is empty, write zeros.  For a split sequence,
+// merge_job indexes its merge job (and completion counter) and its partials
+// are slots [slot_begin, slot_begin + nslots).
 struct WorkItem;
 __host__ __device__ inline WorkItem uniform_item(int i, int splits, int chunk, int len, int base);
 
@@ -34,7 +36,9 @@ struct WorkItem {
   int32_t tok_end;
   int32_t slot;
   int32_t kv_base;  // kv_indptr[batch] as planned
-  int32_t pad[3];
+  int32_t merge_job;
+  int32_t slot_begin;
+  int32_t nslots;
   static constexpr int32_t kWhole = -1;
   static constexpr int32_t kEmpty = -2;
 };
@@ -50,6 +54,9 @@ __host__ __device__ inline WorkItem uniform_item(int i, int splits, int chunk, i
   w.tok_end = (s + 1) * chunk < len ? (s + 1) * chunk : len;
   w.slot = splits == 1 ? WorkItem::kWhole : i;
   w.kv_base = base + b * len;
+  w.merge_job = b;
+  w.slot_begin = b * splits;
+  w.nslots = splits;
   return w;
 }
 
@@ -106,6 +113,11 @@ struct Stage1Args {
   int uniform_chunk;
   int uniform_len;
   int uniform_base;             // kv_indptr[0]
+  // Non-null: the fp8 kernel merges the partials itself.  counters[j] counts
+  // the finished items of merge job j (zero between calls); the item that
+  // finishes last reads the other partials of its sequence and writes the
+  // output, so no merge kernel runs.
+  int* counters;
 };
 
 struct MergeArgs {
@@ -115,6 +127,10 @@ struct MergeArgs {
   const float* part_lse;
   uint16_t* out;
 };
+
+// Largest number of splits of one sequence that the fp8 kernel merges itself
+// (the last item reads the other nslots - 1 partials in groups of four).
+constexpr int kFusedMergeMaxSlots = 12;
 
 // Launchers (mla_kernels.hip).  Return the launch status.
 hipError_t launch_stage1(int fmt, bool paged, const Stage1Args& a, int num_items, hipStream_t s,

@@ -153,6 +153,34 @@ def test_split_count_changes_only_rounding(B, oracle_mod):
         assert np.abs(o - outs[0]).max() < 2e-2
 
 
+@pytest.mark.parametrize("split", [2, 5, 12, 13])
+def test_merge_repeated_calls(B, oracle_mod, split):
+    """With an fp8 cache and at most 12 splits per sequence the split kernel
+    merges the partials itself: per-sequence completion counters, reset by the
+    item that finishes last, pick the merging item; with 13 the merge kernel
+    runs.  Calls on one plan with new data each time must each match the
+    oracle (a partial left from the call before would not), and a repeat of
+    the first must agree with it bit for bit (the merge order does not depend
+    on which item finished last)."""
+    lens = [3000, 1700, 129, 2500, 1]
+    cases = [synth.make_case("fp8", lens, seed=31 + r) for r in range(3)]
+    dec = B.MlaDecode("fp8", 1)
+    try:
+        dec.plan(cases[0].kv_indptr, None, split)
+        outs = []
+        for case in cases + cases[:1]:
+            t = B.case_to_device(case)
+            out = torch.full((case.batch, 16, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
+            dec.run(t["q"], t["kv"], t["kv_scales"], t["kv_indptr"], out)
+            torch.cuda.synchronize()
+            outs.append(out.float().cpu().numpy().astype(np.float64))
+    finally:
+        dec.close()
+    for r, case in enumerate(cases):
+        check_close(outs[r], oracle_out(oracle_mod, case), "fp8", f"split {split} call {r}")
+    assert np.array_equal(outs[0], outs[3])
+
+
 def test_workspace_too_small_is_rejected(B):
     case = synth.make_case("fp8", [4096], seed=29)
     t = B.case_to_device(case)
