@@ -35,12 +35,17 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 DEFAULT_WORKLOAD = "bs64_kv1024_fp8"
 ROTATION_BYTES = 1 << 30  # inputs cycled per timed pass: 4x the 256 MB MALL
 METRIC = "µs/call and effective KV HBM GB/s (% of peak), MLA decode bs×kv_len"
-KERNEL_SRC = os.path.join(ROOT, "latent_attention_decode_amd", "csrc", "mla_kernels.hip")
+# Sources of the fp8 split kernel: a traffic record holds for them as hashed.
+KERNEL_SRCS = [os.path.join(ROOT, "latent_attention_decode_amd", "csrc", f)
+               for f in ("mla_stage1_fp8.hip", "mla_device.h", "mla_internal.h")]
 
 
 def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_record(workload: str):

@@ -34,13 +34,18 @@
  * token j lives in row page*page_size + j%page_size.  A sequence of length 0
  * produces a zero output.
  *
- * Execution.  Two kernel launches per call: each workgroup of the first
- * streams one token range ("work item") of one sequence with an online
- * softmax and writes either the output (the item is the whole sequence) or a
- * normalised partial and its log-sum-exp; the second merges the partials of
- * every split sequence by their log-sum-exp weights (727205 `mla_rd`, 700955
- * `reduce_lse_v71`, 599694 `_flash_fp8_split_s2`).  It is not launched when
- * no sequence is split.
+ * Execution.  Each workgroup of the split kernel streams one token range
+ * ("work item") of one sequence with an online softmax and writes either the
+ * output (the item is the whole sequence) or a normalised partial and its
+ * log-sum-exp; the partials of every split sequence are merged by their
+ * log-sum-exp weights (727205 `mla_rd`, 700955 `reduce_lse_v71`, 599694
+ * `_flash_fp8_split_s2`).  The merge is a second kernel launch, except for an
+ * fp8 cache with a plan whose items differ in length (at most 12 per
+ * sequence): there the item of a sequence that finishes last merges its
+ * partials, so each call is one launch.  No merge runs when no sequence is
+ * split.  The completion counters of that merge belong to the plan: runs of
+ * one handle must not overlap (on any streams), and a plan must not be made
+ * while a run of the handle is still executing.
  *
  * Ownership.  The caller owns every tensor, the workspace and the stream.  A
  * handle owns only its plan (a small device work list, allocated by

@@ -1,0 +1,208 @@
+// Device helpers shared by the gfx950 decode kernels: vector types, the
+// LDS-only workgroup barrier, cross-group reductions, the partial-output
+// layout, cache-to-LDS (LDS-DMA) loads and the fp8 / MX matrix-instruction
+// wrappers.  Included by the kernel translation units only.
+#ifndef MLA_DEVICE_H
+#define MLA_DEVICE_H
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kLazyRescale = 8.0f;  // log2 headroom before O is rescaled
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2 v;
+  v[0] = (__bf16)a;  // round to nearest even
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Max / sum over the four lanes l, l^16, l^32, l^48 (the four MFMA k-groups
+// of one row), with the gfx950 lane-swap instructions: permlane32_swap(x, x)
+// gives every lane the value of its own half in one result and of the other
+// half in the other, and permlane16_swap does the same for 16-lane rows.
+__device__ __forceinline__ float xor_max_groups(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float xor_sum_groups(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Layout of one partial O (a workspace slot, 16 x 512 fp32): the float4 that
+// lane l of wave w holds for column tile v (heads l % 16, dims
+// 128w + 16v + 4(l / 16) .. +3) is float4 number (8w + v) * 64 + l of the
+// slot, so that each store instruction of a wave writes 1 KB contiguously.
+constexpr int kSlotFloat4 = kNumHeads * kVDim / 4;
+__device__ __forceinline__ void store_partial(float* part_o, int slot, int wave, int lane,
+                                              const f32x4 (&o)[8], float f) {
+  f32x4* dst = reinterpret_cast<f32x4*>(part_o) + (int64_t)slot * kSlotFloat4 + 8 * 64 * wave + lane;
+#pragma unroll
+  for (int v = 0; v < 8; ++v) dst[64 * v] = o[v] * f;
+}
+
+// ---------------------------------------------------------------------------
+// workgroup barrier that orders LDS only
+// ---------------------------------------------------------------------------
+// s_waitcnt immediates (gfx9 encoding): vmcnt in bits 3:0 and 15:14, expcnt in
+// 6:4, lgkmcnt in 11:8.  Waiting on lgkmcnt(0) alone leaves the cache-to-LDS
+// loads of later tiles in flight across the barrier.
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 0xF) | (0x7 << 4) | ((lgkm & 0xF) << 8) | (((vm >> 4) & 0x3) << 14);
+}
+constexpr int kWaitLgkm0 = waitcnt_imm(63, 0);
+
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // this wave's LDS reads/writes are done
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+
+// Cache-to-LDS loads: load b of a group writes lane l's 16 bytes to LDS
+// m0 + 1024 b + 16 l; the instruction offset 1024 b is added to the global
+// address as well, so the per-lane address passed in excludes it.  Written as
+// inline assembly so that the compiler does not guard later LDS reads with a
+// wait for every such load in flight; the kernel waits for them explicitly.
+// The loads carry the non-temporal hint: each byte is read once, and
+// streaming reads that do not try to stay in the caches reach a higher HBM
+// rate.  They name m0 as clobbered, which they do write; nothing else in
+// these kernels keeps a value in m0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+template <int N>
+__device__ __forceinline__ void dma_group(const uint8_t* base, const uint32_t* off, uint32_t m0) {
+  static_assert(N >= 1 && N <= 4, "group size");
+  if constexpr (N == 4)
+    asm volatile(
+        "s_mov_b32 m0, %5\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %4 nt\n\t"
+        "global_load_lds_dwordx4 %1, %4 offset:1024 nt\n\t"
+        "global_load_lds_dwordx4 %2, %4 offset:2048 nt\n\t"
+        "global_load_lds_dwordx4 %3, %4 offset:3072 nt"
+        :
+        : "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "s"(base), "s"(m0)
+        : "memory", "m0");
+  else if constexpr (N == 2)
+    asm volatile(
+        "s_mov_b32 m0, %3\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %2 nt\n\t"
+        "global_load_lds_dwordx4 %1, %2 offset:1024 nt"
+        :
+        : "v"(off[0]), "v"(off[1]), "s"(base), "s"(m0)
+        : "memory", "m0");
+  else
+    static_assert(N == 4 || N == 2, "group size");
+}
+template <int N>
+__device__ __forceinline__ void dma_group(const uint8_t* const* src, uint32_t m0) {
+  if constexpr (N == 4)
+    asm volatile(
+        "s_mov_b32 m0, %4\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, off nt\n\t"
+        "global_load_lds_dwordx4 %1, off offset:1024 nt\n\t"
+        "global_load_lds_dwordx4 %2, off offset:2048 nt\n\t"
+        "global_load_lds_dwordx4 %3, off offset:3072 nt"
+        :
+        : "v"(src[0]), "v"(src[1]), "v"(src[2]), "v"(src[3]), "s"(m0)
+        : "memory", "m0");
+  else if constexpr (N == 2)
+    asm volatile(
+        "s_mov_b32 m0, %2\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, off nt\n\t"
+        "global_load_lds_dwordx4 %1, off offset:1024 nt"
+        :
+        : "v"(src[0]), "v"(src[1]), "s"(m0)
+        : "memory", "m0");
+  else
+    static_assert(N == 4 || N == 2, "group size");
+}
+// One load, lane l's 16 bytes at src to LDS m0 + 16 l.
+__device__ __forceinline__ void dma_one(const void* src, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+               :
+               : "v"(src), "s"(m0)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Wait until at most N of this wave's loads are outstanding (loads complete
+// in issue order).
+template <int N>
+__device__ __forceinline__ void wait_loads() {
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(N, 15));
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const uint8_t*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+typedef long fp8x8;                                             // 8 e4m3 codes
+typedef int fp8x32 __attribute__((ext_vector_type(8)));         // 32 e4m3 codes
+
+__device__ __forceinline__ fp8x8 pack_fp8x8(uint32_t lo, uint32_t hi) {
+  return (fp8x8)(((uint64_t)hi << 32) | lo);
+}
+
+// Four floats (|x| <= 448) -> e4m3 hi + lo codes (see above), one word each.
+__device__ __forceinline__ void split_fp8x4(float x0, float x1, float x2, float x3,
+                                            uint32_t& hi, uint32_t& lo) {
+  int h = 0, l = 0;
+  h = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, h, false);
+  h = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, h, true);
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(h, false);
+  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(h, true);
+  l = __builtin_amdgcn_cvt_pk_fp8_f32(x0 - a[0], x1 - a[1], l, false);
+  l = __builtin_amdgcn_cvt_pk_fp8_f32(x2 - b[0], x3 - b[1], l, true);
+  hi = (uint32_t)h;
+  lo = (uint32_t)l;
+}
+
+__device__ __forceinline__ f32x4 mfma_fp8(fp8x8 a, fp8x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, 0, 0, 0);
+}
+// fp8 x fp8, 128 k-values, block scales 2^0 (e8m0 code 127).
+__device__ __forceinline__ f32x4 mfma_fp8_k128(fp8x32 a, fp8x32 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+__device__ __forceinline__ fp8x32 join16(u32x4 a, u32x4 b) {
+  return fp8x32{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+}
+
+}  // namespace
+}  // namespace mla
+
+#endif  // MLA_DEVICE_H

@@ -132,6 +132,9 @@ struct MergeArgs {
 // (the last item reads the other nslots - 1 partials in groups of four).
 constexpr int kFusedMergeMaxSlots = 12;
 
+// The fp8 split kernel (mla_stage1_fp8.hip).
+const void* stage1_fp8_kernel(bool paged);
+
 // Launchers (mla_kernels.hip).  Return the launch status.
 hipError_t launch_stage1(int fmt, bool paged, const Stage1Args& a, int num_items, hipStream_t s,
                          hipEvent_t start = nullptr, hipEvent_t stop = nullptr);

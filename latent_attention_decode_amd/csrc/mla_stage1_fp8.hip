@@ -1,0 +1,531 @@
+// gfx950 split kernel for an fp8-e4m3 cache (per-tensor scale): single-token
+// multi-head latent attention decode, one 256-thread workgroup per planned
+// work item (a token range of one sequence), 128-token tiles streamed
+// HBM -> LDS by cache-to-LDS loads, both contractions on the fp8 / MX matrix
+// instructions straight on the cached codes.  A workgroup whose item is the
+// whole sequence writes the bf16 output; otherwise it writes a normalised
+// partial and its log-sum-exp, and for plans that ask for it the item of a
+// sequence that finishes last merges that sequence's partials.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mla_device.h"
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+// ---------------------------------------------------------------------------
+// stage 1, fp8 cache: cooperative 128-token tiles streamed into LDS
+// ---------------------------------------------------------------------------
+// Both contractions run straight on the cached e4m3 codes (nothing is
+// decoded), on the gfx950 MX matrix instruction v_mfma_scale_f32_16x16x128_
+// f8f6f4 (fp8 x fp8, unit block scales), which takes 128 k-values per step,
+// and on v_mfma_f32_16x16x32_fp8_fp8 for the 64 rope columns.  The other
+// operand is written as a sum of two e4m3 numbers, hi + lo, and each product
+// is taken twice:
+//   * the query row of head h is first scaled by 2^s_h (max |q| in [128, 256))
+//     and split q = hi + lo with hi = e4m3(q) and lo = e4m3(q - hi).  A bf16
+//     value has 8 significant bits and hi keeps the leading 4, so the rest fits
+//     lo exactly whenever it is a normal e4m3 number (|scaled q| >= 1/4, i.e.
+//     every element above 1/1024 of the row maximum; smaller ones are off by at
+//     most 2^-10 in scaled units).  2^-s_h is folded into the score scale.
+//   * the softmax weights p <= 2^8 (lazy maximum) are split the same way,
+//     which keeps about 8 significant bits, as many as a bf16 weight has.
+//
+// Data movement: every byte of the item's cache rows goes HBM -> LDS by
+// cache-to-LDS loads (global_load_lds_dwordx4), in a ring of two 128-token
+// tiles, so one tile is in flight while the other is computed; the query
+// comes the same way.  A tile is its 128 rows at pitch 576 with no padding,
+// 72 loads of 1 KB each (wave w issues loads 18w..18w+17).  One load writes
+// 64 consecutive 16-byte LDS slots, lane l to slot l, and each lane fetches
+// the chunk that belongs there; inside each aligned group of four chunks of a
+// row the chunks are stored XOR-permuted by chunk_swz(row), which makes every
+// LDS read below free of bank conflicts while each load still covers whole
+// 64-byte runs of the rows.
+//
+// Per tile, with wave w:
+//   1. S^T[token, head] = K (Qhi + Qlo)^T for tokens 32w..32w+31 (two 16-token
+//      row blocks), all 576 columns; the query stays in registers;
+//   2. softmax in the log2 domain with a lazy maximum shared by the four
+//      waves: it moves (and O and the sums are rescaled) only when a tile
+//      maximum passes it by more than 8, so p <= 2^8; each wave writes its
+//      e4m3 hi/lo weights P^T to LDS;
+//   3. O^T[dim, head] += V^T (Phi + Plo)^T for dims 128w..128w+127 over all
+//      128 tokens, one MX step per 16 columns; V^T comes from the tile through
+//      the transposing LDS read ds_read_b64_tr_b8.
+// Because the maximum is shared, the waves' outputs need no merge: each wave
+// writes its own 128 columns.
+constexpr int kCTile = 128;                         // tokens per tile
+constexpr int kCTileBytes = kCTile * kQkDim;        // 73728
+constexpr int kCRing = 2;                           // tiles in the LDS ring
+constexpr int kCLoads = kCTileBytes / 1024;         // 72 loads per tile
+constexpr int kCLoadsPerWave = kCLoads / kWaves;    // 18
+constexpr int kQBytes = kNumHeads * kQkDim * 2;     // bf16 query of one sequence
+constexpr int kQLoads = kQBytes / 1024;             // 18
+constexpr int kPRow = kCTile + 16;                  // bytes per head row of P^T
+constexpr int kMaxItemPages = 512;                  // page ids of one item staged in LDS
+static_assert(kCLoads == kWaves * kCLoadsPerWave && kQLoads * 1024 == kQBytes, "load split");
+static_assert(kQBytes <= kCTileBytes, "the query is staged in the last ring slot");
+
+// Position of 16-byte chunk c of tile row r inside the row: c ^ chunk_swz(r),
+// a permutation inside each aligned group of four chunks.  The LDS has 64
+// banks of 4 bytes; with rows at pitch 576, the reads below touch, per phase,
+// 16 rows r0..r0+15 of one chunk (score reads, 16 B per lane) or rows
+// {32g + 8q + e : e < 8} of two neighbouring g (transposing V reads, 8 B per
+// lane), and this permutation puts every phase on distinct banks.
+__host__ __device__ constexpr int chunk_swz(int r) {
+  return ((r >> 2) & 1) | ((((r >> 3) ^ (r >> 5)) & 1) << 1);
+}
+__host__ __device__ constexpr int tile_slot(int r, int c) { return r * 36 + (c ^ chunk_swz(r)); }
+// Position of 16-byte chunk c (0..71) of query head h.
+__host__ __device__ constexpr int q_slot(int h, int c) { return h * 72 + (c ^ (h & 7)); }
+
+// Every slot of a tile holds exactly one chunk of one row, and vice versa.
+constexpr bool tile_slots_are_a_permutation() {
+  bool seen[kCLoads * 64] = {};
+  for (int r = 0; r < kCTile; ++r)
+    for (int c = 0; c < 36; ++c) {
+      const int s = tile_slot(r, c);
+      if (s / 36 != r || seen[s]) return false;
+      seen[s] = true;
+    }
+  return true;
+}
+constexpr bool q_slots_are_a_permutation() {
+  bool seen[kQLoads * 64] = {};
+  for (int h = 0; h < kNumHeads; ++h)
+    for (int c = 0; c < 72; ++c) {
+      const int s = q_slot(h, c);
+      if (s / 72 != h || seen[s]) return false;
+      seen[s] = true;
+    }
+  return true;
+}
+static_assert(tile_slots_are_a_permutation() && q_slots_are_a_permutation(), "slot maps");
+
+struct Fp8Lds {
+  uint8_t tile[kCRing][kCTileBytes];       // the ring; slot 1 first holds the query
+  uint8_t p[2][kNumHeads][kPRow];          // P^T hi / lo as [head][token]
+  float red_m[kNumHeads][kWaves];          // per-wave tile maxima
+  float red_l[kNumHeads][kWaves];          // per-wave sums, at the end
+  int32_t pages[kMaxItemPages];            // paged: page ids of the item
+};
+
+template <bool PAGED>
+__global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a) {
+  __shared__ __attribute__((aligned(16))) Fp8Lds sh;
+
+  const WorkItem item = a.uniform_splits
+                            ? uniform_item(xcd_block(blockIdx.x, gridDim.x), a.uniform_splits, a.uniform_chunk,
+                                           a.uniform_len, a.uniform_base)
+                            : a.items[blockIdx.x];
+  const int tid = threadIdx.x;
+  if (item.slot == WorkItem::kEmpty) {  // empty sequence: its output is zero
+    uint4* dst = reinterpret_cast<uint4*>(a.out + (int64_t)item.batch * kNumHeads * kVDim);
+#pragma unroll
+    for (int k = 0; k < (kNumHeads * kVDim * 2 / 16) / kStage1Threads; ++k)
+      dst[tid + kStage1Threads * k] = uint4{0u, 0u, 0u, 0u};
+    return;
+  }
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+  const int lane = tid & 63;
+  const int r16 = lane & 15;  // MFMA row/column index of this lane
+  const int g = lane >> 4;    // MFMA k-group of this lane
+  const int b = item.batch;
+  const int tok_last = item.tok_end - 1;
+  const int ntiles = (item.tok_end - item.tok_begin + kCTile - 1) / kCTile;
+  const float kv_scale = *a.kv_scale;
+
+  // The query first (it needs only the sequence id): 18 loads into ring slot
+  // 1, load k by wave k % 4.
+  {
+    const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(a.q + (int64_t)b * kNumHeads * kQkDim);
+    const uint32_t qm0 = lds_u32(&sh.tile[kCRing - 1][0]);
+    for (int k = wave; k < kQLoads; k += kWaves) {
+      const int s = 64 * k + lane;
+      const int h = s / 72;
+      const int c = (s - 72 * h) ^ (h & 7);
+      dma_one(qsrc + (h * 72 + c) * 16, qm0 + 1024 * k);
+    }
+  }
+  const int64_t seq_base = item.kv_base;  // kv_indptr[b]: first row, or first page slot
+
+  int page0 = 0;
+  if constexpr (PAGED) {
+    page0 = item.tok_begin >> a.page_shift;
+    const int npages = min(((item.tok_end - 1) >> a.page_shift) - page0 + 1, kMaxItemPages);
+    for (int i = tid; i < npages; i += kStage1Threads)
+      sh.pages[i] = a.page_indices[seq_base + page0 + i];
+    __syncthreads();
+  }
+
+  // This lane's slot in each of its wave's 18 loads of a tile: (tile row << 8)
+  // | chunk.  Load j = 4q + e of a group goes to LDS m0_q + 1024 e.
+  uint32_t rc[kCLoadsPerWave];
+#pragma unroll
+  for (int j = 0; j < kCLoadsPerWave; ++j) {
+    const int s = 64 * (kCLoadsPerWave * wave + j) + lane;
+    const int r = s / 36;
+    const int c = (s - 36 * r) ^ chunk_swz(r);
+    rc[j] = (uint32_t)(r << 8 | c);
+  }
+  const uint32_t ring0 = lds_u32(&sh.tile[0][0]) + 1024 * kCLoadsPerWave * wave;
+
+  // Issue part `part` of this wave's 18 loads of tile t into ring slot t % 2:
+  // loads 4 part .. 4 part + 3 (part 0..3), loads 16 and 17 (part 4), or all
+  // of them (part -1).  Rows past the item's last token fetch that token's row
+  // (finite data, masked later).
+  auto issue = [&](int t, int part) {
+    const int tok0 = item.tok_begin + t * kCTile;
+    const int lim = tok_last - tok0;  // last valid tile row
+    const uint32_t m0 = ring0 + (uint32_t)((t & (kCRing - 1)) * kCTileBytes);
+    if constexpr (!PAGED) {
+      // base 3072 bytes before the tile, so that no per-lane offset (which
+      // excludes the instruction offset of up to 3072) is negative
+      const uint8_t* base = uniform_ptr(a.kv + (seq_base + tok0) * kQkDim - 3072);
+      uint32_t off[kCLoadsPerWave];
+#pragma unroll
+      for (int j = 0; j < kCLoadsPerWave; ++j) {
+        const uint32_t r = min((int)(rc[j] >> 8), lim);
+        off[j] = r * kQkDim + 16 * (rc[j] & 0xFF) + 3072 - 1024 * (j & 3);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (part < 0 || part == q) dma_group<4>(base, off + 4 * q, m0 + 4096 * q);
+      if (part < 0 || part == 4) dma_group<2>(base, off + 16, m0 + 4096 * 4);
+    } else {
+      const int pmask = (1 << a.page_shift) - 1;
+      const uint8_t* src[kCLoadsPerWave];
+#pragma unroll
+      for (int j = 0; j < kCLoadsPerWave; ++j) {
+        const int tok = tok0 + min((int)(rc[j] >> 8), lim);
+        const uint32_t page = (uint32_t)sh.pages[(tok >> a.page_shift) - page0];
+        const int64_t row = (int64_t)((page << a.page_shift) + (uint32_t)(tok & pmask));
+        src[j] = a.kv + row * kQkDim + 16 * (rc[j] & 0xFF) - 1024 * (j & 3);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (part < 0 || part == q) dma_group<4>(src + 4 * q, m0 + 4096 * q);
+      if (part < 0 || part == 4) dma_group<2>(src + 16, m0 + 4096 * 4);
+    }
+  };
+
+  issue(0, -1);
+  wait_loads<kCLoadsPerWave>();  // this wave's query loads have landed
+  lds_barrier();                 // ... and everyone's
+
+  // Query, B operand of S^T = K Q^T, scaled by 2^s and split into e4m3
+  // hi + lo: for 128-column block K (0..3) lane (head r16, group g) holds
+  // q[head][128K + 32g .. +32]; for the rope columns, k-step h (0, 1),
+  // q[head][512 + 16g + 8h .. +8].
+  fp8x32 qh[4], ql[4];
+  fp8x8 rh[2], rl[2];
+  float xscale;
+  {
+    const uint8_t* qlds = &sh.tile[kCRing - 1][0];
+    bf16x8 qv[18];  // [4K + i]: chunk 16K + 4g + i; [16 + h]: chunk 64 + 2g + h
+#pragma unroll
+    for (int K = 0; K < 4; ++K)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        qv[4 * K + i] = *reinterpret_cast<const bf16x8*>(qlds + 16 * q_slot(r16, 16 * K + 4 * g + i));
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      qv[16 + h] = *reinterpret_cast<const bf16x8*>(qlds + 16 * q_slot(r16, 64 + 2 * g + h));
+    float amax = 0.f;
+#pragma unroll
+    for (int k = 0; k < 18; ++k)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)qv[k][e]));
+    amax = xor_max_groups(amax);
+    // 2^s with amax * 2^s in [128, 256)
+    const int s = (amax > 0.f) ? 8 - __builtin_amdgcn_frexp_expf(amax) : 0;
+    xscale = a.score_scale * kv_scale * __builtin_ldexpf(1.0f, -s);
+    uint32_t hw[36], lw[36];  // word 2k + m: elements 4m..4m+3 of qv[k]
+#pragma unroll
+    for (int k = 0; k < 18; ++k)
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+        split_fp8x4(__builtin_ldexpf((float)qv[k][4 * m], s), __builtin_ldexpf((float)qv[k][4 * m + 1], s),
+                    __builtin_ldexpf((float)qv[k][4 * m + 2], s), __builtin_ldexpf((float)qv[k][4 * m + 3], s),
+                    hw[2 * k + m], lw[2 * k + m]);
+#pragma unroll
+    for (int K = 0; K < 4; ++K)
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        qh[K][d] = (int)hw[8 * K + d];
+        ql[K][d] = (int)lw[8 * K + d];
+      }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      rh[h] = pack_fp8x8(hw[32 + 2 * h], hw[33 + 2 * h]);
+      rl[h] = pack_fp8x8(lw[32 + 2 * h], lw[33 + 2 * h]);
+    }
+  }
+
+  f32x4 o[8];  // O^T[dim 128w + 16v + 4g + i][head r16]
+#pragma unroll
+  for (int v = 0; v < 8; ++v) o[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref = kNegInf;  // shared running maximum (log2 units) of head r16
+  float l_part = 0.f;     // this lane's share of the running sum
+
+  // LDS byte offsets of this lane's reads within a tile.  Score rows
+  // 32w + 16s + r16 have chunk_swz(32w + r16) whatever s; value rows
+  // 32g + 8q + (r16 >> 1) have chunk_swz(32g + 8(q & 1) + (r16 >> 1)).
+  const int ksw = chunk_swz(32 * wave + r16);
+  const int k_row = (32 * wave + r16) * kQkDim;
+  const int k_off0 = k_row + 16 * ((2 * g) ^ ksw);      // chunk 8K + 2g
+  const int k_off1 = k_row + 16 * ((2 * g + 1) ^ ksw);  // chunk 8K + 2g + 1
+  const int k_offr = k_row + 16 * (32 + (g ^ ksw));     // chunk 32 + g
+  int v_off[2][4];  // [q % 2][v % 4]; + 64 (v / 4) + 4608 (q & ~1); column chunk 8w + v
+#pragma unroll
+  for (int qp = 0; qp < 2; ++qp) {
+    const int vrow = 32 * g + 8 * qp + (r16 >> 1);
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4)
+      v_off[qp][c4] = vrow * kQkDim + 16 * (8 * wave + (c4 ^ chunk_swz(vrow))) + 8 * (r16 & 1);
+  }
+  uint8_t* const p_hi = &sh.p[0][r16][0];
+  uint8_t* const p_lo = &sh.p[1][r16][0];
+
+  // Tile 1 goes into the query's slot as soon as every wave has its query in
+  // registers, so that the first two tiles stream in together.
+  if (ntiles > 1) {
+    lds_barrier();
+    issue(1, -1);
+  }
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int tok0 = item.tok_begin + t * kCTile;
+    if (t == 0 && ntiles > 1)
+      wait_loads<kCLoadsPerWave>();  // tile 0, not tile 1 behind it
+    else
+      wait_loads<0>();  // this wave's part of tile t
+    lds_barrier();      // all of tile t; everyone is past tile t-1 (and the query)
+    // From tile 1 on, tile t+1 goes into the other slot in five parts spread
+    // over this tile's work, so that the loads queue while the matrix cores run.
+    const bool more = t > 0 && t + 1 < ntiles;
+    if (more) issue(t + 1, 0);
+    const uint8_t* cur = &sh.tile[t & (kCRing - 1)][0];
+
+    // ---- scores of tokens 32w + 16s + (0..15), s = 0, 1 ----
+    f32x4 sacc[2][2];  // [s][hi/lo]
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) sacc[s][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int K = 0; K < 4; ++K) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int ro = s * 16 * kQkDim + 128 * K;
+        const fp8x32 ka = join16(*reinterpret_cast<const u32x4*>(cur + k_off0 + ro),
+                                 *reinterpret_cast<const u32x4*>(cur + k_off1 + ro));
+        sacc[s][0] = mfma_fp8_k128(ka, qh[K], sacc[s][0]);
+        sacc[s][1] = mfma_fp8_k128(ka, ql[K], sacc[s][1]);
+      }
+      if (more && (K == 1 || K == 3)) issue(t + 1, K == 1 ? 1 : 2);
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(cur + k_offr + s * 16 * kQkDim);
+      const fp8x8 ka = pack_fp8x8(w[0], w[1]);
+      const fp8x8 kb = pack_fp8x8(w[2], w[3]);
+      sacc[s][0] = mfma_fp8(ka, rh[0], sacc[s][0]);
+      sacc[s][1] = mfma_fp8(ka, rl[0], sacc[s][1]);
+      sacc[s][0] = mfma_fp8(kb, rh[1], sacc[s][0]);
+      sacc[s][1] = mfma_fp8(kb, rl[1], sacc[s][1]);
+    }
+
+    // ---- softmax: x[s][i] is token 32w + 16s + 4g + i of head r16 ----
+    float x[2][4];
+    float tmax = kNegInf;
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[s][i] = (sacc[s][0][i] + sacc[s][1][i]) * xscale;
+        if (tok0 + 32 * wave + 16 * s + 4 * g + i > tok_last) x[s][i] = kNegInf;
+        tmax = fmaxf(tmax, x[s][i]);
+      }
+    tmax = xor_max_groups(tmax);
+    if (g == 0) sh.red_m[r16][wave] = tmax;
+    float p[2][4];
+    uint32_t ph[2], pl[2];
+    {
+      const float mr = (m_ref == kNegInf) ? 0.0f : m_ref;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[s][i] = __builtin_amdgcn_exp2f(x[s][i] - mr);
+        split_fp8x4(p[s][0], p[s][1], p[s][2], p[s][3], ph[s], pl[s]);
+        *reinterpret_cast<uint32_t*>(p_hi + 32 * wave + 16 * s + 4 * g) = ph[s];
+        *reinterpret_cast<uint32_t*>(p_lo + 32 * wave + 16 * s + 4 * g) = pl[s];
+      }
+    }
+    if (more) issue(t + 1, 3);
+    lds_barrier();  // P^T and the tile maxima of all waves
+
+    const f32x4 maxima = *reinterpret_cast<const f32x4*>(&sh.red_m[r16][0]);
+    fp8x32 bh = join16(*reinterpret_cast<const u32x4*>(p_hi + 32 * g),
+                       *reinterpret_cast<const u32x4*>(p_hi + 32 * g + 16));
+    fp8x32 bl = join16(*reinterpret_cast<const u32x4*>(p_lo + 32 * g),
+                       *reinterpret_cast<const u32x4*>(p_lo + 32 * g + 16));
+    const float tile_max = fmaxf(fmaxf(maxima[0], maxima[1]), fmaxf(maxima[2], maxima[3]));
+    // Every wave reads the same maxima, so this branch is uniform.
+    if (__ballot(tile_max > m_ref + kLazyRescale) != 0) {
+      const float m_new = fmaxf(m_ref, tile_max);
+      const float alpha = (m_ref == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
+#pragma unroll
+      for (int v = 0; v < 8; ++v) o[v] *= alpha;
+      l_part *= alpha;
+      m_ref = m_new;
+      lds_barrier();  // everyone has read the old P^T
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[s][i] = __builtin_amdgcn_exp2f(x[s][i] - m_ref);
+        split_fp8x4(p[s][0], p[s][1], p[s][2], p[s][3], ph[s], pl[s]);
+        *reinterpret_cast<uint32_t*>(p_hi + 32 * wave + 16 * s + 4 * g) = ph[s];
+        *reinterpret_cast<uint32_t*>(p_lo + 32 * wave + 16 * s + 4 * g) = pl[s];
+      }
+      lds_barrier();
+      bh = join16(*reinterpret_cast<const u32x4*>(p_hi + 32 * g),
+                  *reinterpret_cast<const u32x4*>(p_hi + 32 * g + 16));
+      bl = join16(*reinterpret_cast<const u32x4*>(p_lo + 32 * g),
+                  *reinterpret_cast<const u32x4*>(p_lo + 32 * g + 16));
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) l_part += (p[s][0] + p[s][1]) + (p[s][2] + p[s][3]);
+
+    // ---- O^T += V^T P^T over the 128 tokens, two column tiles at a time ----
+#pragma unroll
+    for (int v = 0; v < 8; v += 2) {
+      fp8x32 va[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (lds_i32x2*)(cur + v_off[q & 1][(v + u) & 3] + 64 * ((v + u) >> 2) +
+                           8 * kQkDim * (q & ~1)));
+          va[u][2 * q] = raw[0];
+          va[u][2 * q + 1] = raw[1];
+        }
+      o[v] = mfma_fp8_k128(va[0], bh, o[v]);
+      o[v + 1] = mfma_fp8_k128(va[1], bh, o[v + 1]);
+      o[v] = mfma_fp8_k128(va[0], bl, o[v]);
+      o[v + 1] = mfma_fp8_k128(va[1], bl, o[v + 1]);
+      if (more && v == 2) issue(t + 1, 4);
+    }
+  }
+
+  // ---- sums over the item; each wave writes its 128 columns ----
+  const float l_w = xor_sum_groups(l_part);
+  if (g == 0) sh.red_l[r16][wave] = l_w;
+  lds_barrier();
+  const f32x4 ls = *reinterpret_cast<const f32x4*>(&sh.red_l[r16][0]);
+  const float L = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+  const float f = kv_scale / L;
+  f32x4 res[8];  // this lane's normalised output, O^T[128w + 16v + 4g + i][r16]
+#pragma unroll
+  for (int v = 0; v < 8; ++v) res[v] = o[v] * f;
+  if (item.slot >= 0) {
+    const float lse = m_ref + __log2f(L);
+    if (!a.counters) {  // the merge kernel combines the partials
+      store_partial(a.part_o, item.slot, wave, lane, o, f);
+      if (wave == 0 && g == 0) a.part_lse[(int64_t)item.slot * kNumHeads + r16] = lse;
+      return;
+    }
+
+    // Fused merge.  The partial is written with device-scope (relaxed atomic)
+    // stores, which go through to the level that all XCDs share, and the
+    // workgroup counts itself finished only once they are complete; the other
+    // partials are read back with device-scope loads.  That publishes the data
+    // without a device-scope release / acquire fence, which would write back
+    // or invalidate the whole L2 of the XCD.  The item that finishes last
+    // merges; nothing waits on another workgroup.
+    // Layout of a slot here: float (4v + i) of lane l of wave w at
+    // 2048 w + 64 (4v + i) + l, so that each store writes 256 bytes in a row.
+    float* pdst = a.part_o + (int64_t)item.slot * (4 * kSlotFloat4) + 2048 * wave + lane;
+#pragma unroll
+    for (int v = 0; v < 8; ++v)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __hip_atomic_store(pdst + 64 * (4 * v + i), res[v][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (wave == 0 && g == 0)
+      __hip_atomic_store(a.part_lse + (int64_t)item.slot * kNumHeads + r16, lse, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's stores are complete
+    __shared__ int s_last;
+    __syncthreads();
+    if (tid == 0) {
+      int* cnt = a.counters + item.merge_job;
+      const int done = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = done == item.nslots - 1;
+      if (s_last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // for the next call
+    }
+    __syncthreads();
+    if (!s_last) return;
+    // out = sum_s 2^(lse_s - M) O_s / sum_s 2^(lse_s - M), M = max_s lse_s,
+    // summed in slot order over all the sequence's partials (this item's own
+    // included, as stored), so the result does not depend on which item
+    // finished last.  Each lane reads the float4 numbers it stored itself.
+    float ls[kFusedMergeMaxSlots];
+    f32x4 po[4][8];  // one group of four partials
+    auto load_group = [&](int s0) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int sl = item.slot_begin + min(s0 + k, item.nslots - 1);
+        float* src = a.part_o + (int64_t)sl * (4 * kSlotFloat4) + 2048 * wave + lane;
+#pragma unroll
+        for (int v = 0; v < 8; ++v)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            po[k][v][i] = __hip_atomic_load(src + 64 * (4 * v + i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    };
+#pragma unroll
+    for (int k = 0; k < kFusedMergeMaxSlots; ++k)
+      ls[k] = __hip_atomic_load(a.part_lse + (int64_t)(item.slot_begin + min(k, item.nslots - 1)) * kNumHeads + r16,
+                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    load_group(0);  // in flight together with the lse values
+    float M = kNegInf;
+#pragma unroll
+    for (int k = 0; k < kFusedMergeMaxSlots; ++k)
+      if (k < item.nslots) M = fmaxf(M, ls[k]);
+    float W = 0.0f;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) res[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s0 = 0; s0 < kFusedMergeMaxSlots; s0 += 4) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float w = s0 + k < item.nslots ? __builtin_amdgcn_exp2f(ls[s0 + k] - M) : 0.0f;
+        W += w;
+#pragma unroll
+        for (int v = 0; v < 8; ++v) res[v] += w * po[k][v];
+      }
+      if (s0 + 4 >= item.nslots) break;
+      load_group(s0 + 4);
+    }
+    const float inv = 1.0f / W;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) res[v] *= inv;
+  }
+  uint16_t* dst = a.out + ((int64_t)b * kNumHeads + r16) * kVDim + 128 * wave + 4 * g;
+#pragma unroll
+  for (int v = 0; v < 8; ++v)
+    *reinterpret_cast<uint2*>(dst + 16 * v) =
+        uint2{pack_bf16x2(res[v][0], res[v][1]), pack_bf16x2(res[v][2], res[v][3])};
+}
+
+}  // namespace
+
+const void* stage1_fp8_kernel(bool paged) {
+  return paged ? reinterpret_cast<const void*>(&mla_stage1_fp8<true>)
+               : reinterpret_cast<const void*>(&mla_stage1_fp8<false>);
+}
+
+}  // namespace mla
