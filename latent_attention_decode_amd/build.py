@@ -17,7 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmla_decode.so")
-SOURCES = [os.path.join(CSRC, f) for f in ("mla_kernels.hip", "mla_stage1_fp8.hip", "mla_decode.cpp")]
+SOURCES = [os.path.join(CSRC, f) for f in ("mla_kernels.hip", "mla_stage1_fp8.hip", "mla_stage1_mxfp4.hip",
+                                           "mla_decode.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

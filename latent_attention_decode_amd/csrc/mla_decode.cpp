@@ -348,7 +348,7 @@ mla_status mla_decode_plan(mla_decode_t h, int batch, const int32_t* kv_indptr_h
   // that item; it pays where items finish at different times (ragged plans),
   // while a uniform plan, whose items all finish together, merges faster in
   // the merge kernel.
-  h->fused_merge = h->kv_dtype == MLA_KV_FP8_E4M3 && plan.max_splits <= mla::kFusedMergeMaxSlots &&
+  h->fused_merge = h->kv_dtype != MLA_KV_BF16 && plan.max_splits <= mla::kFusedMergeMaxSlots &&
                    plan.uniform_splits == 0;
   h->uniform_splits = plan.uniform_splits;
   h->uniform_chunk = plan.uniform_chunk;
@@ -458,7 +458,7 @@ mla_status mla_decode_run(mla_decode_t h, const void* q, const void* kv, const v
   a.uniform_len = h->uniform_len;
   a.uniform_base = h->uniform_base;
   const size_t merge_bytes = static_cast<size_t>(h->num_merge) * sizeof(mla::MergeSeq);
-  a.counters = h->fused_merge && h->num_merge > 0
+  a.counters = h->fused_merge && h->num_merge > 0 && mla::stage1_dedicated(h->kv_dtype, a)
                    ? reinterpret_cast<int*>(plan_base + items_bytes + merge_bytes)
                    : nullptr;
 

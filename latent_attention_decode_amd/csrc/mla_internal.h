@@ -132,8 +132,14 @@ struct MergeArgs {
 // (the last item reads the other nslots - 1 partials in groups of four).
 constexpr int kFusedMergeMaxSlots = 12;
 
-// The fp8 split kernel (mla_stage1_fp8.hip).
+// The fp8 and MXFP4 split kernels (mla_stage1_fp8.hip, mla_stage1_mxfp4.hip).
 const void* stage1_fp8_kernel(bool paged);
+const void* stage1_mxfp4_kernel(bool paged);
+// Whether launch_stage1 runs the split kernel of that file for these
+// arguments (it does for fp8; for MXFP4 when the scale array and its row
+// stride are 2-byte aligned, else the bf16-decoding kernel).  Only those
+// kernels can merge partials themselves (Stage1Args::counters).
+bool stage1_dedicated(int fmt, const Stage1Args& a);
 
 // Launchers (mla_kernels.hip).  Return the launch status.
 hipError_t launch_stage1(int fmt, bool paged, const Stage1Args& a, int num_items, hipStream_t s,

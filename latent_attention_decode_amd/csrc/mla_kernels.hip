@@ -516,6 +516,8 @@ template <int F, bool P>
 const void* stage1_fn() {
   if constexpr (F == kFp8)
     return stage1_fp8_kernel(P);
+  else if constexpr (F == kMxfp4)
+    return stage1_mxfp4_kernel(P);
   else
     return reinterpret_cast<const void*>(&mla_stage1<F, P>);
 }
@@ -539,9 +541,18 @@ static hipError_t launch(const void* fn, dim3 grid, dim3 block, void** params, h
   return hipLaunchKernel(fn, grid, block, params, 0, s);
 }
 
+bool stage1_dedicated(int fmt, const Stage1Args& a) {
+  if (fmt == kFp8) return true;
+  if (fmt == kMxfp4) return ((a.scale_stride | (int64_t)(uintptr_t)a.kv_mx_scales) & 1) == 0;
+  return false;
+}
+
 hipError_t launch_stage1(int fmt, bool paged, const Stage1Args& a, int num_items, hipStream_t s,
                          hipEvent_t start, hipEvent_t stop) {
   const void* fn = pick_stage1(fmt, paged);
+  if (fmt == kMxfp4 && !stage1_dedicated(fmt, a))  // two-byte scale loads need even addresses
+    fn = paged ? reinterpret_cast<const void*>(&mla_stage1<kMxfp4, true>)
+               : reinterpret_cast<const void*>(&mla_stage1<kMxfp4, false>);
   if (!fn) return hipErrorInvalidValue;
   Stage1Args args = a;
   void* params[] = {&args};

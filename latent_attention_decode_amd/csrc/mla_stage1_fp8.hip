@@ -428,97 +428,7 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a
   const f32x4 ls = *reinterpret_cast<const f32x4*>(&sh.red_l[r16][0]);
   const float L = (ls[0] + ls[1]) + (ls[2] + ls[3]);
   const float f = kv_scale / L;
-  f32x4 res[8];  // this lane's normalised output, O^T[128w + 16v + 4g + i][r16]
-#pragma unroll
-  for (int v = 0; v < 8; ++v) res[v] = o[v] * f;
-  if (item.slot >= 0) {
-    const float lse = m_ref + __log2f(L);
-    if (!a.counters) {  // the merge kernel combines the partials
-      store_partial(a.part_o, item.slot, wave, lane, o, f);
-      if (wave == 0 && g == 0) a.part_lse[(int64_t)item.slot * kNumHeads + r16] = lse;
-      return;
-    }
-
-    // Fused merge.  The partial is written with device-scope (relaxed atomic)
-    // stores, which go through to the level that all XCDs share, and the
-    // workgroup counts itself finished only once they are complete; the other
-    // partials are read back with device-scope loads.  That publishes the data
-    // without a device-scope release / acquire fence, which would write back
-    // or invalidate the whole L2 of the XCD.  The item that finishes last
-    // merges; nothing waits on another workgroup.
-    // Layout of a slot here: float (4v + i) of lane l of wave w at
-    // 2048 w + 64 (4v + i) + l, so that each store writes 256 bytes in a row.
-    float* pdst = a.part_o + (int64_t)item.slot * (4 * kSlotFloat4) + 2048 * wave + lane;
-#pragma unroll
-    for (int v = 0; v < 8; ++v)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        __hip_atomic_store(pdst + 64 * (4 * v + i), res[v][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (wave == 0 && g == 0)
-      __hip_atomic_store(a.part_lse + (int64_t)item.slot * kNumHeads + r16, lse, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's stores are complete
-    __shared__ int s_last;
-    __syncthreads();
-    if (tid == 0) {
-      int* cnt = a.counters + item.merge_job;
-      const int done = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_last = done == item.nslots - 1;
-      if (s_last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // for the next call
-    }
-    __syncthreads();
-    if (!s_last) return;
-    // out = sum_s 2^(lse_s - M) O_s / sum_s 2^(lse_s - M), M = max_s lse_s,
-    // summed in slot order over all the sequence's partials (this item's own
-    // included, as stored), so the result does not depend on which item
-    // finished last.  Each lane reads the float4 numbers it stored itself.
-    float ls[kFusedMergeMaxSlots];
-    f32x4 po[4][8];  // one group of four partials
-    auto load_group = [&](int s0) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int sl = item.slot_begin + min(s0 + k, item.nslots - 1);
-        float* src = a.part_o + (int64_t)sl * (4 * kSlotFloat4) + 2048 * wave + lane;
-#pragma unroll
-        for (int v = 0; v < 8; ++v)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            po[k][v][i] = __hip_atomic_load(src + 64 * (4 * v + i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    };
-#pragma unroll
-    for (int k = 0; k < kFusedMergeMaxSlots; ++k)
-      ls[k] = __hip_atomic_load(a.part_lse + (int64_t)(item.slot_begin + min(k, item.nslots - 1)) * kNumHeads + r16,
-                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    load_group(0);  // in flight together with the lse values
-    float M = kNegInf;
-#pragma unroll
-    for (int k = 0; k < kFusedMergeMaxSlots; ++k)
-      if (k < item.nslots) M = fmaxf(M, ls[k]);
-    float W = 0.0f;
-#pragma unroll
-    for (int v = 0; v < 8; ++v) res[v] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s0 = 0; s0 < kFusedMergeMaxSlots; s0 += 4) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float w = s0 + k < item.nslots ? __builtin_amdgcn_exp2f(ls[s0 + k] - M) : 0.0f;
-        W += w;
-#pragma unroll
-        for (int v = 0; v < 8; ++v) res[v] += w * po[k][v];
-      }
-      if (s0 + 4 >= item.nslots) break;
-      load_group(s0 + 4);
-    }
-    const float inv = 1.0f / W;
-#pragma unroll
-    for (int v = 0; v < 8; ++v) res[v] *= inv;
-  }
-  uint16_t* dst = a.out + ((int64_t)b * kNumHeads + r16) * kVDim + 128 * wave + 4 * g;
-#pragma unroll
-  for (int v = 0; v < 8; ++v)
-    *reinterpret_cast<uint2*>(dst + 16 * v) =
-        uint2{pack_bf16x2(res[v][0], res[v][1]), pack_bf16x2(res[v][2], res[v][3])};
+  finish_item(a, item, tid, wave, lane, o, f, m_ref + __log2f(L));
 }
 
 }  // namespace

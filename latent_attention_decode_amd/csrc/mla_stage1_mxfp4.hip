@@ -1,0 +1,560 @@
+// gfx950 split kernel for an MXFP4 cache (e2m1 codes, one e8m0 scale per 32
+// columns of a row): single-token multi-head latent attention decode, one
+// 256-thread workgroup per planned work item, 128-token tiles streamed
+// HBM -> LDS by cache-to-LDS loads, both contractions on the MX matrix
+// instruction v_mfma_scale_f32_16x16x128_f8f6f4.
+//
+// Operand layout of that instruction on gfx950 (measured): in each group g of
+// 16 lanes, an fp4 operand holds 32 consecutive k-values 32g..32g+31, an fp8
+// operand holds k = 16g + b in its bytes b < 16 and k = 64 + 16g + (b - 16)
+// in bytes 16..31, and the block scale given by the lanes of group g applies
+// to k-values 32g..32g+31.
+//
+// Scores, S^T[token, head] = K Q^T: the cached e2m1 rows are the A operand
+// as they are, with the cache's own e8m0 scales as block scales (lane group g
+// of k-step K holds columns 128K + 32g..+32 of its row and that block's
+// scale), so the contraction is exact for any scale; the query is the fp8
+// B operand, split into e4m3 hi + lo as for the fp8 cache, and laid out to
+// match (bytes b < 16: column 128K + 16g + b, bytes 16..31: column
+// 128K + 64 + 16g + b - 16).  The 64 rope columns take one more k-step with
+// lane groups 2 and 3 zero.
+//
+// Values, O^T[dim, head] = V^T P^T: a scale of V belongs to a (token, 32
+// columns) block, i.e. runs along the output dimension, which no block scale
+// of a contraction over tokens can express.  So each tile's V is converted
+// once to e4m3 in LDS, relative to the largest scale of each block of 32
+// tokens x 32 columns: value = e2m1 x 2^(e - c) with c = max e over the block,
+// exact whenever the 32 tokens' scales of those columns lie within 8 binades
+// of c (smaller ones are rounded to e4m3, subnormals included).  2^(c - 127)
+// returns as the A block scale of P.V, whose k-values are laid out so that
+// k-block g is tokens 32g..32g+31 (bytes b < 16: token 16g + b, bytes 16..31:
+// token 64 + 16g + b - 16, for V^T and P^T alike).
+//
+// Data movement: per tile, 36 cache-to-LDS loads of 1 KB bring the 128 rows
+// of e2m1 codes (288 bytes each, rows past the item's end repeat its last
+// row) and 20 two-byte loads per lane group bring the 18 scale bytes of each
+// row, two per LDS dword (the two-byte form writes one dword per lane).  Two
+// raw tiles are in flight while a third is worked on: a raw slot is free
+// again as soon as its tile is scored and its V converted.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mla_device.h"
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+constexpr int kXTile = 128;                        // tokens per tile
+constexpr int kXRow = kQkDim / 2;                  // 288 bytes of e2m1 codes per row
+constexpr int kXFp4Bytes = kXTile * kXRow;         // 36864
+constexpr int kXFp4Loads = kXFp4Bytes / 1024;      // 36
+constexpr int kXFp4PerWave = kXFp4Loads / kWaves;  // 9
+constexpr int kXScalePairs = kQkDim / 64;          // 9 two-byte scale pairs per row
+constexpr int kXScaleItems = kXTile * kXScalePairs;  // 1152
+constexpr int kXScalePerWave = 5;                  // two-byte loads per wave and tile
+constexpr int kXScaleLoads = kWaves * kXScalePerWave;  // 20 (1280 lanes >= 1152 pairs)
+constexpr int kXScaleBytes = kXScaleLoads * 256;   // one dword per lane
+constexpr int kXRawBytes = kXFp4Bytes + kXScaleBytes;
+constexpr int kXLoadsPerWave = kXFp4PerWave + kXScalePerWave;  // 14
+constexpr int kXVRow = kVDim + 16;                 // bytes per row of the e4m3 V tile (512 + pad)
+constexpr int kXVBytes = kXTile * kXVRow;          // 65536
+constexpr int kQBytes = kNumHeads * kQkDim * 2;    // bf16 query of one sequence
+constexpr int kQLoads = kQBytes / 1024;            // 18
+constexpr int kPRow = kXTile + 16;                 // bytes per head row of P^T
+constexpr int kMaxItemPages = 512;                 // page ids of one item staged in LDS
+static_assert(kXFp4Loads == kWaves * kXFp4PerWave && kXScaleLoads * 64 >= kXScaleItems, "load split");
+static_assert(kQBytes <= kXVBytes, "the query is staged in the V tile");
+
+// Position of 16-byte chunk c (0..71) of query head h.  (The V tile needs
+// no permutation: at a row pitch of 528 bytes = 132 banks, the eight rows of
+// a transposing read fall on distinct banks.)
+__host__ __device__ constexpr int q_slot(int h, int c) { return h * 72 + (c ^ (h & 7)); }
+
+struct Fp4Lds {
+  uint8_t raw[2][kXRawBytes];              // e2m1 rows, then the scale dwords
+  uint8_t v[kXVBytes];                     // V of the current tile as e4m3 [token][dim]; first the query
+  uint8_t p[2][kNumHeads][kPRow];          // P^T hi / lo as [head][token]
+  float red_m[kNumHeads][kWaves];          // per-wave tile maxima
+  float red_l[kNumHeads][kWaves];          // per-wave sums, at the end
+  uint8_t ctab[4][16];                     // e8m0 block maxima of V: [token block][column block]
+  int32_t pages[kMaxItemPages];            // paged: page ids of the item
+};
+
+// Two-byte cache-to-LDS load: lane l's two bytes at src go to LDS dword
+// m0 + 4 l.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma_u16(const void* src, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_ushort %0, off nt"
+               :
+               : "v"(src), "s"(m0)
+               : "memory", "m0");
+}
+// The same from base + off (off: per lane, unsigned 32-bit).
+__device__ __forceinline__ void dma_u16(const uint8_t* base, uint32_t off, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_ushort %0, %1 nt"
+               :
+               : "v"(off), "s"(base), "s"(m0)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// fp4 (A) x fp8 (B) and fp8 x fp8 MX steps with A block scale sa (e8m0 in
+// byte `sel` of sa) and unit B scale.
+__device__ __forceinline__ f32x4 mfma_fp4_fp8(fp8x32 a, fp8x32 b, f32x4 c, uint32_t sa) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, 0, (int)sa, 0, 127);
+}
+__device__ __forceinline__ f32x4 mfma_fp8_sa(fp8x32 a, fp8x32 b, f32x4 c, uint32_t sa, int sel) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, (int)sa, 0, 127);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 1, (int)sa, 0, 127);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 2, (int)sa, 0, 127);
+    default: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 3, (int)sa, 0, 127);
+  }
+}
+
+// 8 e2m1 codes (low nibble first) times 2^j -> 8 e4m3 codes (two words),
+// through f16 (exact for the products here) and a rounding conversion.
+__device__ __forceinline__ void fp4x8_to_fp8(uint32_t w, float scale, uint32_t& lo, uint32_t& hi) {
+  typedef short i16x2 __attribute__((ext_vector_type(2)));
+  const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 0);
+  const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 1);
+  const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 2);
+  const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 3);
+  i16x2 a = {0, 0}, b = {0, 0};
+  a = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(a, p0, 1.0f, false);
+  a = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(a, p1, 1.0f, true);
+  b = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(b, p2, 1.0f, false);
+  b = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(b, p3, 1.0f, true);
+  lo = __builtin_bit_cast(uint32_t, a);
+  hi = __builtin_bit_cast(uint32_t, b);
+}
+
+// 8 e2m1 codes (low nibble first) times 2^-k, 0 <= k <= 5, -> 8 e4m3 codes
+// (two words) by table lookup: every nonzero e2m1 magnitude {0.5, 1, 1.5, 2,
+// 3, 4, 6} times 2^-k is a normal e4m3 number whose code is the k = 0 code
+// less k in the exponent field, so the 8-entry table (lut_lo: magnitudes
+// 0..3, lut_hi: 4..7) is a shifted constant; v_perm_b32 looks up four
+// magnitudes at once, the sign bit moves from bit 3 to bit 7, and the codes
+// of even and odd nibbles are interleaved back into column order.
+__device__ __forceinline__ void fp4x8_to_fp8_lut(uint32_t w, uint32_t lut_lo, uint32_t lut_hi, uint32_t& lo,
+                                                 uint32_t& hi) {
+  const uint32_t pe = __builtin_amdgcn_perm(lut_hi, lut_lo, w & 0x07070707u);          // even nibbles
+  const uint32_t po = __builtin_amdgcn_perm(lut_hi, lut_lo, (w >> 4) & 0x07070707u);   // odd nibbles
+  const uint32_t ce = ((w << 4) & 0x80808080u) | pe;
+  const uint32_t co = (w & 0x80808080u) | po;
+  lo = __builtin_amdgcn_perm(co, ce, 0x05010400u);  // columns 0, 1, 2, 3
+  hi = __builtin_amdgcn_perm(co, ce, 0x07030602u);  // columns 4, 5, 6, 7
+}
+
+// Maxima of the two 16-bit halves of v over the 32 lanes of this half wave,
+// in the vector unit: DPP lane swaps within quads (xor 1, xor 2), mirrors
+// within 8 and 16 lanes, then the exchange between the two 16-lane rows
+// (permlane16_swap); v_pk_max_u16 combines both halves at once.
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                __builtin_bit_cast(u16x2, b)));
+}
+__device__ __forceinline__ uint32_t half_wave_max2(uint32_t v) {
+  v = pk_max_u16(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  v = pk_max_u16(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  v = pk_max_u16(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = pk_max_u16(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));  // row_mirror
+  const auto x = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return pk_max_u16((uint32_t)x[0], (uint32_t)x[1]);
+}
+
+template <bool PAGED>
+__global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_mxfp4(Stage1Args a) {
+  __shared__ __attribute__((aligned(16))) Fp4Lds sh;
+
+  const WorkItem item = a.uniform_splits
+                            ? uniform_item(xcd_block(blockIdx.x, gridDim.x), a.uniform_splits, a.uniform_chunk,
+                                           a.uniform_len, a.uniform_base)
+                            : a.items[blockIdx.x];
+  const int tid = threadIdx.x;
+  if (item.slot == WorkItem::kEmpty) {  // empty sequence: its output is zero
+    uint4* dst = reinterpret_cast<uint4*>(a.out + (int64_t)item.batch * kNumHeads * kVDim);
+#pragma unroll
+    for (int k = 0; k < (kNumHeads * kVDim * 2 / 16) / kStage1Threads; ++k)
+      dst[tid + kStage1Threads * k] = uint4{0u, 0u, 0u, 0u};
+    return;
+  }
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  const int b = item.batch;
+  const int tok_last = item.tok_end - 1;
+  const int ntiles = (item.tok_end - item.tok_begin + kXTile - 1) / kXTile;
+
+  // The query first: 18 loads into the V tile, load k by wave k % 4.
+  {
+    const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(a.q + (int64_t)b * kNumHeads * kQkDim);
+    const uint32_t qm0 = lds_u32(&sh.v[0]);
+    for (int k = wave; k < kQLoads; k += kWaves) {
+      const int s = 64 * k + lane;
+      const int h = s / 72;
+      const int c = (s - 72 * h) ^ (h & 7);
+      dma_one(qsrc + (h * 72 + c) * 16, qm0 + 1024 * k);
+    }
+  }
+  const int64_t seq_base = item.kv_base;
+
+  int page0 = 0;
+  if constexpr (PAGED) {
+    page0 = item.tok_begin >> a.page_shift;
+    const int npages = min(((item.tok_end - 1) >> a.page_shift) - page0 + 1, kMaxItemPages);
+    for (int i = tid; i < npages; i += kStage1Threads)
+      sh.pages[i] = a.page_indices[seq_base + page0 + i];
+    __syncthreads();
+  }
+
+  // This lane's part of each of its wave's loads of a tile: code load j
+  // (global load 9w + j) fetches 16-byte chunk (row << 8 | chunk), scale
+  // load j (global load 5w + j) the scale pair (row << 8 | pair).
+  uint32_t rc[kXFp4PerWave], rs[kXScalePerWave];
+#pragma unroll
+  for (int j = 0; j < kXFp4PerWave; ++j) {
+    const int s = 64 * (kXFp4PerWave * wave + j) + lane;
+    const int r = s / 18;
+    rc[j] = (uint32_t)(r << 8 | (s - 18 * r));
+  }
+#pragma unroll
+  for (int j = 0; j < kXScalePerWave; ++j) {
+    const int s = min(64 * (kXScalePerWave * wave + j) + lane, kXScaleItems - 1);
+    const int r = s / kXScalePairs;
+    rs[j] = (uint32_t)(r << 8 | (s - kXScalePairs * r));
+  }
+  auto row_of = [&](int tok) -> int64_t {  // cache row of logical token tok
+    if constexpr (PAGED) {
+      const int pmask = (1 << a.page_shift) - 1;
+      const uint32_t page = (uint32_t)sh.pages[(tok >> a.page_shift) - page0];
+      return (int64_t)((page << a.page_shift) + (uint32_t)(tok & pmask));
+    } else {
+      return seq_base + tok;
+    }
+  };
+
+  // Offsets of this lane's loads from the tile's first row (contiguous
+  // cache): code load j reads at coff[j] + 1024 (j & 3) (the instruction
+  // offset of its group of four; 3072 bytes of bias keep coff >= 0), scale
+  // load j at soff[j].
+  uint32_t coff[kXFp4PerWave], soff[kXScalePerWave];
+#pragma unroll
+  for (int j = 0; j < kXFp4PerWave; ++j)
+    coff[j] = (rc[j] >> 8) * kXRow + 16 * (rc[j] & 0xFF) + 3072 - 1024 * (j & 3);
+#pragma unroll
+  for (int j = 0; j < kXScalePerWave; ++j)
+    soff[j] = (uint32_t)((rs[j] >> 8) * a.scale_stride) + 2 * (rs[j] & 0xFF);
+
+  // All of this wave's loads of tile t into raw slot t % 2.  Rows past the
+  // item's last token fetch that token's row (finite data, masked later).
+  auto issue = [&](int t) {
+    const int tok0 = item.tok_begin + t * kXTile;
+    const int lim = tok_last - tok0;
+    const uint32_t m0c = lds_u32(&sh.raw[t & 1][0]) + 1024 * kXFp4PerWave * wave;
+    const uint32_t m0s = lds_u32(&sh.raw[t & 1][kXFp4Bytes]) + 256 * kXScalePerWave * wave;
+    if constexpr (!PAGED) {
+      const uint8_t* cbase = uniform_ptr(a.kv + (seq_base + tok0) * kXRow - 3072);
+      const uint8_t* sbase = uniform_ptr(a.kv_mx_scales + (seq_base + tok0) * a.scale_stride);
+      uint32_t off[kXFp4PerWave], so[kXScalePerWave];
+      if (lim >= kXTile - 1) {  // a whole tile
+#pragma unroll
+        for (int j = 0; j < kXFp4PerWave; ++j) off[j] = coff[j];
+#pragma unroll
+        for (int j = 0; j < kXScalePerWave; ++j) so[j] = soff[j];
+      } else {
+#pragma unroll
+        for (int j = 0; j < kXFp4PerWave; ++j)
+          off[j] = min((int)(rc[j] >> 8), lim) * kXRow + 16 * (rc[j] & 0xFF) + 3072 - 1024 * (j & 3);
+#pragma unroll
+        for (int j = 0; j < kXScalePerWave; ++j)
+          so[j] = (uint32_t)(min((int)(rs[j] >> 8), lim) * a.scale_stride) + 2 * (rs[j] & 0xFF);
+      }
+      dma_group<4>(cbase, off, m0c);
+      dma_group<4>(cbase, off + 4, m0c + 4096);
+      dma_group<1>(cbase, off + 8, m0c + 8192);
+#pragma unroll
+      for (int j = 0; j < kXScalePerWave; ++j) dma_u16(sbase, so[j], m0s + 256 * j);
+    } else {
+      const uint8_t* src[kXFp4PerWave];
+#pragma unroll
+      for (int j = 0; j < kXFp4PerWave; ++j) {
+        const int r = min((int)(rc[j] >> 8), lim);
+        src[j] = a.kv + row_of(tok0 + r) * kXRow + 16 * (rc[j] & 0xFF) - 1024 * (j & 3);
+      }
+      dma_group<4>(src, m0c);
+      dma_group<4>(src + 4, m0c + 4096);
+      dma_one(src[8], m0c + 8192);  // load 8: no instruction offset
+#pragma unroll
+      for (int j = 0; j < kXScalePerWave; ++j) {
+        const int r = min((int)(rs[j] >> 8), lim);
+        dma_u16(a.kv_mx_scales + row_of(tok0 + r) * a.scale_stride + 2 * (rs[j] & 0xFF), m0s + 256 * j);
+      }
+    }
+  };
+
+  issue(0);
+  if (ntiles > 1) issue(1);
+  if (ntiles > 1)
+    wait_loads<2 * kXLoadsPerWave>();  // the query has landed
+  else
+    wait_loads<kXLoadsPerWave>();
+  lds_barrier();
+
+  // Query, B operand of the scores, scaled by 2^s and split into e4m3 hi +
+  // lo.  K-step K (0..3): bytes b < 16 column 128K + 16g + b, bytes 16..31
+  // column 128K + 64 + 16g + b - 16; rope step: bytes b < 16 column
+  // 512 + 16g + b, bytes 16..31 zero.
+  fp8x32 qh[4], ql[4], rh, rl;
+  float xscale;
+  {
+    const uint8_t* qlds = &sh.v[0];
+    bf16x8 qv[18];  // [4K + i]: chunk 16K + 2g + {0, 1, 8, 9}[i]; [16 + h]: chunk 64 + 2g + h
+#pragma unroll
+    for (int K = 0; K < 4; ++K)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        qv[4 * K + i] =
+            *reinterpret_cast<const bf16x8*>(qlds + 16 * q_slot(r16, 16 * K + 2 * g + (i & 1) + 8 * (i >> 1)));
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      qv[16 + h] = *reinterpret_cast<const bf16x8*>(qlds + 16 * q_slot(r16, 64 + 2 * g + h));
+    float amax = 0.f;
+#pragma unroll
+    for (int k = 0; k < 18; ++k)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)qv[k][e]));
+    amax = xor_max_groups(amax);
+    const int s = (amax > 0.f) ? 8 - __builtin_amdgcn_frexp_expf(amax) : 0;
+    xscale = a.score_scale * __builtin_ldexpf(1.0f, -s);
+    uint32_t hw[36], lw[36];
+#pragma unroll
+    for (int k = 0; k < 18; ++k)
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+        split_fp8x4(__builtin_ldexpf((float)qv[k][4 * m], s), __builtin_ldexpf((float)qv[k][4 * m + 1], s),
+                    __builtin_ldexpf((float)qv[k][4 * m + 2], s), __builtin_ldexpf((float)qv[k][4 * m + 3], s),
+                    hw[2 * k + m], lw[2 * k + m]);
+#pragma unroll
+    for (int K = 0; K < 4; ++K)
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        qh[K][d] = (int)hw[8 * K + d];
+        ql[K][d] = (int)lw[8 * K + d];
+      }
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      rh[d] = d < 4 ? (int)hw[32 + d] : 0;
+      rl[d] = d < 4 ? (int)lw[32 + d] : 0;
+    }
+  }
+
+  f32x4 o[8];  // O^T[dim 128w + 16v + 4g + i][head r16]
+#pragma unroll
+  for (int v = 0; v < 8; ++v) o[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref = kNegInf;
+  float l_part = 0.f;
+
+  // Reads of this lane.  Scores: rows 32w + 16s + r16 of the raw tile.  V^T:
+  // tr8 read q (0..3) gives tokens tb(q) + (0..7), tb = 16g + 8q (q < 2) or
+  // 64 + 16g + 8(q - 2), from rows tb(q) + (r16 >> 1), columns
+  // 128w + 16v + 8(r16 & 1).  Conversion: the half wave h = 2w + lane / 32
+  // takes token block cv_tb = h & 3 and the column blocks of parity
+  // cv_odd = h >> 2; the lane, token row 32 cv_tb + (lane & 31).
+  const int hw_id = 2 * wave + (lane >> 5);
+  const int cv_tb = hw_id & 3;
+  const int cv_odd = hw_id >> 2;
+  const int cv_row = 32 * cv_tb + (lane & 31);
+  int voff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    voff[q] = ((q < 2 ? 16 * g + 8 * q : 64 + 16 * g + 8 * (q - 2)) + (r16 >> 1)) * kXVRow + 128 * wave +
+              8 * (r16 & 1);
+  uint8_t* const p_hi = &sh.p[0][r16][0];
+  uint8_t* const p_lo = &sh.p[1][r16][0];
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int tok0 = item.tok_begin + t * kXTile;
+    if (t + 1 < ntiles)
+      wait_loads<kXLoadsPerWave>();  // tile t, not tile t + 1 behind it
+    else
+      wait_loads<0>();
+    lds_barrier();  // tile t everywhere; everyone is past tile t - 1
+    const uint8_t* raw = &sh.raw[t & 1][0];
+    const uint8_t* sdw = raw + kXFp4Bytes;  // scale pair (row, p) at dword 9 row + p
+
+    // ---- scores of tokens 32w + 16s + (0..15), s = 0, 1 ----
+    f32x4 sacc[2][2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      sacc[s][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      sacc[s][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int row = 32 * wave + 16 * s + r16;
+      const uint8_t* rp = raw + row * kXRow;
+      const uint8_t* sp = sdw + 4 * kXScalePairs * row;
+#pragma unroll
+      for (int K = 0; K < 4; ++K) {
+        const int blk = 4 * K + g;
+        const uint32_t sa = sp[4 * (blk >> 1) + (blk & 1)];
+        const u32x4 w = *reinterpret_cast<const u32x4*>(rp + 64 * K + 16 * g);
+        const fp8x32 ka = fp8x32{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
+        sacc[s][0] = mfma_fp4_fp8(ka, qh[K], sacc[s][0], sa);
+        sacc[s][1] = mfma_fp4_fp8(ka, ql[K], sacc[s][1], sa);
+      }
+      u32x4 w = {0u, 0u, 0u, 0u};
+      uint32_t sa = 127;
+      if (g < 2) {
+        w = *reinterpret_cast<const u32x4*>(rp + 256 + 16 * g);
+        sa = sp[4 * 8 + g];
+      }
+      const fp8x32 ka = fp8x32{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
+      sacc[s][0] = mfma_fp4_fp8(ka, rh, sacc[s][0], sa);
+      sacc[s][1] = mfma_fp4_fp8(ka, rl, sacc[s][1], sa);
+    }
+
+    // ---- softmax: x[s][i] is token 32w + 16s + 4g + i of head r16 ----
+    float x[2][4];
+    float tmax = kNegInf;
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[s][i] = (sacc[s][0][i] + sacc[s][1][i]) * xscale;
+        if (tok0 + 32 * wave + 16 * s + 4 * g + i > tok_last) x[s][i] = kNegInf;
+        tmax = fmaxf(tmax, x[s][i]);
+      }
+    tmax = xor_max_groups(tmax);
+    if (g == 0) sh.red_m[r16][wave] = tmax;
+    float p[2][4];
+    uint32_t ph[2], pl[2];
+    {
+      const float mr = (m_ref == kNegInf) ? 0.0f : m_ref;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[s][i] = __builtin_amdgcn_exp2f(x[s][i] - mr);
+        split_fp8x4(p[s][0], p[s][1], p[s][2], p[s][3], ph[s], pl[s]);
+        *reinterpret_cast<uint32_t*>(p_hi + 32 * wave + 16 * s + 4 * g) = ph[s];
+        *reinterpret_cast<uint32_t*>(p_lo + 32 * wave + 16 * s + 4 * g) = pl[s];
+      }
+    }
+
+    // ---- V of this tile to e4m3, per block of 32 tokens x 32 columns ----
+    // This lane converts token row cv_row, column blocks 2k + cv_odd
+    // (k = 0..7): all reads first, then the block maxima (two per
+    // reduction), the conversions and the writes.
+    {
+      uint32_t e[8];
+      u32x4 w[8];
+      const uint8_t* rsrc = raw + cv_row * kXRow + 16 * cv_odd;
+      const uint8_t* ssrc = sdw + 4 * kXScalePairs * cv_row + cv_odd;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        e[k] = ssrc[4 * k];
+        w[k] = *reinterpret_cast<const u32x4*>(rsrc + 32 * k);
+      }
+      uint32_t c[8];
+#pragma unroll
+      for (int k = 0; k < 8; k += 2) {
+        const uint32_t m = half_wave_max2(e[k] | (e[k + 1] << 16));
+        c[k] = m & 0xFFFF;
+        c[k + 1] = m >> 16;
+      }
+      if ((lane & 31) == 0) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) sh.ctab[cv_tb][2 * k + cv_odd] = (uint8_t)c[k];
+      }
+      uint8_t* vdst = &sh.v[cv_row * kXVRow + 32 * cv_odd];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int j = max((int)e[k] - (int)c[k], -126);  // <= 0
+        uint32_t e8[8];  // 32 e4m3 codes, columns 32cb + 4i .. +3 in word i
+        if (__ballot(j < -5) == 0) {  // the whole wave by table
+          const uint32_t kk = (uint32_t)(-j);
+          const uint32_t lut_lo = 0x3C383000u - kk * 0x08080800u;
+          const uint32_t lut_hi = 0x4C484440u - kk * 0x08080808u;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) fp4x8_to_fp8_lut(w[k][i], lut_lo, lut_hi, e8[2 * i], e8[2 * i + 1]);
+        } else {  // a scale more than 5 binades below its block maximum: exact rounding conversions
+          const float scale = __uint_as_float((uint32_t)(127 + j) << 23);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) fp4x8_to_fp8(w[k][i], scale, e8[2 * i], e8[2 * i + 1]);
+        }
+        *reinterpret_cast<u32x4*>(vdst + 64 * k) = u32x4{e8[0], e8[1], e8[2], e8[3]};
+        *reinterpret_cast<u32x4*>(vdst + 64 * k + 16) = u32x4{e8[4], e8[5], e8[6], e8[7]};
+      }
+    }
+    lds_barrier();  // P^T, maxima, the V tile and its block maxima; raw slot t % 2 is free
+    if (t + 2 < ntiles) issue(t + 2);
+
+    const f32x4 maxima = *reinterpret_cast<const f32x4*>(&sh.red_m[r16][0]);
+    fp8x32 bh = join16(*reinterpret_cast<const u32x4*>(p_hi + 16 * g),
+                       *reinterpret_cast<const u32x4*>(p_hi + 64 + 16 * g));
+    fp8x32 bl = join16(*reinterpret_cast<const u32x4*>(p_lo + 16 * g),
+                       *reinterpret_cast<const u32x4*>(p_lo + 64 + 16 * g));
+    const uint32_t csa = *reinterpret_cast<const uint32_t*>(&sh.ctab[g][4 * wave]);
+    const float tile_max = fmaxf(fmaxf(maxima[0], maxima[1]), fmaxf(maxima[2], maxima[3]));
+    if (__ballot(tile_max > m_ref + kLazyRescale) != 0) {
+      const float m_new = fmaxf(m_ref, tile_max);
+      const float alpha = (m_ref == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
+#pragma unroll
+      for (int v = 0; v < 8; ++v) o[v] *= alpha;
+      l_part *= alpha;
+      m_ref = m_new;
+      lds_barrier();  // everyone has read the old P^T
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[s][i] = __builtin_amdgcn_exp2f(x[s][i] - m_ref);
+        split_fp8x4(p[s][0], p[s][1], p[s][2], p[s][3], ph[s], pl[s]);
+        *reinterpret_cast<uint32_t*>(p_hi + 32 * wave + 16 * s + 4 * g) = ph[s];
+        *reinterpret_cast<uint32_t*>(p_lo + 32 * wave + 16 * s + 4 * g) = pl[s];
+      }
+      lds_barrier();
+      bh = join16(*reinterpret_cast<const u32x4*>(p_hi + 16 * g),
+                  *reinterpret_cast<const u32x4*>(p_hi + 64 + 16 * g));
+      bl = join16(*reinterpret_cast<const u32x4*>(p_lo + 16 * g),
+                  *reinterpret_cast<const u32x4*>(p_lo + 64 + 16 * g));
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) l_part += (p[s][0] + p[s][1]) + (p[s][2] + p[s][3]);
+
+    // ---- O^T += V^T P^T, columns 128w + 16v, block scale 2^(c - 127) ----
+#pragma unroll
+    for (int v = 0; v < 8; v += 2) {
+      fp8x32 va[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const i32x2 raw2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(&sh.v[voff[q] + 16 * (v + u)]));
+          va[u][2 * q] = raw2[0];
+          va[u][2 * q + 1] = raw2[1];
+        }
+      o[v] = mfma_fp8_sa(va[0], bh, o[v], csa, v >> 1);
+      o[v + 1] = mfma_fp8_sa(va[1], bh, o[v + 1], csa, v >> 1);
+      o[v] = mfma_fp8_sa(va[0], bl, o[v], csa, v >> 1);
+      o[v + 1] = mfma_fp8_sa(va[1], bl, o[v + 1], csa, v >> 1);
+    }
+  }
+
+  const float l_w = xor_sum_groups(l_part);
+  if (g == 0) sh.red_l[r16][wave] = l_w;
+  lds_barrier();
+  const f32x4 ls = *reinterpret_cast<const f32x4*>(&sh.red_l[r16][0]);
+  const float L = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+  finish_item(a, item, tid, wave, lane, o, 1.0f / L, m_ref + __log2f(L));
+}
+
+}  // namespace
+
+const void* stage1_mxfp4_kernel(bool paged) {
+  return paged ? reinterpret_cast<const void*>(&mla_stage1_mxfp4<true>)
+               : reinterpret_cast<const void*>(&mla_stage1_mxfp4<false>);
+}
+
+}  // namespace mla

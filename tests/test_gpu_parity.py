@@ -119,6 +119,28 @@ def test_constant_values(B, oracle_mod, fmt):
     assert np.abs(got - ref).max() <= 1e-2
 
 
+def test_mxfp4_wide_block_scales(B, oracle_mod):
+    """Rows scaled by 2^r, r uniform in -10..10 per token, so the 32 tokens of
+    a block have e8m0 scales up to 20 binades apart: V is converted to e4m3
+    relative to each block's largest scale by table where every scale is
+    within 5 binades of it, else by rounding conversions (exact within 8)."""
+    lens = [700, 129, 64]
+    rng = np.random.default_rng(41)
+    kv = rng.standard_normal((sum(lens), 576)).astype(np.float32)
+    kv *= np.exp2(rng.integers(-10, 11, size=(sum(lens), 1))).astype(np.float32)
+    case = synth.make_case("mxfp4", lens, seed=41, kv_values=kv)
+    for split in (0, 3):
+        check_close(run_gpu(B, case, split), oracle_out(oracle_mod, case), "mxfp4", f"wide scales split {split}")
+
+
+@pytest.mark.parametrize("stride", [18, 19, 20])
+def test_mxfp4_scale_strides(B, oracle_mod, stride):
+    """Scale rows at any stride >= 18; an odd stride (scales not 2-byte
+    aligned) runs the bf16-decoding kernel instead of the MX one."""
+    case = synth.make_case("mxfp4", [1000, 300, 5], seed=42, scale_stride=stride)
+    check_close(run_gpu(B, case), oracle_out(oracle_mod, case), "mxfp4", f"stride {stride}")
+
+
 def test_empty_sequences_give_zero(B, oracle_mod):
     case = synth.make_case("fp8", [0, 100, 0, 1], seed=24)
     got = run_gpu(B, case)
