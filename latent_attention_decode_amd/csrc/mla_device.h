@@ -205,23 +205,28 @@ __device__ __forceinline__ fp8x32 join16(u32x4 a, u32x4 b) {
   return fp8x32{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
 }
 
-// End of a split-kernel work item, with every wave holding O^T[128w + 16v +
-// 4g + i][r16] (unnormalised) in o, f = scale / L its normaliser and lse the
-// item's log2-sum-exp.  The item is the whole sequence: write bf16 out.  It is
-// one of several: write the partial (and, when a.counters is set, merge the
-// sequence's partials if this item finishes last; see Stage1Args).
-__device__ __forceinline__ void finish_item(const Stage1Args& a, const WorkItem& item, int tid, int wave,
-                                            int lane, const f32x4 (&o)[8], float f, float lse) {
+// End of a split-kernel work item.  The lanes of the workgroup together hold
+// O^T (unnormalised): this lane has, in o[v], O^T[128W + 16(vb + v) + 4g +
+// i][r16] for its 128-column group W and column tiles vb .. vb + NV - 1 of
+// it; f = scale / L is the normaliser and lse the item's log2-sum-exp.  The
+// item is the whole sequence: write bf16 out.  It is one of several: write
+// the partial (and, when a.counters is set, merge the sequence's partials if
+// this item finishes last; see Stage1Args).
+template <int NV>
+__device__ __forceinline__ void finish_item(const Stage1Args& a, const WorkItem& item, int tid, int W, int vb,
+                                            int lane, const f32x4 (&o)[NV], float f, float lse) {
   const int r16 = lane & 15;
   const int g = lane >> 4;
   const int b = item.batch;
-  f32x4 res[8];  // this lane's normalised output, O^T[128w + 16v + 4g + i][r16]
+  f32x4 res[NV];  // this lane's normalised output
 #pragma unroll
-  for (int v = 0; v < 8; ++v) res[v] = o[v] * f;
+  for (int v = 0; v < NV; ++v) res[v] = o[v] * f;
   if (item.slot >= 0) {
     if (!a.counters) {  // the merge kernel combines the partials
-      store_partial(a.part_o, item.slot, wave, lane, o, f);
-      if (wave == 0 && g == 0) a.part_lse[(int64_t)item.slot * kNumHeads + r16] = lse;
+      f32x4* dst = reinterpret_cast<f32x4*>(a.part_o) + (int64_t)item.slot * kSlotFloat4 + 512 * W + lane;
+#pragma unroll
+      for (int v = 0; v < NV; ++v) dst[64 * (vb + v)] = res[v];  // the layout of store_partial
+      if (W == 0 && vb == 0 && g == 0) a.part_lse[(int64_t)item.slot * kNumHeads + r16] = lse;
       return;
     }
 
@@ -232,15 +237,15 @@ __device__ __forceinline__ void finish_item(const Stage1Args& a, const WorkItem&
     // without a device-scope release / acquire fence, which would write back
     // or invalidate the whole L2 of the XCD.  The item that finishes last
     // merges; nothing waits on another workgroup.
-    // Layout of a slot here: float (4v + i) of lane l of wave w at
-    // 2048 w + 64 (4v + i) + l, so that each store writes 256 bytes in a row.
-    float* pdst = a.part_o + (int64_t)item.slot * (4 * kSlotFloat4) + 2048 * wave + lane;
+    // Layout of a slot here: float (4v + i) of lane l in column group W at
+    // 2048 W + 64 (4v + i) + l, so that each store writes 256 bytes in a row.
+    float* pdst = a.part_o + (int64_t)item.slot * (4 * kSlotFloat4) + 2048 * W + lane;
 #pragma unroll
-    for (int v = 0; v < 8; ++v)
+    for (int v = 0; v < NV; ++v)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        __hip_atomic_store(pdst + 64 * (4 * v + i), res[v][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (wave == 0 && g == 0)
+        __hip_atomic_store(pdst + 64 * (4 * (vb + v) + i), res[v][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (W == 0 && vb == 0 && g == 0)
       __hip_atomic_store(a.part_lse + (int64_t)item.slot * kNumHeads + r16, lse, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's stores are complete
@@ -259,17 +264,18 @@ __device__ __forceinline__ void finish_item(const Stage1Args& a, const WorkItem&
     // included, as stored), so the result does not depend on which item
     // finished last.  Each lane reads the float4 numbers it stored itself.
     float ls[kFusedMergeMaxSlots];
-    f32x4 po[4][8];  // one group of four partials
+    f32x4 po[4][NV];  // one group of four partials
     auto load_group = [&](int s0) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int sl = item.slot_begin + min(s0 + k, item.nslots - 1);
-        float* src = a.part_o + (int64_t)sl * (4 * kSlotFloat4) + 2048 * wave + lane;
+        float* src = a.part_o + (int64_t)sl * (4 * kSlotFloat4) + 2048 * W + lane;
 #pragma unroll
-        for (int v = 0; v < 8; ++v)
+        for (int v = 0; v < NV; ++v)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            po[k][v][i] = __hip_atomic_load(src + 64 * (4 * v + i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            po[k][v][i] =
+                __hip_atomic_load(src + 64 * (4 * (vb + v) + i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     };
 #pragma unroll
@@ -281,29 +287,29 @@ __device__ __forceinline__ void finish_item(const Stage1Args& a, const WorkItem&
 #pragma unroll
     for (int k = 0; k < kFusedMergeMaxSlots; ++k)
       if (k < item.nslots) M = fmaxf(M, ls[k]);
-    float W = 0.0f;
+    float wsum = 0.0f;
 #pragma unroll
-    for (int v = 0; v < 8; ++v) res[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int v = 0; v < NV; ++v) res[v] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s0 = 0; s0 < kFusedMergeMaxSlots; s0 += 4) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const float w = s0 + k < item.nslots ? __builtin_amdgcn_exp2f(ls[s0 + k] - M) : 0.0f;
-        W += w;
+        wsum += w;
 #pragma unroll
-        for (int v = 0; v < 8; ++v) res[v] += w * po[k][v];
+        for (int v = 0; v < NV; ++v) res[v] += w * po[k][v];
       }
       if (s0 + 4 >= item.nslots) break;
       load_group(s0 + 4);
     }
-    const float inv = 1.0f / W;
+    const float inv = 1.0f / wsum;
 #pragma unroll
-    for (int v = 0; v < 8; ++v) res[v] *= inv;
+    for (int v = 0; v < NV; ++v) res[v] *= inv;
   }
-  uint16_t* dst = a.out + ((int64_t)b * kNumHeads + r16) * kVDim + 128 * wave + 4 * g;
+  uint16_t* dst = a.out + ((int64_t)b * kNumHeads + r16) * kVDim + 128 * W + 4 * g;
 #pragma unroll
-  for (int v = 0; v < 8; ++v)
-    *reinterpret_cast<uint2*>(dst + 16 * v) =
+  for (int v = 0; v < NV; ++v)
+    *reinterpret_cast<uint2*>(dst + 16 * (vb + v)) =
         uint2{pack_bf16x2(res[v][0], res[v][1]), pack_bf16x2(res[v][2], res[v][3])};
 }
 

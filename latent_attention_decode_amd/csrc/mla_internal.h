@@ -16,6 +16,7 @@ constexpr int kTile = 32;        // token granularity of the planner's splits
 constexpr int kPlanTile = 128;   // tokens per stage-1 tile (fp8); items are whole tiles
 constexpr int kWaves = 4;        // waves per stage-1 workgroup
 constexpr int kStage1Threads = 64 * kWaves;
+constexpr int kStage1ThreadsMxfp4 = 512;  // the MXFP4 split kernel runs eight waves
 constexpr int kMergeThreads = 256;  // two float4 of one head per thread
 
 enum KvFormat : int { kBf16 = 0, kFp8 = 1, kMxfp4 = 2 };

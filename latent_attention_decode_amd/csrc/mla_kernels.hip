@@ -554,9 +554,10 @@ hipError_t launch_stage1(int fmt, bool paged, const Stage1Args& a, int num_items
     fn = paged ? reinterpret_cast<const void*>(&mla_stage1<kMxfp4, true>)
                : reinterpret_cast<const void*>(&mla_stage1<kMxfp4, false>);
   if (!fn) return hipErrorInvalidValue;
+  const int threads = (fmt == kMxfp4 && stage1_dedicated(fmt, a)) ? kStage1ThreadsMxfp4 : kStage1Threads;
   Stage1Args args = a;
   void* params[] = {&args};
-  return launch(fn, dim3(num_items), dim3(kStage1Threads), params, s, start, stop);
+  return launch(fn, dim3(num_items), dim3(threads), params, s, start, stop);
 }
 
 hipError_t launch_merge(const MergeArgs& a, int num_merge_seqs, hipStream_t s, hipEvent_t start,
@@ -576,7 +577,8 @@ hipError_t kernel_attributes(int fmt, bool paged, int which, hipFuncAttributes* 
 hipError_t stage1_occupancy(int fmt, bool paged, int* blocks_per_cu) {
   const void* fn = pick_stage1(fmt, paged);
   if (!fn) return hipErrorInvalidValue;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn, kStage1Threads, 0);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn,
+                                                      fmt == kMxfp4 ? kStage1ThreadsMxfp4 : kStage1Threads, 0);
 }
 
 }  // namespace mla

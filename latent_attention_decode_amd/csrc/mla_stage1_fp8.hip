@@ -428,7 +428,7 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a
   const f32x4 ls = *reinterpret_cast<const f32x4*>(&sh.red_l[r16][0]);
   const float L = (ls[0] + ls[1]) + (ls[2] + ls[3]);
   const float f = kv_scale / L;
-  finish_item(a, item, tid, wave, lane, o, f, m_ref + __log2f(L));
+  finish_item<8>(a, item, tid, wave, 0, lane, o, f, m_ref + __log2f(L));
 }
 
 }  // namespace

@@ -1,8 +1,12 @@
 // gfx950 split kernel for an MXFP4 cache (e2m1 codes, one e8m0 scale per 32
 // columns of a row): single-token multi-head latent attention decode, one
-// 256-thread workgroup per planned work item, 128-token tiles streamed
-// HBM -> LDS by cache-to-LDS loads, both contractions on the MX matrix
-// instruction v_mfma_scale_f32_16x16x128_f8f6f4.
+// 512-thread workgroup (eight waves, two per SIMD) per planned work item,
+// 128-token tiles streamed HBM -> LDS by cache-to-LDS loads, both
+// contractions on the MX matrix instruction v_mfma_scale_f32_16x16x128_f8f6f4.
+// Wave w scores tokens 16w..16w+15 and accumulates output columns
+// 64w..64w+63; the second wave on each SIMD hides the latencies of the first
+// (the V conversion below makes this kernel heavier in vector and LDS work
+// than the fp8 one, and its tiles are half the bytes).
 //
 // Operand layout of that instruction on gfx950 (measured): in each group g of
 // 16 lanes, an fp4 operand holds 32 consecutive k-values 32g..32g+31, an fp8
@@ -32,8 +36,9 @@
 //
 // Data movement: per tile, 36 cache-to-LDS loads of 1 KB bring the 128 rows
 // of e2m1 codes (288 bytes each, rows past the item's end repeat its last
-// row) and 20 two-byte loads per lane group bring the 18 scale bytes of each
-// row, two per LDS dword (the two-byte form writes one dword per lane).  Two
+// row) and 20 two-byte loads bring the 18 scale bytes of each row, two per
+// LDS dword (the two-byte form writes one dword per lane); waves 0-3 issue
+// five code and two scale loads, waves 4-7 four and three.  Two
 // raw tiles are in flight while a third is worked on: a raw slot is free
 // again as soon as its tile is scored and its V converted.
 #include <hip/hip_runtime.h>
@@ -45,25 +50,27 @@
 namespace mla {
 namespace {
 
+constexpr int kXWaves = 8;
+constexpr int kXThreads = 64 * kXWaves;
+static_assert(kXThreads == kStage1ThreadsMxfp4, "launch shape");
 constexpr int kXTile = 128;                        // tokens per tile
 constexpr int kXRow = kQkDim / 2;                  // 288 bytes of e2m1 codes per row
 constexpr int kXFp4Bytes = kXTile * kXRow;         // 36864
 constexpr int kXFp4Loads = kXFp4Bytes / 1024;      // 36
-constexpr int kXFp4PerWave = kXFp4Loads / kWaves;  // 9
 constexpr int kXScalePairs = kQkDim / 64;          // 9 two-byte scale pairs per row
 constexpr int kXScaleItems = kXTile * kXScalePairs;  // 1152
-constexpr int kXScalePerWave = 5;                  // two-byte loads per wave and tile
-constexpr int kXScaleLoads = kWaves * kXScalePerWave;  // 20 (1280 lanes >= 1152 pairs)
+constexpr int kXScaleLoads = 20;                   // 1280 lanes >= 1152 pairs
 constexpr int kXScaleBytes = kXScaleLoads * 256;   // one dword per lane
 constexpr int kXRawBytes = kXFp4Bytes + kXScaleBytes;
-constexpr int kXLoadsPerWave = kXFp4PerWave + kXScalePerWave;  // 14
+constexpr int kXLoadsPerWave = 7;                  // 5 + 2 (waves 0-3) or 4 + 3 (waves 4-7)
 constexpr int kXVRow = kVDim + 16;                 // bytes per row of the e4m3 V tile (512 + pad)
-constexpr int kXVBytes = kXTile * kXVRow;          // 65536
+constexpr int kXVBytes = kXTile * kXVRow;
 constexpr int kQBytes = kNumHeads * kQkDim * 2;    // bf16 query of one sequence
 constexpr int kQLoads = kQBytes / 1024;            // 18
 constexpr int kPRow = kXTile + 16;                 // bytes per head row of P^T
 constexpr int kMaxItemPages = 512;                 // page ids of one item staged in LDS
-static_assert(kXFp4Loads == kWaves * kXFp4PerWave && kXScaleLoads * 64 >= kXScaleItems, "load split");
+static_assert(4 * 5 + 4 * 4 == kXFp4Loads && 4 * 2 + 4 * 3 == kXScaleLoads && kXScaleLoads * 64 >= kXScaleItems,
+              "load split");
 static_assert(kQBytes <= kXVBytes, "the query is staged in the V tile");
 
 // Position of 16-byte chunk c (0..71) of query head h.  (The V tile needs
@@ -75,8 +82,8 @@ struct Fp4Lds {
   uint8_t raw[2][kXRawBytes];              // e2m1 rows, then the scale dwords
   uint8_t v[kXVBytes];                     // V of the current tile as e4m3 [token][dim]; first the query
   uint8_t p[2][kNumHeads][kPRow];          // P^T hi / lo as [head][token]
-  float red_m[kNumHeads][kWaves];          // per-wave tile maxima
-  float red_l[kNumHeads][kWaves];          // per-wave sums, at the end
+  float red_m[kNumHeads][kXWaves];         // per-wave tile maxima
+  float red_l[kNumHeads][kXWaves];         // per-wave sums, at the end
   uint8_t ctab[4][16];                     // e8m0 block maxima of V: [token block][column block]
   int32_t pages[kMaxItemPages];            // paged: page ids of the item
 };
@@ -167,7 +174,7 @@ __device__ __forceinline__ uint32_t half_wave_max2(uint32_t v) {
 }
 
 template <bool PAGED>
-__global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_mxfp4(Stage1Args a) {
+__global__ __launch_bounds__(kXThreads, 1) void mla_stage1_mxfp4(Stage1Args a) {
   __shared__ __attribute__((aligned(16))) Fp4Lds sh;
 
   const WorkItem item = a.uniform_splits
@@ -178,8 +185,8 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_mxfp4(Stage1Args
   if (item.slot == WorkItem::kEmpty) {  // empty sequence: its output is zero
     uint4* dst = reinterpret_cast<uint4*>(a.out + (int64_t)item.batch * kNumHeads * kVDim);
 #pragma unroll
-    for (int k = 0; k < (kNumHeads * kVDim * 2 / 16) / kStage1Threads; ++k)
-      dst[tid + kStage1Threads * k] = uint4{0u, 0u, 0u, 0u};
+    for (int k = 0; k < (kNumHeads * kVDim * 2 / 16) / kXThreads; ++k)
+      dst[tid + kXThreads * k] = uint4{0u, 0u, 0u, 0u};
     return;
   }
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -189,12 +196,13 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_mxfp4(Stage1Args
   const int b = item.batch;
   const int tok_last = item.tok_end - 1;
   const int ntiles = (item.tok_end - item.tok_begin + kXTile - 1) / kXTile;
+  const bool lowq = wave < 4;  // waves 0-3: five code loads and two scale loads per tile
 
-  // The query first: 18 loads into the V tile, load k by wave k % 4.
+  // The query first: 18 loads into the V tile, load k by wave k % 8.
   {
     const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(a.q + (int64_t)b * kNumHeads * kQkDim);
     const uint32_t qm0 = lds_u32(&sh.v[0]);
-    for (int k = wave; k < kQLoads; k += kWaves) {
+    for (int k = wave; k < kQLoads; k += kXWaves) {
       const int s = 64 * k + lane;
       const int h = s / 72;
       const int c = (s - 72 * h) ^ (h & 7);
@@ -207,24 +215,26 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_mxfp4(Stage1Args
   if constexpr (PAGED) {
     page0 = item.tok_begin >> a.page_shift;
     const int npages = min(((item.tok_end - 1) >> a.page_shift) - page0 + 1, kMaxItemPages);
-    for (int i = tid; i < npages; i += kStage1Threads)
+    for (int i = tid; i < npages; i += kXThreads)
       sh.pages[i] = a.page_indices[seq_base + page0 + i];
     __syncthreads();
   }
 
-  // This lane's part of each of its wave's loads of a tile: code load j
-  // (global load 9w + j) fetches 16-byte chunk (row << 8 | chunk), scale
-  // load j (global load 5w + j) the scale pair (row << 8 | pair).
-  uint32_t rc[kXFp4PerWave], rs[kXScalePerWave];
+  // This wave's loads of a tile: code loads j0 .. j0 + 4 (or + 3), scale
+  // loads s0 .. s0 + 1 (or + 2); code load j fetches 16-byte chunk
+  // (row << 8 | chunk), scale load s the scale pair (row << 8 | pair).
+  const int j0 = lowq ? 5 * wave : 20 + 4 * (wave - 4);
+  const int s0 = lowq ? 2 * wave : 8 + 3 * (wave - 4);
+  uint32_t rc[5], rs[3];
 #pragma unroll
-  for (int j = 0; j < kXFp4PerWave; ++j) {
-    const int s = 64 * (kXFp4PerWave * wave + j) + lane;
+  for (int j = 0; j < 5; ++j) {
+    const int s = min(64 * (j0 + j) + lane, 64 * kXFp4Loads - 1);
     const int r = s / 18;
     rc[j] = (uint32_t)(r << 8 | (s - 18 * r));
   }
 #pragma unroll
-  for (int j = 0; j < kXScalePerWave; ++j) {
-    const int s = min(64 * (kXScalePerWave * wave + j) + lane, kXScaleItems - 1);
+  for (int j = 0; j < 3; ++j) {
+    const int s = min(64 * (s0 + j) + lane, kXScaleItems - 1);
     const int r = s / kXScalePairs;
     rs[j] = (uint32_t)(r << 8 | (s - kXScalePairs * r));
   }
@@ -237,63 +247,62 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_mxfp4(Stage1Args
       return seq_base + tok;
     }
   };
-
-  // Offsets of this lane's loads from the tile's first row (contiguous
-  // cache): code load j reads at coff[j] + 1024 (j & 3) (the instruction
-  // offset of its group of four; 3072 bytes of bias keep coff >= 0), scale
-  // load j at soff[j].
-  uint32_t coff[kXFp4PerWave], soff[kXScalePerWave];
+  // Offsets from the tile's first row (contiguous cache): code load j at
+  // coff[j] + 1024 j (the instruction offset within its group of four, none
+  // for j = 4; 3072 bytes of bias keep coff >= 0), scale load j at soff[j].
+  uint32_t coff[5], soff[3];
 #pragma unroll
-  for (int j = 0; j < kXFp4PerWave; ++j)
-    coff[j] = (rc[j] >> 8) * kXRow + 16 * (rc[j] & 0xFF) + 3072 - 1024 * (j & 3);
+  for (int j = 0; j < 5; ++j) coff[j] = (rc[j] >> 8) * kXRow + 16 * (rc[j] & 0xFF) + 3072 - 1024 * (j & 3);
 #pragma unroll
-  for (int j = 0; j < kXScalePerWave; ++j)
-    soff[j] = (uint32_t)((rs[j] >> 8) * a.scale_stride) + 2 * (rs[j] & 0xFF);
+  for (int j = 0; j < 3; ++j) soff[j] = (uint32_t)((rs[j] >> 8) * a.scale_stride) + 2 * (rs[j] & 0xFF);
 
   // All of this wave's loads of tile t into raw slot t % 2.  Rows past the
   // item's last token fetch that token's row (finite data, masked later).
   auto issue = [&](int t) {
     const int tok0 = item.tok_begin + t * kXTile;
     const int lim = tok_last - tok0;
-    const uint32_t m0c = lds_u32(&sh.raw[t & 1][0]) + 1024 * kXFp4PerWave * wave;
-    const uint32_t m0s = lds_u32(&sh.raw[t & 1][kXFp4Bytes]) + 256 * kXScalePerWave * wave;
+    const uint32_t m0c = lds_u32(&sh.raw[t & 1][0]) + 1024 * j0;
+    const uint32_t m0s = lds_u32(&sh.raw[t & 1][kXFp4Bytes]) + 256 * s0;
     if constexpr (!PAGED) {
       const uint8_t* cbase = uniform_ptr(a.kv + (seq_base + tok0) * kXRow - 3072);
       const uint8_t* sbase = uniform_ptr(a.kv_mx_scales + (seq_base + tok0) * a.scale_stride);
-      uint32_t off[kXFp4PerWave], so[kXScalePerWave];
+      uint32_t off[5], so[3];
       if (lim >= kXTile - 1) {  // a whole tile
 #pragma unroll
-        for (int j = 0; j < kXFp4PerWave; ++j) off[j] = coff[j];
+        for (int j = 0; j < 5; ++j) off[j] = coff[j];
 #pragma unroll
-        for (int j = 0; j < kXScalePerWave; ++j) so[j] = soff[j];
+        for (int j = 0; j < 3; ++j) so[j] = soff[j];
       } else {
 #pragma unroll
-        for (int j = 0; j < kXFp4PerWave; ++j)
+        for (int j = 0; j < 5; ++j)
           off[j] = min((int)(rc[j] >> 8), lim) * kXRow + 16 * (rc[j] & 0xFF) + 3072 - 1024 * (j & 3);
 #pragma unroll
-        for (int j = 0; j < kXScalePerWave; ++j)
+        for (int j = 0; j < 3; ++j)
           so[j] = (uint32_t)(min((int)(rs[j] >> 8), lim) * a.scale_stride) + 2 * (rs[j] & 0xFF);
       }
       dma_group<4>(cbase, off, m0c);
-      dma_group<4>(cbase, off + 4, m0c + 4096);
-      dma_group<1>(cbase, off + 8, m0c + 8192);
-#pragma unroll
-      for (int j = 0; j < kXScalePerWave; ++j) dma_u16(sbase, so[j], m0s + 256 * j);
+      if (lowq) dma_group<1>(cbase, off + 4, m0c + 4096);
+      dma_u16(sbase, so[0], m0s);
+      dma_u16(sbase, so[1], m0s + 256);
+      if (!lowq) dma_u16(sbase, so[2], m0s + 512);
     } else {
-      const uint8_t* src[kXFp4PerWave];
+      const uint8_t* src[5];
 #pragma unroll
-      for (int j = 0; j < kXFp4PerWave; ++j) {
+      for (int j = 0; j < 5; ++j) {
         const int r = min((int)(rc[j] >> 8), lim);
         src[j] = a.kv + row_of(tok0 + r) * kXRow + 16 * (rc[j] & 0xFF) - 1024 * (j & 3);
       }
       dma_group<4>(src, m0c);
-      dma_group<4>(src + 4, m0c + 4096);
-      dma_one(src[8], m0c + 8192);  // load 8: no instruction offset
+      if (lowq) dma_one(src[4], m0c + 4096);  // no instruction offset
+      const uint8_t* ssrc[3];
 #pragma unroll
-      for (int j = 0; j < kXScalePerWave; ++j) {
+      for (int j = 0; j < 3; ++j) {
         const int r = min((int)(rs[j] >> 8), lim);
-        dma_u16(a.kv_mx_scales + row_of(tok0 + r) * a.scale_stride + 2 * (rs[j] & 0xFF), m0s + 256 * j);
+        ssrc[j] = a.kv_mx_scales + row_of(tok0 + r) * a.scale_stride + 2 * (rs[j] & 0xFF);
       }
+      dma_u16(ssrc[0], m0s);
+      dma_u16(ssrc[1], m0s + 256);
+      if (!lowq) dma_u16(ssrc[2], m0s + 512);
     }
   };
 
@@ -353,26 +362,26 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_mxfp4(Stage1Args
     }
   }
 
-  f32x4 o[8];  // O^T[dim 128w + 16v + 4g + i][head r16]
+  f32x4 o[4];  // O^T[dim 64w + 16v + 4g + i][head r16]
 #pragma unroll
-  for (int v = 0; v < 8; ++v) o[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int v = 0; v < 4; ++v) o[v] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_ref = kNegInf;
   float l_part = 0.f;
 
-  // Reads of this lane.  Scores: rows 32w + 16s + r16 of the raw tile.  V^T:
-  // tr8 read q (0..3) gives tokens tb(q) + (0..7), tb = 16g + 8q (q < 2) or
+  // Reads of this lane.  Scores: row 16w + r16 of the raw tile.  V^T: tr8
+  // read q (0..3) gives tokens tb(q) + (0..7), tb = 16g + 8q (q < 2) or
   // 64 + 16g + 8(q - 2), from rows tb(q) + (r16 >> 1), columns
-  // 128w + 16v + 8(r16 & 1).  Conversion: the half wave h = 2w + lane / 32
-  // takes token block cv_tb = h & 3 and the column blocks of parity
-  // cv_odd = h >> 2; the lane, token row 32 cv_tb + (lane & 31).
+  // 64w + 16v + 8(r16 & 1).  Conversion: the half wave h = 2w + lane / 32
+  // takes token block h & 3 and column blocks 4k + (h >> 2), k = 0..3; the
+  // lane, token row 32(h & 3) + (lane & 31).
   const int hw_id = 2 * wave + (lane >> 5);
   const int cv_tb = hw_id & 3;
-  const int cv_odd = hw_id >> 2;
+  const int cv_q = hw_id >> 2;
   const int cv_row = 32 * cv_tb + (lane & 31);
   int voff[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    voff[q] = ((q < 2 ? 16 * g + 8 * q : 64 + 16 * g + 8 * (q - 2)) + (r16 >> 1)) * kXVRow + 128 * wave +
+    voff[q] = ((q < 2 ? 16 * g + 8 * q : 64 + 16 * g + 8 * (q - 2)) + (r16 >> 1)) * kXVRow + 64 * wave +
               8 * (r16 & 1);
   uint8_t* const p_hi = &sh.p[0][r16][0];
   uint8_t* const p_lo = &sh.p[1][r16][0];
@@ -387,13 +396,10 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_mxfp4(Stage1Args
     const uint8_t* raw = &sh.raw[t & 1][0];
     const uint8_t* sdw = raw + kXFp4Bytes;  // scale pair (row, p) at dword 9 row + p
 
-    // ---- scores of tokens 32w + 16s + (0..15), s = 0, 1 ----
-    f32x4 sacc[2][2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      sacc[s][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-      sacc[s][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int row = 32 * wave + 16 * s + r16;
+    // ---- scores of tokens 16w + (0..15) ----
+    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    {
+      const int row = 16 * wave + r16;
       const uint8_t* rp = raw + row * kXRow;
       const uint8_t* sp = sdw + 4 * kXScalePairs * row;
 #pragma unroll
@@ -402,8 +408,8 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_mxfp4(Stage1Args
         const uint32_t sa = sp[4 * (blk >> 1) + (blk & 1)];
         const u32x4 w = *reinterpret_cast<const u32x4*>(rp + 64 * K + 16 * g);
         const fp8x32 ka = fp8x32{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
-        sacc[s][0] = mfma_fp4_fp8(ka, qh[K], sacc[s][0], sa);
-        sacc[s][1] = mfma_fp4_fp8(ka, ql[K], sacc[s][1], sa);
+        sacc[0] = mfma_fp4_fp8(ka, qh[K], sacc[0], sa);
+        sacc[1] = mfma_fp4_fp8(ka, ql[K], sacc[1], sa);
       }
       u32x4 w = {0u, 0u, 0u, 0u};
       uint32_t sa = 127;
@@ -412,65 +418,60 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_mxfp4(Stage1Args
         sa = sp[4 * 8 + g];
       }
       const fp8x32 ka = fp8x32{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
-      sacc[s][0] = mfma_fp4_fp8(ka, rh, sacc[s][0], sa);
-      sacc[s][1] = mfma_fp4_fp8(ka, rl, sacc[s][1], sa);
+      sacc[0] = mfma_fp4_fp8(ka, rh, sacc[0], sa);
+      sacc[1] = mfma_fp4_fp8(ka, rl, sacc[1], sa);
     }
 
-    // ---- softmax: x[s][i] is token 32w + 16s + 4g + i of head r16 ----
-    float x[2][4];
+    // ---- softmax: x[i] is token 16w + 4g + i of head r16 ----
+    float x[4];
     float tmax = kNegInf;
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[s][i] = (sacc[s][0][i] + sacc[s][1][i]) * xscale;
-        if (tok0 + 32 * wave + 16 * s + 4 * g + i > tok_last) x[s][i] = kNegInf;
-        tmax = fmaxf(tmax, x[s][i]);
-      }
+    for (int i = 0; i < 4; ++i) {
+      x[i] = (sacc[0][i] + sacc[1][i]) * xscale;
+      if (tok0 + 16 * wave + 4 * g + i > tok_last) x[i] = kNegInf;
+      tmax = fmaxf(tmax, x[i]);
+    }
     tmax = xor_max_groups(tmax);
     if (g == 0) sh.red_m[r16][wave] = tmax;
-    float p[2][4];
-    uint32_t ph[2], pl[2];
+    float p[4];
+    uint32_t ph, pl;
     {
       const float mr = (m_ref == kNegInf) ? 0.0f : m_ref;
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) p[s][i] = __builtin_amdgcn_exp2f(x[s][i] - mr);
-        split_fp8x4(p[s][0], p[s][1], p[s][2], p[s][3], ph[s], pl[s]);
-        *reinterpret_cast<uint32_t*>(p_hi + 32 * wave + 16 * s + 4 * g) = ph[s];
-        *reinterpret_cast<uint32_t*>(p_lo + 32 * wave + 16 * s + 4 * g) = pl[s];
-      }
+      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - mr);
+      split_fp8x4(p[0], p[1], p[2], p[3], ph, pl);
+      *reinterpret_cast<uint32_t*>(p_hi + 16 * wave + 4 * g) = ph;
+      *reinterpret_cast<uint32_t*>(p_lo + 16 * wave + 4 * g) = pl;
     }
 
     // ---- V of this tile to e4m3, per block of 32 tokens x 32 columns ----
-    // This lane converts token row cv_row, column blocks 2k + cv_odd
-    // (k = 0..7): all reads first, then the block maxima (two per
-    // reduction), the conversions and the writes.
+    // This lane converts token row cv_row, column blocks 4k + cv_q: all reads
+    // first, then the block maxima (two per reduction), the conversions and
+    // the writes.
     {
-      uint32_t e[8];
-      u32x4 w[8];
-      const uint8_t* rsrc = raw + cv_row * kXRow + 16 * cv_odd;
-      const uint8_t* ssrc = sdw + 4 * kXScalePairs * cv_row + cv_odd;
+      uint32_t e[4];
+      u32x4 w[4];
+      const uint8_t* rsrc = raw + cv_row * kXRow + 16 * cv_q;
+      const uint8_t* ssrc = sdw + 4 * kXScalePairs * cv_row + 4 * (cv_q >> 1) + (cv_q & 1);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        e[k] = ssrc[4 * k];
-        w[k] = *reinterpret_cast<const u32x4*>(rsrc + 32 * k);
+      for (int k = 0; k < 4; ++k) {
+        e[k] = ssrc[8 * k];
+        w[k] = *reinterpret_cast<const u32x4*>(rsrc + 64 * k);
       }
-      uint32_t c[8];
+      uint32_t c[4];
 #pragma unroll
-      for (int k = 0; k < 8; k += 2) {
+      for (int k = 0; k < 4; k += 2) {
         const uint32_t m = half_wave_max2(e[k] | (e[k + 1] << 16));
         c[k] = m & 0xFFFF;
         c[k + 1] = m >> 16;
       }
       if ((lane & 31) == 0) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) sh.ctab[cv_tb][2 * k + cv_odd] = (uint8_t)c[k];
+        for (int k = 0; k < 4; ++k) sh.ctab[cv_tb][4 * k + cv_q] = (uint8_t)c[k];
       }
-      uint8_t* vdst = &sh.v[cv_row * kXVRow + 32 * cv_odd];
+      uint8_t* vdst = &sh.v[cv_row * kXVRow + 32 * cv_q];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
+      for (int k = 0; k < 4; ++k) {
         const int j = max((int)e[k] - (int)c[k], -126);  // <= 0
         uint32_t e8[8];  // 32 e4m3 codes, columns 32cb + 4i .. +3 in word i
         if (__ballot(j < -5) == 0) {  // the whole wave by table
@@ -484,48 +485,47 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_mxfp4(Stage1Args
 #pragma unroll
           for (int i = 0; i < 4; ++i) fp4x8_to_fp8(w[k][i], scale, e8[2 * i], e8[2 * i + 1]);
         }
-        *reinterpret_cast<u32x4*>(vdst + 64 * k) = u32x4{e8[0], e8[1], e8[2], e8[3]};
-        *reinterpret_cast<u32x4*>(vdst + 64 * k + 16) = u32x4{e8[4], e8[5], e8[6], e8[7]};
+        *reinterpret_cast<u32x4*>(vdst + 128 * k) = u32x4{e8[0], e8[1], e8[2], e8[3]};
+        *reinterpret_cast<u32x4*>(vdst + 128 * k + 16) = u32x4{e8[4], e8[5], e8[6], e8[7]};
       }
     }
     lds_barrier();  // P^T, maxima, the V tile and its block maxima; raw slot t % 2 is free
     if (t + 2 < ntiles) issue(t + 2);
 
-    const f32x4 maxima = *reinterpret_cast<const f32x4*>(&sh.red_m[r16][0]);
+    const f32x4 mx0 = *reinterpret_cast<const f32x4*>(&sh.red_m[r16][0]);
+    const f32x4 mx1 = *reinterpret_cast<const f32x4*>(&sh.red_m[r16][4]);
     fp8x32 bh = join16(*reinterpret_cast<const u32x4*>(p_hi + 16 * g),
                        *reinterpret_cast<const u32x4*>(p_hi + 64 + 16 * g));
     fp8x32 bl = join16(*reinterpret_cast<const u32x4*>(p_lo + 16 * g),
                        *reinterpret_cast<const u32x4*>(p_lo + 64 + 16 * g));
-    const uint32_t csa = *reinterpret_cast<const uint32_t*>(&sh.ctab[g][4 * wave]);
-    const float tile_max = fmaxf(fmaxf(maxima[0], maxima[1]), fmaxf(maxima[2], maxima[3]));
+    // block exponents of V for column blocks 2w, 2w + 1 in bytes 0, 1
+    const uint32_t csa = *reinterpret_cast<const uint32_t*>(&sh.ctab[g][4 * (wave >> 1)]) >> (16 * (wave & 1));
+    const float tile_max = fmaxf(fmaxf(fmaxf(mx0[0], mx0[1]), fmaxf(mx0[2], mx0[3])),
+                                 fmaxf(fmaxf(mx1[0], mx1[1]), fmaxf(mx1[2], mx1[3])));
     if (__ballot(tile_max > m_ref + kLazyRescale) != 0) {
       const float m_new = fmaxf(m_ref, tile_max);
       const float alpha = (m_ref == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
 #pragma unroll
-      for (int v = 0; v < 8; ++v) o[v] *= alpha;
+      for (int v = 0; v < 4; ++v) o[v] *= alpha;
       l_part *= alpha;
       m_ref = m_new;
       lds_barrier();  // everyone has read the old P^T
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) p[s][i] = __builtin_amdgcn_exp2f(x[s][i] - m_ref);
-        split_fp8x4(p[s][0], p[s][1], p[s][2], p[s][3], ph[s], pl[s]);
-        *reinterpret_cast<uint32_t*>(p_hi + 32 * wave + 16 * s + 4 * g) = ph[s];
-        *reinterpret_cast<uint32_t*>(p_lo + 32 * wave + 16 * s + 4 * g) = pl[s];
-      }
+      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - m_ref);
+      split_fp8x4(p[0], p[1], p[2], p[3], ph, pl);
+      *reinterpret_cast<uint32_t*>(p_hi + 16 * wave + 4 * g) = ph;
+      *reinterpret_cast<uint32_t*>(p_lo + 16 * wave + 4 * g) = pl;
       lds_barrier();
       bh = join16(*reinterpret_cast<const u32x4*>(p_hi + 16 * g),
                   *reinterpret_cast<const u32x4*>(p_hi + 64 + 16 * g));
       bl = join16(*reinterpret_cast<const u32x4*>(p_lo + 16 * g),
                   *reinterpret_cast<const u32x4*>(p_lo + 64 + 16 * g));
     }
-#pragma unroll
-    for (int s = 0; s < 2; ++s) l_part += (p[s][0] + p[s][1]) + (p[s][2] + p[s][3]);
+    l_part += (p[0] + p[1]) + (p[2] + p[3]);
 
-    // ---- O^T += V^T P^T, columns 128w + 16v, block scale 2^(c - 127) ----
+    // ---- O^T += V^T P^T, columns 64w + 16v, block scale 2^(c - 127) ----
 #pragma unroll
-    for (int v = 0; v < 8; v += 2) {
+    for (int v = 0; v < 4; v += 2) {
       fp8x32 va[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u)
@@ -545,9 +545,10 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_mxfp4(Stage1Args
   const float l_w = xor_sum_groups(l_part);
   if (g == 0) sh.red_l[r16][wave] = l_w;
   lds_barrier();
-  const f32x4 ls = *reinterpret_cast<const f32x4*>(&sh.red_l[r16][0]);
-  const float L = (ls[0] + ls[1]) + (ls[2] + ls[3]);
-  finish_item(a, item, tid, wave, lane, o, 1.0f / L, m_ref + __log2f(L));
+  const f32x4 ls0 = *reinterpret_cast<const f32x4*>(&sh.red_l[r16][0]);
+  const f32x4 ls1 = *reinterpret_cast<const f32x4*>(&sh.red_l[r16][4]);
+  const float L = ((ls0[0] + ls0[1]) + (ls0[2] + ls0[3])) + ((ls1[0] + ls1[1]) + (ls1[2] + ls1[3]));
+  finish_item<4>(a, item, tid, wave >> 1, 4 * (wave & 1), lane, o, 1.0f / L, m_ref + __log2f(L));
 }
 
 }  // namespace
