@@ -35,20 +35,25 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 DEFAULT_WORKLOAD = "bs64_kv1024_fp8"
 ROTATION_BYTES = 1 << 30  # inputs cycled per timed pass: 4x the 256 MB MALL
 METRIC = "µs/call and effective KV HBM GB/s (% of peak), MLA decode bs×kv_len"
-# Sources of the fp8 split kernel: a traffic record holds for them as hashed.
-KERNEL_SRCS = [os.path.join(ROOT, "latent_attention_decode_amd", "csrc", f)
-               for f in ("mla_stage1_fp8.hip", "mla_device.h", "mla_internal.h")]
+# Sources of each cache format's split kernel: a traffic record holds for
+# them as hashed.
+CSRC = os.path.join(ROOT, "latent_attention_decode_amd", "csrc")
+KERNEL_SRCS = {
+    "fp8": ("mla_stage1_fp8.hip", "mla_device.h", "mla_internal.h"),
+    "mxfp4": ("mla_stage1_mxfp4.hip", "mla_device.h", "mla_internal.h"),
+    "bf16": ("mla_kernels.hip", "mla_device.h", "mla_internal.h"),
+}
 
 
-def kernel_hash() -> str:
+def kernel_hash(kv_dtype: str = "fp8") -> str:
     h = hashlib.sha256()
-    for path in KERNEL_SRCS:
-        with open(path, "rb") as f:
+    for name in KERNEL_SRCS[kv_dtype]:
+        with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def traffic_record(workload: str):
+def traffic_record(workload: str, kv_dtype: str):
     """HBM bytes per stage-1 launch from a committed rocprofv3 --pmc summary,
     if it was taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", f"stage1_{workload}_traffic.json")
@@ -56,7 +61,7 @@ def traffic_record(workload: str):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_sha256_16") != kernel_hash():
+    if rec.get("kernel_sha256_16") != kernel_hash(kv_dtype):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -204,7 +209,7 @@ def main():
     value = alg_bytes / (mean_ms * 1e-3) / 1e9
     s1_mean = float(s1.mean())
     achieved = alg_bytes / (s1_mean * 1e-3) / 1e9
-    traffic = traffic_record(name)
+    traffic = traffic_record(name, kv_dtype)
 
     line = {
         "metric": METRIC,
@@ -221,8 +226,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"bf16": "bf16", "fp8": "fp8-e4m3 (bf16 MFMA, fp32 acc)",
-                  "mxfp4": "mxfp4 (bf16 MFMA, fp32 acc)"}[kv_dtype],
+        "dtype": {"bf16": "bf16 (bf16 MFMA, fp32 acc)",
+                  "fp8": "fp8-e4m3 (fp8 / MX MFMA on the codes, fp32 acc)",
+                  "mxfp4": "mxfp4 (MX MFMA: e2m1 scores, e4m3 values, fp32 acc)"}[kv_dtype],
         "data": "synthetic",
         "config": {"workload": name, "kv_dtype": kv_dtype, "batch": int(case.batch),
                    "kv_len": kv_len if isinstance(kv_len, int) else list(kv_len),

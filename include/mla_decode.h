@@ -40,7 +40,7 @@
  * log-sum-exp; the partials of every split sequence are merged by their
  * log-sum-exp weights (727205 `mla_rd`, 700955 `reduce_lse_v71`, 599694
  * `_flash_fp8_split_s2`).  The merge is a second kernel launch, except for an
- * fp8 cache with a plan whose items differ in length (at most 12 per
+ * fp8 or MXFP4 cache with a plan whose items differ in length (at most 12 per
  * sequence): there the item of a sequence that finishes last merges its
  * partials, so each call is one launch.  No merge runs when no sequence is
  * split.  The completion counters of that merge belong to the plan: runs of

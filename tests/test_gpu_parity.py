@@ -175,18 +175,20 @@ def test_split_count_changes_only_rounding(B, oracle_mod):
         assert np.abs(o - outs[0]).max() < 2e-2
 
 
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
 @pytest.mark.parametrize("split", [2, 5, 12, 13])
-def test_merge_repeated_calls(B, oracle_mod, split):
-    """With an fp8 cache and at most 12 splits per sequence the split kernel
-    merges the partials itself: per-sequence completion counters, reset by the
-    item that finishes last, pick the merging item; with 13 the merge kernel
-    runs.  Calls on one plan with new data each time must each match the
-    oracle (a partial left from the call before would not), and a repeat of
-    the first must agree with it bit for bit (the merge order does not depend
-    on which item finished last)."""
+def test_merge_repeated_calls(B, oracle_mod, fmt, split):
+    """With an fp8 or MXFP4 cache, a plan whose items differ in length and at
+    most 12 splits per sequence, the split kernel merges the partials itself:
+    per-sequence completion counters, reset by the item that finishes last,
+    pick the merging item; with 13 the merge kernel runs.  Calls on one plan
+    with new data each time must each match the oracle (a partial left from
+    the call before would not), and a repeat of the first must agree with it
+    bit for bit (the merge order does not depend on which item finished
+    last)."""
     lens = [3000, 1700, 129, 2500, 1]
-    cases = [synth.make_case("fp8", lens, seed=31 + r) for r in range(3)]
-    dec = B.MlaDecode("fp8", 1)
+    cases = [synth.make_case(fmt, lens, seed=31 + r) for r in range(3)]
+    dec = B.MlaDecode(fmt, 1)
     try:
         dec.plan(cases[0].kv_indptr, None, split)
         outs = []
@@ -199,7 +201,7 @@ def test_merge_repeated_calls(B, oracle_mod, split):
     finally:
         dec.close()
     for r, case in enumerate(cases):
-        check_close(outs[r], oracle_out(oracle_mod, case), "fp8", f"split {split} call {r}")
+        check_close(outs[r], oracle_out(oracle_mod, case), fmt, f"{fmt} split {split} call {r}")
     assert np.array_equal(outs[0], outs[3])
 
 
