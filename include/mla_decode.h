@@ -124,8 +124,10 @@ mla_status mla_decode_plan(mla_decode_t h, int batch, const int32_t* kv_indptr_h
 
 /*
  * The planner alone, on the host, for inspection and testing (no handle, no
- * GPU).  Same inputs as mla_decode_plan plus the device figures it would read
- * (compute units, resident stage-1 workgroups per unit).  Writes up to
+ * GPU).  Same inputs as mla_decode_plan plus the cache format (items are
+ * whole tiles of its split kernel: 64 tokens for bf16, 128 otherwise) and
+ * the device figures it would read (compute units, resident stage-1
+ * workgroups per unit).  Writes up to
  * max_items work items as int32 quadruples (sequence, first token, end token,
  * partial slot, or -1 when the item is the whole sequence, or -2 for the item
  * that writes an empty sequence's zero output) in launch order,
@@ -134,9 +136,9 @@ mla_status mla_decode_plan(mla_decode_t h, int batch, const int32_t* kv_indptr_h
  */
 mla_status mla_decode_plan_preview(int batch, const int32_t* kv_indptr_host,
                                    const int32_t* kv_last_page_len_host, int page_size,
-                                   int split_override, int num_cus, int blocks_per_cu,
-                                   int32_t* items_out, int max_items, int* num_items,
-                                   int* num_slots, size_t* workspace_bytes);
+                                   mla_kv_dtype kv_dtype, int split_override, int num_cus,
+                                   int blocks_per_cu, int32_t* items_out, int max_items,
+                                   int* num_items, int* num_slots, size_t* workspace_bytes);
 
 /*
  * Describe the current plan: number of work items (workgroups launched), the

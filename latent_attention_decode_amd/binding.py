@@ -40,7 +40,7 @@ _lib.mla_decode_create.argtypes = [ctypes.POINTER(_H), ctypes.c_int, ctypes.c_in
                                    ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_int]
 _lib.mla_decode_plan.argtypes = [_H, ctypes.c_int, _P, _P, ctypes.c_int,
                                  ctypes.POINTER(ctypes.c_size_t)]
-_lib.mla_decode_plan_preview.argtypes = [ctypes.c_int, _P, _P, ctypes.c_int, ctypes.c_int,
+_lib.mla_decode_plan_preview.argtypes = [ctypes.c_int, _P, _P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                          ctypes.c_int, ctypes.c_int, _P, ctypes.c_int,
                                          ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
                                          ctypes.POINTER(ctypes.c_size_t)]
@@ -127,7 +127,8 @@ def mla_decode_plan(h, kv_indptr_host, kv_last_page_len_host=None, split_overrid
 
 
 def mla_decode_plan_preview(kv_indptr_host, kv_last_page_len_host=None, page_size: int = 1,
-                            split_override: int = 0, num_cus: int = 256, blocks_per_cu: int = 2):
+                            split_override: int = 0, num_cus: int = 256, blocks_per_cu: int = 2,
+                            kv_dtype: str = "fp8"):
     """Host-only planner.  Returns (items int32 [n, 4], num_slots, workspace_bytes)."""
     ip = _host_i32(kv_indptr_host)
     lp = None if kv_last_page_len_host is None else _host_i32(kv_last_page_len_host)
@@ -135,7 +136,7 @@ def mla_decode_plan_preview(kv_indptr_host, kv_last_page_len_host=None, page_siz
     slots = ctypes.c_int()
     ws = ctypes.c_size_t()
     args = (ip.size - 1, ip.ctypes.data, None if lp is None else lp.ctypes.data, int(page_size),
-            int(split_override), int(num_cus), int(blocks_per_cu))
+            KV_DTYPES[kv_dtype], int(split_override), int(num_cus), int(blocks_per_cu))
     st = _lib.mla_decode_plan_preview(*args, None, 0, ctypes.byref(n), ctypes.byref(slots),
                                       ctypes.byref(ws))
     if st != 0 and n.value == 0:

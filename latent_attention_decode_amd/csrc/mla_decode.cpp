@@ -51,7 +51,7 @@ struct mla_decode_s {
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 1 * 100 + 0;
 
 mla_status fail(mla_decode_t h, mla_status st, const char* fmt, ...) {
   if (h) {
@@ -141,17 +141,17 @@ struct PlanOut {
 
 static int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
-// An item of fewer than two tiles has no load/compute overlap; each (sequence,
-// head) is merged by one workgroup, so the number of partials stays small.
-constexpr int64_t kMinItemTokens = 2 * kPlanTile;
+// Items are whole tiles of the format's split kernel: 128 tokens (fp8 and
+// MXFP4 kernels) or 64 (bf16 kernel).  A small batch is cut down to one tile
+// per item, so that it reaches more compute units; at most kMaxAutoSplits
+// items per sequence keep the merge short.
 constexpr int64_t kMaxAutoSplits = 32;
+static int64_t plan_tile(int kv_dtype) { return kv_dtype == MLA_KV_BF16 ? kPlanTile / 2 : kPlanTile; }
 constexpr int64_t kMaxItemPages = 512;  // LDS staging of one item's page ids (mla_kernels.hip)
 
 static void plan_items(const std::vector<int64_t>& lens, const int32_t* indptr, int split_override,
-                       int num_cus,
-                       int blocks_per_cu, int page_size, PlanOut* out) {
+                       int num_cus, int blocks_per_cu, int page_size, int64_t tile, PlanOut* out) {
   const int batch = static_cast<int>(lens.size());
-  const int64_t tile = kPlanTile;
   int64_t total = 0, max_len = 0, nonempty = 0;
   for (int64_t n : lens) {
     total += n;
@@ -173,7 +173,7 @@ static void plan_items(const std::vector<int64_t>& lens, const int32_t* indptr, 
     const bool ragged = static_cast<double>(max_len) > 1.25 * mean;
     const int64_t slots = static_cast<int64_t>(num_cus) * std::max(blocks_per_cu, 1);
     const int64_t target = slots * (ragged ? 4 : 1);
-    const int64_t c = std::max<int64_t>(kMinItemTokens,
+    const int64_t c = std::max<int64_t>(tile,
                                         round_up((total + target - 1) / target, tile));
     for (int b = 0; b < batch; ++b) {
       if (!lens[b]) continue;
@@ -318,7 +318,7 @@ mla_status mla_decode_plan(mla_decode_t h, int batch, const int32_t* kv_indptr_h
 
   mla::PlanOut plan;
   mla::plan_items(lens, kv_indptr_host, split_override, h->num_cus, h->blocks_per_cu, h->page_size,
-                  &plan);
+                  mla::plan_tile(h->kv_dtype), &plan);
 
   const size_t items_bytes = plan.items.size() * sizeof(mla::WorkItem);
   const size_t merge_bytes = plan.merge.size() * sizeof(mla::MergeSeq);
@@ -364,11 +364,12 @@ mla_status mla_decode_plan(mla_decode_t h, int batch, const int32_t* kv_indptr_h
 
 mla_status mla_decode_plan_preview(int batch, const int32_t* kv_indptr_host,
                                    const int32_t* kv_last_page_len_host, int page_size,
-                                   int split_override, int num_cus, int blocks_per_cu,
-                                   int32_t* items_out, int max_items, int* num_items,
-                                   int* num_slots, size_t* workspace_bytes) {
+                                   mla_kv_dtype kv_dtype, int split_override, int num_cus,
+                                   int blocks_per_cu, int32_t* items_out, int max_items,
+                                   int* num_items, int* num_slots, size_t* workspace_bytes) {
   if (batch < 1 || !kv_indptr_host || page_size < 1 || !is_pow2(page_size) || split_override < 0 ||
-      num_cus < 1 || blocks_per_cu < 1 || max_items < 0 || (max_items > 0 && !items_out))
+      num_cus < 1 || blocks_per_cu < 1 || max_items < 0 || (max_items > 0 && !items_out) ||
+      (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3 && kv_dtype != MLA_KV_MXFP4))
     return MLA_ERR_INVALID_ARG;
   if (page_size > 1 && !kv_last_page_len_host) return MLA_ERR_INVALID_ARG;
   std::vector<int64_t> lens;
@@ -376,7 +377,8 @@ mla_status mla_decode_plan_preview(int batch, const int32_t* kv_indptr_host,
   if (!mla::seq_lengths(kv_indptr_host, kv_last_page_len_host, batch, page_size, &lens, &err))
     return MLA_ERR_INVALID_ARG;
   mla::PlanOut plan;
-  mla::plan_items(lens, kv_indptr_host, split_override, num_cus, blocks_per_cu, page_size, &plan);
+  mla::plan_items(lens, kv_indptr_host, split_override, num_cus, blocks_per_cu, page_size,
+                  mla::plan_tile(kv_dtype), &plan);
   const int n = static_cast<int>(plan.items.size());
   if (num_items) *num_items = n;
   if (num_slots) *num_slots = plan.num_slots;

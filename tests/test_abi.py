@@ -143,6 +143,22 @@ def test_planner_fills_the_gpu_for_uniform_batches(B):
         assert np.bincount(items[:, 0]).max() <= 32
 
 
+def test_planner_tiles_follow_the_format(B):
+    """Items are whole tiles of the format's split kernel (64 tokens for bf16,
+    128 for fp8 / MXFP4); a small batch goes down to one tile per item, while
+    large uniform batches keep one wave of longer items."""
+    indptr = np.arange(5, dtype=np.int32) * 1024  # 4 x 1024
+    items, _, _ = B.mla_decode_plan_preview(indptr, num_cus=256, blocks_per_cu=2, kv_dtype="bf16")
+    assert np.all(items[:, 2] - items[:, 1] == 64) and len(items) == 64
+    items, _, _ = B.mla_decode_plan_preview(indptr, num_cus=256, blocks_per_cu=1, kv_dtype="fp8")
+    assert np.all(items[:, 2] - items[:, 1] == 128) and len(items) == 32
+    for bs, n, per_item in [(64, 1024, 256), (64, 8192, 2048), (32, 8192, 1024)]:
+        indptr = np.arange(bs + 1, dtype=np.int32) * n
+        for fmt in ("fp8", "mxfp4"):
+            items, _, _ = B.mla_decode_plan_preview(indptr, num_cus=256, blocks_per_cu=1, kv_dtype=fmt)
+            assert len(items) == 256 and np.all(items[:, 2] - items[:, 1] == per_item), (bs, n, fmt)
+
+
 def test_planner_split_override(B):
     indptr = np.array([0, 1000, 1033, 1034], dtype=np.int32)
     items, slots, _ = B.mla_decode_plan_preview(indptr, split_override=4)
