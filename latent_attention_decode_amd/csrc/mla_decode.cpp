@@ -147,10 +147,15 @@ static int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 // items per sequence keep the merge short.
 constexpr int64_t kMaxAutoSplits = 32;
 static int64_t plan_tile(int kv_dtype) { return kv_dtype == MLA_KV_BF16 ? kPlanTile / 2 : kPlanTile; }
-constexpr int64_t kMaxItemPages = 512;  // LDS staging of one item's page ids (mla_kernels.hip)
+// Page ids of one item that the format's split kernel stages (the bf16
+// kernel reads them per row and has no limit).
+static int64_t item_pages(int kv_dtype) {
+  return kv_dtype == MLA_KV_FP8_E4M3 ? kItemPagesFp8 : kv_dtype == MLA_KV_MXFP4 ? kItemPagesMxfp4 : INT64_MAX;
+}
 
 static void plan_items(const std::vector<int64_t>& lens, const int32_t* indptr, int split_override,
-                       int num_cus, int blocks_per_cu, int page_size, int64_t tile, PlanOut* out) {
+                       int num_cus, int blocks_per_cu, int page_size, int64_t tile, int64_t max_pages,
+                       PlanOut* out) {
   const int batch = static_cast<int>(lens.size());
   int64_t total = 0, max_len = 0, nonempty = 0;
   for (int64_t n : lens) {
@@ -158,9 +163,11 @@ static void plan_items(const std::vector<int64_t>& lens, const int32_t* indptr, 
     max_len = std::max(max_len, n);
     nonempty += n > 0;
   }
-  // A paged item's page ids are staged in LDS: at most kMaxItemPages of them.
-  const int64_t max_item =
-      page_size > 1 ? (kMaxItemPages - 2) * static_cast<int64_t>(page_size) / tile * tile : INT64_MAX;
+  // A paged item's page ids are staged in LDS: at most max_pages of them
+  // (an item's first and last page may be partial).
+  const int64_t max_item = page_size > 1 && max_pages < INT64_MAX / 2
+                               ? (max_pages - 2) * static_cast<int64_t>(page_size) / tile * tile
+                               : INT64_MAX;
   std::vector<int64_t> chunk(batch, 0);
   if (split_override > 0) {
     for (int b = 0; b < batch; ++b) {
@@ -318,7 +325,7 @@ mla_status mla_decode_plan(mla_decode_t h, int batch, const int32_t* kv_indptr_h
 
   mla::PlanOut plan;
   mla::plan_items(lens, kv_indptr_host, split_override, h->num_cus, h->blocks_per_cu, h->page_size,
-                  mla::plan_tile(h->kv_dtype), &plan);
+                  mla::plan_tile(h->kv_dtype), mla::item_pages(h->kv_dtype), &plan);
 
   const size_t items_bytes = plan.items.size() * sizeof(mla::WorkItem);
   const size_t merge_bytes = plan.merge.size() * sizeof(mla::MergeSeq);
@@ -378,7 +385,7 @@ mla_status mla_decode_plan_preview(int batch, const int32_t* kv_indptr_host,
     return MLA_ERR_INVALID_ARG;
   mla::PlanOut plan;
   mla::plan_items(lens, kv_indptr_host, split_override, num_cus, blocks_per_cu, page_size,
-                  mla::plan_tile(kv_dtype), &plan);
+                  mla::plan_tile(kv_dtype), mla::item_pages(kv_dtype), &plan);
   const int n = static_cast<int>(plan.items.size());
   if (num_items) *num_items = n;
   if (num_slots) *num_slots = plan.num_slots;

@@ -148,6 +148,13 @@ __device__ __forceinline__ void dma_group(const uint8_t* const* src, uint32_t m0
   else
     static_assert(N == 4 || N == 2, "group size");
 }
+// One four-byte load, lane l's dword at src to LDS m0 + 4 l.
+__device__ __forceinline__ void dma_u32(const void* src, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(src), "s"(m0)
+               : "memory", "m0");
+}
 // One load, lane l's 16 bytes at src to LDS m0 + 16 l.
 __device__ __forceinline__ void dma_one(const void* src, uint32_t m0) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"

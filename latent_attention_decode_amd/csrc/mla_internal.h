@@ -17,6 +17,10 @@ constexpr int kPlanTile = 128;   // tokens per stage-1 tile (fp8); items are who
 constexpr int kWaves = 4;        // waves per stage-1 workgroup
 constexpr int kStage1Threads = 64 * kWaves;
 constexpr int kStage1ThreadsMxfp4 = 512;  // the MXFP4 split kernel runs eight waves
+// Page ids of one item that the fp8 / MXFP4 split kernels stage in LDS (what
+// the rest of their LDS leaves); the planner keeps paged items within them.
+constexpr int kItemPagesFp8 = 2560;
+constexpr int kItemPagesMxfp4 = 1536;
 constexpr int kMergeThreads = 256;  // two float4 of one head per thread
 
 enum KvFormat : int { kBf16 = 0, kFp8 = 1, kMxfp4 = 2 };

@@ -64,7 +64,7 @@ constexpr int kCLoadsPerWave = kCLoads / kWaves;    // 18
 constexpr int kQBytes = kNumHeads * kQkDim * 2;     // bf16 query of one sequence
 constexpr int kQLoads = kQBytes / 1024;             // 18
 constexpr int kPRow = kCTile + 16;                  // bytes per head row of P^T
-constexpr int kMaxItemPages = 512;                  // page ids of one item staged in LDS
+constexpr int kMaxItemPages = kItemPagesFp8;       // page ids of one item staged in LDS
 static_assert(kCLoads == kWaves * kCLoadsPerWave && kQLoads * 1024 == kQBytes, "load split");
 static_assert(kQBytes <= kCTileBytes, "the query is staged in the last ring slot");
 
@@ -155,9 +155,14 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a
   if constexpr (PAGED) {
     page0 = item.tok_begin >> a.page_shift;
     const int npages = min(((item.tok_end - 1) >> a.page_shift) - page0 + 1, kMaxItemPages);
-    for (int i = tid; i < npages; i += kStage1Threads)
-      sh.pages[i] = a.page_indices[seq_base + page0 + i];
-    __syncthreads();
+    // the item's page ids into LDS by four-byte cache-to-LDS loads, all in
+    // flight together (lanes past the last page repeat it)
+    const int32_t* psrc = a.page_indices + seq_base + page0;
+    const uint32_t pm0 = lds_u32(&sh.pages[0]);
+    for (int j = wave; 64 * j < npages; j += kWaves)
+      dma_u32(psrc + min(64 * j + lane, npages - 1), pm0 + 256 * j);
+    wait_loads<0>();
+    lds_barrier();
   }
 
   // This lane's slot in each of its wave's 18 loads of a tile: (tile row << 8)

@@ -68,7 +68,7 @@ constexpr int kXVBytes = kXTile * kXVRow;
 constexpr int kQBytes = kNumHeads * kQkDim * 2;    // bf16 query of one sequence
 constexpr int kQLoads = kQBytes / 1024;            // 18
 constexpr int kPRow = kXTile + 16;                 // bytes per head row of P^T
-constexpr int kMaxItemPages = 512;                 // page ids of one item staged in LDS
+constexpr int kMaxItemPages = kItemPagesMxfp4;     // page ids of one item staged in LDS
 static_assert(4 * 5 + 4 * 4 == kXFp4Loads && 4 * 2 + 4 * 3 == kXScaleLoads && kXScaleLoads * 64 >= kXScaleItems,
               "load split");
 static_assert(kQBytes <= kXVBytes, "the query is staged in the V tile");
@@ -215,9 +215,14 @@ __global__ __launch_bounds__(kXThreads, 1) void mla_stage1_mxfp4(Stage1Args a) {
   if constexpr (PAGED) {
     page0 = item.tok_begin >> a.page_shift;
     const int npages = min(((item.tok_end - 1) >> a.page_shift) - page0 + 1, kMaxItemPages);
-    for (int i = tid; i < npages; i += kXThreads)
-      sh.pages[i] = a.page_indices[seq_base + page0 + i];
-    __syncthreads();
+    // the item's page ids into LDS by four-byte cache-to-LDS loads, all in
+    // flight together (lanes past the last page repeat it)
+    const int32_t* psrc = a.page_indices + seq_base + page0;
+    const uint32_t pm0 = lds_u32(&sh.pages[0]);
+    for (int j = wave; 64 * j < npages; j += kXWaves)
+      dma_u32(psrc + min(64 * j + lane, npages - 1), pm0 + 256 * j);
+    wait_loads<0>();
+    lds_barrier();
   }
 
   // This wave's loads of a tile: code loads j0 .. j0 + 4 (or + 3), scale
