@@ -159,6 +159,29 @@ def test_planner_tiles_follow_the_format(B):
             assert len(items) == 256 and np.all(items[:, 2] - items[:, 1] == per_item), (bs, n, fmt)
 
 
+def test_planner_paged_items_fit_the_staged_pages(B):
+    """A paged item's page ids are staged in LDS by the split kernel (2560 for
+    fp8, 1536 for MXFP4, an item's first and last page possibly partial), so
+    the planner caps paged items at (pages - 2) * page_size tokens, in whole
+    tiles; uniform batches plan the same items as a contiguous cache."""
+    ps = 2
+    for fmt, pages in (("fp8", 2560), ("mxfp4", 1536)):
+        lens = [100000, 5]
+        npg = [(n + ps - 1) // ps for n in lens]
+        indptr = np.concatenate([[0], np.cumsum(npg)]).astype(np.int32)
+        last = [n - ps * (p - 1) for n, p in zip(lens, npg)]
+        items, slots, _ = B.mla_decode_plan_preview(indptr, last, page_size=ps, split_override=1,
+                                                    kv_dtype=fmt)
+        sizes = items[:, 2] - items[:, 1]
+        assert sizes.max() <= (pages - 2) * ps // 128 * 128, fmt
+        assert sizes.max() > (pages - 2) * ps // 2, fmt
+        _check_cover(items.tolist(), lens, slots)
+    indptr = np.arange(65, dtype=np.int32) * 4096  # 64 x 8192 tokens in 2-token pages
+    last = np.full(64, 2, dtype=np.int32)
+    items, _, _ = B.mla_decode_plan_preview(indptr, last, page_size=2, num_cus=256, blocks_per_cu=1)
+    assert len(items) == 256 and np.all(items[:, 2] - items[:, 1] == 2048)
+
+
 def test_planner_split_override(B):
     indptr = np.array([0, 1000, 1033, 1034], dtype=np.int32)
     items, slots, _ = B.mla_decode_plan_preview(indptr, split_override=4)
