@@ -8,28 +8,30 @@
 // bf16 output; otherwise it writes a normalised partial plus its log-sum-exp.
 // An empty sequence's item writes zeros.
 //
-//   mla_stage1_fp8  fp8 cache (mla_stage1_fp8.hip): 128-token tiles moved
-//                   HBM -> LDS by cache-to-LDS loads; both contractions on
-//                   fp8 / MX matrix instructions straight on the cached codes.
-//   mla_stage1      bf16 and MXFP4 caches: 64-token tiles staged through
-//                   registers, MXFP4 decoded to bf16 exactly on the way into
-//                   LDS, both contractions on v_mfma_f32_16x16x32_bf16.
-//   mla_merge       per (sequence, quarter of the columns) of the split
-//                   sequences, the log-sum-exp weighted merge of the partials
-//                   (727205 `mla_rd`; 700955 "locked baseline dispatch"
-//                   `reduce_lse_v71`; 599694 `_flash_fp8_split_s2`).
+//   mla_stage1_fp8    fp8 cache (mla_stage1_fp8.hip): 128-token tiles moved
+//                     HBM -> LDS by cache-to-LDS loads; both contractions on
+//                     fp8 / MX matrix instructions straight on the cached codes.
+//   mla_stage1_mxfp4  MXFP4 cache (mla_stage1_mxfp4.hip): the same streaming,
+//                     scores on the e2m1 codes with their e8m0 block scales,
+//                     V converted to e4m3 per tile for P.V.
+//   mla_stage1        (this file) bf16 cache, and MXFP4 whose scale rows are
+//                     not 2-byte aligned: 64-token tiles staged through
+//                     registers, MXFP4 decoded to bf16 exactly on the way into
+//                     LDS, both contractions on v_mfma_f32_16x16x32_bf16.
+//   mla_merge         (this file) per (sequence, quarter of the columns) of
+//                     the split sequences, the log-sum-exp weighted merge of
+//                     the partials (727205 `mla_rd`; 700955 "locked baseline
+//                     dispatch" `reduce_lse_v71`; 599694 `_flash_fp8_split_s2`).
 //
-// In both stage-1 kernels wave w scores a quarter of the tile's tokens
-// against the 16 heads (S^T[token, head] = K Q^T) and accumulates output
-// columns 128w..128w+127 over all of the tile's tokens (O^T[dim, head] +=
-// V^T P^T, V^T through the gfx950 transposing LDS reads); the softmax runs in
-// the log2 domain with a lazy maximum shared by the four waves, which only
-// moves (and O and the sums are rescaled) when a tile maximum passes it by
-// more than 8, bounding every weight by 2^8 and keeping the result exact.
-// Contractions over the 576 columns run in a permuted column order (any order
-// common to both operands is valid).  Everything accumulates in fp32; the fp8
-// per-tensor scale is folded into the score scale and the final
-// normalisation.
+// In mla_stage1 wave w scores a quarter of the tile's tokens against the 16
+// heads (S^T[token, head] = K Q^T) and accumulates output columns
+// 128w..128w+127 over all of the tile's tokens (O^T[dim, head] += V^T P^T,
+// V^T through the gfx950 transposing LDS reads); the softmax runs in the log2
+// domain with a lazy maximum shared by the four waves, which only moves (and
+// O and the sums are rescaled) when a tile maximum passes it by more than 8,
+// bounding every weight by 2^8 and keeping the result exact.  Contractions
+// over the 576 columns run in a permuted column order (any order common to
+// both operands is valid).  Everything accumulates in fp32.
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -45,24 +47,15 @@ namespace {
 // format traits
 // ---------------------------------------------------------------------------
 template <int F> struct Traits;
-template <> struct Traits<kFp8> {
-  static constexpr int kRowBytes = 576;  // stored row
-  static constexpr int kLdsPitch = 592;  // LDS row pitch (fp8 codes + 16 B)
-  static constexpr bool kLdsFp8 = true;
-  static constexpr int kBuffers = 1;     // unused: fp8 runs mla_stage1_fp8
-  static constexpr bool kPrefetch = false;
-};
 template <> struct Traits<kBf16> {
   static constexpr int kRowBytes = 1152;
   static constexpr int kLdsPitch = 1168;  // bf16 elements + 16 B
-  static constexpr bool kLdsFp8 = false;
   static constexpr int kBuffers = 1;
   static constexpr bool kPrefetch = false;  // a bf16 tile is 72 registers per lane
 };
 template <> struct Traits<kMxfp4> {
   static constexpr int kRowBytes = 288;   // e2m1 nibbles; scales live apart
   static constexpr int kLdsPitch = 1168;  // decoded to bf16 in LDS
-  static constexpr bool kLdsFp8 = false;
   static constexpr int kBuffers = 1;
   static constexpr bool kPrefetch = true;
 };
@@ -75,44 +68,30 @@ template <int F> struct Tile {
   // 16-B loads per thread (the MXFP4 tile, 1152 chunks, leaves the last one
   // to half of the threads)
   static constexpr int kChunks = (kChunkTotal + kStage1Threads - 1) / kStage1Threads;
-  // Each group of 16 rows sits 64 B further on than the one before, so that
-  // the transposing reads of an fp8 V step (rows 4g..4g+3 and 16+4g..16+4g+3
-  // together) fall on distinct banks.
+  // Each group of 16 rows sits 64 B further on than the one before, which
+  // spreads the transposing V reads (rows of two 16-row groups together)
+  // over the banks.
   static constexpr int kBytes = kTileTokens * Traits<F>::kLdsPitch + (kTileTokens / 16) * 64;
   __host__ __device__ static constexpr int row_offset(int r) {
     return r * Traits<F>::kLdsPitch + (r >> 4) * 64;
   }
 };
 
-// bytes one LDS row holds: stored row, or the decoded bf16 row for MXFP4
-template <int F> constexpr int kLdsRowBytes = Traits<F>::kLdsFp8 ? kQkDim : 2 * kQkDim;
+// bytes one LDS row holds: the bf16 row (stored, or decoded from MXFP4)
+template <int F> constexpr int kLdsRowBytes = 2 * kQkDim;
 
 template <int F> constexpr bool rows_disjoint() {
   for (int r = 0; r + 1 < kTileTokens; ++r)
     if (Tile<F>::row_offset(r) + kLdsRowBytes<F> > Tile<F>::row_offset(r + 1)) return false;
   return Tile<F>::row_offset(kTileTokens - 1) + kLdsRowBytes<F> <= Tile<F>::kBytes;
 }
-static_assert(rows_disjoint<kFp8>() && rows_disjoint<kBf16>() && rows_disjoint<kMxfp4>(),
-              "LDS tile rows overlap");
+static_assert(rows_disjoint<kBf16>() && rows_disjoint<kMxfp4>(), "LDS tile rows overlap");
 
-static_assert(Tile<kFp8>::kChunks == 9 && Tile<kBf16>::kChunks == 18 && Tile<kMxfp4>::kChunks == 5,
-              "tile chunking");
+static_assert(Tile<kBf16>::kChunks == 18 && Tile<kMxfp4>::kChunks == 5, "tile chunking");
 
 // ---------------------------------------------------------------------------
 // small device helpers
 // ---------------------------------------------------------------------------
-
-// 8 fp8 (e4m3fn) codes -> 8 bf16, exact.
-__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
-  bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
-  bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
-  bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
-  bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
-  bf16x8 r;
-  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
-  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
-  return r;
-}
 
 // 8 e2m1 nibbles (low nibble first) times 2^(e-127) -> 8 bf16, exact.
 __device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t w, float scale) {
@@ -251,16 +230,9 @@ __device__ __forceinline__ void attend_tile(Stage1Lds<F, PAGED>& sh, const uint8
     const uint8_t* kr = cur + k_off;
 #pragma unroll
     for (int j = 0; j < 9; ++j) {
-      bf16x8 kl, kh;
-      if constexpr (Traits<F>::kLdsFp8) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(kr + 64 * j);
-        kl = fp8x8_to_bf16(w[0], w[1]);
-        kh = fp8x8_to_bf16(w[2], w[3]);
-      } else {
-        const bf16x8* p = reinterpret_cast<const bf16x8*>(kr + 128 * j);
-        kl = p[0];
-        kh = p[1];
-      }
+      const bf16x8* p = reinterpret_cast<const bf16x8*>(kr + 128 * j);
+      const bf16x8 kl = p[0];
+      const bf16x8 kh = p[1];
       const int c = 2 * (j & 1);
       sacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl, qf[2 * j], sacc[c], 0, 0, 0);
       sacc[c + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qf[2 * j + 1], sacc[c + 1], 0, 0, 0);
@@ -316,20 +288,11 @@ __device__ __forceinline__ void attend_tile(Stage1Lds<F, PAGED>& sh, const uint8
     const uint8_t* vb = cur + kk * Tile<F>::row_offset(32);
 #pragma unroll
     for (int v = 0; v < 8; ++v) {
-      bf16x8 va;
-      if constexpr (Traits<F>::kLdsFp8) {
-        const i32x2 raw =
-            __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vb + v_off_lo + 16 * v));
-        va = fp8x8_to_bf16((uint32_t)raw[0], (uint32_t)raw[1]);
-      } else {
-        const i16x4 lo =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + v_off_lo + 32 * v));
-        const i16x4 hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + v_off_hi + 32 * v));
-        const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo);
-        const bf16x4 h4 = __builtin_bit_cast(bf16x4, hi);
-        va = bf16x8{l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
-      }
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + v_off_lo + 32 * v));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + v_off_hi + 32 * v));
+      const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo);
+      const bf16x4 h4 = __builtin_bit_cast(bf16x4, hi);
+      const bf16x8 va = bf16x8{l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
       o[v] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pt, o[v], 0, 0, 0);
     }
   }
@@ -361,13 +324,7 @@ __global__ __launch_bounds__(kStage1Threads, 2) void mla_stage1(Stage1Args a) {
   const int ntiles = (item.tok_end - item.tok_begin + kTileTokens - 1) / kTileTokens;
   const int64_t seq_base = item.kv_base;  // kv_indptr[b]: first row, or first page slot
 
-  float vscale = 1.0f;
-  float xscale = a.score_scale;
-  if constexpr (F == kFp8) {
-    const float s = *a.kv_scale;
-    vscale = s;
-    xscale *= s;
-  }
+  const float xscale = a.score_scale;
 
   // Query as the B operand of S^T = K Q^T: lane (head r16, group g) holds,
   // for k-step 2j+h, q[head][64j + 16g + 8h .. +8].
@@ -390,19 +347,12 @@ __global__ __launch_bounds__(kStage1Threads, 2) void mla_stage1(Stage1Args a) {
   float l_part = 0.f;     // this lane's share of the running sum
 
   // per-lane LDS offsets inside a tile buffer
-  const int k_off = Tile<F>::row_offset(16 * wave + r16) + (Traits<F>::kLdsFp8 ? 16 * g : 32 * g);
+  const int k_off = Tile<F>::row_offset(16 * wave + r16) + 32 * g;
   const int dv0 = 128 * wave;  // first output column of this wave
-  int v_off_lo, v_off_hi = 0;
-  if constexpr (Traits<F>::kLdsFp8) {
-    // ds_read_b64_tr_b8: lane pair (2e, 2e+1) names row e of an 8 x 16-byte
-    // block (8 bytes each); lane i receives byte i of each of the 8 rows.
-    v_off_lo = Tile<F>::row_offset(pv_token(g, r16 >> 1)) + (r16 & 1) * 8 + dv0;
-  } else {
-    // ds_read_b64_tr_b16: lane quad (4e..4e+3) names row e of a 4 x 16-element
-    // block (4 elements each); lane i receives element i of each of the 4 rows.
-    v_off_lo = Tile<F>::row_offset(pv_token(g, r16 >> 2)) + (r16 & 3) * 8 + 2 * dv0;
-    v_off_hi = Tile<F>::row_offset(pv_token(g, 4 + (r16 >> 2))) + (r16 & 3) * 8 + 2 * dv0;
-  }
+  // ds_read_b64_tr_b16: lane quad (4e..4e+3) names row e of a 4 x 16-element
+  // block (4 elements each); lane i receives element i of each of the 4 rows.
+  const int v_off_lo = Tile<F>::row_offset(pv_token(g, r16 >> 2)) + (r16 & 3) * 8 + 2 * dv0;
+  const int v_off_hi = Tile<F>::row_offset(pv_token(g, 4 + (r16 >> 2))) + (r16 & 3) * 8 + 2 * dv0;
 
   {
     // ---- register-staged tiles through one LDS buffer ----
@@ -432,7 +382,7 @@ __global__ __launch_bounds__(kStage1Threads, 2) void mla_stage1(Stage1Args a) {
   if (g == 0) sh.lsum[wave][r16] = l_w;
   __syncthreads();
   const float L = (sh.lsum[0][r16] + sh.lsum[1][r16]) + (sh.lsum[2][r16] + sh.lsum[3][r16]);
-  const float f = vscale / L;
+  const float f = 1.0f / L;
   if (item.slot < 0) {
     uint16_t* dst = a.out + ((int64_t)b * kNumHeads + r16) * kVDim + dv0 + 4 * g;
 #pragma unroll
