@@ -139,20 +139,17 @@ __device__ __forceinline__ void fp4x8_to_fp8(uint32_t w, float scale, uint32_t& 
 }
 
 // 8 e2m1 codes (low nibble first) times 2^-k, 0 <= k <= 5, -> 8 e4m3 codes
-// (two words) by table lookup: every nonzero e2m1 magnitude {0.5, 1, 1.5, 2,
-// 3, 4, 6} times 2^-k is a normal e4m3 number whose code is the k = 0 code
-// less k in the exponent field, so the 8-entry table (lut_lo: magnitudes
-// 0..3, lut_hi: 4..7) is a shifted constant; v_perm_b32 looks up four
-// magnitudes at once, the sign bit moves from bit 3 to bit 7, and the codes
-// of even and odd nibbles are interleaved back into column order.
-__device__ __forceinline__ void fp4x8_to_fp8_lut(uint32_t w, uint32_t lut_lo, uint32_t lut_hi, uint32_t& lo,
-                                                 uint32_t& hi) {
-  const uint32_t pe = __builtin_amdgcn_perm(lut_hi, lut_lo, w & 0x07070707u);          // even nibbles
-  const uint32_t po = __builtin_amdgcn_perm(lut_hi, lut_lo, (w >> 4) & 0x07070707u);   // odd nibbles
-  const uint32_t ce = ((w << 4) & 0x80808080u) | pe;
-  const uint32_t co = (w & 0x80808080u) | po;
-  lo = __builtin_amdgcn_perm(co, ce, 0x05010400u);  // columns 0, 1, 2, 3
-  hi = __builtin_amdgcn_perm(co, ce, 0x07030602u);  // columns 4, 5, 6, 7
+// by table lookup: every nonzero e2m1 magnitude {0.5, 1, 1.5, 2, 3, 4, 6}
+// times 2^-k is a normal e4m3 number whose code is the k = 0 code less k in
+// the exponent field, so the 8-entry table (lut_lo: magnitudes 0..3, lut_hi:
+// 4..7) is a shifted constant; v_perm_b32 looks up four magnitudes at once
+// and the sign bit moves from bit 3 to bit 7.  The codes come out as the V
+// tile stores a group of 8 columns: even columns (0, 2, 4, 6) in `ev`, odd
+// ones in `od`.
+__device__ __forceinline__ void fp4x8_to_fp8_lut(uint32_t w, uint32_t lut_lo, uint32_t lut_hi, uint32_t& ev,
+                                                 uint32_t& od) {
+  ev = ((w << 4) & 0x80808080u) | __builtin_amdgcn_perm(lut_hi, lut_lo, w & 0x07070707u);
+  od = (w & 0x80808080u) | __builtin_amdgcn_perm(lut_hi, lut_lo, (w >> 4) & 0x07070707u);
 }
 
 // Maxima of the two 16-bit halves of v over the 32 lanes of this half wave,
@@ -478,7 +475,7 @@ __global__ __launch_bounds__(kXThreads, 1) void mla_stage1_mxfp4(Stage1Args a) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int j = max((int)e[k] - (int)c[k], -126);  // <= 0
-        uint32_t e8[8];  // 32 e4m3 codes, columns 32cb + 4i .. +3 in word i
+        uint32_t e8[8];  // 32 e4m3 codes: word 2i columns 32cb + 8i + {0,2,4,6}, word 2i+1 the odd ones
         if (__ballot(j < -5) == 0) {  // the whole wave by table
           const uint32_t kk = (uint32_t)(-j);
           const uint32_t lut_lo = 0x3C383000u - kk * 0x08080800u;
@@ -488,7 +485,12 @@ __global__ __launch_bounds__(kXThreads, 1) void mla_stage1_mxfp4(Stage1Args a) {
         } else {  // a scale more than 5 binades below its block maximum: exact rounding conversions
           const float scale = __uint_as_float((uint32_t)(127 + j) << 23);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) fp4x8_to_fp8(w[k][i], scale, e8[2 * i], e8[2 * i + 1]);
+          for (int i = 0; i < 4; ++i) {
+            uint32_t lo, hi;  // columns 0..3, 4..7
+            fp4x8_to_fp8(w[k][i], scale, lo, hi);
+            e8[2 * i] = __builtin_amdgcn_perm(hi, lo, 0x06040200u);      // columns 0, 2, 4, 6
+            e8[2 * i + 1] = __builtin_amdgcn_perm(hi, lo, 0x07050301u);  // columns 1, 3, 5, 7
+          }
         }
         *reinterpret_cast<u32x4*>(vdst + 128 * k) = u32x4{e8[0], e8[1], e8[2], e8[3]};
         *reinterpret_cast<u32x4*>(vdst + 128 * k + 16) = u32x4{e8[4], e8[5], e8[6], e8[7]};
@@ -553,6 +555,20 @@ __global__ __launch_bounds__(kXThreads, 1) void mla_stage1_mxfp4(Stage1Args a) {
   const f32x4 ls0 = *reinterpret_cast<const f32x4*>(&sh.red_l[r16][0]);
   const f32x4 ls1 = *reinterpret_cast<const f32x4*>(&sh.red_l[r16][4]);
   const float L = ((ls0[0] + ls0[1]) + (ls0[2] + ls0[3])) + ((ls1[0] + ls1[1]) + (ls1[2] + ls1[3]));
+  // The V tile holds each group of 8 columns as (0, 2, 4, 6, 1, 3, 5, 7), so
+  // lane group g has output columns 8(g >> 1) + 2i + (g & 1) of each column
+  // tile; lanes l and l ^ 16 trade two values each to return to columns
+  // 4g + i.
+  {
+    const int partner = (lane ^ 16) << 2;
+    const bool odd = (g & 1) != 0;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float r0 = __int_as_float(__builtin_amdgcn_ds_bpermute(partner, __float_as_int(odd ? o[v][0] : o[v][2])));
+      const float r1 = __int_as_float(__builtin_amdgcn_ds_bpermute(partner, __float_as_int(odd ? o[v][1] : o[v][3])));
+      o[v] = odd ? f32x4{r0, o[v][2], r1, o[v][3]} : f32x4{o[v][0], r0, o[v][1], r1};
+    }
+  }
   finish_item<4>(a, item, tid, wave >> 1, 4 * (wave & 1), lane, o, 1.0f / L, m_ref + __log2f(L));
 }
 
