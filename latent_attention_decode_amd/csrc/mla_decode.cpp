@@ -157,12 +157,8 @@ static void plan_items(const std::vector<int64_t>& lens, const int32_t* indptr, 
                        int num_cus, int blocks_per_cu, int page_size, int64_t tile, int64_t max_pages,
                        PlanOut* out) {
   const int batch = static_cast<int>(lens.size());
-  int64_t total = 0, max_len = 0, nonempty = 0;
-  for (int64_t n : lens) {
-    total += n;
-    max_len = std::max(max_len, n);
-    nonempty += n > 0;
-  }
+  int64_t total = 0;
+  for (int64_t n : lens) total += n;
   // A paged item's page ids are staged in LDS: at most max_pages of them
   // (an item's first and last page may be partial).
   const int64_t max_item = page_size > 1 && max_pages < INT64_MAX / 2
@@ -176,10 +172,12 @@ static void plan_items(const std::vector<int64_t>& lens, const int32_t* indptr, 
       chunk[b] = round_up((lens[b] + ns - 1) / ns, kTile);
     }
   } else if (total > 0) {
-    const double mean = static_cast<double>(total) / static_cast<double>(nonempty);
-    const bool ragged = static_cast<double>(max_len) > 1.25 * mean;
+    // About one item per resident workgroup slot, ragged batches included:
+    // every item start and end costs the streaming a few microseconds, which
+    // outweighs the finer load balance of more, shorter items (measured on
+    // the ragged bs256 batch: 1, 2, 4 items per slot -> 151, 156, 160 us).
     const int64_t slots = static_cast<int64_t>(num_cus) * std::max(blocks_per_cu, 1);
-    const int64_t target = slots * (ragged ? 4 : 1);
+    const int64_t target = slots;
     const int64_t c = std::max<int64_t>(tile,
                                         round_up((total + target - 1) / target, tile));
     for (int b = 0; b < batch; ++b) {

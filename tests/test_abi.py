@@ -190,13 +190,17 @@ def test_planner_split_override(B):
     _check_cover(items.tolist(), [1000, 33, 1], slots)
 
 
-def test_planner_ragged_gets_more_items(B):
+def test_planner_ragged_batch_one_item_per_slot(B):
+    """A ragged batch is cut like a uniform one, into about one item per
+    resident workgroup slot (each sequence adds at most one shorter piece):
+    every item boundary costs streaming time that finer balancing does not
+    win back."""
     from latent_attention_decode_amd import synth
     lens = synth.config_lens("bs256_ragged1024-8192_fp8_paged2")
     pages = (lens + 1) // 2
     indptr = np.concatenate([[0], np.cumsum(pages)]).astype(np.int32)
     last = (lens - 2 * (pages - 1)).astype(np.int32)
     items, slots, _ = B.mla_decode_plan_preview(indptr, last, page_size=2, num_cus=256,
-                                                blocks_per_cu=2)
-    assert len(items) > 2 * 512
+                                                blocks_per_cu=1)
+    assert 256 <= len(items) <= 256 + len(lens)
     _check_cover(items.tolist(), lens.tolist(), slots)
