@@ -39,7 +39,10 @@
  * output (the item is the whole sequence) or a normalised partial and its
  * log-sum-exp; the partials of every split sequence are merged by their
  * log-sum-exp weights (727205 `mla_rd`, 700955 `reduce_lse_v71`, 599694
- * `_flash_fp8_split_s2`).  The merge is a second kernel launch, except for an
+ * `_flash_fp8_split_s2`).  For an fp8 or MXFP4 cache and sequences of
+ * different lengths, the planner cuts the batch into bins of about equal
+ * work, one per resident workgroup, and a workgroup runs the items of its
+ * bin in turn (a sequence may span bins).  The merge is a second kernel launch, except for an
  * fp8 or MXFP4 cache with a plan whose items differ in length (at most 12 per
  * sequence): there the item of a sequence that finishes last merges its
  * partials, so each call is one launch.  No merge runs when no sequence is
@@ -128,11 +131,15 @@ mla_status mla_decode_plan(mla_decode_t h, int batch, const int32_t* kv_indptr_h
  * whole tiles of its split kernel: 64 tokens for bf16, 128 otherwise) and
  * the device figures it would read (compute units, resident stage-1
  * workgroups per unit).  Writes up to
- * max_items work items as int32 quadruples (sequence, first token, end token,
- * partial slot, or -1 when the item is the whole sequence, or -2 for the item
- * that writes an empty sequence's zero output) in launch order,
- * and the number of items, partial slots and the workspace bytes.  Returns
- * MLA_ERR_INVALID_ARG when max_items is too small (num_items still set).
+ * max_items work items as rows of five int32 (sequence, first token, end
+ * token, partial slot or -1 when the item is the whole sequence or -2 for the
+ * item that writes an empty sequence's zero output, and the workgroup that
+ * runs it) in launch order, and the number of items, partial slots and the
+ * workspace bytes.  For fp8 and MXFP4 caches a ragged batch is cut into bins
+ * of about equal work, one per resident workgroup, whose items one
+ * workgroup runs in turn; otherwise each item has a workgroup of its own.
+ * Returns MLA_ERR_INVALID_ARG when max_items is too small (num_items still
+ * set).
  */
 mla_status mla_decode_plan_preview(int batch, const int32_t* kv_indptr_host,
                                    const int32_t* kv_last_page_len_host, int page_size,
@@ -141,9 +148,10 @@ mla_status mla_decode_plan_preview(int batch, const int32_t* kv_indptr_host,
                                    int* num_items, int* num_slots, size_t* workspace_bytes);
 
 /*
- * Describe the current plan: number of work items (workgroups launched), the
- * largest number of items given to one sequence, and the number of partials
- * written to the workspace.  Any output pointer may be NULL.
+ * Describe the current plan: number of work items (workgroups launched,
+ * unless the plan has bins: see mla_decode_plan_preview), the largest number
+ * of items given to one sequence, and the number of partials written to the
+ * workspace.  Any output pointer may be NULL.
  */
 mla_status mla_decode_plan_info(mla_decode_t h, int* num_items, int* max_splits,
                                 int* num_partials);

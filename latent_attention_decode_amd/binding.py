@@ -129,7 +129,8 @@ def mla_decode_plan(h, kv_indptr_host, kv_last_page_len_host=None, split_overrid
 def mla_decode_plan_preview(kv_indptr_host, kv_last_page_len_host=None, page_size: int = 1,
                             split_override: int = 0, num_cus: int = 256, blocks_per_cu: int = 2,
                             kv_dtype: str = "fp8"):
-    """Host-only planner.  Returns (items int32 [n, 4], num_slots, workspace_bytes)."""
+    """Host-only planner.  Returns (items int32 [n, 5], num_slots, workspace_bytes); an item
+    row is (sequence, first token, end token, slot, workgroup)."""
     ip = _host_i32(kv_indptr_host)
     lp = None if kv_last_page_len_host is None else _host_i32(kv_last_page_len_host)
     n = ctypes.c_int()
@@ -141,7 +142,7 @@ def mla_decode_plan_preview(kv_indptr_host, kv_last_page_len_host=None, page_siz
                                       ctypes.byref(ws))
     if st != 0 and n.value == 0:
         _check(st, "mla_decode_plan_preview")
-    items = np.zeros((max(n.value, 1), 4), dtype=np.int32)
+    items = np.zeros((max(n.value, 1), 5), dtype=np.int32)
     st = _lib.mla_decode_plan_preview(*args, items.ctypes.data, n.value, ctypes.byref(n),
                                       ctypes.byref(slots), ctypes.byref(ws))
     _check(st, "mla_decode_plan_preview")

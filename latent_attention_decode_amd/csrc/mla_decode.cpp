@@ -35,7 +35,9 @@ struct mla_decode_s {
   int num_merge = 0;  // sequences with >= 2 partials
   bool fused_merge = false;  // the fp8 kernel merges them itself (no merge launch)
   int uniform_splits = 0, uniform_chunk = 0, uniform_len = 0, uniform_base = 0;
-  // device: [num_items] WorkItem, [num_merge] MergeSeq, [num_merge] int32 counters
+  int num_bins = 0;  // > 0: binned plan (see PlanOut)
+  // device: [num_items] WorkItem, [num_merge] MergeSeq, [num_merge] int32
+  // counters, [num_bins + 1] int32 bin starts
   void* dev_plan = nullptr;
   size_t dev_plan_bytes = 0;
   int num_cus = 0;
@@ -51,7 +53,7 @@ struct mla_decode_s {
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 1 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 2 * 100 + 0;
 
 mla_status fail(mla_decode_t h, mla_status st, const char* fmt, ...) {
   if (h) {
@@ -133,6 +135,9 @@ static bool seq_lengths(const int32_t* indptr, const int32_t* last, int batch, i
 struct PlanOut {
   std::vector<WorkItem> items;
   std::vector<MergeSeq> merge;
+  // Binned plan: workgroup k runs items bins[k] .. bins[k + 1] - 1 (bins has
+  // one entry more than there are workgroups); empty: workgroup k runs item k.
+  std::vector<int32_t> bins;
   // uniform plan (see Stage1Args): splits per sequence, chunk, length; 0 if not
   int uniform_splits = 0, uniform_chunk = 0, uniform_len = 0;
   int num_slots = 0;
@@ -152,10 +157,152 @@ static int64_t plan_tile(int kv_dtype) { return kv_dtype == MLA_KV_BF16 ? kPlanT
 static int64_t item_pages(int kv_dtype) {
   return kv_dtype == MLA_KV_FP8_E4M3 ? kItemPagesFp8 : kv_dtype == MLA_KV_MXFP4 ? kItemPagesMxfp4 : INT64_MAX;
 }
+// The formats whose split kernel runs bins of items.
+static bool plan_binned(int kv_dtype) { return kv_dtype != MLA_KV_BF16; }
+
+// Bins for a ragged batch (fp8 and MXFP4 kernels, which run the items of a
+// bin one after the other).  One item per workgroup leaves the compute units
+// that drew the short items idle while the long ones finish (a quarter of
+// the time on lengths spread evenly over 1024..8192); here the sequences,
+// longest first, are laid end to end and cut into at most `slots` bins of
+// about equal cost, a piece costing its tokens plus kPieceCost for its start
+// and finish.  A sequence cut across bins becomes several items, merged like
+// any split.  No piece is shorter than kMinPiece unless its sequence is.
+constexpr int64_t kPieceCost = 96;
+constexpr int64_t kMinPiece = 256;
+
+struct Piece {
+  int32_t batch;
+  int64_t t0, t1;
+};
+
+// Greedy fill of bins of cost capacity C in stream order; returns the number
+// of bins and the largest number of pieces of one sequence.
+static int64_t fill_bins(const std::vector<int64_t>& lens, const std::vector<int32_t>& order, int64_t C,
+                         int64_t tile, int64_t max_item, std::vector<std::vector<Piece>>* out,
+                         int64_t* max_pieces) {
+  int64_t bins = 1, r = C, most = 0;
+  if (out) out->assign(1, {});
+  for (int32_t b : order) {
+    const int64_t n = lens[b];
+    int64_t pos = 0, pieces = 0;
+    while (pos < n) {
+      const int64_t rest = n - pos;
+      int64_t take;
+      if (rest <= max_item && rest + kPieceCost <= r) {
+        take = rest;
+      } else {
+        take = std::min((r - kPieceCost) / tile * tile, max_item);
+        if (rest - take < kMinPiece) take = (rest - kMinPiece) / tile * tile;
+        if (take < kMinPiece) {  // the bin is full
+          ++bins;
+          r = C;
+          if (out) out->emplace_back();
+          continue;
+        }
+      }
+      if (out) out->back().push_back(Piece{b, pos, pos + take});
+      pos += take;
+      r -= take + kPieceCost;
+      ++pieces;
+    }
+    most = std::max(most, pieces);
+  }
+  if (max_pieces) *max_pieces = most;
+  return bins;
+}
+
+// Whether a batch gets bins, and then the plan.  Returns false (nothing
+// written) for batches the one-item-per-workgroup plan serves as well:
+// equal lengths, or too few tokens per slot for a bin to hold more than one
+// piece of the minimum size.
+static bool plan_bins(const std::vector<int64_t>& lens, const int32_t* indptr, int64_t slots, int64_t tile,
+                      int64_t max_item, int64_t max_splits, PlanOut* out) {
+  const int batch = static_cast<int>(lens.size());
+  int64_t total = 0, longest = 0;
+  bool equal = true;
+  for (int64_t n : lens) {
+    total += n;
+    longest = std::max(longest, n);
+    equal = equal && n == lens[0];
+  }
+  const int64_t c_min = kPieceCost + 2 * kMinPiece;
+  if (equal || slots < 1 || (total + slots - 1) / slots < c_min || max_item < 2 * kMinPiece) return false;
+  std::vector<int32_t> order;
+  for (int b = 0; b < batch; ++b)
+    if (lens[b]) order.push_back(b);
+  std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) { return lens[x] > lens[y]; });
+
+  // the least capacity that fits the batch into `slots` bins, no sequence in
+  // more than max_splits pieces (the fill is monotone in C)
+  auto fits = [&](int64_t C) {
+    int64_t most = 0;
+    return fill_bins(lens, order, C, tile, max_item, nullptr, &most) <= slots && most <= max_splits;
+  };
+  int64_t lo = std::max((total + slots - 1) / slots, c_min);
+  int64_t hi = lo;
+  // one bin holds the whole batch beyond this capacity; if that still
+  // splits a sequence too often (page staging), bins do not apply
+  const int64_t one_bin = total + kPieceCost * (batch + total / kMinPiece + 2) + c_min;
+  while (!fits(hi)) {
+    if (hi > one_bin) return false;
+    hi *= 2;
+  }
+  while (lo < hi) {
+    const int64_t mid = lo + (hi - lo) / 2;
+    if (fits(mid))
+      hi = mid;
+    else
+      lo = mid + 1;
+  }
+  std::vector<std::vector<Piece>> bins;
+  fill_bins(lens, order, lo, tile, max_item, &bins, nullptr);
+  while (!bins.empty() && bins.back().empty()) bins.pop_back();
+
+  // slots: the pieces of a sequence, in stream order
+  std::vector<int32_t> npieces(batch, 0), first_slot(batch, 0), job(batch, -1), seen(batch, 0);
+  for (const auto& bin : bins)
+    for (const Piece& p : bin) ++npieces[p.batch];
+  out->items.clear();
+  out->merge.clear();
+  out->bins.clear();
+  out->num_slots = 0;
+  out->max_splits = 0;
+  for (int b = 0; b < batch; ++b) {
+    out->max_splits = std::max<int>(out->max_splits, npieces[b]);
+    if (npieces[b] < 2) continue;
+    job[b] = static_cast<int32_t>(out->merge.size());
+    first_slot[b] = out->num_slots;
+    out->merge.push_back(MergeSeq{b, out->num_slots, npieces[b], 0});
+    out->num_slots += npieces[b];
+  }
+  // empty sequences: their zero-output items go to the bins in turn
+  std::vector<int32_t> empties;
+  for (int b = 0; b < batch; ++b)
+    if (!lens[b]) empties.push_back(b);
+  const size_t nbins = std::max<size_t>(bins.size(), 1);
+  for (size_t k = 0; k < nbins; ++k) {
+    out->bins.push_back(static_cast<int32_t>(out->items.size()));
+    if (k < bins.size())
+      for (const Piece& p : bins[k]) {
+        const int b = p.batch;
+        const bool whole = npieces[b] == 1;
+        out->items.push_back(WorkItem{b, static_cast<int32_t>(p.t0), static_cast<int32_t>(p.t1),
+                                      whole ? WorkItem::kWhole : first_slot[b] + seen[b]++, indptr[b],
+                                      whole ? -1 : job[b], whole ? 0 : first_slot[b],
+                                      whole ? 0 : npieces[b]});
+      }
+    for (size_t e = k; e < empties.size(); e += nbins)
+      out->items.push_back(WorkItem{empties[e], 0, 0, WorkItem::kEmpty, indptr[empties[e]], -1, 0, 0});
+  }
+  out->bins.push_back(static_cast<int32_t>(out->items.size()));
+  out->uniform_splits = out->uniform_chunk = out->uniform_len = 0;
+  return true;
+}
 
 static void plan_items(const std::vector<int64_t>& lens, const int32_t* indptr, int split_override,
                        int num_cus, int blocks_per_cu, int page_size, int64_t tile, int64_t max_pages,
-                       PlanOut* out) {
+                       bool binned, PlanOut* out) {
   const int batch = static_cast<int>(lens.size());
   int64_t total = 0;
   for (int64_t n : lens) total += n;
@@ -164,6 +311,11 @@ static void plan_items(const std::vector<int64_t>& lens, const int32_t* indptr, 
   const int64_t max_item = page_size > 1 && max_pages < INT64_MAX / 2
                                ? (max_pages - 2) * static_cast<int64_t>(page_size) / tile * tile
                                : INT64_MAX;
+  out->bins.clear();
+  if (binned && split_override == 0 &&
+      plan_bins(lens, indptr, static_cast<int64_t>(num_cus) * std::max(blocks_per_cu, 1), tile, max_item,
+                kMaxAutoSplits, out))
+    return;
   std::vector<int64_t> chunk(batch, 0);
   if (split_override > 0) {
     for (int b = 0; b < batch; ++b) {
@@ -323,13 +475,14 @@ mla_status mla_decode_plan(mla_decode_t h, int batch, const int32_t* kv_indptr_h
 
   mla::PlanOut plan;
   mla::plan_items(lens, kv_indptr_host, split_override, h->num_cus, h->blocks_per_cu, h->page_size,
-                  mla::plan_tile(h->kv_dtype), mla::item_pages(h->kv_dtype), &plan);
+                  mla::plan_tile(h->kv_dtype), mla::item_pages(h->kv_dtype), mla::plan_binned(h->kv_dtype), &plan);
 
   const size_t items_bytes = plan.items.size() * sizeof(mla::WorkItem);
   const size_t merge_bytes = plan.merge.size() * sizeof(mla::MergeSeq);
   // completion counters of the fused merge, zero as uploaded
   const size_t counter_bytes = plan.merge.size() * sizeof(int32_t);
-  const size_t need = items_bytes + merge_bytes + counter_bytes;
+  const size_t bins_bytes = plan.bins.size() * sizeof(int32_t);
+  const size_t need = items_bytes + merge_bytes + counter_bytes + bins_bytes;
   if (need > h->dev_plan_bytes) {
     if (h->dev_plan) (void)hipFree(h->dev_plan);
     h->dev_plan = nullptr;
@@ -341,11 +494,14 @@ mla_status mla_decode_plan(mla_decode_t h, int batch, const int32_t* kv_indptr_h
   std::vector<unsigned char> blob(need, 0);
   if (items_bytes) std::memcpy(blob.data(), plan.items.data(), items_bytes);
   if (merge_bytes) std::memcpy(blob.data() + items_bytes, plan.merge.data(), merge_bytes);
+  if (bins_bytes)
+    std::memcpy(blob.data() + items_bytes + merge_bytes + counter_bytes, plan.bins.data(), bins_bytes);
   if (hipMemcpy(h->dev_plan, blob.data(), need, hipMemcpyHostToDevice) != hipSuccess)
     return fail(h, MLA_ERR_HIP, "uploading the work list failed");
 
   h->batch = batch;
   h->num_items = static_cast<int>(plan.items.size());
+  h->num_bins = plan.bins.empty() ? 0 : static_cast<int>(plan.bins.size()) - 1;
   h->num_slots = plan.num_slots;
   h->max_splits = plan.max_splits;
   h->num_merge = static_cast<int>(plan.merge.size());
@@ -383,17 +539,20 @@ mla_status mla_decode_plan_preview(int batch, const int32_t* kv_indptr_host,
     return MLA_ERR_INVALID_ARG;
   mla::PlanOut plan;
   mla::plan_items(lens, kv_indptr_host, split_override, num_cus, blocks_per_cu, page_size,
-                  mla::plan_tile(kv_dtype), mla::item_pages(kv_dtype), &plan);
+                  mla::plan_tile(kv_dtype), mla::item_pages(kv_dtype), mla::plan_binned(kv_dtype), &plan);
   const int n = static_cast<int>(plan.items.size());
   if (num_items) *num_items = n;
   if (num_slots) *num_slots = plan.num_slots;
   if (workspace_bytes) *workspace_bytes = static_cast<size_t>(plan.num_slots) * slot_bytes();
   if (n > max_items) return MLA_ERR_INVALID_ARG;
+  int bin = 0;
   for (int i = 0; i < n; ++i) {
-    items_out[4 * i + 0] = plan.items[i].batch;
-    items_out[4 * i + 1] = plan.items[i].tok_begin;
-    items_out[4 * i + 2] = plan.items[i].tok_end;
-    items_out[4 * i + 3] = plan.items[i].slot;
+    while (!plan.bins.empty() && i >= plan.bins[bin + 1]) ++bin;
+    items_out[5 * i + 0] = plan.items[i].batch;
+    items_out[5 * i + 1] = plan.items[i].tok_begin;
+    items_out[5 * i + 2] = plan.items[i].tok_end;
+    items_out[5 * i + 3] = plan.items[i].slot;
+    items_out[5 * i + 4] = plan.bins.empty() ? i : bin;
   }
   return MLA_OK;
 }
@@ -472,7 +631,13 @@ mla_status mla_decode_run(mla_decode_t h, const void* q, const void* kv, const v
   const bool timed = h->profiling && h->events_ready;
   h->timed_run = false;
   h->merge_timed = false;
-  hipError_t e = mla::launch_stage1(h->kv_dtype, h->page_size > 1, a, h->num_items, s,
+  // The fp8 and MXFP4 kernels run a binned plan bin by bin; the generic one
+  // (MXFP4 with odd scale addresses) takes its items one per workgroup.
+  const bool by_bin = h->num_bins > 0 && mla::stage1_dedicated(h->kv_dtype, a);
+  a.bins = by_bin ? reinterpret_cast<const int32_t*>(plan_base + items_bytes + merge_bytes +
+                                                     static_cast<size_t>(h->num_merge) * sizeof(int32_t))
+                  : nullptr;
+  hipError_t e = mla::launch_stage1(h->kv_dtype, h->page_size > 1, a, by_bin ? h->num_bins : h->num_items, s,
                                      timed ? h->ev[0] : nullptr, timed ? h->ev[1] : nullptr);
   if (e != hipSuccess) return fail(h, MLA_ERR_HIP, "stage-1 launch: %s", hipGetErrorString(e));
   if (h->num_merge > 0 && !a.counters) {

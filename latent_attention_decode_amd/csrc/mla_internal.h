@@ -123,6 +123,10 @@ struct Stage1Args {
   // finishes last reads the other partials of its sequence and writes the
   // output, so no merge kernel runs.
   int* counters;
+  // Non-null (fp8 and MXFP4 kernels): workgroup k runs items
+  // bins[k] .. bins[k + 1] - 1, one after the other; null: workgroup k runs
+  // item k.  The bins of a ragged batch carry about equal work.
+  const int32_t* bins;
 };
 
 struct MergeArgs {

@@ -66,6 +66,7 @@ constexpr int kQLoads = kQBytes / 1024;             // 18
 constexpr int kPRow = kCTile + 16;                  // bytes per head row of P^T
 constexpr int kMaxItemPages = kItemPagesFp8;       // page ids of one item staged in LDS
 static_assert(kCLoads == kWaves * kCLoadsPerWave && kQLoads * 1024 == kQBytes, "load split");
+static_assert(2 * kQBytes <= kCTileBytes, "the query and its e4m3 words fit a ring slot");
 static_assert(kQBytes <= kCTileBytes, "the query is staged in the last ring slot");
 
 // Position of 16-byte chunk c of tile row r inside the row: c ^ chunk_swz(r),
@@ -112,14 +113,9 @@ struct Fp8Lds {
   int32_t pages[kMaxItemPages];            // paged: page ids of the item
 };
 
+// One work item: tokens [tok_begin, tok_end) of one sequence.
 template <bool PAGED>
-__global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a) {
-  __shared__ __attribute__((aligned(16))) Fp8Lds sh;
-
-  const WorkItem item = a.uniform_splits
-                            ? uniform_item(xcd_block(blockIdx.x, gridDim.x), a.uniform_splits, a.uniform_chunk,
-                                           a.uniform_len, a.uniform_base)
-                            : a.items[blockIdx.x];
+__device__ __forceinline__ void fp8_item(const Stage1Args& a, const WorkItem& item, Fp8Lds& sh) {
   const int tid = threadIdx.x;
   if (item.slot == WorkItem::kEmpty) {  // empty sequence: its output is zero
     uint4* dst = reinterpret_cast<uint4*>(a.out + (int64_t)item.batch * kNumHeads * kVDim);
@@ -223,49 +219,72 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a
   // Query, B operand of S^T = K Q^T, scaled by 2^s and split into e4m3
   // hi + lo: for 128-column block K (0..3) lane (head r16, group g) holds
   // q[head][128K + 32g .. +32]; for the rope columns, k-step h (0, 1),
-  // q[head][512 + 16g + 8h .. +8].
+  // q[head][512 + 16g + 8h .. +8].  Every wave needs all of it; wave w
+  // converts block K = w (and waves 0, 1 rope step h = w), and the waves
+  // trade their head maxima and then the converted words through LDS, in
+  // the query's ring slot behind the bf16 query.
   fp8x32 qh[4], ql[4];
   fp8x8 rh[2], rl[2];
   float xscale;
   {
     const uint8_t* qlds = &sh.tile[kCRing - 1][0];
-    bf16x8 qv[18];  // [4K + i]: chunk 16K + 4g + i; [16 + h]: chunk 64 + 2g + h
+    // converted words: [K][hi, lo][lane][8], then rope [h][hi, lo][lane][2]
+    uint32_t* const qcv = reinterpret_cast<uint32_t*>(&sh.tile[kCRing - 1][kQBytes]);
+    const bool rope = wave < 2;
+    bf16x8 qv[5];  // [i]: chunk 16 wave + 4g + i; [4]: rope chunk 64 + 2g + wave
 #pragma unroll
-    for (int K = 0; K < 4; ++K)
+    for (int i = 0; i < 4; ++i)
+      qv[i] = *reinterpret_cast<const bf16x8*>(qlds + 16 * q_slot(r16, 16 * wave + 4 * g + i));
+    qv[4] = rope ? *reinterpret_cast<const bf16x8*>(qlds + 16 * q_slot(r16, 64 + 2 * g + wave)) : bf16x8{};
+    float am[5];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        qv[4 * K + i] = *reinterpret_cast<const bf16x8*>(qlds + 16 * q_slot(r16, 16 * K + 4 * g + i));
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      qv[16 + h] = *reinterpret_cast<const bf16x8*>(qlds + 16 * q_slot(r16, 64 + 2 * g + h));
-    float amax = 0.f;
-#pragma unroll
-    for (int k = 0; k < 18; ++k)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)qv[k][e]));
-    amax = xor_max_groups(amax);
+    for (int k = 0; k < 5; ++k) {
+      float m0 = fmaxf(fabsf((float)qv[k][0]), fabsf((float)qv[k][1]));
+      float m1 = fmaxf(fabsf((float)qv[k][2]), fabsf((float)qv[k][3]));
+      float m2 = fmaxf(fabsf((float)qv[k][4]), fabsf((float)qv[k][5]));
+      float m3 = fmaxf(fabsf((float)qv[k][6]), fabsf((float)qv[k][7]));
+      am[k] = fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
+    }
+    float amax = xor_max_groups(fmaxf(fmaxf(fmaxf(am[0], am[1]), fmaxf(am[2], am[3])), am[4]));
+    if (g == 0) sh.red_m[r16][wave] = amax;
+    lds_barrier();
+    const f32x4 wm = *reinterpret_cast<const f32x4*>(&sh.red_m[r16][0]);
+    amax = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
     // 2^s with amax * 2^s in [128, 256)
     const int s = (amax > 0.f) ? 8 - __builtin_amdgcn_frexp_expf(amax) : 0;
     xscale = a.score_scale * kv_scale * __builtin_ldexpf(1.0f, -s);
-    uint32_t hw[36], lw[36];  // word 2k + m: elements 4m..4m+3 of qv[k]
+    uint32_t hw[10], lw[10];  // word 2k + m: elements 4m..4m+3 of qv[k]
 #pragma unroll
-    for (int k = 0; k < 18; ++k)
+    for (int k = 0; k < 5; ++k)
 #pragma unroll
       for (int m = 0; m < 2; ++m)
         split_fp8x4(__builtin_ldexpf((float)qv[k][4 * m], s), __builtin_ldexpf((float)qv[k][4 * m + 1], s),
                     __builtin_ldexpf((float)qv[k][4 * m + 2], s), __builtin_ldexpf((float)qv[k][4 * m + 3], s),
                     hw[2 * k + m], lw[2 * k + m]);
+    u32x4* const kh = reinterpret_cast<u32x4*>(qcv + ((2 * wave) * 64 + lane) * 8);
+    u32x4* const kl = reinterpret_cast<u32x4*>(qcv + ((2 * wave + 1) * 64 + lane) * 8);
+    kh[0] = u32x4{hw[0], hw[1], hw[2], hw[3]};
+    kh[1] = u32x4{hw[4], hw[5], hw[6], hw[7]};
+    kl[0] = u32x4{lw[0], lw[1], lw[2], lw[3]};
+    kl[1] = u32x4{lw[4], lw[5], lw[6], lw[7]};
+    if (rope) {
+      *reinterpret_cast<uint2*>(qcv + 4096 + ((2 * wave) * 64 + lane) * 2) = uint2{hw[8], hw[9]};
+      *reinterpret_cast<uint2*>(qcv + 4096 + ((2 * wave + 1) * 64 + lane) * 2) = uint2{lw[8], lw[9]};
+    }
+    lds_barrier();
 #pragma unroll
-    for (int K = 0; K < 4; ++K)
-#pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        qh[K][d] = (int)hw[8 * K + d];
-        ql[K][d] = (int)lw[8 * K + d];
-      }
+    for (int K = 0; K < 4; ++K) {
+      const u32x4* h = reinterpret_cast<const u32x4*>(qcv + ((2 * K) * 64 + lane) * 8);
+      const u32x4* l = reinterpret_cast<const u32x4*>(qcv + ((2 * K + 1) * 64 + lane) * 8);
+      qh[K] = join16(h[0], h[1]);
+      ql[K] = join16(l[0], l[1]);
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      rh[h] = pack_fp8x8(hw[32 + 2 * h], hw[33 + 2 * h]);
-      rl[h] = pack_fp8x8(lw[32 + 2 * h], lw[33 + 2 * h]);
+      const uint2 wh = *reinterpret_cast<const uint2*>(qcv + 4096 + ((2 * h) * 64 + lane) * 2);
+      const uint2 wl = *reinterpret_cast<const uint2*>(qcv + 4096 + ((2 * h + 1) * 64 + lane) * 2);
+      rh[h] = pack_fp8x8(wh.x, wh.y);
+      rl[h] = pack_fp8x8(wl.x, wl.y);
     }
   }
 
@@ -434,6 +453,26 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a
   const float L = (ls[0] + ls[1]) + (ls[2] + ls[3]);
   const float f = kv_scale / L;
   finish_item<8>(a, item, tid, wave, 0, lane, o, f, m_ref + __log2f(L));
+}
+
+// A workgroup runs one item, or with bins the items of bin blockIdx.x in
+// order (see Stage1Args).  Between two items every load and store of the
+// first is complete and every wave is past it, so the next may reuse LDS.
+template <bool PAGED>
+__global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a) {
+  __shared__ __attribute__((aligned(16))) Fp8Lds sh;
+  int i = a.bins ? a.bins[blockIdx.x] : (int)blockIdx.x;
+  const int i_end = a.bins ? a.bins[blockIdx.x + 1] : i + 1;
+  while (i < i_end) {
+    const WorkItem item = a.uniform_splits
+                              ? uniform_item(xcd_block(blockIdx.x, gridDim.x), a.uniform_splits, a.uniform_chunk,
+                                             a.uniform_len, a.uniform_base)
+                              : a.items[i];
+    fp8_item<PAGED>(a, item, sh);
+    if (++i == i_end) break;
+    wait_loads<0>();
+    lds_barrier();
+  }
 }
 
 }  // namespace

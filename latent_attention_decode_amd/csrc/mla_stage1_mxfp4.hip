@@ -71,7 +71,7 @@ constexpr int kPRow = kXTile + 16;                 // bytes per head row of P^T
 constexpr int kMaxItemPages = kItemPagesMxfp4;     // page ids of one item staged in LDS
 static_assert(4 * 5 + 4 * 4 == kXFp4Loads && 4 * 2 + 4 * 3 == kXScaleLoads && kXScaleLoads * 64 >= kXScaleItems,
               "load split");
-static_assert(kQBytes <= kXVBytes, "the query is staged in the V tile");
+static_assert(2 * kQBytes <= kXVBytes, "the query and its e4m3 words are staged in the V tile");
 
 // Position of 16-byte chunk c (0..71) of query head h.  (The V tile needs
 // no permutation: at a row pitch of 528 bytes = 132 banks, the eight rows of
@@ -170,14 +170,9 @@ __device__ __forceinline__ uint32_t half_wave_max2(uint32_t v) {
   return pk_max_u16((uint32_t)x[0], (uint32_t)x[1]);
 }
 
+// One work item: tokens [tok_begin, tok_end) of one sequence.
 template <bool PAGED>
-__global__ __launch_bounds__(kXThreads, 1) void mla_stage1_mxfp4(Stage1Args a) {
-  __shared__ __attribute__((aligned(16))) Fp4Lds sh;
-
-  const WorkItem item = a.uniform_splits
-                            ? uniform_item(xcd_block(blockIdx.x, gridDim.x), a.uniform_splits, a.uniform_chunk,
-                                           a.uniform_len, a.uniform_base)
-                            : a.items[blockIdx.x];
+__device__ __forceinline__ void mxfp4_item(const Stage1Args& a, const WorkItem& item, Fp4Lds& sh) {
   const int tid = threadIdx.x;
   if (item.slot == WorkItem::kEmpty) {  // empty sequence: its output is zero
     uint4* dst = reinterpret_cast<uint4*>(a.out + (int64_t)item.batch * kNumHeads * kVDim);
@@ -319,48 +314,69 @@ __global__ __launch_bounds__(kXThreads, 1) void mla_stage1_mxfp4(Stage1Args a) {
   // Query, B operand of the scores, scaled by 2^s and split into e4m3 hi +
   // lo.  K-step K (0..3): bytes b < 16 column 128K + 16g + b, bytes 16..31
   // column 128K + 64 + 16g + b - 16; rope step: bytes b < 16 column
-  // 512 + 16g + b, bytes 16..31 zero.
+  // 512 + 16g + b, bytes 16..31 zero.  Every wave needs all of it; wave w
+  // converts half j = w & 1 (bytes 16j .. 16j + 15) of K-step w >> 1, and
+  // waves 0, 1 half w of the rope step; the waves trade their head maxima
+  // and then the converted words through LDS, behind the bf16 query.
   fp8x32 qh[4], ql[4], rh, rl;
   float xscale;
   {
     const uint8_t* qlds = &sh.v[0];
-    bf16x8 qv[18];  // [4K + i]: chunk 16K + 2g + {0, 1, 8, 9}[i]; [16 + h]: chunk 64 + 2g + h
+    // converted words: [K][hi, lo][lane][8], then rope [hi, lo][lane][4]
+    uint32_t* const qcv = reinterpret_cast<uint32_t*>(&sh.v[kQBytes]);
+    const int K0 = wave >> 1, j = wave & 1;
+    const bool rope = wave < 2;
+    bf16x8 qv[3];  // [i]: chunk 16 K0 + 2g + 8j + i; [2]: rope chunk 64 + 2g + wave
 #pragma unroll
-    for (int K = 0; K < 4; ++K)
+    for (int i = 0; i < 2; ++i)
+      qv[i] = *reinterpret_cast<const bf16x8*>(qlds + 16 * q_slot(r16, 16 * K0 + 2 * g + 8 * j + i));
+    qv[2] = rope ? *reinterpret_cast<const bf16x8*>(qlds + 16 * q_slot(r16, 64 + 2 * g + wave)) : bf16x8{};
+    float am[3];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        qv[4 * K + i] =
-            *reinterpret_cast<const bf16x8*>(qlds + 16 * q_slot(r16, 16 * K + 2 * g + (i & 1) + 8 * (i >> 1)));
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      qv[16 + h] = *reinterpret_cast<const bf16x8*>(qlds + 16 * q_slot(r16, 64 + 2 * g + h));
-    float amax = 0.f;
-#pragma unroll
-    for (int k = 0; k < 18; ++k)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)qv[k][e]));
-    amax = xor_max_groups(amax);
+    for (int k = 0; k < 3; ++k) {
+      float m0 = fmaxf(fabsf((float)qv[k][0]), fabsf((float)qv[k][1]));
+      float m1 = fmaxf(fabsf((float)qv[k][2]), fabsf((float)qv[k][3]));
+      float m2 = fmaxf(fabsf((float)qv[k][4]), fabsf((float)qv[k][5]));
+      float m3 = fmaxf(fabsf((float)qv[k][6]), fabsf((float)qv[k][7]));
+      am[k] = fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
+    }
+    float amax = xor_max_groups(fmaxf(fmaxf(am[0], am[1]), am[2]));
+    if (g == 0) sh.red_m[r16][wave] = amax;
+    lds_barrier();
+    const f32x4 wm0 = *reinterpret_cast<const f32x4*>(&sh.red_m[r16][0]);
+    const f32x4 wm1 = *reinterpret_cast<const f32x4*>(&sh.red_m[r16][4]);
+    amax = fmaxf(fmaxf(fmaxf(wm0[0], wm0[1]), fmaxf(wm0[2], wm0[3])),
+                 fmaxf(fmaxf(wm1[0], wm1[1]), fmaxf(wm1[2], wm1[3])));
     const int s = (amax > 0.f) ? 8 - __builtin_amdgcn_frexp_expf(amax) : 0;
     xscale = a.score_scale * __builtin_ldexpf(1.0f, -s);
-    uint32_t hw[36], lw[36];
+    uint32_t hw[6], lw[6];  // word 2k + m: elements 4m..4m+3 of qv[k]
 #pragma unroll
-    for (int k = 0; k < 18; ++k)
+    for (int k = 0; k < 3; ++k)
 #pragma unroll
       for (int m = 0; m < 2; ++m)
         split_fp8x4(__builtin_ldexpf((float)qv[k][4 * m], s), __builtin_ldexpf((float)qv[k][4 * m + 1], s),
                     __builtin_ldexpf((float)qv[k][4 * m + 2], s), __builtin_ldexpf((float)qv[k][4 * m + 3], s),
                     hw[2 * k + m], lw[2 * k + m]);
+    *reinterpret_cast<u32x4*>(qcv + ((2 * K0) * 64 + lane) * 8 + 4 * j) = u32x4{hw[0], hw[1], hw[2], hw[3]};
+    *reinterpret_cast<u32x4*>(qcv + ((2 * K0 + 1) * 64 + lane) * 8 + 4 * j) = u32x4{lw[0], lw[1], lw[2], lw[3]};
+    if (rope) {
+      *reinterpret_cast<uint2*>(qcv + 4096 + lane * 4 + 2 * wave) = uint2{hw[4], hw[5]};
+      *reinterpret_cast<uint2*>(qcv + 4096 + (64 + lane) * 4 + 2 * wave) = uint2{lw[4], lw[5]};
+    }
+    lds_barrier();
 #pragma unroll
-    for (int K = 0; K < 4; ++K)
-#pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        qh[K][d] = (int)hw[8 * K + d];
-        ql[K][d] = (int)lw[8 * K + d];
-      }
+    for (int K = 0; K < 4; ++K) {
+      const u32x4* h = reinterpret_cast<const u32x4*>(qcv + ((2 * K) * 64 + lane) * 8);
+      const u32x4* l = reinterpret_cast<const u32x4*>(qcv + ((2 * K + 1) * 64 + lane) * 8);
+      qh[K] = join16(h[0], h[1]);
+      ql[K] = join16(l[0], l[1]);
+    }
+    const u32x4 wh = *reinterpret_cast<const u32x4*>(qcv + 4096 + lane * 4);
+    const u32x4 wl = *reinterpret_cast<const u32x4*>(qcv + 4096 + (64 + lane) * 4);
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
-      rh[d] = d < 4 ? (int)hw[32 + d] : 0;
-      rl[d] = d < 4 ? (int)lw[32 + d] : 0;
+      rh[d] = d < 4 ? (int)wh[d] : 0;
+      rl[d] = d < 4 ? (int)wl[d] : 0;
     }
   }
 
@@ -570,6 +586,26 @@ __global__ __launch_bounds__(kXThreads, 1) void mla_stage1_mxfp4(Stage1Args a) {
     }
   }
   finish_item<4>(a, item, tid, wave >> 1, 4 * (wave & 1), lane, o, 1.0f / L, m_ref + __log2f(L));
+}
+
+// A workgroup runs one item, or with bins the items of bin blockIdx.x in
+// order (see Stage1Args).  Between two items every load and store of the
+// first is complete and every wave is past it, so the next may reuse LDS.
+template <bool PAGED>
+__global__ __launch_bounds__(kXThreads, 1) void mla_stage1_mxfp4(Stage1Args a) {
+  __shared__ __attribute__((aligned(16))) Fp4Lds sh;
+  int i = a.bins ? a.bins[blockIdx.x] : (int)blockIdx.x;
+  const int i_end = a.bins ? a.bins[blockIdx.x + 1] : i + 1;
+  while (i < i_end) {
+    const WorkItem item = a.uniform_splits
+                              ? uniform_item(xcd_block(blockIdx.x, gridDim.x), a.uniform_splits, a.uniform_chunk,
+                                             a.uniform_len, a.uniform_base)
+                              : a.items[i];
+    mxfp4_item<PAGED>(a, item, sh);
+    if (++i == i_end) break;
+    wait_loads<0>();
+    lds_barrier();
+  }
 }
 
 }  // namespace

@@ -84,7 +84,11 @@ def test_plan_and_run_validate_before_any_gpu_call(B):
 
 
 def _check_cover(items, lens, slots):
-    """Every token of every sequence is in exactly one item; slots are a partition."""
+    """Every token of every sequence is in exactly one item; slots are a partition;
+    items are listed workgroup by workgroup."""
+    wg = [it[4] for it in items]
+    assert wg == sorted(wg) and (not wg or (wg[0] == 0 and set(wg) == set(range(wg[-1] + 1))))
+    items = [it[:4] for it in items]
     seen = {b: np.zeros(n, dtype=np.int32) for b, n in enumerate(lens)}
     used_slots = []
     empty = [b for b, t0, t1, s in items if s == -2]
@@ -117,7 +121,8 @@ def test_planner_covers_every_token_once(B, lens):
     items, slots, ws = B.mla_decode_plan_preview(indptr, num_cus=256, blocks_per_cu=2)
     _check_cover(items.tolist(), lens, slots)
     assert ws == slots * 16 * 513 * 4
-    # items are listed longest first
+    # one item per workgroup (these batches are too small for bins), longest first
+    assert np.all(items[:, 4] == np.arange(len(items)))
     sizes = items[:, 2] - items[:, 1]
     assert np.all(np.diff(sizes) <= 0)
 
@@ -190,17 +195,76 @@ def test_planner_split_override(B):
     _check_cover(items.tolist(), [1000, 33, 1], slots)
 
 
-def test_planner_ragged_batch_one_item_per_slot(B):
-    """A ragged batch is cut like a uniform one, into about one item per
-    resident workgroup slot (each sequence adds at most one shorter piece):
-    every item boundary costs streaming time that finer balancing does not
-    win back."""
+def _bin_costs(items):
+    """Tokens plus 96 per item (the planner's cost of an item's start and
+    finish) of each workgroup's bin."""
+    cost = np.zeros(items[:, 4].max() + 1, dtype=np.int64)
+    np.add.at(cost, items[:, 4], (items[:, 2] - items[:, 1]) + 96)
+    return cost
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("page_size", [1, 2, 16])
+def test_planner_ragged_batch_gets_even_bins(B, fmt, page_size):
+    """fp8 / MXFP4 and a ragged batch (lengths spread over 1024..8192): the
+    sequences are cut into at most one bin per resident workgroup, whose
+    costs (tokens + 96 per item) are within one short item of each other,
+    instead of one item per workgroup that leaves the short ones idle."""
     from latent_attention_decode_amd import synth
     lens = synth.config_lens("bs256_ragged1024-8192_fp8_paged2")
-    pages = (lens + 1) // 2
+    pages = (lens + page_size - 1) // page_size
     indptr = np.concatenate([[0], np.cumsum(pages)]).astype(np.int32)
-    last = (lens - 2 * (pages - 1)).astype(np.int32)
-    items, slots, _ = B.mla_decode_plan_preview(indptr, last, page_size=2, num_cus=256,
-                                                blocks_per_cu=1)
-    assert 256 <= len(items) <= 256 + len(lens)
+    last = (lens - page_size * (pages - 1)).astype(np.int32)
+    items, slots, _ = B.mla_decode_plan_preview(indptr, last if page_size > 1 else None, page_size=page_size,
+                                                num_cus=256, blocks_per_cu=1, kv_dtype=fmt)
     _check_cover(items.tolist(), lens.tolist(), slots)
+    cost = _bin_costs(items)
+    assert len(cost) <= 256
+    mean = (lens.sum() + 96 * len(items)) / 256
+    assert cost.max() <= mean + 256 + 96, (cost.max(), mean)
+    assert cost.max() < 1.1 * mean
+    sizes = items[:, 2] - items[:, 1]
+    whole = items[:, 3] == -1
+    assert np.all(sizes[~whole] >= 256)            # no piece shorter than 256 tokens
+    assert np.all(items[~whole, 1] % 128 == 0)     # pieces start on a tile
+    assert np.bincount(items[:, 0]).max() <= 12    # the kernels merge these themselves
+    if page_size > 1:
+        cap = 2560 if fmt == "fp8" else 1536
+        first = items[:, 1] // page_size
+        lastp = (items[:, 2] - 1) // page_size
+        assert np.all(lastp - first + 1 <= cap)
+
+
+def test_planner_bins_respect_the_page_cap_and_split_limit(B):
+    """Bins never give a paged item more pages than the kernel stages (1536
+    for MXFP4: at most 1534 whole 2-token pages, 2944 tokens in whole tiles),
+    and no sequence more than 32 items; where the page cap alone would need
+    more, the batch falls back to one item per workgroup."""
+    ps = 2
+    for lens in ([60000, 3000, 1200] + [900] * 300, [2000, 120000, 700] + [1000] * 200):
+        lens = np.array(lens)
+        pages = (lens + ps - 1) // ps
+        indptr = np.concatenate([[0], np.cumsum(pages)]).astype(np.int32)
+        last = (lens - ps * (pages - 1)).astype(np.int32)
+        items, slots, _ = B.mla_decode_plan_preview(indptr, last, page_size=ps, num_cus=256,
+                                                    blocks_per_cu=1, kv_dtype="mxfp4")
+        _check_cover(items.tolist(), lens.tolist(), slots)
+        sizes = items[:, 2] - items[:, 1]
+        assert sizes.max() <= 2944
+        binned = len(items) > 0 and items[-1, 4] < len(items) - 1
+        assert binned == (lens.max() <= 32 * 2944), lens.max()
+        if binned:
+            assert np.bincount(items[:, 0]).max() <= 32
+
+
+def test_planner_bins_hold_empty_sequences_and_no_bf16(B):
+    """Empty sequences of a binned batch get their zero-output item in some
+    bin; bf16 caches (whose kernel runs one item per workgroup) get no bins."""
+    lens = np.array([0, 5000, 0, 300] + [4000, 1500] * 100 + [0])
+    indptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    items, slots, _ = B.mla_decode_plan_preview(indptr, num_cus=64, blocks_per_cu=1, kv_dtype="fp8")
+    _check_cover(items.tolist(), lens.tolist(), slots)
+    assert items[:, 4].max() + 1 <= 64 and len(items) > 64
+    items, slots, _ = B.mla_decode_plan_preview(indptr, num_cus=64, blocks_per_cu=1, kv_dtype="bf16")
+    _check_cover(items.tolist(), lens.tolist(), slots)
+    assert np.all(items[:, 4] == np.arange(len(items)))

@@ -149,6 +149,42 @@ def test_paged_items_at_the_page_cap(B, oracle_mod, fmt):
     check_close(run_gpu(B, case, 1), oracle_out(oracle_mod, case), fmt, f"{fmt} page cap")
 
 
+def _binned_lens(kind):
+    rng = np.random.default_rng(77 if kind == "mixed" else 78)
+    if kind == "mixed":  # short and long sequences, empty and 1-token ones: bins of up to 7 items
+        lens = np.concatenate([rng.integers(1, 600, 60), rng.integers(600, 4000, 100), [0, 0, 1, 1, 9000, 7000]])
+    else:  # one sequence across more than 12 bins: the merge kernel combines its partials
+        lens = np.concatenate([[90000], rng.integers(500, 1100, 250)])
+    rng.shuffle(lens)
+    return lens.tolist()
+
+
+@pytest.mark.parametrize("kind", ["mixed", "one_long"])
+@pytest.mark.parametrize("fmt,ps,shuffled,stride", [
+    ("fp8", 1, False, 18), ("fp8", 2, True, 18), ("mxfp4", 1, False, 18), ("mxfp4", 16, True, 18),
+    ("mxfp4", 1, False, 19),
+])
+def test_binned_ragged_batch(B, oracle_mod, kind, fmt, ps, shuffled, stride):
+    """A ragged batch large enough for bins (fp8 / MXFP4: one bin of about
+    equal work per resident workgroup, whose items one workgroup runs in
+    turn, a sequence possibly spanning bins): every output against the
+    oracle, and a repeat bit for bit.  With odd MXFP4 scale strides the
+    bf16-decoding kernel runs the same items one per workgroup."""
+    lens = _binned_lens(kind)
+    case = synth.make_case(fmt, lens, seed=44, page_size=ps, shuffle_pages=shuffled, scale_stride=stride)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    items, _, _ = B.mla_decode_plan_preview(case.kv_indptr, case.kv_last_page_len if ps > 1 else None,
+                                            page_size=ps, num_cus=cus, blocks_per_cu=1, kv_dtype=fmt)
+    per_bin = np.bincount(items[:, 4])
+    splits = np.bincount(items[:, 0]).max()
+    note(f"{kind} {fmt} ps {ps}: {len(items)} items in {len(per_bin)} bins, up to {per_bin.max()} per bin, "
+         f"{splits} per sequence")
+    assert per_bin.max() > 1 and (splits > 12) == (kind == "one_long")
+    a, b = run_gpu(B, case, repeats=2)
+    check_close(a, oracle_out(oracle_mod, case), fmt, f"binned {kind} {fmt} ps {ps}")
+    assert np.array_equal(a, b)
+
+
 def test_empty_sequences_give_zero(B, oracle_mod):
     case = synth.make_case("fp8", [0, 100, 0, 1], seed=24)
     got = run_gpu(B, case)
