@@ -40,7 +40,8 @@ E2M1_GRID = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)  # codes 0..7 (OCP MX v1.0)
 class DecodeCase:
     """One decode call's worth of inputs (host arrays).
 
-    q_bits            uint16 [batch, 16, 576]: bf16 bit patterns of the query.
+    q_bits            uint16 [rows, 16, 576]: bf16 bit patterns of the query (rows =
+                      batch, or the query tokens of all sequences with qo_indptr).
     kv                uint8  [rows, row_bytes]: the cache rows as stored.
     kv_scale          fp32 per-tensor dequant scale (fp8); 1.0 otherwise.
     kv_scales         uint8  [rows, scale_stride] e8m0 block scales (mxfp4) or None.
@@ -48,6 +49,7 @@ class DecodeCase:
     kv_page_indices   int32  [num_pages_used] physical page ids, or None (page_size 1).
     kv_last_page_len  int32  [batch] valid tokens in each last page, or None.
     lens              int64  [batch] tokens per sequence.
+    qo_indptr         int32  [batch+1] query rows per sequence (multi-token decode), or None.
     """
 
     kv_dtype: str
@@ -61,6 +63,12 @@ class DecodeCase:
     kv_indptr: np.ndarray
     kv_page_indices: Optional[np.ndarray]
     kv_last_page_len: Optional[np.ndarray]
+    qo_indptr: Optional[np.ndarray] = None
+
+    @property
+    def rows(self) -> int:
+        """Query (and output) rows."""
+        return int(self.q_bits.shape[0])
 
     @property
     def scale_stride(self) -> int:
@@ -173,14 +181,17 @@ def make_case(kv_dtype: str,
               scale_stride: int = MX_BLOCKS,
               guard_rows: int = 0,
               q_values: Optional[np.ndarray] = None,
-              kv_values: Optional[np.ndarray] = None) -> DecodeCase:
+              kv_values: Optional[np.ndarray] = None,
+              q_lens: Optional[Sequence[int]] = None) -> DecodeCase:
     """Build a seeded decode case.
 
     Values: q ~ N(0,1) [batch,16,576] and one N(0,1) latent row per token, in
     logical token order (sequence 0 first), both drawn from one
     ``torch.Generator`` seeded with ``seed`` (q first, then the cache, then the
     page permutation).  ``q_values`` / ``kv_values`` (fp32, same shapes)
-    replace the draws for structured tests.  Unreferenced rows -- the slack of
+    replace the draws for structured tests.  ``q_lens`` (multi-token decode)
+    gives each sequence that many query rows: q is then [sum(q_lens), 16, 576]
+    and the case carries qo_indptr.  Unreferenced rows -- the slack of
     each last page and ``guard_rows`` extra rows at the end -- are filled with
     NaN-producing bytes so that reading them shows up in the output.
     """
@@ -193,10 +204,19 @@ def make_case(kv_dtype: str,
     total = int(lens_np.sum())
     g = torch.Generator().manual_seed(int(seed))
 
+    qo_indptr = None
+    rows = batch
+    if q_lens is not None:
+        ql = np.asarray(q_lens, dtype=np.int64)
+        if ql.size != batch or np.any(ql < 0) or np.any(ql > lens_np):
+            raise ValueError("q_lens: one count per sequence, 0 <= q_len <= its length")
+        qo_indptr = np.zeros(batch + 1, dtype=np.int32)
+        qo_indptr[1:] = np.cumsum(ql)
+        rows = int(qo_indptr[-1])
     if q_values is None:
-        q = torch.randn((batch, NUM_HEADS, QK_DIM), generator=g, dtype=torch.float32)
+        q = torch.randn((rows, NUM_HEADS, QK_DIM), generator=g, dtype=torch.float32)
     else:
-        q = torch.as_tensor(np.asarray(q_values, dtype=np.float32)).reshape(batch, NUM_HEADS, QK_DIM)
+        q = torch.as_tensor(np.asarray(q_values, dtype=np.float32)).reshape(rows, NUM_HEADS, QK_DIM)
     if kv_values is None:
         x = torch.randn((total, QK_DIM), generator=g, dtype=torch.float32)
     else:
@@ -250,7 +270,8 @@ def make_case(kv_dtype: str,
 
     return DecodeCase(kv_dtype=kv_dtype, batch=batch, page_size=page_size, lens=lens_np,
                       q_bits=q_bits, kv=kv, kv_scale=float(kv_scale), kv_scales=scales,
-                      kv_indptr=indptr, kv_page_indices=page_indices, kv_last_page_len=last_len)
+                      kv_indptr=indptr, kv_page_indices=page_indices, kv_last_page_len=last_len,
+                      qo_indptr=qo_indptr)
 
 
 def ragged_lens(batch: int, lo: int, hi: int, seed: int) -> np.ndarray:
@@ -268,16 +289,21 @@ CONFIGS = {
     "bs256_ragged1024-8192_fp8_paged2": ("fp8", 256, (1024, 8192), 2, True, 1004),
     "bs32_kv8192_fp8": ("fp8", 32, 8192, 1, False, 1005),
     "bs64_kv8192_fp8": ("fp8", 64, 8192, 1, False, 1006),
+    # multi-token decode: every sequence has q query tokens (its last q positions)
+    "bs64_kv8192_q2_fp8": ("fp8", 64, 8192, 1, False, 1007, 2),
+    "bs16_kv8192_q4_fp8": ("fp8", 16, 8192, 1, False, 1008, 4),
 }
 
 
 def config_lens(name: str) -> np.ndarray:
-    kv_dtype, batch, kv_len, _ps, _sh, seed = CONFIGS[name]
+    kv_dtype, batch, kv_len, _ps, _sh, seed = CONFIGS[name][:6]
     if isinstance(kv_len, tuple):
         return ragged_lens(batch, kv_len[0], kv_len[1], seed + 7919)
     return np.full(batch, kv_len, dtype=np.int64)
 
 
 def config_case(name: str) -> DecodeCase:
-    kv_dtype, _batch, _kv_len, ps, shuffled, seed = CONFIGS[name]
-    return make_case(kv_dtype, config_lens(name), seed=seed, page_size=ps, shuffle_pages=shuffled)
+    kv_dtype, batch, _kv_len, ps, shuffled, seed = CONFIGS[name][:6]
+    q = CONFIGS[name][6] if len(CONFIGS[name]) > 6 else 1
+    return make_case(kv_dtype, config_lens(name), seed=seed, page_size=ps, shuffle_pages=shuffled,
+                     q_lens=None if q == 1 else np.full(batch, q))

@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for single-token MLA decode -- TEST INFRASTRUCTURE ONLY.
+"""fp64 CPU oracle for MLA decode (single- and multi-token) -- TEST INFRASTRUCTURE ONLY.
 
 Only the tests, the package smoke check and the benchmark's CPU-baseline leg
 may import this package.  The product path (``latent_attention_decode_amd``)
@@ -47,6 +47,11 @@ class OracleLib:
                                           ctypes.c_int64, P, P, P, ctypes.c_int, P, P, P,
                                           ctypes.c_int, ctypes.c_int, P, P]
         lib.oracle_mla_decode.restype = ctypes.c_int
+        lib.oracle_mla_decode_multi.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                ctypes.c_double, ctypes.c_int, P, ctypes.c_double, P,
+                                                ctypes.c_int64, P, P, P, ctypes.c_int, P, P,
+                                                ctypes.c_int, ctypes.c_int, P, P]
+        lib.oracle_mla_decode_multi.restype = ctypes.c_int
         self.lib = lib
         self.path = path
 
@@ -83,16 +88,24 @@ class OracleLib:
                    kv_last_page_len: Optional[np.ndarray] = None, v_dim: int = 512,
                    sm_scale: Optional[float] = None,
                    splits: Optional[Sequence[Sequence[int]]] = None,
-                   batches: Optional[Sequence[int]] = None, nthreads: Optional[int] = None):
-        """Exact decode.  Returns (out [bs, nh, v_dim] fp64, lse [bs, nh] fp64).
+                   batches: Optional[Sequence[int]] = None, nthreads: Optional[int] = None,
+                   qo_indptr: Optional[np.ndarray] = None):
+        """Exact decode.  Returns (out [rows, nh, v_dim] fp64, lse [rows, nh] fp64).
 
-        q_bits: uint16 bf16 patterns [bs, nh, qk_dim].  ``splits[b]`` (split
-        mode) lists the exclusive end token of each range of sequence b, in
-        order, the last one being the sequence length.  ``batches`` restricts
-        the work to those sequences (the other rows are NaN).
+        q_bits: uint16 bf16 patterns [rows, nh, qk_dim]; one row per sequence,
+        or with ``qo_indptr`` (multi-token decode, int32 [bs + 1]) rows
+        qo_indptr[b] .. qo_indptr[b + 1] - 1 for the query tokens of sequence
+        b.  ``splits[b]`` (split mode, single-token only) lists the exclusive
+        end token of each range of sequence b, in order, the last one being
+        the sequence length.  ``batches`` restricts the work to those
+        sequences (the other rows are NaN).
         """
         q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
-        bs, nh, qk_dim = q_bits.shape
+        rows, nh, qk_dim = q_bits.shape
+        bs = rows if qo_indptr is None else len(qo_indptr) - 1
+        qo = None if qo_indptr is None else np.ascontiguousarray(qo_indptr, dtype=np.int32)
+        if qo is not None and (qo[-1] != rows or splits is not None):
+            raise ValueError("qo_indptr must end at the number of query rows, without split mode")
         if sm_scale is None:
             sm_scale = 1.0 / np.sqrt(float(qk_dim))
         kv = np.ascontiguousarray(kv, dtype=np.uint8)
@@ -111,15 +124,22 @@ class OracleLib:
                 else np.zeros(1, dtype=np.int32), dtype=np.int32)
         sel = None if batches is None else np.ascontiguousarray(batches, dtype=np.int32)
         n_sel = 0 if sel is None else sel.size
-        out = np.full((bs, nh, v_dim), np.nan, dtype=np.float64)
-        lse = np.full((bs, nh), np.nan, dtype=np.float64)
+        out = np.full((rows, nh, v_dim), np.nan, dtype=np.float64)
+        lse = np.full((rows, nh), np.nan, dtype=np.float64)
         if nthreads is None:
             nthreads = max(1, len(os.sched_getaffinity(0)))
-        rc = self.lib.oracle_mla_decode(_ptr(q_bits), bs, nh, qk_dim, v_dim, float(sm_scale),
-                                        _FMT[kv_dtype], _ptr(kv), float(kv_scale), _ptr(sc), stride,
-                                        _ptr(indptr), _ptr(pages), _ptr(last), int(page_size),
-                                        _ptr(split_indptr), _ptr(split_bounds), _ptr(sel), n_sel,
-                                        int(nthreads), _ptr(out), _ptr(lse))
+        if qo is None:
+            rc = self.lib.oracle_mla_decode(_ptr(q_bits), bs, nh, qk_dim, v_dim, float(sm_scale),
+                                            _FMT[kv_dtype], _ptr(kv), float(kv_scale), _ptr(sc), stride,
+                                            _ptr(indptr), _ptr(pages), _ptr(last), int(page_size),
+                                            _ptr(split_indptr), _ptr(split_bounds), _ptr(sel), n_sel,
+                                            int(nthreads), _ptr(out), _ptr(lse))
+        else:
+            rc = self.lib.oracle_mla_decode_multi(_ptr(q_bits), bs, nh, qk_dim, v_dim, float(sm_scale),
+                                                  _FMT[kv_dtype], _ptr(kv), float(kv_scale), _ptr(sc), stride,
+                                                  _ptr(indptr), _ptr(pages), _ptr(last), int(page_size),
+                                                  _ptr(qo), _ptr(sel), n_sel, int(nthreads), _ptr(out),
+                                                  _ptr(lse))
         if rc:
             raise ValueError(f"oracle_mla_decode failed (code {rc})")
         return out, lse
@@ -129,7 +149,8 @@ class OracleLib:
         return self.mla_decode(case.q_bits, case.kv_dtype, case.kv, case.kv_indptr,
                                kv_scale=case.kv_scale, kv_scales=case.kv_scales,
                                page_size=case.page_size, kv_page_indices=case.kv_page_indices,
-                               kv_last_page_len=case.kv_last_page_len, **kw)
+                               kv_last_page_len=case.kv_last_page_len,
+                               qo_indptr=getattr(case, "qo_indptr", None), **kw)
 
 
 _default: Optional[OracleLib] = None

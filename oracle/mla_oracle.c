@@ -1,5 +1,6 @@
 /*
- * fp64 CPU oracle for single-token multi-head latent attention (MLA) decode.
+ * fp64 CPU oracle for multi-head latent attention (MLA) decode, with one or
+ * several query tokens per sequence.
  *
  * TEST INFRASTRUCTURE ONLY.  Only the tests, the package's smoke check and the
  * benchmark's CPU-baseline leg may load this library.  It shares no code,
@@ -35,6 +36,16 @@
  *     bit, exponent 0 subnormal;
  *   - page tables: kv_indptr counts pages, the last page holds
  *     kv_last_page_len tokens (page_size 1: kv_indptr counts tokens).
+ *
+ * Multi-token decode (oracle_mla_decode_multi): sequence b has q_b query
+ * tokens, rows qo_indptr[b] .. qo_indptr[b+1]-1 of q and out.  Query token j is
+ * the token at position n_b - q_b + j of its sequence (the cache holds the
+ * rows of all its query tokens) and attends causally: every cache token gets
+ * a score, and the tokens after position n_b - q_b + j are masked out of the
+ * maximum and the sum.  The submissions pass qo_indptr = 0, 1, .., bs with a
+ * maximum query length of 1 to aiter (599694 "overhead elimination", its
+ * aiter path; 727205 "v25: LEAN", its metadata call); the causal placement of
+ * longer query runs is the plainest reading of that argument.
  *
  * The optional split mode computes, for a caller-given partition of each
  * sequence into token ranges, every range's exact (normalised output, lse) and
@@ -149,6 +160,7 @@ typedef struct {
     const int32_t* page_indices;
     const int32_t* last_page_len;
     int page_size;
+    const int32_t* qo_indptr;     /* optional [bs+1]: multi-token rows (see above) */
     const int32_t* split_indptr;  /* optional [bs+1] into split_bounds */
     const int32_t* split_bounds;  /* per split: end token (exclusive) within the sequence */
     double* out;                /* [bs, nh, v_dim] */
@@ -198,10 +210,46 @@ static double attend_range(const problem_t* p, int b, int h, const double* c,
     return m + log(Z);
 }
 
+/* Multi-token decode of sequence b: the causal definition written out. */
+static void solve_sequence_multi(const problem_t* p, int b, const double* c, double* z) {
+    int64_t n = seq_len(p, b), t;
+    int q = p->qo_indptr[b + 1] - p->qo_indptr[b], j, h, d;
+    for (j = 0; j < q; ++j) {
+        int64_t row = (int64_t)p->qo_indptr[b] + j;
+        int64_t pos = n - q + j; /* this query token's position */
+        for (h = 0; h < p->nh; ++h) {
+            const uint16_t* qh = p->q + (row * p->nh + h) * p->qk_dim;
+            double* o = p->out + (row * p->nh + h) * p->v_dim;
+            double m = -INFINITY, Z = 0.0;
+            for (t = 0; t < n; ++t) {
+                const double* ct = c + t * p->qk_dim;
+                double s = 0.0;
+                for (d = 0; d < p->qk_dim; ++d) s += oracle_bf16_to_f64(qh[d]) * ct[d];
+                z[t] = p->sm_scale * s;
+            }
+            for (t = 0; t < n; ++t)
+                if (t <= pos && z[t] > m) m = z[t]; /* causal mask */
+            for (d = 0; d < p->v_dim; ++d) o[d] = 0.0;
+            for (t = 0; t < n; ++t) {
+                const double* ct = c + t * p->qk_dim;
+                double w = t <= pos ? exp(z[t] - m) : 0.0; /* causal mask */
+                Z += w;
+                for (d = 0; d < p->v_dim; ++d) o[d] += w * ct[d];
+            }
+            for (d = 0; d < p->v_dim; ++d) o[d] /= Z;
+            if (p->lse) p->lse[row * p->nh + h] = m + log(Z);
+        }
+    }
+}
+
 static void solve_sequence(const problem_t* p, int b, double* cbuf, double* z, double* tmp) {
     int64_t n = seq_len(p, b), j;
     int h, d;
     for (j = 0; j < n; ++j) dequant_row(&p->cache, token_row(p, b, j), cbuf + j * p->qk_dim);
+    if (p->qo_indptr) {
+        solve_sequence_multi(p, b, cbuf, z);
+        return;
+    }
     for (h = 0; h < p->nh; ++h) {
         double* o = p->out + ((int64_t)b * p->nh + h) * p->v_dim;
         double lse;
@@ -274,18 +322,14 @@ static void* worker(void* arg) {
     return NULL;
 }
 
-/*
- * Full decode.  Returns 0 on success, nonzero on bad arguments or allocation
- * failure.  `batches` (optional, n_batches entries) restricts the work to the
- * listed sequences; the other rows of `out`/`lse` are left untouched.
- * `split_indptr`/`split_bounds` (optional) switch on split mode.
- */
-int oracle_mla_decode(const uint16_t* q, int bs, int nh, int qk_dim, int v_dim, double sm_scale,
-                      int fmt, const uint8_t* kv, double kv_scale, const uint8_t* scales,
-                      int64_t scale_stride, const int32_t* kv_indptr, const int32_t* page_indices,
-                      const int32_t* last_page_len, int page_size, const int32_t* split_indptr,
-                      const int32_t* split_bounds, const int32_t* batches, int n_batches,
-                      int nthreads, double* out, double* lse) {
+/* Full decode, single-token (qo_indptr NULL) or multi-token; see the two
+ * exported entry points below. */
+static int decode(const uint16_t* q, int bs, int nh, int qk_dim, int v_dim, double sm_scale, int fmt,
+                  const uint8_t* kv, double kv_scale, const uint8_t* scales, int64_t scale_stride,
+                  const int32_t* kv_indptr, const int32_t* page_indices, const int32_t* last_page_len,
+                  int page_size, const int32_t* qo_indptr, const int32_t* split_indptr,
+                  const int32_t* split_bounds, const int32_t* batches, int n_batches, int nthreads,
+                  double* out, double* lse) {
     problem_t p;
     pool_t pool;
     pthread_t* th;
@@ -301,6 +345,8 @@ int oracle_mla_decode(const uint16_t* q, int bs, int nh, int qk_dim, int v_dim, 
     p.cache.scale_stride = scale_stride; p.cache.kv_scale = kv_scale;
     p.kv_indptr = kv_indptr; p.page_indices = page_indices; p.last_page_len = last_page_len;
     p.page_size = page_size; p.split_indptr = split_indptr; p.split_bounds = split_bounds;
+    p.qo_indptr = qo_indptr;
+    if (qo_indptr && split_indptr) return 1;
     p.out = out; p.lse = lse;
 
     if (!batches) {
@@ -317,6 +363,10 @@ int oracle_mla_decode(const uint16_t* q, int bs, int nh, int qk_dim, int v_dim, 
         if (batches[i] < 0 || batches[i] >= bs) { free(all); return 1; }
         n = seq_len(&p, batches[i]);
         if (n < 0) { free(all); return 1; }
+        if (qo_indptr) {
+            int qn = qo_indptr[batches[i] + 1] - qo_indptr[batches[i]];
+            if (qn < 0 || qn > n) { free(all); return 1; }
+        }
         if (n > pool.max_len) pool.max_len = n;
     }
     pthread_mutex_init(&pool.mu, NULL);
@@ -330,4 +380,37 @@ int oracle_mla_decode(const uint16_t* q, int bs, int nh, int qk_dim, int v_dim, 
     free(th);
     free(all);
     return pool.failed ? 2 : 0;
+}
+
+/*
+ * Single-token decode: row b of q and out is sequence b.  Returns 0 on
+ * success, nonzero on bad arguments or allocation failure.  `batches`
+ * (optional, n_batches entries) restricts the work to the listed sequences;
+ * the other rows of `out`/`lse` are left untouched.  `split_indptr` /
+ * `split_bounds` (optional) switch on split mode.
+ */
+int oracle_mla_decode(const uint16_t* q, int bs, int nh, int qk_dim, int v_dim, double sm_scale,
+                      int fmt, const uint8_t* kv, double kv_scale, const uint8_t* scales,
+                      int64_t scale_stride, const int32_t* kv_indptr, const int32_t* page_indices,
+                      const int32_t* last_page_len, int page_size, const int32_t* split_indptr,
+                      const int32_t* split_bounds, const int32_t* batches, int n_batches,
+                      int nthreads, double* out, double* lse) {
+    return decode(q, bs, nh, qk_dim, v_dim, sm_scale, fmt, kv, kv_scale, scales, scale_stride, kv_indptr,
+                  page_indices, last_page_len, page_size, NULL, split_indptr, split_bounds, batches, n_batches,
+                  nthreads, out, lse);
+}
+
+/*
+ * Multi-token decode (see the header): q and out have qo_indptr[bs] rows;
+ * `batches` lists sequences, all of whose rows are computed.  No split mode.
+ */
+int oracle_mla_decode_multi(const uint16_t* q, int bs, int nh, int qk_dim, int v_dim, double sm_scale,
+                            int fmt, const uint8_t* kv, double kv_scale, const uint8_t* scales,
+                            int64_t scale_stride, const int32_t* kv_indptr, const int32_t* page_indices,
+                            const int32_t* last_page_len, int page_size, const int32_t* qo_indptr,
+                            const int32_t* batches, int n_batches, int nthreads, double* out, double* lse) {
+    if (!qo_indptr || qo_indptr[0] != 0) return 1;
+    return decode(q, bs, nh, qk_dim, v_dim, sm_scale, fmt, kv, kv_scale, scales, scale_stride, kv_indptr,
+                  page_indices, last_page_len, page_size, qo_indptr, NULL, NULL, batches, n_batches, nthreads,
+                  out, lse);
 }

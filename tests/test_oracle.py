@@ -118,6 +118,34 @@ def _brute_force(case):
     return torch.stack(outs).numpy(), torch.stack(lses).numpy()
 
 
+def _brute_force_multi(case):
+    """Multi-token decode: softmax(q k^T / sqrt(576) + mask) v in torch float64,
+    with the bottom-right aligned causal mask (query token j of a sequence of n
+    tokens with q query tokens is position n - q + j): entries above diagonal
+    n - q + 1 of the [q, n] score matrix are masked."""
+    q_all = torch.from_numpy(case.q_bits.view(np.int16)).view(torch.bfloat16).to(torch.float64)
+    seqs = _dequant_independent(case)
+    outs, lses = [], []
+    for b, c in enumerate(seqs):
+        r0, r1 = int(case.qo_indptr[b]), int(case.qo_indptr[b + 1])
+        kv = torch.from_numpy(c)
+        n, nq = kv.shape[0], r1 - r0
+        z = torch.einsum("jhd,td->jht", q_all[r0:r1], kv) / np.sqrt(576.0)
+        masked = torch.ones(nq, n, dtype=torch.bool).triu(n - nq + 1)
+        z = z.masked_fill(masked[:, None, :], -np.inf)
+        outs.append(torch.softmax(z, dim=-1) @ kv[:, :512])
+        lses.append(torch.logsumexp(z, dim=-1))
+    return torch.cat(outs).numpy(), torch.cat(lses).numpy()
+
+
+TINY_MULTI = [
+    # fmt, lens, q_lens, page_size, shuffle
+    ("bf16", [1, 4, 9], [1, 4, 3], 1, False),
+    ("fp8", [17, 6, 2], [2, 0, 2], 2, True),
+    ("mxfp4", [33, 5, 40], [5, 1, 7], 4, True),
+]
+
+
 TINY = [
     ("bf16", [1, 2, 3], 1, False),
     ("fp8", [15, 16, 17], 1, False),
@@ -139,6 +167,56 @@ def test_oracle_matches_brute_force(oracle_mod, fmt, lens, ps, shuffle):
     fin = np.isfinite(ref_lse)
     np.testing.assert_allclose(lse[fin], ref_lse[fin], rtol=1e-12, atol=1e-12)
     assert np.all(np.isneginf(lse[~fin]))
+
+
+@pytest.mark.parametrize("fmt,lens,qls,ps,shuffle", TINY_MULTI)
+def test_multi_token_matches_brute_force(oracle_mod, fmt, lens, qls, ps, shuffle):
+    case = synth.make_case(fmt, lens, seed=9 + ps, page_size=ps, shuffle_pages=shuffle, guard_rows=2,
+                           q_lens=qls)
+    out, lse = oracle_mod.decode_case(case)
+    ref, ref_lse = _brute_force_multi(case)
+    assert out.shape[0] == sum(qls) and np.all(np.isfinite(out))
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse, ref_lse, rtol=1e-12, atol=1e-12)
+
+
+def test_multi_token_closed_forms(oracle_mod):
+    """A sequence whose cache holds only its query tokens: the first returns V
+    row 0 exactly; with a zero query, token j returns the mean of V rows
+    0..n - q + j."""
+    lens, qls = [3, 6], [3, 4]
+    case = synth.make_case("fp8", lens, seed=12, q_lens=qls)
+    out, _ = oracle_mod.decode_case(case)
+    v0 = oracle_mod.dequant_rows("fp8", case.kv, [0], kv_scale=case.kv_scale)[0, :512]
+    np.testing.assert_array_equal(out[0], np.broadcast_to(v0, (16, 512)))
+    zq = synth.make_case("fp8", lens, seed=12, q_lens=qls, q_values=np.zeros((sum(qls), 16, 576), np.float32))
+    out, _ = oracle_mod.decode_case(zq)
+    for b in range(2):
+        v = oracle_mod.dequant_rows("fp8", zq.kv, zq.token_rows(b), kv_scale=zq.kv_scale)[:, :512]
+        for j in range(qls[b]):
+            pos = lens[b] - qls[b] + j
+            np.testing.assert_allclose(out[zq.qo_indptr[b] + j], np.broadcast_to(v[:pos + 1].mean(0), (16, 512)),
+                                       rtol=1e-13, atol=1e-15)
+
+
+def test_multi_token_reduces_to_single_token(oracle_mod):
+    """One query token per sequence is single-token decode, bit for bit; the
+    last query token of a sequence sees the whole sequence, and the first the
+    sequence without the other query tokens' rows."""
+    lens = [40, 7, 19]
+    one = synth.make_case("mxfp4", lens, seed=13, q_lens=[1, 1, 1])
+    single = synth.make_case("mxfp4", lens, seed=13)
+    assert np.array_equal(one.q_bits, single.q_bits)
+    np.testing.assert_array_equal(oracle_mod.decode_case(one)[0], oracle_mod.decode_case(single)[0])
+    qls = [3, 2, 5]
+    case = synth.make_case("bf16", lens, seed=14, q_lens=qls)
+    out, _ = oracle_mod.decode_case(case)
+    for b in range(3):
+        for j, n in ((qls[b] - 1, lens[b]), (0, lens[b] - qls[b] + 1)):
+            r = int(case.qo_indptr[b]) + j
+            ip = np.array([0, n], dtype=np.int32)
+            ref, _ = oracle_mod.mla_decode(case.q_bits[r:r + 1], "bf16", case.kv[case.kv_indptr[b]:], ip)
+            np.testing.assert_allclose(out[r], ref[0], rtol=1e-13, atol=1e-15)
 
 
 def test_dequant_rows_matches_independent_decode(oracle_mod):
@@ -245,6 +323,11 @@ MUTANTS = {
                           "for (d = 0; d < p->v_dim; ++d) s += oracle_bf16_to_f64(qh[d]) * ct[d];"),
     "scale not applied": ("z[t] = p->sm_scale * s;", "z[t] = s;"),
     "normaliser off": ("for (d = 0; d < p->v_dim; ++d) o[d] /= Z;", "for (d = 0; d < p->v_dim; ++d) o[d] /= (Z + 1.0);"),
+    # multi-token causal mask
+    "causal mask off by one": ("t <= pos", "t < pos"),
+    "causal mask from the start": ("int64_t pos = n - q + j;", "int64_t pos = j;"),
+    "query rows reversed": ("int64_t row = (int64_t)p->qo_indptr[b] + j;",
+                            "int64_t row = (int64_t)p->qo_indptr[b] + (q - 1 - j);"),
     "V from the rope end": ("o[d] += w * ct[d];", "o[d] += w * ct[d + (p->qk_dim - p->v_dim)];"),
     # layout
     "page index wrong": ("p->page_indices[(int64_t)p->kv_indptr[b] + j / p->page_size]",
@@ -265,6 +348,12 @@ def _pins_pass(lib) -> bool:
                                    shuffle_pages=shuffle, guard_rows=3)
             out, _ = lib.decode_case(case)
             ref, _ = _brute_force(case)
+            np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+        for fmt, lens, qls, ps, shuffle in TINY_MULTI:
+            case = synth.make_case(fmt, lens, seed=9 + ps, page_size=ps, shuffle_pages=shuffle, guard_rows=2,
+                                   q_lens=qls)
+            out, _ = lib.decode_case(case)
+            ref, _ = _brute_force_multi(case)
             np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
         case = synth.make_case("fp8", [100, 64, 3], seed=15, page_size=2, shuffle_pages=True)
         full, _ = lib.decode_case(case)
