@@ -134,12 +134,12 @@ def main():
         return
 
     name = args.workload
-    kv_dtype, batch, kv_len, ps, shuffled, seed = synth.CONFIGS[name]
+    kv_dtype, batch, kv_len, ps, shuffled, seed = synth.CONFIGS[name][:6]
     print(f"[bench] generating {name}", file=sys.stderr, flush=True)
     case = synth.config_case(name)
     base = binding.case_to_device(case, dev)
-    out = torch.empty((case.batch, 16, 512), dtype=torch.bfloat16, device=dev)
-    alg_bytes = case.kv_algorithmic_bytes()
+    out = torch.empty((case.rows, 16, 512), dtype=torch.bfloat16, device=dev)
+    alg_bytes = case.kv_algorithmic_bytes()  # the cache once, whatever the query tokens per sequence
 
     # Cold-cache protocol: consecutive calls read different copies of the
     # inputs (same bytes, other addresses), cycling through at least 1 GiB, so
@@ -152,7 +152,7 @@ def main():
 
     dec = binding.MlaDecode(kv_dtype, ps, device=0)
     t0 = time.perf_counter()
-    ws_bytes = dec.plan(case.kv_indptr, case.kv_last_page_len, args.split)
+    ws_bytes = dec.plan(case.kv_indptr, case.kv_last_page_len, args.split, case.qo_indptr)
     plan_us = (time.perf_counter() - t0) * 1e6
     n_items, max_splits, n_partials = binding.mla_decode_plan_info(dec.h)
     res1 = binding.mla_decode_kernel_resources(dec.h, 0)
@@ -231,6 +231,7 @@ def main():
                   "mxfp4": "mxfp4 (MX MFMA: e2m1 scores, e4m3 values, fp32 acc)"}[kv_dtype],
         "data": "synthetic",
         "config": {"workload": name, "kv_dtype": kv_dtype, "batch": int(case.batch),
+                   "query_rows": int(case.rows),
                    "kv_len": kv_len if isinstance(kv_len, int) else list(kv_len),
                    "total_tokens": int(case.total_tokens), "page_size": ps,
                    "algorithmic_kv_bytes": int(alg_bytes)},

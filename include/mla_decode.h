@@ -148,6 +148,39 @@ mla_status mla_decode_plan_preview(int batch, const int32_t* kv_indptr_host,
                                    int* num_items, int* num_slots, size_t* workspace_bytes);
 
 /*
+ * Multi-token decode: a plan for several query tokens per sequence (draft
+ * tokens being verified, or a chunk of new tokens).  The submissions call
+ * aiter's decode with one query token per sequence (qo_indptr = 0, 1, ..,
+ * batch and a maximum query length of 1: 599694 "overhead elimination", its
+ * aiter path; 727205 "v25: LEAN", its metadata call); this takes the same
+ * qo_indptr argument with longer query runs.
+ *   qo_indptr_host  int32 [batch+1], qo_indptr[0] = 0, non-decreasing; sequence
+ *                   b has q_b = qo_indptr[b+1] - qo_indptr[b] query tokens,
+ *                   0 <= q_b <= its cache length n_b, at least one in all.
+ * Query token j of sequence b is row r = qo_indptr[b] + j of q
+ * [qo_indptr[batch], 16, 576] and of out [qo_indptr[batch], 16, 512].  It is
+ * the token at position n_b - q_b + j of its sequence, whose cache already
+ * holds the rows of all its query tokens, and it attends causally: to cache
+ * tokens 0 .. n_b - q_b + j.  A sequence with q_b = 0 produces no row.  The
+ * other arguments, the run call and the errors are those of mla_decode_plan;
+ * with q_b = 1 everywhere the plan is the single-token plan.  Each row's
+ * cache range is read by its own items; the copies for the q_b rows of a
+ * sequence are launched together so that they stream the same rows at the
+ * same time.
+ */
+mla_status mla_decode_plan_multi(mla_decode_t h, int batch, const int32_t* qo_indptr_host,
+                                 const int32_t* kv_indptr_host, const int32_t* kv_last_page_len_host,
+                                 int split_override, size_t* workspace_bytes);
+
+/* mla_decode_plan_preview for a multi-token plan (see mla_decode_plan_multi);
+ * the first column of an item row is the query row. */
+mla_status mla_decode_plan_preview_multi(int batch, const int32_t* qo_indptr_host, const int32_t* kv_indptr_host,
+                                         const int32_t* kv_last_page_len_host, int page_size,
+                                         mla_kv_dtype kv_dtype, int split_override, int num_cus,
+                                         int blocks_per_cu, int32_t* items_out, int max_items,
+                                         int* num_items, int* num_slots, size_t* workspace_bytes);
+
+/*
  * Describe the current plan: number of work items (workgroups launched,
  * unless the plan has bins: see mla_decode_plan_preview), the largest number
  * of items given to one sequence, and the number of partials written to the

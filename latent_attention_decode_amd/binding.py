@@ -44,6 +44,12 @@ _lib.mla_decode_plan_preview.argtypes = [ctypes.c_int, _P, _P, ctypes.c_int, cty
                                          ctypes.c_int, ctypes.c_int, _P, ctypes.c_int,
                                          ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
                                          ctypes.POINTER(ctypes.c_size_t)]
+_lib.mla_decode_plan_multi.argtypes = [_H, ctypes.c_int, _P, _P, _P, ctypes.c_int,
+                                       ctypes.POINTER(ctypes.c_size_t)]
+_lib.mla_decode_plan_preview_multi.argtypes = [ctypes.c_int, _P, _P, _P, ctypes.c_int, ctypes.c_int,
+                                               ctypes.c_int, ctypes.c_int, ctypes.c_int, _P, ctypes.c_int,
+                                               ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
+                                               ctypes.POINTER(ctypes.c_size_t)]
 _lib.mla_decode_plan_info.argtypes = [_H, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
                                       ctypes.POINTER(ctypes.c_int)]
 _lib.mla_decode_run.argtypes = [_H, _P, _P, _P, ctypes.c_int64, _P, _P, _P, _P, _P,
@@ -55,13 +61,15 @@ _lib.mla_decode_kernel_resources.argtypes = [_H, ctypes.c_int, ctypes.POINTER(ct
 _lib.mla_decode_destroy.argtypes = [_H]
 _lib.mla_decode_last_error.argtypes = [_H]
 _lib.mla_decode_last_error.restype = ctypes.c_char_p
-for _name in ("mla_decode_create", "mla_decode_plan", "mla_decode_plan_preview",
+for _name in ("mla_decode_create", "mla_decode_plan", "mla_decode_plan_preview", "mla_decode_plan_multi",
+              "mla_decode_plan_preview_multi",
               "mla_decode_plan_info", "mla_decode_run", "mla_decode_set_profiling",
               "mla_decode_kernel_time_ms", "mla_decode_kernel_resources", "mla_decode_destroy"):
     getattr(_lib, _name).restype = ctypes.c_int
 
 EXPORTED = ("mla_decode_version", "mla_status_string", "mla_decode_create", "mla_decode_plan",
-            "mla_decode_plan_preview", "mla_decode_plan_info", "mla_decode_run",
+            "mla_decode_plan_preview", "mla_decode_plan_multi", "mla_decode_plan_preview_multi",
+            "mla_decode_plan_info", "mla_decode_run",
             "mla_decode_set_profiling", "mla_decode_kernel_time_ms", "mla_decode_kernel_resources",
             "mla_decode_destroy", "mla_decode_last_error")
 
@@ -126,25 +134,49 @@ def mla_decode_plan(h, kv_indptr_host, kv_last_page_len_host=None, split_overrid
     return ws.value
 
 
-def mla_decode_plan_preview(kv_indptr_host, kv_last_page_len_host=None, page_size: int = 1,
-                            split_override: int = 0, num_cus: int = 256, blocks_per_cu: int = 2,
-                            kv_dtype: str = "fp8"):
-    """Host-only planner.  Returns (items int32 [n, 5], num_slots, workspace_bytes); an item
-    row is (sequence, first token, end token, slot, workgroup)."""
+def mla_decode_plan_multi(h, qo_indptr_host, kv_indptr_host, kv_last_page_len_host=None,
+                          split_override: int = 0) -> int:
+    """Plans a multi-token batch (query tokens per sequence from qo_indptr); returns the
+    workspace size in bytes."""
+    qo = _host_i32(qo_indptr_host)
     ip = _host_i32(kv_indptr_host)
     lp = None if kv_last_page_len_host is None else _host_i32(kv_last_page_len_host)
+    if qo.size != ip.size:
+        raise ValueError("qo_indptr and kv_indptr must have the same length")
+    ws = ctypes.c_size_t()
+    st = _lib.mla_decode_plan_multi(h, ip.size - 1, qo.ctypes.data, ip.ctypes.data,
+                                    None if lp is None else lp.ctypes.data, int(split_override), ctypes.byref(ws))
+    _check(st, "mla_decode_plan_multi", h)
+    return ws.value
+
+
+def mla_decode_plan_preview(kv_indptr_host, kv_last_page_len_host=None, page_size: int = 1,
+                            split_override: int = 0, num_cus: int = 256, blocks_per_cu: int = 2,
+                            kv_dtype: str = "fp8", qo_indptr_host=None):
+    """Host-only planner.  Returns (items int32 [n, 5], num_slots, workspace_bytes); an item
+    row is (query row, first token, end token, slot, workgroup).  With qo_indptr_host, the
+    multi-token planner (query rows per sequence from qo_indptr)."""
+    ip = _host_i32(kv_indptr_host)
+    lp = None if kv_last_page_len_host is None else _host_i32(kv_last_page_len_host)
+    qo = None if qo_indptr_host is None else _host_i32(qo_indptr_host)
     n = ctypes.c_int()
     slots = ctypes.c_int()
     ws = ctypes.c_size_t()
-    args = (ip.size - 1, ip.ctypes.data, None if lp is None else lp.ctypes.data, int(page_size),
-            KV_DTYPES[kv_dtype], int(split_override), int(num_cus), int(blocks_per_cu))
-    st = _lib.mla_decode_plan_preview(*args, None, 0, ctypes.byref(n), ctypes.byref(slots),
-                                      ctypes.byref(ws))
+    rest = (None if lp is None else lp.ctypes.data, int(page_size), KV_DTYPES[kv_dtype], int(split_override),
+            int(num_cus), int(blocks_per_cu))
+
+    def call(items_ptr, cap):
+        if qo is None:
+            return _lib.mla_decode_plan_preview(ip.size - 1, ip.ctypes.data, *rest, items_ptr, cap, ctypes.byref(n),
+                                                ctypes.byref(slots), ctypes.byref(ws))
+        return _lib.mla_decode_plan_preview_multi(ip.size - 1, qo.ctypes.data, ip.ctypes.data, *rest, items_ptr,
+                                                  cap, ctypes.byref(n), ctypes.byref(slots), ctypes.byref(ws))
+
+    st = call(None, 0)
     if st != 0 and n.value == 0:
         _check(st, "mla_decode_plan_preview")
     items = np.zeros((max(n.value, 1), 5), dtype=np.int32)
-    st = _lib.mla_decode_plan_preview(*args, items.ctypes.data, n.value, ctypes.byref(n),
-                                      ctypes.byref(slots), ctypes.byref(ws))
+    st = call(items.ctypes.data, n.value)
     _check(st, "mla_decode_plan_preview")
     return items[:n.value], slots.value, ws.value
 
@@ -212,8 +244,13 @@ class MlaDecode:
         self.h = mla_decode_create(self.device, kv_dtype, page_size, sm_scale=sm_scale)
         self.workspace: Optional[torch.Tensor] = None
 
-    def plan(self, kv_indptr_host, kv_last_page_len_host=None, split_override: int = 0) -> int:
-        nbytes = mla_decode_plan(self.h, kv_indptr_host, kv_last_page_len_host, split_override)
+    def plan(self, kv_indptr_host, kv_last_page_len_host=None, split_override: int = 0,
+             qo_indptr_host=None) -> int:
+        if qo_indptr_host is None:
+            nbytes = mla_decode_plan(self.h, kv_indptr_host, kv_last_page_len_host, split_override)
+        else:
+            nbytes = mla_decode_plan_multi(self.h, qo_indptr_host, kv_indptr_host, kv_last_page_len_host,
+                                           split_override)
         if nbytes and (self.workspace is None or self.workspace.numel() * 4 < nbytes):
             self.workspace = torch.empty((nbytes + 3) // 4, dtype=torch.float32,
                                          device=f"cuda:{self.device}")

@@ -53,7 +53,7 @@ struct mla_decode_s {
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 2 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 3 * 100 + 0;
 
 mla_status fail(mla_decode_t h, mla_status st, const char* fmt, ...) {
   if (h) {
@@ -121,6 +121,35 @@ static bool seq_lengths(const int32_t* indptr, const int32_t* last, int batch, i
       *err = "sequence too long";
       return false;
     }
+  }
+  return true;
+}
+
+// Query tokens per sequence from qo_indptr (multi-token decode): at least
+// none, at most the sequence's length (its query tokens' own rows are in the
+// cache), at least one in all.
+static bool query_counts(const int32_t* qo_indptr, int batch, const std::vector<int64_t>& lens,
+                         std::vector<int32_t>* q, std::string* err) {
+  if (qo_indptr[0] != 0) {
+    *err = "qo_indptr[0] must be 0";
+    return false;
+  }
+  q->resize(batch);
+  for (int b = 0; b < batch; ++b) {
+    const int64_t n = static_cast<int64_t>(qo_indptr[b + 1]) - qo_indptr[b];
+    if (n < 0) {
+      *err = "qo_indptr is not non-decreasing at sequence " + std::to_string(b);
+      return false;
+    }
+    if (n > lens[b]) {
+      *err = "sequence " + std::to_string(b) + " has more query tokens than cache tokens";
+      return false;
+    }
+    (*q)[b] = static_cast<int32_t>(n);
+  }
+  if (qo_indptr[batch] < 1) {
+    *err = "no query tokens";
+    return false;
   }
   return true;
 }
@@ -403,6 +432,89 @@ static void plan_items(const std::vector<int64_t>& lens, const int32_t* indptr, 
   out->uniform_len = len;
 }
 
+// Multi-token decode.  Query token j of sequence b (row qo_indptr[b] + j)
+// sits at position n_b - q_b + j and attends to tokens 0 .. n_b - q_b + j.
+// The sequences are planned as for single-token decode on 1 / max_b q_b of
+// the workgroup slots, and every item becomes q_b items, one per query
+// token, over the same tokens clipped to that token's causal end.  The q_b
+// copies of an item are listed together (with bins: parent bin k becomes
+// bins q k .. q k + q - 1, q = max_b q_b), so workgroups launched together
+// stream the same cache rows at about the same pace and all but the first
+// find them in the memory-side cache.
+static void plan_multi(const std::vector<int64_t>& lens, const std::vector<int32_t>& qlen,
+                       const int32_t* qo_indptr, const int32_t* indptr, int split_override, int num_cus,
+                       int blocks_per_cu, int page_size, int64_t tile, int64_t max_pages, bool binned,
+                       PlanOut* out) {
+  const int batch = static_cast<int>(lens.size());
+  int qmax = 0;
+  bool single = true;
+  for (int b = 0; b < batch; ++b) {
+    qmax = std::max(qmax, qlen[b]);
+    single = single && qlen[b] == 1;
+  }
+  if (single) {  // one query token per sequence: rows are sequences
+    plan_items(lens, indptr, split_override, num_cus, blocks_per_cu, page_size, tile, max_pages, binned, out);
+    return;
+  }
+  std::vector<int64_t> plens(batch);
+  for (int b = 0; b < batch; ++b) plens[b] = qlen[b] ? lens[b] : 0;
+  const int64_t slots = static_cast<int64_t>(num_cus) * std::max(blocks_per_cu, 1);
+  PlanOut par;
+  plan_items(plens, indptr, split_override, static_cast<int>(std::max<int64_t>(1, slots / qmax)), 1, page_size,
+             tile, max_pages, binned, &par);
+
+  out->items.clear();
+  out->merge.clear();
+  out->bins.clear();
+  out->num_slots = 0;
+  out->max_splits = 0;
+  out->uniform_splits = out->uniform_chunk = out->uniform_len = 0;
+  const bool by_bin = !par.bins.empty();
+  const size_t groups = by_bin ? par.bins.size() - 1 : par.items.size();
+  for (size_t k = 0; k < groups; ++k) {
+    const size_t i0 = by_bin ? static_cast<size_t>(par.bins[k]) : k;
+    const size_t i1 = by_bin ? static_cast<size_t>(par.bins[k + 1]) : k + 1;
+    for (int j = 0; j < qmax; ++j) {
+      if (by_bin) out->bins.push_back(static_cast<int32_t>(out->items.size()));
+      for (size_t i = i0; i < i1; ++i) {
+        const WorkItem& it = par.items[i];
+        if (it.slot == WorkItem::kEmpty) continue;  // a sequence without query tokens
+        const int b = it.batch;
+        if (j >= qlen[b]) continue;
+        const int64_t end = lens[b] - qlen[b] + j + 1;  // this token's causal end
+        const int32_t t1 = static_cast<int32_t>(std::min<int64_t>(it.tok_end, end));
+        if (it.tok_begin >= t1) continue;
+        out->items.push_back(WorkItem{qo_indptr[b] + j, it.tok_begin, t1, 0, indptr[b], -1, 0, 0});
+      }
+    }
+  }
+  if (by_bin) out->bins.push_back(static_cast<int32_t>(out->items.size()));
+
+  // slots and merge jobs per row, its items in list order
+  const int rows = qo_indptr[batch];
+  std::vector<int32_t> npieces(rows, 0), first(rows, 0), job(rows, -1), seen(rows, 0);
+  for (const WorkItem& it : out->items) ++npieces[it.batch];
+  for (int r = 0; r < rows; ++r) {
+    out->max_splits = std::max(out->max_splits, static_cast<int>(npieces[r]));
+    if (npieces[r] < 2) continue;
+    job[r] = static_cast<int32_t>(out->merge.size());
+    first[r] = out->num_slots;
+    out->merge.push_back(MergeSeq{r, out->num_slots, npieces[r], 0});
+    out->num_slots += npieces[r];
+  }
+  for (WorkItem& it : out->items) {
+    const int r = it.batch;
+    if (npieces[r] == 1) {
+      it.slot = WorkItem::kWhole;
+      continue;
+    }
+    it.slot = first[r] + seen[r]++;
+    it.merge_job = job[r];
+    it.slot_begin = first[r];
+    it.nslots = npieces[r];
+  }
+}
+
 }  // namespace mla
 
 extern "C" {
@@ -443,9 +555,10 @@ mla_status mla_decode_create(mla_decode_t* out, int device, int num_heads, int q
   return MLA_OK;
 }
 
-mla_status mla_decode_plan(mla_decode_t h, int batch, const int32_t* kv_indptr_host,
-                           const int32_t* kv_last_page_len_host, int split_override,
-                           size_t* workspace_bytes) {
+namespace {
+
+mla_status plan_impl(mla_decode_t h, int batch, const int32_t* qo_indptr_host, const int32_t* kv_indptr_host,
+                     const int32_t* kv_last_page_len_host, int split_override, size_t* workspace_bytes) {
   if (!h) return MLA_ERR_INVALID_ARG;
   h->last_error.clear();
   if (batch < 1) return fail(h, MLA_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", batch);
@@ -458,6 +571,15 @@ mla_status mla_decode_plan(mla_decode_t h, int batch, const int32_t* kv_indptr_h
   std::string err;
   if (!mla::seq_lengths(kv_indptr_host, kv_last_page_len_host, batch, h->page_size, &lens, &err))
     return fail(h, MLA_ERR_INVALID_ARG, "%s", err.c_str());
+  std::vector<int32_t> qlen(batch, 1), qo_unit;
+  if (qo_indptr_host) {
+    if (!mla::query_counts(qo_indptr_host, batch, lens, &qlen, &err))
+      return fail(h, MLA_ERR_INVALID_ARG, "%s", err.c_str());
+  } else {
+    qo_unit.resize(batch + 1);
+    for (int b = 0; b <= batch; ++b) qo_unit[b] = b;
+    qo_indptr_host = qo_unit.data();
+  }
 
   h->planned = false;
   DeviceGuard guard(h->device);
@@ -474,8 +596,9 @@ mla_status mla_decode_plan(mla_decode_t h, int batch, const int32_t* kv_indptr_h
   }
 
   mla::PlanOut plan;
-  mla::plan_items(lens, kv_indptr_host, split_override, h->num_cus, h->blocks_per_cu, h->page_size,
-                  mla::plan_tile(h->kv_dtype), mla::item_pages(h->kv_dtype), mla::plan_binned(h->kv_dtype), &plan);
+  mla::plan_multi(lens, qlen, qo_indptr_host, kv_indptr_host, split_override, h->num_cus, h->blocks_per_cu,
+                  h->page_size, mla::plan_tile(h->kv_dtype), mla::item_pages(h->kv_dtype),
+                  mla::plan_binned(h->kv_dtype), &plan);
 
   const size_t items_bytes = plan.items.size() * sizeof(mla::WorkItem);
   const size_t merge_bytes = plan.merge.size() * sizeof(mla::MergeSeq);
@@ -499,7 +622,7 @@ mla_status mla_decode_plan(mla_decode_t h, int batch, const int32_t* kv_indptr_h
   if (hipMemcpy(h->dev_plan, blob.data(), need, hipMemcpyHostToDevice) != hipSuccess)
     return fail(h, MLA_ERR_HIP, "uploading the work list failed");
 
-  h->batch = batch;
+  h->batch = qo_indptr_host[batch];  // output rows
   h->num_items = static_cast<int>(plan.items.size());
   h->num_bins = plan.bins.empty() ? 0 : static_cast<int>(plan.bins.size()) - 1;
   h->num_slots = plan.num_slots;
@@ -516,18 +639,17 @@ mla_status mla_decode_plan(mla_decode_t h, int batch, const int32_t* kv_indptr_h
   h->uniform_len = plan.uniform_len;
   h->uniform_base = kv_indptr_host[0];
   h->total_tokens = 0;
-  for (int64_t n : lens) h->total_tokens += n;
+  for (const mla::WorkItem& it : plan.items) h->total_tokens += it.tok_end - it.tok_begin;
   h->workspace_bytes = static_cast<size_t>(plan.num_slots) * slot_bytes();
   h->planned = true;
   *workspace_bytes = h->workspace_bytes;
   return MLA_OK;
 }
 
-mla_status mla_decode_plan_preview(int batch, const int32_t* kv_indptr_host,
-                                   const int32_t* kv_last_page_len_host, int page_size,
-                                   mla_kv_dtype kv_dtype, int split_override, int num_cus,
-                                   int blocks_per_cu, int32_t* items_out, int max_items,
-                                   int* num_items, int* num_slots, size_t* workspace_bytes) {
+mla_status preview_impl(int batch, const int32_t* qo_indptr_host, const int32_t* kv_indptr_host,
+                        const int32_t* kv_last_page_len_host, int page_size, mla_kv_dtype kv_dtype,
+                        int split_override, int num_cus, int blocks_per_cu, int32_t* items_out, int max_items,
+                        int* num_items, int* num_slots, size_t* workspace_bytes) {
   if (batch < 1 || !kv_indptr_host || page_size < 1 || !is_pow2(page_size) || split_override < 0 ||
       num_cus < 1 || blocks_per_cu < 1 || max_items < 0 || (max_items > 0 && !items_out) ||
       (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3 && kv_dtype != MLA_KV_MXFP4))
@@ -537,8 +659,16 @@ mla_status mla_decode_plan_preview(int batch, const int32_t* kv_indptr_host,
   std::string err;
   if (!mla::seq_lengths(kv_indptr_host, kv_last_page_len_host, batch, page_size, &lens, &err))
     return MLA_ERR_INVALID_ARG;
+  std::vector<int32_t> qlen(batch, 1), qo_unit;
+  if (qo_indptr_host) {
+    if (!mla::query_counts(qo_indptr_host, batch, lens, &qlen, &err)) return MLA_ERR_INVALID_ARG;
+  } else {
+    qo_unit.resize(batch + 1);
+    for (int b = 0; b <= batch; ++b) qo_unit[b] = b;
+    qo_indptr_host = qo_unit.data();
+  }
   mla::PlanOut plan;
-  mla::plan_items(lens, kv_indptr_host, split_override, num_cus, blocks_per_cu, page_size,
+  mla::plan_multi(lens, qlen, qo_indptr_host, kv_indptr_host, split_override, num_cus, blocks_per_cu, page_size,
                   mla::plan_tile(kv_dtype), mla::item_pages(kv_dtype), mla::plan_binned(kv_dtype), &plan);
   const int n = static_cast<int>(plan.items.size());
   if (num_items) *num_items = n;
@@ -555,6 +685,43 @@ mla_status mla_decode_plan_preview(int batch, const int32_t* kv_indptr_host,
     items_out[5 * i + 4] = plan.bins.empty() ? i : bin;
   }
   return MLA_OK;
+}
+
+}  // namespace
+
+mla_status mla_decode_plan(mla_decode_t h, int batch, const int32_t* kv_indptr_host,
+                           const int32_t* kv_last_page_len_host, int split_override,
+                           size_t* workspace_bytes) {
+  return plan_impl(h, batch, nullptr, kv_indptr_host, kv_last_page_len_host, split_override, workspace_bytes);
+}
+
+mla_status mla_decode_plan_multi(mla_decode_t h, int batch, const int32_t* qo_indptr_host,
+                                 const int32_t* kv_indptr_host, const int32_t* kv_last_page_len_host,
+                                 int split_override, size_t* workspace_bytes) {
+  if (!h) return MLA_ERR_INVALID_ARG;
+  if (!qo_indptr_host) return fail(h, MLA_ERR_INVALID_ARG, "qo_indptr_host is NULL");
+  return plan_impl(h, batch, qo_indptr_host, kv_indptr_host, kv_last_page_len_host, split_override,
+                   workspace_bytes);
+}
+
+mla_status mla_decode_plan_preview(int batch, const int32_t* kv_indptr_host,
+                                   const int32_t* kv_last_page_len_host, int page_size,
+                                   mla_kv_dtype kv_dtype, int split_override, int num_cus,
+                                   int blocks_per_cu, int32_t* items_out, int max_items,
+                                   int* num_items, int* num_slots, size_t* workspace_bytes) {
+  return preview_impl(batch, nullptr, kv_indptr_host, kv_last_page_len_host, page_size, kv_dtype, split_override,
+                      num_cus, blocks_per_cu, items_out, max_items, num_items, num_slots, workspace_bytes);
+}
+
+mla_status mla_decode_plan_preview_multi(int batch, const int32_t* qo_indptr_host, const int32_t* kv_indptr_host,
+                                         const int32_t* kv_last_page_len_host, int page_size,
+                                         mla_kv_dtype kv_dtype, int split_override, int num_cus,
+                                         int blocks_per_cu, int32_t* items_out, int max_items,
+                                         int* num_items, int* num_slots, size_t* workspace_bytes) {
+  if (!qo_indptr_host) return MLA_ERR_INVALID_ARG;
+  return preview_impl(batch, qo_indptr_host, kv_indptr_host, kv_last_page_len_host, page_size, kv_dtype,
+                      split_override, num_cus, blocks_per_cu, items_out, max_items, num_items, num_slots,
+                      workspace_bytes);
 }
 
 mla_status mla_decode_plan_info(mla_decode_t h, int* num_items, int* max_splits,

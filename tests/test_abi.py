@@ -268,3 +268,78 @@ def test_planner_bins_hold_empty_sequences_and_no_bf16(B):
     items, slots, _ = B.mla_decode_plan_preview(indptr, num_cus=64, blocks_per_cu=1, kv_dtype="bf16")
     _check_cover(items.tolist(), lens.tolist(), slots)
     assert np.all(items[:, 4] == np.arange(len(items)))
+
+
+def _check_cover_multi(items, lens, qls, slots):
+    """Row r = qo[b] + j covers tokens [0, n_b - q_b + j] exactly once; slots are a
+    partition; items are listed workgroup by workgroup."""
+    qo = np.concatenate([[0], np.cumsum(qls)])
+    rows = int(qo[-1])
+    ends = np.zeros(rows, dtype=np.int64)
+    for b, (n, q) in enumerate(zip(lens, qls)):
+        for j in range(q):
+            ends[qo[b] + j] = n - q + j + 1
+    wg = items[:, 4].tolist()
+    assert wg == sorted(wg)
+    seen = [np.zeros(int(e), dtype=np.int32) for e in ends]
+    used = []
+    for r, t0, t1, s, _ in items.tolist():
+        assert s != -2 and 0 <= t0 < t1 <= ends[r]
+        seen[r][t0:t1] += 1
+        if s >= 0:
+            used.append(s)
+    assert all(np.all(x == 1) for x in seen)
+    assert sorted(used) == list(range(slots))
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "bf16"])
+@pytest.mark.parametrize("lens,qls,ps", [
+    ([8192] * 64, [2] * 64, 1),
+    ([1000, 37, 5000, 4], [4, 0, 1, 4], 1),
+    ([3000] * 8 + [700] * 8, [3] * 8 + [1] * 8, 2),
+    (list(range(1500, 1500 + 300 * 40, 300)), [2, 3] * 20, 4),
+])
+def test_planner_multi_token_rows(B, fmt, lens, qls, ps):
+    """Multi-token plans: every query row covers exactly its causal range; the
+    copies of an item for a sequence's query tokens are listed together."""
+    lens, qls = np.array(lens), np.array(qls)
+    pages = (lens + ps - 1) // ps
+    indptr = np.concatenate([[0], np.cumsum(pages)]).astype(np.int32)
+    last = (lens - ps * (pages - 1)).astype(np.int32)
+    qo = np.concatenate([[0], np.cumsum(qls)]).astype(np.int32)
+    items, slots, ws = B.mla_decode_plan_preview(indptr, last if ps > 1 else None, page_size=ps, num_cus=256,
+                                                blocks_per_cu=1, kv_dtype=fmt, qo_indptr_host=qo)
+    _check_cover_multi(items, lens.tolist(), qls.tolist(), slots)
+    assert ws == slots * 16 * 513 * 4
+    # rows of one sequence: same start tokens, listed next to each other
+    row_seq = np.repeat(np.arange(len(lens)), qls)
+    starts = {}
+    for r, t0, t1, s, wg in items.tolist():
+        starts.setdefault((row_seq[r], t0), []).append((r, wg))
+    for (b, t0), lst in starts.items():
+        rs = sorted(r for r, _ in lst)
+        assert rs == list(range(qo[b] + qls[b] - len(rs), qo[b] + qls[b])), (b, t0, rs)
+        wgs = sorted(w for _, w in lst)
+        assert wgs[-1] - wgs[0] <= qls.max() - 1, (b, t0, wgs)  # launched together
+
+
+def test_planner_multi_token_single_is_the_plain_plan(B):
+    lens = [8192] * 32 + [100] * 3
+    indptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    qo = np.arange(len(lens) + 1, dtype=np.int32)
+    a = B.mla_decode_plan_preview(indptr, num_cus=256, blocks_per_cu=1)
+    b = B.mla_decode_plan_preview(indptr, num_cus=256, blocks_per_cu=1, qo_indptr_host=qo)
+    assert np.array_equal(a[0], b[0]) and a[1:] == b[1:]
+
+
+@pytest.mark.parametrize("qo,why", [
+    ([0, 2, 1], "decreasing"),
+    ([1, 2, 3], "not starting at 0"),
+    ([0, 0, 0], "no query tokens"),
+    ([0, 11, 12], "more query tokens than cache tokens"),
+])
+def test_planner_multi_token_rejects_bad_qo_indptr(B, qo, why):
+    indptr = np.array([0, 10, 20], dtype=np.int32)
+    with pytest.raises(B.MlaError) as e:
+        B.mla_decode_plan_preview(indptr, qo_indptr_host=np.array(qo, dtype=np.int32))
+    assert e.value.status == 1, why

@@ -33,10 +33,10 @@ def run_gpu(B, case, split_override=0, repeats=1):
     t = B.case_to_device(case)
     dec = B.MlaDecode(case.kv_dtype, case.page_size)
     try:
-        dec.plan(case.kv_indptr, case.kv_last_page_len, split_override)
+        dec.plan(case.kv_indptr, case.kv_last_page_len, split_override, case.qo_indptr)
         outs = []
         for _ in range(repeats):
-            out = torch.full((case.batch, 16, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
+            out = torch.full((case.rows, 16, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
             dec.run(t["q"], t["kv"], t["kv_scales"], t["kv_indptr"], out, t["kv_page_indices"],
                     t["kv_last_page_len"])
             torch.cuda.synchronize()
@@ -185,6 +185,49 @@ def test_binned_ragged_batch(B, oracle_mod, kind, fmt, ps, shuffled, stride):
     assert np.array_equal(a, b)
 
 
+MULTI = [
+    # fmt, lens, q_lens, page_size, shuffled
+    ("fp8", [1, 63, 200, 1000, 5], [1, 2, 4, 3, 5], 1, False),
+    ("bf16", [130, 700, 9], [2, 1, 4], 4, True),
+    ("mxfp4", [31, 2, 900], [3, 2, 2], 2, True),
+    ("fp8", [3000, 17, 800], [4, 0, 2], 8, True),
+    ("mxfp4", [3000, 17, 800], [4, 0, 2], 1, False),
+]
+
+
+@pytest.mark.parametrize("split", [0, 3])
+@pytest.mark.parametrize("fmt,lens,qls,ps,shuffled", MULTI)
+def test_multi_token_parity(B, oracle_mod, fmt, lens, qls, ps, shuffled, split):
+    """Multi-token decode (query token j of a sequence of n tokens with q query
+    tokens attends to tokens 0 .. n - q + j): every row against the oracle's
+    causal definition, including one-token rows, sequences without query
+    tokens and rows whose range ends inside a tile."""
+    note(f"multi {fmt} lens {lens} q {qls} ps {ps} split {split}")
+    case = synth.make_case(fmt, lens, seed=50, page_size=ps, shuffle_pages=shuffled, q_lens=qls, guard_rows=2)
+    check_close(run_gpu(B, case, split), oracle_out(oracle_mod, case), fmt, f"multi {fmt} ps {ps} split {split}")
+
+
+def test_multi_token_binned_ragged_batch(B, oracle_mod):
+    """A ragged batch large enough for bins, with 1..4 query tokens per
+    sequence: the copies of each bin for the query tokens run side by side;
+    sampled sequences against the oracle, and a repeat bit for bit."""
+    rng = np.random.default_rng(51)
+    lens = rng.integers(600, 4000, 96).tolist()
+    qls = rng.integers(1, 5, 96).tolist()
+    case = synth.make_case("fp8", lens, seed=51, page_size=2, shuffle_pages=True, q_lens=qls)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    items, _, _ = B.mla_decode_plan_preview(case.kv_indptr, case.kv_last_page_len, page_size=2, num_cus=cus,
+                                            blocks_per_cu=1, kv_dtype="fp8", qo_indptr_host=case.qo_indptr)
+    note(f"multi binned: {len(items)} items, {items[:, 4].max() + 1} workgroups")
+    assert items[-1, 4] < len(items) - 1  # bins
+    a, b = run_gpu(B, case, repeats=2)
+    sample = [0, 17, 50, 95]
+    ref = oracle_out(oracle_mod, case, batches=sample)
+    rows = [r for s in sample for r in range(case.qo_indptr[s], case.qo_indptr[s + 1])]
+    check_close(a[rows], ref[rows], "fp8", "multi binned")
+    assert np.all(np.isfinite(a)) and np.array_equal(a, b)
+
+
 def test_empty_sequences_give_zero(B, oracle_mod):
     case = synth.make_case("fp8", [0, 100, 0, 1], seed=24)
     got = run_gpu(B, case)
@@ -278,4 +321,6 @@ def test_full_size_configs(B, oracle_mod, name):
     rng = np.random.default_rng(30)
     sample = sorted(rng.choice(case.batch, size=min(case.batch, 4), replace=False).tolist())
     ref = oracle_out(oracle_mod, case, batches=sample)
-    check_close(got[sample], ref[sample], case.kv_dtype, name)
+    rows = sample if case.qo_indptr is None else [r for b in sample
+                                                    for r in range(case.qo_indptr[b], case.qo_indptr[b + 1])]
+    check_close(got[rows], ref[rows], case.kv_dtype, name)
