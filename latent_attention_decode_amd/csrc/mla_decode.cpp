@@ -437,10 +437,8 @@ static void plan_items(const std::vector<int64_t>& lens, const int32_t* indptr, 
 // The sequences are planned as for single-token decode on 1 / max_b q_b of
 // the workgroup slots, and every item becomes q_b items, one per query
 // token, over the same tokens clipped to that token's causal end.  The q_b
-// copies of an item are listed together (with bins: parent bin k becomes
-// bins q k .. q k + q - 1, q = max_b q_b), so workgroups launched together
-// stream the same cache rows at about the same pace and all but the first
-// find them in the memory-side cache.
+// copies of an item go to workgroups launched together on one XCD, so that
+// they stream the same cache rows at about the same pace through one L2.
 static void plan_multi(const std::vector<int64_t>& lens, const std::vector<int32_t>& qlen,
                        const int32_t* qo_indptr, const int32_t* indptr, int split_override, int num_cus,
                        int blocks_per_cu, int page_size, int64_t tile, int64_t max_pages, bool binned,
@@ -469,26 +467,48 @@ static void plan_multi(const std::vector<int64_t>& lens, const std::vector<int32
   out->num_slots = 0;
   out->max_splits = 0;
   out->uniform_splits = out->uniform_chunk = out->uniform_len = 0;
-  const bool by_bin = !par.bins.empty();
-  const size_t groups = by_bin ? par.bins.size() - 1 : par.items.size();
-  for (size_t k = 0; k < groups; ++k) {
-    const size_t i0 = by_bin ? static_cast<size_t>(par.bins[k]) : k;
-    const size_t i1 = by_bin ? static_cast<size_t>(par.bins[k + 1]) : k + 1;
-    for (int j = 0; j < qmax; ++j) {
-      if (by_bin) out->bins.push_back(static_cast<int32_t>(out->items.size()));
-      for (size_t i = i0; i < i1; ++i) {
-        const WorkItem& it = par.items[i];
-        if (it.slot == WorkItem::kEmpty) continue;  // a sequence without query tokens
-        const int b = it.batch;
-        if (j >= qlen[b]) continue;
-        const int64_t end = lens[b] - qlen[b] + j + 1;  // this token's causal end
-        const int32_t t1 = static_cast<int32_t>(std::min<int64_t>(it.tok_end, end));
-        if (it.tok_begin >= t1) continue;
-        out->items.push_back(WorkItem{qo_indptr[b] + j, it.tok_begin, t1, 0, indptr[b], -1, 0, 0});
-      }
+  // Parent group k (a bin, or an item) and query token j become one group of
+  // the expanded plan.  Kernels that run bins get bin 8 (q (k / 8) + j) + k % 8
+  // (empty where there is nothing to do): workgroup x runs on XCD x mod 8, so
+  // the q copies of a parent group share one XCD's L2.  The one-item kernel
+  // gets the copies one after another.
+  const size_t groups = par.bins.empty() ? par.items.size() : par.bins.size() - 1;
+  auto parent_range = [&](size_t k, size_t* i0, size_t* i1) {
+    *i0 = par.bins.empty() ? k : static_cast<size_t>(par.bins[k]);
+    *i1 = par.bins.empty() ? k + 1 : static_cast<size_t>(par.bins[k + 1]);
+  };
+  auto emit = [&](size_t i0, size_t i1, int j) {
+    for (size_t i = i0; i < i1; ++i) {
+      const WorkItem& it = par.items[i];
+      if (it.slot == WorkItem::kEmpty) continue;  // a sequence without query tokens
+      const int b = it.batch;
+      if (j >= qlen[b]) continue;
+      const int64_t end = lens[b] - qlen[b] + j + 1;  // this token's causal end
+      const int32_t t1 = static_cast<int32_t>(std::min<int64_t>(it.tok_end, end));
+      if (it.tok_begin >= t1) continue;
+      out->items.push_back(WorkItem{qo_indptr[b] + j, it.tok_begin, t1, 0, indptr[b], -1, 0, 0});
+    }
+  };
+  if (binned) {
+    const size_t nbins = 8 * static_cast<size_t>(qmax) * ((groups + 7) / 8);
+    for (size_t x = 0; x < nbins; ++x) {
+      out->bins.push_back(static_cast<int32_t>(out->items.size()));
+      const size_t lane = x % 8, rest = x / 8;
+      const int j = static_cast<int>(rest % qmax);
+      const size_t k = 8 * (rest / qmax) + lane;
+      if (k >= groups) continue;
+      size_t i0, i1;
+      parent_range(k, &i0, &i1);
+      emit(i0, i1, j);
+    }
+    out->bins.push_back(static_cast<int32_t>(out->items.size()));
+  } else {
+    for (size_t k = 0; k < groups; ++k) {
+      size_t i0, i1;
+      parent_range(k, &i0, &i1);
+      for (int j = 0; j < qmax; ++j) emit(i0, i1, j);
     }
   }
-  if (by_bin) out->bins.push_back(static_cast<int32_t>(out->items.size()));
 
   // slots and merge jobs per row, its items in list order
   const int rows = qo_indptr[batch];
