@@ -186,19 +186,23 @@ static int64_t plan_tile(int kv_dtype) { return kv_dtype == MLA_KV_BF16 ? kPlanT
 static int64_t item_pages(int kv_dtype) {
   return kv_dtype == MLA_KV_FP8_E4M3 ? kItemPagesFp8 : kv_dtype == MLA_KV_MXFP4 ? kItemPagesMxfp4 : INT64_MAX;
 }
-// The formats whose split kernel runs bins of items.
-static bool plan_binned(int kv_dtype) { return kv_dtype != MLA_KV_BF16; }
 
 // Bins for a ragged batch (fp8 and MXFP4 kernels, which run the items of a
 // bin one after the other).  One item per workgroup leaves the compute units
 // that drew the short items idle while the long ones finish (a quarter of
 // the time on lengths spread evenly over 1024..8192); here the sequences,
 // longest first, are laid end to end and cut into at most `slots` bins of
-// about equal cost, a piece costing its tokens plus kPieceCost for its start
-// and finish.  A sequence cut across bins becomes several items, merged like
-// any split.  No piece is shorter than kMinPiece unless its sequence is.
-constexpr int64_t kPieceCost = 96;
+// about equal cost, a piece costing its tokens plus a fixed cost for its
+// start and finish (measured with wall-clock stamps around the items: about
+// 200 tokens of streaming for the fp8 kernel, more for the MXFP4 one, whose
+// best value on ragged batches was 288).  A sequence cut across bins becomes
+// several items, merged like any split.  No piece is shorter than kMinPiece
+// unless its sequence is.
 constexpr int64_t kMinPiece = 256;
+// (0: the format's kernel runs one item per workgroup, no bins)
+static int64_t bin_piece_cost(int kv_dtype) {
+  return kv_dtype == MLA_KV_MXFP4 ? 288 : kv_dtype == MLA_KV_FP8_E4M3 ? 192 : 0;
+}
 
 struct Piece {
   int32_t batch;
@@ -208,7 +212,7 @@ struct Piece {
 // Greedy fill of bins of cost capacity C in stream order; returns the number
 // of bins and the largest number of pieces of one sequence.
 static int64_t fill_bins(const std::vector<int64_t>& lens, const std::vector<int32_t>& order, int64_t C,
-                         int64_t tile, int64_t max_item, std::vector<std::vector<Piece>>* out,
+                         int64_t tile, int64_t max_item, int64_t kPieceCost, std::vector<std::vector<Piece>>* out,
                          int64_t* max_pieces) {
   int64_t bins = 1, r = C, most = 0;
   if (out) out->assign(1, {});
@@ -246,7 +250,7 @@ static int64_t fill_bins(const std::vector<int64_t>& lens, const std::vector<int
 // equal lengths, or too few tokens per slot for a bin to hold more than one
 // piece of the minimum size.
 static bool plan_bins(const std::vector<int64_t>& lens, const int32_t* indptr, int64_t slots, int64_t tile,
-                      int64_t max_item, int64_t max_splits, PlanOut* out) {
+                      int64_t max_item, int64_t max_splits, int64_t kPieceCost, PlanOut* out) {
   const int batch = static_cast<int>(lens.size());
   int64_t total = 0, longest = 0;
   bool equal = true;
@@ -266,7 +270,7 @@ static bool plan_bins(const std::vector<int64_t>& lens, const int32_t* indptr, i
   // more than max_splits pieces (the fill is monotone in C)
   auto fits = [&](int64_t C) {
     int64_t most = 0;
-    return fill_bins(lens, order, C, tile, max_item, nullptr, &most) <= slots && most <= max_splits;
+    return fill_bins(lens, order, C, tile, max_item, kPieceCost, nullptr, &most) <= slots && most <= max_splits;
   };
   int64_t lo = std::max((total + slots - 1) / slots, c_min);
   int64_t hi = lo;
@@ -285,7 +289,7 @@ static bool plan_bins(const std::vector<int64_t>& lens, const int32_t* indptr, i
       lo = mid + 1;
   }
   std::vector<std::vector<Piece>> bins;
-  fill_bins(lens, order, lo, tile, max_item, &bins, nullptr);
+  fill_bins(lens, order, lo, tile, max_item, kPieceCost, &bins, nullptr);
   while (!bins.empty() && bins.back().empty()) bins.pop_back();
 
   // slots: the pieces of a sequence, in stream order
@@ -331,7 +335,7 @@ static bool plan_bins(const std::vector<int64_t>& lens, const int32_t* indptr, i
 
 static void plan_items(const std::vector<int64_t>& lens, const int32_t* indptr, int split_override,
                        int num_cus, int blocks_per_cu, int page_size, int64_t tile, int64_t max_pages,
-                       bool binned, PlanOut* out) {
+                       int64_t bin_cost, PlanOut* out) {
   const int batch = static_cast<int>(lens.size());
   int64_t total = 0;
   for (int64_t n : lens) total += n;
@@ -341,9 +345,9 @@ static void plan_items(const std::vector<int64_t>& lens, const int32_t* indptr, 
                                ? (max_pages - 2) * static_cast<int64_t>(page_size) / tile * tile
                                : INT64_MAX;
   out->bins.clear();
-  if (binned && split_override == 0 &&
+  if (bin_cost > 0 && split_override == 0 &&
       plan_bins(lens, indptr, static_cast<int64_t>(num_cus) * std::max(blocks_per_cu, 1), tile, max_item,
-                kMaxAutoSplits, out))
+                kMaxAutoSplits, bin_cost, out))
     return;
   std::vector<int64_t> chunk(batch, 0);
   if (split_override > 0) {
@@ -441,7 +445,7 @@ static void plan_items(const std::vector<int64_t>& lens, const int32_t* indptr, 
 // they stream the same cache rows at about the same pace through one L2.
 static void plan_multi(const std::vector<int64_t>& lens, const std::vector<int32_t>& qlen,
                        const int32_t* qo_indptr, const int32_t* indptr, int split_override, int num_cus,
-                       int blocks_per_cu, int page_size, int64_t tile, int64_t max_pages, bool binned,
+                       int blocks_per_cu, int page_size, int64_t tile, int64_t max_pages, int64_t bin_cost,
                        PlanOut* out) {
   const int batch = static_cast<int>(lens.size());
   int qmax = 0;
@@ -451,7 +455,7 @@ static void plan_multi(const std::vector<int64_t>& lens, const std::vector<int32
     single = single && qlen[b] == 1;
   }
   if (single) {  // one query token per sequence: rows are sequences
-    plan_items(lens, indptr, split_override, num_cus, blocks_per_cu, page_size, tile, max_pages, binned, out);
+    plan_items(lens, indptr, split_override, num_cus, blocks_per_cu, page_size, tile, max_pages, bin_cost, out);
     return;
   }
   std::vector<int64_t> plens(batch);
@@ -459,7 +463,7 @@ static void plan_multi(const std::vector<int64_t>& lens, const std::vector<int32
   const int64_t slots = static_cast<int64_t>(num_cus) * std::max(blocks_per_cu, 1);
   PlanOut par;
   plan_items(plens, indptr, split_override, static_cast<int>(std::max<int64_t>(1, slots / qmax)), 1, page_size,
-             tile, max_pages, binned, &par);
+             tile, max_pages, bin_cost, &par);
 
   out->items.clear();
   out->merge.clear();
@@ -489,7 +493,7 @@ static void plan_multi(const std::vector<int64_t>& lens, const std::vector<int32
       out->items.push_back(WorkItem{qo_indptr[b] + j, it.tok_begin, t1, 0, indptr[b], -1, 0, 0});
     }
   };
-  if (binned) {
+  if (bin_cost > 0) {
     const size_t nbins = 8 * static_cast<size_t>(qmax) * ((groups + 7) / 8);
     for (size_t x = 0; x < nbins; ++x) {
       out->bins.push_back(static_cast<int32_t>(out->items.size()));
@@ -618,7 +622,7 @@ mla_status plan_impl(mla_decode_t h, int batch, const int32_t* qo_indptr_host, c
   mla::PlanOut plan;
   mla::plan_multi(lens, qlen, qo_indptr_host, kv_indptr_host, split_override, h->num_cus, h->blocks_per_cu,
                   h->page_size, mla::plan_tile(h->kv_dtype), mla::item_pages(h->kv_dtype),
-                  mla::plan_binned(h->kv_dtype), &plan);
+                  mla::bin_piece_cost(h->kv_dtype), &plan);
 
   const size_t items_bytes = plan.items.size() * sizeof(mla::WorkItem);
   const size_t merge_bytes = plan.merge.size() * sizeof(mla::MergeSeq);
@@ -689,7 +693,7 @@ mla_status preview_impl(int batch, const int32_t* qo_indptr_host, const int32_t*
   }
   mla::PlanOut plan;
   mla::plan_multi(lens, qlen, qo_indptr_host, kv_indptr_host, split_override, num_cus, blocks_per_cu, page_size,
-                  mla::plan_tile(kv_dtype), mla::item_pages(kv_dtype), mla::plan_binned(kv_dtype), &plan);
+                  mla::plan_tile(kv_dtype), mla::item_pages(kv_dtype), mla::bin_piece_cost(kv_dtype), &plan);
   const int n = static_cast<int>(plan.items.size());
   if (num_items) *num_items = n;
   if (num_slots) *num_slots = plan.num_slots;

@@ -195,11 +195,14 @@ def test_planner_split_override(B):
     _check_cover(items.tolist(), [1000, 33, 1], slots)
 
 
-def _bin_costs(items):
-    """Tokens plus 96 per item (the planner's cost of an item's start and
-    finish) of each workgroup's bin."""
+# The planner's cost of an item's start and finish, in tokens, per format.
+ITEM_COST = {"fp8": 192, "mxfp4": 288}
+
+
+def _bin_costs(items, fmt):
+    """Tokens plus the item cost per item, of each workgroup's bin."""
     cost = np.zeros(items[:, 4].max() + 1, dtype=np.int64)
-    np.add.at(cost, items[:, 4], (items[:, 2] - items[:, 1]) + 96)
+    np.add.at(cost, items[:, 4], (items[:, 2] - items[:, 1]) + ITEM_COST[fmt])
     return cost
 
 
@@ -208,7 +211,7 @@ def _bin_costs(items):
 def test_planner_ragged_batch_gets_even_bins(B, fmt, page_size):
     """fp8 / MXFP4 and a ragged batch (lengths spread over 1024..8192): the
     sequences are cut into at most one bin per resident workgroup, whose
-    costs (tokens + 96 per item) are within one short item of each other,
+    costs (tokens + the format's item cost) are within one short item of each other,
     instead of one item per workgroup that leaves the short ones idle."""
     from latent_attention_decode_amd import synth
     lens = synth.config_lens("bs256_ragged1024-8192_fp8_paged2")
@@ -218,10 +221,10 @@ def test_planner_ragged_batch_gets_even_bins(B, fmt, page_size):
     items, slots, _ = B.mla_decode_plan_preview(indptr, last if page_size > 1 else None, page_size=page_size,
                                                 num_cus=256, blocks_per_cu=1, kv_dtype=fmt)
     _check_cover(items.tolist(), lens.tolist(), slots)
-    cost = _bin_costs(items)
+    cost = _bin_costs(items, fmt)
     assert len(cost) <= 256
-    mean = (lens.sum() + 96 * len(items)) / 256
-    assert cost.max() <= mean + 256 + 96, (cost.max(), mean)
+    mean = (lens.sum() + ITEM_COST[fmt] * len(items)) / 256
+    assert cost.max() <= mean + 256 + ITEM_COST[fmt], (cost.max(), mean)
     assert cost.max() < 1.1 * mean
     sizes = items[:, 2] - items[:, 1]
     whole = items[:, 3] == -1
