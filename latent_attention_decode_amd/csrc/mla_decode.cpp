@@ -176,11 +176,17 @@ struct PlanOut {
 static int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 // Items are whole tiles of the format's split kernel: 128 tokens (fp8 and
-// MXFP4 kernels) or 64 (bf16 kernel).  A small batch is cut down to one tile
-// per item, so that it reaches more compute units; at most kMaxAutoSplits
-// items per sequence keep the merge short.
-constexpr int64_t kMaxAutoSplits = 32;
+// MXFP4 kernels) or 64 (bf16 kernel).  A small batch is cut down to items of
+// min_item_tokens, so that it reaches more compute units, with at most
+// kMaxAutoSplits items per sequence (the merge kernel spreads a small
+// batch's merge over up to 32 workgroups per sequence); bins keep
+// kMaxBinSplits, within the fused merge's reach.  Measured on bs4 x 8192
+// fp8: 256 items of one tile 15.8 us a call, 128 of two tiles 14.9; on bs4 x
+// 1024 bf16: 64 items of one 64-token tile 10.5 us, 32 of two 11.9.
+constexpr int64_t kMaxAutoSplits = 256;
+constexpr int64_t kMaxBinSplits = 32;
 static int64_t plan_tile(int kv_dtype) { return kv_dtype == MLA_KV_BF16 ? kPlanTile / 2 : kPlanTile; }
+static int64_t min_item_tokens(int kv_dtype) { return kv_dtype == MLA_KV_BF16 ? kPlanTile / 2 : 2 * kPlanTile; }
 // Page ids of one item that the format's split kernel stages (the bf16
 // kernel reads them per row and has no limit).
 static int64_t item_pages(int kv_dtype) {
@@ -334,8 +340,8 @@ static bool plan_bins(const std::vector<int64_t>& lens, const int32_t* indptr, i
 }
 
 static void plan_items(const std::vector<int64_t>& lens, const int32_t* indptr, int split_override,
-                       int num_cus, int blocks_per_cu, int page_size, int64_t tile, int64_t max_pages,
-                       int64_t bin_cost, PlanOut* out) {
+                       int num_cus, int blocks_per_cu, int page_size, int64_t tile, int64_t min_item,
+                       int64_t max_pages, int64_t bin_cost, PlanOut* out) {
   const int batch = static_cast<int>(lens.size());
   int64_t total = 0;
   for (int64_t n : lens) total += n;
@@ -347,7 +353,7 @@ static void plan_items(const std::vector<int64_t>& lens, const int32_t* indptr, 
   out->bins.clear();
   if (bin_cost > 0 && split_override == 0 &&
       plan_bins(lens, indptr, static_cast<int64_t>(num_cus) * std::max(blocks_per_cu, 1), tile, max_item,
-                kMaxAutoSplits, bin_cost, out))
+                kMaxBinSplits, bin_cost, out))
     return;
   std::vector<int64_t> chunk(batch, 0);
   if (split_override > 0) {
@@ -363,8 +369,7 @@ static void plan_items(const std::vector<int64_t>& lens, const int32_t* indptr, 
     // the ragged bs256 batch: 1, 2, 4 items per slot -> 151, 156, 160 us).
     const int64_t slots = static_cast<int64_t>(num_cus) * std::max(blocks_per_cu, 1);
     const int64_t target = slots;
-    const int64_t c = std::max<int64_t>(tile,
-                                        round_up((total + target - 1) / target, tile));
+    const int64_t c = std::max<int64_t>(min_item, round_up((total + target - 1) / target, tile));
     for (int b = 0; b < batch; ++b) {
       if (!lens[b]) continue;
       // bound the partials one merge workgroup reads
@@ -445,8 +450,8 @@ static void plan_items(const std::vector<int64_t>& lens, const int32_t* indptr, 
 // they stream the same cache rows at about the same pace through one L2.
 static void plan_multi(const std::vector<int64_t>& lens, const std::vector<int32_t>& qlen,
                        const int32_t* qo_indptr, const int32_t* indptr, int split_override, int num_cus,
-                       int blocks_per_cu, int page_size, int64_t tile, int64_t max_pages, int64_t bin_cost,
-                       PlanOut* out) {
+                       int blocks_per_cu, int page_size, int64_t tile, int64_t min_item, int64_t max_pages,
+                       int64_t bin_cost, PlanOut* out) {
   const int batch = static_cast<int>(lens.size());
   int qmax = 0;
   bool single = true;
@@ -455,7 +460,8 @@ static void plan_multi(const std::vector<int64_t>& lens, const std::vector<int32
     single = single && qlen[b] == 1;
   }
   if (single) {  // one query token per sequence: rows are sequences
-    plan_items(lens, indptr, split_override, num_cus, blocks_per_cu, page_size, tile, max_pages, bin_cost, out);
+    plan_items(lens, indptr, split_override, num_cus, blocks_per_cu, page_size, tile, min_item, max_pages, bin_cost,
+               out);
     return;
   }
   std::vector<int64_t> plens(batch);
@@ -463,7 +469,7 @@ static void plan_multi(const std::vector<int64_t>& lens, const std::vector<int32
   const int64_t slots = static_cast<int64_t>(num_cus) * std::max(blocks_per_cu, 1);
   PlanOut par;
   plan_items(plens, indptr, split_override, static_cast<int>(std::max<int64_t>(1, slots / qmax)), 1, page_size,
-             tile, max_pages, bin_cost, &par);
+             tile, min_item, max_pages, bin_cost, &par);
 
   out->items.clear();
   out->merge.clear();
@@ -621,7 +627,7 @@ mla_status plan_impl(mla_decode_t h, int batch, const int32_t* qo_indptr_host, c
 
   mla::PlanOut plan;
   mla::plan_multi(lens, qlen, qo_indptr_host, kv_indptr_host, split_override, h->num_cus, h->blocks_per_cu,
-                  h->page_size, mla::plan_tile(h->kv_dtype), mla::item_pages(h->kv_dtype),
+                  h->page_size, mla::plan_tile(h->kv_dtype), mla::min_item_tokens(h->kv_dtype), mla::item_pages(h->kv_dtype),
                   mla::bin_piece_cost(h->kv_dtype), &plan);
 
   const size_t items_bytes = plan.items.size() * sizeof(mla::WorkItem);
@@ -693,7 +699,7 @@ mla_status preview_impl(int batch, const int32_t* qo_indptr_host, const int32_t*
   }
   mla::PlanOut plan;
   mla::plan_multi(lens, qlen, qo_indptr_host, kv_indptr_host, split_override, num_cus, blocks_per_cu, page_size,
-                  mla::plan_tile(kv_dtype), mla::item_pages(kv_dtype), mla::bin_piece_cost(kv_dtype), &plan);
+                  mla::plan_tile(kv_dtype), mla::min_item_tokens(kv_dtype), mla::item_pages(kv_dtype), mla::bin_piece_cost(kv_dtype), &plan);
   const int n = static_cast<int>(plan.items.size());
   if (num_items) *num_items = n;
   if (num_slots) *num_slots = plan.num_slots;

@@ -155,6 +155,9 @@ hipError_t launch_stage1(int fmt, bool paged, const Stage1Args& a, int num_items
                          hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 hipError_t launch_merge(const MergeArgs& a, int num_merge_seqs, hipStream_t s,
                         hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
+// Workgroups per merge job (column parts): 4 for 32 jobs or more, up to 32
+// for fewer, so that a small batch's merge still spreads over many CUs.
+int merge_parts(int num_merge_seqs);
 // Static resources of a kernel (which: 0 stage 1 for `fmt`/`paged`, 1 merge).
 hipError_t kernel_attributes(int fmt, bool paged, int which, hipFuncAttributes* attr);
 // Resident stage-1 workgroups per compute unit.

@@ -462,6 +462,86 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge(MergeArgs a) {
   }
 }
 
+// The same merge for a few sequences with many partials each: a job's 2048
+// float4 of output are cut into P parts (8, 16 or 32), one workgroup each, so
+// that a small batch still spreads its merge over many compute units.  The
+// workgroup's 256 threads are S = P / 8 groups of 2048 / P threads; thread t
+// of group q merges float4 e = (2048 / P) part + t over the partials q,
+// q + S, q + 2S, .., and group 0 then merges the S results (running maximum,
+// weight sum and accumulator) through LDS.
+template <int P>
+__global__ __launch_bounds__(kMergeThreads) void mla_merge_wide(MergeArgs a) {
+  constexpr int kPart = 2048 / P;  // float4 per part
+  constexpr int S = kMergeThreads / kPart;
+  static_assert(kPart * S == kMergeThreads && S >= 1, "part split");
+  __shared__ float sh_m[S][kPart], sh_w[S][kPart];
+  __shared__ f32x4 sh_acc[S][kPart];
+  // uniform plans: numbered like their stage-1 items (xcd_block), so that a
+  // sequence's merge runs on the XCD whose L2 holds its partials
+  const int idx = a.uniform_nslots > 0 ? xcd_block(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+  const int job = idx / P, part = idx % P;
+  const MergeSeq seq = a.uniform_nslots > 0 ? MergeSeq{job, job * a.uniform_nslots, a.uniform_nslots, 0}
+                                            : a.work[job];
+  const int t = threadIdx.x % kPart, grp = threadIdx.x / kPart;
+  const int e = kPart * part + t;  // float4 of the slot; its head is e % 16
+  const int h = e & 15;
+  const float* lse = a.part_lse + (int64_t)seq.slot_begin * kNumHeads + h;
+  const f32x4* po = reinterpret_cast<const f32x4*>(a.part_o) + (int64_t)seq.slot_begin * kSlotFloat4 + e;
+  float M = kNegInf;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float W = 0.f;
+  for (int s0 = grp; s0 < seq.nslots; s0 += S * kMergeBatch) {
+    float l[kMergeBatch];
+    f32x4 x[kMergeBatch];
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {  // all loads of the batch in flight together
+      const int s = min(s0 + S * k, seq.nslots - 1);
+      l[k] = lse[s * kNumHeads];
+      x[k] = po[(int64_t)s * kSlotFloat4];
+    }
+    float mb = M;
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k)
+      if (s0 + S * k < seq.nslots) mb = fmaxf(mb, l[k]);
+    const float r = __builtin_amdgcn_exp2f(M - mb);  // 0 on the first batch
+    acc *= r;
+    W *= r;
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      const float wk = (s0 + S * k < seq.nslots) ? __builtin_amdgcn_exp2f(l[k] - mb) : 0.f;
+      W += wk;
+      acc += wk * x[k];
+    }
+    M = mb;
+  }
+  if constexpr (S > 1) {
+    sh_m[grp][t] = M;
+    sh_w[grp][t] = W;
+    sh_acc[grp][t] = acc;
+    __syncthreads();
+    if (grp != 0) return;
+    float Mall = M;
+#pragma unroll
+    for (int q = 1; q < S; ++q) Mall = fmaxf(Mall, sh_m[q][t]);
+    const float r0 = M == kNegInf ? 0.f : __builtin_amdgcn_exp2f(M - Mall);
+    acc *= r0;
+    W *= r0;
+#pragma unroll
+    for (int q = 1; q < S; ++q) {
+      const float mq = sh_m[q][t];
+      const float rq = mq == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mq - Mall);
+      W += rq * sh_w[q][t];
+      acc += rq * sh_acc[q][t];
+    }
+  }
+  const f32x4 res = acc * (1.0f / W);
+  // float4 e: column tile v = (e % 512) / 64, lane group (e % 64) / 16 of the
+  // 128-column quarter e / 512
+  const int d = 128 * (e >> 9) + 16 * ((e & 511) >> 6) + 4 * ((e & 63) >> 4);
+  *reinterpret_cast<uint2*>(a.out + ((int64_t)seq.batch * kNumHeads + h) * kVDim + d) =
+      uint2{pack_bf16x2(res[0], res[1]), pack_bf16x2(res[2], res[3])};
+}
+
 template <int F, bool P>
 const void* stage1_fn() {
   if constexpr (F == kFp8)
@@ -510,12 +590,24 @@ hipError_t launch_stage1(int fmt, bool paged, const Stage1Args& a, int num_items
   return launch(fn, dim3(num_items), dim3(threads), params, s, start, stop);
 }
 
+int merge_parts(int num_merge_seqs) {
+  // 4 parts down to 32 jobs, then up to 32 parts for the smallest batches
+  if (num_merge_seqs >= 32) return 4;
+  if (num_merge_seqs >= 16) return 8;
+  if (num_merge_seqs >= 8) return 16;
+  return 32;
+}
+
 hipError_t launch_merge(const MergeArgs& a, int num_merge_seqs, hipStream_t s, hipEvent_t start,
                         hipEvent_t stop) {
   MergeArgs args = a;
   void* params[] = {&args};
-  return launch(reinterpret_cast<const void*>(&mla_merge), dim3(num_merge_seqs * 4),
-                dim3(kMergeThreads), params, s, start, stop);
+  const int parts = merge_parts(num_merge_seqs);
+  const void* fn = parts == 4    ? reinterpret_cast<const void*>(&mla_merge)
+                   : parts == 8  ? reinterpret_cast<const void*>(&mla_merge_wide<8>)
+                   : parts == 16 ? reinterpret_cast<const void*>(&mla_merge_wide<16>)
+                                 : reinterpret_cast<const void*>(&mla_merge_wide<32>);
+  return launch(fn, dim3(num_merge_seqs * parts), dim3(kMergeThreads), params, s, start, stop);
 }
 
 hipError_t kernel_attributes(int fmt, bool paged, int which, hipFuncAttributes* attr) {

@@ -150,18 +150,31 @@ def test_planner_fills_the_gpu_for_uniform_batches(B):
 
 def test_planner_tiles_follow_the_format(B):
     """Items are whole tiles of the format's split kernel (64 tokens for bf16,
-    128 for fp8 / MXFP4); a small batch goes down to one tile per item, while
-    large uniform batches keep one wave of longer items."""
+    128 for fp8 / MXFP4); a small batch goes down to one 64-token tile (bf16)
+    or two 128-token tiles per item, while large uniform batches keep one
+    wave of longer items."""
     indptr = np.arange(5, dtype=np.int32) * 1024  # 4 x 1024
     items, _, _ = B.mla_decode_plan_preview(indptr, num_cus=256, blocks_per_cu=2, kv_dtype="bf16")
     assert np.all(items[:, 2] - items[:, 1] == 64) and len(items) == 64
     items, _, _ = B.mla_decode_plan_preview(indptr, num_cus=256, blocks_per_cu=1, kv_dtype="fp8")
-    assert np.all(items[:, 2] - items[:, 1] == 128) and len(items) == 32
+    assert np.all(items[:, 2] - items[:, 1] == 256) and len(items) == 16
     for bs, n, per_item in [(64, 1024, 256), (64, 8192, 2048), (32, 8192, 1024)]:
         indptr = np.arange(bs + 1, dtype=np.int32) * n
         for fmt in ("fp8", "mxfp4"):
             items, _, _ = B.mla_decode_plan_preview(indptr, num_cus=256, blocks_per_cu=1, kv_dtype=fmt)
             assert len(items) == 256 and np.all(items[:, 2] - items[:, 1] == per_item), (bs, n, fmt)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+def test_planner_small_batch_long_context_fills_the_gpu(B, fmt):
+    """One or two long sequences are split across every compute unit (up to
+    256 items per sequence, merged by a merge spread over 32 workgroups per
+    sequence), instead of stopping at 32 splits."""
+    for lens, per in (([131072], 512), ([32768, 32768], 256), ([8192] * 4, 256)):
+        indptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        items, slots, _ = B.mla_decode_plan_preview(indptr, num_cus=256, blocks_per_cu=1, kv_dtype=fmt)
+        assert np.all(items[:, 2] - items[:, 1] == per), lens
+        assert len(items) == sum(lens) // per and len(items) <= 256 and slots == len(items)
 
 
 def test_planner_paged_items_fit_the_staged_pages(B):

@@ -228,6 +228,28 @@ def test_multi_token_binned_ragged_batch(B, oracle_mod):
     assert np.all(np.isfinite(a)) and np.array_equal(a, b)
 
 
+EXTREMES = [
+    # what, fmt, lens, page_size
+    ("one 131072-token sequence in 256 items, merge in 32 parts", "fp8", [131072], 1),
+    ("one 32768-token MXFP4 sequence", "mxfp4", [32768], 1),
+    ("one 65536-token bf16 sequence and a short one", "bf16", [65536, 3], 1),
+    ("8 x 4096, merge in 16 parts", "fp8", [4096] * 8, 1),
+    ("16 x 2048 MXFP4, merge in 8 parts", "mxfp4", [2048] * 16, 1),
+    ("2048 sequences of 0..64 tokens", "fp8", np.random.default_rng(60).integers(0, 65, 2048).tolist(), 1),
+    ("1024-token pages", "mxfp4", [5000, 1024, 1, 2047], 1024),
+]
+
+
+@pytest.mark.parametrize("what,fmt,lens,ps", EXTREMES, ids=[e[0] for e in EXTREMES])
+def test_extreme_shapes(B, oracle_mod, what, fmt, lens, ps):
+    """Sizes at the ends of the range: the longest single sequences (split over
+    every compute unit), the widest merges, thousands of tiny or empty
+    sequences, the largest page size.  Every output against the oracle."""
+    note(f"extreme: {what}")
+    case = synth.make_case(fmt, lens, seed=61, page_size=ps, shuffle_pages=ps > 1, guard_rows=2)
+    check_close(run_gpu(B, case), oracle_out(oracle_mod, case), fmt, what)
+
+
 def test_empty_sequences_give_zero(B, oracle_mod):
     case = synth.make_case("fp8", [0, 100, 0, 1], seed=24)
     got = run_gpu(B, case)
