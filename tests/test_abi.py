@@ -364,3 +364,65 @@ def test_planner_multi_token_rejects_bad_qo_indptr(B, qo, why):
     with pytest.raises(B.MlaError) as e:
         B.mla_decode_plan_preview(indptr, qo_indptr_host=np.array(qo, dtype=np.int32))
     assert e.value.status == 1, why
+
+
+# ---------------------------------------------------------------------------
+# planner properties over random batches
+# ---------------------------------------------------------------------------
+
+from hypothesis import given, settings, strategies as st  # noqa: E402
+
+PAGE_CAP = {"fp8": 2560, "mxfp4": 1536}
+
+
+@settings(max_examples=150, deadline=None)
+@given(lens=st.lists(st.integers(0, 20000), min_size=1, max_size=48),
+       fmt=st.sampled_from(["fp8", "mxfp4", "bf16"]),
+       ps=st.sampled_from([1, 2, 16, 1024]),
+       split=st.sampled_from([0, 0, 0, 1, 3, 40]),
+       cus=st.sampled_from([8, 64, 256]),
+       bpc=st.sampled_from([1, 2]),
+       data=st.data())
+def test_planner_properties(B, lens, fmt, ps, split, cus, bpc, data):
+    """Any batch, format, page size, split override and device size: every
+    query row's causal range is covered exactly once, slots partition the
+    workspace, items are listed workgroup by workgroup, paged items fit the
+    page ids the kernel stages, and bins (if any) number at most the
+    resident workgroups times the query tokens of the widest sequence."""
+    lens = np.array(lens)
+    multi = data.draw(st.booleans())
+    qls = None
+    if multi:
+        qls = np.array([data.draw(st.integers(0, min(4, int(n)))) for n in lens])
+        if qls.sum() == 0:
+            qls[int(np.argmax(lens))] = 1 if lens.max() > 0 else 0
+        if qls.sum() == 0:
+            return  # every sequence empty: no query row can exist
+    pages = (lens + ps - 1) // ps
+    indptr = np.concatenate([[0], np.cumsum(pages)]).astype(np.int32)
+    last = np.where(pages > 0, lens - ps * (pages - 1), 0).astype(np.int32)
+    qo = None if qls is None else np.concatenate([[0], np.cumsum(qls)]).astype(np.int32)
+    items, slots, ws = B.mla_decode_plan_preview(indptr, last if ps > 1 else None, page_size=ps,
+                                                split_override=split, num_cus=cus, blocks_per_cu=bpc,
+                                                kv_dtype=fmt, qo_indptr_host=qo)
+    assert ws == slots * 16 * 513 * 4
+    if qls is None:
+        _check_cover(items.tolist(), lens.tolist(), slots)
+    else:
+        _check_cover_multi(items, lens.tolist(), qls.tolist(), slots)
+    if ps > 1 and fmt in PAGE_CAP:
+        nonempty = items[:, 2] > items[:, 1]
+        first, lastp = items[nonempty, 1] // ps, (items[nonempty, 2] - 1) // ps
+        assert np.all(lastp - first + 1 <= PAGE_CAP[fmt])
+    groups = items[:, 4].max() + 1
+    if not np.array_equal(items[:, 4], np.arange(len(items))):  # bins (possibly empty ones)
+        assert fmt != "bf16"
+        if qls is None:
+            assert groups <= cus * bpc
+        else:  # one group per parent item (or parent bin) and query token, 8 groups to a block
+            row_seq = np.repeat(np.arange(len(lens)), qls)
+            parents = len({(row_seq[r], t0) for r, t0 in items[:, :2].tolist()})
+            qmax = int(qls.max())
+            assert groups <= 8 * qmax * -(-parents // 8)
+    else:
+        assert groups == len(items)
