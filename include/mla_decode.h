@@ -1,6 +1,7 @@
 /*
- * mla_decode.h -- C ABI of the MI355X (gfx950) single-token multi-head latent
- * attention (MLA) decode library, libmla_decode.so.
+ * mla_decode.h -- C ABI of the MI355X (gfx950) multi-head latent attention
+ * (MLA) decode library, libmla_decode.so: one query token per sequence, or
+ * several (mla_decode_plan_multi).
  *
  * The operation.  For every sequence b of a batch and every query head h
  * (16 heads share one latent KV head):
@@ -108,8 +109,11 @@ mla_status mla_decode_create(mla_decode_t* out, int device, int num_heads, int q
 
 /*
  * Plan a batch: splits every sequence into work items (token ranges, whole
- * 128-token tiles except at a sequence's end) sized against the device's
- * compute-unit count and the stage-1 kernel's residency, uploads the
+ * tiles of the format's split kernel -- 128 tokens for fp8 and MXFP4, 64 for
+ * bf16 -- except at a sequence's end or under split_override, which cuts at
+ * 32-token boundaries) sized against the device's compute-unit count and
+ * the stage-1 kernel's residency (up to 256 items for one long sequence),
+ * uploads the
  * work list to the device (synchronously) and reports the workspace size the
  * run needs (bytes; may be 0).  kv_indptr_host has batch+1 entries (tokens if
  * page_size == 1, pages otherwise; non-decreasing, starting anywhere >= 0);
