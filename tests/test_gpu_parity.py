@@ -207,6 +207,13 @@ def test_multi_token_parity(B, oracle_mod, fmt, lens, qls, ps, shuffled, split):
     check_close(run_gpu(B, case, split), oracle_out(oracle_mod, case), fmt, f"multi {fmt} ps {ps} split {split}")
 
 
+def test_multi_token_mxfp4_odd_scale_stride(B, oracle_mod):
+    """Multi-token rows on an MXFP4 cache whose scale rows have an odd stride:
+    the bf16-decoding kernel runs the plan's items one per workgroup."""
+    case = synth.make_case("mxfp4", [3000, 17, 800], seed=52, q_lens=[4, 0, 2], scale_stride=19)
+    check_close(run_gpu(B, case), oracle_out(oracle_mod, case), "mxfp4", "multi mxfp4 stride 19")
+
+
 def test_multi_token_binned_ragged_batch(B, oracle_mod):
     """A ragged batch large enough for bins, with 1..4 query tokens per
     sequence: the copies of each bin for the query tokens run side by side;
