@@ -36,6 +36,7 @@ struct mla_decode_s {
   bool fused_merge = false;  // the fp8 kernel merges them itself (no merge launch)
   int uniform_splits = 0, uniform_chunk = 0, uniform_len = 0, uniform_base = 0;
   int num_bins = 0;  // > 0: binned plan (see PlanOut)
+  bool row_pairs = false;  // the fp8 kernel runs pairs of query rows (see PlanOut)
   // device: [num_items] WorkItem, [num_merge] MergeSeq, [num_merge] int32
   // counters, [num_bins + 1] int32 bin starts
   void* dev_plan = nullptr;
@@ -171,6 +172,9 @@ struct PlanOut {
   int uniform_splits = 0, uniform_chunk = 0, uniform_len = 0;
   int num_slots = 0;
   int max_splits = 0;
+  // the items come in pairs of query rows for the fp8 kernel that runs them
+  // together (see plan_multi)
+  bool row_pairs = false;
 };
 
 static int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -451,7 +455,7 @@ static void plan_items(const std::vector<int64_t>& lens, const int32_t* indptr, 
 static void plan_multi(const std::vector<int64_t>& lens, const std::vector<int32_t>& qlen,
                        const int32_t* qo_indptr, const int32_t* indptr, int split_override, int num_cus,
                        int blocks_per_cu, int page_size, int64_t tile, int64_t min_item, int64_t max_pages,
-                       int64_t bin_cost, PlanOut* out) {
+                       int64_t bin_cost, bool pairs, PlanOut* out) {
   const int batch = static_cast<int>(lens.size());
   int qmax = 0;
   bool single = true;
@@ -462,13 +466,23 @@ static void plan_multi(const std::vector<int64_t>& lens, const std::vector<int32
   if (single) {  // one query token per sequence: rows are sequences
     plan_items(lens, indptr, split_override, num_cus, blocks_per_cu, page_size, tile, min_item, max_pages, bin_cost,
                out);
+    out->row_pairs = false;
     return;
   }
+  // With pairs (fp8, whose kernel runs two query rows of a sequence over the
+  // same tokens together), a parent group's rows take ceil(q / 2) workgroups.
+  // Pairs pay where they keep the parents' pieces as long as single rows
+  // would: 2 query tokens (bs64 x 8192: 82.5 -> 72.1 us a call).  With 4 the
+  // parents are cut twice as fine, and the extra partials cost more than the
+  // shared tile reads save (bs16 x 8192: 45.3 -> 48.2 us), so single rows.
+  pairs = pairs && bin_cost > 0 && qmax == 2;
+  const int lanes = pairs ? (qmax + 1) / 2 : qmax;
+  if (pairs) max_pages = std::min<int64_t>(max_pages, kItemPagesFp8Pair);
   std::vector<int64_t> plens(batch);
   for (int b = 0; b < batch; ++b) plens[b] = qlen[b] ? lens[b] : 0;
   const int64_t slots = static_cast<int64_t>(num_cus) * std::max(blocks_per_cu, 1);
   PlanOut par;
-  plan_items(plens, indptr, split_override, static_cast<int>(std::max<int64_t>(1, slots / qmax)), 1, page_size,
+  plan_items(plens, indptr, split_override, static_cast<int>(std::max<int64_t>(1, slots / lanes)), 1, page_size,
              tile, min_item, max_pages, bin_cost, &par);
 
   out->items.clear();
@@ -477,7 +491,9 @@ static void plan_multi(const std::vector<int64_t>& lens, const std::vector<int32
   out->num_slots = 0;
   out->max_splits = 0;
   out->uniform_splits = out->uniform_chunk = out->uniform_len = 0;
-  // Parent group k (a bin, or an item) and query token j become one group of
+  out->row_pairs = pairs;
+  // Parent group k (a bin, or an item) and query token j (with pairs: tokens
+  // 2j and 2j + 1, each parent item's two listed together) become one group of
   // the expanded plan.  Kernels that run bins get bin 8 (q (k / 8) + j) + k % 8
   // (empty where there is nothing to do): workgroup x runs on XCD x mod 8, so
   // the q copies of a parent group share one XCD's L2.  The one-item kernel
@@ -487,36 +503,40 @@ static void plan_multi(const std::vector<int64_t>& lens, const std::vector<int32
     *i0 = par.bins.empty() ? k : static_cast<size_t>(par.bins[k]);
     *i1 = par.bins.empty() ? k + 1 : static_cast<size_t>(par.bins[k + 1]);
   };
-  auto emit = [&](size_t i0, size_t i1, int j) {
+  auto emit = [&](size_t i0, size_t i1, int j0, int j1) {
     for (size_t i = i0; i < i1; ++i) {
       const WorkItem& it = par.items[i];
       if (it.slot == WorkItem::kEmpty) continue;  // a sequence without query tokens
       const int b = it.batch;
-      if (j >= qlen[b]) continue;
-      const int64_t end = lens[b] - qlen[b] + j + 1;  // this token's causal end
-      const int32_t t1 = static_cast<int32_t>(std::min<int64_t>(it.tok_end, end));
-      if (it.tok_begin >= t1) continue;
-      out->items.push_back(WorkItem{qo_indptr[b] + j, it.tok_begin, t1, 0, indptr[b], -1, 0, 0});
+      for (int j = j0; j < j1 && j < qlen[b]; ++j) {
+        const int64_t end = lens[b] - qlen[b] + j + 1;  // this token's causal end
+        const int32_t t1 = static_cast<int32_t>(std::min<int64_t>(it.tok_end, end));
+        if (it.tok_begin >= t1) continue;
+        out->items.push_back(WorkItem{qo_indptr[b] + j, it.tok_begin, t1, 0, indptr[b], -1, 0, 0});
+      }
     }
   };
   if (bin_cost > 0) {
-    const size_t nbins = 8 * static_cast<size_t>(qmax) * ((groups + 7) / 8);
+    const size_t nbins = 8 * static_cast<size_t>(lanes) * ((groups + 7) / 8);
     for (size_t x = 0; x < nbins; ++x) {
       out->bins.push_back(static_cast<int32_t>(out->items.size()));
       const size_t lane = x % 8, rest = x / 8;
-      const int j = static_cast<int>(rest % qmax);
-      const size_t k = 8 * (rest / qmax) + lane;
+      const int j = static_cast<int>(rest % lanes);
+      const size_t k = 8 * (rest / lanes) + lane;
       if (k >= groups) continue;
       size_t i0, i1;
       parent_range(k, &i0, &i1);
-      emit(i0, i1, j);
+      if (pairs)
+        emit(i0, i1, 2 * j, 2 * j + 2);
+      else
+        emit(i0, i1, j, j + 1);
     }
     out->bins.push_back(static_cast<int32_t>(out->items.size()));
   } else {
     for (size_t k = 0; k < groups; ++k) {
       size_t i0, i1;
       parent_range(k, &i0, &i1);
-      for (int j = 0; j < qmax; ++j) emit(i0, i1, j);
+      for (int j = 0; j < qmax; ++j) emit(i0, i1, j, j + 1);
     }
   }
 
@@ -628,7 +648,7 @@ mla_status plan_impl(mla_decode_t h, int batch, const int32_t* qo_indptr_host, c
   mla::PlanOut plan;
   mla::plan_multi(lens, qlen, qo_indptr_host, kv_indptr_host, split_override, h->num_cus, h->blocks_per_cu,
                   h->page_size, mla::plan_tile(h->kv_dtype), mla::min_item_tokens(h->kv_dtype), mla::item_pages(h->kv_dtype),
-                  mla::bin_piece_cost(h->kv_dtype), &plan);
+                  mla::bin_piece_cost(h->kv_dtype), h->kv_dtype == MLA_KV_FP8_E4M3, &plan);
 
   const size_t items_bytes = plan.items.size() * sizeof(mla::WorkItem);
   const size_t merge_bytes = plan.merge.size() * sizeof(mla::MergeSeq);
@@ -655,6 +675,7 @@ mla_status plan_impl(mla_decode_t h, int batch, const int32_t* qo_indptr_host, c
   h->batch = qo_indptr_host[batch];  // output rows
   h->num_items = static_cast<int>(plan.items.size());
   h->num_bins = plan.bins.empty() ? 0 : static_cast<int>(plan.bins.size()) - 1;
+  h->row_pairs = plan.row_pairs;
   h->num_slots = plan.num_slots;
   h->max_splits = plan.max_splits;
   h->num_merge = static_cast<int>(plan.merge.size());
@@ -699,7 +720,8 @@ mla_status preview_impl(int batch, const int32_t* qo_indptr_host, const int32_t*
   }
   mla::PlanOut plan;
   mla::plan_multi(lens, qlen, qo_indptr_host, kv_indptr_host, split_override, num_cus, blocks_per_cu, page_size,
-                  mla::plan_tile(kv_dtype), mla::min_item_tokens(kv_dtype), mla::item_pages(kv_dtype), mla::bin_piece_cost(kv_dtype), &plan);
+                  mla::plan_tile(kv_dtype), mla::min_item_tokens(kv_dtype), mla::item_pages(kv_dtype), mla::bin_piece_cost(kv_dtype),
+                  kv_dtype == MLA_KV_FP8_E4M3, &plan);
   const int n = static_cast<int>(plan.items.size());
   if (num_items) *num_items = n;
   if (num_slots) *num_slots = plan.num_slots;
@@ -834,7 +856,8 @@ mla_status mla_decode_run(mla_decode_t h, const void* q, const void* kv, const v
   a.bins = by_bin ? reinterpret_cast<const int32_t*>(plan_base + items_bytes + merge_bytes +
                                                      static_cast<size_t>(h->num_merge) * sizeof(int32_t))
                   : nullptr;
-  hipError_t e = mla::launch_stage1(h->kv_dtype, h->page_size > 1, a, by_bin ? h->num_bins : h->num_items, s,
+  hipError_t e = mla::launch_stage1(h->kv_dtype, h->page_size > 1, by_bin && h->row_pairs, a,
+                                     by_bin ? h->num_bins : h->num_items, s,
                                      timed ? h->ev[0] : nullptr, timed ? h->ev[1] : nullptr);
   if (e != hipSuccess) return fail(h, MLA_ERR_HIP, "stage-1 launch: %s", hipGetErrorString(e));
   if (h->num_merge > 0 && !a.counters) {

@@ -20,6 +20,7 @@ constexpr int kStage1ThreadsMxfp4 = 512;  // the MXFP4 split kernel runs eight w
 // Page ids of one item that the fp8 / MXFP4 split kernels stage in LDS (what
 // the rest of their LDS leaves); the planner keeps paged items within them.
 constexpr int kItemPagesFp8 = 2560;
+constexpr int kItemPagesFp8Pair = 1536;  // the fp8 kernel that runs pairs of query rows
 constexpr int kItemPagesMxfp4 = 1536;
 constexpr int kMergeThreads = 256;  // two float4 of one head per thread
 
@@ -142,7 +143,7 @@ struct MergeArgs {
 constexpr int kFusedMergeMaxSlots = 12;
 
 // The fp8 and MXFP4 split kernels (mla_stage1_fp8.hip, mla_stage1_mxfp4.hip).
-const void* stage1_fp8_kernel(bool paged);
+const void* stage1_fp8_kernel(bool paged, bool row_pairs);
 const void* stage1_mxfp4_kernel(bool paged);
 // Whether launch_stage1 runs the split kernel of that file for these
 // arguments (it does for fp8; for MXFP4 when the scale array and its row
@@ -151,7 +152,9 @@ const void* stage1_mxfp4_kernel(bool paged);
 bool stage1_dedicated(int fmt, const Stage1Args& a);
 
 // Launchers (mla_kernels.hip).  Return the launch status.
-hipError_t launch_stage1(int fmt, bool paged, const Stage1Args& a, int num_items, hipStream_t s,
+// row_pairs: the plan lists pairs of query rows to run together (fp8
+// multi-token plans), for the fp8 kernel that does.
+hipError_t launch_stage1(int fmt, bool paged, bool row_pairs, const Stage1Args& a, int num_items, hipStream_t s,
                          hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 hipError_t launch_merge(const MergeArgs& a, int num_merge_seqs, hipStream_t s,
                         hipEvent_t start = nullptr, hipEvent_t stop = nullptr);

@@ -545,7 +545,7 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_wide(MergeArgs a) {
 template <int F, bool P>
 const void* stage1_fn() {
   if constexpr (F == kFp8)
-    return stage1_fp8_kernel(P);
+    return stage1_fp8_kernel(P, false);
   else if constexpr (F == kMxfp4)
     return stage1_mxfp4_kernel(P);
   else
@@ -577,9 +577,9 @@ bool stage1_dedicated(int fmt, const Stage1Args& a) {
   return false;
 }
 
-hipError_t launch_stage1(int fmt, bool paged, const Stage1Args& a, int num_items, hipStream_t s,
+hipError_t launch_stage1(int fmt, bool paged, bool row_pairs, const Stage1Args& a, int num_items, hipStream_t s,
                          hipEvent_t start, hipEvent_t stop) {
-  const void* fn = pick_stage1(fmt, paged);
+  const void* fn = (fmt == kFp8 && row_pairs) ? stage1_fp8_kernel(paged, true) : pick_stage1(fmt, paged);
   if (fmt == kMxfp4 && !stage1_dedicated(fmt, a))  // two-byte scale loads need even addresses
     fn = paged ? reinterpret_cast<const void*>(&mla_stage1<kMxfp4, true>)
                : reinterpret_cast<const void*>(&mla_stage1<kMxfp4, false>);

@@ -64,7 +64,6 @@ constexpr int kCLoadsPerWave = kCLoads / kWaves;    // 18
 constexpr int kQBytes = kNumHeads * kQkDim * 2;     // bf16 query of one sequence
 constexpr int kQLoads = kQBytes / 1024;             // 18
 constexpr int kPRow = kCTile + 16;                  // bytes per head row of P^T
-constexpr int kMaxItemPages = kItemPagesFp8;       // page ids of one item staged in LDS
 static_assert(kCLoads == kWaves * kCLoadsPerWave && kQLoads * 1024 == kQBytes, "load split");
 static_assert(2 * kQBytes <= kCTileBytes, "the query and its e4m3 words fit a ring slot");
 static_assert(kQBytes <= kCTileBytes, "the query is staged in the last ring slot");
@@ -105,19 +104,31 @@ constexpr bool q_slots_are_a_permutation() {
 }
 static_assert(tile_slots_are_a_permutation() && q_slots_are_a_permutation(), "slot maps");
 
+// LDS of the kernel for groups of up to NR query rows of one sequence (NR
+// = 2 pairs two query tokens of a multi-token plan; it then stages fewer
+// page ids per item to make room for the second row's P and maxima).
+template <int NR>
 struct Fp8Lds {
-  uint8_t tile[kCRing][kCTileBytes];       // the ring; slot 1 first holds the query
-  uint8_t p[2][kNumHeads][kPRow];          // P^T hi / lo as [head][token]
-  float red_m[kNumHeads][kWaves];          // per-wave tile maxima
+  static constexpr int kPages = NR == 1 ? kItemPagesFp8 : kItemPagesFp8Pair;
+  uint8_t tile[kCRing][kCTileBytes];       // the ring; slot 1 first holds the query rows
+  uint8_t p[NR][2][kNumHeads][kPRow];      // per row: P^T hi / lo as [head][token]
+  float red_m[NR][kNumHeads][kWaves];      // per row: per-wave tile maxima
   float red_l[kNumHeads][kWaves];          // per-wave sums, at the end
-  int32_t pages[kMaxItemPages];            // paged: page ids of the item
+  int32_t pages[kPages];                   // paged: page ids of the item
 };
+static_assert(sizeof(Fp8Lds<2>) <= 160 * 1024, "LDS of the paired kernel");
+static_assert(2 * 2 * kQBytes <= kCTileBytes, "two query rows and their e4m3 words fit a ring slot");
 
-// One work item: tokens [tok_begin, tok_end) of one sequence.
-template <bool PAGED>
-__device__ __forceinline__ void fp8_item(const Stage1Args& a, const WorkItem& item, Fp8Lds& sh) {
+// One group of NR work items: NR consecutive query rows of one sequence over
+// the same tokens from tok_begin (NR = 1: any work item).  Row r stops at its
+// own tok_end; the cache tiles are loaded once for all rows, and the score and
+// value contractions share each operand read from them.
+template <bool PAGED, int NR, int NRL>
+__device__ __forceinline__ void fp8_item(const Stage1Args& a, const WorkItem* items, Fp8Lds<NRL>& sh) {
+  constexpr int kMaxItemPages = Fp8Lds<NRL>::kPages;
+  const WorkItem& item = items[0];  // the rows share kv_base and tok_begin
   const int tid = threadIdx.x;
-  if (item.slot == WorkItem::kEmpty) {  // empty sequence: its output is zero
+  if (NR == 1 && item.slot == WorkItem::kEmpty) {  // empty sequence: its output is zero
     uint4* dst = reinterpret_cast<uint4*>(a.out + (int64_t)item.batch * kNumHeads * kVDim);
 #pragma unroll
     for (int k = 0; k < (kNumHeads * kVDim * 2 / 16) / kStage1Threads; ++k)
@@ -128,21 +139,28 @@ __device__ __forceinline__ void fp8_item(const Stage1Args& a, const WorkItem& it
   const int lane = tid & 63;
   const int r16 = lane & 15;  // MFMA row/column index of this lane
   const int g = lane >> 4;    // MFMA k-group of this lane
-  const int b = item.batch;
-  const int tok_last = item.tok_end - 1;
-  const int ntiles = (item.tok_end - item.tok_begin + kCTile - 1) / kCTile;
+  int tok_last_r[NR];         // last token of each row
+  int tok_end = item.tok_end;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    tok_last_r[r] = items[r].tok_end - 1;
+    tok_end = max(tok_end, items[r].tok_end);
+  }
+  const int tok_last = tok_end - 1;
+  const int ntiles = (tok_end - item.tok_begin + kCTile - 1) / kCTile;
   const float kv_scale = *a.kv_scale;
 
-  // The query first (it needs only the sequence id): 18 loads into ring slot
-  // 1, load k by wave k % 4.
+  // The query rows first (they need only the row ids): 18 loads per row into
+  // ring slot 1, row r at r * 18 KB, load k by wave k % 4.
   {
-    const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(a.q + (int64_t)b * kNumHeads * kQkDim);
     const uint32_t qm0 = lds_u32(&sh.tile[kCRing - 1][0]);
-    for (int k = wave; k < kQLoads; k += kWaves) {
-      const int s = 64 * k + lane;
+    for (int k = wave; k < kQLoads * NR; k += kWaves) {
+      const int r = k / kQLoads, kk = k - kQLoads * r;
+      const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(a.q + (int64_t)items[r].batch * kNumHeads * kQkDim);
+      const int s = 64 * kk + lane;
       const int h = s / 72;
       const int c = (s - 72 * h) ^ (h & 7);
-      dma_one(qsrc + (h * 72 + c) * 16, qm0 + 1024 * k);
+      dma_one(qsrc + (h * 72 + c) * 16, qm0 + r * kQBytes + 1024 * kk);
     }
   }
   const int64_t seq_base = item.kv_base;  // kv_indptr[b]: first row, or first page slot
@@ -150,7 +168,7 @@ __device__ __forceinline__ void fp8_item(const Stage1Args& a, const WorkItem& it
   int page0 = 0;
   if constexpr (PAGED) {
     page0 = item.tok_begin >> a.page_shift;
-    const int npages = min(((item.tok_end - 1) >> a.page_shift) - page0 + 1, kMaxItemPages);
+    const int npages = min(((tok_end - 1) >> a.page_shift) - page0 + 1, kMaxItemPages);
     // the item's page ids into LDS by four-byte cache-to-LDS loads, all in
     // flight together (lanes past the last page repeat it)
     const int32_t* psrc = a.page_indices + seq_base + page0;
@@ -175,8 +193,8 @@ __device__ __forceinline__ void fp8_item(const Stage1Args& a, const WorkItem& it
 
   // Issue part `part` of this wave's 18 loads of tile t into ring slot t % 2:
   // loads 4 part .. 4 part + 3 (part 0..3), loads 16 and 17 (part 4), or all
-  // of them (part -1).  Rows past the item's last token fetch that token's row
-  // (finite data, masked later).
+  // of them (part -1).  Rows past the group's last token fetch that token's
+  // row (finite data, masked later).
   auto issue = [&](int t, int part) {
     const int tok0 = item.tok_begin + t * kCTile;
     const int lim = tok_last - tok0;  // last valid tile row
@@ -216,83 +234,97 @@ __device__ __forceinline__ void fp8_item(const Stage1Args& a, const WorkItem& it
   wait_loads<kCLoadsPerWave>();  // this wave's query loads have landed
   lds_barrier();                 // ... and everyone's
 
-  // Query, B operand of S^T = K Q^T, scaled by 2^s and split into e4m3
-  // hi + lo: for 128-column block K (0..3) lane (head r16, group g) holds
-  // q[head][128K + 32g .. +32]; for the rope columns, k-step h (0, 1),
+  // Query rows, B operands of S^T = K Q^T, scaled by 2^s and split into
+  // e4m3 hi + lo: for 128-column block K (0..3) lane (head r16, group g)
+  // holds q[head][128K + 32g .. +32]; for the rope columns, k-step h (0, 1),
   // q[head][512 + 16g + 8h .. +8].  Every wave needs all of it; wave w
-  // converts block K = w (and waves 0, 1 rope step h = w), and the waves
-  // trade their head maxima and then the converted words through LDS, in
-  // the query's ring slot behind the bf16 query.
-  fp8x32 qh[4], ql[4];
-  fp8x8 rh[2], rl[2];
-  float xscale;
+  // converts block K = w (and waves 0, 1 rope step h = w) of every row, and
+  // the waves trade their head maxima and then the converted words through
+  // LDS, in the query's ring slot behind the bf16 rows.
+  fp8x32 qh[NR][4], ql[NR][4];
+  fp8x8 rh[NR][2], rl[NR][2];
+  float xscale[NR];
   {
-    const uint8_t* qlds = &sh.tile[kCRing - 1][0];
-    // converted words: [K][hi, lo][lane][8], then rope [h][hi, lo][lane][2]
-    uint32_t* const qcv = reinterpret_cast<uint32_t*>(&sh.tile[kCRing - 1][kQBytes]);
     const bool rope = wave < 2;
-    bf16x8 qv[5];  // [i]: chunk 16 wave + 4g + i; [4]: rope chunk 64 + 2g + wave
+    bf16x8 qv[NR][5];  // [r][i]: chunk 16 wave + 4g + i; [r][4]: rope chunk 64 + 2g + wave
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      qv[i] = *reinterpret_cast<const bf16x8*>(qlds + 16 * q_slot(r16, 16 * wave + 4 * g + i));
-    qv[4] = rope ? *reinterpret_cast<const bf16x8*>(qlds + 16 * q_slot(r16, 64 + 2 * g + wave)) : bf16x8{};
-    float am[5];
+    for (int r = 0; r < NR; ++r) {
+      const uint8_t* qlds = &sh.tile[kCRing - 1][r * kQBytes];
 #pragma unroll
-    for (int k = 0; k < 5; ++k) {
-      float m0 = fmaxf(fabsf((float)qv[k][0]), fabsf((float)qv[k][1]));
-      float m1 = fmaxf(fabsf((float)qv[k][2]), fabsf((float)qv[k][3]));
-      float m2 = fmaxf(fabsf((float)qv[k][4]), fabsf((float)qv[k][5]));
-      float m3 = fmaxf(fabsf((float)qv[k][6]), fabsf((float)qv[k][7]));
-      am[k] = fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
-    }
-    float amax = xor_max_groups(fmaxf(fmaxf(fmaxf(am[0], am[1]), fmaxf(am[2], am[3])), am[4]));
-    if (g == 0) sh.red_m[r16][wave] = amax;
-    lds_barrier();
-    const f32x4 wm = *reinterpret_cast<const f32x4*>(&sh.red_m[r16][0]);
-    amax = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
-    // 2^s with amax * 2^s in [128, 256)
-    const int s = (amax > 0.f) ? 8 - __builtin_amdgcn_frexp_expf(amax) : 0;
-    xscale = a.score_scale * kv_scale * __builtin_ldexpf(1.0f, -s);
-    uint32_t hw[10], lw[10];  // word 2k + m: elements 4m..4m+3 of qv[k]
+      for (int i = 0; i < 4; ++i)
+        qv[r][i] = *reinterpret_cast<const bf16x8*>(qlds + 16 * q_slot(r16, 16 * wave + 4 * g + i));
+      qv[r][4] = rope ? *reinterpret_cast<const bf16x8*>(qlds + 16 * q_slot(r16, 64 + 2 * g + wave)) : bf16x8{};
+      float am[5];
 #pragma unroll
-    for (int k = 0; k < 5; ++k)
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-        split_fp8x4(__builtin_ldexpf((float)qv[k][4 * m], s), __builtin_ldexpf((float)qv[k][4 * m + 1], s),
-                    __builtin_ldexpf((float)qv[k][4 * m + 2], s), __builtin_ldexpf((float)qv[k][4 * m + 3], s),
-                    hw[2 * k + m], lw[2 * k + m]);
-    u32x4* const kh = reinterpret_cast<u32x4*>(qcv + ((2 * wave) * 64 + lane) * 8);
-    u32x4* const kl = reinterpret_cast<u32x4*>(qcv + ((2 * wave + 1) * 64 + lane) * 8);
-    kh[0] = u32x4{hw[0], hw[1], hw[2], hw[3]};
-    kh[1] = u32x4{hw[4], hw[5], hw[6], hw[7]};
-    kl[0] = u32x4{lw[0], lw[1], lw[2], lw[3]};
-    kl[1] = u32x4{lw[4], lw[5], lw[6], lw[7]};
-    if (rope) {
-      *reinterpret_cast<uint2*>(qcv + 4096 + ((2 * wave) * 64 + lane) * 2) = uint2{hw[8], hw[9]};
-      *reinterpret_cast<uint2*>(qcv + 4096 + ((2 * wave + 1) * 64 + lane) * 2) = uint2{lw[8], lw[9]};
+      for (int k = 0; k < 5; ++k) {
+        float m0 = fmaxf(fabsf((float)qv[r][k][0]), fabsf((float)qv[r][k][1]));
+        float m1 = fmaxf(fabsf((float)qv[r][k][2]), fabsf((float)qv[r][k][3]));
+        float m2 = fmaxf(fabsf((float)qv[r][k][4]), fabsf((float)qv[r][k][5]));
+        float m3 = fmaxf(fabsf((float)qv[r][k][6]), fabsf((float)qv[r][k][7]));
+        am[k] = fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
+      }
+      const float amax = xor_max_groups(fmaxf(fmaxf(fmaxf(am[0], am[1]), fmaxf(am[2], am[3])), am[4]));
+      if (g == 0) sh.red_m[r][r16][wave] = amax;
     }
     lds_barrier();
 #pragma unroll
-    for (int K = 0; K < 4; ++K) {
-      const u32x4* h = reinterpret_cast<const u32x4*>(qcv + ((2 * K) * 64 + lane) * 8);
-      const u32x4* l = reinterpret_cast<const u32x4*>(qcv + ((2 * K + 1) * 64 + lane) * 8);
-      qh[K] = join16(h[0], h[1]);
-      ql[K] = join16(l[0], l[1]);
-    }
+    for (int r = 0; r < NR; ++r) {
+      uint32_t* const qcv = reinterpret_cast<uint32_t*>(&sh.tile[kCRing - 1][(NR + r) * kQBytes]);
+      const f32x4 wm = *reinterpret_cast<const f32x4*>(&sh.red_m[r][r16][0]);
+      const float amax = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
+      // 2^s with amax * 2^s in [128, 256)
+      const int s = (amax > 0.f) ? 8 - __builtin_amdgcn_frexp_expf(amax) : 0;
+      xscale[r] = a.score_scale * kv_scale * __builtin_ldexpf(1.0f, -s);
+      uint32_t hw[10], lw[10];  // word 2k + m: elements 4m..4m+3 of qv[r][k]
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint2 wh = *reinterpret_cast<const uint2*>(qcv + 4096 + ((2 * h) * 64 + lane) * 2);
-      const uint2 wl = *reinterpret_cast<const uint2*>(qcv + 4096 + ((2 * h + 1) * 64 + lane) * 2);
-      rh[h] = pack_fp8x8(wh.x, wh.y);
-      rl[h] = pack_fp8x8(wl.x, wl.y);
+      for (int k = 0; k < 5; ++k)
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+          split_fp8x4(__builtin_ldexpf((float)qv[r][k][4 * m], s), __builtin_ldexpf((float)qv[r][k][4 * m + 1], s),
+                      __builtin_ldexpf((float)qv[r][k][4 * m + 2], s),
+                      __builtin_ldexpf((float)qv[r][k][4 * m + 3], s), hw[2 * k + m], lw[2 * k + m]);
+      u32x4* const kh = reinterpret_cast<u32x4*>(qcv + ((2 * wave) * 64 + lane) * 8);
+      u32x4* const kl = reinterpret_cast<u32x4*>(qcv + ((2 * wave + 1) * 64 + lane) * 8);
+      kh[0] = u32x4{hw[0], hw[1], hw[2], hw[3]};
+      kh[1] = u32x4{hw[4], hw[5], hw[6], hw[7]};
+      kl[0] = u32x4{lw[0], lw[1], lw[2], lw[3]};
+      kl[1] = u32x4{lw[4], lw[5], lw[6], lw[7]};
+      if (rope) {
+        *reinterpret_cast<uint2*>(qcv + 4096 + ((2 * wave) * 64 + lane) * 2) = uint2{hw[8], hw[9]};
+        *reinterpret_cast<uint2*>(qcv + 4096 + ((2 * wave + 1) * 64 + lane) * 2) = uint2{lw[8], lw[9]};
+      }
+    }
+    lds_barrier();
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const uint32_t* const qcv = reinterpret_cast<const uint32_t*>(&sh.tile[kCRing - 1][(NR + r) * kQBytes]);
+#pragma unroll
+      for (int K = 0; K < 4; ++K) {
+        const u32x4* h = reinterpret_cast<const u32x4*>(qcv + ((2 * K) * 64 + lane) * 8);
+        const u32x4* l = reinterpret_cast<const u32x4*>(qcv + ((2 * K + 1) * 64 + lane) * 8);
+        qh[r][K] = join16(h[0], h[1]);
+        ql[r][K] = join16(l[0], l[1]);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint2 wh = *reinterpret_cast<const uint2*>(qcv + 4096 + ((2 * h) * 64 + lane) * 2);
+        const uint2 wl = *reinterpret_cast<const uint2*>(qcv + 4096 + ((2 * h + 1) * 64 + lane) * 2);
+        rh[r][h] = pack_fp8x8(wh.x, wh.y);
+        rl[r][h] = pack_fp8x8(wl.x, wl.y);
+      }
     }
   }
 
-  f32x4 o[8];  // O^T[dim 128w + 16v + 4g + i][head r16]
+  f32x4 o[NR][8];     // O^T[dim 128w + 16v + 4g + i][head r16] of each row
+  float m_ref[NR];    // shared running maximum (log2 units) of head r16
+  float l_part[NR];   // this lane's share of the running sum
 #pragma unroll
-  for (int v = 0; v < 8; ++v) o[v] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref = kNegInf;  // shared running maximum (log2 units) of head r16
-  float l_part = 0.f;     // this lane's share of the running sum
+  for (int r = 0; r < NR; ++r) {
+#pragma unroll
+    for (int v = 0; v < 8; ++v) o[r][v] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_ref[r] = kNegInf;
+    l_part[r] = 0.f;
+  }
 
   // LDS byte offsets of this lane's reads within a tile.  Score rows
   // 32w + 16s + r16 have chunk_swz(32w + r16) whatever s; value rows
@@ -310,8 +342,6 @@ __device__ __forceinline__ void fp8_item(const Stage1Args& a, const WorkItem& it
     for (int c4 = 0; c4 < 4; ++c4)
       v_off[qp][c4] = vrow * kQkDim + 16 * (8 * wave + (c4 ^ chunk_swz(vrow))) + 8 * (r16 & 1);
   }
-  uint8_t* const p_hi = &sh.p[0][r16][0];
-  uint8_t* const p_lo = &sh.p[1][r16][0];
 
   // Tile 1 goes into the query's slot as soon as every wave has its query in
   // registers, so that the first two tiles stream in together.
@@ -334,11 +364,13 @@ __device__ __forceinline__ void fp8_item(const Stage1Args& a, const WorkItem& it
     const uint8_t* cur = &sh.tile[t & (kCRing - 1)][0];
 
     // ---- scores of tokens 32w + 16s + (0..15), s = 0, 1 ----
-    f32x4 sacc[2][2];  // [s][hi/lo]
+    f32x4 sacc[NR][2][2];  // [row][s][hi/lo]
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int r = 0; r < NR; ++r)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) sacc[s][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) sacc[r][s][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int K = 0; K < 4; ++K) {
 #pragma unroll
@@ -346,8 +378,11 @@ __device__ __forceinline__ void fp8_item(const Stage1Args& a, const WorkItem& it
         const int ro = s * 16 * kQkDim + 128 * K;
         const fp8x32 ka = join16(*reinterpret_cast<const u32x4*>(cur + k_off0 + ro),
                                  *reinterpret_cast<const u32x4*>(cur + k_off1 + ro));
-        sacc[s][0] = mfma_fp8_k128(ka, qh[K], sacc[s][0]);
-        sacc[s][1] = mfma_fp8_k128(ka, ql[K], sacc[s][1]);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          sacc[r][s][0] = mfma_fp8_k128(ka, qh[r][K], sacc[r][s][0]);
+          sacc[r][s][1] = mfma_fp8_k128(ka, ql[r][K], sacc[r][s][1]);
+        }
       }
       if (more && (K == 1 || K == 3)) issue(t + 1, K == 1 ? 1 : 2);
     }
@@ -356,72 +391,109 @@ __device__ __forceinline__ void fp8_item(const Stage1Args& a, const WorkItem& it
       const u32x4 w = *reinterpret_cast<const u32x4*>(cur + k_offr + s * 16 * kQkDim);
       const fp8x8 ka = pack_fp8x8(w[0], w[1]);
       const fp8x8 kb = pack_fp8x8(w[2], w[3]);
-      sacc[s][0] = mfma_fp8(ka, rh[0], sacc[s][0]);
-      sacc[s][1] = mfma_fp8(ka, rl[0], sacc[s][1]);
-      sacc[s][0] = mfma_fp8(kb, rh[1], sacc[s][0]);
-      sacc[s][1] = mfma_fp8(kb, rl[1], sacc[s][1]);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        sacc[r][s][0] = mfma_fp8(ka, rh[r][0], sacc[r][s][0]);
+        sacc[r][s][1] = mfma_fp8(ka, rl[r][0], sacc[r][s][1]);
+        sacc[r][s][0] = mfma_fp8(kb, rh[r][1], sacc[r][s][0]);
+        sacc[r][s][1] = mfma_fp8(kb, rl[r][1], sacc[r][s][1]);
+      }
     }
 
-    // ---- softmax: x[s][i] is token 32w + 16s + 4g + i of head r16 ----
-    float x[2][4];
-    float tmax = kNegInf;
+    // ---- softmax: x[r][s][i] is token 32w + 16s + 4g + i of head r16 ----
+    float x[NR][2][4];
+    float p[NR][2][4];
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int r = 0; r < NR; ++r) {
+      float tmax = kNegInf;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[s][i] = (sacc[s][0][i] + sacc[s][1][i]) * xscale;
-        if (tok0 + 32 * wave + 16 * s + 4 * g + i > tok_last) x[s][i] = kNegInf;
-        tmax = fmaxf(tmax, x[s][i]);
-      }
-    tmax = xor_max_groups(tmax);
-    if (g == 0) sh.red_m[r16][wave] = tmax;
-    float p[2][4];
-    uint32_t ph[2], pl[2];
-    {
-      const float mr = (m_ref == kNegInf) ? 0.0f : m_ref;
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[r][s][i] = (sacc[r][s][0][i] + sacc[r][s][1][i]) * xscale[r];
+          if (tok0 + 32 * wave + 16 * s + 4 * g + i > tok_last_r[r]) x[r][s][i] = kNegInf;
+          tmax = fmaxf(tmax, x[r][s][i]);
+        }
+      tmax = xor_max_groups(tmax);
+      if (g == 0) sh.red_m[r][r16][wave] = tmax;
+      const float mr = (m_ref[r] == kNegInf) ? 0.0f : m_ref[r];
+      uint8_t* const p_hi = &sh.p[r][0][r16][0];
+      uint8_t* const p_lo = &sh.p[r][1][r16][0];
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
+        uint32_t ph, pl;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p[s][i] = __builtin_amdgcn_exp2f(x[s][i] - mr);
-        split_fp8x4(p[s][0], p[s][1], p[s][2], p[s][3], ph[s], pl[s]);
-        *reinterpret_cast<uint32_t*>(p_hi + 32 * wave + 16 * s + 4 * g) = ph[s];
-        *reinterpret_cast<uint32_t*>(p_lo + 32 * wave + 16 * s + 4 * g) = pl[s];
+        for (int i = 0; i < 4; ++i) p[r][s][i] = __builtin_amdgcn_exp2f(x[r][s][i] - mr);
+        split_fp8x4(p[r][s][0], p[r][s][1], p[r][s][2], p[r][s][3], ph, pl);
+        *reinterpret_cast<uint32_t*>(p_hi + 32 * wave + 16 * s + 4 * g) = ph;
+        *reinterpret_cast<uint32_t*>(p_lo + 32 * wave + 16 * s + 4 * g) = pl;
       }
     }
     if (more) issue(t + 1, 3);
     lds_barrier();  // P^T and the tile maxima of all waves
 
-    const f32x4 maxima = *reinterpret_cast<const f32x4*>(&sh.red_m[r16][0]);
-    fp8x32 bh = join16(*reinterpret_cast<const u32x4*>(p_hi + 32 * g),
-                       *reinterpret_cast<const u32x4*>(p_hi + 32 * g + 16));
-    fp8x32 bl = join16(*reinterpret_cast<const u32x4*>(p_lo + 32 * g),
-                       *reinterpret_cast<const u32x4*>(p_lo + 32 * g + 16));
-    const float tile_max = fmaxf(fmaxf(maxima[0], maxima[1]), fmaxf(maxima[2], maxima[3]));
-    // Every wave reads the same maxima, so this branch is uniform.
-    if (__ballot(tile_max > m_ref + kLazyRescale) != 0) {
-      const float m_new = fmaxf(m_ref, tile_max);
-      const float alpha = (m_ref == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
+    fp8x32 bh[NR], bl[NR];
+    float tile_max[NR];
+    bool rescale = false;
 #pragma unroll
-      for (int v = 0; v < 8; ++v) o[v] *= alpha;
-      l_part *= alpha;
-      m_ref = m_new;
+    for (int r = 0; r < NR; ++r) {
+      const f32x4 maxima = *reinterpret_cast<const f32x4*>(&sh.red_m[r][r16][0]);
+      const uint8_t* const p_hi = &sh.p[r][0][r16][0];
+      const uint8_t* const p_lo = &sh.p[r][1][r16][0];
+      bh[r] = join16(*reinterpret_cast<const u32x4*>(p_hi + 32 * g),
+                     *reinterpret_cast<const u32x4*>(p_hi + 32 * g + 16));
+      bl[r] = join16(*reinterpret_cast<const u32x4*>(p_lo + 32 * g),
+                     *reinterpret_cast<const u32x4*>(p_lo + 32 * g + 16));
+      tile_max[r] = fmaxf(fmaxf(maxima[0], maxima[1]), fmaxf(maxima[2], maxima[3]));
+      rescale = rescale || __ballot(tile_max[r] > m_ref[r] + kLazyRescale) != 0;
+    }
+    // Every wave reads the same maxima, so this branch is uniform.
+    if (rescale) {
+      bool moved[NR];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        moved[r] = __ballot(tile_max[r] > m_ref[r] + kLazyRescale) != 0;
+        if (moved[r]) {
+          const float m_new = fmaxf(m_ref[r], tile_max[r]);
+          const float alpha = (m_ref[r] == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(m_ref[r] - m_new);
+#pragma unroll
+          for (int v = 0; v < 8; ++v) o[r][v] *= alpha;
+          l_part[r] *= alpha;
+          m_ref[r] = m_new;
+        }
+      }
       lds_barrier();  // everyone has read the old P^T
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
+      for (int r = 0; r < NR; ++r) {
+        if (!moved[r]) continue;
+        uint8_t* const p_hi = &sh.p[r][0][r16][0];
+        uint8_t* const p_lo = &sh.p[r][1][r16][0];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p[s][i] = __builtin_amdgcn_exp2f(x[s][i] - m_ref);
-        split_fp8x4(p[s][0], p[s][1], p[s][2], p[s][3], ph[s], pl[s]);
-        *reinterpret_cast<uint32_t*>(p_hi + 32 * wave + 16 * s + 4 * g) = ph[s];
-        *reinterpret_cast<uint32_t*>(p_lo + 32 * wave + 16 * s + 4 * g) = pl[s];
+        for (int s = 0; s < 2; ++s) {
+          uint32_t ph, pl;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) p[r][s][i] = __builtin_amdgcn_exp2f(x[r][s][i] - m_ref[r]);
+          split_fp8x4(p[r][s][0], p[r][s][1], p[r][s][2], p[r][s][3], ph, pl);
+          *reinterpret_cast<uint32_t*>(p_hi + 32 * wave + 16 * s + 4 * g) = ph;
+          *reinterpret_cast<uint32_t*>(p_lo + 32 * wave + 16 * s + 4 * g) = pl;
+        }
       }
       lds_barrier();
-      bh = join16(*reinterpret_cast<const u32x4*>(p_hi + 32 * g),
-                  *reinterpret_cast<const u32x4*>(p_hi + 32 * g + 16));
-      bl = join16(*reinterpret_cast<const u32x4*>(p_lo + 32 * g),
-                  *reinterpret_cast<const u32x4*>(p_lo + 32 * g + 16));
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        if (!moved[r]) continue;
+        const uint8_t* const p_hi = &sh.p[r][0][r16][0];
+        const uint8_t* const p_lo = &sh.p[r][1][r16][0];
+        bh[r] = join16(*reinterpret_cast<const u32x4*>(p_hi + 32 * g),
+                       *reinterpret_cast<const u32x4*>(p_hi + 32 * g + 16));
+        bl[r] = join16(*reinterpret_cast<const u32x4*>(p_lo + 32 * g),
+                       *reinterpret_cast<const u32x4*>(p_lo + 32 * g + 16));
+      }
     }
 #pragma unroll
-    for (int s = 0; s < 2; ++s) l_part += (p[s][0] + p[s][1]) + (p[s][2] + p[s][3]);
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) l_part[r] += (p[r][s][0] + p[r][s][1]) + (p[r][s][2] + p[r][s][3]);
 
     // ---- O^T += V^T P^T over the 128 tokens, two column tiles at a time ----
 #pragma unroll
@@ -437,38 +509,63 @@ __device__ __forceinline__ void fp8_item(const Stage1Args& a, const WorkItem& it
           va[u][2 * q] = raw[0];
           va[u][2 * q + 1] = raw[1];
         }
-      o[v] = mfma_fp8_k128(va[0], bh, o[v]);
-      o[v + 1] = mfma_fp8_k128(va[1], bh, o[v + 1]);
-      o[v] = mfma_fp8_k128(va[0], bl, o[v]);
-      o[v + 1] = mfma_fp8_k128(va[1], bl, o[v + 1]);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        o[r][v] = mfma_fp8_k128(va[0], bh[r], o[r][v]);
+        o[r][v + 1] = mfma_fp8_k128(va[1], bh[r], o[r][v + 1]);
+        o[r][v] = mfma_fp8_k128(va[0], bl[r], o[r][v]);
+        o[r][v + 1] = mfma_fp8_k128(va[1], bl[r], o[r][v + 1]);
+      }
       if (more && v == 2) issue(t + 1, 4);
     }
   }
 
-  // ---- sums over the item; each wave writes its 128 columns ----
-  const float l_w = xor_sum_groups(l_part);
-  if (g == 0) sh.red_l[r16][wave] = l_w;
-  lds_barrier();
-  const f32x4 ls = *reinterpret_cast<const f32x4*>(&sh.red_l[r16][0]);
-  const float L = (ls[0] + ls[1]) + (ls[2] + ls[3]);
-  const float f = kv_scale / L;
-  finish_item<8>(a, item, tid, wave, 0, lane, o, f, m_ref + __log2f(L));
+  // ---- sums over each row; each wave writes its 128 columns ----
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    if (r > 0) lds_barrier();  // everyone has read the previous row's sums
+    const float l_w = xor_sum_groups(l_part[r]);
+    if (g == 0) sh.red_l[r16][wave] = l_w;
+    lds_barrier();
+    const f32x4 ls = *reinterpret_cast<const f32x4*>(&sh.red_l[r16][0]);
+    const float L = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    const float f = kv_scale / L;
+    finish_item<8>(a, items[r], tid, wave, 0, lane, o[r], f, m_ref[r] + __log2f(L));
+  }
 }
 
 // A workgroup runs one item, or with bins the items of bin blockIdx.x in
 // order (see Stage1Args).  Between two items every load and store of the
 // first is complete and every wave is past it, so the next may reuse LDS.
-template <bool PAGED>
+// MAXROWS = 2 (multi-token plans): two items next to each other in a bin
+// that are consecutive query rows of one sequence over the same tokens run
+// together.
+template <bool PAGED, int MAXROWS>
 __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a) {
-  __shared__ __attribute__((aligned(16))) Fp8Lds sh;
+  __shared__ __attribute__((aligned(16))) Fp8Lds<MAXROWS> sh;
   int i = a.bins ? a.bins[blockIdx.x] : (int)blockIdx.x;
   const int i_end = a.bins ? a.bins[blockIdx.x + 1] : i + 1;
   while (i < i_end) {
+    if constexpr (MAXROWS == 2) {
+      if (i + 1 < i_end) {
+        WorkItem pair[2] = {a.items[i], a.items[i + 1]};
+        if (pair[0].slot != WorkItem::kEmpty && pair[1].slot != WorkItem::kEmpty &&
+            pair[1].batch == pair[0].batch + 1 && pair[1].kv_base == pair[0].kv_base &&
+            pair[1].tok_begin == pair[0].tok_begin) {
+          fp8_item<PAGED, 2>(a, pair, sh);
+          i += 2;
+          if (i == i_end) break;
+          wait_loads<0>();
+          lds_barrier();
+          continue;
+        }
+      }
+    }
     const WorkItem item = a.uniform_splits
                               ? uniform_item(xcd_block(blockIdx.x, gridDim.x), a.uniform_splits, a.uniform_chunk,
                                              a.uniform_len, a.uniform_base)
                               : a.items[i];
-    fp8_item<PAGED>(a, item, sh);
+    fp8_item<PAGED, 1>(a, &item, sh);
     if (++i == i_end) break;
     wait_loads<0>();
     lds_barrier();
@@ -477,9 +574,12 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a
 
 }  // namespace
 
-const void* stage1_fp8_kernel(bool paged) {
-  return paged ? reinterpret_cast<const void*>(&mla_stage1_fp8<true>)
-               : reinterpret_cast<const void*>(&mla_stage1_fp8<false>);
+const void* stage1_fp8_kernel(bool paged, bool row_pairs) {
+  if (row_pairs)
+    return paged ? reinterpret_cast<const void*>(&mla_stage1_fp8<true, 2>)
+                 : reinterpret_cast<const void*>(&mla_stage1_fp8<false, 2>);
+  return paged ? reinterpret_cast<const void*>(&mla_stage1_fp8<true, 1>)
+               : reinterpret_cast<const void*>(&mla_stage1_fp8<false, 1>);
 }
 
 }  // namespace mla

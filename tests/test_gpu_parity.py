@@ -214,6 +214,31 @@ def test_multi_token_mxfp4_odd_scale_stride(B, oracle_mod):
     check_close(run_gpu(B, case), oracle_out(oracle_mod, case), "mxfp4", "multi mxfp4 stride 19")
 
 
+@pytest.mark.parametrize("split", [0, 2, 7])
+@pytest.mark.parametrize("ps", [1, 2, 16])
+def test_multi_token_pairs_fp8(B, oracle_mod, ps, split):
+    """fp8 with at most 2 query tokens per sequence: the kernel runs the two
+    rows of a sequence over each token range together (one tile read for
+    both, each row masked at its own causal end); sequences with one query
+    token run alone in the same kernel.  Every row against the oracle."""
+    lens, qls = [1, 63, 200, 1000, 5, 3000, 129], [1, 2, 2, 1, 2, 2, 2]
+    case = synth.make_case("fp8", lens, seed=53, page_size=ps, shuffle_pages=ps > 1, q_lens=qls, guard_rows=2)
+    check_close(run_gpu(B, case, split), oracle_out(oracle_mod, case), "fp8", f"pairs ps {ps} split {split}")
+
+
+def test_multi_token_pairs_binned(B, oracle_mod):
+    """A ragged fp8 batch large enough for bins, 1 or 2 query tokens per
+    sequence: bins of several parent items, each listing its row pair; all
+    rows against the oracle, and a repeat bit for bit."""
+    rng = np.random.default_rng(54)
+    lens = rng.integers(600, 4000, 120).tolist()
+    qls = rng.integers(1, 3, 120).tolist()
+    case = synth.make_case("fp8", lens, seed=54, page_size=2, shuffle_pages=True, q_lens=qls)
+    a, b = run_gpu(B, case, repeats=2)
+    check_close(a, oracle_out(oracle_mod, case), "fp8", "pairs binned")
+    assert np.array_equal(a, b)
+
+
 def test_multi_token_binned_ragged_batch(B, oracle_mod):
     """A ragged batch large enough for bins, with 1..4 query tokens per
     sequence: the copies of each bin for the query tokens run side by side;
