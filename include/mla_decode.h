@@ -205,7 +205,8 @@ mla_status mla_decode_plan_info(mla_decode_t h, int* num_items, int* max_splits,
  *   kv_indptr         int32 [batch+1] (as planned).
  *   kv_page_indices   int32 page ids (page_size > 1), else ignored.
  *   kv_last_page_len  int32 [batch] (page_size > 1), else ignored.
- *   out               bf16 [batch, 16, 512], row-major; every element written.
+ *   out               bf16 [batch, 16, 512], row-major, 16-byte aligned; every
+ *                     element written.
  *   workspace         device scratch of >= the planned size (16-byte aligned;
  *                     may be NULL when the planned size is 0).  Its contents
  *                     need no initialisation and are garbage afterwards.

@@ -102,6 +102,18 @@ def _dptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return t.data_ptr()
 
 
+def _check_run_tensors(q, out, *int32_arrays) -> None:
+    if q.dtype != torch.bfloat16 or q.dim() < 2 or tuple(q.shape[-2:]) != (NUM_HEADS, QK_DIM):
+        raise ValueError(f"q must be bf16 [rows, {NUM_HEADS}, {QK_DIM}] (got {q.dtype} {tuple(q.shape)})")
+    if out.dtype != torch.bfloat16 or out.dim() < 2 or tuple(out.shape[-2:]) != (NUM_HEADS, V_DIM):
+        raise ValueError(f"out must be bf16 [rows, {NUM_HEADS}, {V_DIM}] (got {out.dtype} {tuple(out.shape)})")
+    if q.numel() // (NUM_HEADS * QK_DIM) != out.numel() // (NUM_HEADS * V_DIM):
+        raise ValueError(f"q {tuple(q.shape)} and out {tuple(out.shape)} hold different numbers of rows")
+    for a in int32_arrays:
+        if a is not None and a.dtype != torch.int32:
+            raise ValueError(f"kv_indptr and the page table arrays must be int32 (got {a.dtype})")
+
+
 def mla_decode_version() -> int:
     return _lib.mla_decode_version()
 
@@ -195,7 +207,12 @@ def mla_decode_run(h, q: torch.Tensor, kv: torch.Tensor, kv_scales: Optional[tor
                    kv_page_indices: Optional[torch.Tensor] = None,
                    kv_last_page_len: Optional[torch.Tensor] = None,
                    stream: Optional[torch.cuda.Stream] = None) -> None:
-    """Launches the planned decode on `stream` (default: torch's current stream)."""
+    """Launches the planned decode on `stream` (default: torch's current stream).
+
+    The library takes bare pointers, so the tensors' element types and row
+    shapes are checked here: a wrong one would otherwise be read or written
+    out of bounds on the device."""
+    _check_run_tensors(q, out, kv_indptr, kv_page_indices, kv_last_page_len)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     stride = int(kv_scales.shape[-1]) if (kv_scales is not None and kv_scales.dtype == torch.uint8) else 0
@@ -243,14 +260,19 @@ class MlaDecode:
         self.page_size = page_size
         self.h = mla_decode_create(self.device, kv_dtype, page_size, sm_scale=sm_scale)
         self.workspace: Optional[torch.Tensor] = None
+        self.rows: Optional[int] = None
 
     def plan(self, kv_indptr_host, kv_last_page_len_host=None, split_override: int = 0,
              qo_indptr_host=None) -> int:
+        self.rows = None
         if qo_indptr_host is None:
             nbytes = mla_decode_plan(self.h, kv_indptr_host, kv_last_page_len_host, split_override)
+            rows = len(_host_i32(kv_indptr_host)) - 1
         else:
             nbytes = mla_decode_plan_multi(self.h, qo_indptr_host, kv_indptr_host, kv_last_page_len_host,
                                            split_override)
+            rows = int(_host_i32(qo_indptr_host)[-1])
+        self.rows = rows  # query / output rows the plan covers
         if nbytes and (self.workspace is None or self.workspace.numel() * 4 < nbytes):
             self.workspace = torch.empty((nbytes + 3) // 4, dtype=torch.float32,
                                          device=f"cuda:{self.device}")
@@ -258,6 +280,10 @@ class MlaDecode:
 
     def run(self, q, kv, kv_scales, kv_indptr, out, kv_page_indices=None, kv_last_page_len=None,
             stream=None) -> torch.Tensor:
+        if self.rows is not None and (q.numel() // (NUM_HEADS * QK_DIM) < self.rows
+                                      or out.numel() // (NUM_HEADS * V_DIM) < self.rows):
+            raise ValueError(f"the plan covers {self.rows} query rows; q {tuple(q.shape)} / out "
+                             f"{tuple(out.shape)} hold fewer")
         mla_decode_run(self.h, q, kv, kv_scales, kv_indptr, out, self.workspace, kv_page_indices,
                        kv_last_page_len, stream)
         return out

@@ -799,8 +799,8 @@ mla_status mla_decode_run(mla_decode_t h, const void* q, const void* kv, const v
     return fail(h, MLA_ERR_INVALID_ARG, "null q/kv/kv_indptr/out");
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(kv)) & 15)
     return fail(h, MLA_ERR_INVALID_ARG, "q and kv must be 16-byte aligned");
-  if (reinterpret_cast<uintptr_t>(out) & 7)
-    return fail(h, MLA_ERR_INVALID_ARG, "out must be 8-byte aligned");
+  if (reinterpret_cast<uintptr_t>(out) & 15)
+    return fail(h, MLA_ERR_INVALID_ARG, "out must be 16-byte aligned");
   if (reads_cache && h->kv_dtype != MLA_KV_BF16 && !kv_scales)
     return fail(h, MLA_ERR_INVALID_ARG, "kv_scales is NULL for a scaled cache format");
   if (h->kv_dtype == MLA_KV_MXFP4 && kv_scale_stride < 18)

@@ -83,6 +83,25 @@ def test_plan_and_run_validate_before_any_gpu_call(B):
         B.mla_decode_destroy(h)
 
 
+def test_run_rejects_wrong_tensor_types_and_shapes(B):
+    """The binding checks element types and row shapes before any pointer reaches the
+    library (which takes bare pointers and could not tell)."""
+    import torch
+    q = torch.zeros((2, 16, 576), dtype=torch.bfloat16)
+    out = torch.zeros((2, 16, 512), dtype=torch.bfloat16)
+    ip = torch.tensor([0, 4, 8], dtype=torch.int32)
+    bad = [
+        (q.float(), out, ip, "q must be bf16"),
+        (q[:, :, :512], out, ip, "q must be bf16"),
+        (q, out.view(2, 16, 16, 32), ip, "out must be bf16"),
+        (q, out[:1], ip, "different numbers of rows"),
+        (q, out, ip.long(), "must be int32"),
+    ]
+    for qq, oo, ii, msg in bad:
+        with pytest.raises(ValueError, match=msg):
+            B.mla_decode_run(None, qq, None, None, ii, oo)
+
+
 def _check_cover(items, lens, slots):
     """Every token of every sequence is in exactly one item; slots are a partition;
     items are listed workgroup by workgroup."""

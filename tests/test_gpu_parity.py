@@ -358,6 +358,13 @@ def test_workspace_too_small_is_rejected(B):
         with pytest.raises(B.MlaError) as e:
             B.mla_decode_run(dec.h, t["q"], t["kv"], t["kv_scales"], t["kv_indptr"], out, small)
         assert e.value.status == 4
+        # an output 8 bytes off a 16-byte boundary is refused before any launch
+        big = torch.empty(16 * 512 + 8, dtype=torch.bfloat16, device="cuda")
+        out8 = big[4:4 + 16 * 512].view(1, 16, 512)
+        assert out8.data_ptr() % 16 == 8
+        with pytest.raises(B.MlaError) as e:
+            B.mla_decode_run(dec.h, t["q"], t["kv"], t["kv_scales"], t["kv_indptr"], out8, dec.workspace)
+        assert e.value.status == 1 and "16-byte" in str(e.value)
     finally:
         dec.close()
 
