@@ -289,6 +289,10 @@ CONFIGS = {
     "bs256_ragged1024-8192_fp8_paged2": ("fp8", 256, (1024, 8192), 2, True, 1004),
     "bs32_kv8192_fp8": ("fp8", 32, 8192, 1, False, 1005),
     "bs64_kv8192_fp8": ("fp8", 64, 8192, 1, False, 1006),
+    # the largest shape of the leaderboard set (256 x 8192), in MXFP4 (the shape
+    # submission 727205 reports its split kernel's time for) and in fp8
+    "bs256_kv8192_mxfp4": ("mxfp4", 256, 8192, 1, False, 1009),
+    "bs256_kv8192_fp8": ("fp8", 256, 8192, 1, False, 1010),
     # multi-token decode: every sequence has q query tokens (its last q positions)
     "bs64_kv8192_q2_fp8": ("fp8", 64, 8192, 1, False, 1007, 2),
     "bs16_kv8192_q4_fp8": ("fp8", 16, 8192, 1, False, 1008, 4),
