@@ -102,15 +102,19 @@ def _dptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return t.data_ptr()
 
 
+_BF16, _I32 = torch.bfloat16, torch.int32
+
+
 def _check_run_tensors(q, out, *int32_arrays) -> None:
-    if q.dtype != torch.bfloat16 or q.dim() < 2 or tuple(q.shape[-2:]) != (NUM_HEADS, QK_DIM):
-        raise ValueError(f"q must be bf16 [rows, {NUM_HEADS}, {QK_DIM}] (got {q.dtype} {tuple(q.shape)})")
-    if out.dtype != torch.bfloat16 or out.dim() < 2 or tuple(out.shape[-2:]) != (NUM_HEADS, V_DIM):
-        raise ValueError(f"out must be bf16 [rows, {NUM_HEADS}, {V_DIM}] (got {out.dtype} {tuple(out.shape)})")
-    if q.numel() // (NUM_HEADS * QK_DIM) != out.numel() // (NUM_HEADS * V_DIM):
-        raise ValueError(f"q {tuple(q.shape)} and out {tuple(out.shape)} hold different numbers of rows")
+    qs, os_ = q.shape, out.shape
+    if q.dtype is not _BF16 or len(qs) < 2 or qs[-1] != QK_DIM or qs[-2] != NUM_HEADS:
+        raise ValueError(f"q must be bf16 [rows, {NUM_HEADS}, {QK_DIM}] (got {q.dtype} {tuple(qs)})")
+    if out.dtype is not _BF16 or len(os_) < 2 or os_[-1] != V_DIM or os_[-2] != NUM_HEADS:
+        raise ValueError(f"out must be bf16 [rows, {NUM_HEADS}, {V_DIM}] (got {out.dtype} {tuple(os_)})")
+    if q.numel() * V_DIM != out.numel() * QK_DIM:
+        raise ValueError(f"q {tuple(qs)} and out {tuple(os_)} hold different numbers of rows")
     for a in int32_arrays:
-        if a is not None and a.dtype != torch.int32:
+        if a is not None and a.dtype is not _I32:
             raise ValueError(f"kv_indptr and the page table arrays must be int32 (got {a.dtype})")
 
 
