@@ -282,6 +282,40 @@ def test_extreme_shapes(B, oracle_mod, what, fmt, lens, ps):
     check_close(run_gpu(B, case), oracle_out(oracle_mod, case), fmt, what)
 
 
+def random_cases(n=120, seed=2024):
+    """Seeded mixed cases: format, ragged and empty lengths, page size and shuffling,
+    MXFP4 scale stride, split override and sometimes several query tokens per
+    sequence."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for k in range(n):
+        fmt = synth.FORMATS[k % 3]
+        batch = int(rng.integers(1, 13))
+        lens = rng.integers(0, 3000, size=batch)
+        lens[rng.random(batch) < 0.15] = 0
+        if lens.sum() == 0:
+            lens[0] = int(rng.integers(1, 600))
+        ps = int(rng.choice([1, 1, 2, 4, 16, 64]))
+        stride = int(rng.choice([18, 18, 20, 19])) if fmt == "mxfp4" else 18
+        split = int(rng.choice([0, 0, 0, 1, 2, 5]))
+        q_lens = None
+        if rng.random() < 0.3:
+            q_lens = [int(min(n_b, rng.integers(0, 4))) for n_b in lens]
+            if sum(q_lens) == 0:
+                q_lens = None
+        cases.append((k, fmt, [int(x) for x in lens], ps, stride, split, q_lens))
+    return cases
+
+
+@pytest.mark.parametrize("k,fmt,lens,ps,stride,split,q_lens", random_cases(), ids=lambda v: None)
+def test_random_mixed_cases(B, oracle_mod, k, fmt, lens, ps, stride, split, q_lens):
+    note(f"random case {k}: {fmt} lens={lens} ps={ps} stride={stride} split={split} q_lens={q_lens}")
+    case = synth.make_case(fmt, lens, seed=5000 + k, page_size=ps, shuffle_pages=ps > 1, scale_stride=stride,
+                           q_lens=q_lens, guard_rows=3)
+    got = run_gpu(B, case, split)
+    check_close(got, oracle_out(oracle_mod, case), fmt, f"random case {k}")
+
+
 def test_empty_sequences_give_zero(B, oracle_mod):
     case = synth.make_case("fp8", [0, 100, 0, 1], seed=24)
     got = run_gpu(B, case)
