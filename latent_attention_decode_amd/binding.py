@@ -227,6 +227,31 @@ def mla_decode_run(h, q: torch.Tensor, kv: torch.Tensor, kv_scales: Optional[tor
     _check(st, "mla_decode_run", h)
 
 
+class PreparedRun:
+    """mla_decode_run with its arguments marshalled once (the same checks as
+    mla_decode_run).  Each call launches the planned decode on the same
+    tensors and stream, at the cost of one foreign call.  The tensors must stay
+    alive and in place (the object holds references), and the handle must not
+    be planned again while the object is used."""
+
+    def __init__(self, h, q, kv, kv_scales, kv_indptr, out, workspace=None, kv_page_indices=None,
+                 kv_last_page_len=None, stream=None):
+        _check_run_tensors(q, out, kv_indptr, kv_page_indices, kv_last_page_len)
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device)
+        stride = int(kv_scales.shape[-1]) if (kv_scales is not None and kv_scales.dtype == torch.uint8) else 0
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        self._keep = (q, kv, kv_scales, kv_indptr, out, workspace, kv_page_indices, kv_last_page_len, stream)
+        self._h = h
+        self._args = (h, _dptr(q), _dptr(kv), _dptr(kv_scales), stride, _dptr(kv_indptr), _dptr(kv_page_indices),
+                      _dptr(kv_last_page_len), _dptr(out), _dptr(workspace), ws_bytes, stream.cuda_stream)
+
+    def __call__(self) -> None:
+        st = _lib.mla_decode_run(*self._args)
+        if st != 0:
+            _check(st, "mla_decode_run", self._h)
+
+
 def mla_decode_set_profiling(h, enable: bool) -> None:
     _check(_lib.mla_decode_set_profiling(h, int(bool(enable))), "mla_decode_set_profiling", h)
 
@@ -284,13 +309,23 @@ class MlaDecode:
 
     def run(self, q, kv, kv_scales, kv_indptr, out, kv_page_indices=None, kv_last_page_len=None,
             stream=None) -> torch.Tensor:
+        self._check_rows(q, out)
+        mla_decode_run(self.h, q, kv, kv_scales, kv_indptr, out, self.workspace, kv_page_indices,
+                       kv_last_page_len, stream)
+        return out
+
+    def prepare(self, q, kv, kv_scales, kv_indptr, out, kv_page_indices=None, kv_last_page_len=None,
+                stream=None) -> PreparedRun:
+        """A PreparedRun of this handle's current plan and workspace."""
+        self._check_rows(q, out)
+        return PreparedRun(self.h, q, kv, kv_scales, kv_indptr, out, self.workspace, kv_page_indices,
+                           kv_last_page_len, stream)
+
+    def _check_rows(self, q, out) -> None:
         if self.rows is not None and (q.numel() // (NUM_HEADS * QK_DIM) < self.rows
                                       or out.numel() // (NUM_HEADS * V_DIM) < self.rows):
             raise ValueError(f"the plan covers {self.rows} query rows; q {tuple(q.shape)} / out "
                              f"{tuple(out.shape)} hold fewer")
-        mla_decode_run(self.h, q, kv, kv_scales, kv_indptr, out, self.workspace, kv_page_indices,
-                       kv_last_page_len, stream)
-        return out
 
     def close(self) -> None:
         if self.h:

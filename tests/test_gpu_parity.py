@@ -380,6 +380,28 @@ def test_merge_repeated_calls(B, oracle_mod, fmt, split):
     assert np.array_equal(outs[0], outs[3])
 
 
+@pytest.mark.parametrize("fmt,lens,ps", [("fp8", [3000, 40, 700], 2), ("mxfp4", [1500, 9], 1), ("bf16", [600], 1)])
+def test_prepared_run_matches_run(B, fmt, lens, ps):
+    """A PreparedRun (arguments marshalled once) launches exactly what run() does."""
+    case = synth.make_case(fmt, lens, seed=77, page_size=ps, shuffle_pages=ps > 1)
+    t = B.case_to_device(case)
+    dec = B.MlaDecode(fmt, ps)
+    try:
+        dec.plan(case.kv_indptr, case.kv_last_page_len)
+        ref = torch.full((case.rows, 16, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
+        dec.run(t["q"], t["kv"], t["kv_scales"], t["kv_indptr"], ref, t["kv_page_indices"], t["kv_last_page_len"])
+        out = torch.full_like(ref, float("nan"))
+        call = dec.prepare(t["q"], t["kv"], t["kv_scales"], t["kv_indptr"], out, t["kv_page_indices"],
+                           t["kv_last_page_len"])
+        for _ in range(3):
+            out.fill_(float("nan"))
+            call()
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    finally:
+        dec.close()
+
+
 def test_workspace_too_small_is_rejected(B):
     case = synth.make_case("fp8", [4096], seed=29)
     t = B.case_to_device(case)
