@@ -40,9 +40,12 @@ namespace {
 // 72 loads of 1 KB each (wave w issues loads 18w..18w+17).  One load writes
 // 64 consecutive 16-byte LDS slots, lane l to slot l, and each lane fetches
 // the chunk that belongs there; inside each aligned group of four chunks of a
-// row the chunks are stored XOR-permuted by chunk_swz(row), which makes every
-// LDS read below free of bank conflicts while each load still covers whole
-// 64-byte runs of the rows.
+// row the chunks are stored XOR-permuted by chunk_swz(row), which spreads
+// the LDS reads below over the banks while each load still covers whole
+// 64-byte runs of the rows (measured: the transposing V reads run without
+// bank conflicts; the 16-byte score, rope and P reads still see some, about
+// a third of the LDS's active cycles, and the LDS is active for a seventh of
+// the kernel's).
 //
 // Per tile, with wave w:
 //   1. S^T[token, head] = K (Qhi + Qlo)^T for tokens 32w..32w+31 (two 16-token
@@ -73,7 +76,8 @@ static_assert(kQBytes <= kCTileBytes, "the query is staged in the last ring slot
 // banks of 4 bytes; with rows at pitch 576, the reads below touch, per phase,
 // 16 rows r0..r0+15 of one chunk (score reads, 16 B per lane) or rows
 // {32g + 8q + e : e < 8} of two neighbouring g (transposing V reads, 8 B per
-// lane), and this permutation puts every phase on distinct banks.
+// lane).  In a model of 64 four-byte banks this permutation puts each such
+// phase on distinct banks.
 __host__ __device__ constexpr int chunk_swz(int r) {
   return ((r >> 2) & 1) | ((((r >> 3) ^ (r >> 5)) & 1) << 1);
 }
