@@ -425,6 +425,55 @@ def test_workspace_too_small_is_rejected(B):
         dec.close()
 
 
+def test_run_validates_arguments(B):
+    """Every malformed run is refused with a status and a message before anything is
+    launched; the handle still runs correctly afterwards."""
+    def status(fn):
+        with pytest.raises(B.MlaError) as e:
+            fn()
+        return e.value.status, str(e.value)
+
+    case = synth.make_case("mxfp4", [700, 300], seed=81)
+    t = B.case_to_device(case)
+    dec = B.MlaDecode("mxfp4")
+    try:
+        dec.plan(case.kv_indptr)
+        out = torch.empty((2, 16, 512), dtype=torch.bfloat16, device="cuda")
+        run = lambda **kw: B.mla_decode_run(dec.h, **{**dict(q=t["q"], kv=t["kv"], kv_scales=t["kv_scales"],
+                                                             kv_indptr=t["kv_indptr"], out=out,
+                                                             workspace=dec.workspace), **kw})
+        st, msg = status(lambda: run(kv_scales=t["kv_scales"][:, :17].contiguous()))
+        assert st == 1 and ">= 18" in msg
+        st, msg = status(lambda: run(kv_scales=None))
+        assert st == 1 and "kv_scales" in msg
+        flat = torch.empty(t["q"].numel() + 8, dtype=torch.bfloat16, device="cuda")
+        q8 = flat[4:4 + t["q"].numel()].view_as(t["q"])
+        st, msg = status(lambda: run(q=q8))
+        assert st == 1 and "16-byte" in msg
+        st, msg = status(lambda: run(workspace=None))
+        assert st == 4
+        got = run_gpu(B, case)  # a fresh handle still agrees with the oracle
+        assert np.all(np.isfinite(got))
+    finally:
+        dec.close()
+
+    paged = synth.make_case("fp8", [50, 9], seed=82, page_size=4, shuffle_pages=True)
+    tp = B.case_to_device(paged)
+    dec = B.MlaDecode("fp8", 4)
+    try:
+        dec.plan(paged.kv_indptr, paged.kv_last_page_len)
+        out = torch.empty((2, 16, 512), dtype=torch.bfloat16, device="cuda")
+        st, msg = status(lambda: B.mla_decode_run(dec.h, tp["q"], tp["kv"], tp["kv_scales"], tp["kv_indptr"], out,
+                                                  dec.workspace, None, tp["kv_last_page_len"]))
+        assert st == 1 and "page table" in msg
+        dec.run(tp["q"], tp["kv"], tp["kv_scales"], tp["kv_indptr"], out, tp["kv_page_indices"],
+                tp["kv_last_page_len"])
+        torch.cuda.synchronize()
+        assert torch.isfinite(out.float()).all()
+    finally:
+        dec.close()
+
+
 # Full-size workloads: every output of a few sampled sequences against the oracle.
 FULL = list(synth.CONFIGS)
 
