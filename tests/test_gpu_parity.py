@@ -425,6 +425,34 @@ def test_workspace_too_small_is_rejected(B):
         dec.close()
 
 
+def test_two_handles_on_two_streams(B, oracle_mod):
+    """Handles share no state: two plans (one with a fused merge, one with the merge kernel)
+    run interleaved on two streams, several times, and both match the oracle every time."""
+    case_a = synth.make_case("fp8", [3000, 700, 4100, 90], seed=91, page_size=2, shuffle_pages=True)
+    case_b = synth.make_case("fp8", [2048] * 8, seed=92)
+    ref_a, ref_b = oracle_out(oracle_mod, case_a), oracle_out(oracle_mod, case_b)
+    ta, tb = B.case_to_device(case_a), B.case_to_device(case_b)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    da, db = B.MlaDecode("fp8", 2), B.MlaDecode("fp8")
+    try:
+        da.plan(case_a.kv_indptr, case_a.kv_last_page_len)
+        db.plan(case_b.kv_indptr)
+        outs_a = [torch.full((4, 16, 512), float("nan"), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+        outs_b = [torch.full((8, 16, 512), float("nan"), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+        torch.cuda.synchronize()
+        for oa, ob in zip(outs_a, outs_b):
+            da.run(ta["q"], ta["kv"], ta["kv_scales"], ta["kv_indptr"], oa, ta["kv_page_indices"],
+                   ta["kv_last_page_len"], stream=sa)
+            db.run(tb["q"], tb["kv"], tb["kv_scales"], tb["kv_indptr"], ob, stream=sb)
+        torch.cuda.synchronize()
+        for k in range(3):
+            check_close(outs_a[k].float().cpu().numpy().astype(np.float64), ref_a, "fp8", f"handle a call {k}")
+            check_close(outs_b[k].float().cpu().numpy().astype(np.float64), ref_b, "fp8", f"handle b call {k}")
+    finally:
+        da.close()
+        db.close()
+
+
 def test_run_validates_arguments(B):
     """Every malformed run is refused with a status and a message before anything is
     launched; the handle still runs correctly afterwards."""
