@@ -141,7 +141,7 @@ struct TileRegs {
       const uint8_t* base = a.kv + (seq_base + tok0) * kRB + tid * 16;
 #pragma unroll
       for (int j = 0; j < kN; ++j)
-        d[j] = *reinterpret_cast<const u32x4*>(base + j * (16 * kStage1Threads));
+        d[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + j * (16 * kStage1Threads)));
       return;
     }
     uint32_t my_row = 0;  // physical row of tile row (tid & 63), paged only
@@ -160,7 +160,7 @@ struct TileRegs {
           row = (uint32_t)__shfl((int)my_row, r, 64);
         else
           row = (uint32_t)(seq_base + min(tok0 + r, tok_last));
-        d[j] = *reinterpret_cast<const u32x4*>(a.kv + (int64_t)row * kRB + cc * 16);
+        d[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.kv + (int64_t)row * kRB + cc * 16));
         if constexpr (F == kMxfp4) s[j] = a.kv_mx_scales[(int64_t)row * a.scale_stride + cc];
       }
       cc += kStepCols;
