@@ -15,9 +15,12 @@
 //                     scores on the e2m1 codes with their e8m0 block scales,
 //                     V converted to e4m3 per tile for P.V.
 //   mla_stage1        (this file) bf16 cache, and MXFP4 whose scale rows are
-//                     not 2-byte aligned: 64-token tiles staged through
-//                     registers, MXFP4 decoded to bf16 exactly on the way into
-//                     LDS, both contractions on v_mfma_f32_16x16x32_bf16.
+//                     not 2-byte aligned: 64-token tiles, both contractions
+//                     on v_mfma_f32_16x16x32_bf16.  A contiguous bf16 cache
+//                     streams into a ring of two LDS buffers by cache-to-LDS
+//                     loads (one workgroup per CU); a paged one, and MXFP4
+//                     (decoded to bf16 exactly on the way into LDS), are
+//                     staged through registers (two workgroups per CU).
 //   mla_merge         (this file) per (sequence, quarter of the columns) of
 //                     the split sequences, the log-sum-exp weighted merge of
 //                     the partials (727205 `mla_rd`; 700955 "locked baseline
@@ -36,6 +39,8 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "mla_device.h"
 #include "mla_internal.h"
@@ -205,6 +210,34 @@ template <int F>
 struct Stage1Tiles {
   uint8_t tile[Traits<F>::kBuffers][Tile<F>::kBytes];
 };
+// The contiguous bf16 cache streams into a ring of two tile buffers by
+// cache-to-LDS loads (one workgroup per CU), in the same padded row layout:
+// the 74 loads of 1 KB fill the buffer slot by slot, a slot in a row's data
+// taking its 16 bytes of the row and a padding slot a harmless copy of the
+// row's first 16.
+constexpr int kDmaLoads = 74;                 // 1 KB loads per tile buffer
+constexpr int kDmaTileBytes = kDmaLoads * 1024;
+static_assert(kDmaTileBytes >= Tile<kBf16>::kBytes, "a DMA buffer holds a padded bf16 tile");
+struct DmaRing {
+  uint8_t tile[2][kDmaTileBytes];
+};
+// Tile row and 16-byte chunk whose data belongs at byte o of a padded bf16
+// tile (chunk 0 of the row for a padding slot; the last row past the end).
+// With s = o / 16: a group of 16 rows spans 16 * 73 + 4 = 1172 slots (73 per
+// row, the last of them padding, then 4 more), so the row is 16 (s / 1172) +
+// (s % 1172) / 73 and the chunk (s % 1172) % 73.
+__device__ __forceinline__ void dma_slot_source(int o, int& r, int& c) {
+  constexpr int kRowSlots = Traits<kBf16>::kLdsPitch / 16;  // 73
+  constexpr int kGroupSlots = 16 * kRowSlots + 4;           // 1172
+  const int s = o >> 4;
+  const int grp = s / kGroupSlots;
+  const int in = s - grp * kGroupSlots;
+  const int rr = in / kRowSlots;
+  r = min(16 * grp + min(rr, 15), kTileTokens - 1);
+  c = in - rr * kRowSlots;
+  if (rr > 15 || c >= 2 * kQkDim / 16 || 16 * grp + rr >= kTileTokens) c = 0;  // padding
+}
+
 template <int F, bool PAGED>
 struct Stage1Lds {
   uint2 p[kWaves][64];               // 4 bf16 probabilities per lane
@@ -300,7 +333,8 @@ __device__ __forceinline__ void attend_tile(Stage1Lds<F, PAGED>& sh, const uint8
 
 template <int F, bool PAGED>
 __global__ __launch_bounds__(kStage1Threads, 2) void mla_stage1(Stage1Args a) {
-  __shared__ __attribute__((aligned(16))) Stage1Tiles<F> tiles;
+  constexpr bool kDma = F == kBf16 && !PAGED;
+  __shared__ __attribute__((aligned(16))) typename std::conditional<kDma, DmaRing, Stage1Tiles<F>>::type tiles;
   __shared__ __attribute__((aligned(16))) Stage1Lds<F, PAGED> sh;
 
   const WorkItem item = a.uniform_splits
@@ -354,7 +388,48 @@ __global__ __launch_bounds__(kStage1Threads, 2) void mla_stage1(Stage1Args a) {
   const int v_off_lo = Tile<F>::row_offset(pv_token(g, r16 >> 2)) + (r16 & 3) * 8 + 2 * dv0;
   const int v_off_hi = Tile<F>::row_offset(pv_token(g, 4 + (r16 >> 2))) + (r16 & 3) * 8 + 2 * dv0;
 
-  {
+  if constexpr (kDma) {
+    // ---- cache-to-LDS ring of two buffers ----
+    // This wave's loads of a tile: 19 (waves 0, 1) or 18 (waves 2, 3), load
+    // j being number l0 + j of the tile's 74, at LDS 1024 (l0 + j).
+    const int nl = wave < 2 ? 19 : 18;
+    const int l0 = wave < 2 ? 19 * wave : 38 + 18 * (wave - 2);
+    int srow[19], scol[19];
+#pragma unroll
+    for (int j = 0; j < 19; ++j) dma_slot_source(1024 * (l0 + min(j, nl - 1)) + 16 * lane, srow[j], scol[j]);
+    auto issue = [&](int n) {  // tile n into buffer n % 2
+      const int tok0 = item.tok_begin + n * kTileTokens;
+      const int lim = tok_last - tok0;
+      const uint8_t* rows = a.kv + (seq_base + tok0) * (int64_t)(2 * kQkDim);
+      const uint32_t m0 = lds_u32(&tiles.tile[n & 1][0]) + 1024 * l0;
+      const uint8_t* src[19];
+#pragma unroll
+      for (int j = 0; j < 19; ++j)
+        src[j] = rows + min(srow[j], lim) * (2 * kQkDim) + 16 * scol[j] - (j < 18 ? 1024 * (j & 3) : 0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dma_group<4>(src + 4 * q, m0 + 4096 * q);
+      dma_group<2>(src + 16, m0 + 4096 * 4);
+      if (nl == 19) dma_one(src[18], m0 + 1024 * 18);
+    };
+    issue(0);
+    if (ntiles > 1) issue(1);
+    for (int n = 0; n < ntiles; ++n) {
+      const int tok0 = item.tok_begin + n * kTileTokens;
+      if (n == 0 && ntiles > 1) {  // tile 0, not tile 1 behind it
+        if (nl == 19)
+          wait_loads<19>();
+        else
+          wait_loads<18>();
+      } else {
+        wait_loads<0>();
+      }
+      lds_barrier();  // tile n everywhere; everyone is past tile n - 1 (and its P)
+      if (n >= 1 && n + 1 < ntiles) issue(n + 1);  // into the buffer tile n - 1 used
+      attend_tile<F, PAGED>(sh, tiles.tile[n & 1], qf, o, m_ref, l_part, tok0, tok_last, xscale, wave, lane,
+                            k_off, v_off_lo, v_off_hi);
+    }
+    lds_barrier();  // the last P.V reads are done
+  } else {
     // ---- register-staged tiles through one LDS buffer ----
     TileRegs<F, PAGED> regs;
     regs.issue(a, seq_base, item.tok_begin, tok_last, tid);
