@@ -191,10 +191,9 @@ constexpr int64_t kMaxAutoSplits = 256;
 constexpr int64_t kMaxBinSplits = 32;
 static int64_t plan_tile(int kv_dtype) { return kv_dtype == MLA_KV_BF16 ? kPlanTile / 2 : kPlanTile; }
 static int64_t min_item_tokens(int kv_dtype) { return kv_dtype == MLA_KV_BF16 ? kPlanTile / 2 : 2 * kPlanTile; }
-// Page ids of one item that the format's split kernel stages (the bf16
-// kernel reads them per row and has no limit).
+// Page ids of one item that the format's split kernel stages in LDS.
 static int64_t item_pages(int kv_dtype) {
-  return kv_dtype == MLA_KV_FP8_E4M3 ? kItemPagesFp8 : kv_dtype == MLA_KV_MXFP4 ? kItemPagesMxfp4 : INT64_MAX;
+  return kv_dtype == MLA_KV_FP8_E4M3 ? kItemPagesFp8 : kv_dtype == MLA_KV_MXFP4 ? kItemPagesMxfp4 : kItemPagesBf16;
 }
 
 // Bins for a ragged batch (fp8 and MXFP4 kernels, which run the items of a

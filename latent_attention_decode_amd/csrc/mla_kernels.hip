@@ -243,6 +243,7 @@ struct Stage1Lds {
   uint2 p[kWaves][64];               // 4 bf16 probabilities per lane
   f32x4 tmax[kWaves][kNumHeads];     // [wave][head][lane group] tile maxima
   float lsum[kWaves][kNumHeads];
+  int32_t pages[F == kBf16 && PAGED ? kItemPagesBf16 : 1];  // paged bf16: page ids of the item
 };
 
 // One 64-token tile held in `cur`: scores, shared lazy max, P.V.  Ends after
@@ -333,7 +334,7 @@ __device__ __forceinline__ void attend_tile(Stage1Lds<F, PAGED>& sh, const uint8
 
 template <int F, bool PAGED>
 __global__ __launch_bounds__(kStage1Threads, 2) void mla_stage1(Stage1Args a) {
-  constexpr bool kDma = F == kBf16 && !PAGED;
+  constexpr bool kDma = F == kBf16;
   __shared__ __attribute__((aligned(16))) typename std::conditional<kDma, DmaRing, Stage1Tiles<F>>::type tiles;
   __shared__ __attribute__((aligned(16))) Stage1Lds<F, PAGED> sh;
 
@@ -397,15 +398,35 @@ __global__ __launch_bounds__(kStage1Threads, 2) void mla_stage1(Stage1Args a) {
     int srow[19], scol[19];
 #pragma unroll
     for (int j = 0; j < 19; ++j) dma_slot_source(1024 * (l0 + min(j, nl - 1)) + 16 * lane, srow[j], scol[j]);
+    int page0 = 0;
+    if constexpr (PAGED) {
+      // the item's page ids into LDS by four-byte cache-to-LDS loads, all in
+      // flight together (lanes past the last page repeat it)
+      page0 = item.tok_begin >> a.page_shift;
+      const int npages = min(((item.tok_end - 1) >> a.page_shift) - page0 + 1, kItemPagesBf16);
+      const int32_t* psrc = a.page_indices + seq_base + page0;
+      const uint32_t pm0 = lds_u32(&sh.pages[0]);
+      for (int j = wave; 64 * j < npages; j += kWaves) dma_u32(psrc + min(64 * j + lane, npages - 1), pm0 + 256 * j);
+      wait_loads<0>();
+      lds_barrier();
+    }
     auto issue = [&](int n) {  // tile n into buffer n % 2
       const int tok0 = item.tok_begin + n * kTileTokens;
       const int lim = tok_last - tok0;
-      const uint8_t* rows = a.kv + (seq_base + tok0) * (int64_t)(2 * kQkDim);
       const uint32_t m0 = lds_u32(&tiles.tile[n & 1][0]) + 1024 * l0;
       const uint8_t* src[19];
 #pragma unroll
-      for (int j = 0; j < 19; ++j)
-        src[j] = rows + min(srow[j], lim) * (2 * kQkDim) + 16 * scol[j] - (j < 18 ? 1024 * (j & 3) : 0);
+      for (int j = 0; j < 19; ++j) {
+        int64_t row;
+        if constexpr (PAGED) {
+          const int tok = tok0 + min(srow[j], lim);
+          const uint32_t page = (uint32_t)sh.pages[(tok >> a.page_shift) - page0];
+          row = (int64_t)((page << a.page_shift) + (uint32_t)(tok & ((1 << a.page_shift) - 1)));
+        } else {
+          row = seq_base + tok0 + min(srow[j], lim);
+        }
+        src[j] = a.kv + row * (2 * kQkDim) + 16 * scol[j] - (j < 18 ? 1024 * (j & 3) : 0);
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q) dma_group<4>(src + 4 * q, m0 + 4096 * q);
       dma_group<2>(src + 16, m0 + 4096 * 4);

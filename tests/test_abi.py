@@ -198,11 +198,13 @@ def test_planner_small_batch_long_context_fills_the_gpu(B, fmt):
 
 def test_planner_paged_items_fit_the_staged_pages(B):
     """A paged item's page ids are staged in LDS by the split kernel (2560 for
-    fp8, 1536 for MXFP4, an item's first and last page possibly partial), so
-    the planner caps paged items at (pages - 2) * page_size tokens, in whole
-    tiles; uniform batches plan the same items as a contiguous cache."""
+    fp8, 1536 for MXFP4, 2048 for bf16, an item's first and last page possibly
+    partial), so the planner caps paged items at (pages - 2) * page_size
+    tokens, in whole tiles (128 tokens, 64 for bf16); uniform batches plan the
+    same items as a contiguous cache."""
     ps = 2
-    for fmt, pages in (("fp8", 2560), ("mxfp4", 1536)):
+    for fmt, pages in (("fp8", 2560), ("mxfp4", 1536), ("bf16", 2048)):
+        tile = 64 if fmt == "bf16" else 128
         lens = [100000, 5]
         npg = [(n + ps - 1) // ps for n in lens]
         indptr = np.concatenate([[0], np.cumsum(npg)]).astype(np.int32)
@@ -210,7 +212,7 @@ def test_planner_paged_items_fit_the_staged_pages(B):
         items, slots, _ = B.mla_decode_plan_preview(indptr, last, page_size=ps, split_override=1,
                                                     kv_dtype=fmt)
         sizes = items[:, 2] - items[:, 1]
-        assert sizes.max() <= (pages - 2) * ps // 128 * 128, fmt
+        assert sizes.max() <= (pages - 2) * ps // tile * tile, fmt
         assert sizes.max() > (pages - 2) * ps // 2, fmt
         _check_cover(items.tolist(), lens, slots)
     indptr = np.arange(65, dtype=np.int32) * 4096  # 64 x 8192 tokens in 2-token pages
