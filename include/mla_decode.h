@@ -40,13 +40,14 @@
  * output (the item is the whole sequence) or a normalised partial and its
  * log-sum-exp; the partials of every split sequence are merged by their
  * log-sum-exp weights (727205 `mla_rd`, 700955 `reduce_lse_v71`, 599694
- * `_flash_fp8_split_s2`).  For an fp8 or MXFP4 cache and sequences of
- * different lengths, the planner cuts the batch into bins of about equal
- * work, one per resident workgroup, and a workgroup runs the items of its
- * bin in turn (a sequence may span bins).  The merge is a second kernel launch, except for an
- * fp8 or MXFP4 cache with a plan whose items differ in length (at most 12 per
- * sequence): there the item of a sequence that finishes last merges its
- * partials, so each call is one launch.  No merge runs when no sequence is
+ * `_flash_fp8_split_s2`).  For sequences of different lengths the planner
+ * cuts the batch into bins of about equal work, one per resident workgroup,
+ * and a workgroup runs the items of its bin in turn (a sequence may span
+ * bins).  The merge is a second kernel launch, except for a plan whose items
+ * differ in length (at most 12 per sequence): there the item of a sequence
+ * that finishes last merges its partials, so each call is one launch (an
+ * MXFP4 cache whose scale array or stride is odd always takes the second
+ * launch, one item per workgroup).  No merge runs when no sequence is
  * split.  The completion counters of that merge belong to the plan: runs of
  * one handle must not overlap (on any streams), and a plan must not be made
  * while a run of the handle is still executing.
@@ -139,9 +140,9 @@ mla_status mla_decode_plan(mla_decode_t h, int batch, const int32_t* kv_indptr_h
  * token, partial slot or -1 when the item is the whole sequence or -2 for the
  * item that writes an empty sequence's zero output, and the workgroup that
  * runs it) in launch order, and the number of items, partial slots and the
- * workspace bytes.  For fp8 and MXFP4 caches a ragged batch is cut into bins
- * of about equal work, one per resident workgroup, whose items one
- * workgroup runs in turn; otherwise each item has a workgroup of its own.
+ * workspace bytes.  A ragged batch is cut into bins of about equal work, one
+ * per resident workgroup, whose items one workgroup runs in turn; otherwise
+ * each item has a workgroup of its own.
  * Returns MLA_ERR_INVALID_ARG when max_items is too small (num_items still
  * set).
  */

@@ -33,7 +33,7 @@ struct mla_decode_s {
   int64_t total_tokens = 0;
   size_t workspace_bytes = 0;
   int num_merge = 0;  // sequences with >= 2 partials
-  bool fused_merge = false;  // the fp8 kernel merges them itself (no merge launch)
+  bool fused_merge = false;  // the split kernel merges them itself (no merge launch)
   int uniform_splits = 0, uniform_chunk = 0, uniform_len = 0, uniform_base = 0;
   int num_bins = 0;  // > 0: binned plan (see PlanOut)
   bool row_pairs = false;  // the fp8 kernel runs pairs of query rows (see PlanOut)
@@ -196,7 +196,7 @@ static int64_t item_pages(int kv_dtype) {
   return kv_dtype == MLA_KV_FP8_E4M3 ? kItemPagesFp8 : kv_dtype == MLA_KV_MXFP4 ? kItemPagesMxfp4 : kItemPagesBf16;
 }
 
-// Bins for a ragged batch (fp8 and MXFP4 kernels, which run the items of a
+// Bins for a ragged batch (the split kernels, which run the items of a
 // bin one after the other).  One item per workgroup leaves the compute units
 // that drew the short items idle while the long ones finish (a quarter of
 // the time on lengths spread evenly over 1024..8192); here the sequences,
@@ -204,13 +204,14 @@ static int64_t item_pages(int kv_dtype) {
 // about equal cost, a piece costing its tokens plus a fixed cost for its
 // start and finish (measured with wall-clock stamps around the items: about
 // 200 tokens of streaming for the fp8 kernel, more for the MXFP4 one, whose
-// best value on ragged batches was 288).  A sequence cut across bins becomes
+// best value on ragged batches was 288; the bf16 kernel streams half as many
+// tokens in the same time, so its fixed cost is about half the fp8 one in
+// tokens, 96).  A sequence cut across bins becomes
 // several items, merged like any split.  No piece is shorter than kMinPiece
 // unless its sequence is.
 constexpr int64_t kMinPiece = 256;
-// (0: the format's kernel runs one item per workgroup, no bins)
 static int64_t bin_piece_cost(int kv_dtype) {
-  return kv_dtype == MLA_KV_MXFP4 ? 288 : kv_dtype == MLA_KV_FP8_E4M3 ? 192 : 0;
+  return kv_dtype == MLA_KV_MXFP4 ? 288 : kv_dtype == MLA_KV_FP8_E4M3 ? 192 : 96;
 }
 
 struct Piece {
@@ -682,8 +683,7 @@ mla_status plan_impl(mla_decode_t h, int batch, const int32_t* qo_indptr_host, c
   // that item; it pays where items finish at different times (ragged plans),
   // while a uniform plan, whose items all finish together, merges faster in
   // the merge kernel.
-  h->fused_merge = h->kv_dtype != MLA_KV_BF16 && plan.max_splits <= mla::kFusedMergeMaxSlots &&
-                   plan.uniform_splits == 0;
+  h->fused_merge = plan.max_splits <= mla::kFusedMergeMaxSlots && plan.uniform_splits == 0;
   h->uniform_splits = plan.uniform_splits;
   h->uniform_chunk = plan.uniform_chunk;
   h->uniform_len = plan.uniform_len;

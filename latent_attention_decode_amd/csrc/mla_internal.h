@@ -120,12 +120,13 @@ struct Stage1Args {
   int uniform_chunk;
   int uniform_len;
   int uniform_base;             // kv_indptr[0]
-  // Non-null: the fp8 kernel merges the partials itself.  counters[j] counts
+  // Non-null: the split kernel merges the partials itself.  counters[j] counts
   // the finished items of merge job j (zero between calls); the item that
   // finishes last reads the other partials of its sequence and writes the
   // output, so no merge kernel runs.
   int* counters;
-  // Non-null (fp8 and MXFP4 kernels): workgroup k runs items
+  // Non-null (every split kernel but the MXFP4 one for odd scale addresses):
+  // workgroup k runs items
   // bins[k] .. bins[k + 1] - 1, one after the other; null: workgroup k runs
   // item k.  The bins of a ragged batch carry about equal work.
   const int32_t* bins;

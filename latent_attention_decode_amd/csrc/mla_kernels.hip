@@ -52,11 +52,9 @@ namespace {
 // format traits
 // ---------------------------------------------------------------------------
 template <int F> struct Traits;
-template <> struct Traits<kBf16> {
+template <> struct Traits<kBf16> {  // streamed by cache-to-LDS loads (DmaRing)
   static constexpr int kRowBytes = 1152;
   static constexpr int kLdsPitch = 1168;  // bf16 elements + 16 B
-  static constexpr int kBuffers = 1;
-  static constexpr bool kPrefetch = false;  // a bf16 tile is 72 registers per lane
 };
 template <> struct Traits<kMxfp4> {
   static constexpr int kRowBytes = 288;   // e2m1 nibbles; scales live apart
@@ -332,16 +330,14 @@ __device__ __forceinline__ void attend_tile(Stage1Lds<F, PAGED>& sh, const uint8
   }
 }
 
-template <int F, bool PAGED>
-__global__ __launch_bounds__(kStage1Threads, 2) void mla_stage1(Stage1Args a) {
-  constexpr bool kDma = F == kBf16;
-  __shared__ __attribute__((aligned(16))) typename std::conditional<kDma, DmaRing, Stage1Tiles<F>>::type tiles;
-  __shared__ __attribute__((aligned(16))) Stage1Lds<F, PAGED> sh;
+template <int F>
+using Stage1Buffers = typename std::conditional<F == kBf16, DmaRing, Stage1Tiles<F>>::type;
 
-  const WorkItem item = a.uniform_splits
-                            ? uniform_item(xcd_block(blockIdx.x, gridDim.x), a.uniform_splits, a.uniform_chunk,
-                                           a.uniform_len, a.uniform_base)
-                            : a.items[blockIdx.x];
+// One work item: tokens [tok_begin, tok_end) of one sequence.
+template <int F, bool PAGED>
+__device__ __forceinline__ void stage1_item(const Stage1Args& a, const WorkItem& item, Stage1Buffers<F>& tiles,
+                                            Stage1Lds<F, PAGED>& sh) {
+  constexpr bool kDma = F == kBf16;
   const int tid = threadIdx.x;
   if (item.slot == WorkItem::kEmpty) {  // empty sequence: its output is zero
     uint4* dst = reinterpret_cast<uint4*>(a.out + (int64_t)item.batch * kNumHeads * kVDim);
@@ -478,19 +474,29 @@ __global__ __launch_bounds__(kStage1Threads, 2) void mla_stage1(Stage1Args a) {
   if (g == 0) sh.lsum[wave][r16] = l_w;
   __syncthreads();
   const float L = (sh.lsum[0][r16] + sh.lsum[1][r16]) + (sh.lsum[2][r16] + sh.lsum[3][r16]);
-  const float f = 1.0f / L;
-  if (item.slot < 0) {
-    uint16_t* dst = a.out + ((int64_t)b * kNumHeads + r16) * kVDim + dv0 + 4 * g;
-#pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      const f32x4 val = o[v] * f;
-      *reinterpret_cast<uint2*>(dst + 16 * v) =
-          uint2{pack_bf16x2(val[0], val[1]), pack_bf16x2(val[2], val[3])};
-    }
-    return;
+  finish_item<8>(a, item, tid, wave, 0, lane, o, 1.0f / L, m_ref + __log2f(L));
+}
+
+// A workgroup runs one item, or with bins (bf16 cache) the items of bin
+// blockIdx.x in order (see Stage1Args).  Between two items every load and
+// store of the first is complete and every wave is past it, so the next may
+// reuse LDS.
+template <int F, bool PAGED>
+__global__ __launch_bounds__(kStage1Threads, F == kBf16 ? 1 : 2) void mla_stage1(Stage1Args a) {
+  __shared__ __attribute__((aligned(16))) Stage1Buffers<F> tiles;
+  __shared__ __attribute__((aligned(16))) Stage1Lds<F, PAGED> sh;
+  int i = a.bins ? a.bins[blockIdx.x] : (int)blockIdx.x;
+  const int i_end = a.bins ? a.bins[blockIdx.x + 1] : i + 1;
+  while (i < i_end) {
+    const WorkItem item = a.uniform_splits
+                              ? uniform_item(xcd_block(blockIdx.x, gridDim.x), a.uniform_splits, a.uniform_chunk,
+                                             a.uniform_len, a.uniform_base)
+                              : a.items[i];
+    stage1_item<F, PAGED>(a, item, tiles, sh);
+    if (++i == i_end) break;
+    wait_loads<0>();
+    lds_barrier();
   }
-  store_partial(a.part_o, item.slot, wave, lane, o, f);
-  if (tid < kNumHeads) a.part_lse[(int64_t)item.slot * kNumHeads + tid] = m_ref + __log2f(L);
 }
 
 // ---------------------------------------------------------------------------
@@ -668,7 +674,7 @@ static hipError_t launch(const void* fn, dim3 grid, dim3 block, void** params, h
 }
 
 bool stage1_dedicated(int fmt, const Stage1Args& a) {
-  if (fmt == kFp8) return true;
+  if (fmt == kFp8 || fmt == kBf16) return true;
   if (fmt == kMxfp4) return ((a.scale_stride | (int64_t)(uintptr_t)a.kv_mx_scales) & 1) == 0;
   return false;
 }

@@ -294,17 +294,15 @@ def test_planner_bins_respect_the_page_cap_and_split_limit(B):
             assert np.bincount(items[:, 0]).max() <= 32
 
 
-def test_planner_bins_hold_empty_sequences_and_no_bf16(B):
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4", "bf16"])
+def test_planner_bins_hold_empty_sequences(B, fmt):
     """Empty sequences of a binned batch get their zero-output item in some
-    bin; bf16 caches (whose kernel runs one item per workgroup) get no bins."""
+    bin, for every cache format (every split kernel runs bins)."""
     lens = np.array([0, 5000, 0, 300] + [4000, 1500] * 100 + [0])
     indptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    items, slots, _ = B.mla_decode_plan_preview(indptr, num_cus=64, blocks_per_cu=1, kv_dtype="fp8")
+    items, slots, _ = B.mla_decode_plan_preview(indptr, num_cus=64, blocks_per_cu=1, kv_dtype=fmt)
     _check_cover(items.tolist(), lens.tolist(), slots)
     assert items[:, 4].max() + 1 <= 64 and len(items) > 64
-    items, slots, _ = B.mla_decode_plan_preview(indptr, num_cus=64, blocks_per_cu=1, kv_dtype="bf16")
-    _check_cover(items.tolist(), lens.tolist(), slots)
-    assert np.all(items[:, 4] == np.arange(len(items)))
 
 
 def _check_cover_multi(items, lens, qls, slots):
@@ -339,8 +337,7 @@ def _check_cover_multi(items, lens, qls, slots):
 def test_planner_multi_token_rows(B, fmt, lens, qls, ps):
     """Multi-token plans: every query row covers exactly its causal range; the
     copies of an item for a sequence's query tokens go to workgroups launched
-    together: on one XCD (workgroups 8 apart) for the fp8 / MXFP4 kernels,
-    which run bins, next to each other for the bf16 kernel."""
+    together on one XCD (bins 8 apart)."""
     lens, qls = np.array(lens), np.array(qls)
     pages = (lens + ps - 1) // ps
     indptr = np.concatenate([[0], np.cumsum(pages)]).astype(np.int32)
@@ -359,10 +356,7 @@ def test_planner_multi_token_rows(B, fmt, lens, qls, ps):
         rs = sorted(r for r, _ in lst)
         assert rs == list(range(qo[b] + qls[b] - len(rs), qo[b] + qls[b])), (b, t0, rs)
         wgs = sorted(w for _, w in lst)
-        if fmt == "bf16":
-            assert wgs[-1] - wgs[0] <= qls.max() - 1, (b, t0, wgs)
-        else:
-            assert len({w % 8 for w in wgs}) == 1 and wgs[-1] - wgs[0] <= 8 * (qls.max() - 1), (b, t0, wgs)
+        assert len({w % 8 for w in wgs}) == 1 and wgs[-1] - wgs[0] <= 8 * (qls.max() - 1), (b, t0, wgs)
 
 
 def test_planner_multi_token_single_is_the_plain_plan(B):
@@ -393,7 +387,7 @@ def test_planner_multi_token_rejects_bad_qo_indptr(B, qo, why):
 
 from hypothesis import given, settings, strategies as st  # noqa: E402
 
-PAGE_CAP = {"fp8": 2560, "mxfp4": 1536}
+PAGE_CAP = {"fp8": 2560, "mxfp4": 1536, "bf16": 2048}
 
 
 @settings(max_examples=150, deadline=None)
@@ -437,7 +431,6 @@ def test_planner_properties(B, lens, fmt, ps, split, cus, bpc, data):
         assert np.all(lastp - first + 1 <= PAGE_CAP[fmt])
     groups = items[:, 4].max() + 1
     if not np.array_equal(items[:, 4], np.arange(len(items))):  # bins (possibly empty ones)
-        assert fmt != "bf16"
         if qls is None:
             assert groups <= cus * bpc
         else:  # one group per parent item (or parent bin) and query token, 8 groups to a block

@@ -163,14 +163,14 @@ def _binned_lens(kind):
 @pytest.mark.parametrize("kind", ["mixed", "one_long"])
 @pytest.mark.parametrize("fmt,ps,shuffled,stride", [
     ("fp8", 1, False, 18), ("fp8", 2, True, 18), ("mxfp4", 1, False, 18), ("mxfp4", 16, True, 18),
-    ("mxfp4", 1, False, 19),
+    ("mxfp4", 1, False, 19), ("bf16", 1, False, 18), ("bf16", 4, True, 18),
 ])
 def test_binned_ragged_batch(B, oracle_mod, kind, fmt, ps, shuffled, stride):
-    """A ragged batch large enough for bins (fp8 / MXFP4: one bin of about
-    equal work per resident workgroup, whose items one workgroup runs in
-    turn, a sequence possibly spanning bins): every output against the
-    oracle, and a repeat bit for bit.  With odd MXFP4 scale strides the
-    bf16-decoding kernel runs the same items one per workgroup."""
+    """A ragged batch large enough for bins (one bin of about equal work per
+    resident workgroup, whose items one workgroup runs in turn, a sequence
+    possibly spanning bins): every output against the oracle, and a repeat
+    bit for bit.  With odd MXFP4 scale strides the bf16-decoding kernel runs
+    the same items one per workgroup."""
     lens = _binned_lens(kind)
     case = synth.make_case(fmt, lens, seed=44, page_size=ps, shuffle_pages=shuffled, scale_stride=stride)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
