@@ -240,24 +240,25 @@ def test_multi_token_pairs_binned(B, oracle_mod):
     assert np.array_equal(a, b)
 
 
-def test_multi_token_binned_ragged_batch(B, oracle_mod):
+@pytest.mark.parametrize("fmt", ["fp8", "bf16"])
+def test_multi_token_binned_ragged_batch(B, oracle_mod, fmt):
     """A ragged batch large enough for bins, with 1..4 query tokens per
     sequence: the copies of each bin for the query tokens run side by side;
     sampled sequences against the oracle, and a repeat bit for bit."""
     rng = np.random.default_rng(51)
     lens = rng.integers(600, 4000, 96).tolist()
     qls = rng.integers(1, 5, 96).tolist()
-    case = synth.make_case("fp8", lens, seed=51, page_size=2, shuffle_pages=True, q_lens=qls)
+    case = synth.make_case(fmt, lens, seed=51, page_size=2, shuffle_pages=True, q_lens=qls)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     items, _, _ = B.mla_decode_plan_preview(case.kv_indptr, case.kv_last_page_len, page_size=2, num_cus=cus,
-                                            blocks_per_cu=1, kv_dtype="fp8", qo_indptr_host=case.qo_indptr)
+                                            blocks_per_cu=1, kv_dtype=fmt, qo_indptr_host=case.qo_indptr)
     note(f"multi binned: {len(items)} items, {items[:, 4].max() + 1} workgroups")
     assert items[-1, 4] < len(items) - 1  # bins
     a, b = run_gpu(B, case, repeats=2)
     sample = [0, 17, 50, 95]
     ref = oracle_out(oracle_mod, case, batches=sample)
     rows = [r for s in sample for r in range(case.qo_indptr[s], case.qo_indptr[s + 1])]
-    check_close(a[rows], ref[rows], "fp8", "multi binned")
+    check_close(a[rows], ref[rows], fmt, f"multi binned {fmt}")
     assert np.all(np.isfinite(a)) and np.array_equal(a, b)
 
 
