@@ -293,6 +293,8 @@ CONFIGS = {
     # submission 727205 reports its split kernel's time for) and in fp8
     "bs256_kv8192_mxfp4": ("mxfp4", 256, 8192, 1, False, 1009),
     "bs256_kv8192_fp8": ("fp8", 256, 8192, 1, False, 1010),
+    # a bf16 cache at a serving size (the listed bf16 case is 4 x 1024)
+    "bs64_kv8192_bf16": ("bf16", 64, 8192, 1, False, 1011),
     # multi-token decode: every sequence has q query tokens (its last q positions)
     "bs64_kv8192_q2_fp8": ("fp8", 64, 8192, 1, False, 1007, 2),
     "bs16_kv8192_q4_fp8": ("fp8", 16, 8192, 1, False, 1008, 4),
