@@ -271,6 +271,8 @@ EXTREMES = [
     ("16 x 2048 MXFP4, merge in 8 parts", "mxfp4", [2048] * 16, 1),
     ("2048 sequences of 0..64 tokens", "fp8", np.random.default_rng(60).integers(0, 65, 2048).tolist(), 1),
     ("1024-token pages", "mxfp4", [5000, 1024, 1, 2047], 1024),
+    ("1024-token pages, bf16", "bf16", [5000, 1024, 1, 2047, 0], 1024),
+    ("a 9000-token bf16 sequence in 2-token pages, split over many CUs", "bf16", [9000, 3], 2),
 ]
 
 
