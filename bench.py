@@ -2,7 +2,8 @@
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
-A step is one decode call (split stage 1 + LSE merge kernel) over one batch
+A step is one decode call (the split kernel, plus the LSE merge kernel when
+the plan needs one) over one batch
 of seeded synthetic inputs already resident in HBM; the split plan is made
 once beforehand (reported as plan_us).  Every timed step is cold: the steps
 cycle through copies of the inputs totalling at least 1 GiB, so no step finds
