@@ -457,6 +457,29 @@ def test_two_handles_on_two_streams(B, oracle_mod):
         db.close()
 
 
+@pytest.mark.parametrize("fmt", synth.FORMATS)
+def test_replanning_one_handle(B, oracle_mod, fmt):
+    """One handle planned again and again for batches of other shapes (uniform with the
+    merge kernel, ragged with bins and the in-kernel merge, a single item, empty
+    sequences, more query rows): every run matches the oracle, so no state of an earlier
+    plan (work list, completion counters, bins) leaks into a later one."""
+    shapes = [([2048] * 8, None), (list(range(300, 300 + 150 * 60, 150)) + [0, 0], None), ([77], None),
+              ([0, 5, 1200], None), ([900, 2500, 40], [2, 1, 3]), ([2048] * 8, None)]
+    dec = B.MlaDecode(fmt)
+    try:
+        for k, (lens, qls) in enumerate(shapes):
+            case = synth.make_case(fmt, lens, seed=200 + k, q_lens=qls)
+            t = B.case_to_device(case)
+            dec.plan(case.kv_indptr, None, 0, case.qo_indptr)
+            out = torch.full((case.rows, 16, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
+            dec.run(t["q"], t["kv"], t["kv_scales"], t["kv_indptr"], out)
+            torch.cuda.synchronize()
+            check_close(out.float().cpu().numpy().astype(np.float64), oracle_out(oracle_mod, case), fmt,
+                        f"replan {fmt} shape {k}")
+    finally:
+        dec.close()
+
+
 def test_run_validates_arguments(B):
     """Every malformed run is refused with a status and a message before anything is
     launched; the handle still runs correctly afterwards."""
