@@ -693,8 +693,9 @@ hipError_t launch_stage1(int fmt, bool paged, bool row_pairs, const Stage1Args& 
 }
 
 int merge_parts(int num_merge_seqs) {
-  // 4 parts down to 32 jobs, then up to 32 parts for the smallest batches
-  if (num_merge_seqs >= 32) return 4;
+  // 4 parts down to 64 jobs, then up to 32 parts for the smallest batches
+  // (32 sequences of 8 partials: 8 parts 31.9-32.2 us a call, 4 parts 32.4-32.5)
+  if (num_merge_seqs >= 64) return 4;
   if (num_merge_seqs >= 16) return 8;
   if (num_merge_seqs >= 8) return 16;
   return 32;
