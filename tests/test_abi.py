@@ -100,6 +100,8 @@ def test_run_rejects_wrong_tensor_types_and_shapes(B):
     for qq, oo, ii, msg in bad:
         with pytest.raises(ValueError, match=msg):
             B.mla_decode_run(None, qq, None, None, ii, oo)
+        with pytest.raises(ValueError, match=msg):  # a prepared run checks the same, once
+            B.PreparedRun(None, qq, None, None, ii, oo)
 
 
 def _check_cover(items, lens, slots):
