@@ -207,6 +207,31 @@ __device__ __forceinline__ f32x4 mfma_fp8(fp8x8 a, fp8x8 b, f32x4 c) {
 __device__ __forceinline__ f32x4 mfma_fp8_k128(fp8x32 a, fp8x32 b, f32x4 c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
+// The same with B block scale 2^(sb - 127) (e8m0 in the low byte of sb):
+// the lanes of group g give the scale of k-values 32g..32g+31 of their column.
+__device__ __forceinline__ f32x4 mfma_fp8_k128_sb(fp8x32 a, fp8x32 b, f32x4 c, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, sb);
+}
+
+// Softmax weights on the MX instruction.  The weights of one 32-token k-block
+// of a P.V step are written relative to that block's own maximum: with F =
+// floor(block maximum) (log2 units), a token of logit x is stored as the e4m3
+// hi + lo pair of 2^(x - F + 7), in [0, 256), and the block's B scale
+// 2^(F - 7 - m_ref) restores 2^(x - m_ref).  The running maximum m_ref is kept
+// integral, so that the scale is an exact power of two and the stored weights
+// never depend on it.  Relative to the block's largest weight, the pair is
+// exact to about 8 significant bits down to 2^-9 and off by at most 2^-18
+// below, whatever the spread of the logits across blocks.
+__device__ __forceinline__ float weight_block_floor(float block_max) {
+  return block_max == kNegInf ? 0.0f : floorf(block_max);
+}
+// e8m0 code of that B scale (a block with no valid token has zero weights and
+// takes 2^0; a block below 2^-127 of the running maximum is clamped there).
+__device__ __forceinline__ int weight_block_scale(float block_max, float m_ref) {
+  if (block_max == kNegInf) return 127;
+  const int c = 127 + (int)floorf(block_max) - 7 - (int)m_ref;
+  return min(max(c, 0), 254);
+}
 
 __device__ __forceinline__ fp8x32 join16(u32x4 a, u32x4 b) {
   return fp8x32{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};

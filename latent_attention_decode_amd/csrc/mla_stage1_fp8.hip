@@ -20,7 +20,8 @@ namespace {
 // ---------------------------------------------------------------------------
 // Both contractions run straight on the cached e4m3 codes (nothing is
 // decoded), on the gfx950 MX matrix instruction v_mfma_scale_f32_16x16x128_
-// f8f6f4 (fp8 x fp8, unit block scales), which takes 128 k-values per step,
+// f8f6f4 (fp8 x fp8; unit block scales for the scores), which takes 128
+// k-values per step,
 // and on v_mfma_f32_16x16x32_fp8_fp8 for the 64 rope columns.  The other
 // operand is written as a sum of two e4m3 numbers, hi + lo, and each product
 // is taken twice:
@@ -30,8 +31,11 @@ namespace {
 //     lo exactly whenever it is a normal e4m3 number (|scaled q| >= 1/4, i.e.
 //     every element above 1/1024 of the row maximum; smaller ones are off by at
 //     most 2^-10 in scaled units).  2^-s_h is folded into the score scale.
-//   * the softmax weights p <= 2^8 (lazy maximum) are split the same way,
-//     which keeps about 8 significant bits, as many as a bf16 weight has.
+//   * the softmax weights are split the same way, each 32-token k-block of the
+//     P.V step relative to its own maximum, which returns as the block's B
+//     scale (see weight_block_scale): about 8 significant bits per weight, as
+//     a bf16 weight has, and no weight lost to the range of e4m3 however far
+//     the logits of different blocks lie apart.
 //
 // Data movement: every byte of the item's cache rows goes HBM -> LDS by
 // cache-to-LDS loads (global_load_lds_dwordx4), in a ring of two 128-token
@@ -48,12 +52,14 @@ namespace {
 // the kernel's).
 //
 // Per tile, with wave w:
-//   1. S^T[token, head] = K (Qhi + Qlo)^T for tokens 32w..32w+31 (two 16-token
-//      row blocks), all 576 columns; the query stays in registers;
-//   2. softmax in the log2 domain with a lazy maximum shared by the four
-//      waves: it moves (and O and the sums are rescaled) only when a tile
-//      maximum passes it by more than 8, so p <= 2^8; each wave writes its
-//      e4m3 hi/lo weights P^T to LDS;
+//   1. S^T[token, head] = K (Qhi + Qlo)^T for the 32 tokens of k-block w of
+//      the P.V step (two 16-token row blocks, tokens blk_base(w) + 32s +
+//      0..15), all 576 columns; the query stays in registers;
+//   2. softmax in the log2 domain; each wave writes the e4m3 hi/lo weights
+//      of its block, relative to the block's maximum, to P^T in LDS.  The
+//      running maximum is shared by the four waves and lazy: it moves (to an
+//      integer, and O and the sums are rescaled by a power of two) only when
+//      a tile maximum passes it by more than 8;
 //   3. O^T[dim, head] += V^T (Phi + Plo)^T for dims 128w..128w+127 over all
 //      128 tokens, one MX step per 16 columns; V^T comes from the tile through
 //      the transposing LDS read ds_read_b64_tr_b8.
@@ -107,6 +113,25 @@ constexpr bool q_slots_are_a_permutation() {
   return true;
 }
 static_assert(tile_slots_are_a_permutation() && q_slots_are_a_permutation(), "slot maps");
+
+// Tokens of k-block j of a 128-token P.V step: blk_base(j) + 0..15 and
+// blk_base(j) + 32..47.  P^T and V^T give lane group g the tile tokens
+// 32g..32g+31 in its operand bytes 0..31, and the MX instruction's fp8 operand
+// holds k-values 16g + b in bytes b < 16 and 64 + 16g + b - 16 in bytes
+// 16..31; a block scale covers k-values 32j..32j+31.  Wave w scores the
+// tokens of k-block w, so the block's maximum is the wave's own.
+__host__ __device__ constexpr int blk_base(int j) { return 64 * (j & 1) + 16 * (j >> 1); }
+constexpr bool blocks_match_operand_layout() {
+  for (int tok = 0; tok < kCTile; ++tok) {
+    const int g = tok / 32, b = tok % 32;
+    const int k = b < 16 ? 16 * g + b : 64 + 16 * g + (b - 16);
+    const int j = k / 32;
+    const int d = tok - blk_base(j);
+    if (!((d >= 0 && d < 16) || (d >= 32 && d < 48))) return false;
+  }
+  return true;
+}
+static_assert(blocks_match_operand_layout(), "k-blocks of the P.V step");
 
 // LDS of the kernel for groups of up to NR query rows of one sequence (NR
 // = 2 pairs two query tokens of a multi-token plan; it then stages fewer
@@ -331,13 +356,18 @@ __device__ __forceinline__ void fp8_item(const Stage1Args& a, const WorkItem* it
   }
 
   // LDS byte offsets of this lane's reads within a tile.  Score rows
-  // 32w + 16s + r16 have chunk_swz(32w + r16) whatever s; value rows
-  // 32g + 8q + (r16 >> 1) have chunk_swz(32g + 8(q & 1) + (r16 >> 1)).
-  const int ksw = chunk_swz(32 * wave + r16);
-  const int k_row = (32 * wave + r16) * kQkDim;
-  const int k_off0 = k_row + 16 * ((2 * g) ^ ksw);      // chunk 8K + 2g
-  const int k_off1 = k_row + 16 * ((2 * g + 1) ^ ksw);  // chunk 8K + 2g + 1
-  const int k_offr = k_row + 16 * (32 + (g ^ ksw));     // chunk 32 + g
+  // blk_base(w) + 32s + r16 (s = 0, 1); value rows 32g + 8q + (r16 >> 1) have
+  // chunk_swz(32g + 8(q & 1) + (r16 >> 1)).
+  const int base = blk_base(wave);
+  int k_off0[2], k_off1[2], k_offr[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int row = base + 32 * s + r16;
+    const int ksw = chunk_swz(row);
+    k_off0[s] = row * kQkDim + 16 * ((2 * g) ^ ksw);      // chunk 8K + 2g
+    k_off1[s] = row * kQkDim + 16 * ((2 * g + 1) ^ ksw);  // chunk 8K + 2g + 1
+    k_offr[s] = row * kQkDim + 16 * (32 + (g ^ ksw));     // chunk 32 + g
+  }
   int v_off[2][4];  // [q % 2][v % 4]; + 64 (v / 4) + 4608 (q & ~1); column chunk 8w + v
 #pragma unroll
   for (int qp = 0; qp < 2; ++qp) {
@@ -367,7 +397,7 @@ __device__ __forceinline__ void fp8_item(const Stage1Args& a, const WorkItem* it
     if (more) issue(t + 1, 0);
     const uint8_t* cur = &sh.tile[t & (kCRing - 1)][0];
 
-    // ---- scores of tokens 32w + 16s + (0..15), s = 0, 1 ----
+    // ---- scores of tokens base + 32s + (0..15), s = 0, 1 ----
     f32x4 sacc[NR][2][2];  // [row][s][hi/lo]
 #pragma unroll
     for (int r = 0; r < NR; ++r)
@@ -379,9 +409,8 @@ __device__ __forceinline__ void fp8_item(const Stage1Args& a, const WorkItem* it
     for (int K = 0; K < 4; ++K) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const int ro = s * 16 * kQkDim + 128 * K;
-        const fp8x32 ka = join16(*reinterpret_cast<const u32x4*>(cur + k_off0 + ro),
-                                 *reinterpret_cast<const u32x4*>(cur + k_off1 + ro));
+        const fp8x32 ka = join16(*reinterpret_cast<const u32x4*>(cur + k_off0[s] + 128 * K),
+                                 *reinterpret_cast<const u32x4*>(cur + k_off1[s] + 128 * K));
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
           sacc[r][s][0] = mfma_fp8_k128(ka, qh[r][K], sacc[r][s][0]);
@@ -392,7 +421,7 @@ __device__ __forceinline__ void fp8_item(const Stage1Args& a, const WorkItem* it
     }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(cur + k_offr + s * 16 * kQkDim);
+      const u32x4 w = *reinterpret_cast<const u32x4*>(cur + k_offr[s]);
       const fp8x8 ka = pack_fp8x8(w[0], w[1]);
       const fp8x8 kb = pack_fp8x8(w[2], w[3]);
 #pragma unroll
@@ -404,41 +433,50 @@ __device__ __forceinline__ void fp8_item(const Stage1Args& a, const WorkItem* it
       }
     }
 
-    // ---- softmax: x[r][s][i] is token 32w + 16s + 4g + i of head r16 ----
-    float x[NR][2][4];
-    float p[NR][2][4];
+    // ---- softmax: x[s][i] is token base + 32s + 4g + i of head r16 ----
+    // The wave's tokens are k-block w of the P.V step: their weights are
+    // written relative to the block's own maximum (weight_block_scale).
+    float psum[NR];  // this lane's weights as written, in units of 2^(F - 7 - m_ref)
+    float fblk[NR];  // F = floor of the wave's block maximum (0 if all masked)
+    bool live[NR];   // the block has a valid token
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
+      float x[2][4];
       float tmax = kNegInf;
 #pragma unroll
       for (int s = 0; s < 2; ++s)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          x[r][s][i] = (sacc[r][s][0][i] + sacc[r][s][1][i]) * xscale[r];
-          if (tok0 + 32 * wave + 16 * s + 4 * g + i > tok_last_r[r]) x[r][s][i] = kNegInf;
-          tmax = fmaxf(tmax, x[r][s][i]);
+          x[s][i] = (sacc[r][s][0][i] + sacc[r][s][1][i]) * xscale[r];
+          if (tok0 + base + 32 * s + 4 * g + i > tok_last_r[r]) x[s][i] = kNegInf;
+          tmax = fmaxf(tmax, x[s][i]);
         }
       tmax = xor_max_groups(tmax);
       if (g == 0) sh.red_m[r][r16][wave] = tmax;
-      const float mr = (m_ref[r] == kNegInf) ? 0.0f : m_ref[r];
+      live[r] = tmax != kNegInf;
+      fblk[r] = weight_block_floor(tmax);
+      const float shift = 7.0f - fblk[r];  // x + shift < 8
       uint8_t* const p_hi = &sh.p[r][0][r16][0];
       uint8_t* const p_lo = &sh.p[r][1][r16][0];
+      float ps = 0.f;
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
+        float p[4];
         uint32_t ph, pl;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p[r][s][i] = __builtin_amdgcn_exp2f(x[r][s][i] - mr);
-        split_fp8x4(p[r][s][0], p[r][s][1], p[r][s][2], p[r][s][3], ph, pl);
-        *reinterpret_cast<uint32_t*>(p_hi + 32 * wave + 16 * s + 4 * g) = ph;
-        *reinterpret_cast<uint32_t*>(p_lo + 32 * wave + 16 * s + 4 * g) = pl;
+        for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[s][i] + shift);
+        split_fp8x4(p[0], p[1], p[2], p[3], ph, pl);
+        *reinterpret_cast<uint32_t*>(p_hi + base + 32 * s + 4 * g) = ph;
+        *reinterpret_cast<uint32_t*>(p_lo + base + 32 * s + 4 * g) = pl;
+        ps += (p[0] + p[1]) + (p[2] + p[3]);
       }
+      psum[r] = ps;
     }
     if (more) issue(t + 1, 3);
-    lds_barrier();  // P^T and the tile maxima of all waves
+    lds_barrier();  // P^T and the block maxima of all waves
 
     fp8x32 bh[NR], bl[NR];
-    float tile_max[NR];
-    bool rescale = false;
+    int sb[NR];  // B block scale of k-block g (wave g's tokens) for head r16
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
       const f32x4 maxima = *reinterpret_cast<const f32x4*>(&sh.red_m[r][r16][0]);
@@ -448,56 +486,20 @@ __device__ __forceinline__ void fp8_item(const Stage1Args& a, const WorkItem* it
                      *reinterpret_cast<const u32x4*>(p_hi + 32 * g + 16));
       bl[r] = join16(*reinterpret_cast<const u32x4*>(p_lo + 32 * g),
                      *reinterpret_cast<const u32x4*>(p_lo + 32 * g + 16));
-      tile_max[r] = fmaxf(fmaxf(maxima[0], maxima[1]), fmaxf(maxima[2], maxima[3]));
-      rescale = rescale || __ballot(tile_max[r] > m_ref[r] + kLazyRescale) != 0;
+      const float tile_max = fmaxf(fmaxf(maxima[0], maxima[1]), fmaxf(maxima[2], maxima[3]));
+      // Every wave reads the same maxima, so this branch is uniform.
+      if (__ballot(tile_max > m_ref[r] + kLazyRescale) != 0) {
+        const float m_new = floorf(fmaxf(m_ref[r], tile_max));
+        const float alpha = (m_ref[r] == kNegInf) ? 0.0f : __builtin_ldexpf(1.0f, (int)(m_ref[r] - m_new));
+#pragma unroll
+        for (int v = 0; v < 8; ++v) o[r][v] *= alpha;
+        l_part[r] *= alpha;
+        m_ref[r] = m_new;
+      }
+      if (live[r]) l_part[r] += __builtin_ldexpf(psum[r], (int)fblk[r] - 7 - (int)m_ref[r]);
+      const float bm = g == 0 ? maxima[0] : g == 1 ? maxima[1] : g == 2 ? maxima[2] : maxima[3];
+      sb[r] = weight_block_scale(bm, m_ref[r]);
     }
-    // Every wave reads the same maxima, so this branch is uniform.
-    if (rescale) {
-      bool moved[NR];
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        moved[r] = __ballot(tile_max[r] > m_ref[r] + kLazyRescale) != 0;
-        if (moved[r]) {
-          const float m_new = fmaxf(m_ref[r], tile_max[r]);
-          const float alpha = (m_ref[r] == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(m_ref[r] - m_new);
-#pragma unroll
-          for (int v = 0; v < 8; ++v) o[r][v] *= alpha;
-          l_part[r] *= alpha;
-          m_ref[r] = m_new;
-        }
-      }
-      lds_barrier();  // everyone has read the old P^T
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        if (!moved[r]) continue;
-        uint8_t* const p_hi = &sh.p[r][0][r16][0];
-        uint8_t* const p_lo = &sh.p[r][1][r16][0];
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          uint32_t ph, pl;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) p[r][s][i] = __builtin_amdgcn_exp2f(x[r][s][i] - m_ref[r]);
-          split_fp8x4(p[r][s][0], p[r][s][1], p[r][s][2], p[r][s][3], ph, pl);
-          *reinterpret_cast<uint32_t*>(p_hi + 32 * wave + 16 * s + 4 * g) = ph;
-          *reinterpret_cast<uint32_t*>(p_lo + 32 * wave + 16 * s + 4 * g) = pl;
-        }
-      }
-      lds_barrier();
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        if (!moved[r]) continue;
-        const uint8_t* const p_hi = &sh.p[r][0][r16][0];
-        const uint8_t* const p_lo = &sh.p[r][1][r16][0];
-        bh[r] = join16(*reinterpret_cast<const u32x4*>(p_hi + 32 * g),
-                       *reinterpret_cast<const u32x4*>(p_hi + 32 * g + 16));
-        bl[r] = join16(*reinterpret_cast<const u32x4*>(p_lo + 32 * g),
-                       *reinterpret_cast<const u32x4*>(p_lo + 32 * g + 16));
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < NR; ++r)
-#pragma unroll
-      for (int s = 0; s < 2; ++s) l_part[r] += (p[r][s][0] + p[r][s][1]) + (p[r][s][2] + p[r][s][3]);
 
     // ---- O^T += V^T P^T over the 128 tokens, two column tiles at a time ----
 #pragma unroll
@@ -515,10 +517,10 @@ __device__ __forceinline__ void fp8_item(const Stage1Args& a, const WorkItem* it
         }
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
-        o[r][v] = mfma_fp8_k128(va[0], bh[r], o[r][v]);
-        o[r][v + 1] = mfma_fp8_k128(va[1], bh[r], o[r][v + 1]);
-        o[r][v] = mfma_fp8_k128(va[0], bl[r], o[r][v]);
-        o[r][v + 1] = mfma_fp8_k128(va[1], bl[r], o[r][v + 1]);
+        o[r][v] = mfma_fp8_k128_sb(va[0], bh[r], o[r][v], sb[r]);
+        o[r][v + 1] = mfma_fp8_k128_sb(va[1], bh[r], o[r][v + 1], sb[r]);
+        o[r][v] = mfma_fp8_k128_sb(va[0], bl[r], o[r][v], sb[r]);
+        o[r][v + 1] = mfma_fp8_k128_sb(va[1], bl[r], o[r][v + 1], sb[r]);
       }
       if (more && v == 2) issue(t + 1, 4);
     }

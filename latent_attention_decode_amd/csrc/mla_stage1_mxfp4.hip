@@ -26,13 +26,16 @@
 // Values, O^T[dim, head] = V^T P^T: a scale of V belongs to a (token, 32
 // columns) block, i.e. runs along the output dimension, which no block scale
 // of a contraction over tokens can express.  So each tile's V is converted
-// once to e4m3 in LDS, relative to the largest scale of each block of 32
-// tokens x 32 columns: value = e2m1 x 2^(e - c) with c = max e over the block,
-// exact whenever the 32 tokens' scales of those columns lie within 8 binades
-// of c (smaller ones are rounded to e4m3, subnormals included).  2^(c - 127)
-// returns as the A block scale of P.V, whose k-values are laid out so that
-// k-block g is tokens 32g..32g+31 (bytes b < 16: token 16g + b, bytes 16..31:
-// token 64 + 16g + b - 16, for V^T and P^T alike).
+// once to e4m3 in LDS, each token row relative to its own largest V scale E:
+// value = e2m1 x 2^(e - E), exact whenever the row's scales of columns
+// 0..511 lie within 8 binades of E (smaller ones are rounded to e4m3,
+// subnormals included).  The row's 2^(E - 127) joins the token's softmax
+// weight, so the weight of P.V is 2^(x + E - 127 - m) for logit x; those of
+// each 32-token k-block are written relative to the block's largest and the
+// block's B scale restores them (weight_block_scale).  The k-values are laid
+// out so that k-block g is tokens 32g..32g+31 (bytes b < 16: token 16g + b,
+// bytes 16..31: token 64 + 16g + b - 16, for V^T and P^T alike); the two
+// waves that score a block trade their maxima through LDS before writing P.
 //
 // Data movement: per tile, 36 cache-to-LDS loads of 1 KB bring the 128 rows
 // of e2m1 codes (288 bytes each, rows past the item's end repeat its last
@@ -82,9 +85,8 @@ struct Fp4Lds {
   uint8_t raw[2][kXRawBytes];              // e2m1 rows, then the scale dwords
   uint8_t v[kXVBytes];                     // V of the current tile as e4m3 [token][dim]; first the query
   uint8_t p[2][kNumHeads][kPRow];          // P^T hi / lo as [head][token]
-  float red_m[kNumHeads][kXWaves];         // per-wave tile maxima
-  float red_l[kNumHeads][kXWaves];         // per-wave sums, at the end
-  uint8_t ctab[4][16];                     // e8m0 block maxima of V: [token block][column block]
+  float red_m[kNumHeads][kXWaves];         // per-wave tile maxima of the logits
+  float red_y[kNumHeads][kXWaves];         // per-wave maxima of logit + row scale; the sums at the end
   int32_t pages[kMaxItemPages];            // paged: page ids of the item
 };
 
@@ -107,20 +109,10 @@ __device__ __forceinline__ void dma_u16(const uint8_t* base, uint32_t off, uint3
 }
 #pragma clang diagnostic pop
 
-// fp4 (A) x fp8 (B) and fp8 x fp8 MX steps with A block scale sa (e8m0 in
-// byte `sel` of sa) and unit B scale.
+// fp4 (A) x fp8 (B) MX step with A block scale sa (e8m0) and unit B scale.
 __device__ __forceinline__ f32x4 mfma_fp4_fp8(fp8x32 a, fp8x32 b, f32x4 c, uint32_t sa) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, 0, (int)sa, 0, 127);
 }
-__device__ __forceinline__ f32x4 mfma_fp8_sa(fp8x32 a, fp8x32 b, f32x4 c, uint32_t sa, int sel) {
-  switch (sel) {
-    case 0: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, (int)sa, 0, 127);
-    case 1: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 1, (int)sa, 0, 127);
-    case 2: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 2, (int)sa, 0, 127);
-    default: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 3, (int)sa, 0, 127);
-  }
-}
-
 // 8 e2m1 codes (low nibble first) times 2^j -> 8 e4m3 codes (two words),
 // through f16 (exact for the products here) and a rounding conversion.
 __device__ __forceinline__ void fp4x8_to_fp8(uint32_t w, float scale, uint32_t& lo, uint32_t& hi) {
@@ -150,24 +142,6 @@ __device__ __forceinline__ void fp4x8_to_fp8_lut(uint32_t w, uint32_t lut_lo, ui
                                                  uint32_t& od) {
   ev = ((w << 4) & 0x80808080u) | __builtin_amdgcn_perm(lut_hi, lut_lo, w & 0x07070707u);
   od = (w & 0x80808080u) | __builtin_amdgcn_perm(lut_hi, lut_lo, (w >> 4) & 0x07070707u);
-}
-
-// Maxima of the two 16-bit halves of v over the 32 lanes of this half wave,
-// in the vector unit: DPP lane swaps within quads (xor 1, xor 2), mirrors
-// within 8 and 16 lanes, then the exchange between the two 16-lane rows
-// (permlane16_swap); v_pk_max_u16 combines both halves at once.
-__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
-  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
-                                                                __builtin_bit_cast(u16x2, b)));
-}
-__device__ __forceinline__ uint32_t half_wave_max2(uint32_t v) {
-  v = pk_max_u16(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
-  v = pk_max_u16(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
-  v = pk_max_u16(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
-  v = pk_max_u16(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));  // row_mirror
-  const auto x = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  return pk_max_u16((uint32_t)x[0], (uint32_t)x[1]);
 }
 
 // One work item: tokens [tok_begin, tok_end) of one sequence.
@@ -389,13 +363,9 @@ __device__ __forceinline__ void mxfp4_item(const Stage1Args& a, const WorkItem& 
   // Reads of this lane.  Scores: row 16w + r16 of the raw tile.  V^T: tr8
   // read q (0..3) gives tokens tb(q) + (0..7), tb = 16g + 8q (q < 2) or
   // 64 + 16g + 8(q - 2), from rows tb(q) + (r16 >> 1), columns
-  // 64w + 16v + 8(r16 & 1).  Conversion: the half wave h = 2w + lane / 32
-  // takes token block h & 3 and column blocks 4k + (h >> 2), k = 0..3; the
-  // lane, token row 32(h & 3) + (lane & 31).
-  const int hw_id = 2 * wave + (lane >> 5);
-  const int cv_tb = hw_id & 3;
-  const int cv_q = hw_id >> 2;
-  const int cv_row = 32 * cv_tb + (lane & 31);
+  // 64w + 16v + 8(r16 & 1).  Conversion: the lane takes token row 16w + r16
+  // (the wave's own tokens) and column blocks 4k + g, k = 0..3.
+  const int cv_row = 16 * wave + r16;
   int voff[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q)
@@ -440,57 +410,27 @@ __device__ __forceinline__ void mxfp4_item(const Stage1Args& a, const WorkItem& 
       sacc[1] = mfma_fp4_fp8(ka, rl, sacc[1], sa);
     }
 
-    // ---- softmax: x[i] is token 16w + 4g + i of head r16 ----
-    float x[4];
-    float tmax = kNegInf;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[i] = (sacc[0][i] + sacc[1][i]) * xscale;
-      if (tok0 + 16 * wave + 4 * g + i > tok_last) x[i] = kNegInf;
-      tmax = fmaxf(tmax, x[i]);
-    }
-    tmax = xor_max_groups(tmax);
-    if (g == 0) sh.red_m[r16][wave] = tmax;
-    float p[4];
-    uint32_t ph, pl;
-    {
-      const float mr = (m_ref == kNegInf) ? 0.0f : m_ref;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - mr);
-      split_fp8x4(p[0], p[1], p[2], p[3], ph, pl);
-      *reinterpret_cast<uint32_t*>(p_hi + 16 * wave + 4 * g) = ph;
-      *reinterpret_cast<uint32_t*>(p_lo + 16 * wave + 4 * g) = pl;
-    }
-
-    // ---- V of this tile to e4m3, per block of 32 tokens x 32 columns ----
-    // This lane converts token row cv_row, column blocks 4k + cv_q: all reads
-    // first, then the block maxima (two per reduction), the conversions and
-    // the writes.
+    // ---- V of this tile to e4m3, each token row relative to its own largest
+    // V scale E (the largest of its 16 e8m0 scales of columns 0..511) ----
+    // This lane converts token row 16w + r16, column blocks 4k + g; the four
+    // lane groups together hold the row's 16 scales, so E is their maximum.
+    float erow;  // E of token 16w + r16
     {
       uint32_t e[4];
       u32x4 w[4];
-      const uint8_t* rsrc = raw + cv_row * kXRow + 16 * cv_q;
-      const uint8_t* ssrc = sdw + 4 * kXScalePairs * cv_row + 4 * (cv_q >> 1) + (cv_q & 1);
+      const uint8_t* rsrc = raw + cv_row * kXRow + 16 * g;
+      const uint8_t* ssrc = sdw + 4 * kXScalePairs * cv_row + 4 * (g >> 1) + (g & 1);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         e[k] = ssrc[8 * k];
         w[k] = *reinterpret_cast<const u32x4*>(rsrc + 64 * k);
       }
-      uint32_t c[4];
-#pragma unroll
-      for (int k = 0; k < 4; k += 2) {
-        const uint32_t m = half_wave_max2(e[k] | (e[k + 1] << 16));
-        c[k] = m & 0xFFFF;
-        c[k + 1] = m >> 16;
-      }
-      if ((lane & 31) == 0) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) sh.ctab[cv_tb][4 * k + cv_q] = (uint8_t)c[k];
-      }
-      uint8_t* vdst = &sh.v[cv_row * kXVRow + 32 * cv_q];
+      erow = xor_max_groups((float)max(max(e[0], e[1]), max(e[2], e[3])));
+      const int E = (int)erow;
+      uint8_t* vdst = &sh.v[cv_row * kXVRow + 32 * g];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int j = max((int)e[k] - (int)c[k], -126);  // <= 0
+        const int j = max((int)e[k] - E, -126);  // <= 0
         uint32_t e8[8];  // 32 e4m3 codes: word 2i columns 32cb + 8i + {0,2,4,6}, word 2i+1 the odd ones
         if (__ballot(j < -5) == 0) {  // the whole wave by table
           const uint32_t kk = (uint32_t)(-j);
@@ -498,7 +438,7 @@ __device__ __forceinline__ void mxfp4_item(const Stage1Args& a, const WorkItem& 
           const uint32_t lut_hi = 0x4C484440u - kk * 0x08080808u;
 #pragma unroll
           for (int i = 0; i < 4; ++i) fp4x8_to_fp8_lut(w[k][i], lut_lo, lut_hi, e8[2 * i], e8[2 * i + 1]);
-        } else {  // a scale more than 5 binades below its block maximum: exact rounding conversions
+        } else {  // a scale more than 5 binades below the row's largest: rounding conversions
           const float scale = __uint_as_float((uint32_t)(127 + j) << 23);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -512,41 +452,75 @@ __device__ __forceinline__ void mxfp4_item(const Stage1Args& a, const WorkItem& 
         *reinterpret_cast<u32x4*>(vdst + 128 * k + 16) = u32x4{e8[4], e8[5], e8[6], e8[7]};
       }
     }
-    lds_barrier();  // P^T, maxima, the V tile and its block maxima; raw slot t % 2 is free
+
+    // ---- softmax: x[i] is token 16w + 4g + i of head r16 ----
+    // y = x + E - 127 is the log2 size of the token's weight times its row
+    // scale 2^(E - 127), which the e4m3 V rows leave out; the weights of a
+    // 32-token k-block of P.V (waves 2j, 2j + 1) are written relative to the
+    // block's largest y (weight_block_scale), once both waves' maxima are in.
+    float x[4], y[4];
+    float tmax = kNegInf, ymax = kNegInf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float ei = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (4 * g + i), __float_as_int(erow)));
+      x[i] = (sacc[0][i] + sacc[1][i]) * xscale;
+      if (tok0 + 16 * wave + 4 * g + i > tok_last) x[i] = kNegInf;
+      y[i] = x[i] + (ei - 127.0f);
+      tmax = fmaxf(tmax, x[i]);
+      ymax = fmaxf(ymax, y[i]);
+    }
+    tmax = xor_max_groups(tmax);
+    ymax = xor_max_groups(ymax);
+    if (g == 0) {
+      sh.red_m[r16][wave] = tmax;
+      sh.red_y[r16][wave] = ymax;
+    }
+    lds_barrier();  // maxima and the V tile; raw slot t % 2 is free
     if (t + 2 < ntiles) issue(t + 2);
 
     const f32x4 mx0 = *reinterpret_cast<const f32x4*>(&sh.red_m[r16][0]);
     const f32x4 mx1 = *reinterpret_cast<const f32x4*>(&sh.red_m[r16][4]);
-    fp8x32 bh = join16(*reinterpret_cast<const u32x4*>(p_hi + 16 * g),
-                       *reinterpret_cast<const u32x4*>(p_hi + 64 + 16 * g));
-    fp8x32 bl = join16(*reinterpret_cast<const u32x4*>(p_lo + 16 * g),
-                       *reinterpret_cast<const u32x4*>(p_lo + 64 + 16 * g));
-    // block exponents of V for column blocks 2w, 2w + 1 in bytes 0, 1
-    const uint32_t csa = *reinterpret_cast<const uint32_t*>(&sh.ctab[g][4 * (wave >> 1)]) >> (16 * (wave & 1));
+    const f32x4 my0 = *reinterpret_cast<const f32x4*>(&sh.red_y[r16][0]);
+    const f32x4 my1 = *reinterpret_cast<const f32x4*>(&sh.red_y[r16][4]);
     const float tile_max = fmaxf(fmaxf(fmaxf(mx0[0], mx0[1]), fmaxf(mx0[2], mx0[3])),
                                  fmaxf(fmaxf(mx1[0], mx1[1]), fmaxf(mx1[2], mx1[3])));
+    // Every wave reads the same maxima, so this branch is uniform.
     if (__ballot(tile_max > m_ref + kLazyRescale) != 0) {
-      const float m_new = fmaxf(m_ref, tile_max);
-      const float alpha = (m_ref == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
+      const float m_new = floorf(fmaxf(m_ref, tile_max));
+      const float alpha = (m_ref == kNegInf) ? 0.0f : __builtin_ldexpf(1.0f, (int)(m_ref - m_new));
 #pragma unroll
       for (int v = 0; v < 4; ++v) o[v] *= alpha;
       l_part *= alpha;
       m_ref = m_new;
-      lds_barrier();  // everyone has read the old P^T
+    }
+    // block maxima of y: k-block j is waves 2j, 2j + 1
+    const float yb0 = fmaxf(my0[0], my0[1]), yb1 = fmaxf(my0[2], my0[3]);
+    const float yb2 = fmaxf(my1[0], my1[1]), yb3 = fmaxf(my1[2], my1[3]);
+    {
+      const int jb = wave >> 1;  // this wave's block
+      const float own = jb == 0 ? yb0 : jb == 1 ? yb1 : jb == 2 ? yb2 : yb3;
+      const float shift = 7.0f - weight_block_floor(own);  // y + shift < 8
+      float p[4];
+      uint32_t ph, pl;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - m_ref);
+      for (int i = 0; i < 4; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(y[i] + shift);
+        l_part += __builtin_amdgcn_exp2f(x[i] - m_ref);
+      }
       split_fp8x4(p[0], p[1], p[2], p[3], ph, pl);
       *reinterpret_cast<uint32_t*>(p_hi + 16 * wave + 4 * g) = ph;
       *reinterpret_cast<uint32_t*>(p_lo + 16 * wave + 4 * g) = pl;
-      lds_barrier();
-      bh = join16(*reinterpret_cast<const u32x4*>(p_hi + 16 * g),
-                  *reinterpret_cast<const u32x4*>(p_hi + 64 + 16 * g));
-      bl = join16(*reinterpret_cast<const u32x4*>(p_lo + 16 * g),
-                  *reinterpret_cast<const u32x4*>(p_lo + 64 + 16 * g));
     }
-    l_part += (p[0] + p[1]) + (p[2] + p[3]);
+    // B scale of k-block g for head r16
+    const int sb = weight_block_scale(g == 0 ? yb0 : g == 1 ? yb1 : g == 2 ? yb2 : yb3, m_ref);
+    lds_barrier();  // P^T of all waves
 
-    // ---- O^T += V^T P^T, columns 64w + 16v, block scale 2^(c - 127) ----
+    const fp8x32 bh = join16(*reinterpret_cast<const u32x4*>(p_hi + 16 * g),
+                             *reinterpret_cast<const u32x4*>(p_hi + 64 + 16 * g));
+    const fp8x32 bl = join16(*reinterpret_cast<const u32x4*>(p_lo + 16 * g),
+                             *reinterpret_cast<const u32x4*>(p_lo + 64 + 16 * g));
+
+    // ---- O^T += V^T P^T, columns 64w + 16v ----
 #pragma unroll
     for (int v = 0; v < 4; v += 2) {
       fp8x32 va[2];
@@ -558,18 +532,18 @@ __device__ __forceinline__ void mxfp4_item(const Stage1Args& a, const WorkItem& 
           va[u][2 * q] = raw2[0];
           va[u][2 * q + 1] = raw2[1];
         }
-      o[v] = mfma_fp8_sa(va[0], bh, o[v], csa, v >> 1);
-      o[v + 1] = mfma_fp8_sa(va[1], bh, o[v + 1], csa, v >> 1);
-      o[v] = mfma_fp8_sa(va[0], bl, o[v], csa, v >> 1);
-      o[v + 1] = mfma_fp8_sa(va[1], bl, o[v + 1], csa, v >> 1);
+      o[v] = mfma_fp8_k128_sb(va[0], bh, o[v], sb);
+      o[v + 1] = mfma_fp8_k128_sb(va[1], bh, o[v + 1], sb);
+      o[v] = mfma_fp8_k128_sb(va[0], bl, o[v], sb);
+      o[v + 1] = mfma_fp8_k128_sb(va[1], bl, o[v + 1], sb);
     }
   }
 
   const float l_w = xor_sum_groups(l_part);
-  if (g == 0) sh.red_l[r16][wave] = l_w;
+  if (g == 0) sh.red_y[r16][wave] = l_w;  // every read of the last tile's maxima is behind a barrier
   lds_barrier();
-  const f32x4 ls0 = *reinterpret_cast<const f32x4*>(&sh.red_l[r16][0]);
-  const f32x4 ls1 = *reinterpret_cast<const f32x4*>(&sh.red_l[r16][4]);
+  const f32x4 ls0 = *reinterpret_cast<const f32x4*>(&sh.red_y[r16][0]);
+  const f32x4 ls1 = *reinterpret_cast<const f32x4*>(&sh.red_y[r16][4]);
   const float L = ((ls0[0] + ls0[1]) + (ls0[2] + ls0[3])) + ((ls1[0] + ls1[1]) + (ls1[2] + ls1[3]));
   // The V tile holds each group of 8 columns as (0, 2, 4, 6, 1, 3, 5, 7), so
   // lane group g has output columns 8(g >> 1) + 2i + (g & 1) of each column
