@@ -218,6 +218,25 @@ mla_status mla_decode_run(mla_decode_t h, const void* q, const void* kv, const v
                           void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mla_decode_run without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation): the partials go to a device array of the library
+ * (MLA_SCRATCH_BYTES, 16 MiB, room for 511 partials), which each GPU the
+ * library runs on holds until the process ends.  No allocation, no host
+ * synchronisation; the arguments are those of mla_decode_run less the
+ * workspace.  Every call on one GPU shares that GPU's array: calls that
+ * overlap on a GPU (from any handle, on any stream) race, and must be
+ * ordered by the caller.  Nothing in the array needs clearing: a run writes
+ * every partial it reads.  A plan whose workspace_bytes exceed
+ * MLA_SCRATCH_BYTES is refused with MLA_ERR_UNSUPPORTED before any launch.
+ */
+#define MLA_SCRATCH_BYTES (16u << 20)
+mla_status mla_decode_run_noalloc(mla_decode_t h, const void* q, const void* kv, const void* kv_scales,
+                                  int64_t kv_scale_stride, const int32_t* kv_indptr,
+                                  const int32_t* kv_page_indices, const int32_t* kv_last_page_len, void* out,
+                                  void* stream);
+
+/*
  * Kernel timing for measurement.  While enabled, mla_decode_run launches its
  * kernels with a pair of HIP events each, which the launch itself records
  * when the kernel starts and when it ends (hipExtLaunchKernel);

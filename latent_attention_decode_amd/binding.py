@@ -23,6 +23,7 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED",
           3: "MLA_ERR_NOT_PLANNED", 4: "MLA_ERR_WORKSPACE_TOO_SMALL", 5: "MLA_ERR_HIP"}
 
 NUM_HEADS, QK_DIM, V_DIM = 16, 576, 512
+MLA_SCRATCH_BYTES = 16 << 20  # the allocation-free run's device array (MLA_SCRATCH_BYTES)
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m latent_attention_decode_amd.build`"
@@ -54,6 +55,7 @@ _lib.mla_decode_plan_info.argtypes = [_H, ctypes.POINTER(ctypes.c_int), ctypes.P
                                       ctypes.POINTER(ctypes.c_int)]
 _lib.mla_decode_run.argtypes = [_H, _P, _P, _P, ctypes.c_int64, _P, _P, _P, _P, _P,
                                 ctypes.c_size_t, _P]
+_lib.mla_decode_run_noalloc.argtypes = [_H, _P, _P, _P, ctypes.c_int64, _P, _P, _P, _P, _P]
 _lib.mla_decode_set_profiling.argtypes = [_H, ctypes.c_int]
 _lib.mla_decode_kernel_time_ms.argtypes = [_H, ctypes.c_int, ctypes.POINTER(ctypes.c_float)]
 _lib.mla_decode_kernel_resources.argtypes = [_H, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
@@ -63,13 +65,13 @@ _lib.mla_decode_last_error.argtypes = [_H]
 _lib.mla_decode_last_error.restype = ctypes.c_char_p
 for _name in ("mla_decode_create", "mla_decode_plan", "mla_decode_plan_preview", "mla_decode_plan_multi",
               "mla_decode_plan_preview_multi",
-              "mla_decode_plan_info", "mla_decode_run", "mla_decode_set_profiling",
+              "mla_decode_plan_info", "mla_decode_run", "mla_decode_run_noalloc", "mla_decode_set_profiling",
               "mla_decode_kernel_time_ms", "mla_decode_kernel_resources", "mla_decode_destroy"):
     getattr(_lib, _name).restype = ctypes.c_int
 
 EXPORTED = ("mla_decode_version", "mla_status_string", "mla_decode_create", "mla_decode_plan",
             "mla_decode_plan_preview", "mla_decode_plan_multi", "mla_decode_plan_preview_multi",
-            "mla_decode_plan_info", "mla_decode_run",
+            "mla_decode_plan_info", "mla_decode_run", "mla_decode_run_noalloc",
             "mla_decode_set_profiling", "mla_decode_kernel_time_ms", "mla_decode_kernel_resources",
             "mla_decode_destroy", "mla_decode_last_error")
 
@@ -225,6 +227,23 @@ def mla_decode_run(h, q: torch.Tensor, kv: torch.Tensor, kv_scales: Optional[tor
                              _dptr(kv_page_indices), _dptr(kv_last_page_len), _dptr(out),
                              _dptr(workspace), ws_bytes, stream.cuda_stream)
     _check(st, "mla_decode_run", h)
+
+
+def mla_decode_run_noalloc(h, q: torch.Tensor, kv: torch.Tensor, kv_scales: Optional[torch.Tensor],
+                           kv_indptr: torch.Tensor, out: torch.Tensor,
+                           kv_page_indices: Optional[torch.Tensor] = None,
+                           kv_last_page_len: Optional[torch.Tensor] = None,
+                           stream: Optional[torch.cuda.Stream] = None) -> None:
+    """mla_decode_run with the library's own device scratch array in place of a
+    workspace (no allocation anywhere; calls on one GPU must not overlap)."""
+    _check_run_tensors(q, out, kv_indptr, kv_page_indices, kv_last_page_len)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    stride = int(kv_scales.shape[-1]) if (kv_scales is not None and kv_scales.dtype == torch.uint8) else 0
+    st = _lib.mla_decode_run_noalloc(h, _dptr(q), _dptr(kv), _dptr(kv_scales), stride, _dptr(kv_indptr),
+                                     _dptr(kv_page_indices), _dptr(kv_last_page_len), _dptr(out),
+                                     stream.cuda_stream)
+    _check(st, "mla_decode_run_noalloc", h)
 
 
 class PreparedRun:

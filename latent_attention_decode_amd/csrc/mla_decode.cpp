@@ -54,7 +54,8 @@ struct mla_decode_s {
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 3 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 4 * 100 + 0;
+static_assert(MLA_SCRATCH_BYTES == mla::kScratchBytes, "scratch size in the header");
 
 mla_status fail(mla_decode_t h, mla_status st, const char* fmt, ...) {
   if (h) {
@@ -874,6 +875,30 @@ mla_status mla_decode_run(mla_decode_t h, const void* q, const void* kv, const v
   }
   h->timed_run = timed;
   return MLA_OK;
+}
+
+mla_status mla_decode_run_noalloc(mla_decode_t h, const void* q, const void* kv, const void* kv_scales,
+                                  int64_t kv_scale_stride, const int32_t* kv_indptr,
+                                  const int32_t* kv_page_indices, const int32_t* kv_last_page_len, void* out,
+                                  void* stream) {
+  if (!h) return MLA_ERR_INVALID_ARG;
+  h->last_error.clear();
+  if (!h->planned) return fail(h, MLA_ERR_NOT_PLANNED, "mla_decode_run_noalloc before a successful plan");
+  if (h->workspace_bytes > mla::kScratchBytes)
+    return fail(h, MLA_ERR_UNSUPPORTED,
+                "the plan needs %zu bytes of partials; the allocation-free run holds at most %zu "
+                "(plan with a smaller split_override, or use mla_decode_run with a workspace)",
+                h->workspace_bytes, mla::kScratchBytes);
+  void* scratch = nullptr;
+  if (h->workspace_bytes) {
+    DeviceGuard guard(h->device);
+    if (!guard.ok) return fail(h, MLA_ERR_HIP, "cannot select HIP device %d", h->device);
+    const hipError_t e = mla::scratch_address(h->device, &scratch);
+    if (e != hipSuccess)
+      return fail(h, MLA_ERR_HIP, "device address of the scratch array: %s", hipGetErrorString(e));
+  }
+  return mla_decode_run(h, q, kv, kv_scales, kv_scale_stride, kv_indptr, kv_page_indices, kv_last_page_len, out,
+                        scratch, scratch ? mla::kScratchBytes : 0, stream);
 }
 
 mla_status mla_decode_set_profiling(mla_decode_t h, int enable) {

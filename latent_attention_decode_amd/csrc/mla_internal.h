@@ -144,6 +144,14 @@ struct MergeArgs {
 // (the last item reads the other nslots - 1 partials in groups of four).
 constexpr int kFusedMergeMaxSlots = 12;
 
+// Size of the device array that the allocation-free run entry point uses in
+// place of the caller's workspace (mla_kernels.hip): room for 511 partials,
+// about twice what one item per compute unit of a 256-CU device needs.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+// Device address of that array on `device`, which must be the current
+// device; looked up once per device and kept.
+hipError_t scratch_address(int device, void** ptr);
+
 // The fp8 and MXFP4 split kernels (mla_stage1_fp8.hip, mla_stage1_mxfp4.hip).
 const void* stage1_fp8_kernel(bool paged, bool row_pairs);
 const void* stage1_mxfp4_kernel(bool paged);

@@ -40,7 +40,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
+#include <vector>
 
 #include "mla_device.h"
 #include "mla_internal.h"
@@ -664,6 +666,30 @@ const void* pick_stage1(int fmt, bool paged) {
 }
 
 }  // namespace
+
+// Scratch of the allocation-free run: every run on a GPU shares that GPU's
+// copy (runs that overlap on one GPU race), and it keeps the last run's
+// partials, which no run reads before writing them.  In host code `scratch`
+// names a host-side stand-in, never the device memory: kernels get the
+// address that hipGetSymbolAddress returns for the device.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+hipError_t scratch_address(int device, void** ptr) {
+  static std::mutex mu;
+  static std::vector<void*> addr;  // per device ordinal
+  int cur = -1;
+  if (device < 0 || hipGetDevice(&cur) != hipSuccess || cur != device) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (static_cast<size_t>(device) >= addr.size()) addr.resize(static_cast<size_t>(device) + 1, nullptr);
+  if (!addr[device]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[device] = p;
+  }
+  *ptr = addr[device];
+  return hipSuccess;
+}
 
 // With events, the launch records them at the start and the end of the
 // kernel itself (hipExtLaunchKernel), so their difference is its duration.

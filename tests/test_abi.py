@@ -32,6 +32,11 @@ def test_header_symbols_are_exported(B):
     assert sorted(B.EXPORTED) == names
 
 
+def test_scratch_size_matches_the_header(B):
+    m = re.search(r"#define\s+MLA_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == B.MLA_SCRATCH_BYTES
+
+
 def test_version_and_status_strings(B):
     assert B.mla_decode_version() >= 10000
     for code, name in B.STATUS.items():
@@ -76,6 +81,9 @@ def test_plan_and_run_validate_before_any_gpu_call(B):
         # run before a successful plan: raw call with dummy pointers
         st = B._lib.mla_decode_run(h, 16, 16, 16, 0, 16, 16, 16, 16, None, 0, None)
         assert st == 3
+        st = B._lib.mla_decode_run_noalloc(h, 16, 16, 16, 0, 16, 16, 16, 16, None)
+        assert st == 3 and "before a successful plan" in B.mla_decode_last_error(h)
+        assert B._lib.mla_decode_run_noalloc(None, 16, 16, 16, 0, 16, 16, 16, 16, None) == 1
         with pytest.raises(B.MlaError) as e:
             B.mla_decode_plan_info(h)
         assert e.value.status == 3
