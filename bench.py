@@ -1,15 +1,24 @@
 """Benchmark: single-token MLA decode on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--targets A,B|none]
+                    [--cold-calls N] [--no-cpu-baseline]
 
 A step is one decode call (the split kernel, plus the LSE merge kernel when
-the plan needs one) over one batch
-of seeded synthetic inputs already resident in HBM; the split plan is made
-once beforehand (reported as plan_us).  Every timed step is cold: the steps
-cycle through copies of the inputs totalling at least 1 GiB, so no step finds
-its KV in the 256 MB last-level (MALL) cache.  The `steps` calls run back to
-back between two events; ms_per_step = elapsed / steps and value =
-algorithmic KV bytes / ms_per_step.
+the plan needs one) over one batch of seeded synthetic inputs already
+resident in HBM; the split plan is made once beforehand (plan_us).  The
+headline workload is the largest listed one: 256 sequences of 1024-8192
+tokens (uniform draw) in an fp8 cache of 2-token pages, shuffled.  Every
+timed step is cold: the steps cycle through copies of the inputs totalling
+at least 1 GiB, so no step finds its KV in the 256 MB last-level (MALL)
+cache.  The `steps` calls run back to back between two events; ms_per_step =
+elapsed / steps and value = algorithmic KV bytes / ms_per_step.
+
+Beside that: cold_single_us, the median and the mean without the fastest and
+slowest of calls timed one at a time (events around each call, the GPU idle
+before it); us_per_call_warm, back-to-back calls on one copy of the inputs;
+plan.replan_us, the host time of re-planning the live handle between runs;
+and, under "targets", the same record for 32 and 64 sequences of 8192 tokens
+in an fp8 cache (the target shapes).
 
 Algorithmic bytes = tokens x stored bytes per row (bf16 1152, fp8 576, MXFP4
 288 + 18 scale bytes); query, output, partials and page ids are overhead.
@@ -33,7 +42,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
-DEFAULT_WORKLOAD = "bs64_kv1024_fp8"
+DEFAULT_WORKLOAD = "bs256_ragged1024-8192_fp8_paged2"  # the largest listed workload
+# The target shapes (at least 32 sequences of 8192 tokens, fp8 cache), measured in
+# the same run and reported under "targets".
+TARGETS = ("bs32_kv8192_fp8", "bs64_kv8192_fp8")
 ROTATION_BYTES = 1 << 30  # inputs cycled per timed pass: 4x the 256 MB MALL
 METRIC = "µs/call and effective KV HBM GB/s (% of peak), MLA decode bs×kv_len"
 # Times the pages report for one of these workloads on MI355X (µs per call;
@@ -103,45 +115,12 @@ def cpu_baseline(case, budget_s: float = 10.0):
             "us_per_call_extrapolated": round(full_us, 1)}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--warm-iters", type=int, default=100)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--split", type=int, default=0, help="split override (0 = planner)")
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help="only copy MIB MiB device-to-device 5 times (a kernel of known traffic "
-                         "for scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
-    args = ap.parse_args()
-
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this decode path "
-              "shards by sequence with no exchange, so run one process per GPU.", file=sys.stderr)
-        sys.exit(2)
-
-    import torch
-    from latent_attention_decode_amd import binding, synth
-
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    torch.cuda.set_device(0)
-    dev = torch.device("cuda:0")
-
-    if args.copy_calibration:
-        n = args.copy_calibration << 20
-        src = torch.ones(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes": n, "copies": 5}), flush=True)
-        return
-
-    name = args.workload
+def measure(name, args, dev, torch, binding, synth, full=True):
+    """One workload: plan once, then the cold back-to-back pass (steps calls
+    between two events), the same calls with the library's kernel events
+    (stage-1 and merge durations), individually event-timed cold calls
+    (median and the mean without the fastest and slowest), warm calls, and
+    the cost of re-planning the live handle."""
     kv_dtype, batch, kv_len, ps, shuffled, seed = synth.CONFIGS[name][:6]
     print(f"[bench] generating {name}", file=sys.stderr, flush=True)
     case = synth.config_case(name)
@@ -182,7 +161,7 @@ def main():
     torch.cuda.synchronize()
 
     # Timed region: exactly `steps` calls back to back, each on the next copy.
-    print(f"[bench] timing {args.steps} cold steps over {n_copies} input copies",
+    print(f"[bench] {name}: timing {args.steps} cold steps over {n_copies} input copies",
           file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -192,7 +171,7 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    call_ms = [ev0.elapsed_time(ev1) / args.steps]
+    mean_ms = ev0.elapsed_time(ev1) / args.steps
 
     # Kernel durations: the same calls again with the library recording HIP
     # events around each of its kernel launches on the same stream (the event
@@ -205,6 +184,19 @@ def main():
         mg_ms.append(binding.mla_decode_kernel_time_ms(dec.h, 1))
     binding.mla_decode_set_profiling(dec.h, False)
 
+    # Cold calls one at a time: events around each call, the GPU idle before
+    # it, the call's inputs last read n_copies calls earlier.
+    single = []
+    for i in range(args.cold_calls):
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        run(i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        single.append(ev0.elapsed_time(ev1) * 1e3)
+    single = np.sort(np.array(single))
+    trimmed = float(single[1:-1].mean()) if single.size > 2 else float(single.mean())
+
     # warm: back-to-back calls on one copy (its KV may sit in the MALL)
     run(0)
     torch.cuda.synchronize()
@@ -215,25 +207,120 @@ def main():
     torch.cuda.synchronize()
     warm_us = ev0.elapsed_time(ev1) / args.warm_iters * 1e3
 
+    # Re-planning the live handle for the same batch, as a decode loop does
+    # each step (lengths change by one token), interleaved with runs in
+    # flight: host time of each plan call.
+    replan = []
+    t = copies[0]
+    for i in range(20):
+        t0 = time.perf_counter()
+        dec.plan(case.kv_indptr, case.kv_last_page_len, args.split, case.qo_indptr)
+        replan.append((time.perf_counter() - t0) * 1e6)
+        dec.run(t["q"], t["kv"], t["kv_scales"], t["kv_indptr"], out, t["kv_page_indices"],
+                t["kv_last_page_len"])
+    torch.cuda.synchronize()
+
     s1 = np.array(s1_ms)
-    mean_ms = float(call_ms[0])
     value = alg_bytes / (mean_ms * 1e-3) / 1e9
     s1_mean = float(s1.mean())
     achieved = alg_bytes / (s1_mean * 1e-3) / 1e9
-    traffic = traffic_record(name, kv_dtype)
+    rec = {
+        "us_per_call": round(mean_ms * 1e3, 2),
+        "gbs": round(value, 2),
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "cold_single_us": {"median": round(float(np.median(single)), 2), "trimmed_mean": round(trimmed, 2),
+                           "min": round(float(single[0]), 2), "max": round(float(single[-1]), 2),
+                           "calls": int(single.size)},
+        "us_per_call_warm": round(warm_us, 2),
+        "kernels": {"stage1_us": round(s1_mean * 1e3, 2),
+                    "merge_us": round(float(np.mean(mg_ms)) * 1e3, 2),
+                    "stage1_vgprs": res1["vgprs"], "stage1_lds_bytes": res1["lds_bytes"],
+                    "stage1_scratch_bytes": res1["scratch_bytes"]},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_record(name, kv_dtype)},
+        "plan": {"items": n_items, "max_splits": max_splits, "partials": n_partials,
+                 "workspace_bytes": int(ws_bytes), "plan_us": round(plan_us, 1),
+                 "replan_us": round(float(np.median(replan)), 1)},
+    }
+    if full:
+        rec["config"] = {"workload": name, "kv_dtype": kv_dtype, "batch": int(case.batch),
+                         "query_rows": int(case.rows),
+                         "kv_len": kv_len if isinstance(kv_len, int) else list(kv_len),
+                         "total_tokens": int(case.total_tokens), "page_size": ps,
+                         "algorithmic_kv_bytes": int(alg_bytes)}
+        rec["input_copies"] = n_copies
+        rec["timed_wall_s"] = round(wall, 3)
+        rec["mean_ms"] = mean_ms
+        rec["kv_dtype"] = kv_dtype
+    else:
+        rec["algorithmic_kv_bytes"] = int(alg_bytes)
+    del calls
+    dec.close()
+    del copies, base
+    torch.cuda.empty_cache()
+    return rec, case
 
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--targets", default=",".join(TARGETS),
+                    help="comma-separated workloads measured in the same run and reported under "
+                         "'targets' ('none' for none)")
+    ap.add_argument("--warm-iters", type=int, default=100)
+    ap.add_argument("--cold-calls", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--split", type=int, default=0, help="split override (0 = planner)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB device-to-device 5 times (a kernel of known traffic "
+                         "for scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this decode path "
+              "shards by sequence with no exchange, so run one process per GPU.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from latent_attention_decode_amd import binding, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 5}), flush=True)
+        return
+
+    name = args.workload
+    rec, case = measure(name, args, dev, torch, binding, synth, full=True)
+    kv_dtype = rec.pop("kv_dtype")
+    mean_ms = rec.pop("mean_ms")
     line = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": rec["gbs"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(mean_ms, 5),
-        "us_per_call": round(mean_ms * 1e3, 2),
-        "input_copies": n_copies,
-        "us_per_call_warm": round(warm_us, 2),
-        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "us_per_call": rec["us_per_call"],
+        "input_copies": rec["input_copies"],
+        "cold_single_us": rec["cold_single_us"],
+        "us_per_call_warm": rec["us_per_call_warm"],
+        "pct_of_hbm_peak": rec["pct_of_hbm_peak"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": round(PAGE_US[name] / (mean_ms * 1e3), 3) if name in PAGE_US else None,
@@ -241,25 +328,18 @@ def main():
                   "fp8": "fp8-e4m3 (fp8 / MX MFMA on the codes, fp32 acc)",
                   "mxfp4": "mxfp4 (MX MFMA: e2m1 scores, e4m3 values, fp32 acc)"}[kv_dtype],
         "data": "synthetic",
-        "config": {"workload": name, "kv_dtype": kv_dtype, "batch": int(case.batch),
-                   "query_rows": int(case.rows),
-                   "kv_len": kv_len if isinstance(kv_len, int) else list(kv_len),
-                   "total_tokens": int(case.total_tokens), "page_size": ps,
-                   "algorithmic_kv_bytes": int(alg_bytes)},
-        "plan": {"items": n_items, "max_splits": max_splits, "partials": n_partials,
-                 "workspace_bytes": int(ws_bytes), "plan_us": round(plan_us, 1)},
-        "kernels": {"stage1_us": round(s1_mean * 1e3, 2),
-                    "merge_us": round(float(np.mean(mg_ms)) * 1e3, 2),
-                    "stage1_vgprs": res1["vgprs"], "stage1_lds_bytes": res1["lds_bytes"],
-                    "stage1_scratch_bytes": res1["scratch_bytes"]},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic},
-        "timed_wall_s": round(wall, 3),
+        "config": rec["config"],
+        "plan": rec["plan"],
+        "kernels": rec["kernels"],
+        "roofline": rec["roofline"],
+        "timed_wall_s": rec["timed_wall_s"],
     }
-    del calls
-    dec.close()
-    del copies, base
+    targets = [t for t in args.targets.split(",") if t and t != "none" and t != name]
+    if targets:
+        line["targets"] = {}
+        for t in targets:
+            sub, _ = measure(t, args, dev, torch, binding, synth, full=False)
+            line["targets"][t] = sub
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(case)

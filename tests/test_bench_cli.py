@@ -48,3 +48,15 @@ def test_page_time_is_only_for_its_workload():
     from latent_attention_decode_amd import synth
     assert set(bench.PAGE_US) <= set(synth.CONFIGS)
     assert bench.PAGE_US == {"bs256_kv8192_mxfp4": pytest.approx(236.6)}
+
+
+def test_headline_and_target_workloads():
+    """The headline is the largest listed workload (256 ragged sequences in 2-token
+    pages); the target shapes (32 and 64 sequences of 8192 tokens, fp8) ride in
+    the same line."""
+    import bench
+    from latent_attention_decode_amd import synth
+    assert bench.DEFAULT_WORKLOAD == "bs256_ragged1024-8192_fp8_paged2"
+    for t in bench.TARGETS:
+        fmt, batch, kv_len = synth.CONFIGS[t][:3]
+        assert fmt == "fp8" and batch >= 32 and kv_len == 8192
