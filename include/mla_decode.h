@@ -49,8 +49,11 @@
  * MXFP4 cache whose scale array or stride is odd always takes the second
  * launch, one item per workgroup).  No merge runs when no sequence is
  * split.  The completion counters of that merge belong to the plan: runs of
- * one handle must not overlap (on any streams), and a plan must not be made
- * while a run of the handle is still executing.
+ * one handle must not overlap (on any streams).  A plan may be made while
+ * runs of the previous plan are still executing: it builds the work list on
+ * the host and uploads it, without waiting, into the other of the handle's
+ * two plan buffers (a decode loop re-plans every step as its sequences
+ * grow).
  *
  * Ownership.  The caller owns every tensor, the workspace and the stream.  A
  * handle owns only its plan (a small device work list, allocated by
@@ -114,9 +117,16 @@ mla_status mla_decode_create(mla_decode_t* out, int device, int num_heads, int q
  * bf16 -- except at a sequence's end or under split_override, which cuts at
  * 32-token boundaries) sized against the device's compute-unit count and
  * the stage-1 kernel's residency (up to 256 items for one long sequence),
- * uploads the
- * work list to the device (synchronously) and reports the workspace size the
- * run needs (bytes; may be 0).  kv_indptr_host has batch+1 entries (tokens if
+ * uploads the work list to the device and reports the workspace size the
+ * run needs (bytes; may be 0).  The upload goes from pinned host memory on a
+ * stream of the handle, ordered after the runs that read the buffer it
+ * overwrites; the host does not wait for it (except to reuse a host buffer
+ * whose upload from two plans ago is still queued), and the first run of the
+ * plan on each stream waits for it on the device.  The first plan of a
+ * handle (and one that needs a larger buffer) allocates device and pinned
+ * host memory.  This is the host planner of 700955 ("locked baseline
+ * dispatch"), `_compute_custom_splits` (split counts from the batch and the
+ * compute units), rebuilt around the stage-1 kernel's measured residency.  kv_indptr_host has batch+1 entries (tokens if
  * page_size == 1, pages otherwise; non-decreasing, starting anywhere >= 0);
  * kv_last_page_len_host has batch entries when page_size > 1 and is ignored
  * (may be NULL) otherwise.  split_override > 0 forces that many items per

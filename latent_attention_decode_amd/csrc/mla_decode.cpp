@@ -37,10 +37,28 @@ struct mla_decode_s {
   int uniform_splits = 0, uniform_chunk = 0, uniform_len = 0, uniform_base = 0;
   int num_bins = 0;  // > 0: binned plan (see PlanOut)
   bool row_pairs = false;  // the fp8 kernel runs pairs of query rows (see PlanOut)
-  // device: [num_items] WorkItem, [num_merge] MergeSeq, [num_merge] int32
-  // counters, [num_bins + 1] int32 bin starts
-  void* dev_plan = nullptr;
-  size_t dev_plan_bytes = 0;
+  // Device plan, two buffers used in turn: [num_items] WorkItem, [num_merge]
+  // MergeSeq, [num_merge] int32 counters, [num_bins + 1] int32 bin starts.
+  // plan() fills the pinned host copy of the other buffer and uploads it on
+  // a stream of the handle (no host wait), so a decode loop can re-plan
+  // while the previous run is in flight; the first run of a plan waits on
+  // its upload (uploaded[]), and a buffer is written again only after the
+  // runs that read it (released[], recorded on the last run's stream when
+  // the next plan is made).
+  void* dev_plan[2] = {nullptr, nullptr};
+  size_t dev_plan_bytes[2] = {0, 0};
+  void* host_plan[2] = {nullptr, nullptr};
+  size_t host_plan_bytes[2] = {0, 0};
+  hipEvent_t uploaded[2] = {nullptr, nullptr};
+  hipEvent_t released[2] = {nullptr, nullptr};
+  bool upload_pending[2] = {false, false};
+  bool release_pending[2] = {false, false};
+  hipStream_t upload_stream = nullptr;
+  int cur = 1;                     // buffer of the current plan
+  bool ran_since_plan = false;     // a run has used the current plan
+  hipStream_t waited_stream = nullptr;  // a stream that already waits on the current upload
+  bool waited = false;
+  hipStream_t last_run_stream = nullptr;
   int num_cus = 0;
   int blocks_per_cu = 0;
 
@@ -658,21 +676,64 @@ mla_status plan_impl(mla_decode_t h, int batch, const int32_t* qo_indptr_host, c
   const size_t counter_bytes = plan.merge.size() * sizeof(int32_t);
   const size_t bins_bytes = plan.bins.size() * sizeof(int32_t);
   const size_t need = items_bytes + merge_bytes + counter_bytes + bins_bytes;
-  if (need > h->dev_plan_bytes) {
-    if (h->dev_plan) (void)hipFree(h->dev_plan);
-    h->dev_plan = nullptr;
-    h->dev_plan_bytes = 0;
-    if (hipMalloc(&h->dev_plan, need) != hipSuccess)
-      return fail(h, MLA_ERR_HIP, "hipMalloc of %zu plan bytes failed", need);
-    h->dev_plan_bytes = need;
+
+  if (!h->upload_stream) {
+    if (hipStreamCreateWithFlags(&h->upload_stream, hipStreamNonBlocking) != hipSuccess) {
+      h->upload_stream = nullptr;
+      return fail(h, MLA_ERR_HIP, "cannot create the plan upload stream");
+    }
+    for (int k = 0; k < 2; ++k)
+      if (hipEventCreateWithFlags(&h->uploaded[k], hipEventDisableTiming) != hipSuccess ||
+          hipEventCreateWithFlags(&h->released[k], hipEventDisableTiming) != hipSuccess)
+        return fail(h, MLA_ERR_HIP, "hipEventCreate failed");
   }
-  std::vector<unsigned char> blob(need, 0);
-  if (items_bytes) std::memcpy(blob.data(), plan.items.data(), items_bytes);
-  if (merge_bytes) std::memcpy(blob.data() + items_bytes, plan.merge.data(), merge_bytes);
-  if (bins_bytes)
-    std::memcpy(blob.data() + items_bytes + merge_bytes + counter_bytes, plan.bins.data(), bins_bytes);
-  if (hipMemcpy(h->dev_plan, blob.data(), need, hipMemcpyHostToDevice) != hipSuccess)
-    return fail(h, MLA_ERR_HIP, "uploading the work list failed");
+  // The runs of the current plan have all been enqueued on last_run_stream
+  // (runs of a handle do not overlap): its buffer is free once they are done.
+  if (h->ran_since_plan) {
+    if (hipEventRecord(h->released[h->cur], h->last_run_stream) != hipSuccess)
+      return fail(h, MLA_ERR_HIP, "recording the end of the last run failed");
+    h->release_pending[h->cur] = true;
+  }
+  const int b = h->cur ^ 1;
+  if (need > h->dev_plan_bytes[b]) {
+    if (h->release_pending[b] && hipEventSynchronize(h->released[b]) != hipSuccess)
+      return fail(h, MLA_ERR_HIP, "waiting for the runs of an earlier plan failed");
+    h->release_pending[b] = false;
+    if (h->dev_plan[b]) (void)hipFree(h->dev_plan[b]);
+    h->dev_plan[b] = nullptr;
+    h->dev_plan_bytes[b] = 0;
+    if (hipMalloc(&h->dev_plan[b], need) != hipSuccess)
+      return fail(h, MLA_ERR_HIP, "hipMalloc of %zu plan bytes failed", need);
+    h->dev_plan_bytes[b] = need;
+  }
+  // the host copy of buffer b is free again once its last upload is done
+  if (h->upload_pending[b] && hipEventSynchronize(h->uploaded[b]) != hipSuccess)
+    return fail(h, MLA_ERR_HIP, "waiting for an earlier plan upload failed");
+  h->upload_pending[b] = false;
+  if (need > h->host_plan_bytes[b]) {
+    if (h->host_plan[b]) (void)hipHostFree(h->host_plan[b]);
+    h->host_plan[b] = nullptr;
+    h->host_plan_bytes[b] = 0;
+    if (hipHostMalloc(&h->host_plan[b], need, hipHostMallocDefault) != hipSuccess)
+      return fail(h, MLA_ERR_HIP, "hipHostMalloc of %zu plan bytes failed", need);
+    h->host_plan_bytes[b] = need;
+  }
+  unsigned char* blob = static_cast<unsigned char*>(h->host_plan[b]);
+  if (items_bytes) std::memcpy(blob, plan.items.data(), items_bytes);
+  if (merge_bytes) std::memcpy(blob + items_bytes, plan.merge.data(), merge_bytes);
+  if (counter_bytes) std::memset(blob + items_bytes + merge_bytes, 0, counter_bytes);
+  if (bins_bytes) std::memcpy(blob + items_bytes + merge_bytes + counter_bytes, plan.bins.data(), bins_bytes);
+  if (need) {
+    if (h->release_pending[b] && hipStreamWaitEvent(h->upload_stream, h->released[b], 0) != hipSuccess)
+      return fail(h, MLA_ERR_HIP, "ordering the plan upload after earlier runs failed");
+    if (hipMemcpyAsync(h->dev_plan[b], blob, need, hipMemcpyHostToDevice, h->upload_stream) != hipSuccess ||
+        hipEventRecord(h->uploaded[b], h->upload_stream) != hipSuccess)
+      return fail(h, MLA_ERR_HIP, "uploading the work list failed");
+    h->upload_pending[b] = true;
+  }
+  h->cur = b;
+  h->ran_since_plan = false;
+  h->waited = false;
 
   h->batch = qo_indptr_host[batch];  // output rows
   h->num_items = static_cast<int>(plan.items.size());
@@ -828,7 +889,16 @@ mla_status mla_decode_run(mla_decode_t h, const void* q, const void* kv, const v
   a.kv_indptr = kv_indptr;
   a.page_indices = kv_page_indices;
   a.page_shift = h->page_shift;
-  unsigned char* plan_base = static_cast<unsigned char*>(h->dev_plan);
+  // The first run of a plan on a stream waits for the plan's upload.
+  if (h->upload_pending[h->cur] && (!h->waited || h->waited_stream != s)) {
+    if (hipStreamWaitEvent(s, h->uploaded[h->cur], 0) != hipSuccess)
+      return fail(h, MLA_ERR_HIP, "ordering the run after the plan upload failed");
+    h->waited = true;
+    h->waited_stream = s;
+  }
+  h->ran_since_plan = true;
+  h->last_run_stream = s;
+  unsigned char* plan_base = static_cast<unsigned char*>(h->dev_plan[h->cur]);
   const size_t items_bytes = static_cast<size_t>(h->num_items) * sizeof(mla::WorkItem);
   a.items = reinterpret_cast<const mla::WorkItem*>(plan_base);
   a.part_o = static_cast<float*>(workspace);
@@ -943,7 +1013,13 @@ mla_status mla_decode_destroy(mla_decode_t h) {
   if (!h) return MLA_OK;
   {
     DeviceGuard guard(h->device);
-    if (h->dev_plan) (void)hipFree(h->dev_plan);
+    for (int k = 0; k < 2; ++k) {
+      if (h->dev_plan[k]) (void)hipFree(h->dev_plan[k]);
+      if (h->host_plan[k]) (void)hipHostFree(h->host_plan[k]);
+      if (h->uploaded[k]) (void)hipEventDestroy(h->uploaded[k]);
+      if (h->released[k]) (void)hipEventDestroy(h->released[k]);
+    }
+    if (h->upload_stream) (void)hipStreamDestroy(h->upload_stream);
     for (auto& e : h->ev)
       if (e) (void)hipEventDestroy(e);
   }

@@ -605,6 +605,42 @@ def test_replanning_one_handle(B, oracle_mod, fmt):
         dec.close()
 
 
+@pytest.mark.parametrize("fmt,ps", [("fp8", 1), ("fp8", 2), ("mxfp4", 1), ("bf16", 2)])
+def test_replan_while_runs_are_in_flight(B, oracle_mod, fmt, ps):
+    """A decode loop: every step appends one token to each sequence, re-plans
+    the handle and runs, with no host synchronisation between steps (the
+    plan's upload goes to the other of two plan buffers and each run waits for
+    its own upload on the device); two plans in a row without a run, and a
+    plan that needs a larger buffer, included.  Every step's output against
+    the oracle."""
+    steps = [[3000, 700, 129, 2500], [3001, 701, 130, 2501], None, [3002, 702, 131, 2502],
+             [3003, 703, 132, 2503] + [4000] * 40, [3004, 704, 133, 2504]]
+    dec = B.MlaDecode(fmt, ps)
+    try:
+        runs = []
+        for k, lens in enumerate(steps):
+            if lens is None:  # a plan no run uses
+                dec.plan(*_plan_args(synth.make_case(fmt, [5000, 9], seed=599, page_size=ps)))
+                continue
+            case = synth.make_case(fmt, lens, seed=600 + k, page_size=ps, shuffle_pages=ps > 1)
+            t = B.case_to_device(case)
+            out = torch.full((case.rows, 16, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
+            dec.plan(*_plan_args(case))
+            dec.run(t["q"], t["kv"], t["kv_scales"], t["kv_indptr"], out, t["kv_page_indices"],
+                    t["kv_last_page_len"])
+            runs.append((case, t, out))
+        torch.cuda.synchronize()
+        for k, (case, _t, out) in enumerate(runs):
+            check_close(out.float().cpu().numpy().astype(np.float64), oracle_out(oracle_mod, case), fmt,
+                        f"in-flight re-plan {fmt} ps {ps} step {k}")
+    finally:
+        dec.close()
+
+
+def _plan_args(case):
+    return case.kv_indptr, case.kv_last_page_len, 0, case.qo_indptr
+
+
 def test_run_validates_arguments(B):
     """Every malformed run is refused with a status and a message before anything is
     launched; the handle still runs correctly afterwards."""
