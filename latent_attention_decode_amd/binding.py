@@ -120,6 +120,55 @@ def _check_run_tensors(q, out, *int32_arrays) -> None:
             raise ValueError(f"kv_indptr and the page table arrays must be int32 (got {a.dtype})")
 
 
+ROW_BYTES = {"bf16": 2 * QK_DIM, "fp8": QK_DIM, "mxfp4": QK_DIM // 2}
+_KV_DTYPES = {"bf16": (torch.bfloat16, torch.uint8), "fp8": (torch.uint8, torch.float8_e4m3fn, torch.int8),
+              "mxfp4": (torch.uint8,)}
+
+
+def check_cache_tensors(kv_dtype: str, page_size: int, batch: int, indptr_end: int, total_tokens: int, kv,
+                        kv_scales, kv_indptr, kv_page_indices=None, kv_last_page_len=None) -> None:
+    """The cache tensors of a run against the handle's format and its plan.
+
+    A plan of `batch` sequences whose host kv_indptr ends at `indptr_end`
+    (tokens, or pages when page_size > 1) and covers `total_tokens` tokens
+    reads cache rows up to kv_indptr[-1] (contiguous), or page-table entries
+    up to kv_indptr[-1] (paged), and per MXFP4 row 18 scale bytes.  The
+    library takes bare pointers, so a tensor of the wrong element type or too
+    few rows is refused here.  (With pages, the page ids themselves sit in
+    device memory and are not checked: each must name a page inside kv.)"""
+    rb = ROW_BYTES[kv_dtype]
+    if total_tokens == 0 and kv is None:
+        return
+    if kv is None:
+        raise ValueError("kv is None for a plan that reads the cache")
+    if kv.dtype not in _KV_DTYPES[kv_dtype]:
+        raise ValueError(f"a {kv_dtype} cache cannot be a {kv.dtype} tensor")
+    if kv.dim() < 2 or kv.shape[-1] * kv.element_size() != rb:
+        raise ValueError(f"{kv_dtype} cache rows are {rb} bytes (got {kv.dtype} {tuple(kv.shape)})")
+    rows = kv.numel() * kv.element_size() // rb
+    if page_size == 1 and rows < indptr_end:
+        raise ValueError(f"the plan reads cache rows up to {indptr_end}; kv holds {rows}")
+    if page_size > 1:
+        if rows < page_size:
+            raise ValueError(f"kv holds {rows} rows, less than one page of {page_size}")
+        if kv_page_indices is None or kv_page_indices.numel() < indptr_end:
+            raise ValueError(f"the plan reads {indptr_end} page-table entries; kv_page_indices holds "
+                             f"{0 if kv_page_indices is None else kv_page_indices.numel()}")
+        if kv_last_page_len is None or kv_last_page_len.numel() < batch:
+            raise ValueError(f"kv_last_page_len needs {batch} entries")
+    if kv_indptr.numel() < batch + 1:
+        raise ValueError(f"kv_indptr needs {batch + 1} entries (got {kv_indptr.numel()})")
+    if kv_dtype == "fp8":
+        if kv_scales is None or kv_scales.dtype is not torch.float32 or kv_scales.numel() < 1:
+            raise ValueError("an fp8 cache takes kv_scales: one float32 per-tensor scale")
+    elif kv_dtype == "mxfp4":
+        if (kv_scales is None or kv_scales.dtype is not torch.uint8 or kv_scales.dim() != 2
+                or kv_scales.shape[1] < 18):
+            raise ValueError("an MXFP4 cache takes kv_scales: uint8 [rows, stride >= 18] e8m0 scales")
+        if kv_scales.shape[0] < rows:
+            raise ValueError(f"kv_scales holds {kv_scales.shape[0]} rows of scales for {rows} cache rows")
+
+
 def mla_decode_version() -> int:
     return _lib.mla_decode_version()
 
@@ -321,6 +370,15 @@ class MlaDecode:
                                            split_override)
             rows = int(_host_i32(qo_indptr_host)[-1])
         self.rows = rows  # query / output rows the plan covers
+        ip = _host_i32(kv_indptr_host)
+        self._batch = len(ip) - 1
+        self._indptr_end = int(ip[-1])
+        if self.page_size == 1:
+            self._total_tokens = int(ip[-1] - ip[0])
+        else:
+            lp = _host_i32(kv_last_page_len_host)
+            n = np.diff(ip.astype(np.int64))
+            self._total_tokens = int(np.where(n > 0, (n - 1) * self.page_size + lp[:len(n)], 0).sum())
         if nbytes and (self.workspace is None or self.workspace.numel() * 4 < nbytes):
             self.workspace = torch.empty((nbytes + 3) // 4, dtype=torch.float32,
                                          device=f"cuda:{self.device}")
@@ -329,6 +387,7 @@ class MlaDecode:
     def run(self, q, kv, kv_scales, kv_indptr, out, kv_page_indices=None, kv_last_page_len=None,
             stream=None) -> torch.Tensor:
         self._check_rows(q, out)
+        self._check_cache(kv, kv_scales, kv_indptr, kv_page_indices, kv_last_page_len)
         mla_decode_run(self.h, q, kv, kv_scales, kv_indptr, out, self.workspace, kv_page_indices,
                        kv_last_page_len, stream)
         return out
@@ -337,8 +396,15 @@ class MlaDecode:
                 stream=None) -> PreparedRun:
         """A PreparedRun of this handle's current plan and workspace."""
         self._check_rows(q, out)
+        self._check_cache(kv, kv_scales, kv_indptr, kv_page_indices, kv_last_page_len)
         return PreparedRun(self.h, q, kv, kv_scales, kv_indptr, out, self.workspace, kv_page_indices,
                            kv_last_page_len, stream)
+
+    def _check_cache(self, kv, kv_scales, kv_indptr, kv_page_indices, kv_last_page_len) -> None:
+        if self.rows is None:
+            raise ValueError("run before a successful plan")
+        check_cache_tensors(self.kv_dtype, self.page_size, self._batch, self._indptr_end, self._total_tokens, kv,
+                            kv_scales, kv_indptr, kv_page_indices, kv_last_page_len)
 
     def _check_rows(self, q, out) -> None:
         if self.rows is not None and (q.numel() // (NUM_HEADS * QK_DIM) < self.rows

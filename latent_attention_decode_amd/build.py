@@ -23,12 +23,22 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, sanitize: str = "", out: str = LIB) -> str:
+    """Compile the library to `out`.  sanitize = "address" or "undefined"
+    instruments the host code only (each -fsanitize= goes after -Xarch_host;
+    the device code is built as usual) and links the sanitizer runtime
+    dynamically; such a build is for host-side tests of the planner and the
+    argument checks, loaded with the runtime preloaded."""
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-mllvm", "-amdgpu-mfma-vgpr-form",
            "-Wall", "-Wno-unused-command-line-argument",
-           "-I", INCLUDE, "-I", CSRC, "-o", LIB + ".tmp"] + SOURCES
+           "-I", INCLUDE, "-I", CSRC, "-o", out + ".tmp"] + SOURCES
+    if sanitize:
+        if sanitize not in ("address", "undefined"):
+            raise ValueError("sanitize must be 'address' or 'undefined'")
+        cmd[1:1] = ["-Xarch_host", f"-fsanitize={sanitize}", "-Xarch_host", "-fno-omit-frame-pointer",
+                    "-Xarch_host", "-fno-sanitize-recover=all", "-shared-libsan", "-g"]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -39,8 +49,21 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def sanitizer_runtime(sanitize: str) -> str:
+    """Path of the clang sanitizer runtime that a build(sanitize=...) library
+    links against (to preload into a process that loads the library)."""
+    import glob
+    name = {"address": "libclang_rt.asan-x86_64.so", "undefined": "libclang_rt.ubsan_standalone-x86_64.so"}[sanitize]
+    hits = sorted(glob.glob(os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(HIPCC))),
+                                         "llvm", "lib", "clang", "*", "lib", "linux", name)))
+    hits += sorted(glob.glob(os.path.join("/opt/rocm/llvm/lib/clang/*/lib/linux", name)))
+    if not hits:
+        raise FileNotFoundError(name)
+    return hits[0]
 
 
 if __name__ == "__main__":

@@ -103,6 +103,17 @@ struct DeviceGuard {
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
+// The integer a C caller passed for an enum parameter.  A C caller may pass
+// any int, and loading a value outside the enumerators' range as the C++ enum
+// type is undefined, so the value is read from its object representation.
+template <class E>
+int enum_value(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "C enums are int-sized");
+  int v;
+  std::memcpy(&v, &e, sizeof v);
+  return v;
+}
+
 size_t slot_bytes() {
   return static_cast<size_t>(mla::kNumHeads) * (mla::kVDim + 1) * sizeof(float);
 }
@@ -592,7 +603,7 @@ extern "C" {
 int mla_decode_version(void) { return kVersion; }
 
 const char* mla_status_string(mla_status s) {
-  switch (s) {
+  switch (enum_value(s)) {
     case MLA_OK: return "MLA_OK";
     case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG";
     case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
@@ -611,13 +622,13 @@ mla_status mla_decode_create(mla_decode_t* out, int device, int num_heads, int q
     return MLA_ERR_INVALID_ARG;
   if (num_heads != mla::kNumHeads || qk_dim != mla::kQkDim || v_dim != mla::kVDim)
     return MLA_ERR_UNSUPPORTED;
-  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3 && kv_dtype != MLA_KV_MXFP4)
-    return MLA_ERR_UNSUPPORTED;
+  const int fmt = enum_value(kv_dtype);
+  if (fmt != MLA_KV_BF16 && fmt != MLA_KV_FP8_E4M3 && fmt != MLA_KV_MXFP4) return MLA_ERR_UNSUPPORTED;
   if (!is_pow2(page_size) || page_size > 1024) return MLA_ERR_UNSUPPORTED;
   mla_decode_t h = new (std::nothrow) mla_decode_s();
   if (!h) return MLA_ERR_INVALID_ARG;
   h->device = device;
-  h->kv_dtype = kv_dtype;
+  h->kv_dtype = fmt;
   h->page_size = page_size;
   while ((1 << h->page_shift) < page_size) ++h->page_shift;
   h->sm_scale = sm_scale;
@@ -760,7 +771,7 @@ mla_status plan_impl(mla_decode_t h, int batch, const int32_t* qo_indptr_host, c
 }
 
 mla_status preview_impl(int batch, const int32_t* qo_indptr_host, const int32_t* kv_indptr_host,
-                        const int32_t* kv_last_page_len_host, int page_size, mla_kv_dtype kv_dtype,
+                        const int32_t* kv_last_page_len_host, int page_size, int kv_dtype,
                         int split_override, int num_cus, int blocks_per_cu, int32_t* items_out, int max_items,
                         int* num_items, int* num_slots, size_t* workspace_bytes) {
   if (batch < 1 || !kv_indptr_host || page_size < 1 || !is_pow2(page_size) || split_override < 0 ||
@@ -823,7 +834,8 @@ mla_status mla_decode_plan_preview(int batch, const int32_t* kv_indptr_host,
                                    mla_kv_dtype kv_dtype, int split_override, int num_cus,
                                    int blocks_per_cu, int32_t* items_out, int max_items,
                                    int* num_items, int* num_slots, size_t* workspace_bytes) {
-  return preview_impl(batch, nullptr, kv_indptr_host, kv_last_page_len_host, page_size, kv_dtype, split_override,
+  return preview_impl(batch, nullptr, kv_indptr_host, kv_last_page_len_host, page_size, enum_value(kv_dtype),
+                      split_override,
                       num_cus, blocks_per_cu, items_out, max_items, num_items, num_slots, workspace_bytes);
 }
 
@@ -833,8 +845,8 @@ mla_status mla_decode_plan_preview_multi(int batch, const int32_t* qo_indptr_hos
                                          int blocks_per_cu, int32_t* items_out, int max_items,
                                          int* num_items, int* num_slots, size_t* workspace_bytes) {
   if (!qo_indptr_host) return MLA_ERR_INVALID_ARG;
-  return preview_impl(batch, qo_indptr_host, kv_indptr_host, kv_last_page_len_host, page_size, kv_dtype,
-                      split_override, num_cus, blocks_per_cu, items_out, max_items, num_items, num_slots,
+  return preview_impl(batch, qo_indptr_host, kv_indptr_host, kv_last_page_len_host, page_size,
+                      enum_value(kv_dtype), split_override, num_cus, blocks_per_cu, items_out, max_items, num_items, num_slots,
                       workspace_bytes);
 }
 

@@ -112,6 +112,49 @@ def test_run_rejects_wrong_tensor_types_and_shapes(B):
             B.PreparedRun(None, qq, None, None, ii, oo)
 
 
+def test_cache_tensors_are_checked_against_the_plan(B):
+    """The handle's format and plan fix the cache's element type, row bytes and
+    row count, the page table's length and the scales; each mismatch is refused
+    before a pointer reaches the library."""
+    import torch
+    u8 = torch.uint8
+    ip = torch.tensor([0, 4, 8], dtype=torch.int32)
+    fp8_scale = torch.ones(1, dtype=torch.float32)
+    ok = dict(kv_dtype="fp8", page_size=1, batch=2, indptr_end=8, total_tokens=8,
+              kv=torch.zeros((8, 576), dtype=u8), kv_scales=fp8_scale, kv_indptr=ip)
+    B.check_cache_tensors(**ok)
+    bad = [
+        (dict(kv=torch.zeros((8, 576), dtype=torch.bfloat16)), "cannot be a"),          # bf16 tensor, fp8 handle
+        (dict(kv=torch.zeros((8, 288), dtype=u8)), "rows are 576 bytes"),
+        (dict(kv=torch.zeros((7, 576), dtype=u8)), "up to 8"),                          # too few rows
+        (dict(kv=None), "kv is None"),
+        (dict(kv_scales=None), "per-tensor scale"),
+        (dict(kv_scales=torch.ones(1, dtype=torch.float64)), "per-tensor scale"),
+        (dict(kv_indptr=ip[:2]), "kv_indptr needs 3"),
+        (dict(kv_dtype="bf16", kv=torch.zeros((8, 576), dtype=u8)), "rows are 1152 bytes"),
+        (dict(kv_dtype="mxfp4", kv=torch.zeros((8, 288), dtype=u8), kv_scales=torch.zeros((8, 17), dtype=u8)),
+         "stride >= 18"),
+        (dict(kv_dtype="mxfp4", kv=torch.zeros((8, 288), dtype=u8), kv_scales=torch.zeros((7, 18), dtype=u8)),
+         "7 rows of scales"),
+        (dict(kv_dtype="mxfp4", kv=torch.zeros((8, 288), dtype=u8), kv_scales=fp8_scale), "e8m0"),
+        (dict(page_size=4, indptr_end=3, kv=torch.zeros((12, 576), dtype=u8),
+              kv_page_indices=torch.zeros(2, dtype=torch.int32), kv_last_page_len=torch.ones(2, dtype=torch.int32)),
+         "3 page-table entries"),
+        (dict(page_size=4, indptr_end=3, kv=torch.zeros((12, 576), dtype=u8),
+              kv_page_indices=torch.zeros(3, dtype=torch.int32), kv_last_page_len=None), "kv_last_page_len"),
+        (dict(page_size=4, indptr_end=3, kv=torch.zeros((3, 576), dtype=u8),
+              kv_page_indices=torch.zeros(3, dtype=torch.int32), kv_last_page_len=torch.ones(2, dtype=torch.int32)),
+         "less than one page"),
+    ]
+    for change, msg in bad:
+        with pytest.raises(ValueError, match=msg):
+            B.check_cache_tensors(**{**ok, **change})
+    # accepted: the bf16 cache as bf16 elements or bytes, an empty plan without a cache
+    B.check_cache_tensors(**{**ok, "kv_dtype": "bf16", "kv": torch.zeros((8, 576), dtype=torch.bfloat16)})
+    B.check_cache_tensors(**{**ok, "kv_dtype": "bf16", "kv": torch.zeros((8, 1152), dtype=u8)})
+    B.check_cache_tensors(**{**ok, "total_tokens": 0, "indptr_end": 0, "kv": None})
+
+
 def _check_cover(items, lens, slots):
     """Every token of every sequence is in exactly one item; slots are a partition;
     items are listed workgroup by workgroup."""
