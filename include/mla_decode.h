@@ -206,7 +206,11 @@ mla_status mla_decode_plan_info(mla_decode_t h, int* num_items, int* max_splits,
 
 /*
  * Run the planned decode on `stream` (a hipStream_t; NULL = the default
- * stream).  Asynchronous: no allocation, no host synchronisation.
+ * stream).  Asynchronous: no allocation, no host synchronisation.  The split
+ * kernel, then (when the plan needs one) the log-sum-exp merge, on that one
+ * stream: the launchers `run_s1` / `run_rd` of 727205 ("v25: LEAN") and
+ * `hip_mla_v71` of 700955 ("locked baseline dispatch"), with the work list of
+ * the plan in place of their (batch x splits) grids.
  *   q                 bf16 [batch, 16, 576], row-major, 16-byte aligned.
  *   kv                cache rows (layout above), 16-byte aligned; may be NULL
  *                     only when every planned sequence is empty.
@@ -266,7 +270,12 @@ mla_status mla_decode_kernel_time_ms(mla_decode_t h, int which, float* ms);
 mla_status mla_decode_kernel_resources(mla_decode_t h, int which, int* vgprs, int* lds_bytes,
                                        int* scratch_bytes);
 
-/* Destroy a handle (NULL is accepted and ignored). */
+/*
+ * Destroy a handle (NULL is accepted and ignored): frees its plan buffers,
+ * upload stream and events.  No run of the handle may still be executing.
+ * (The pages keep such per-shape state in module-level caches: 727205
+ * `_cache`, 700955 `_cache` and `_custom_v71_scratch_cache`.)
+ */
 mla_status mla_decode_destroy(mla_decode_t h);
 
 /* Detail of the last failure on this handle (empty string if none). */

@@ -268,7 +268,11 @@ __device__ __forceinline__ void finish_item(const Stage1Args& a, const WorkItem&
     // partials are read back with device-scope loads.  That publishes the data
     // without a device-scope release / acquire fence, which would write back
     // or invalidate the whole L2 of the XCD.  The item that finishes last
-    // merges; nothing waits on another workgroup.
+    // merges; nothing waits on another workgroup.  The ordering rests on how
+    // gfx950 executes these instructions (sc1 stores written through and
+    // acknowledged before s_waitcnt returns, the counter atomic at the shared
+    // level, sc1 loads missing the XCD's L2), not on the language's memory
+    // model, under which relaxed operations alone would not order them.
     // Layout of a slot here: float (4v + i) of lane l in column group W at
     // 2048 W + 64 (4v + i) + l, so that each store writes 256 bytes in a row.
     float* pdst = a.part_o + (int64_t)item.slot * (4 * kSlotFloat4) + 2048 * W + lane;
