@@ -109,6 +109,14 @@ __device__ __forceinline__ void dma_u16(const uint8_t* base, uint32_t off, uint3
 }
 #pragma clang diagnostic pop
 
+// An fp4 MX operand (16 bytes per lane) in the instruction's 8-register
+// tuple, whose upper half the instruction does not read.
+__device__ __forceinline__ fp8x32 fp4_operand(u32x4 w) {
+  typedef int i32x4v __attribute__((ext_vector_type(4)));
+  const i32x4v v = __builtin_bit_cast(i32x4v, w);
+  return __builtin_shufflevector(v, v, 0, 1, 2, 3, -1, -1, -1, -1);
+}
+
 // fp4 (A) x fp8 (B) MX step with A block scale sa (e8m0) and unit B scale.
 __device__ __forceinline__ f32x4 mfma_fp4_fp8(fp8x32 a, fp8x32 b, f32x4 c, uint32_t sa) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, 0, (int)sa, 0, 127);
@@ -385,6 +393,8 @@ __device__ __forceinline__ void mxfp4_item(const Stage1Args& a, const WorkItem& 
     const uint8_t* sdw = raw + kXFp4Bytes;  // scale pair (row, p) at dword 9 row + p
 
     // ---- scores of tokens 16w + (0..15) ----
+    // The fp4 A operand is 16 bytes; the upper half of its register tuple is
+    // not read, so it is left undefined rather than zeroed.
     f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
     {
       const int row = 16 * wave + r16;
@@ -395,7 +405,7 @@ __device__ __forceinline__ void mxfp4_item(const Stage1Args& a, const WorkItem& 
         const int blk = 4 * K + g;
         const uint32_t sa = sp[4 * (blk >> 1) + (blk & 1)];
         const u32x4 w = *reinterpret_cast<const u32x4*>(rp + 64 * K + 16 * g);
-        const fp8x32 ka = fp8x32{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
+        const fp8x32 ka = fp4_operand(w);
         sacc[0] = mfma_fp4_fp8(ka, qh[K], sacc[0], sa);
         sacc[1] = mfma_fp4_fp8(ka, ql[K], sacc[1], sa);
       }
@@ -405,7 +415,7 @@ __device__ __forceinline__ void mxfp4_item(const Stage1Args& a, const WorkItem& 
         w = *reinterpret_cast<const u32x4*>(rp + 256 + 16 * g);
         sa = sp[4 * 8 + g];
       }
-      const fp8x32 ka = fp8x32{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
+      const fp8x32 ka = fp4_operand(w);
       sacc[0] = mfma_fp4_fp8(ka, rh, sacc[0], sa);
       sacc[1] = mfma_fp4_fp8(ka, rl, sacc[1], sa);
     }
@@ -414,40 +424,34 @@ __device__ __forceinline__ void mxfp4_item(const Stage1Args& a, const WorkItem& 
     // V scale E (the largest of its 16 e8m0 scales of columns 0..511) ----
     // This lane converts token row 16w + r16, column blocks 4k + g; the four
     // lane groups together hold the row's 16 scales, so E is their maximum.
+    // By table, exact for blocks within 5 binades of the row's E (nearly all);
+    // the rare block further below is converted again, by rounding
+    // conversions, after the softmax (so that the common path has no branch
+    // and the score steps can overlap this vector work).
     float erow;  // E of token 16w + r16
+    int jv[4];   // shift of each block, <= 0
+    u32x4 wv[4];
+    uint8_t* const vdst = &sh.v[cv_row * kXVRow + 32 * g];
     {
       uint32_t e[4];
-      u32x4 w[4];
       const uint8_t* rsrc = raw + cv_row * kXRow + 16 * g;
       const uint8_t* ssrc = sdw + 4 * kXScalePairs * cv_row + 4 * (g >> 1) + (g & 1);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         e[k] = ssrc[8 * k];
-        w[k] = *reinterpret_cast<const u32x4*>(rsrc + 64 * k);
+        wv[k] = *reinterpret_cast<const u32x4*>(rsrc + 64 * k);
       }
       erow = xor_max_groups((float)max(max(e[0], e[1]), max(e[2], e[3])));
       const int E = (int)erow;
-      uint8_t* vdst = &sh.v[cv_row * kXVRow + 32 * g];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int j = max((int)e[k] - E, -126);  // <= 0
+        jv[k] = max((int)e[k] - E, -126);
+        const uint32_t kk = (uint32_t)min(-jv[k], 5);
+        const uint32_t lut_lo = 0x3C383000u - kk * 0x08080800u;
+        const uint32_t lut_hi = 0x4C484440u - kk * 0x08080808u;
         uint32_t e8[8];  // 32 e4m3 codes: word 2i columns 32cb + 8i + {0,2,4,6}, word 2i+1 the odd ones
-        if (__ballot(j < -5) == 0) {  // the whole wave by table
-          const uint32_t kk = (uint32_t)(-j);
-          const uint32_t lut_lo = 0x3C383000u - kk * 0x08080800u;
-          const uint32_t lut_hi = 0x4C484440u - kk * 0x08080808u;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) fp4x8_to_fp8_lut(w[k][i], lut_lo, lut_hi, e8[2 * i], e8[2 * i + 1]);
-        } else {  // a scale more than 5 binades below the row's largest: rounding conversions
-          const float scale = __uint_as_float((uint32_t)(127 + j) << 23);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            uint32_t lo, hi;  // columns 0..3, 4..7
-            fp4x8_to_fp8(w[k][i], scale, lo, hi);
-            e8[2 * i] = __builtin_amdgcn_perm(hi, lo, 0x06040200u);      // columns 0, 2, 4, 6
-            e8[2 * i + 1] = __builtin_amdgcn_perm(hi, lo, 0x07050301u);  // columns 1, 3, 5, 7
-          }
-        }
+        for (int i = 0; i < 4; ++i) fp4x8_to_fp8_lut(wv[k][i], lut_lo, lut_hi, e8[2 * i], e8[2 * i + 1]);
         *reinterpret_cast<u32x4*>(vdst + 128 * k) = u32x4{e8[0], e8[1], e8[2], e8[3]};
         *reinterpret_cast<u32x4*>(vdst + 128 * k + 16) = u32x4{e8[4], e8[5], e8[6], e8[7]};
       }
@@ -458,22 +462,53 @@ __device__ __forceinline__ void mxfp4_item(const Stage1Args& a, const WorkItem& 
     // scale 2^(E - 127), which the e4m3 V rows leave out; the weights of a
     // 32-token k-block of P.V (waves 2j, 2j + 1) are written relative to the
     // block's largest y (weight_block_scale), once both waves' maxima are in.
-    float x[4], y[4];
-    float tmax = kNegInf, ymax = kNegInf;
+    // The sum of this lane's weights is taken against the wave's own integral
+    // reference c (the floor of its tile maximum) and moved to the running
+    // maximum's scale once that is known.
+    float y[4];
+    float lsum = 0.f, cw;
+    bool wlive;
+    {
+      float x[4];
+      float tmax = kNegInf, ymax = kNegInf;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float ei = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (4 * g + i), __float_as_int(erow)));
-      x[i] = (sacc[0][i] + sacc[1][i]) * xscale;
-      if (tok0 + 16 * wave + 4 * g + i > tok_last) x[i] = kNegInf;
-      y[i] = x[i] + (ei - 127.0f);
-      tmax = fmaxf(tmax, x[i]);
-      ymax = fmaxf(ymax, y[i]);
+      for (int i = 0; i < 4; ++i) {
+        const float ei = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (4 * g + i), __float_as_int(erow)));
+        x[i] = (sacc[0][i] + sacc[1][i]) * xscale;
+        if (tok0 + 16 * wave + 4 * g + i > tok_last) x[i] = kNegInf;
+        y[i] = x[i] + (ei - 127.0f);
+        tmax = fmaxf(tmax, x[i]);
+        ymax = fmaxf(ymax, y[i]);
+      }
+      tmax = xor_max_groups(tmax);
+      ymax = xor_max_groups(ymax);
+      if (g == 0) {
+        sh.red_m[r16][wave] = tmax;
+        sh.red_y[r16][wave] = ymax;
+      }
+      wlive = tmax != kNegInf;
+      cw = weight_block_floor(tmax);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lsum += __builtin_amdgcn_exp2f(x[i] - cw);
     }
-    tmax = xor_max_groups(tmax);
-    ymax = xor_max_groups(ymax);
-    if (g == 0) {
-      sh.red_m[r16][wave] = tmax;
-      sh.red_y[r16][wave] = ymax;
+    // blocks more than 5 binades below their row's E: by rounding
+    // conversions (exact within 8 binades, rounded to e4m3 beyond)
+    if (__ballot(min(min(jv[0], jv[1]), min(jv[2], jv[3])) < -5) != 0) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (jv[k] >= -5) continue;
+        const float scale = __uint_as_float((uint32_t)(127 + jv[k]) << 23);
+        uint32_t e8[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint32_t lo, hi;  // columns 0..3, 4..7
+          fp4x8_to_fp8(wv[k][i], scale, lo, hi);
+          e8[2 * i] = __builtin_amdgcn_perm(hi, lo, 0x06040200u);      // columns 0, 2, 4, 6
+          e8[2 * i + 1] = __builtin_amdgcn_perm(hi, lo, 0x07050301u);  // columns 1, 3, 5, 7
+        }
+        *reinterpret_cast<u32x4*>(vdst + 128 * k) = u32x4{e8[0], e8[1], e8[2], e8[3]};
+        *reinterpret_cast<u32x4*>(vdst + 128 * k + 16) = u32x4{e8[4], e8[5], e8[6], e8[7]};
+      }
     }
     lds_barrier();  // maxima and the V tile; raw slot t % 2 is free
     if (t + 2 < ntiles) issue(t + 2);
@@ -493,6 +528,7 @@ __device__ __forceinline__ void mxfp4_item(const Stage1Args& a, const WorkItem& 
       l_part *= alpha;
       m_ref = m_new;
     }
+    if (wlive) l_part += __builtin_ldexpf(lsum, (int)cw - (int)m_ref);
     // block maxima of y: k-block j is waves 2j, 2j + 1
     const float yb0 = fmaxf(my0[0], my0[1]), yb1 = fmaxf(my0[2], my0[3]);
     const float yb2 = fmaxf(my1[0], my1[1]), yb3 = fmaxf(my1[2], my1[3]);
@@ -503,10 +539,7 @@ __device__ __forceinline__ void mxfp4_item(const Stage1Args& a, const WorkItem& 
       float p[4];
       uint32_t ph, pl;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[i] = __builtin_amdgcn_exp2f(y[i] + shift);
-        l_part += __builtin_amdgcn_exp2f(x[i] - m_ref);
-      }
+      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(y[i] + shift);
       split_fp8x4(p[0], p[1], p[2], p[3], ph, pl);
       *reinterpret_cast<uint32_t*>(p_hi + 16 * wave + 4 * g) = ph;
       *reinterpret_cast<uint32_t*>(p_lo + 16 * wave + 4 * g) = pl;
