@@ -85,8 +85,9 @@ struct Fp4Lds {
   uint8_t raw[2][kXRawBytes];              // e2m1 rows, then the scale dwords
   uint8_t v[kXVBytes];                     // V of the current tile as e4m3 [token][dim]; first the query
   uint8_t p[2][kNumHeads][kPRow];          // P^T hi / lo as [head][token]
-  float red_m[kNumHeads][kXWaves];         // per-wave tile maxima of the logits
-  float red_y[kNumHeads][kXWaves];         // per-wave maxima of logit + row scale; the sums at the end
+  float red_m[kNumHeads][kXWaves];         // query head maxima (8 waves), then per scoring wave logit maxima
+  float red_y[kNumHeads][4];               // per scoring wave: maxima of logit + row scale
+  float red_l[kNumHeads][4];               // per scoring wave: weight sums, at the end
   int32_t pages[kMaxItemPages];            // paged: page ids of the item
 };
 
@@ -368,12 +369,17 @@ __device__ __forceinline__ void mxfp4_item(const Stage1Args& a, const WorkItem& 
   float m_ref = kNegInf;
   float l_part = 0.f;
 
-  // Reads of this lane.  Scores: row 16w + r16 of the raw tile.  V^T: tr8
-  // read q (0..3) gives tokens tb(q) + (0..7), tb = 16g + 8q (q < 2) or
-  // 64 + 16g + 8(q - 2), from rows tb(q) + (r16 >> 1), columns
-  // 64w + 16v + 8(r16 & 1).  Conversion: the lane takes token row 16w + r16
-  // (the wave's own tokens) and column blocks 4k + g, k = 0..3.
-  const int cv_row = 16 * wave + r16;
+  // Roles.  Waves 0-3 score: wave s takes the 32 tokens 32s..32s+31 of the
+  // tile (two 16-row MFMA blocks), which are exactly k-block s of the P.V
+  // step, so the maximum that scales the block's weights is the wave's own.
+  // Waves 4-7 convert V: wave 4 + c converts token rows 32c..32c+31, lane l
+  // row 32c + (l & 31) and column blocks 8(l >> 5)..+7.  With one scoring and
+  // one converting wave on each SIMD, the matrix steps of one overlap the
+  // vector work of the other.  Then every wave runs P.V for its 64 columns.
+  // Reads of this lane for P.V: tr8 read q (0..3) gives tokens tb(q) +
+  // (0..7), tb = 16g + 8q (q < 2) or 64 + 16g + 8(q - 2), from rows tb(q) +
+  // (r16 >> 1), columns 64w + 16v + 8(r16 & 1).
+  const bool scorer = wave < 4;
   int voff[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q)
@@ -392,94 +398,78 @@ __device__ __forceinline__ void mxfp4_item(const Stage1Args& a, const WorkItem& 
     const uint8_t* raw = &sh.raw[t & 1][0];
     const uint8_t* sdw = raw + kXFp4Bytes;  // scale pair (row, p) at dword 9 row + p
 
-    // ---- scores of tokens 16w + (0..15) ----
-    // The fp4 A operand is 16 bytes; the upper half of its register tuple is
-    // not read, so it is left undefined rather than zeroed.
-    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    {
-      const int row = 16 * wave + r16;
-      const uint8_t* rp = raw + row * kXRow;
-      const uint8_t* sp = sdw + 4 * kXScalePairs * row;
+    float lsum = 0.f, cw = 0.f;  // scorers: this lane's weights against the wave's reference cw
+    bool wlive = false;
+    if (scorer) {
+      // ---- scores of tokens 32s + 16h + (0..15), h = 0, 1 ----
+      // The fp4 A operand is 16 bytes; the upper half of its register tuple
+      // is not read, so it is left undefined rather than zeroed.
+      f32x4 sacc[2][2];
 #pragma unroll
-      for (int K = 0; K < 4; ++K) {
-        const int blk = 4 * K + g;
-        const uint32_t sa = sp[4 * (blk >> 1) + (blk & 1)];
-        const u32x4 w = *reinterpret_cast<const u32x4*>(rp + 64 * K + 16 * g);
+      for (int h = 0; h < 2; ++h) sacc[h][0] = sacc[h][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int row = 32 * wave + 16 * h + r16;
+        const uint8_t* rp = raw + row * kXRow;
+        const uint8_t* sp = sdw + 4 * kXScalePairs * row;
+#pragma unroll
+        for (int K = 0; K < 4; ++K) {
+          const int blk = 4 * K + g;
+          const uint32_t sa = sp[4 * (blk >> 1) + (blk & 1)];
+          const fp8x32 ka = fp4_operand(*reinterpret_cast<const u32x4*>(rp + 64 * K + 16 * g));
+          sacc[h][0] = mfma_fp4_fp8(ka, qh[K], sacc[h][0], sa);
+          sacc[h][1] = mfma_fp4_fp8(ka, ql[K], sacc[h][1], sa);
+        }
+        u32x4 w = {0u, 0u, 0u, 0u};
+        uint32_t sa = 127;
+        if (g < 2) {
+          w = *reinterpret_cast<const u32x4*>(rp + 256 + 16 * g);
+          sa = sp[4 * 8 + g];
+        }
         const fp8x32 ka = fp4_operand(w);
-        sacc[0] = mfma_fp4_fp8(ka, qh[K], sacc[0], sa);
-        sacc[1] = mfma_fp4_fp8(ka, ql[K], sacc[1], sa);
+        sacc[h][0] = mfma_fp4_fp8(ka, rh, sacc[h][0], sa);
+        sacc[h][1] = mfma_fp4_fp8(ka, rl, sacc[h][1], sa);
       }
-      u32x4 w = {0u, 0u, 0u, 0u};
-      uint32_t sa = 127;
-      if (g < 2) {
-        w = *reinterpret_cast<const u32x4*>(rp + 256 + 16 * g);
-        sa = sp[4 * 8 + g];
-      }
-      const fp8x32 ka = fp4_operand(w);
-      sacc[0] = mfma_fp4_fp8(ka, rh, sacc[0], sa);
-      sacc[1] = mfma_fp4_fp8(ka, rl, sacc[1], sa);
-    }
 
-    // ---- V of this tile to e4m3, each token row relative to its own largest
-    // V scale E (the largest of its 16 e8m0 scales of columns 0..511) ----
-    // This lane converts token row 16w + r16, column blocks 4k + g; the four
-    // lane groups together hold the row's 16 scales, so E is their maximum.
-    // By table, exact for blocks within 5 binades of the row's E (nearly all);
-    // the rare block further below is converted again, by rounding
-    // conversions, after the softmax (so that the common path has no branch
-    // and the score steps can overlap this vector work).
-    float erow;  // E of token 16w + r16
-    int jv[4];   // shift of each block, <= 0
-    u32x4 wv[4];
-    uint8_t* const vdst = &sh.v[cv_row * kXVRow + 32 * g];
-    {
-      uint32_t e[4];
-      const uint8_t* rsrc = raw + cv_row * kXRow + 16 * g;
-      const uint8_t* ssrc = sdw + 4 * kXScalePairs * cv_row + 4 * (g >> 1) + (g & 1);
+      // E of the wave's tokens (the largest of each row's 16 scales of
+      // columns 0..511): lanes l and l ^ 32 take 8 scales each of token
+      // 32s + (l & 31); then lane (head r16, group g) fetches the E of its
+      // tokens 16h + 4g + i.
+      float erow;
+      {
+        const uint32_t* srow = reinterpret_cast<const uint32_t*>(sdw) + kXScalePairs * (32 * wave + (lane & 31)) +
+                               4 * (lane >> 5);
+        uint32_t em = 0;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        e[k] = ssrc[8 * k];
-        wv[k] = *reinterpret_cast<const u32x4*>(rsrc + 64 * k);
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t d = srow[k];  // scale pair in the low 16 bits
+          em = max(em, max(d & 0xFFu, (d >> 8) & 0xFFu));
+        }
+        const auto sw = __builtin_amdgcn_permlane32_swap(em, em, false, false);
+        erow = (float)max((uint32_t)sw[0], (uint32_t)sw[1]);
       }
-      erow = xor_max_groups((float)max(max(e[0], e[1]), max(e[2], e[3])));
-      const int E = (int)erow;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        jv[k] = max((int)e[k] - E, -126);
-        const uint32_t kk = (uint32_t)min(-jv[k], 5);
-        const uint32_t lut_lo = 0x3C383000u - kk * 0x08080800u;
-        const uint32_t lut_hi = 0x4C484440u - kk * 0x08080808u;
-        uint32_t e8[8];  // 32 e4m3 codes: word 2i columns 32cb + 8i + {0,2,4,6}, word 2i+1 the odd ones
-#pragma unroll
-        for (int i = 0; i < 4; ++i) fp4x8_to_fp8_lut(wv[k][i], lut_lo, lut_hi, e8[2 * i], e8[2 * i + 1]);
-        *reinterpret_cast<u32x4*>(vdst + 128 * k) = u32x4{e8[0], e8[1], e8[2], e8[3]};
-        *reinterpret_cast<u32x4*>(vdst + 128 * k + 16) = u32x4{e8[4], e8[5], e8[6], e8[7]};
-      }
-    }
 
-    // ---- softmax: x[i] is token 16w + 4g + i of head r16 ----
-    // y = x + E - 127 is the log2 size of the token's weight times its row
-    // scale 2^(E - 127), which the e4m3 V rows leave out; the weights of a
-    // 32-token k-block of P.V (waves 2j, 2j + 1) are written relative to the
-    // block's largest y (weight_block_scale), once both waves' maxima are in.
-    // The sum of this lane's weights is taken against the wave's own integral
-    // reference c (the floor of its tile maximum) and moved to the running
-    // maximum's scale once that is known.
-    float y[4];
-    float lsum = 0.f, cw;
-    bool wlive;
-    {
-      float x[4];
+      // ---- softmax: x[h][i] is token 32s + 16h + 4g + i of head r16 ----
+      // y = x + E - 127 is the log2 size of the token's weight times its row
+      // scale 2^(E - 127), which the e4m3 V rows leave out; the block's
+      // weights are written relative to its largest y (weight_block_scale).
+      // The sum of this lane's weights is taken against the wave's integral
+      // reference cw (the floor of its logit maximum) and moved to the running
+      // maximum's scale once that is known.
+      float x[2][4], y[2][4];
       float tmax = kNegInf, ymax = kNegInf;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float ei = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (4 * g + i), __float_as_int(erow)));
-        x[i] = (sacc[0][i] + sacc[1][i]) * xscale;
-        if (tok0 + 16 * wave + 4 * g + i > tok_last) x[i] = kNegInf;
-        y[i] = x[i] + (ei - 127.0f);
-        tmax = fmaxf(tmax, x[i]);
-        ymax = fmaxf(ymax, y[i]);
-      }
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float ei =
+              __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (16 * h + 4 * g + i), __float_as_int(erow)));
+          x[h][i] = (sacc[h][0][i] + sacc[h][1][i]) * xscale;
+          if (tok0 + 32 * wave + 16 * h + 4 * g + i > tok_last) x[h][i] = kNegInf;
+          y[h][i] = x[h][i] + (ei - 127.0f);
+          tmax = fmaxf(tmax, x[h][i]);
+          ymax = fmaxf(ymax, y[h][i]);
+        }
       tmax = xor_max_groups(tmax);
       ymax = xor_max_groups(ymax);
       if (g == 0) {
@@ -488,37 +478,82 @@ __device__ __forceinline__ void mxfp4_item(const Stage1Args& a, const WorkItem& 
       }
       wlive = tmax != kNegInf;
       cw = weight_block_floor(tmax);
+      const float shift = 7.0f - weight_block_floor(ymax);  // y + shift < 8
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lsum += __builtin_amdgcn_exp2f(x[i] - cw);
-    }
-    // blocks more than 5 binades below their row's E: by rounding
-    // conversions (exact within 8 binades, rounded to e4m3 beyond)
-    if (__ballot(min(min(jv[0], jv[1]), min(jv[2], jv[3])) < -5) != 0) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        if (jv[k] >= -5) continue;
-        const float scale = __uint_as_float((uint32_t)(127 + jv[k]) << 23);
-        uint32_t e8[8];
+      for (int h = 0; h < 2; ++h) {
+        float pw[4];
+        uint32_t ph, pl;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          uint32_t lo, hi;  // columns 0..3, 4..7
-          fp4x8_to_fp8(wv[k][i], scale, lo, hi);
-          e8[2 * i] = __builtin_amdgcn_perm(hi, lo, 0x06040200u);      // columns 0, 2, 4, 6
-          e8[2 * i + 1] = __builtin_amdgcn_perm(hi, lo, 0x07050301u);  // columns 1, 3, 5, 7
+          pw[i] = __builtin_amdgcn_exp2f(y[h][i] + shift);
+          lsum += __builtin_amdgcn_exp2f(x[h][i] - cw);
         }
-        *reinterpret_cast<u32x4*>(vdst + 128 * k) = u32x4{e8[0], e8[1], e8[2], e8[3]};
-        *reinterpret_cast<u32x4*>(vdst + 128 * k + 16) = u32x4{e8[4], e8[5], e8[6], e8[7]};
+        split_fp8x4(pw[0], pw[1], pw[2], pw[3], ph, pl);
+        *reinterpret_cast<uint32_t*>(p_hi + 32 * wave + 16 * h + 4 * g) = ph;
+        *reinterpret_cast<uint32_t*>(p_lo + 32 * wave + 16 * h + 4 * g) = pl;
+      }
+    } else {
+      // ---- V of this tile to e4m3, each token row relative to its own
+      // largest V scale E: lanes l and l ^ 32 hold the row's 16 scales ----
+      // By table, exact for blocks within 5 binades of the row's E (nearly
+      // all); a block further below is converted again by rounding
+      // conversions (exact within 8 binades, rounded to e4m3 beyond).
+      const int row = 32 * (wave - 4) + (lane & 31);
+      const int cb0 = 8 * (lane >> 5);
+      uint32_t e[8];
+      u32x4 wv[8];
+      const uint8_t* rsrc = raw + row * kXRow + 16 * cb0;
+      const uint8_t* ssrc = sdw + 4 * kXScalePairs * row + 2 * cb0;  // pair cb/2 at dword 9 row + cb/2
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        e[k] = ssrc[4 * (k >> 1) + (k & 1)];
+        wv[k] = *reinterpret_cast<const u32x4*>(rsrc + 16 * k);
+      }
+      uint32_t em = 0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) em = max(em, e[k]);
+      const auto sw = __builtin_amdgcn_permlane32_swap(em, em, false, false);
+      const int E = (int)max((uint32_t)sw[0], (uint32_t)sw[1]);
+      uint8_t* const vdst = &sh.v[row * kXVRow + 32 * cb0];
+      int jmin = 0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int j = max((int)e[k] - E, -126);  // <= 0
+        jmin = min(jmin, j);
+        const uint32_t kk = (uint32_t)min(-j, 5);
+        const uint32_t lut_lo = 0x3C383000u - kk * 0x08080800u;
+        const uint32_t lut_hi = 0x4C484440u - kk * 0x08080808u;
+        uint32_t e8[8];  // 32 e4m3 codes: word 2i columns 32cb + 8i + {0,2,4,6}, word 2i+1 the odd ones
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fp4x8_to_fp8_lut(wv[k][i], lut_lo, lut_hi, e8[2 * i], e8[2 * i + 1]);
+        *reinterpret_cast<u32x4*>(vdst + 32 * k) = u32x4{e8[0], e8[1], e8[2], e8[3]};
+        *reinterpret_cast<u32x4*>(vdst + 32 * k + 16) = u32x4{e8[4], e8[5], e8[6], e8[7]};
+      }
+      if (__ballot(jmin < -5) != 0) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int j = max((int)e[k] - E, -126);
+          if (j >= -5) continue;
+          const float scale = __uint_as_float((uint32_t)(127 + j) << 23);
+          uint32_t e8[8];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            uint32_t lo, hi;  // columns 0..3, 4..7
+            fp4x8_to_fp8(wv[k][i], scale, lo, hi);
+            e8[2 * i] = __builtin_amdgcn_perm(hi, lo, 0x06040200u);      // columns 0, 2, 4, 6
+            e8[2 * i + 1] = __builtin_amdgcn_perm(hi, lo, 0x07050301u);  // columns 1, 3, 5, 7
+          }
+          *reinterpret_cast<u32x4*>(vdst + 32 * k) = u32x4{e8[0], e8[1], e8[2], e8[3]};
+          *reinterpret_cast<u32x4*>(vdst + 32 * k + 16) = u32x4{e8[4], e8[5], e8[6], e8[7]};
+        }
       }
     }
-    lds_barrier();  // maxima and the V tile; raw slot t % 2 is free
+    lds_barrier();  // P^T, the maxima and the V tile; raw slot t % 2 is free
     if (t + 2 < ntiles) issue(t + 2);
 
-    const f32x4 mx0 = *reinterpret_cast<const f32x4*>(&sh.red_m[r16][0]);
-    const f32x4 mx1 = *reinterpret_cast<const f32x4*>(&sh.red_m[r16][4]);
-    const f32x4 my0 = *reinterpret_cast<const f32x4*>(&sh.red_y[r16][0]);
-    const f32x4 my1 = *reinterpret_cast<const f32x4*>(&sh.red_y[r16][4]);
-    const float tile_max = fmaxf(fmaxf(fmaxf(mx0[0], mx0[1]), fmaxf(mx0[2], mx0[3])),
-                                 fmaxf(fmaxf(mx1[0], mx1[1]), fmaxf(mx1[2], mx1[3])));
+    const f32x4 mx = *reinterpret_cast<const f32x4*>(&sh.red_m[r16][0]);
+    const f32x4 my = *reinterpret_cast<const f32x4*>(&sh.red_y[r16][0]);
+    const float tile_max = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
     // Every wave reads the same maxima, so this branch is uniform.
     if (__ballot(tile_max > m_ref + kLazyRescale) != 0) {
       const float m_new = floorf(fmaxf(m_ref, tile_max));
@@ -529,25 +564,8 @@ __device__ __forceinline__ void mxfp4_item(const Stage1Args& a, const WorkItem& 
       m_ref = m_new;
     }
     if (wlive) l_part += __builtin_ldexpf(lsum, (int)cw - (int)m_ref);
-    // block maxima of y: k-block j is waves 2j, 2j + 1
-    const float yb0 = fmaxf(my0[0], my0[1]), yb1 = fmaxf(my0[2], my0[3]);
-    const float yb2 = fmaxf(my1[0], my1[1]), yb3 = fmaxf(my1[2], my1[3]);
-    {
-      const int jb = wave >> 1;  // this wave's block
-      const float own = jb == 0 ? yb0 : jb == 1 ? yb1 : jb == 2 ? yb2 : yb3;
-      const float shift = 7.0f - weight_block_floor(own);  // y + shift < 8
-      float p[4];
-      uint32_t ph, pl;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(y[i] + shift);
-      split_fp8x4(p[0], p[1], p[2], p[3], ph, pl);
-      *reinterpret_cast<uint32_t*>(p_hi + 16 * wave + 4 * g) = ph;
-      *reinterpret_cast<uint32_t*>(p_lo + 16 * wave + 4 * g) = pl;
-    }
-    // B scale of k-block g for head r16
-    const int sb = weight_block_scale(g == 0 ? yb0 : g == 1 ? yb1 : g == 2 ? yb2 : yb3, m_ref);
-    lds_barrier();  // P^T of all waves
-
+    // B scale of k-block g (scoring wave g's tokens) for head r16
+    const int sb = weight_block_scale(g == 0 ? my[0] : g == 1 ? my[1] : g == 2 ? my[2] : my[3], m_ref);
     const fp8x32 bh = join16(*reinterpret_cast<const u32x4*>(p_hi + 16 * g),
                              *reinterpret_cast<const u32x4*>(p_hi + 64 + 16 * g));
     const fp8x32 bl = join16(*reinterpret_cast<const u32x4*>(p_lo + 16 * g),
@@ -572,12 +590,12 @@ __device__ __forceinline__ void mxfp4_item(const Stage1Args& a, const WorkItem& 
     }
   }
 
+  // Only the scoring waves hold weight sums.
   const float l_w = xor_sum_groups(l_part);
-  if (g == 0) sh.red_y[r16][wave] = l_w;  // every read of the last tile's maxima is behind a barrier
+  if (scorer && g == 0) sh.red_l[r16][wave] = l_w;
   lds_barrier();
-  const f32x4 ls0 = *reinterpret_cast<const f32x4*>(&sh.red_y[r16][0]);
-  const f32x4 ls1 = *reinterpret_cast<const f32x4*>(&sh.red_y[r16][4]);
-  const float L = ((ls0[0] + ls0[1]) + (ls0[2] + ls0[3])) + ((ls1[0] + ls1[1]) + (ls1[2] + ls1[3]));
+  const f32x4 ls = *reinterpret_cast<const f32x4*>(&sh.red_l[r16][0]);
+  const float L = (ls[0] + ls[1]) + (ls[2] + ls[3]);
   // The V tile holds each group of 8 columns as (0, 2, 4, 6, 1, 3, 5, 7), so
   // lane group g has output columns 8(g >> 1) + 2i + (g & 1) of each column
   // tile; lanes l and l ^ 16 trade two values each to return to columns
