@@ -21,7 +21,7 @@ constexpr int kStage1ThreadsMxfp4 = 512;  // the MXFP4 split kernel runs eight w
 // the rest of their LDS leaves); the planner keeps paged items within them.
 constexpr int kItemPagesFp8 = 2560;
 constexpr int kItemPagesFp8Pair = 1536;  // the fp8 kernel that runs pairs of query rows
-constexpr int kItemPagesMxfp4 = 1536;
+constexpr int kItemPagesMxfp4 = 1024;
 constexpr int kItemPagesBf16 = 2048;  // the bf16 kernel's LDS ring leaves room for this many
 constexpr int kMergeThreads = 256;  // two float4 of one head per thread
 

@@ -3,10 +3,6 @@
 // 512-thread workgroup (eight waves, two per SIMD) per planned work item,
 // 128-token tiles streamed HBM -> LDS by cache-to-LDS loads, both
 // contractions on the MX matrix instruction v_mfma_scale_f32_16x16x128_f8f6f4.
-// Wave w scores tokens 16w..16w+15 and accumulates output columns
-// 64w..64w+63; the second wave on each SIMD hides the latencies of the first
-// (the V conversion below makes this kernel heavier in vector and LDS work
-// than the fp8 one, and its tiles are half the bytes).
 //
 // Operand layout of that instruction on gfx950 (measured): in each group g of
 // 16 lanes, an fp4 operand holds 32 consecutive k-values 32g..32g+31, an fp8
@@ -32,18 +28,34 @@
 // subnormals included).  The row's 2^(E - 127) joins the token's softmax
 // weight, so the weight of P.V is 2^(x + E - 127 - m) for logit x; those of
 // each 32-token k-block are written relative to the block's largest and the
-// block's B scale restores them (weight_block_scale).  The k-values are laid
-// out so that k-block g is tokens 32g..32g+31 (bytes b < 16: token 16g + b,
-// bytes 16..31: token 64 + 16g + b - 16, for V^T and P^T alike); the two
-// waves that score a block trade their maxima through LDS before writing P.
+// block's B scale restores them (weight_block_scale).  The k-values of P.V
+// are the tile's tokens in order (bytes b < 16 of lane group g: token
+// 16g + b, bytes 16..31: token 64 + 16g + b - 16, for V^T and P^T alike), so
+// k-block g is tokens 32g..32g+31.
+//
+// Roles.  Waves 0-3 score: wave s takes tokens 32s..32s+31 of each tile
+// (two 16-row blocks), exactly k-block s of P.V, so the maximum that scales
+// the block's weights is the wave's own; these waves also issue every cache
+// load.  Waves 4-7 hold V: wave 4 + c converts columns 128c..128c+127 of
+// every token of a tile into its own e4m3 block of LDS and contracts them
+// with P.  Each SIMD runs one wave of each kind.
+//
+// Pipeline, iteration i of an item: barrier; every wave copies what it needs
+// of raw tile i into registers, and the scoring waves find the row exponents E;
+// barrier, after which the raw slot is free and the tile after next is
+// issued into it.  Then the scoring waves score tile i and write its weights
+// P_i, while each V wave runs P.V of tile i - 1 over its own columns and
+// converts tile i into them (its stores come after its last read of tile
+// i - 1), so that the vector work of converting shares an instruction stream
+// with the matrix work of P.V, and the scoring wave's contraction runs beside
+// both on the same SIMD.  P and the block maxima alternate between two
+// buffers by tile parity; one iteration more than tiles drains the last P.V.
 //
 // Data movement: per tile, 36 cache-to-LDS loads of 1 KB bring the 128 rows
 // of e2m1 codes (288 bytes each, rows past the item's end repeat its last
 // row) and 20 two-byte loads bring the 18 scale bytes of each row, two per
-// LDS dword (the two-byte form writes one dword per lane); waves 0-3 issue
-// five code and two scale loads, waves 4-7 four and three.  Two
-// raw tiles are in flight while a third is worked on: a raw slot is free
-// again as soon as its tile is scored and its V converted.
+// LDS dword (the two-byte form writes one dword per lane); each scoring wave
+// issues nine code and five scale loads.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -56,40 +68,51 @@ namespace {
 constexpr int kXWaves = 8;
 constexpr int kXThreads = 64 * kXWaves;
 static_assert(kXThreads == kStage1ThreadsMxfp4, "launch shape");
-constexpr int kXTile = 128;                        // tokens per tile
-constexpr int kXRow = kQkDim / 2;                  // 288 bytes of e2m1 codes per row
-constexpr int kXFp4Bytes = kXTile * kXRow;         // 36864
-constexpr int kXFp4Loads = kXFp4Bytes / 1024;      // 36
-constexpr int kXScalePairs = kQkDim / 64;          // 9 two-byte scale pairs per row
+constexpr int kXTile = 128;                          // tokens per tile
+constexpr int kXRow = kQkDim / 2;                    // 288 bytes of e2m1 codes per row
+constexpr int kXFp4Bytes = kXTile * kXRow;           // 36864
+constexpr int kXFp4Loads = kXFp4Bytes / 1024;        // 36
+constexpr int kXScalePairs = kQkDim / 64;            // 9 two-byte scale pairs per row
 constexpr int kXScaleItems = kXTile * kXScalePairs;  // 1152
-constexpr int kXScaleLoads = 20;                   // 1280 lanes >= 1152 pairs
-constexpr int kXScaleBytes = kXScaleLoads * 256;   // one dword per lane
+constexpr int kXScaleLoads = 20;                     // 1280 lanes >= 1152 pairs
+constexpr int kXScaleBytes = kXScaleLoads * 256;     // one dword per lane
 constexpr int kXRawBytes = kXFp4Bytes + kXScaleBytes;
-constexpr int kXLoadsPerWave = 7;                  // 5 + 2 (waves 0-3) or 4 + 3 (waves 4-7)
-constexpr int kXVRow = kVDim + 16;                 // bytes per row of the e4m3 V tile (512 + pad)
-constexpr int kXVBytes = kXTile * kXVRow;
-constexpr int kQBytes = kNumHeads * kQkDim * 2;    // bf16 query of one sequence
-constexpr int kQLoads = kQBytes / 1024;            // 18
-constexpr int kPRow = kXTile + 16;                 // bytes per head row of P^T
-constexpr int kMaxItemPages = kItemPagesMxfp4;     // page ids of one item staged in LDS
-static_assert(4 * 5 + 4 * 4 == kXFp4Loads && 4 * 2 + 4 * 3 == kXScaleLoads && kXScaleLoads * 64 >= kXScaleItems,
+constexpr int kXCodeLoads = kXFp4Loads / 4;          // per scoring wave
+constexpr int kXPairLoads = kXScaleLoads / 4;        // per scoring wave
+constexpr int kXLoadsPerWave = kXCodeLoads + kXPairLoads;
+constexpr int kXCols = kVDim / 4;                    // V columns per V wave
+constexpr int kXVBytes = kXTile * kXCols;            // its e4m3 block: [16-column chunk][token][16]
+constexpr int kQBytes = kNumHeads * kQkDim * 2;      // bf16 query of one sequence
+constexpr int kQLoads = kQBytes / 1024;              // 18
+constexpr int kMaxItemPages = kItemPagesMxfp4;       // page ids of one item staged in LDS
+static_assert(4 * kXCodeLoads == kXFp4Loads && 4 * kXPairLoads == kXScaleLoads && kXScaleLoads * 64 >= kXScaleItems,
               "load split");
-static_assert(2 * kQBytes <= kXVBytes, "the query and its e4m3 words are staged in the V tile");
+static_assert(2 * kQBytes <= 4 * kXVBytes, "the query and its e4m3 words are staged in the V blocks");
+static_assert(4 * 8 * 64 * 16 <= kXRawBytes, "the output hand-over fits a raw slot");
 
-// Position of 16-byte chunk c (0..71) of query head h.  (The V tile needs
-// no permutation: at a row pitch of 528 bytes = 132 banks, the eight rows of
-// a transposing read fall on distinct banks.)
+// Position of 16-byte chunk c (0..71) of query head h.
 __host__ __device__ constexpr int q_slot(int h, int c) { return h * 72 + (c ^ (h & 7)); }
+// A V block stores 16-column chunk c of token row r at 2048 c + 16 v_slot(r):
+// the 16 rows that one store instruction writes, and the eight rows of a
+// transposing read, are consecutive 16-byte words, and the two halves of odd
+// groups of 16 rows trade places, so that lane groups 0 and 1 of a read (rows
+// 8q.. and 16 + 8q..) fall on different banks as well.
+constexpr int kXVChunk = kXTile * 16;
+__host__ __device__ constexpr int v_slot(int r) { return r ^ (((r >> 4) & 1) << 3); }
+// Chunk c (0..7) of head row h of P^T (rows of 128 bytes), permuted so that
+// the 16 head rows reading one chunk fall on distinct banks.
+__host__ __device__ constexpr int p_chunk(int h, int c) { return c ^ ((h >> 1) & 7); }
 
 struct Fp4Lds {
-  uint8_t raw[2][kXRawBytes];              // e2m1 rows, then the scale dwords
-  uint8_t v[kXVBytes];                     // V of the current tile as e4m3 [token][dim]; first the query
-  uint8_t p[2][kNumHeads][kPRow];          // P^T hi / lo as [head][token]
-  float red_m[kNumHeads][kXWaves];         // query head maxima (8 waves), then per scoring wave logit maxima
-  float red_y[kNumHeads][4];               // per scoring wave: maxima of logit + row scale
-  float red_l[kNumHeads][4];               // per scoring wave: weight sums, at the end
-  int32_t pages[kMaxItemPages];            // paged: page ids of the item
+  uint8_t raw[2][kXRawBytes];            // e2m1 rows, then the scale dwords
+  uint8_t v[4][kXVBytes];                // V wave c's e4m3 columns; first the query
+  uint8_t p[2][2][kNumHeads][kXTile];    // [tile parity][hi, lo][head][token]: P^T
+  float red_m[2][kNumHeads][4];          // [tile parity][head][scoring wave]: logit maxima
+  float red_y[2][kNumHeads][4];          // the same for logit + row exponent
+  int32_t erow[kXTile];                  // row exponents E of the tile in hand
+  int32_t pages[kMaxItemPages];          // paged: page ids of the item
 };
+static_assert(sizeof(Fp4Lds) <= 160 * 1024, "LDS");
 
 // Two-byte cache-to-LDS load: lane l's two bytes at src go to LDS dword
 // m0 + 4 l.
@@ -110,11 +133,12 @@ __device__ __forceinline__ void dma_u16(const uint8_t* base, uint32_t off, uint3
 }
 #pragma clang diagnostic pop
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
 // An fp4 MX operand (16 bytes per lane) in the instruction's 8-register
 // tuple, whose upper half the instruction does not read.
 __device__ __forceinline__ fp8x32 fp4_operand(u32x4 w) {
-  typedef int i32x4v __attribute__((ext_vector_type(4)));
-  const i32x4v v = __builtin_bit_cast(i32x4v, w);
+  const i32x4 v = __builtin_bit_cast(i32x4, w);
   return __builtin_shufflevector(v, v, 0, 1, 2, 3, -1, -1, -1, -1);
 }
 
@@ -145,12 +169,19 @@ __device__ __forceinline__ void fp4x8_to_fp8(uint32_t w, float scale, uint32_t& 
 // the exponent field, so the 8-entry table (lut_lo: magnitudes 0..3, lut_hi:
 // 4..7) is a shifted constant; v_perm_b32 looks up four magnitudes at once
 // and the sign bit moves from bit 3 to bit 7.  The codes come out as the V
-// tile stores a group of 8 columns: even columns (0, 2, 4, 6) in `ev`, odd
+// blocks store a group of 8 columns: even columns (0, 2, 4, 6) in `ev`, odd
 // ones in `od`.
 __device__ __forceinline__ void fp4x8_to_fp8_lut(uint32_t w, uint32_t lut_lo, uint32_t lut_hi, uint32_t& ev,
                                                  uint32_t& od) {
   ev = ((w << 4) & 0x80808080u) | __builtin_amdgcn_perm(lut_hi, lut_lo, w & 0x07070707u);
   od = (w & 0x80808080u) | __builtin_amdgcn_perm(lut_hi, lut_lo, (w >> 4) & 0x07070707u);
+}
+// Table words for 2^-k: 8k off every byte but that of magnitude 0.
+__device__ __forceinline__ void fp4_lut(uint32_t k, uint32_t& lut_lo, uint32_t& lut_hi) {
+  const uint32_t k8 = k << 3;
+  const uint32_t rep = __builtin_amdgcn_perm(0u, k8, 0u);  // k8 in every byte
+  lut_lo = (0x3C383000u | k8) - rep;
+  lut_hi = 0x4C484440u - rep;
 }
 
 // One work item: tokens [tok_begin, tok_end) of one sequence.
@@ -171,12 +202,12 @@ __device__ __forceinline__ void mxfp4_item(const Stage1Args& a, const WorkItem& 
   const int b = item.batch;
   const int tok_last = item.tok_end - 1;
   const int ntiles = (item.tok_end - item.tok_begin + kXTile - 1) / kXTile;
-  const bool lowq = wave < 4;  // waves 0-3: five code loads and two scale loads per tile
+  const bool scorer = wave < 4;
 
-  // The query first: 18 loads into the V tile, load k by wave k % 8.
+  // The query first: 18 loads into the V blocks, load k by wave k % 8.
   {
     const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(a.q + (int64_t)b * kNumHeads * kQkDim);
-    const uint32_t qm0 = lds_u32(&sh.v[0]);
+    const uint32_t qm0 = lds_u32(&sh.v[0][0]);
     for (int k = wave; k < kQLoads; k += kXWaves) {
       const int s = 64 * k + lane;
       const int h = s / 72;
@@ -200,24 +231,6 @@ __device__ __forceinline__ void mxfp4_item(const Stage1Args& a, const WorkItem& 
     lds_barrier();
   }
 
-  // This wave's loads of a tile: code loads j0 .. j0 + 4 (or + 3), scale
-  // loads s0 .. s0 + 1 (or + 2); code load j fetches 16-byte chunk
-  // (row << 8 | chunk), scale load s the scale pair (row << 8 | pair).
-  const int j0 = lowq ? 5 * wave : 20 + 4 * (wave - 4);
-  const int s0 = lowq ? 2 * wave : 8 + 3 * (wave - 4);
-  uint32_t rc[5], rs[3];
-#pragma unroll
-  for (int j = 0; j < 5; ++j) {
-    const int s = min(64 * (j0 + j) + lane, 64 * kXFp4Loads - 1);
-    const int r = s / 18;
-    rc[j] = (uint32_t)(r << 8 | (s - 18 * r));
-  }
-#pragma unroll
-  for (int j = 0; j < 3; ++j) {
-    const int s = min(64 * (s0 + j) + lane, kXScaleItems - 1);
-    const int r = s / kXScalePairs;
-    rs[j] = (uint32_t)(r << 8 | (s - kXScalePairs * r));
-  }
   auto row_of = [&](int tok) -> int64_t {  // cache row of logical token tok
     if constexpr (PAGED) {
       const int pmask = (1 << a.page_shift) - 1;
@@ -227,86 +240,85 @@ __device__ __forceinline__ void mxfp4_item(const Stage1Args& a, const WorkItem& 
       return seq_base + tok;
     }
   };
-  // Offsets from the tile's first row (contiguous cache): code load j at
-  // coff[j] + 1024 j (the instruction offset within its group of four, none
-  // for j = 4; 3072 bytes of bias keep coff >= 0), scale load j at soff[j].
-  uint32_t coff[5], soff[3];
+  // Scale loads of whole tiles of a contiguous cache: pair sp = 64 j' + lane
+  // of the tile (row sp / 9, pair sp % 9) at soff[j] from the tile's first
+  // scale row, j' = 5 wave + j (the offsets fit 32 bits for strides up to
+  // 2^24).
+  const bool short_stride = a.scale_stride <= (int64_t(1) << 24);
+  uint32_t soff[kXPairLoads];
 #pragma unroll
-  for (int j = 0; j < 5; ++j) coff[j] = (rc[j] >> 8) * kXRow + 16 * (rc[j] & 0xFF) + 3072 - 1024 * (j & 3);
-#pragma unroll
-  for (int j = 0; j < 3; ++j) soff[j] = (uint32_t)((rs[j] >> 8) * a.scale_stride) + 2 * (rs[j] & 0xFF);
+  for (int j = 0; j < kXPairLoads; ++j) {
+    const int sp = min(64 * (kXPairLoads * wave + j) + lane, kXScaleItems - 1);
+    const int r = sp / kXScalePairs;
+    soff[j] = (uint32_t)(r * (short_stride ? (int)a.scale_stride : 0)) + 2 * (sp - kXScalePairs * r);
+  }
 
-  // All of this wave's loads of tile t into raw slot t % 2.  Rows past the
-  // item's last token fetch that token's row (finite data, masked later).
+  // All loads of tile t into raw slot t % 2, issued by scoring wave `wave`:
+  // code loads j' = 9 wave .. 9 wave + 8 (16-byte chunk 64 j' + lane of the
+  // tile's rows: row / 18, chunk % 18) and scale loads 5 wave .. 5 wave + 4.
+  // Rows past the item's last token fetch that token's row (finite data,
+  // masked later).
   auto issue = [&](int t) {
     const int tok0 = item.tok_begin + t * kXTile;
     const int lim = tok_last - tok0;
-    const uint32_t m0c = lds_u32(&sh.raw[t & 1][0]) + 1024 * j0;
-    const uint32_t m0s = lds_u32(&sh.raw[t & 1][kXFp4Bytes]) + 256 * s0;
-    if constexpr (!PAGED) {
-      const uint8_t* cbase = uniform_ptr(a.kv + (seq_base + tok0) * kXRow - 3072);
+    const uint32_t m0c = lds_u32(&sh.raw[t & 1][0]) + 1024 * kXCodeLoads * wave;
+    const uint32_t m0s = lds_u32(&sh.raw[t & 1][kXFp4Bytes]) + 256 * kXPairLoads * wave;
+    if (!PAGED && lim >= kXTile - 1 && short_stride) {  // a whole tile of a contiguous cache
+      const uint8_t* cb = uniform_ptr(a.kv + (seq_base + tok0) * kXRow + 1024 * kXCodeLoads * wave);
+      const uint32_t o16 = 16 * lane;
+      const uint32_t off[4] = {o16, o16, o16, o16};
+      dma_group<4>(cb, off, m0c);
+      dma_group<4>(cb + 4096, off, m0c + 4096);
+      dma_group<1>(cb + 8192, off, m0c + 8192);
       const uint8_t* sbase = uniform_ptr(a.kv_mx_scales + (seq_base + tok0) * a.scale_stride);
-      uint32_t off[5], so[3];
-      if (lim >= kXTile - 1) {  // a whole tile
 #pragma unroll
-        for (int j = 0; j < 5; ++j) off[j] = coff[j];
-#pragma unroll
-        for (int j = 0; j < 3; ++j) so[j] = soff[j];
-      } else {
-#pragma unroll
-        for (int j = 0; j < 5; ++j)
-          off[j] = min((int)(rc[j] >> 8), lim) * kXRow + 16 * (rc[j] & 0xFF) + 3072 - 1024 * (j & 3);
-#pragma unroll
-        for (int j = 0; j < 3; ++j)
-          so[j] = (uint32_t)(min((int)(rs[j] >> 8), lim) * a.scale_stride) + 2 * (rs[j] & 0xFF);
-      }
-      dma_group<4>(cbase, off, m0c);
-      if (lowq) dma_group<1>(cbase, off + 4, m0c + 4096);
-      dma_u16(sbase, so[0], m0s);
-      dma_u16(sbase, so[1], m0s + 256);
-      if (!lowq) dma_u16(sbase, so[2], m0s + 512);
+      for (int j = 0; j < kXPairLoads; ++j) dma_u16(sbase, soff[j], m0s + 256 * j);
     } else {
-      const uint8_t* src[5];
+      const uint8_t* src[kXCodeLoads];  // less the instruction offset 1024 (j % 4)
 #pragma unroll
-      for (int j = 0; j < 5; ++j) {
-        const int r = min((int)(rc[j] >> 8), lim);
-        src[j] = a.kv + row_of(tok0 + r) * kXRow + 16 * (rc[j] & 0xFF) - 1024 * (j & 3);
+      for (int j = 0; j < kXCodeLoads; ++j) {
+        const int c = 64 * (kXCodeLoads * wave + j) + lane;
+        const int r = c / 18;
+        src[j] = a.kv + row_of(tok0 + min(r, lim)) * kXRow + 16 * (c - 18 * r) - 1024 * (j & 3);
       }
       dma_group<4>(src, m0c);
-      if (lowq) dma_one(src[4], m0c + 4096);  // no instruction offset
-      const uint8_t* ssrc[3];
+      dma_group<4>(src + 4, m0c + 4096);
+      dma_one(src[8], m0c + 8192);
 #pragma unroll
-      for (int j = 0; j < 3; ++j) {
-        const int r = min((int)(rs[j] >> 8), lim);
-        ssrc[j] = a.kv_mx_scales + row_of(tok0 + r) * a.scale_stride + 2 * (rs[j] & 0xFF);
+      for (int j = 0; j < kXPairLoads; ++j) {
+        const int sp = min(64 * (kXPairLoads * wave + j) + lane, kXScaleItems - 1);
+        const int r = sp / kXScalePairs;
+        dma_u16(a.kv_mx_scales + row_of(tok0 + min(r, lim)) * a.scale_stride + 2 * (sp - kXScalePairs * r),
+                m0s + 256 * j);
       }
-      dma_u16(ssrc[0], m0s);
-      dma_u16(ssrc[1], m0s + 256);
-      if (!lowq) dma_u16(ssrc[2], m0s + 512);
     }
   };
 
-  issue(0);
-  if (ntiles > 1) issue(1);
-  if (ntiles > 1)
-    wait_loads<2 * kXLoadsPerWave>();  // the query has landed
-  else
-    wait_loads<kXLoadsPerWave>();
+  if (scorer) {
+    issue(0);
+    if (ntiles > 1) issue(1);
+    if (ntiles > 1)
+      wait_loads<2 * kXLoadsPerWave>();  // the query has landed
+    else
+      wait_loads<kXLoadsPerWave>();
+  } else {
+    wait_loads<0>();
+  }
   lds_barrier();
 
   // Query, B operand of the scores, scaled by 2^s and split into e4m3 hi +
   // lo.  K-step K (0..3): bytes b < 16 column 128K + 16g + b, bytes 16..31
   // column 128K + 64 + 16g + b - 16; rope step: bytes b < 16 column
-  // 512 + 16g + b, bytes 16..31 zero.  Every wave needs all of it; wave w
-  // converts half j = w & 1 (bytes 16j .. 16j + 15) of K-step w >> 1, and
-  // waves 0, 1 half w of the rope step; the waves trade their head maxima
-  // and then the converted words through LDS, behind the bf16 query.
-  fp8x32 qh[4], ql[4], rh, rl;
+  // 512 + 16g + b, bytes 16..31 zero.  The scoring waves need all of it;
+  // wave w converts half j = w & 1 (bytes 16j .. 16j + 15) of K-step w >> 1,
+  // and waves 0, 1 half w of the rope step; the waves trade their head
+  // maxima and then the converted words through LDS, behind the bf16 query.
+  uint32_t* const qcv = reinterpret_cast<uint32_t*>(&sh.v[0][0] + kQBytes);
   float xscale;
   {
-    const uint8_t* qlds = &sh.v[0];
+    float(*const qmax)[8] = reinterpret_cast<float(*)[8]>(&sh.red_m[0][0][0]);
+    const uint8_t* qlds = &sh.v[0][0];
     // converted words: [K][hi, lo][lane][8], then rope [hi, lo][lane][4]
-    uint32_t* const qcv = reinterpret_cast<uint32_t*>(&sh.v[kQBytes]);
     const int K0 = wave >> 1, j = wave & 1;
     const bool rope = wave < 2;
     bf16x8 qv[3];  // [i]: chunk 16 K0 + 2g + 8j + i; [2]: rope chunk 64 + 2g + wave
@@ -324,10 +336,10 @@ __device__ __forceinline__ void mxfp4_item(const Stage1Args& a, const WorkItem& 
       am[k] = fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
     }
     float amax = xor_max_groups(fmaxf(fmaxf(am[0], am[1]), am[2]));
-    if (g == 0) sh.red_m[r16][wave] = amax;
+    if (g == 0) qmax[r16][wave] = amax;
     lds_barrier();
-    const f32x4 wm0 = *reinterpret_cast<const f32x4*>(&sh.red_m[r16][0]);
-    const f32x4 wm1 = *reinterpret_cast<const f32x4*>(&sh.red_m[r16][4]);
+    const f32x4 wm0 = *reinterpret_cast<const f32x4*>(&qmax[r16][0]);
+    const f32x4 wm1 = *reinterpret_cast<const f32x4*>(&qmax[r16][4]);
     amax = fmaxf(fmaxf(fmaxf(wm0[0], wm0[1]), fmaxf(wm0[2], wm0[3])),
                  fmaxf(fmaxf(wm1[0], wm1[1]), fmaxf(wm1[2], wm1[3])));
     const int s = (amax > 0.f) ? 8 - __builtin_amdgcn_frexp_expf(amax) : 0;
@@ -347,6 +359,18 @@ __device__ __forceinline__ void mxfp4_item(const Stage1Args& a, const WorkItem& 
       *reinterpret_cast<uint2*>(qcv + 4096 + (64 + lane) * 4 + 2 * wave) = uint2{lw[4], lw[5]};
     }
     lds_barrier();
+  }
+
+  // At the end, raw slot 0 hands the V waves' output over ([V wave][column
+  // tile][lane]) and raw slot 1 holds the weight sums and references.
+  f32x4* const hand = reinterpret_cast<f32x4*>(&sh.raw[0][0]);
+  float* const fin_m = reinterpret_cast<float*>(&sh.raw[1][0]);  // [head]: running maximum of P.V
+  float(*const fin_l)[4] = reinterpret_cast<float(*)[4]>(&sh.raw[1][256]);   // [head][scoring wave]
+  float(*const fin_ls)[4] = reinterpret_cast<float(*)[4]>(&sh.raw[1][512]);  // their references
+
+  if (scorer) {
+    const int s = wave;
+    fp8x32 qh[4], ql[4], rh, rl;
 #pragma unroll
     for (int K = 0; K < 4; ++K) {
       const u32x4* h = reinterpret_cast<const u32x4*>(qcv + ((2 * K) * 64 + lane) * 8);
@@ -354,263 +378,338 @@ __device__ __forceinline__ void mxfp4_item(const Stage1Args& a, const WorkItem& 
       qh[K] = join16(h[0], h[1]);
       ql[K] = join16(l[0], l[1]);
     }
-    const u32x4 wh = *reinterpret_cast<const u32x4*>(qcv + 4096 + lane * 4);
-    const u32x4 wl = *reinterpret_cast<const u32x4*>(qcv + 4096 + (64 + lane) * 4);
+    {
+      const u32x4 wh = *reinterpret_cast<const u32x4*>(qcv + 4096 + lane * 4);
+      const u32x4 wl = *reinterpret_cast<const u32x4*>(qcv + 4096 + (64 + lane) * 4);
 #pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      rh[d] = d < 4 ? (int)wh[d] : 0;
-      rl[d] = d < 4 ? (int)wl[d] : 0;
+      for (int d = 0; d < 8; ++d) {
+        rh[d] = d < 4 ? (int)wh[d] : 0;
+        rl[d] = d < 4 ? (int)wl[d] : 0;
+      }
     }
-  }
+    // This wave's weight sum per head, against its own integral reference.
+    float m_s = kNegInf, l_s = 0.f;
+    const int pw_off = r16 * kXTile + 4 * g;  // + 16 p_chunk(r16, 2s + h): tokens 32s + 16h + 4g ..
 
-  f32x4 o[4];  // O^T[dim 64w + 16v + 4g + i][head r16]
+    for (int i = 0; i <= ntiles; ++i) {
+      if (i < ntiles) {
+        if (i + 1 < ntiles)
+          wait_loads<kXLoadsPerWave>();  // tile i, not tile i + 1 behind it
+        else
+          wait_loads<0>();
+      }
+      lds_barrier();  // tile i everywhere; every wave is past iteration i - 1
+      // Rows 32s + 16h + r16 of tile i: lane group g of k-step K holds
+      // columns 128K + 32g .. +31 and their scale; the rope step groups 0, 1.
+      u32x4 kc[2][5];
+      uint32_t sa[2][5];
+      if (i < ntiles) {
+        const uint8_t* raw = &sh.raw[i & 1][0];
+        const uint8_t* sdw = raw + kXFp4Bytes;  // scale pair (row, p) at dword 9 row + p
 #pragma unroll
-  for (int v = 0; v < 4; ++v) o[v] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref = kNegInf;
-  float l_part = 0.f;
-
-  // Roles.  Waves 0-3 score: wave s takes the 32 tokens 32s..32s+31 of the
-  // tile (two 16-row MFMA blocks), which are exactly k-block s of the P.V
-  // step, so the maximum that scales the block's weights is the wave's own.
-  // Waves 4-7 convert V: wave 4 + c converts token rows 32c..32c+31, lane l
-  // row 32c + (l & 31) and column blocks 8(l >> 5)..+7.  With one scoring and
-  // one converting wave on each SIMD, the matrix steps of one overlap the
-  // vector work of the other.  Then every wave runs P.V for its 64 columns.
-  // Reads of this lane for P.V: tr8 read q (0..3) gives tokens tb(q) +
-  // (0..7), tb = 16g + 8q (q < 2) or 64 + 16g + 8(q - 2), from rows tb(q) +
-  // (r16 >> 1), columns 64w + 16v + 8(r16 & 1).
-  const bool scorer = wave < 4;
-  int voff[4];
+        for (int h = 0; h < 2; ++h) {
+          const int row = 32 * s + 16 * h + r16;
+          const uint8_t* rp = raw + row * kXRow;
+          const uint8_t* sp = sdw + 4 * kXScalePairs * row;
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-    voff[q] = ((q < 2 ? 16 * g + 8 * q : 64 + 16 * g + 8 * (q - 2)) + (r16 >> 1)) * kXVRow + 64 * wave +
-              8 * (r16 & 1);
-  uint8_t* const p_hi = &sh.p[0][r16][0];
-  uint8_t* const p_lo = &sh.p[1][r16][0];
+          for (int K = 0; K < 4; ++K) {
+            const int blk = 4 * K + g;
+            kc[h][K] = *reinterpret_cast<const u32x4*>(rp + 64 * K + 16 * g);
+            sa[h][K] = sp[4 * (blk >> 1) + (blk & 1)];
+          }
+          kc[h][4] = u32x4{0u, 0u, 0u, 0u};
+          sa[h][4] = 127;
+          if (g < 2) {
+            kc[h][4] = *reinterpret_cast<const u32x4*>(rp + 256 + 16 * g);
+            sa[h][4] = sp[4 * 8 + g];
+          }
+        }
+        // E of rows 32s + (lane & 31), the largest of the row's 16 scales of
+        // columns 0..511: lanes l and l ^ 32 take pairs 0..3 / 4..7.
+        const uint32_t* er =
+            reinterpret_cast<const uint32_t*>(sdw) + kXScalePairs * (32 * s + (lane & 31)) + 4 * (lane >> 5);
+        uint32_t em = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t d = er[k];  // scale pair in the low 16 bits
+          em = max(em, max(d & 0xFFu, (d >> 8) & 0xFFu));
+        }
+        const auto sw = __builtin_amdgcn_permlane32_swap(em, em, false, false);
+        if (lane < 32) sh.erow[32 * s + lane] = (int)max((uint32_t)sw[0], (uint32_t)sw[1]);
+      }
+      lds_barrier();  // raw slot i % 2 is read; the row exponents of tile i are in LDS
+      if (i + 2 < ntiles) issue(i + 2);
+      if (i == ntiles) continue;
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int tok0 = item.tok_begin + t * kXTile;
-    if (t + 1 < ntiles)
-      wait_loads<kXLoadsPerWave>();  // tile t, not tile t + 1 behind it
-    else
-      wait_loads<0>();
-    lds_barrier();  // tile t everywhere; everyone is past tile t - 1
-    const uint8_t* raw = &sh.raw[t & 1][0];
-    const uint8_t* sdw = raw + kXFp4Bytes;  // scale pair (row, p) at dword 9 row + p
-
-    float lsum = 0.f, cw = 0.f;  // scorers: this lane's weights against the wave's reference cw
-    bool wlive = false;
-    if (scorer) {
-      // ---- scores of tokens 32s + 16h + (0..15), h = 0, 1 ----
+      // ---- scores of tokens 32s + 16h + (0..15) ----
       // The fp4 A operand is 16 bytes; the upper half of its register tuple
       // is not read, so it is left undefined rather than zeroed.
       f32x4 sacc[2][2];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) sacc[h][0] = sacc[h][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int row = 32 * wave + 16 * h + r16;
-        const uint8_t* rp = raw + row * kXRow;
-        const uint8_t* sp = sdw + 4 * kXScalePairs * row;
+        sacc[h][0] = sacc[h][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int K = 0; K < 4; ++K) {
-          const int blk = 4 * K + g;
-          const uint32_t sa = sp[4 * (blk >> 1) + (blk & 1)];
-          const fp8x32 ka = fp4_operand(*reinterpret_cast<const u32x4*>(rp + 64 * K + 16 * g));
-          sacc[h][0] = mfma_fp4_fp8(ka, qh[K], sacc[h][0], sa);
-          sacc[h][1] = mfma_fp4_fp8(ka, ql[K], sacc[h][1], sa);
+        for (int K = 0; K < 5; ++K) {
+          const fp8x32 ka = fp4_operand(kc[h][K]);
+          sacc[h][0] = mfma_fp4_fp8(ka, K < 4 ? qh[K] : rh, sacc[h][0], sa[h][K]);
+          sacc[h][1] = mfma_fp4_fp8(ka, K < 4 ? ql[K] : rl, sacc[h][1], sa[h][K]);
         }
-        u32x4 w = {0u, 0u, 0u, 0u};
-        uint32_t sa = 127;
-        if (g < 2) {
-          w = *reinterpret_cast<const u32x4*>(rp + 256 + 16 * g);
-          sa = sp[4 * 8 + g];
-        }
-        const fp8x32 ka = fp4_operand(w);
-        sacc[h][0] = mfma_fp4_fp8(ka, rh, sacc[h][0], sa);
-        sacc[h][1] = mfma_fp4_fp8(ka, rl, sacc[h][1], sa);
-      }
-
-      // E of the wave's tokens (the largest of each row's 16 scales of
-      // columns 0..511): lanes l and l ^ 32 take 8 scales each of token
-      // 32s + (l & 31); then lane (head r16, group g) fetches the E of its
-      // tokens 16h + 4g + i.
-      float erow;
-      {
-        const uint32_t* srow = reinterpret_cast<const uint32_t*>(sdw) + kXScalePairs * (32 * wave + (lane & 31)) +
-                               4 * (lane >> 5);
-        uint32_t em = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint32_t d = srow[k];  // scale pair in the low 16 bits
-          em = max(em, max(d & 0xFFu, (d >> 8) & 0xFFu));
-        }
-        const auto sw = __builtin_amdgcn_permlane32_swap(em, em, false, false);
-        erow = (float)max((uint32_t)sw[0], (uint32_t)sw[1]);
       }
 
       // ---- softmax: x[h][i] is token 32s + 16h + 4g + i of head r16 ----
       // y = x + E - 127 is the log2 size of the token's weight times its row
       // scale 2^(E - 127), which the e4m3 V rows leave out; the block's
-      // weights are written relative to its largest y (weight_block_scale).
-      // The sum of this lane's weights is taken against the wave's integral
-      // reference cw (the floor of its logit maximum) and moved to the running
-      // maximum's scale once that is known.
-      float x[2][4], y[2][4];
+      // weights are written relative to its largest y, F = floor(max y)
+      // (weight_block_scale).  With cw = floor(max x), u = 2^(x - cw) is the
+      // token's share of this wave's weight sum and its stored weight is
+      // 2^(y - F + 7) = u 2^(E - 120 - F + cw), both exact powers of two away.
+      const int tok0 = item.tok_begin + i * kXTile;
+      i32x4 ev[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) ev[h] = *reinterpret_cast<const i32x4*>(&sh.erow[32 * s + 16 * h + 4 * g]);
+      float x[2][4];
       float tmax = kNegInf, ymax = kNegInf;
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float ei =
-              __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (16 * h + 4 * g + i), __float_as_int(erow)));
-          x[h][i] = (sacc[h][0][i] + sacc[h][1][i]) * xscale;
-          if (tok0 + 32 * wave + 16 * h + 4 * g + i > tok_last) x[h][i] = kNegInf;
-          y[h][i] = x[h][i] + (ei - 127.0f);
-          tmax = fmaxf(tmax, x[h][i]);
-          ymax = fmaxf(ymax, y[h][i]);
+        for (int k = 0; k < 4; ++k) {
+          x[h][k] = (sacc[h][0][k] + sacc[h][1][k]) * xscale;
+          if (tok0 + 32 * s + 16 * h + 4 * g + k > tok_last) x[h][k] = kNegInf;
+          tmax = fmaxf(tmax, x[h][k]);
+          ymax = fmaxf(ymax, x[h][k] + (float)(ev[h][k] - 127));
         }
       tmax = xor_max_groups(tmax);
       ymax = xor_max_groups(ymax);
       if (g == 0) {
-        sh.red_m[r16][wave] = tmax;
-        sh.red_y[r16][wave] = ymax;
+        sh.red_m[i & 1][r16][s] = tmax;
+        sh.red_y[i & 1][r16][s] = ymax;
       }
-      wlive = tmax != kNegInf;
-      cw = weight_block_floor(tmax);
-      const float shift = 7.0f - weight_block_floor(ymax);  // y + shift < 8
+      const float cw = weight_block_floor(tmax);
+      const int kbase = (int)cw - 120 - (int)weight_block_floor(ymax);
+      float lsum = 0.f;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         float pw[4];
-        uint32_t ph, pl;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pw[i] = __builtin_amdgcn_exp2f(y[h][i] + shift);
-          lsum += __builtin_amdgcn_exp2f(x[h][i] - cw);
+        for (int k = 0; k < 4; ++k) {
+          const float u = __builtin_amdgcn_exp2f(x[h][k] - cw);
+          lsum += u;
+          pw[k] = __builtin_ldexpf(u, ev[h][k] + kbase);
         }
+        uint32_t ph, pl;
         split_fp8x4(pw[0], pw[1], pw[2], pw[3], ph, pl);
-        *reinterpret_cast<uint32_t*>(p_hi + 32 * wave + 16 * h + 4 * g) = ph;
-        *reinterpret_cast<uint32_t*>(p_lo + 32 * wave + 16 * h + 4 * g) = pl;
+        const int at = pw_off + 16 * p_chunk(r16, 2 * s + h);
+        *reinterpret_cast<uint32_t*>(&sh.p[i & 1][0][0][0] + at) = ph;
+        *reinterpret_cast<uint32_t*>(&sh.p[i & 1][1][0][0] + at) = pl;
       }
-    } else {
-      // ---- V of this tile to e4m3, each token row relative to its own
-      // largest V scale E: lanes l and l ^ 32 hold the row's 16 scales ----
-      // By table, exact for blocks within 5 binades of the row's E (nearly
-      // all); a block further below is converted again by rounding
-      // conversions (exact within 8 binades, rounded to e4m3 beyond).
-      const int row = 32 * (wave - 4) + (lane & 31);
-      const int cb0 = 8 * (lane >> 5);
-      uint32_t e[8];
-      u32x4 wv[8];
-      const uint8_t* rsrc = raw + row * kXRow + 16 * cb0;
-      const uint8_t* ssrc = sdw + 4 * kXScalePairs * row + 2 * cb0;  // pair cb/2 at dword 9 row + cb/2
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        e[k] = ssrc[4 * (k >> 1) + (k & 1)];
-        wv[k] = *reinterpret_cast<const u32x4*>(rsrc + 16 * k);
+      if (tmax != kNegInf) {
+        if (cw > m_s) {
+          l_s = (m_s == kNegInf) ? 0.0f : __builtin_ldexpf(l_s, (int)(m_s - cw));
+          m_s = cw;
+        }
+        l_s += __builtin_ldexpf(lsum, (int)(cw - m_s));
       }
-      uint32_t em = 0;
+    }
+    const float l_w = xor_sum_groups(l_s);
+    if (g == 0) {
+      fin_l[r16][s] = l_w;
+      fin_ls[r16][s] = m_s;
+    }
+  } else {
+    const int c = wave - 4;
+    uint8_t* const vblk = &sh.v[c][0];
+    f32x4 o[8];  // O^T[128c + 16v + (columns of lane group g)][head r16]
 #pragma unroll
-      for (int k = 0; k < 8; ++k) em = max(em, e[k]);
-      const auto sw = __builtin_amdgcn_permlane32_swap(em, em, false, false);
-      const int E = (int)max((uint32_t)sw[0], (uint32_t)sw[1]);
-      uint8_t* const vdst = &sh.v[row * kXVRow + 32 * cb0];
-      int jmin = 0;
+    for (int v = 0; v < 8; ++v) o[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_ref = kNegInf;
+    // Reads of this lane for P.V: tr8 read q (0..3) gives tokens tb(q) +
+    // (0..7), tb = 16g + 8q (q < 2) or 64 + 16g + 8(q - 2), from rows tb(q) +
+    // (r16 >> 1), bytes 8(r16 & 1) .. +7 of chunk v: at voff[q] + 2048 v.
+    int voff[4];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int j = max((int)e[k] - E, -126);  // <= 0
-        jmin = min(jmin, j);
-        const uint32_t kk = (uint32_t)min(-j, 5);
-        const uint32_t lut_lo = 0x3C383000u - kk * 0x08080800u;
-        const uint32_t lut_hi = 0x4C484440u - kk * 0x08080808u;
-        uint32_t e8[8];  // 32 e4m3 codes: word 2i columns 32cb + 8i + {0,2,4,6}, word 2i+1 the odd ones
+    for (int q = 0; q < 4; ++q)
+      voff[q] = 16 * v_slot((q < 2 ? 16 * g + 8 * q : 64 + 16 * g + 8 * (q - 2)) + (r16 >> 1)) + 8 * (r16 & 1);
+    const int pr0 = r16 * kXTile + 16 * p_chunk(r16, g);      // P^T tokens 16g .. +15
+    const int pr1 = r16 * kXTile + 16 * p_chunk(r16, 4 + g);  // tokens 64 + 16g .. +15
+
+    // P.V of tile i - 1, first the running maximum and the B scale of k-block
+    // g (scoring wave g's tokens) for head r16.
+    auto pv_scale = [&](const f32x4& mx, const f32x4& my) -> int {
+      const float tile_max = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
+      // Every V wave reads the same maxima, so this branch is uniform.
+      if (__ballot(tile_max > m_ref + kLazyRescale) != 0) {
+        const float m_new = floorf(fmaxf(m_ref, tile_max));
+        const float alpha = (m_ref == kNegInf) ? 0.0f : __builtin_ldexpf(1.0f, (int)(m_ref - m_new));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) fp4x8_to_fp8_lut(wv[k][i], lut_lo, lut_hi, e8[2 * i], e8[2 * i + 1]);
-        *reinterpret_cast<u32x4*>(vdst + 32 * k) = u32x4{e8[0], e8[1], e8[2], e8[3]};
-        *reinterpret_cast<u32x4*>(vdst + 32 * k + 16) = u32x4{e8[4], e8[5], e8[6], e8[7]};
+        for (int v = 0; v < 8; ++v) o[v] *= alpha;
+        m_ref = m_new;
       }
-      if (__ballot(jmin < -5) != 0) {
+      return weight_block_scale(g == 0 ? my[0] : g == 1 ? my[1] : g == 2 ? my[2] : my[3], m_ref);
+    };
+    // Block k of row rr of tile i to e4m3, relative to the row's E, by table
+    // (exact for blocks within 5 binades of E, nearly all); returns E - e.
+    auto convert_block = [&](const u32x4 (&wv)[2][4], const uint32_t (&sd)[2][2], const int (&E)[2], int rr,
+                             int k) -> int {
+      const int d = E[rr] - (int)((sd[rr][k >> 1] >> (8 * (k & 1))) & 0xFFu);  // >= 0
+      uint32_t lut_lo, lut_hi;
+      fp4_lut((uint32_t)min(d, 5), lut_lo, lut_hi);
+      uint32_t e8[8];  // 32 e4m3 codes: word 2i columns 32k + 8i + {0,2,4,6}, word 2i+1 the odd ones
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int j = max((int)e[k] - E, -126);
+      for (int m = 0; m < 4; ++m) fp4x8_to_fp8_lut(wv[rr][k][m], lut_lo, lut_hi, e8[2 * m], e8[2 * m + 1]);
+      uint8_t* const vrow = vblk + 16 * v_slot(lane + 64 * rr);
+      *reinterpret_cast<u32x4*>(vrow + kXVChunk * (2 * k)) = u32x4{e8[0], e8[1], e8[2], e8[3]};
+      *reinterpret_cast<u32x4*>(vrow + kXVChunk * (2 * k + 1)) = u32x4{e8[4], e8[5], e8[6], e8[7]};
+      return d;
+    };
+    // Blocks further than 5 binades below their row's E, converted again by
+    // rounding conversions (exact within 8 binades, rounded to e4m3 beyond).
+    auto convert_far = [&](const u32x4 (&wv)[2][4], const uint32_t (&sd)[2][2], const int (&E)[2]) {
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+        uint8_t* const vrow = vblk + 16 * v_slot(lane + 64 * rr);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int j = max((int)((sd[rr][k >> 1] >> (8 * (k & 1))) & 0xFFu) - E[rr], -126);
           if (j >= -5) continue;
           const float scale = __uint_as_float((uint32_t)(127 + j) << 23);
           uint32_t e8[8];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
+          for (int m = 0; m < 4; ++m) {
             uint32_t lo, hi;  // columns 0..3, 4..7
-            fp4x8_to_fp8(wv[k][i], scale, lo, hi);
-            e8[2 * i] = __builtin_amdgcn_perm(hi, lo, 0x06040200u);      // columns 0, 2, 4, 6
-            e8[2 * i + 1] = __builtin_amdgcn_perm(hi, lo, 0x07050301u);  // columns 1, 3, 5, 7
+            fp4x8_to_fp8(wv[rr][k][m], scale, lo, hi);
+            e8[2 * m] = __builtin_amdgcn_perm(hi, lo, 0x06040200u);      // columns 0, 2, 4, 6
+            e8[2 * m + 1] = __builtin_amdgcn_perm(hi, lo, 0x07050301u);  // columns 1, 3, 5, 7
           }
-          *reinterpret_cast<u32x4*>(vdst + 32 * k) = u32x4{e8[0], e8[1], e8[2], e8[3]};
-          *reinterpret_cast<u32x4*>(vdst + 32 * k + 16) = u32x4{e8[4], e8[5], e8[6], e8[7]};
+          *reinterpret_cast<u32x4*>(vrow + kXVChunk * (2 * k)) = u32x4{e8[0], e8[1], e8[2], e8[3]};
+          *reinterpret_cast<u32x4*>(vrow + kXVChunk * (2 * k + 1)) = u32x4{e8[4], e8[5], e8[6], e8[7]};
+        }
+      }
+    };
+
+    for (int i = 0; i <= ntiles; ++i) {
+      lds_barrier();  // tile i everywhere; P of tile i - 1 written
+      const bool pv = i >= 1, cv = i < ntiles;
+      // Token rows lane and lane + 64 of tile i, column blocks 4c .. 4c + 3
+      // (16 code bytes each) and their scales (pairs 2c, 2c + 1).
+      u32x4 wv[2][4];
+      uint32_t sd[2][2];
+      if (cv) {
+        const uint8_t* raw = &sh.raw[i & 1][0];
+        const uint32_t* sdw = reinterpret_cast<const uint32_t*>(raw + kXFp4Bytes);
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+          const int row = lane + 64 * rr;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) wv[rr][k] = *reinterpret_cast<const u32x4*>(raw + row * kXRow + 64 * c + 16 * k);
+          sd[rr][0] = sdw[kXScalePairs * row + 2 * c];
+          sd[rr][1] = sdw[kXScalePairs * row + 2 * c + 1];
+        }
+      }
+      // The operands of P.V for tile i - 1, read together with the above:
+      // the block maxima and P^T (this wave's V^T follows below).
+      f32x4 mx, my;
+      fp8x32 bh, bl;
+      if (pv) {
+        const int par = (i - 1) & 1;
+        mx = *reinterpret_cast<const f32x4*>(&sh.red_m[par][r16][0]);
+        my = *reinterpret_cast<const f32x4*>(&sh.red_y[par][r16][0]);
+        const uint8_t* pt = &sh.p[par][0][0][0];
+        bh = join16(*reinterpret_cast<const u32x4*>(pt + pr0), *reinterpret_cast<const u32x4*>(pt + pr1));
+        pt = &sh.p[par][1][0][0];
+        bl = join16(*reinterpret_cast<const u32x4*>(pt + pr0), *reinterpret_cast<const u32x4*>(pt + pr1));
+      }
+      lds_barrier();  // the row exponents of tile i; raw slot i % 2 is read
+      // Column tile v of V^T for P.V of tile i - 1, by transposing reads.
+      auto read_va = [&](int v) -> fp8x32 {
+        fp8x32 va;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const i32x2 r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vblk + voff[q] + kXVChunk * v));
+          va[2 * q] = r2[0];
+          va[2 * q + 1] = r2[1];
+        }
+        return va;
+      };
+      // Converting tile i is vector work, P.V of tile i - 1 LDS reads and
+      // matrix work.  Step j converts block j & 3 of row half j >> 2, which
+      // overwrites column tiles 2(j & 3) and 2(j & 3) + 1 of the block: steps
+      // 0..3 first read those two tiles of tile i - 1 (a wave's LDS accesses
+      // execute in order), and their MFMAs follow the step, the lo halves one
+      // step after the hi ones.  So the reads and the matrix unit work while
+      // this wave converts.
+      if (cv) {
+        const int E[2] = {sh.erow[lane], sh.erow[lane + 64]};
+        int gap = 0;
+        if (pv) {
+          const int sb = pv_scale(mx, my);
+          fp8x32 va0, va1, vp0, vp1;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            if (j < 4) {
+              va0 = read_va(2 * j);
+              va1 = read_va(2 * j + 1);
+            }
+            gap = max(gap, convert_block(wv, sd, E, j >> 2, j & 3));
+            __builtin_amdgcn_sched_barrier(0);
+            if (j < 4) {
+              o[2 * j] = mfma_fp8_k128_sb(va0, bh, o[2 * j], sb);
+              o[2 * j + 1] = mfma_fp8_k128_sb(va1, bh, o[2 * j + 1], sb);
+            }
+            if (j >= 1 && j <= 4) {
+              o[2 * j - 2] = mfma_fp8_k128_sb(vp0, bl, o[2 * j - 2], sb);
+              o[2 * j - 1] = mfma_fp8_k128_sb(vp1, bl, o[2 * j - 1], sb);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (j < 4) {
+              vp0 = va0;
+              vp1 = va1;
+            }
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) gap = max(gap, convert_block(wv, sd, E, j >> 2, j & 3));
+        }
+        if (__ballot(gap > 5) != 0) convert_far(wv, sd, E);
+      } else if (pv) {
+        const int sb = pv_scale(mx, my);
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          const fp8x32 va = read_va(v);
+          o[v] = mfma_fp8_k128_sb(va, bh, o[v], sb);
+          o[v] = mfma_fp8_k128_sb(va, bl, o[v], sb);
         }
       }
     }
-    lds_barrier();  // P^T, the maxima and the V tile; raw slot t % 2 is free
-    if (t + 2 < ntiles) issue(t + 2);
 
-    const f32x4 mx = *reinterpret_cast<const f32x4*>(&sh.red_m[r16][0]);
-    const f32x4 my = *reinterpret_cast<const f32x4*>(&sh.red_y[r16][0]);
-    const float tile_max = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
-    // Every wave reads the same maxima, so this branch is uniform.
-    if (__ballot(tile_max > m_ref + kLazyRescale) != 0) {
-      const float m_new = floorf(fmaxf(m_ref, tile_max));
-      const float alpha = (m_ref == kNegInf) ? 0.0f : __builtin_ldexpf(1.0f, (int)(m_ref - m_new));
-#pragma unroll
-      for (int v = 0; v < 4; ++v) o[v] *= alpha;
-      l_part *= alpha;
-      m_ref = m_new;
-    }
-    if (wlive) l_part += __builtin_ldexpf(lsum, (int)cw - (int)m_ref);
-    // B scale of k-block g (scoring wave g's tokens) for head r16
-    const int sb = weight_block_scale(g == 0 ? my[0] : g == 1 ? my[1] : g == 2 ? my[2] : my[3], m_ref);
-    const fp8x32 bh = join16(*reinterpret_cast<const u32x4*>(p_hi + 16 * g),
-                             *reinterpret_cast<const u32x4*>(p_hi + 64 + 16 * g));
-    const fp8x32 bl = join16(*reinterpret_cast<const u32x4*>(p_lo + 16 * g),
-                             *reinterpret_cast<const u32x4*>(p_lo + 64 + 16 * g));
-
-    // ---- O^T += V^T P^T, columns 64w + 16v ----
-#pragma unroll
-    for (int v = 0; v < 4; v += 2) {
-      fp8x32 va[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const i32x2 raw2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(&sh.v[voff[q] + 16 * (v + u)]));
-          va[u][2 * q] = raw2[0];
-          va[u][2 * q + 1] = raw2[1];
-        }
-      o[v] = mfma_fp8_k128_sb(va[0], bh, o[v], sb);
-      o[v + 1] = mfma_fp8_k128_sb(va[1], bh, o[v + 1], sb);
-      o[v] = mfma_fp8_k128_sb(va[0], bl, o[v], sb);
-      o[v + 1] = mfma_fp8_k128_sb(va[1], bl, o[v + 1], sb);
-    }
-  }
-
-  // Only the scoring waves hold weight sums.
-  const float l_w = xor_sum_groups(l_part);
-  if (scorer && g == 0) sh.red_l[r16][wave] = l_w;
-  lds_barrier();
-  const f32x4 ls = *reinterpret_cast<const f32x4*>(&sh.red_l[r16][0]);
-  const float L = (ls[0] + ls[1]) + (ls[2] + ls[3]);
-  // The V tile holds each group of 8 columns as (0, 2, 4, 6, 1, 3, 5, 7), so
-  // lane group g has output columns 8(g >> 1) + 2i + (g & 1) of each column
-  // tile; lanes l and l ^ 16 trade two values each to return to columns
-  // 4g + i.
-  {
+    // The V blocks hold each group of 8 columns as (0, 2, 4, 6, 1, 3, 5, 7),
+    // so lane group g has output columns 8(g >> 1) + 2i + (g & 1) of each
+    // column tile; lanes l and l ^ 16 trade two values each to return to
+    // columns 4g + i.  Then the output goes to raw slot 0 for all waves.
     const int partner = (lane ^ 16) << 2;
     const bool odd = (g & 1) != 0;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
+    for (int v = 0; v < 8; ++v) {
       const float r0 = __int_as_float(__builtin_amdgcn_ds_bpermute(partner, __float_as_int(odd ? o[v][0] : o[v][2])));
       const float r1 = __int_as_float(__builtin_amdgcn_ds_bpermute(partner, __float_as_int(odd ? o[v][1] : o[v][3])));
-      o[v] = odd ? f32x4{r0, o[v][2], r1, o[v][3]} : f32x4{o[v][0], r0, o[v][1], r1};
+      hand[(8 * c + v) * 64 + lane] = odd ? f32x4{r0, o[v][2], r1, o[v][3]} : f32x4{o[v][0], r0, o[v][1], r1};
     }
+    if (c == 0 && g == 0) fin_m[r16] = m_ref;
   }
-  finish_item<4>(a, item, tid, wave >> 1, 4 * (wave & 1), lane, o, 1.0f / L, m_ref + __log2f(L));
+  lds_barrier();  // the output, the weight sums and the references
+
+  const float m_ref = fin_m[r16];
+  const f32x4 lv = *reinterpret_cast<const f32x4*>(&fin_l[r16][0]);
+  const f32x4 mv = *reinterpret_cast<const f32x4*>(&fin_ls[r16][0]);
+  float L = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (mv[k] != kNegInf) L += __builtin_ldexpf(lv[k], (int)(mv[k] - m_ref));
+  // Wave w finishes columns 64w .. 64w + 63: tiles 4(w & 1) .. +3 of V wave w >> 1.
+  const int W = wave >> 1, vb = 4 * (wave & 1);
+  f32x4 ow[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) ow[v] = hand[(8 * W + vb + v) * 64 + lane];
+  finish_item<4>(a, item, tid, W, vb, lane, ow, 1.0f / L, m_ref + __log2f(L));
 }
 
 // A workgroup runs one item, or with bins the items of bin blockIdx.x in

@@ -251,12 +251,12 @@ def test_planner_small_batch_long_context_fills_the_gpu(B, fmt):
 
 def test_planner_paged_items_fit_the_staged_pages(B):
     """A paged item's page ids are staged in LDS by the split kernel (2560 for
-    fp8, 1536 for MXFP4, 2048 for bf16, an item's first and last page possibly
+    fp8, 1024 for MXFP4, 2048 for bf16, an item's first and last page possibly
     partial), so the planner caps paged items at (pages - 2) * page_size
     tokens, in whole tiles (128 tokens, 64 for bf16); uniform batches plan the
     same items as a contiguous cache."""
     ps = 2
-    for fmt, pages in (("fp8", 2560), ("mxfp4", 1536), ("bf16", 2048)):
+    for fmt, pages in (("fp8", 2560), ("mxfp4", 1024), ("bf16", 2048)):
         tile = 64 if fmt == "bf16" else 128
         lens = [100000, 5]
         npg = [(n + ps - 1) // ps for n in lens]
@@ -319,15 +319,15 @@ def test_planner_ragged_batch_gets_even_bins(B, fmt, page_size):
     assert np.all(items[~whole, 1] % 128 == 0)     # pieces start on a tile
     assert np.bincount(items[:, 0]).max() <= 12    # the kernels merge these themselves
     if page_size > 1:
-        cap = 2560 if fmt == "fp8" else 1536
+        cap = 2560 if fmt == "fp8" else 1024
         first = items[:, 1] // page_size
         lastp = (items[:, 2] - 1) // page_size
         assert np.all(lastp - first + 1 <= cap)
 
 
 def test_planner_bins_respect_the_page_cap_and_split_limit(B):
-    """Bins never give a paged item more pages than the kernel stages (1536
-    for MXFP4: at most 1534 whole 2-token pages, 2944 tokens in whole tiles),
+    """Bins never give a paged item more pages than the kernel stages (1024
+    for MXFP4: at most 1022 whole 2-token pages, 1920 tokens in whole tiles),
     and no sequence more than 32 items; where the page cap alone would need
     more, the batch falls back to one item per workgroup."""
     ps = 2
@@ -340,9 +340,9 @@ def test_planner_bins_respect_the_page_cap_and_split_limit(B):
                                                     blocks_per_cu=1, kv_dtype="mxfp4")
         _check_cover(items.tolist(), lens.tolist(), slots)
         sizes = items[:, 2] - items[:, 1]
-        assert sizes.max() <= 2944
+        assert sizes.max() <= 1920
         binned = len(items) > 0 and items[-1, 4] < len(items) - 1
-        assert binned == (lens.max() <= 32 * 2944), lens.max()
+        assert binned == (lens.max() <= 32 * 1920), lens.max()
         if binned:
             assert np.bincount(items[:, 0]).max() <= 32
 
@@ -440,7 +440,7 @@ def test_planner_multi_token_rejects_bad_qo_indptr(B, qo, why):
 
 from hypothesis import given, settings, strategies as st  # noqa: E402
 
-PAGE_CAP = {"fp8": 2560, "mxfp4": 1536, "bf16": 2048}
+PAGE_CAP = {"fp8": 2560, "mxfp4": 1024, "bf16": 2048}
 
 
 @settings(max_examples=150, deadline=None)

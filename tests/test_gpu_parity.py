@@ -239,7 +239,7 @@ def test_mxfp4_scale_strides(B, oracle_mod, stride):
 @pytest.mark.parametrize("fmt", ["fp8", "mxfp4", "bf16"])
 def test_paged_items_at_the_page_cap(B, oracle_mod, fmt):
     """One split per sequence forces paged items up to the number of page ids
-    the split kernel stages in LDS (2560 fp8, 1536 MXFP4, 2048 bf16; 2-token
+    the split kernel stages in LDS (2560 fp8, 1024 MXFP4, 2048 bf16; 2-token
     pages)."""
     case = synth.make_case(fmt, [11000, 300, 7], seed=43, page_size=2, shuffle_pages=True, guard_rows=3)
     check_close(run_gpu(B, case, 1), oracle_out(oracle_mod, case), fmt, f"{fmt} page cap")
