@@ -138,6 +138,8 @@ def measure(name, args, dev, torch, binding, synth, full=True):
                        for _ in range(n_copies - 1)]
 
     dec = binding.MlaDecode(kv_dtype, ps, device=0)
+    if args.query_format != "exact":
+        dec.set_query_format(args.query_format)
     t0 = time.perf_counter()
     ws_bytes = dec.plan(case.kv_indptr, case.kv_last_page_len, args.split, case.qo_indptr)
     plan_us = (time.perf_counter() - t0) * 1e6
@@ -238,7 +240,7 @@ def measure(name, args, dev, torch, binding, synth, full=True):
                     "stage1_scratch_bytes": res1["scratch_bytes"]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_record(name, kv_dtype)},
+                     "traffic": traffic_record(name, kv_dtype) if args.query_format == "exact" else None},
         "plan": {"items": n_items, "max_splits": max_splits, "partials": n_partials,
                  "workspace_bytes": int(ws_bytes), "plan_us": round(plan_us, 1),
                  "replan_us": round(float(np.median(replan)), 1)},
@@ -248,7 +250,7 @@ def measure(name, args, dev, torch, binding, synth, full=True):
                          "query_rows": int(case.rows),
                          "kv_len": kv_len if isinstance(kv_len, int) else list(kv_len),
                          "total_tokens": int(case.total_tokens), "page_size": ps,
-                         "algorithmic_kv_bytes": int(alg_bytes)}
+                         "query_format": args.query_format, "algorithmic_kv_bytes": int(alg_bytes)}
         rec["input_copies"] = n_copies
         rec["timed_wall_s"] = round(wall, 3)
         rec["mean_ms"] = mean_ms
@@ -275,6 +277,8 @@ def main():
     ap.add_argument("--cold-calls", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--split", type=int, default=0, help="split override (0 = planner)")
+    ap.add_argument("--query-format", choices=("exact", "e4m3"), default="exact",
+                    help="the query in the scores: exact (e4m3 hi + lo, default) or one e4m3 code per element")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device 5 times (a kernel of known traffic "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")

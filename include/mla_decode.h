@@ -251,6 +251,32 @@ mla_status mla_decode_run_noalloc(mla_decode_t h, const void* q, const void* kv,
                                   void* stream);
 
 /*
+ * Precision of the query in the score contraction of the fp8 and MXFP4 split
+ * kernels.  Default MLA_QUERY_EXACT: each query element enters as the sum of
+ * two e4m3 codes (hi + lo) after a power-of-two scaling per (row, head), which
+ * keeps every element exactly but those below 2^-10 of the head's largest.
+ * MLA_QUERY_E4M3: each element enters as one e4m3 code -- the query row of
+ * each head is scaled by the power of two 2^s that puts its largest |q| in
+ * [128, 256), and q * 2^s is rounded to the nearest e4m3 value, ties to even
+ * -- so the scores take one matrix product instead of two.  This is the
+ * low-precision query of submission 599694 ("overhead elimination", the
+ * static fp8 query scale of its fast path), with the scale found per row and
+ * head instead of fixed in advance.  It rounds the query to 4 significant
+ * bits: scores move by up to 2^-4 of |q|.|c_t| per element, which is harmless
+ * on well-scaled caches but not on caches whose rows reach large magnitudes.
+ * MLA_ERR_UNSUPPORTED for a bf16 cache; an MXFP4 run with an odd scale
+ * stride or scale address (which uses the bf16-decoding kernel) is refused
+ * with MLA_ERR_UNSUPPORTED while MLA_QUERY_E4M3 is set.  Takes effect from
+ * the next run; MLA_ERR_INVALID_ARG for any other value.
+ */
+typedef enum {
+  MLA_QUERY_EXACT = 0,
+  MLA_QUERY_E4M3 = 1
+} mla_query_format;
+
+mla_status mla_decode_set_query_format(mla_decode_t h, int query_format);
+
+/*
  * Kernel timing for measurement.  While enabled, mla_decode_run launches its
  * kernels with a pair of HIP events each, which the launch itself records
  * when the kernel starts and when it ends (hipExtLaunchKernel);

@@ -24,6 +24,8 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED",
 
 NUM_HEADS, QK_DIM, V_DIM = 16, 576, 512
 MLA_SCRATCH_BYTES = 16 << 20  # the allocation-free run's device array (MLA_SCRATCH_BYTES)
+MLA_QUERY_EXACT, MLA_QUERY_E4M3 = 0, 1
+QUERY_FORMATS = {"exact": MLA_QUERY_EXACT, "e4m3": MLA_QUERY_E4M3}
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m latent_attention_decode_amd.build`"
@@ -57,6 +59,7 @@ _lib.mla_decode_run.argtypes = [_H, _P, _P, _P, ctypes.c_int64, _P, _P, _P, _P, 
                                 ctypes.c_size_t, _P]
 _lib.mla_decode_run_noalloc.argtypes = [_H, _P, _P, _P, ctypes.c_int64, _P, _P, _P, _P, _P]
 _lib.mla_decode_set_profiling.argtypes = [_H, ctypes.c_int]
+_lib.mla_decode_set_query_format.argtypes = [_H, ctypes.c_int]
 _lib.mla_decode_kernel_time_ms.argtypes = [_H, ctypes.c_int, ctypes.POINTER(ctypes.c_float)]
 _lib.mla_decode_kernel_resources.argtypes = [_H, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
                                              ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
@@ -66,14 +69,15 @@ _lib.mla_decode_last_error.restype = ctypes.c_char_p
 for _name in ("mla_decode_create", "mla_decode_plan", "mla_decode_plan_preview", "mla_decode_plan_multi",
               "mla_decode_plan_preview_multi",
               "mla_decode_plan_info", "mla_decode_run", "mla_decode_run_noalloc", "mla_decode_set_profiling",
-              "mla_decode_kernel_time_ms", "mla_decode_kernel_resources", "mla_decode_destroy"):
+              "mla_decode_set_query_format", "mla_decode_kernel_time_ms", "mla_decode_kernel_resources",
+              "mla_decode_destroy"):
     getattr(_lib, _name).restype = ctypes.c_int
 
 EXPORTED = ("mla_decode_version", "mla_status_string", "mla_decode_create", "mla_decode_plan",
             "mla_decode_plan_preview", "mla_decode_plan_multi", "mla_decode_plan_preview_multi",
             "mla_decode_plan_info", "mla_decode_run", "mla_decode_run_noalloc",
-            "mla_decode_set_profiling", "mla_decode_kernel_time_ms", "mla_decode_kernel_resources",
-            "mla_decode_destroy", "mla_decode_last_error")
+            "mla_decode_set_profiling", "mla_decode_set_query_format", "mla_decode_kernel_time_ms",
+            "mla_decode_kernel_resources", "mla_decode_destroy", "mla_decode_last_error")
 
 
 class MlaError(RuntimeError):
@@ -320,6 +324,13 @@ class PreparedRun:
             _check(st, "mla_decode_run", self._h)
 
 
+def mla_decode_set_query_format(h, query_format: str) -> None:
+    """'exact' (default: the query as e4m3 hi + lo) or 'e4m3' (one e4m3 code per element)."""
+    if query_format not in QUERY_FORMATS:
+        raise ValueError(f"query_format must be one of {sorted(QUERY_FORMATS)}")
+    _check(_lib.mla_decode_set_query_format(h, QUERY_FORMATS[query_format]), "mla_decode_set_query_format", h)
+
+
 def mla_decode_set_profiling(h, enable: bool) -> None:
     _check(_lib.mla_decode_set_profiling(h, int(bool(enable))), "mla_decode_set_profiling", h)
 
@@ -411,6 +422,9 @@ class MlaDecode:
                                       or out.numel() // (NUM_HEADS * V_DIM) < self.rows):
             raise ValueError(f"the plan covers {self.rows} query rows; q {tuple(q.shape)} / out "
                              f"{tuple(out.shape)} hold fewer")
+
+    def set_query_format(self, query_format: str) -> None:
+        mla_decode_set_query_format(self.h, query_format)
 
     def close(self) -> None:
         if self.h:

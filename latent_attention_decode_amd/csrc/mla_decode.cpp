@@ -64,6 +64,7 @@ struct mla_decode_s {
 
   // measurement
   bool profiling = false;
+  int query_format = MLA_QUERY_EXACT;
   bool events_ready = false;
   bool timed_run = false;
   bool merge_timed = false;
@@ -72,7 +73,7 @@ struct mla_decode_s {
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 4 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 5 * 100 + 0;
 static_assert(MLA_SCRATCH_BYTES == mla::kScratchBytes, "scratch size in the header");
 
 mla_status fail(mla_decode_t h, mla_status st, const char* fmt, ...) {
@@ -925,6 +926,10 @@ mla_status mla_decode_run(mla_decode_t h, const void* q, const void* kv, const v
   a.uniform_chunk = h->uniform_chunk;
   a.uniform_len = h->uniform_len;
   a.uniform_base = h->uniform_base;
+  a.query_e4m3 = h->query_format == MLA_QUERY_E4M3;
+  if (a.query_e4m3 && !mla::stage1_dedicated(h->kv_dtype, a))
+    return fail(h, MLA_ERR_UNSUPPORTED,
+                "MLA_QUERY_E4M3 needs the MXFP4 split kernel, which needs an even scale stride and scale address");
   const size_t merge_bytes = static_cast<size_t>(h->num_merge) * sizeof(mla::MergeSeq);
   a.counters = h->fused_merge && h->num_merge > 0 && mla::stage1_dedicated(h->kv_dtype, a)
                    ? reinterpret_cast<int*>(plan_base + items_bytes + merge_bytes)
@@ -981,6 +986,18 @@ mla_status mla_decode_run_noalloc(mla_decode_t h, const void* q, const void* kv,
   }
   return mla_decode_run(h, q, kv, kv_scales, kv_scale_stride, kv_indptr, kv_page_indices, kv_last_page_len, out,
                         scratch, scratch ? mla::kScratchBytes : 0, stream);
+}
+
+mla_status mla_decode_set_query_format(mla_decode_t h, int query_format) {
+  if (!h) return MLA_ERR_INVALID_ARG;
+  h->last_error.clear();
+  if (query_format != MLA_QUERY_EXACT && query_format != MLA_QUERY_E4M3)
+    return fail(h, MLA_ERR_INVALID_ARG, "query_format must be MLA_QUERY_EXACT or MLA_QUERY_E4M3 (got %d)",
+                query_format);
+  if (query_format == MLA_QUERY_E4M3 && h->kv_dtype == MLA_KV_BF16)
+    return fail(h, MLA_ERR_UNSUPPORTED, "MLA_QUERY_E4M3 applies to fp8 and MXFP4 caches");
+  h->query_format = query_format;
+  return MLA_OK;
 }
 
 mla_status mla_decode_set_profiling(mla_decode_t h, int enable) {

@@ -130,6 +130,9 @@ struct Stage1Args {
   // bins[k] .. bins[k + 1] - 1, one after the other; null: workgroup k runs
   // item k.  The bins of a ragged batch carry about equal work.
   const int32_t* bins;
+  // Host side only: launch the split kernel's variant that takes the query as
+  // one e4m3 code per element (fp8 and MXFP4 split kernels).
+  int query_e4m3;
 };
 
 struct MergeArgs {
@@ -153,8 +156,9 @@ constexpr size_t kScratchBytes = size_t(16) << 20;
 hipError_t scratch_address(int device, void** ptr);
 
 // The fp8 and MXFP4 split kernels (mla_stage1_fp8.hip, mla_stage1_mxfp4.hip).
-const void* stage1_fp8_kernel(bool paged, bool row_pairs);
-const void* stage1_mxfp4_kernel(bool paged);
+// query_e4m3: the variant that takes the query as one e4m3 code per element.
+const void* stage1_fp8_kernel(bool paged, bool row_pairs, bool query_e4m3 = false);
+const void* stage1_mxfp4_kernel(bool paged, bool query_e4m3 = false);
 // Whether launch_stage1 runs the split kernel of that file for these
 // arguments (it does for fp8; for MXFP4 when the scale array and its row
 // stride are 2-byte aligned, else the bf16-decoding kernel).  Only those

@@ -707,10 +707,14 @@ bool stage1_dedicated(int fmt, const Stage1Args& a) {
 
 hipError_t launch_stage1(int fmt, bool paged, bool row_pairs, const Stage1Args& a, int num_items, hipStream_t s,
                          hipEvent_t start, hipEvent_t stop) {
-  const void* fn = (fmt == kFp8 && row_pairs) ? stage1_fp8_kernel(paged, true) : pick_stage1(fmt, paged);
-  if (fmt == kMxfp4 && !stage1_dedicated(fmt, a))  // two-byte scale loads need even addresses
+  const void* fn = fmt == kFp8     ? stage1_fp8_kernel(paged, row_pairs, a.query_e4m3 != 0)
+                   : fmt == kMxfp4 ? stage1_mxfp4_kernel(paged, a.query_e4m3 != 0)
+                                   : pick_stage1(fmt, paged);
+  if (fmt == kMxfp4 && !stage1_dedicated(fmt, a)) {  // two-byte scale loads need even addresses
+    if (a.query_e4m3) return hipErrorNotSupported;
     fn = paged ? reinterpret_cast<const void*>(&mla_stage1<kMxfp4, true>)
                : reinterpret_cast<const void*>(&mla_stage1<kMxfp4, false>);
+  }
   if (!fn) return hipErrorInvalidValue;
   const int threads = (fmt == kMxfp4 && stage1_dedicated(fmt, a)) ? kStage1ThreadsMxfp4 : kStage1Threads;
   Stage1Args args = a;

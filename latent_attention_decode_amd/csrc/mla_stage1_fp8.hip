@@ -151,8 +151,9 @@ static_assert(2 * 2 * kQBytes <= kCTileBytes, "two query rows and their e4m3 wor
 // One group of NR work items: NR consecutive query rows of one sequence over
 // the same tokens from tok_begin (NR = 1: any work item).  Row r stops at its
 // own tok_end; the cache tiles are loaded once for all rows, and the score and
-// value contractions share each operand read from them.
-template <bool PAGED, int NR, int NRL>
+// value contractions share each operand read from them.  Q1: the query enters
+// the scores as one e4m3 code per element (hi alone), not as hi + lo.
+template <bool PAGED, int NR, bool Q1, int NRL>
 __device__ __forceinline__ void fp8_item(const Stage1Args& a, const WorkItem* items, Fp8Lds<NRL>& sh) {
   constexpr int kMaxItemPages = Fp8Lds<NRL>::kPages;
   const WorkItem& item = items[0];  // the rows share kv_base and tok_begin
@@ -316,11 +317,13 @@ __device__ __forceinline__ void fp8_item(const Stage1Args& a, const WorkItem* it
       u32x4* const kl = reinterpret_cast<u32x4*>(qcv + ((2 * wave + 1) * 64 + lane) * 8);
       kh[0] = u32x4{hw[0], hw[1], hw[2], hw[3]};
       kh[1] = u32x4{hw[4], hw[5], hw[6], hw[7]};
-      kl[0] = u32x4{lw[0], lw[1], lw[2], lw[3]};
-      kl[1] = u32x4{lw[4], lw[5], lw[6], lw[7]};
+      if constexpr (!Q1) {
+        kl[0] = u32x4{lw[0], lw[1], lw[2], lw[3]};
+        kl[1] = u32x4{lw[4], lw[5], lw[6], lw[7]};
+      }
       if (rope) {
         *reinterpret_cast<uint2*>(qcv + 4096 + ((2 * wave) * 64 + lane) * 2) = uint2{hw[8], hw[9]};
-        *reinterpret_cast<uint2*>(qcv + 4096 + ((2 * wave + 1) * 64 + lane) * 2) = uint2{lw[8], lw[9]};
+        if constexpr (!Q1) *reinterpret_cast<uint2*>(qcv + 4096 + ((2 * wave + 1) * 64 + lane) * 2) = uint2{lw[8], lw[9]};
       }
     }
     lds_barrier();
@@ -332,14 +335,16 @@ __device__ __forceinline__ void fp8_item(const Stage1Args& a, const WorkItem* it
         const u32x4* h = reinterpret_cast<const u32x4*>(qcv + ((2 * K) * 64 + lane) * 8);
         const u32x4* l = reinterpret_cast<const u32x4*>(qcv + ((2 * K + 1) * 64 + lane) * 8);
         qh[r][K] = join16(h[0], h[1]);
-        ql[r][K] = join16(l[0], l[1]);
+        if constexpr (!Q1) ql[r][K] = join16(l[0], l[1]);
       }
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const uint2 wh = *reinterpret_cast<const uint2*>(qcv + 4096 + ((2 * h) * 64 + lane) * 2);
-        const uint2 wl = *reinterpret_cast<const uint2*>(qcv + 4096 + ((2 * h + 1) * 64 + lane) * 2);
         rh[r][h] = pack_fp8x8(wh.x, wh.y);
-        rl[r][h] = pack_fp8x8(wl.x, wl.y);
+        if constexpr (!Q1) {
+          const uint2 wl = *reinterpret_cast<const uint2*>(qcv + 4096 + ((2 * h + 1) * 64 + lane) * 2);
+          rl[r][h] = pack_fp8x8(wl.x, wl.y);
+        }
       }
     }
   }
@@ -414,7 +419,7 @@ __device__ __forceinline__ void fp8_item(const Stage1Args& a, const WorkItem* it
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
           sacc[r][s][0] = mfma_fp8_k128(ka, qh[r][K], sacc[r][s][0]);
-          sacc[r][s][1] = mfma_fp8_k128(ka, ql[r][K], sacc[r][s][1]);
+          if constexpr (!Q1) sacc[r][s][1] = mfma_fp8_k128(ka, ql[r][K], sacc[r][s][1]);
         }
       }
       if (more && (K == 1 || K == 3)) issue(t + 1, K == 1 ? 1 : 2);
@@ -427,9 +432,15 @@ __device__ __forceinline__ void fp8_item(const Stage1Args& a, const WorkItem* it
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
         sacc[r][s][0] = mfma_fp8(ka, rh[r][0], sacc[r][s][0]);
-        sacc[r][s][1] = mfma_fp8(ka, rl[r][0], sacc[r][s][1]);
-        sacc[r][s][0] = mfma_fp8(kb, rh[r][1], sacc[r][s][0]);
-        sacc[r][s][1] = mfma_fp8(kb, rl[r][1], sacc[r][s][1]);
+        if constexpr (Q1) {
+          // the second rope step on the idle accumulator: no two of these
+          // steps chained back to back on one accumulator
+          sacc[r][s][1] = mfma_fp8(kb, rh[r][1], sacc[r][s][1]);
+        } else {
+          sacc[r][s][1] = mfma_fp8(ka, rl[r][0], sacc[r][s][1]);
+          sacc[r][s][0] = mfma_fp8(kb, rh[r][1], sacc[r][s][0]);
+          sacc[r][s][1] = mfma_fp8(kb, rl[r][1], sacc[r][s][1]);
+        }
       }
     }
 
@@ -546,7 +557,7 @@ __device__ __forceinline__ void fp8_item(const Stage1Args& a, const WorkItem* it
 // MAXROWS = 2 (multi-token plans): two items next to each other in a bin
 // that are consecutive query rows of one sequence over the same tokens run
 // together.
-template <bool PAGED, int MAXROWS>
+template <bool PAGED, int MAXROWS, bool Q1>
 __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a) {
   __shared__ __attribute__((aligned(16))) Fp8Lds<MAXROWS> sh;
   int i = a.bins ? a.bins[blockIdx.x] : (int)blockIdx.x;
@@ -558,7 +569,7 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a
         if (pair[0].slot != WorkItem::kEmpty && pair[1].slot != WorkItem::kEmpty &&
             pair[1].batch == pair[0].batch + 1 && pair[1].kv_base == pair[0].kv_base &&
             pair[1].tok_begin == pair[0].tok_begin) {
-          fp8_item<PAGED, 2>(a, pair, sh);
+          fp8_item<PAGED, 2, Q1>(a, pair, sh);
           i += 2;
           if (i == i_end) break;
           wait_loads<0>();
@@ -571,7 +582,7 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a
                               ? uniform_item(xcd_block(blockIdx.x, gridDim.x), a.uniform_splits, a.uniform_chunk,
                                              a.uniform_len, a.uniform_base)
                               : a.items[i];
-    fp8_item<PAGED, 1>(a, &item, sh);
+    fp8_item<PAGED, 1, Q1>(a, &item, sh);
     if (++i == i_end) break;
     wait_loads<0>();
     lds_barrier();
@@ -580,12 +591,17 @@ __global__ __launch_bounds__(kStage1Threads, 1) void mla_stage1_fp8(Stage1Args a
 
 }  // namespace
 
-const void* stage1_fp8_kernel(bool paged, bool row_pairs) {
+template <bool Q1>
+const void* fp8_kernel(bool paged, bool row_pairs) {
   if (row_pairs)
-    return paged ? reinterpret_cast<const void*>(&mla_stage1_fp8<true, 2>)
-                 : reinterpret_cast<const void*>(&mla_stage1_fp8<false, 2>);
-  return paged ? reinterpret_cast<const void*>(&mla_stage1_fp8<true, 1>)
-               : reinterpret_cast<const void*>(&mla_stage1_fp8<false, 1>);
+    return paged ? reinterpret_cast<const void*>(&mla_stage1_fp8<true, 2, Q1>)
+                 : reinterpret_cast<const void*>(&mla_stage1_fp8<false, 2, Q1>);
+  return paged ? reinterpret_cast<const void*>(&mla_stage1_fp8<true, 1, Q1>)
+               : reinterpret_cast<const void*>(&mla_stage1_fp8<false, 1, Q1>);
+}
+
+const void* stage1_fp8_kernel(bool paged, bool row_pairs, bool query_e4m3) {
+  return query_e4m3 ? fp8_kernel<true>(paged, row_pairs) : fp8_kernel<false>(paged, row_pairs);
 }
 
 }  // namespace mla

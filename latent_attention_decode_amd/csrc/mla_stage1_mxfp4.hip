@@ -184,8 +184,9 @@ __device__ __forceinline__ void fp4_lut(uint32_t k, uint32_t& lut_lo, uint32_t& 
   lut_hi = 0x4C484440u - rep;
 }
 
-// One work item: tokens [tok_begin, tok_end) of one sequence.
-template <bool PAGED>
+// One work item: tokens [tok_begin, tok_end) of one sequence.  Q1: the query
+// enters the scores as one e4m3 code per element (hi alone), not as hi + lo.
+template <bool PAGED, bool Q1>
 __device__ __forceinline__ void mxfp4_item(const Stage1Args& a, const WorkItem& item, Fp4Lds& sh) {
   const int tid = threadIdx.x;
   if (item.slot == WorkItem::kEmpty) {  // empty sequence: its output is zero
@@ -452,7 +453,7 @@ __device__ __forceinline__ void mxfp4_item(const Stage1Args& a, const WorkItem& 
         for (int K = 0; K < 5; ++K) {
           const fp8x32 ka = fp4_operand(kc[h][K]);
           sacc[h][0] = mfma_fp4_fp8(ka, K < 4 ? qh[K] : rh, sacc[h][0], sa[h][K]);
-          sacc[h][1] = mfma_fp4_fp8(ka, K < 4 ? ql[K] : rl, sacc[h][1], sa[h][K]);
+          if constexpr (!Q1) sacc[h][1] = mfma_fp4_fp8(ka, K < 4 ? ql[K] : rl, sacc[h][1], sa[h][K]);
         }
       }
 
@@ -715,7 +716,7 @@ __device__ __forceinline__ void mxfp4_item(const Stage1Args& a, const WorkItem& 
 // A workgroup runs one item, or with bins the items of bin blockIdx.x in
 // order (see Stage1Args).  Between two items every load and store of the
 // first is complete and every wave is past it, so the next may reuse LDS.
-template <bool PAGED>
+template <bool PAGED, bool Q1>
 __global__ __launch_bounds__(kXThreads, 1) void mla_stage1_mxfp4(Stage1Args a) {
   __shared__ __attribute__((aligned(16))) Fp4Lds sh;
   int i = a.bins ? a.bins[blockIdx.x] : (int)blockIdx.x;
@@ -725,7 +726,7 @@ __global__ __launch_bounds__(kXThreads, 1) void mla_stage1_mxfp4(Stage1Args a) {
                               ? uniform_item(xcd_block(blockIdx.x, gridDim.x), a.uniform_splits, a.uniform_chunk,
                                              a.uniform_len, a.uniform_base)
                               : a.items[i];
-    mxfp4_item<PAGED>(a, item, sh);
+    mxfp4_item<PAGED, Q1>(a, item, sh);
     if (++i == i_end) break;
     wait_loads<0>();
     lds_barrier();
@@ -734,9 +735,12 @@ __global__ __launch_bounds__(kXThreads, 1) void mla_stage1_mxfp4(Stage1Args a) {
 
 }  // namespace
 
-const void* stage1_mxfp4_kernel(bool paged) {
-  return paged ? reinterpret_cast<const void*>(&mla_stage1_mxfp4<true>)
-               : reinterpret_cast<const void*>(&mla_stage1_mxfp4<false>);
+const void* stage1_mxfp4_kernel(bool paged, bool query_e4m3) {
+  if (query_e4m3)
+    return paged ? reinterpret_cast<const void*>(&mla_stage1_mxfp4<true, true>)
+                 : reinterpret_cast<const void*>(&mla_stage1_mxfp4<false, true>);
+  return paged ? reinterpret_cast<const void*>(&mla_stage1_mxfp4<true, false>)
+               : reinterpret_cast<const void*>(&mla_stage1_mxfp4<false, false>);
 }
 
 }  // namespace mla

@@ -52,6 +52,8 @@ class OracleLib:
                                                 ctypes.c_int64, P, P, P, ctypes.c_int, P, P,
                                                 ctypes.c_int, ctypes.c_int, P, P]
         lib.oracle_mla_decode_multi.restype = ctypes.c_int
+        lib.oracle_round_query_e4m3.argtypes = [P, ctypes.c_int64, ctypes.c_int, ctypes.c_int, P]
+        lib.oracle_round_query_e4m3.restype = ctypes.c_int
         self.lib = lib
         self.path = path
 
@@ -66,6 +68,17 @@ class OracleLib:
 
     def e2m1_to_f64(self, nibble: int) -> float:
         return self.lib.oracle_e2m1_to_f64(int(nibble))
+
+    def round_query_e4m3(self, q_bits: np.ndarray) -> np.ndarray:
+        """The query rounded to one e4m3 code per element under the power-of-two
+        scale of each (row, head), as bf16 bit patterns of the same shape."""
+        q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
+        rows, nh, qk_dim = q_bits.shape
+        out = np.empty_like(q_bits)
+        rc = self.lib.oracle_round_query_e4m3(_ptr(q_bits), rows, nh, qk_dim, _ptr(out))
+        if rc:
+            raise ValueError(f"oracle_round_query_e4m3 failed (code {rc})")
+        return out
 
     def dequant_rows(self, kv_dtype: str, kv: np.ndarray, rows: Sequence[int], *,
                      kv_scale: float = 1.0, kv_scales: Optional[np.ndarray] = None,
@@ -179,6 +192,10 @@ def e8m0_to_f64(code):
 
 def e2m1_to_f64(nibble):
     return default().e2m1_to_f64(nibble)
+
+
+def round_query_e4m3(*a, **kw):
+    return default().round_query_e4m3(*a, **kw)
 
 
 def dequant_rows(*a, **kw):

@@ -47,6 +47,15 @@
  * aiter path; 727205 "v25: LEAN", its metadata call); the causal placement of
  * longer query runs is the plainest reading of that argument.
  *
+ * The low-precision query (oracle_round_query_e4m3) is a pre-processing of q
+ * for the exact decode: submission 599694 ("overhead elimination") quantises
+ * the query to fp8 e4m3 under a scale (the static query scale of its fast
+ * path) before its aiter call.  Here the scale is the power of two 2^s per
+ * (row, head) that puts the head's largest |q| in [128, 256) -- the reading
+ * of "a scale" that needs no assumption about the query's range -- and
+ * q * 2^s is rounded to the nearest e4m3 value, ties to even, then scaled
+ * back.  The decode of the rounded query is the definition of that mode.
+ *
  * The optional split mode computes, for a caller-given partition of each
  * sequence into token ranges, every range's exact (normalised output, lse) and
  * then merges them by lse weights: M = max_s lse_s, w_s = exp(lse_s - M),
@@ -137,6 +146,58 @@ static void dequant_row(const cache_t* c, int64_t row, double* out) {
             out[d] = oracle_e2m1_to_f64(nib) * oracle_e8m0_to_f64(sc[d / 32]);
         }
     }
+}
+
+/* ---- the low-precision query --------------------------------------------- */
+
+/* Nearest e4m3 value to x, ties to the even code: 4 significant bits with the
+ * leading bit at 2^e, e >= -6 (steps of 2^-9 below 2^-6).  |x| < 448 here. */
+static double round_e4m3(double x) {
+    double a = fabs(x), r;
+    int e;
+    if (a == 0.0) return x;
+    frexp(a, &e);                 /* a = f * 2^e, f in [0.5, 1): leading bit 2^(e-1) */
+    e = e - 1;
+    if (e < -6) e = -6;
+    r = nearbyint(ldexp(a, 3 - e));   /* in units of 2^(e-3); the default mode rounds ties to even */
+    r = ldexp(r, e - 3);
+    return copysign(r, x);
+}
+
+/* q [rows, nh, qk_dim] bf16 bit patterns -> out, the same shape: each element
+ * rounded to one e4m3 code under the per-(row, head) scale 2^s, s = 8 - e for
+ * the head's largest |q| = f * 2^e, f in [0.5, 1) (s = 0 for a zero head).
+ * The result is exact in bf16.  Returns 0, or -1 for a non-finite query
+ * element, -2 if a result would not be a bf16 value. */
+int oracle_round_query_e4m3(const uint16_t* q, int64_t rows, int nh, int qk_dim, uint16_t* out) {
+    int64_t r;
+    int h, d;
+    for (r = 0; r < rows; ++r)
+        for (h = 0; h < nh; ++h) {
+            const uint16_t* qh = q + (r * nh + h) * qk_dim;
+            uint16_t* oh = out + (r * nh + h) * qk_dim;
+            double amax = 0.0;
+            int s = 0, e;
+            for (d = 0; d < qk_dim; ++d) {
+                double v = fabs(oracle_bf16_to_f64(qh[d]));
+                if (!isfinite(v)) return -1;
+                if (v > amax) amax = v;
+            }
+            if (amax > 0.0) {
+                frexp(amax, &e);
+                s = 8 - e;
+            }
+            for (d = 0; d < qk_dim; ++d) {
+                double y = ldexp(round_e4m3(ldexp(oracle_bf16_to_f64(qh[d]), s)), -s);
+                float f = (float)y;
+                uint32_t u;
+                if ((double)f != y) return -2;
+                memcpy(&u, &f, sizeof u);
+                if (u & 0xFFFFu) return -2;
+                oh[d] = (uint16_t)(u >> 16);
+            }
+        }
+    return 0;
 }
 
 int oracle_dequant_rows(int fmt, int qk_dim, const uint8_t* kv, const uint8_t* scales,

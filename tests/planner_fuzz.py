@@ -28,6 +28,7 @@ def main(path: str, seed: int, calls: int) -> None:
     lib.mla_decode_plan.argtypes = [P, I, P, P, I, SP]
     lib.mla_decode_run.argtypes = [P, P, P, P, ctypes.c_int64, P, P, P, P, P, ctypes.c_size_t, P]
     lib.mla_decode_run_noalloc.argtypes = [P, P, P, P, ctypes.c_int64, P, P, P, P, P]
+    lib.mla_decode_set_query_format.argtypes = [P, I]
     lib.mla_decode_destroy.argtypes = [P]
     lib.mla_decode_last_error.argtypes = [P]
     lib.mla_decode_last_error.restype = ctypes.c_char_p
@@ -100,6 +101,9 @@ def main(path: str, seed: int, calls: int) -> None:
     assert lib.mla_decode_run(h, 16, 16, 16, 0, 16, 16, 16, 16, None, 0, None) == 3
     assert lib.mla_decode_run_noalloc(h, 16, 16, 16, 0, 16, 16, 16, 16, None) == 3
     assert lib.mla_decode_last_error(h)
+    for fmt_q, want in ((1, 0), (0, 0), (2, 1), (-5, 1)):
+        assert lib.mla_decode_set_query_format(h, fmt_q) == want
+    assert lib.mla_decode_set_query_format(None, 1) == 1
     assert lib.mla_decode_destroy(h) == 0
     assert lib.mla_decode_destroy(None) == 0
     for args in ((0, 8, 576, 512, 1.0, 1, 1), (0, 16, 576, 512, -1.0, 1, 1), (0, 16, 576, 512, 1.0, 1, 3),

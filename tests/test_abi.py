@@ -63,6 +63,32 @@ def test_create_validates_arguments(B):
     B.mla_decode_destroy(None)
 
 
+def test_query_format_setting(B):
+    """The query format: exact by default, one e4m3 code on request for fp8
+    and MXFP4 caches; refused for bf16 caches and for unknown values (no GPU)."""
+    for fmt in ("fp8", "mxfp4"):
+        h = B.mla_decode_create(0, fmt)
+        try:
+            B.mla_decode_set_query_format(h, "e4m3")
+            B.mla_decode_set_query_format(h, "exact")
+            for bad in (2, -1, 7):
+                assert B._lib.mla_decode_set_query_format(h, bad) == 1
+                assert b"query_format" in B._lib.mla_decode_last_error(h)
+        finally:
+            B.mla_decode_destroy(h)
+    h = B.mla_decode_create(0, "bf16")
+    try:
+        B.mla_decode_set_query_format(h, "exact")
+        with pytest.raises(B.MlaError) as e:
+            B.mla_decode_set_query_format(h, "e4m3")
+        assert e.value.status == 2
+    finally:
+        B.mla_decode_destroy(h)
+    assert B._lib.mla_decode_set_query_format(None, 0) == 1
+    with pytest.raises(ValueError):
+        B.mla_decode_set_query_format(None, "fp4")
+
+
 def test_plan_and_run_validate_before_any_gpu_call(B):
     h = B.mla_decode_create(0, "fp8", page_size=2)
     try:

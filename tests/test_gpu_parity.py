@@ -4,6 +4,7 @@ Tolerances (fixed here, from the task): bf16 cache -> max |gpu - oracle| <= 1e-2
 fp8 / MXFP4 cache -> |gpu - oracle| <= 0.1 + 0.1 |oracle| for every element.
 """
 
+import dataclasses
 import sys
 
 import numpy as np
@@ -29,10 +30,12 @@ def note(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def run_gpu(B, case, split_override=0, repeats=1):
+def run_gpu(B, case, split_override=0, repeats=1, query_format=None):
     t = B.case_to_device(case)
     dec = B.MlaDecode(case.kv_dtype, case.page_size)
     try:
+        if query_format is not None:
+            dec.set_query_format(query_format)
         dec.plan(case.kv_indptr, case.kv_last_page_len, split_override, case.qo_indptr)
         outs = []
         for _ in range(repeats):
@@ -701,3 +704,35 @@ def test_full_size_configs(B, oracle_mod, name):
     got = run_gpu(B, case)
     ref = oracle_out(oracle_mod, case)
     check_close(got, ref, case.kv_dtype, name)
+
+
+@pytest.mark.parametrize("fmt,lens,ps,split,q_lens", [
+    ("fp8", [8192, 3000, 129, 0], 1, 0, None),
+    ("fp8", [5000, 700, 1], 2, 1, None),
+    ("fp8", [3000, 17, 800], 1, 0, [2, 1, 2]),     # paired query rows
+    ("fp8", [2000, 900], 4, 0, [3, 4]),            # single rows of a multi-token plan
+    ("mxfp4", [8192, 3000, 129, 0], 1, 0, None),
+    ("mxfp4", [2000, 300, 33], 16, 1, None),
+    ("mxfp4", [3000, 17, 800], 2, 0, [2, 1, 2]),
+])
+def test_query_e4m3(B, oracle_mod, fmt, lens, ps, split, q_lens):
+    """MLA_QUERY_E4M3: the decode of the query rounded to one e4m3 code per
+    element (oracle_round_query_e4m3), to the usual tolerance; the distance to
+    the exact decode is printed."""
+    case = synth.make_case(fmt, lens, seed=97, page_size=ps, shuffle_pages=ps > 1, q_lens=q_lens)
+    rounded = dataclasses.replace(case, q_bits=oracle_mod.round_query_e4m3(case.q_bits))
+    got = run_gpu(B, case, split, query_format="e4m3")
+    check_close(got, oracle_out(oracle_mod, rounded), fmt, f"query e4m3 {fmt} split {split}")
+    exact = oracle_out(oracle_mod, case)
+    note(f"query e4m3 {fmt}: max|gpu - exact decode| = {np.nanmax(np.abs(got - exact)):.3e}")
+
+
+def test_query_e4m3_refused_for_odd_scale_addresses(B, oracle_mod):
+    """The bf16-decoding MXFP4 kernel (odd scale stride) has no single-code
+    query: such a run is refused before any launch, and the exact query still
+    runs."""
+    case = synth.make_case("mxfp4", [300, 20], seed=98, scale_stride=19)
+    with pytest.raises(B.MlaError) as e:
+        run_gpu(B, case, query_format="e4m3")
+    assert e.value.status == 2
+    check_close(run_gpu(B, case, query_format="exact"), oracle_out(oracle_mod, case), "mxfp4", "stride 19 exact")

@@ -375,3 +375,106 @@ def test_planted_mistakes_are_caught(oracle_mod, tmp_path):
         mutant.write_text(src.replace(old, new))
         lib = oracle_mod.OracleLib(obuild.build(src=str(mutant), lib=str(mutant) + ".so"))
         assert not _pins_pass(lib), f"planted mistake not caught: {name}"
+
+
+# ---------------------------------------------------------------------------
+# the low-precision query (one e4m3 code per element)
+# ---------------------------------------------------------------------------
+
+def _bits_to_f64(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).double()
+
+
+def _torch_round_query_e4m3(q_bits):
+    """Written here independently: torch's float8_e4m3fn cast (nearest, ties
+    to even) of q * 2^s, s = 8 - frexp exponent of each (row, head) maximum."""
+    q = _bits_to_f64(q_bits)
+    amax = q.abs().amax(dim=-1, keepdim=True)
+    _, ex = torch.frexp(amax)
+    s = torch.where(amax > 0, 8 - ex, torch.zeros_like(ex))
+    x = torch.ldexp(q, s.double())
+    assert float(x.abs().max()) < 256.0
+    y = torch.ldexp(x.to(torch.float8_e4m3fn).double(), -s.double())
+    return y.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _query_cases():
+    """bf16 queries whose heads span 2^-20 .. 2^20, with elements down in
+    e4m3's subnormal range after scaling, and exact ties."""
+    rng = np.random.default_rng(21)
+    q = rng.standard_normal((5, 16, 576)) * np.exp2(rng.integers(-20, 21, size=(5, 16, 1)))
+    q[:, :, 100:140] *= np.exp2(-np.arange(40, dtype=np.float64) / 2.0)  # 2^-1 .. 2^-20 of the head's scale
+    q[1, 3] = 0.0  # a zero head
+    # ties: a head with max 128 (scale 2^0) and elements halfway between e4m3 values
+    q[2, 5] = 0.0
+    q[2, 5, 0] = 128.0
+    q[2, 5, 1:7] = [1.0625, 1.1875, -1.0625, -1.1875, 3.0 / 1024.0, 5.0 / 1024.0]
+    t = torch.from_numpy(q).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def test_query_rounding_matches_torch_cast(oracle_mod):
+    q = _query_cases()
+    got = oracle_mod.round_query_e4m3(q)
+    assert np.array_equal(got, _torch_round_query_e4m3(q))
+
+
+def test_query_rounding_closed_forms(oracle_mod):
+    q = _query_cases()
+    got = _bits_to_f64(oracle_mod.round_query_e4m3(q)).numpy()
+    # ties to the even code: 1.0625 -> 1.0, 1.1875 -> 1.25; below 2^-6 the step is 2^-9
+    assert list(got[2, 5, :7]) == [128.0, 1.0, 1.25, -1.0, -1.25, 2.0 / 512.0, 2.0 / 512.0]
+    assert np.all(got[1, 3] == 0.0)  # a zero head stays zero
+    # values already on the e4m3 grid of their head stay (rounding twice is rounding once)
+    qf = _bits_to_f64(q).numpy()
+    again = _bits_to_f64(oracle_mod.round_query_e4m3(oracle_mod.round_query_e4m3(q))).numpy()
+    assert np.array_equal(again, got)
+    # each nonzero head's largest |q| lands in [128, 256) under its scale, its rounding in [128, 256]
+    amax_q = np.abs(qf).max(axis=-1)
+    live = amax_q > 0
+    s = 8 - np.frexp(amax_q[live])[1]
+    assert np.all((np.ldexp(amax_q[live], s) >= 128) & (np.ldexp(amax_q[live], s) < 256))
+    top = np.ldexp(np.abs(got).max(axis=-1)[live], s)
+    assert np.all((top >= 128) & (top <= 256))
+    # at most 2^-4 relative error above the subnormal range, 2^-10 of the head's maximum below
+    amax = np.abs(qf).max(axis=-1, keepdims=True)
+    err = np.abs(got - qf)
+    assert np.all(err <= np.maximum(np.abs(qf) / 16.0, amax * 2.0 ** -17) + 0.0)
+    # scaling a head by 2^k scales the result by 2^k
+    q2 = torch.from_numpy(qf * 2.0 ** 7).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got2 = _bits_to_f64(oracle_mod.round_query_e4m3(q2)).numpy()
+    assert np.array_equal(got2, got * 2.0 ** 7)
+
+
+QUERY_MUTANTS = {
+    "ties away from zero": ("r = nearbyint(ldexp(a, 3 - e));", "r = round(ldexp(a, 3 - e));"),
+    "truncated": ("r = nearbyint(ldexp(a, 3 - e));", "r = trunc(ldexp(a, 3 - e));"),
+    "scale off by one": ("s = 8 - e;", "s = 7 - e;"),
+    "no subnormal steps": ("if (e < -6) e = -6;", "if (e < -60) e = -60;"),
+    "one scale per row": ("for (d = 0; d < qk_dim; ++d) {\n                double v = fabs(oracle_bf16_to_f64(qh[d]));",
+                          "for (d = 0; d < qk_dim * nh; ++d) {\n                double v = fabs(oracle_bf16_to_f64(q[r * nh * qk_dim + d]));"),
+}
+
+
+def _query_pins_pass(lib) -> bool:
+    q = _query_cases()
+    try:
+        got = lib.round_query_e4m3(q)
+    except ValueError:
+        return False
+    if not np.array_equal(got, _torch_round_query_e4m3(q)):
+        return False
+    f = _bits_to_f64(got).numpy()
+    return list(f[2, 5, :7]) == [128.0, 1.0, 1.25, -1.0, -1.25, 2.0 / 512.0, 2.0 / 512.0]
+
+
+def test_query_rounding_planted_mistakes_are_caught(oracle_mod, tmp_path):
+    from oracle import build as obuild
+    src = open(obuild.SRC).read()
+    assert _query_pins_pass(oracle_mod.default())
+    for name, (old, new) in QUERY_MUTANTS.items():
+        assert src.count(old) == 1, name
+        mutant = tmp_path / (name.replace(" ", "_") + ".c")
+        mutant.write_text(src.replace(old, new))
+        lib = oracle_mod.OracleLib(obuild.build(src=str(mutant), lib=str(mutant) + ".so"))
+        assert not _query_pins_pass(lib), f"planted mistake not caught: {name}"
