@@ -1,7 +1,7 @@
 """Benchmark: single-token MLA decode on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--targets A,B|none]
-                    [--cold-calls N] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--warmup-ms T] [--workload NAME]
+                    [--targets A,B|none] [--cold-calls N] [--no-cpu-baseline]
 
 A step is one decode call (the split kernel, plus the LSE merge kernel when
 the plan needs one) over one batch of seeded synthetic inputs already
@@ -11,12 +11,17 @@ tokens (uniform draw) in an fp8 cache of 2-token pages, shuffled.  Every
 timed step is cold: the steps cycle through copies of the inputs totalling
 at least 1 GiB, so no step finds its KV in the 256 MB last-level (MALL)
 cache.  The `steps` calls run back to back between two events; ms_per_step =
-elapsed / steps and value = algorithmic KV bytes / ms_per_step.
+elapsed / steps and value = algorithmic KV bytes / ms_per_step.  Before them,
+untimed, at least W calls and then back-to-back calls until T ms (default 60)
+have run: after an idle spell the chip holds a lower core clock through the
+first ~25 ms of sustained load, and the timed calls are meant to see the clock
+it sustains.  "warmup" in the line is the number of warm-up calls made.
 
 Beside that: cold_single_us, the median and the mean without the fastest and
 slowest of calls timed one at a time (events around each call, the GPU idle
 before it); us_per_call_warm, back-to-back calls on one copy of the inputs;
-plan.replan_us, the host time of re-planning the live handle between runs;
+plan.replan_us, the host time of re-planning the live handle between runs
+(plan.replan_loop_us: the same in a plan/run loop that runs ahead of the GPU);
 and, under "targets", the same record for 32 and 64 sequences of 8192 tokens
 in an fp8 cache (the target shapes).
 
@@ -158,9 +163,30 @@ def measure(name, args, dev, torch, binding, synth, full=True):
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
 
-    for i in range(max(args.warmup, n_copies)):
-        run(i)
-    torch.cuda.synchronize()
+    # Untimed warm-up: at least `warmup` calls and one pass over the copies,
+    # then back-to-back calls until `warmup_ms` of them have run.  After an
+    # idle spell the chip runs the first ~25 ms of back-to-back calls at a
+    # lower core clock (1.5-2.0 GHz, against the 2.2-2.4 GHz it then
+    # sustains), so the timed region starts once that has passed.
+    # The first chunk also pays one-time costs (first launches), so the
+    # sustained time is counted from the second chunk on.
+    n_warm = 0
+    chunk = max(args.warmup, n_copies)
+    sustained_ms = -1.0
+    while True:
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(chunk):
+            run(n_warm + i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        dt = ev0.elapsed_time(ev1)
+        n_warm += chunk
+        sustained_ms = 0.0 if sustained_ms < 0 else sustained_ms + dt
+        if sustained_ms >= args.warmup_ms:
+            break
+        per_call_ms = max(dt / chunk, 1e-3)
+        chunk = max(8, int(np.ceil((args.warmup_ms - sustained_ms) / per_call_ms)))
 
     # Timed region: exactly `steps` calls back to back, each on the next copy.
     print(f"[bench] {name}: timing {args.steps} cold steps over {n_copies} input copies",
@@ -210,14 +236,25 @@ def measure(name, args, dev, torch, binding, synth, full=True):
     warm_us = ev0.elapsed_time(ev1) / args.warm_iters * 1e3
 
     # Re-planning the live handle for the same batch, as a decode loop does
-    # each step (lengths change by one token), interleaved with runs in
-    # flight: host time of each plan call.
-    replan = []
+    # each step (lengths change by one token): the host time of a plan call
+    # with the GPU idle (the planner and the enqueued upload), and in a loop of
+    # plan, run, plan, run, ... with runs in flight, where a plan also waits for
+    # the run two plans back, whose plan buffer it reuses, whenever the host
+    # is that far ahead of the GPU.
+    replan, replan_loop = [], []
     t = copies[0]
     for i in range(20):
+        torch.cuda.synchronize()
         t0 = time.perf_counter()
         dec.plan(case.kv_indptr, case.kv_last_page_len, args.split, case.qo_indptr)
         replan.append((time.perf_counter() - t0) * 1e6)
+        dec.run(t["q"], t["kv"], t["kv_scales"], t["kv_indptr"], out, t["kv_page_indices"],
+                t["kv_last_page_len"])
+    torch.cuda.synchronize()
+    for i in range(20):
+        t0 = time.perf_counter()
+        dec.plan(case.kv_indptr, case.kv_last_page_len, args.split, case.qo_indptr)
+        replan_loop.append((time.perf_counter() - t0) * 1e6)
         dec.run(t["q"], t["kv"], t["kv_scales"], t["kv_indptr"], out, t["kv_page_indices"],
                 t["kv_last_page_len"])
     torch.cuda.synchronize()
@@ -243,7 +280,8 @@ def measure(name, args, dev, torch, binding, synth, full=True):
                      "traffic": traffic_record(name, kv_dtype) if args.query_format == "exact" else None},
         "plan": {"items": n_items, "max_splits": max_splits, "partials": n_partials,
                  "workspace_bytes": int(ws_bytes), "plan_us": round(plan_us, 1),
-                 "replan_us": round(float(np.median(replan)), 1)},
+                 "replan_us": round(float(np.median(replan)), 1),
+                 "replan_loop_us": round(float(np.median(replan_loop)), 1)},
     }
     if full:
         rec["config"] = {"workload": name, "kv_dtype": kv_dtype, "batch": int(case.batch),
@@ -257,6 +295,7 @@ def measure(name, args, dev, torch, binding, synth, full=True):
         rec["kv_dtype"] = kv_dtype
     else:
         rec["algorithmic_kv_bytes"] = int(alg_bytes)
+    rec["warmup_calls"] = n_warm
     del calls
     dec.close()
     del copies, base
@@ -267,8 +306,10 @@ def measure(name, args, dev, torch, binding, synth, full=True):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup-ms", type=float, default=60.0,
+                    help="after the `warmup` calls, keep calling back to back until this much GPU time has run")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--targets", default=",".join(TARGETS),
                     help="comma-separated workloads measured in the same run and reported under "
@@ -318,7 +359,7 @@ def main():
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": rec.pop("warmup_calls"),
         "ms_per_step": round(mean_ms, 5),
         "us_per_call": rec["us_per_call"],
         "input_copies": rec["input_copies"],

@@ -177,6 +177,16 @@ __device__ __forceinline__ void fp4x8_to_fp8_lut(uint32_t w, uint32_t lut_lo, ui
   od = (w & 0x80808080u) | __builtin_amdgcn_perm(lut_hi, lut_lo, (w >> 4) & 0x07070707u);
 }
 // Table words for 2^-k: 8k off every byte but that of magnitude 0.
+// The thread's index, hidden from the optimiser at the point of the call, so
+// that values derived from it are computed there instead of being hoisted out
+// of the item and tile loops and kept live (or spilled) across them.
+__device__ __forceinline__ int opaque_tid() {
+  int t = (int)threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+__device__ __forceinline__ int opaque_lane() { return opaque_tid() & 63; }
+
 __device__ __forceinline__ void fp4_lut(uint32_t k, uint32_t& lut_lo, uint32_t& lut_hi) {
   const uint32_t k8 = k << 3;
   const uint32_t rep = __builtin_amdgcn_perm(0u, k8, 0u);  // k8 in every byte
@@ -188,7 +198,7 @@ __device__ __forceinline__ void fp4_lut(uint32_t k, uint32_t& lut_lo, uint32_t& 
 // enters the scores as one e4m3 code per element (hi alone), not as hi + lo.
 template <bool PAGED, bool Q1>
 __device__ __forceinline__ void mxfp4_item(const Stage1Args& a, const WorkItem& item, Fp4Lds& sh) {
-  const int tid = threadIdx.x;
+  const int tid = opaque_tid();
   if (item.slot == WorkItem::kEmpty) {  // empty sequence: its output is zero
     uint4* dst = reinterpret_cast<uint4*>(a.out + (int64_t)item.batch * kNumHeads * kVDim);
 #pragma unroll
@@ -512,9 +522,10 @@ __device__ __forceinline__ void mxfp4_item(const Stage1Args& a, const WorkItem& 
       }
     }
     const float l_w = xor_sum_groups(l_s);
-    if (g == 0) {
-      fin_l[r16][s] = l_w;
-      fin_ls[r16][s] = m_s;
+    const int lane_f = opaque_lane();
+    if (lane_f < 16) {
+      fin_l[lane_f][s] = l_w;
+      fin_ls[lane_f][s] = m_s;
     }
   } else {
     const int c = wave - 4;
@@ -686,21 +697,27 @@ __device__ __forceinline__ void mxfp4_item(const Stage1Args& a, const WorkItem& 
     // so lane group g has output columns 8(g >> 1) + 2i + (g & 1) of each
     // column tile; lanes l and l ^ 16 trade two values each to return to
     // columns 4g + i.  Then the output goes to raw slot 0 for all waves.
-    const int partner = (lane ^ 16) << 2;
-    const bool odd = (g & 1) != 0;
+    const int lane_h = opaque_lane();
+    const int partner = (lane_h ^ 16) << 2;
+    const bool odd = ((lane_h >> 4) & 1) != 0;
 #pragma unroll
     for (int v = 0; v < 8; ++v) {
       const float r0 = __int_as_float(__builtin_amdgcn_ds_bpermute(partner, __float_as_int(odd ? o[v][0] : o[v][2])));
       const float r1 = __int_as_float(__builtin_amdgcn_ds_bpermute(partner, __float_as_int(odd ? o[v][1] : o[v][3])));
-      hand[(8 * c + v) * 64 + lane] = odd ? f32x4{r0, o[v][2], r1, o[v][3]} : f32x4{o[v][0], r0, o[v][1], r1};
+      hand[(8 * c + v) * 64 + lane_h] = odd ? f32x4{r0, o[v][2], r1, o[v][3]} : f32x4{o[v][0], r0, o[v][1], r1};
     }
-    if (c == 0 && g == 0) fin_m[r16] = m_ref;
+    if (c == 0 && lane_h < 16) fin_m[lane_h] = m_ref;
   }
   lds_barrier();  // the output, the weight sums and the references
 
-  const float m_ref = fin_m[r16];
-  const f32x4 lv = *reinterpret_cast<const f32x4*>(&fin_l[r16][0]);
-  const f32x4 mv = *reinterpret_cast<const f32x4*>(&fin_ls[r16][0]);
+  // Lane values for the epilogue are derived afresh here, so that none of
+  // them stays live (or spilled) through the tile loop.
+  const int tid_e = opaque_tid();
+  const int lane_e = tid_e & 63, r16_e = lane_e & 15;
+
+  const float m_ref = fin_m[r16_e];
+  const f32x4 lv = *reinterpret_cast<const f32x4*>(&fin_l[r16_e][0]);
+  const f32x4 mv = *reinterpret_cast<const f32x4*>(&fin_ls[r16_e][0]);
   float L = 0.f;
 #pragma unroll
   for (int k = 0; k < 4; ++k)
@@ -709,8 +726,8 @@ __device__ __forceinline__ void mxfp4_item(const Stage1Args& a, const WorkItem& 
   const int W = wave >> 1, vb = 4 * (wave & 1);
   f32x4 ow[4];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) ow[v] = hand[(8 * W + vb + v) * 64 + lane];
-  finish_item<4>(a, item, tid, W, vb, lane, ow, 1.0f / L, m_ref + __log2f(L));
+  for (int v = 0; v < 4; ++v) ow[v] = hand[(8 * W + vb + v) * 64 + lane_e];
+  finish_item<4>(a, item, tid_e, W, vb, lane_e, ow, 1.0f / L, m_ref + __log2f(L));
 }
 
 // A workgroup runs one item, or with bins the items of bin blockIdx.x in
