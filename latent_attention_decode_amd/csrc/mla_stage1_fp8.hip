@@ -205,9 +205,12 @@ __device__ __forceinline__ void fp8_item(const Stage1Args& a, const WorkItem* it
     const uint32_t pm0 = lds_u32(&sh.pages[0]);
     for (int j = wave; 64 * j < npages; j += kWaves)
       dma_u32(psrc + min(64 * j + lane, npages - 1), pm0 + 256 * j);
-    wait_loads<0>();
-    lds_barrier();
   }
+  // The query (and the page ids) land before tile 0 is issued: issued
+  // together with the first tile of every CU, the query rows would queue
+  // behind those 19 MB at the memory and land last.
+  wait_loads<0>();
+  lds_barrier();
 
   // This lane's slot in each of its wave's 18 loads of a tile: (tile row << 8)
   // | chunk.  Load j = 4q + e of a group goes to LDS m0_q + 1024 e.
@@ -261,8 +264,6 @@ __device__ __forceinline__ void fp8_item(const Stage1Args& a, const WorkItem* it
   };
 
   issue(0, -1);
-  wait_loads<kCLoadsPerWave>();  // this wave's query loads have landed
-  lds_barrier();                 // ... and everyone's
 
   // Query rows, B operands of S^T = K Q^T, scaled by 2^s and split into
   // e4m3 hi + lo: for 128-column block K (0..3) lane (head r16, group g)
