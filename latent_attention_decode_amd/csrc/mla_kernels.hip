@@ -405,9 +405,12 @@ __device__ __forceinline__ void stage1_item(const Stage1Args& a, const WorkItem&
       const int32_t* psrc = a.page_indices + seq_base + page0;
       const uint32_t pm0 = lds_u32(&sh.pages[0]);
       for (int j = wave; 64 * j < npages; j += kWaves) dma_u32(psrc + min(64 * j + lane, npages - 1), pm0 + 256 * j);
-      wait_loads<0>();
-      lds_barrier();
     }
+    // The query (and the page ids) land before the first tiles are issued:
+    // issued together with the first tiles of every CU, the query would
+    // queue behind them at the memory and land last.
+    wait_loads<0>();
+    if constexpr (PAGED) lds_barrier();
     auto issue = [&](int n) {  // tile n into buffer n % 2
       const int tok0 = item.tok_begin + n * kTileTokens;
       const int lim = tok_last - tok0;

@@ -176,7 +176,6 @@ __device__ __forceinline__ void fp4x8_to_fp8_lut(uint32_t w, uint32_t lut_lo, ui
   ev = ((w << 4) & 0x80808080u) | __builtin_amdgcn_perm(lut_hi, lut_lo, w & 0x07070707u);
   od = (w & 0x80808080u) | __builtin_amdgcn_perm(lut_hi, lut_lo, (w >> 4) & 0x07070707u);
 }
-// Table words for 2^-k: 8k off every byte but that of magnitude 0.
 // The thread's index, hidden from the optimiser at the point of the call, so
 // that values derived from it are computed there instead of being hoisted out
 // of the item and tile loops and kept live (or spilled) across them.
@@ -187,6 +186,7 @@ __device__ __forceinline__ int opaque_tid() {
 }
 __device__ __forceinline__ int opaque_lane() { return opaque_tid() & 63; }
 
+// Table words for 2^-k: 8k off every byte but that of magnitude 0.
 __device__ __forceinline__ void fp4_lut(uint32_t k, uint32_t& lut_lo, uint32_t& lut_hi) {
   const uint32_t k8 = k << 3;
   const uint32_t rep = __builtin_amdgcn_perm(0u, k8, 0u);  // k8 in every byte
@@ -238,9 +238,12 @@ __device__ __forceinline__ void mxfp4_item(const Stage1Args& a, const WorkItem& 
     const uint32_t pm0 = lds_u32(&sh.pages[0]);
     for (int j = wave; 64 * j < npages; j += kXWaves)
       dma_u32(psrc + min(64 * j + lane, npages - 1), pm0 + 256 * j);
-    wait_loads<0>();
-    lds_barrier();
   }
+  // The query (and the page ids) land before the first tiles are issued:
+  // issued together with the first tiles of every CU, the query would queue
+  // behind them at the memory and land last.
+  wait_loads<0>();
+  lds_barrier();
 
   auto row_of = [&](int tok) -> int64_t {  // cache row of logical token tok
     if constexpr (PAGED) {
@@ -308,14 +311,7 @@ __device__ __forceinline__ void mxfp4_item(const Stage1Args& a, const WorkItem& 
   if (scorer) {
     issue(0);
     if (ntiles > 1) issue(1);
-    if (ntiles > 1)
-      wait_loads<2 * kXLoadsPerWave>();  // the query has landed
-    else
-      wait_loads<kXLoadsPerWave>();
-  } else {
-    wait_loads<0>();
   }
-  lds_barrier();
 
   // Query, B operand of the scores, scaled by 2^s and split into e4m3 hi +
   // lo.  K-step K (0..3): bytes b < 16 column 128K + 16g + b, bytes 16..31
