@@ -251,38 +251,51 @@ struct Piece {
   int64_t t0, t1;
 };
 
+// x rounded toward zero to a multiple of the power of two `tile` (what
+// x / tile * tile gives, without the division).
+static_assert((kPlanTile & (kPlanTile - 1)) == 0 && kPlanTile >= 2, "planner tiles are powers of two");
+static inline int64_t trunc_tile(int64_t x, int64_t tile) {
+  return x >= 0 ? (x & ~(tile - 1)) : -((-x) & ~(tile - 1));
+}
+
 // Greedy fill of bins of cost capacity C in stream order; returns the number
-// of bins and the largest number of pieces of one sequence.
+// of bins and the largest number of pieces of one sequence.  With `pieces`,
+// the pieces in bin order and, in `starts`, each bin's first piece (one more
+// entry than there are bins).
 static int64_t fill_bins(const std::vector<int64_t>& lens, const std::vector<int32_t>& order, int64_t C,
-                         int64_t tile, int64_t max_item, int64_t kPieceCost, std::vector<std::vector<Piece>>* out,
-                         int64_t* max_pieces) {
+                         int64_t tile, int64_t max_item, int64_t kPieceCost, std::vector<Piece>* pieces,
+                         std::vector<int32_t>* starts, int64_t* max_pieces) {
   int64_t bins = 1, r = C, most = 0;
-  if (out) out->assign(1, {});
+  if (pieces) {
+    pieces->clear();
+    starts->assign(1, 0);
+  }
   for (int32_t b : order) {
     const int64_t n = lens[b];
-    int64_t pos = 0, pieces = 0;
+    int64_t pos = 0, count = 0;
     while (pos < n) {
       const int64_t rest = n - pos;
       int64_t take;
       if (rest <= max_item && rest + kPieceCost <= r) {
         take = rest;
       } else {
-        take = std::min((r - kPieceCost) / tile * tile, max_item);
-        if (rest - take < kMinPiece) take = (rest - kMinPiece) / tile * tile;
+        take = std::min(trunc_tile(r - kPieceCost, tile), max_item);
+        if (rest - take < kMinPiece) take = trunc_tile(rest - kMinPiece, tile);
         if (take < kMinPiece) {  // the bin is full
           ++bins;
           r = C;
-          if (out) out->emplace_back();
+          if (pieces) starts->push_back(static_cast<int32_t>(pieces->size()));
           continue;
         }
       }
-      if (out) out->back().push_back(Piece{b, pos, pos + take});
+      if (pieces) pieces->push_back(Piece{b, pos, pos + take});
       pos += take;
       r -= take + kPieceCost;
-      ++pieces;
+      ++count;
     }
-    most = std::max(most, pieces);
+    most = std::max(most, count);
   }
+  if (pieces) starts->push_back(static_cast<int32_t>(pieces->size()));
   if (max_pieces) *max_pieces = most;
   return bins;
 }
@@ -303,25 +316,40 @@ static bool plan_bins(const std::vector<int64_t>& lens, const int32_t* indptr, i
   }
   const int64_t c_min = kPieceCost + 2 * kMinPiece;
   if (equal || slots < 1 || (total + slots - 1) / slots < c_min || max_item < 2 * kMinPiece) return false;
+  // longest first, ties in sequence order (the order of a stable sort)
   std::vector<int32_t> order;
+  order.reserve(batch);
   for (int b = 0; b < batch; ++b)
     if (lens[b]) order.push_back(b);
-  std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) { return lens[x] > lens[y]; });
+  std::sort(order.begin(), order.end(),
+            [&](int32_t x, int32_t y) { return lens[x] > lens[y] || (lens[x] == lens[y] && x < y); });
 
   // the least capacity that fits the batch into `slots` bins, no sequence in
   // more than max_splits pieces (the fill is monotone in C)
   auto fits = [&](int64_t C) {
     int64_t most = 0;
-    return fill_bins(lens, order, C, tile, max_item, kPieceCost, nullptr, &most) <= slots && most <= max_splits;
+    return fill_bins(lens, order, C, tile, max_item, kPieceCost, nullptr, nullptr, &most) <= slots &&
+           most <= max_splits;
   };
-  int64_t lo = std::max((total + slots - 1) / slots, c_min);
-  int64_t hi = lo;
+  // every sequence has at least one piece, each costing kPieceCost beyond
+  // its tokens, so no capacity below lo fits
+  const int64_t nonempty = static_cast<int64_t>(order.size());
+  int64_t lo = std::max((total + kPieceCost * nonempty + slots - 1) / slots, c_min);
   // one bin holds the whole batch beyond this capacity; if that still
   // splits a sequence too often (page staging), bins do not apply
   const int64_t one_bin = total + kPieceCost * (batch + total / kMinPiece + 2) + c_min;
-  while (!fits(hi)) {
-    if (hi > one_bin) return false;
-    hi *= 2;
+  // the answer is usually within a quarter above lo: try that first
+  int64_t hi = lo + lo / 4;
+  if (fits(hi)) {
+    // search [lo, hi]
+  } else {
+    lo = hi + 1;
+    hi = 2 * hi;
+    while (!fits(hi)) {
+      if (hi > one_bin) return false;
+      lo = hi + 1;
+      hi *= 2;
+    }
   }
   while (lo < hi) {
     const int64_t mid = lo + (hi - lo) / 2;
@@ -330,14 +358,15 @@ static bool plan_bins(const std::vector<int64_t>& lens, const int32_t* indptr, i
     else
       lo = mid + 1;
   }
-  std::vector<std::vector<Piece>> bins;
-  fill_bins(lens, order, lo, tile, max_item, kPieceCost, &bins, nullptr);
-  while (!bins.empty() && bins.back().empty()) bins.pop_back();
+  std::vector<Piece> pieces;
+  std::vector<int32_t> starts;
+  fill_bins(lens, order, lo, tile, max_item, kPieceCost, &pieces, &starts, nullptr);
+  size_t nb = starts.size() - 1;  // bins, the last ones possibly empty
+  while (nb > 0 && starts[nb - 1] == starts[nb]) --nb;
 
   // slots: the pieces of a sequence, in stream order
   std::vector<int32_t> npieces(batch, 0), first_slot(batch, 0), job(batch, -1), seen(batch, 0);
-  for (const auto& bin : bins)
-    for (const Piece& p : bin) ++npieces[p.batch];
+  for (const Piece& p : pieces) ++npieces[p.batch];
   out->items.clear();
   out->merge.clear();
   out->bins.clear();
@@ -355,11 +384,14 @@ static bool plan_bins(const std::vector<int64_t>& lens, const int32_t* indptr, i
   std::vector<int32_t> empties;
   for (int b = 0; b < batch; ++b)
     if (!lens[b]) empties.push_back(b);
-  const size_t nbins = std::max<size_t>(bins.size(), 1);
+  const size_t nbins = std::max<size_t>(nb, 1);
+  out->items.reserve(pieces.size() + empties.size());
+  out->bins.reserve(nbins + 1);
   for (size_t k = 0; k < nbins; ++k) {
     out->bins.push_back(static_cast<int32_t>(out->items.size()));
-    if (k < bins.size())
-      for (const Piece& p : bins[k]) {
+    if (k < nb)
+      for (int32_t i = starts[k]; i < starts[k + 1]; ++i) {
+        const Piece& p = pieces[i];
         const int b = p.batch;
         const bool whole = npieces[b] == 1;
         out->items.push_back(WorkItem{b, static_cast<int32_t>(p.t0), static_cast<int32_t>(p.t1),
