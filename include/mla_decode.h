@@ -289,9 +289,11 @@ mla_status mla_decode_set_profiling(mla_decode_t h, int enable);
 mla_status mla_decode_kernel_time_ms(mla_decode_t h, int which, float* ms);
 
 /*
- * Static resource usage of kernel `which` (0 = split stage for this handle's
- * format and layout, 1 = merge): registers per lane, LDS bytes per
- * workgroup, scratch (spill) bytes per lane.  Any output pointer may be NULL.
+ * Static resource usage of kernel `which` (0 = the split-stage kernel that
+ * mla_decode_run launches for this handle's format, layout, query format and
+ * current plan, for an MXFP4 scale array at even addresses; 1 = merge):
+ * registers per lane, LDS bytes per workgroup, scratch (spill) bytes per
+ * lane.  Any output pointer may be NULL.
  */
 mla_status mla_decode_kernel_resources(mla_decode_t h, int which, int* vgprs, int* lds_bytes,
                                        int* scratch_bytes);

@@ -1062,7 +1062,8 @@ mla_status mla_decode_kernel_resources(mla_decode_t h, int which, int* vgprs, in
   DeviceGuard guard(h->device);
   if (!guard.ok) return fail(h, MLA_ERR_HIP, "cannot select HIP device %d", h->device);
   hipFuncAttributes attr{};
-  if (mla::kernel_attributes(h->kv_dtype, h->page_size > 1, which, &attr) != hipSuccess)
+  if (mla::kernel_attributes(h->kv_dtype, h->page_size > 1, h->planned && h->row_pairs,
+                            h->query_format == MLA_QUERY_E4M3, which, &attr) != hipSuccess)
     return fail(h, MLA_ERR_HIP, "hipFuncGetAttributes failed");
   if (vgprs) *vgprs = attr.numRegs;
   if (lds_bytes) *lds_bytes = static_cast<int>(attr.sharedSizeBytes);

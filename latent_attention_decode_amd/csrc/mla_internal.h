@@ -175,8 +175,11 @@ hipError_t launch_merge(const MergeArgs& a, int num_merge_seqs, hipStream_t s,
 // Workgroups per merge job (column parts): 4 for 32 jobs or more, up to 32
 // for fewer, so that a small batch's merge still spreads over many CUs.
 int merge_parts(int num_merge_seqs);
-// Static resources of a kernel (which: 0 stage 1 for `fmt`/`paged`, 1 merge).
-hipError_t kernel_attributes(int fmt, bool paged, int which, hipFuncAttributes* attr);
+// Static resources of a kernel (which: 0 the stage-1 kernel launch_stage1
+// picks for `fmt`, `paged`, `row_pairs` and `query_e4m3` with even MXFP4
+// scale addresses, 1 the merge).
+hipError_t kernel_attributes(int fmt, bool paged, bool row_pairs, bool query_e4m3, int which,
+                             hipFuncAttributes* attr);
 // Resident stage-1 workgroups per compute unit.
 hipError_t stage1_occupancy(int fmt, bool paged, int* blocks_per_cu);
 

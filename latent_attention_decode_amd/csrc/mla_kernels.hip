@@ -746,8 +746,12 @@ hipError_t launch_merge(const MergeArgs& a, int num_merge_seqs, hipStream_t s, h
   return launch(fn, dim3(num_merge_seqs * parts), dim3(kMergeThreads), params, s, start, stop);
 }
 
-hipError_t kernel_attributes(int fmt, bool paged, int which, hipFuncAttributes* attr) {
-  const void* fn = which == 0 ? pick_stage1(fmt, paged) : reinterpret_cast<const void*>(&mla_merge);
+hipError_t kernel_attributes(int fmt, bool paged, bool row_pairs, bool query_e4m3, int which,
+                             hipFuncAttributes* attr) {
+  const void* fn = which != 0        ? reinterpret_cast<const void*>(&mla_merge)
+                   : fmt == kFp8     ? stage1_fp8_kernel(paged, row_pairs, query_e4m3)
+                   : fmt == kMxfp4   ? stage1_mxfp4_kernel(paged, query_e4m3)
+                                     : pick_stage1(fmt, paged);
   if (!fn) return hipErrorInvalidValue;
   return hipFuncGetAttributes(attr, fn);
 }

@@ -736,3 +736,29 @@ def test_query_e4m3_refused_for_odd_scale_addresses(B, oracle_mod):
         run_gpu(B, case, query_format="e4m3")
     assert e.value.status == 2
     check_close(run_gpu(B, case, query_format="exact"), oracle_out(oracle_mod, case), "mxfp4", "stride 19 exact")
+
+
+@pytest.mark.parametrize("fmt,ps,qf", [
+    ("fp8", 1, "exact"), ("fp8", 2, "exact"), ("fp8", 1, "e4m3"),
+    ("mxfp4", 1, "exact"), ("mxfp4", 2, "exact"), ("mxfp4", 1, "e4m3"), ("mxfp4", 2, "e4m3"),
+    ("bf16", 1, "exact"), ("bf16", 2, "exact"),
+])
+def test_split_kernels_keep_registers_out_of_scratch(B, fmt, ps, qf):
+    """The one-row split kernels run without register spills (scratch memory
+    per lane 0): a spill of values live across the tile loop costs a round
+    trip to memory on every item (the MXFP4 kernel once lost 10 % of its time
+    to 20 such registers).  The MXFP4 kernel keeps its two waves per SIMD (at
+    most 256 registers each)."""
+    case = synth.make_case(fmt, [700, 300], seed=99, page_size=ps, shuffle_pages=ps > 1)
+    dec = B.MlaDecode(fmt, ps)
+    try:
+        if qf != "exact":
+            dec.set_query_format(qf)
+        dec.plan(case.kv_indptr, case.kv_last_page_len, 0)
+        res = B.mla_decode_kernel_resources(dec.h, 0)
+    finally:
+        dec.close()
+    note(f"{fmt} page {ps} query {qf}: {res}")
+    assert res["scratch_bytes"] == 0, res
+    if fmt == "mxfp4":
+        assert res["vgprs"] <= 256, res
