@@ -384,7 +384,7 @@ def test_extreme_shapes(B, oracle_mod, what, fmt, lens, ps):
     check_close(run_gpu(B, case), oracle_out(oracle_mod, case), fmt, what)
 
 
-def random_cases(n=120, seed=2024):
+def random_cases(n=240, seed=2024):
     """Seeded mixed cases: format, ragged and empty lengths, page size and shuffling,
     MXFP4 scale stride, split override and sometimes several query tokens per
     sequence."""
@@ -411,11 +411,16 @@ def random_cases(n=120, seed=2024):
 
 @pytest.mark.parametrize("k,fmt,lens,ps,stride,split,q_lens", random_cases(), ids=lambda v: None)
 def test_random_mixed_cases(B, oracle_mod, k, fmt, lens, ps, stride, split, q_lens):
-    note(f"random case {k}: {fmt} lens={lens} ps={ps} stride={stride} split={split} q_lens={q_lens}")
+    """Every third fp8 / MXFP4 case (even scale addresses) takes the
+    single-code query, against the decode of the rounded query."""
+    e4m3 = fmt != "bf16" and k % 3 == 0 and stride % 2 == 0
+    note(f"random case {k}: {fmt} lens={lens} ps={ps} stride={stride} split={split} q_lens={q_lens} "
+         f"query {'e4m3' if e4m3 else 'exact'}")
     case = synth.make_case(fmt, lens, seed=5000 + k, page_size=ps, shuffle_pages=ps > 1, scale_stride=stride,
                            q_lens=q_lens, guard_rows=3)
-    got = run_gpu(B, case, split)
-    check_close(got, oracle_out(oracle_mod, case), fmt, f"random case {k}")
+    got = run_gpu(B, case, split, query_format="e4m3" if e4m3 else None)
+    ref = dataclasses.replace(case, q_bits=oracle_mod.round_query_e4m3(case.q_bits)) if e4m3 else case
+    check_close(got, oracle_out(oracle_mod, ref), fmt, f"random case {k}")
 
 
 def test_empty_sequences_give_zero(B, oracle_mod):
