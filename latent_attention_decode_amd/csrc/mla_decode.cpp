@@ -214,8 +214,10 @@ static int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 // MXFP4 kernels) or 64 (bf16 kernel).  A small batch is cut down to items of
 // min_item_tokens, so that it reaches more compute units, with at most
 // kMaxAutoSplits items per sequence (the merge kernel spreads a small
-// batch's merge over up to 32 workgroups per sequence); bins keep
-// kMaxBinSplits, within the fused merge's reach.  Measured on bs4 x 8192
+// batch's merge over up to 32 workgroups per sequence); bins cut a sequence
+// into at most kMaxBinSplits items (merged inside the split kernel when there
+// are at most kFusedMergeMaxSlots and the format takes the fused merge, else
+// by the merge kernel).  Measured on bs4 x 8192
 // fp8: 256 items of one tile 15.8 us a call, 128 of two tiles 14.9; on bs4 x
 // 1024 bf16: 64 items of one 64-token tile 10.5 us, 32 of two 11.9.
 constexpr int64_t kMaxAutoSplits = 256;
