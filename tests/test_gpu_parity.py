@@ -284,6 +284,38 @@ def test_binned_ragged_batch(B, oracle_mod, kind, fmt, ps, shuffled, stride):
     assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("fmt,pairs,merge_kernel", [
+    ("fp8", False, True), ("mxfp4", False, False), ("bf16", False, False), ("fp8", True, False),
+])
+def test_where_the_merge_runs(B, oracle_mod, fmt, pairs, merge_kernel):
+    """Which kernel combines a ragged plan's partials (at most 12 per
+    sequence): the merge kernel for one-row fp8 items, the split kernel
+    itself (the item that finishes last) for MXFP4 and bf16 caches and for
+    fp8 plans of paired query rows.  The merge kernel's time from the
+    kernel-attached events is 0 exactly when it was not launched; every
+    output against the oracle."""
+    if pairs:  # at most 2 query tokens per sequence: the fp8 kernel runs rows in pairs
+        case = synth.make_case(fmt, [1500, 1100, 129, 1200, 900], seed=96, q_lens=[2, 2, 1, 2, 2])
+    else:
+        case = synth.make_case(fmt, _binned_lens("mixed"), seed=96)
+    t = B.case_to_device(case)
+    dec = B.MlaDecode(fmt)
+    try:
+        dec.plan(case.kv_indptr, None, 0, case.qo_indptr)
+        _, splits, _ = B.mla_decode_plan_info(dec.h)
+        assert 2 <= splits <= 12
+        B.mla_decode_set_profiling(dec.h, True)
+        out = torch.full((case.rows, 16, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
+        dec.run(t["q"], t["kv"], t["kv_scales"], t["kv_indptr"], out)
+        torch.cuda.synchronize()
+        assert B.mla_decode_kernel_time_ms(dec.h, 0) > 0
+        assert (B.mla_decode_kernel_time_ms(dec.h, 1) > 0) == merge_kernel
+    finally:
+        dec.close()
+    check_close(out.float().cpu().numpy().astype(np.float64), oracle_out(oracle_mod, case), fmt,
+                f"merge placement {fmt} pairs {pairs}")
+
+
 MULTI = [
     # fmt, lens, q_lens, page_size, shuffled
     ("fp8", [1, 63, 200, 1000, 5], [1, 2, 4, 3, 5], 1, False),
