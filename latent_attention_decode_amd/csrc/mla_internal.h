@@ -143,7 +143,7 @@ struct MergeArgs {
   uint16_t* out;
 };
 
-// Largest number of splits of one sequence that the fp8 kernel merges itself
+// Largest number of splits of one sequence that a split kernel merges itself
 // (the last item reads the other nslots - 1 partials in groups of four).
 constexpr int kFusedMergeMaxSlots = 12;
 
@@ -159,10 +159,11 @@ hipError_t scratch_address(int device, void** ptr);
 // query_e4m3: the variant that takes the query as one e4m3 code per element.
 const void* stage1_fp8_kernel(bool paged, bool row_pairs, bool query_e4m3 = false);
 const void* stage1_mxfp4_kernel(bool paged, bool query_e4m3 = false);
-// Whether launch_stage1 runs the split kernel of that file for these
-// arguments (it does for fp8; for MXFP4 when the scale array and its row
-// stride are 2-byte aligned, else the bf16-decoding kernel).  Only those
-// kernels can merge partials themselves (Stage1Args::counters).
+// Whether launch_stage1 runs the format's own split kernel for these
+// arguments (it does for fp8 and bf16 caches; for MXFP4 when the scale array
+// and its row stride are 2-byte aligned, else the bf16-decoding kernel takes
+// the MXFP4 items one per workgroup).  Only those kernels run bins and can
+// merge partials themselves (Stage1Args::bins, Stage1Args::counters).
 bool stage1_dedicated(int fmt, const Stage1Args& a);
 
 // Launchers (mla_kernels.hip).  Return the launch status.
