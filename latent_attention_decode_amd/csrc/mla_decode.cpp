@@ -965,6 +965,7 @@ mla_status mla_decode_run(mla_decode_t h, const void* q, const void* kv, const v
   a.uniform_len = h->uniform_len;
   a.uniform_base = h->uniform_base;
   a.query_e4m3 = h->query_format == MLA_QUERY_E4M3;
+  a.part_bf16 = h->kv_dtype != MLA_KV_BF16;
   if (a.query_e4m3 && !mla::stage1_dedicated(h->kv_dtype, a))
     return fail(h, MLA_ERR_UNSUPPORTED,
                 "MLA_QUERY_E4M3 needs the MXFP4 split kernel, which needs an even scale stride and scale address");
@@ -990,6 +991,7 @@ mla_status mla_decode_run(mla_decode_t h, const void* q, const void* kv, const v
     mla::MergeArgs m{};
     m.work = reinterpret_cast<const mla::MergeSeq*>(plan_base + items_bytes);
     m.uniform_nslots = h->uniform_splits > 1 ? h->uniform_splits : 0;
+    m.part_bf16 = a.part_bf16;
     m.part_o = a.part_o;
     m.part_lse = a.part_lse;
     m.out = a.out;

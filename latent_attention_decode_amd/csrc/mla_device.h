@@ -52,17 +52,12 @@ __device__ __forceinline__ float xor_sum_groups(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Layout of one partial O (a workspace slot, 16 x 512 fp32): the float4 that
+// Layout of one partial O (a workspace slot, 16 x 512): the float4 that
 // lane l of wave w holds for column tile v (heads l % 16, dims
 // 128w + 16v + 4(l / 16) .. +3) is float4 number (8w + v) * 64 + l of the
-// slot, so that each store instruction of a wave writes 1 KB contiguously.
+// slot, so that each store instruction of a wave writes 1 KB contiguously
+// (512 B with bf16 partials, four bf16 in place of each float4).
 constexpr int kSlotFloat4 = kNumHeads * kVDim / 4;
-__device__ __forceinline__ void store_partial(float* part_o, int slot, int wave, int lane,
-                                              const f32x4 (&o)[8], float f) {
-  f32x4* dst = reinterpret_cast<f32x4*>(part_o) + (int64_t)slot * kSlotFloat4 + 8 * 64 * wave + lane;
-#pragma unroll
-  for (int v = 0; v < 8; ++v) dst[64 * v] = o[v] * f;
-}
 
 // ---------------------------------------------------------------------------
 // workgroup barrier that orders LDS only
@@ -255,9 +250,17 @@ __device__ __forceinline__ void finish_item(const Stage1Args& a, const WorkItem&
   for (int v = 0; v < NV; ++v) res[v] = o[v] * f;
   if (item.slot >= 0) {
     if (!a.counters) {  // the merge kernel combines the partials
-      f32x4* dst = reinterpret_cast<f32x4*>(a.part_o) + (int64_t)item.slot * kSlotFloat4 + 512 * W + lane;
+      const int64_t at = (int64_t)item.slot * kSlotFloat4 + 512 * W + lane;  // the layout above
+      if (a.part_bf16) {
+        uint2* dst = reinterpret_cast<uint2*>(a.part_o) + at;
 #pragma unroll
-      for (int v = 0; v < NV; ++v) dst[64 * (vb + v)] = res[v];  // the layout of store_partial
+        for (int v = 0; v < NV; ++v)
+          dst[64 * (vb + v)] = uint2{pack_bf16x2(res[v][0], res[v][1]), pack_bf16x2(res[v][2], res[v][3])};
+      } else {
+        f32x4* dst = reinterpret_cast<f32x4*>(a.part_o) + at;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) dst[64 * (vb + v)] = res[v];
+      }
       if (W == 0 && vb == 0 && g == 0) a.part_lse[(int64_t)item.slot * kNumHeads + r16] = lse;
       return;
     }

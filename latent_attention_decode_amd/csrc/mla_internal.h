@@ -133,11 +133,17 @@ struct Stage1Args {
   // Host side only: launch the split kernel's variant that takes the query as
   // one e4m3 code per element (fp8 and MXFP4 split kernels).
   int query_e4m3;
+  // Partials for the merge kernel as bf16 (fp8 and MXFP4 caches) instead of
+  // fp32 (bf16 cache): slot s's O at 16 KB s of part_o, the fp32 layout's
+  // float4 positions holding four bf16 each.  The merge inside the split
+  // kernel always keeps fp32.
+  int part_bf16;
 };
 
 struct MergeArgs {
   const MergeSeq* work;         // the sequences with >= 2 partials
   int uniform_nslots;           // > 0: merge job m is sequence m, slots [m n, m n + n)
+  int part_bf16;                // the partials' O is bf16 (see Stage1Args)
   const float* part_o;
   const float* part_lse;
   uint16_t* out;

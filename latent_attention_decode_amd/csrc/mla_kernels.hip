@@ -510,11 +510,25 @@ __global__ __launch_bounds__(kStage1Threads, F == kBf16 ? 1 : 2) void mla_stage1
 // (727205 `mla_rd`; 700955 `reduce_lse_v71`; 599694 `_flash_fp8_split_s2`).
 // One workgroup per (sequence, quarter of the columns): thread t merges
 // float4 numbers t and t + 256 of that quarter of every partial (both of head
-// t % 16, see store_partial), reading kMergeBatch partials at a time so that
-// their loads are in flight together.
+// t % 16, see kSlotFloat4), reading kMergeBatch partials at a time so that
+// their loads are in flight together.  BF: the partials' O is bf16.
 // ---------------------------------------------------------------------------
 constexpr int kMergeBatch = 4;
 
+// Float4 number e of the partial O at slot offset `slot` (in float4), fp32 or
+// bf16 (four bf16 in place of each float4).
+template <bool BF>
+__device__ __forceinline__ f32x4 load_partial(const float* part_o, int64_t slot, int e) {
+  if constexpr (BF) {
+    const uint2 u = reinterpret_cast<const uint2*>(part_o)[slot + e];
+    return f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u), __uint_as_float(u.y << 16),
+                 __uint_as_float(u.y & 0xFFFF0000u)};
+  } else {
+    return reinterpret_cast<const f32x4*>(part_o)[slot + e];
+  }
+}
+
+template <bool BF>
 __global__ __launch_bounds__(kMergeThreads) void mla_merge(MergeArgs a) {
   const int job = a.uniform_nslots > 0 ? xcd_block(blockIdx.x, gridDim.x) : (int)blockIdx.x;
   const MergeSeq seq = a.uniform_nslots > 0
@@ -524,8 +538,8 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge(MergeArgs a) {
   const int t = threadIdx.x;
   const int h = t & 15;
   const float* lse = a.part_lse + (int64_t)seq.slot_begin * kNumHeads + h;
-  const f32x4* po = reinterpret_cast<const f32x4*>(a.part_o) + (int64_t)seq.slot_begin * kSlotFloat4 +
-                    512 * quarter + t;
+  const int64_t po = (int64_t)seq.slot_begin * kSlotFloat4;
+  const int e0 = 512 * quarter + t;
   float M = kNegInf;  // running maximum of the lse seen so far
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   float W = 0.f;
@@ -536,8 +550,8 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge(MergeArgs a) {
     for (int k = 0; k < kMergeBatch; ++k) {  // all loads of the batch in flight together
       const int s = min(s0 + k, seq.nslots - 1);
       l[k] = lse[s * kNumHeads];
-      x0[k] = po[(int64_t)s * kSlotFloat4];
-      x1[k] = po[(int64_t)s * kSlotFloat4 + 256];
+      x0[k] = load_partial<BF>(a.part_o, po + (int64_t)s * kSlotFloat4, e0);
+      x1[k] = load_partial<BF>(a.part_o, po + (int64_t)s * kSlotFloat4, e0 + 256);
     }
     float mb = M;
 #pragma unroll
@@ -576,7 +590,7 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge(MergeArgs a) {
 // of group q merges float4 e = (2048 / P) part + t over the partials q,
 // q + S, q + 2S, .., and group 0 then merges the S results (running maximum,
 // weight sum and accumulator) through LDS.
-template <int P>
+template <int P, bool BF>
 __global__ __launch_bounds__(kMergeThreads) void mla_merge_wide(MergeArgs a) {
   constexpr int kPart = 2048 / P;  // float4 per part
   constexpr int S = kMergeThreads / kPart;
@@ -593,7 +607,7 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_wide(MergeArgs a) {
   const int e = kPart * part + t;  // float4 of the slot; its head is e % 16
   const int h = e & 15;
   const float* lse = a.part_lse + (int64_t)seq.slot_begin * kNumHeads + h;
-  const f32x4* po = reinterpret_cast<const f32x4*>(a.part_o) + (int64_t)seq.slot_begin * kSlotFloat4 + e;
+  const int64_t po = (int64_t)seq.slot_begin * kSlotFloat4;
   float M = kNegInf;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float W = 0.f;
@@ -604,7 +618,7 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_wide(MergeArgs a) {
     for (int k = 0; k < kMergeBatch; ++k) {  // all loads of the batch in flight together
       const int s = min(s0 + S * k, seq.nslots - 1);
       l[k] = lse[s * kNumHeads];
-      x[k] = po[(int64_t)s * kSlotFloat4];
+      x[k] = load_partial<BF>(a.part_o, po + (int64_t)s * kSlotFloat4, e);
     }
     float mb = M;
 #pragma unroll
@@ -739,16 +753,21 @@ hipError_t launch_merge(const MergeArgs& a, int num_merge_seqs, hipStream_t s, h
   MergeArgs args = a;
   void* params[] = {&args};
   const int parts = merge_parts(num_merge_seqs);
-  const void* fn = parts == 4    ? reinterpret_cast<const void*>(&mla_merge)
-                   : parts == 8  ? reinterpret_cast<const void*>(&mla_merge_wide<8>)
-                   : parts == 16 ? reinterpret_cast<const void*>(&mla_merge_wide<16>)
-                                 : reinterpret_cast<const void*>(&mla_merge_wide<32>);
+  const void* fn =
+      a.part_bf16 ? (parts == 4    ? reinterpret_cast<const void*>(&mla_merge<true>)
+                     : parts == 8  ? reinterpret_cast<const void*>(&mla_merge_wide<8, true>)
+                     : parts == 16 ? reinterpret_cast<const void*>(&mla_merge_wide<16, true>)
+                                   : reinterpret_cast<const void*>(&mla_merge_wide<32, true>))
+                  : (parts == 4    ? reinterpret_cast<const void*>(&mla_merge<false>)
+                     : parts == 8  ? reinterpret_cast<const void*>(&mla_merge_wide<8, false>)
+                     : parts == 16 ? reinterpret_cast<const void*>(&mla_merge_wide<16, false>)
+                                   : reinterpret_cast<const void*>(&mla_merge_wide<32, false>));
   return launch(fn, dim3(num_merge_seqs * parts), dim3(kMergeThreads), params, s, start, stop);
 }
 
 hipError_t kernel_attributes(int fmt, bool paged, bool row_pairs, bool query_e4m3, int which,
                              hipFuncAttributes* attr) {
-  const void* fn = which != 0        ? reinterpret_cast<const void*>(&mla_merge)
+  const void* fn = which != 0        ? reinterpret_cast<const void*>(&mla_merge<true>)
                    : fmt == kFp8     ? stage1_fp8_kernel(paged, row_pairs, query_e4m3)
                    : fmt == kMxfp4   ? stage1_mxfp4_kernel(paged, query_e4m3)
                                      : pick_stage1(fmt, paged);
