@@ -43,13 +43,12 @@
  * `_flash_fp8_split_s2`).  For sequences of different lengths the planner
  * cuts the batch into bins of about equal work, one per resident workgroup,
  * and a workgroup runs the items of its bin in turn (a sequence may span
- * bins).  The merge is a second kernel launch, except for a bf16 or MXFP4
- * plan, or an fp8 plan of paired query rows (multi-token decode), whose
- * items differ in length (at most 12 per sequence): there the item of a
- * sequence that finishes last merges its partials, so each call is one
- * launch.  A one-row fp8 plan runs faster with the second launch and keeps
- * it, and an MXFP4 cache whose scale array or stride is odd always takes it
- * (one item per workgroup).  No merge runs when no sequence is split.  The completion counters of that merge belong to the plan: runs of
+ * bins).  The merge is a second kernel launch, except for a bf16 cache
+ * whose plan's items differ in length (at most 12 per sequence): there the
+ * item of a sequence that finishes last merges its partials, so each call is
+ * one launch.  fp8 and MXFP4 plans hand their partials to the merge kernel
+ * as bf16, which measured faster than merging them inside the split kernel.
+ * No merge runs when no sequence is split.  The completion counters of that merge belong to the plan: runs of
  * one handle must not overlap (on any streams).  A plan may be made while
  * runs of the previous plan are still executing: it builds the work list on
  * the host and uploads it, without waiting, into the other of the handle's

@@ -789,14 +789,14 @@ mla_status plan_impl(mla_decode_t h, int batch, const int32_t* qo_indptr_host, c
   h->max_splits = plan.max_splits;
   h->num_merge = static_cast<int>(plan.merge.size());
   // The fused merge adds the last item's read-back of the other partials to
-  // that item, and to every split item a wait for its partial stores and a
-  // counter round trip.  Measured: a uniform plan, whose items all finish
-  // together, merges faster in the merge kernel, and so does a ragged plan of
-  // one-row fp8 items (1-4 % per call), where those waits hold up the next
-  // item of a bin that streams at the memory's pace; ragged MXFP4 and bf16
-  // plans and fp8 plans of paired query rows run about 1 % faster fused.
+  // that item, and to every split item a wait for its fp32 partial stores and
+  // a counter round trip.  Measured: a uniform plan, whose items all finish
+  // together, merges faster in the merge kernel, and so does every ragged
+  // fp8 and MXFP4 plan, whose partials go to the merge kernel as bf16
+  // (3-4 % per call); ragged bf16 plans, whose partials stay fp32, run about
+  // 1 % faster fused.
   h->fused_merge = plan.max_splits <= mla::kFusedMergeMaxSlots && plan.uniform_splits == 0 &&
-                   !(h->kv_dtype == MLA_KV_FP8_E4M3 && !plan.row_pairs);
+                   h->kv_dtype == MLA_KV_BF16;
   h->uniform_splits = plan.uniform_splits;
   h->uniform_chunk = plan.uniform_chunk;
   h->uniform_len = plan.uniform_len;

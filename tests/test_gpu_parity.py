@@ -285,15 +285,15 @@ def test_binned_ragged_batch(B, oracle_mod, kind, fmt, ps, shuffled, stride):
 
 
 @pytest.mark.parametrize("fmt,pairs,merge_kernel", [
-    ("fp8", False, True), ("mxfp4", False, False), ("bf16", False, False), ("fp8", True, False),
+    ("fp8", False, True), ("mxfp4", False, True), ("bf16", False, False), ("fp8", True, True),
 ])
 def test_where_the_merge_runs(B, oracle_mod, fmt, pairs, merge_kernel):
     """Which kernel combines a ragged plan's partials (at most 12 per
-    sequence): the merge kernel for one-row fp8 items, the split kernel
-    itself (the item that finishes last) for MXFP4 and bf16 caches and for
-    fp8 plans of paired query rows.  The merge kernel's time from the
-    kernel-attached events is 0 exactly when it was not launched; every
-    output against the oracle."""
+    sequence): the merge kernel for fp8 and MXFP4 caches (bf16 partials),
+    paired query rows included, the split kernel itself (the item that
+    finishes last, fp32 partials) for a bf16 cache.  The merge kernel's time
+    from the kernel-attached events is 0 exactly when it was not launched;
+    every output against the oracle."""
     if pairs:  # at most 2 query tokens per sequence: the fp8 kernel runs rows in pairs
         case = synth.make_case(fmt, [1500, 1100, 129, 1200, 900], seed=96, q_lens=[2, 2, 1, 2, 2])
     else:
@@ -492,14 +492,14 @@ def test_split_count_changes_only_rounding(B, oracle_mod):
 @pytest.mark.parametrize("fmt", ["fp8", "mxfp4", "bf16"])
 @pytest.mark.parametrize("split", [2, 5, 12, 13])
 def test_merge_repeated_calls(B, oracle_mod, fmt, split):
-    """With an MXFP4 or bf16 cache, a plan whose items differ in length and at
-    most 12 splits per sequence, the split kernel merges the partials itself:
+    """With a bf16 cache, a plan whose items differ in length and at most 12
+    splits per sequence, the split kernel merges the partials itself:
     per-sequence completion counters, reset by the item that finishes last,
-    pick the merging item; with 13, and for one-row fp8 plans, the merge
-    kernel runs.  Calls on one plan with new data each time must each match
-    the oracle (a partial left from the call before would not), and a repeat
-    of the first must agree with it bit for bit (the merge order does not
-    depend on which item finished last)."""
+    pick the merging item; with 13, and for fp8 and MXFP4 caches, the merge
+    kernel runs on bf16 partials.  Calls on one plan with new data each time
+    must each match the oracle (a partial left from the call before would
+    not), and a repeat of the first must agree with it bit for bit (the merge
+    order does not depend on which item finished last)."""
     lens = [3000, 1700, 129, 2500, 1]
     cases = [synth.make_case(fmt, lens, seed=31 + r) for r in range(3)]
     dec = B.MlaDecode(fmt, 1)
@@ -544,7 +544,7 @@ def test_prepared_run_matches_run(B, fmt, lens, ps):
 @pytest.mark.parametrize("fmt,lens,ps,split,stride", [
     ("fp8", [4096] * 8, 1, 0, 18),                 # uniform plan: the merge kernel
     ("fp8", [3000, 1700, 129, 2500, 1], 2, 5, 18),  # uneven items, then the merge kernel
-    ("mxfp4", [3000, 1700, 129, 2500, 1], 1, 5, 18),  # the merge inside the split kernel
+    ("bf16", [3000, 1700, 129, 2500, 1], 1, 5, 18),  # the merge inside the split kernel
     ("fp8", [3000, 1700, 129, 2500, 1], 1, 13, 18),  # too many splits for it: the merge kernel
     ("mxfp4", [3000, 1700, 129], 1, 0, 18),
     ("mxfp4", [2000, 300, 77], 1, 3, 19),          # odd scale stride: the bf16-decoding kernel
@@ -598,14 +598,14 @@ def test_workspace_too_small_is_rejected(B):
 def test_two_handles_on_two_streams(B, oracle_mod):
     """Handles share no state: two plans (one with a fused merge, one with the merge kernel)
     run interleaved on two streams, several times, and both match the oracle every time."""
-    case_a = synth.make_case("mxfp4", [3000, 700, 4100, 90], seed=91, page_size=2, shuffle_pages=True)
+    case_a = synth.make_case("bf16", [3000, 700, 4100, 90], seed=91, page_size=2, shuffle_pages=True)
     case_b = synth.make_case("fp8", [2048] * 8, seed=92)
     ref_a, ref_b = oracle_out(oracle_mod, case_a), oracle_out(oracle_mod, case_b)
     ta, tb = B.case_to_device(case_a), B.case_to_device(case_b)
     sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
-    da, db = B.MlaDecode("mxfp4", 2), B.MlaDecode("fp8")
+    da, db = B.MlaDecode("bf16", 2), B.MlaDecode("fp8")
     try:
-        da.plan(case_a.kv_indptr, case_a.kv_last_page_len)
+        da.plan(case_a.kv_indptr, case_a.kv_last_page_len, 5)  # uneven items, at most 12 each: fused
         db.plan(case_b.kv_indptr)
         outs_a = [torch.full((4, 16, 512), float("nan"), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
         outs_b = [torch.full((8, 16, 512), float("nan"), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
@@ -616,7 +616,7 @@ def test_two_handles_on_two_streams(B, oracle_mod):
             db.run(tb["q"], tb["kv"], tb["kv_scales"], tb["kv_indptr"], ob, stream=sb)
         torch.cuda.synchronize()
         for k in range(3):
-            check_close(outs_a[k].float().cpu().numpy().astype(np.float64), ref_a, "mxfp4", f"handle a call {k}")
+            check_close(outs_a[k].float().cpu().numpy().astype(np.float64), ref_a, "bf16", f"handle a call {k}")
             check_close(outs_b[k].float().cpu().numpy().astype(np.float64), ref_b, "fp8", f"handle b call {k}")
     finally:
         da.close()
@@ -626,7 +626,7 @@ def test_two_handles_on_two_streams(B, oracle_mod):
 @pytest.mark.parametrize("fmt", synth.FORMATS)
 def test_replanning_one_handle(B, oracle_mod, fmt):
     """One handle planned again and again for batches of other shapes (uniform with the
-    merge kernel, ragged with bins and the in-kernel merge (MXFP4, bf16), a single item, empty
+    merge kernel, ragged with bins and the in-kernel merge (bf16), a single item, empty
     sequences, more query rows): every run matches the oracle, so no state of an earlier
     plan (work list, completion counters, bins) leaks into a later one."""
     shapes = [([2048] * 8, None), (list(range(300, 300 + 150 * 60, 150)) + [0, 0], None), ([77], None),
